@@ -1,0 +1,215 @@
+"""fp64 CPU oracle for the DiG GLA token mixer and SREM step (ctypes over dig_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The product library never imports it.
+
+What each function computes, and the passages it follows, is documented in
+``dig_oracle.c``.  Arrays are float64 numpy arrays in the layouts stated there:
+GLA tensors ``[B, L, H, d]``, SREM tensors ``[B, L, D]``, conv weights ``[D, 3, 3]``.
+
+Functions with no pin of their own besides the tests in ``tests/test_oracle_*.py``:
+none -- every entry point is pinned there (brute force, closed forms, finite
+differences, library convolution, explicit transposes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dig_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ROW, ROW_REV, COL, COL_REV = 0, 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile dig_oracle.c with gcc (-O2, no fast-math, OpenMP over independent units)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        D = ctypes.POINTER(ctypes.c_double)
+        I64 = ctypes.POINTER(ctypes.c_int64)
+        i, d, v, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64
+        lib.oref_logsigmoid.argtypes = [d]
+        lib.oref_logsigmoid.restype = d
+        lib.oref_sigmoid.argtypes = [d]
+        lib.oref_sigmoid.restype = d
+        lib.oref_gate_logalpha.argtypes = [ctypes.c_size_t, D, d, D]
+        lib.oref_gla_recurrence.argtypes = [i, i, i, i, i, D, D, D, D, d, D]
+        lib.oref_output_stage.argtypes = [i, i, i, i, D, D, D, d, D, D]
+        lib.oref_gla_fwd.argtypes = [i, i, i, i, i, D, D, D, D, D, D, d, d, d, D, D, D]
+        lib.oref_gla_bwd_logalpha.argtypes = [i, i, i, i, i, D, D, D, D, D, D, d, d, D,
+                                              D, D, D, D, D, D]
+        lib.oref_gla_bwd.argtypes = [i, i, i, i, i, D, D, D, D, D, D, d, d, d, D,
+                                     D, D, D, D, D, D]
+        lib.oref_scan_canonical.argtypes = [i, i64, i64, i64]
+        lib.oref_scan_canonical.restype = i64
+        lib.oref_scan_perm.argtypes = [i, i64, i64, I64, I64]
+        lib.oref_reorient.argtypes = [i, i64, i64, i64, i, i, v, v]
+        lib.oref_dwconv3x3.argtypes = [i, i64, i64, i, i, i, D, D, D, D]
+        lib.oref_dwconv3x3_bwd.argtypes = [i, i64, i64, i, i, i, D, D, D, D, D, D]
+        lib.oref_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return int(_load().oref_num_threads())
+
+
+# ----------------------------------------------------------------------------- gate
+def logsigmoid(z: float) -> float:
+    return float(_load().oref_logsigmoid(float(z)))
+
+
+def gate_logalpha(z, tau: float):
+    z = _f64(z)
+    out = np.empty_like(z)
+    _load().oref_gate_logalpha(z.size, _p(z), float(tau), _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------- forward
+def gla_recurrence(q, k, v, loga, q_scale: float = 1.0):
+    """o_pre from the token-by-token recurrence, gate given as log(alpha) ([B,L,H,d_k])."""
+    q, k, v, loga = map(_f64, (q, k, v, loga))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.empty((B, L, H, dv))
+    _load().oref_gla_recurrence(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(loga),
+                                float(q_scale), _p(o))
+    return o
+
+
+def output_stage(o_pre, r, gamma=None, eps: float = 1e-5):
+    """(y, rstd): head-wise RMSNorm x gamma x Swish(r)."""
+    o_pre, r = _f64(o_pre), _f64(r)
+    B, L, H, dv = o_pre.shape
+    g = None if gamma is None else _f64(gamma)
+    y = np.empty_like(o_pre)
+    rstd = np.empty((B, L, H))
+    _load().oref_output_stage(B, L, H, dv, _p(o_pre), _p(r), _p(g), float(eps), _p(y), _p(rstd))
+    return y, rstd
+
+
+def gla_fwd(q, k, v, z, r, gamma=None, tau: float = 16.0, q_scale: float = 1.0,
+            eps: float = 1e-5):
+    """(y, o_pre, rstd) of the whole mixer forward with gate logits z."""
+    q, k, v, z, r = map(_f64, (q, k, v, z, r))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    g = None if gamma is None else _f64(gamma)
+    y = np.empty((B, L, H, dv))
+    o = np.empty((B, L, H, dv))
+    rstd = np.empty((B, L, H))
+    _load().oref_gla_fwd(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(z), _p(r), _p(g),
+                         float(tau), float(q_scale), float(eps), _p(y), _p(o), _p(rstd))
+    return y, o, rstd
+
+
+# ---------------------------------------------------------------------- backward
+def gla_bwd_logalpha(q, k, v, loga, r, dy, gamma=None, q_scale: float = 1.0,
+                     eps: float = 1e-5):
+    """dict of dq, dk, dv, dloga, dr, dgamma for L = <dy, y>, gate given as log(alpha)."""
+    q, k, v, loga, r, dy = map(_f64, (q, k, v, loga, r, dy))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    g = None if gamma is None else _f64(gamma)
+    out = {n: np.empty_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dloga", loga),
+                                            ("dr", r))}
+    out["dgamma"] = np.empty(dv)
+    _load().oref_gla_bwd_logalpha(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(loga), _p(r), _p(g),
+                                  float(q_scale), float(eps), _p(dy), _p(out["dq"]),
+                                  _p(out["dk"]), _p(out["dv"]), _p(out["dloga"]), _p(out["dr"]),
+                                  _p(out["dgamma"]))
+    return out
+
+
+def gla_bwd(q, k, v, z, r, dy, gamma=None, tau: float = 16.0, q_scale: float = 1.0,
+            eps: float = 1e-5):
+    """dict of dq, dk, dv, dz, dr, dgamma for L = <dy, y> with gate logits z."""
+    q, k, v, z, r, dy = map(_f64, (q, k, v, z, r, dy))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    g = None if gamma is None else _f64(gamma)
+    out = {n: np.empty_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dz", z),
+                                            ("dr", r))}
+    out["dgamma"] = np.empty(dv)
+    _load().oref_gla_bwd(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(z), _p(r), _p(g), float(tau),
+                         float(q_scale), float(eps), _p(dy), _p(out["dq"]), _p(out["dk"]),
+                         _p(out["dv"]), _p(out["dz"]), _p(out["dr"]), _p(out["dgamma"]))
+    return out
+
+
+# ------------------------------------------------------------------------- SREM
+def scan_canonical(d: int, gh: int, gw: int, p: int) -> int:
+    return int(_load().oref_scan_canonical(int(d), int(gh), int(gw), int(p)))
+
+
+def scan_perm(d: int, gh: int, gw: int):
+    """(perm, inv): perm[p] = canonical id at position p in order d; inv is its inverse."""
+    L = gh * gw
+    perm = np.empty(L, dtype=np.int64)
+    inv = np.empty(L, dtype=np.int64)
+    P = ctypes.POINTER(ctypes.c_int64)
+    _load().oref_scan_perm(int(d), int(gh), int(gw), perm.ctypes.data_as(P), inv.ctypes.data_as(P))
+    return perm, inv
+
+
+def reorient(x: np.ndarray, gh: int, gw: int, frm: int, to: int) -> np.ndarray:
+    """Exact byte gather of token rows; x is [B, L, D] of any fixed-size dtype."""
+    x = np.ascontiguousarray(x)
+    B, L, D = x.shape
+    assert L == gh * gw
+    y = np.empty_like(x)
+    _load().oref_reorient(B, gh, gw, D * x.itemsize, int(frm), int(to),
+                          x.ctypes.data_as(ctypes.c_void_p), y.ctypes.data_as(ctypes.c_void_p))
+    return y
+
+
+def dwconv3x3(x, w, gh: int, gw: int, layout: int, out_layout: int, bias=None):
+    x, w = _f64(x), _f64(w)
+    B, L, D = x.shape
+    b = None if bias is None else _f64(bias)
+    y = np.empty_like(x)
+    _load().oref_dwconv3x3(B, gh, gw, D, int(layout), int(out_layout), _p(x), _p(w), _p(b), _p(y))
+    return y
+
+
+def dwconv3x3_bwd(x, w, dy, gh: int, gw: int, layout: int, out_layout: int):
+    """(dx, dw, dbias) for L = <dy, dwconv3x3(x, w, bias)>."""
+    x, w, dy = _f64(x), _f64(w), _f64(dy)
+    B, L, D = x.shape
+    dx = np.empty_like(x)
+    dw = np.empty((D, 3, 3))
+    db = np.empty(D)
+    _load().oref_dwconv3x3_bwd(B, gh, gw, D, int(layout), int(out_layout), _p(x), _p(w), _p(dy),
+                               _p(dx), _p(dw), _p(db))
+    return dx, dw, db
