@@ -1,0 +1,103 @@
+// dig_internal.h -- host-side parameter blocks and launchers shared by the C-ABI layer
+// (dig_api.cpp) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dig {
+
+// ------------------------------------------------------------------ GLA forward
+struct GlaShape {
+  int B, L, H, dk, dv, C;   // C = chunk
+  int bf16;                 // 1: bf16 I/O, 0: fp32 I/O
+  int NC;                   // chunks per sequence = ceil(L / C)
+  int sc;                   // chunks per segment
+  int nseg;                 // segments per sequence = ceil(NC / sc)
+};
+
+// LDS carve-up of the chunk kernels (byte offsets; 0-sized arrays are unused).
+struct GlaLds {
+  int DKP, DK16, DV16, DVP, CK;
+  int off_q, off_k, off_kbt, off_vt, off_s, off_b, off_raw, off_r, off_gam, off_misc;
+  int bytes;
+};
+
+struct GlaFwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* z;
+  const void* r;
+  const float* norm_w;
+  void* y;
+  void* o_pre;
+  float* states;   // [B*H][NC][dk][dv] fp32: state entering each chunk
+  float* seg_lg;   // [B*H][nseg][dk] fp32: log2 of each segment's total decay
+  int B, L, H, dk, dv, NC, sc, nseg;
+  float g2scale;   // log2(e) / tau
+  float q_scale, eps;
+  int write_states;
+  GlaLds lds;
+};
+
+GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks);
+GlaLds gla_fwd_lds(const GlaShape& s, bool out_pass);
+size_t gla_states_bytes(const GlaShape& s);
+size_t gla_seglg_bytes(const GlaShape& s);
+int gla_max_state_tiles();
+
+hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
+
+// ----------------------------------------------------------------- GLA backward
+struct GlaBwdLds {
+  int DKP, DK16, DV16, DVP, DVK, CK;
+  int off_q, off_k, off_kb, off_v, off_do, off_s0, off_g, off_p, off_d, off_w, off_b, off_raw,
+      off_rdy, off_part, off_gam, off_misc;
+  int bytes;
+};
+
+struct GlaBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* z;
+  const void* r;
+  const float* norm_w;
+  const void* dy;
+  const float* states;  // forward's chunk-entry states [B*H][NC][dk][dv]
+  void* dq;
+  void* dk_;
+  void* dv_;
+  void* dz;
+  void* dr;
+  float* d_norm_w;
+  float* gstates;       // [B*H][nseg][dk][dv] gradient entering each segment's end
+  float* seg_lg;        // [B*H][nseg][dk]
+  float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
+  int B, L, H, dk, dv, NC, sc, nseg;
+  float g2scale, inv_tau, q_scale, eps;
+  GlaBwdLds lds;
+};
+
+GlaBwdLds gla_bwd_lds(const GlaShape& s, bool final_pass);
+size_t gla_bwd_workspace(const GlaShape& s);
+hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
+
+// ------------------------------------------------------------------------- misc
+// Zero n floats with a kernel (usable inside captured graphs, unlike a memset node).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
+
+// ------------------------------------------------------------------------- SREM
+hipError_t launch_reorient(int B, int gh, int gw, int D, int elt, int from, int to,
+                           const void* x, void* y, hipStream_t st);
+hipError_t launch_dwconv(int B, int gh, int gw, int D, int bf16, int layout, int out_layout,
+                         const void* x, const float* w, const float* bias, void* y,
+                         hipStream_t st);
+size_t dwconv_bwd_workspace(int B, int gh, int gw, int D);
+hipError_t launch_dwconv_bwd(int B, int gh, int gw, int D, int bf16, int layout, int out_layout,
+                             const void* x, const float* w, const void* dy, void* dx, float* dw,
+                             float* dbias, void* workspace, hipStream_t st);
+
+}  // namespace dig

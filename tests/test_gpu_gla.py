@@ -1,0 +1,232 @@
+"""GPU parity of the GLA mixer (dig_gla_fwd / dig_gla_bwd) against the fp64 oracle.
+
+Every case feeds identical quantised inputs to both sides and compares element by element
+with the normwise max-relative error max|gpu - ref| / max|ref|: <= 2e-2 for bf16 I/O and
+<= 1e-4 for fp32 I/O.  Outputs are NaN-poisoned before each call so unwritten elements fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import TOL, announce, gla_backward, gla_forward, has_gpu, maxrel, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+
+def _ref_fwd(case, q_scale=1.0, tau=16.0):
+    return oracle.gla_fwd(case.q, case.k, case.v, case.z, case.r, case.gamma, tau=tau,
+                          q_scale=q_scale)
+
+
+def _check_fwd(case, out, tol, q_scale=1.0, tau=16.0, what=""):
+    y_ref, o_ref, _ = _ref_fwd(case, q_scale, tau)
+    ey = maxrel(to_f64(out["y"]), y_ref)
+    eo = maxrel(to_f64(out["o_pre"]), o_ref) if out.get("o_pre") is not None else 0.0
+    print("  %s err y=%.3e o_pre=%.3e (tol %.0e)" % (what, ey, eo, tol), flush=True)
+    assert ey <= tol, ("y", ey)
+    assert eo <= tol, ("o_pre", eo)
+    return y_ref
+
+
+def _case(name, **kw):
+    cfg = W.CONFIGS[name]
+    over = {k: kw.pop(k) for k in list(kw) if k in ("batch", "seq_len")}
+    cfg_over = {k: kw.pop(k) for k in list(kw) if k in ("dtype",)}
+    if cfg_over:
+        cfg = W.cfg_replace(cfg, **cfg_over)
+    return W.make_gla_case(cfg, **over, **kw)
+
+
+# ----------------------------------------------------------------------- forward
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("seg", [0, 1])
+def test_fwd_tiny_f32(chunk, seg):
+    announce("fwd tiny_f32 chunk=%d seg=%d" % (chunk, seg))
+    case = _case("tiny_f32", random_gamma=True)
+    out = gla_forward(case, chunk, seg_chunks=seg)
+    _check_fwd(case, out, TOL["f32"])
+
+
+@pytest.mark.parametrize("name,batch,seq_len,chunk,seg", [
+    ("dig_s2_256", 2, 256, 64, 0),
+    ("dig_s2_256", 2, 256, 64, 1),
+    ("dig_s2_256", 1, 200, 64, 0),     # ragged tail
+    ("dig_s2_256", 1, 777, 32, 2),     # ragged, several segments
+    ("dig_s2_256", 1, 100, 16, 1),
+    ("dig_xl2_1024", 1, 1000, 64, 0),  # padded head dims 36/72, ragged
+    ("dig_xl2_1024", 1, 1000, 64, 3),
+    ("dig_xl2_1024", 2, 130, 16, 2),
+    ("dig_xl2_1024", 1, 1, 64, 0),     # single token
+])
+def test_fwd_bf16_shapes(name, batch, seq_len, chunk, seg):
+    announce("fwd %s B=%d L=%d chunk=%d seg=%d" % (name, batch, seq_len, chunk, seg))
+    case = _case(name, batch=batch, seq_len=seq_len, random_gamma=True)
+    out = gla_forward(case, chunk, seg_chunks=seg)
+    _check_fwd(case, out, TOL["bf16"])
+
+
+@pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fwd_gate_stress(stress, dtype):
+    kw = {"long_memory": dict(gate_bias=6.0), "fast_decay": dict(gate_bias=-6.0),
+          "wide_logits": dict(z_std=4.0), "extreme_decay": dict(gate_bias=-40.0, z_std=1.0)}[stress]
+    announce("fwd stress %s %s" % (stress, dtype))
+    case = _case("dig_s2_256", batch=1, seq_len=300, dtype=dtype, **kw)
+    out = gla_forward(case, 64, seg_chunks=2)
+    _check_fwd(case, out, TOL[dtype])
+    if dtype == "f32":  # fp32 backward at these head dims fits LDS with 32-token chunks
+        f = gla_forward(case, 32, seg_chunks=3, want_saved=True)
+        _check_fwd(case, f, TOL[dtype])
+        _check_bwd(case, gla_backward(case, f), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fwd_cancelling_first_token(dtype):
+    """o_0 = (q_0.k_0) v_0; with q_0.k_0 near zero the head-wise RMSNorm magnifies any
+    error of that dot product, so the diagonal of the chunk's gated Q K^T must be exact."""
+    announce("fwd cancelling first token %s" % dtype)
+    case = _case("dig_xl2_1024", batch=1, seq_len=130, dtype=dtype)
+    q0, k0 = case.q[:, 0], case.k[:, 0]                       # [B, H, dk]
+    proj = np.sum(q0 * k0, -1, keepdims=True) / np.sum(q0 * q0, -1, keepdims=True)
+    case.k[:, 0] = W.quantize(k0 - proj * q0, dtype)          # q_0.k_0 ~ rounding level
+    out = gla_forward(case, 64)
+    _check_fwd(case, out, TOL[dtype])
+
+
+def test_fwd_q_scale_tau_and_no_gamma():
+    announce("fwd q_scale=0.5 tau=4 gamma=None")
+    case = _case("dig_xl2_1024", batch=1, seq_len=160)
+    out = gla_forward(case, 32, q_scale=0.5, tau=4.0, gamma=False)
+    case.gamma = np.ones_like(case.gamma)
+    _check_fwd(case, out, TOL["bf16"], q_scale=0.5, tau=4.0)
+
+
+def test_fwd_chunk_invariance_and_determinism():
+    announce("fwd chunk invariance S shapes")
+    case = _case("dig_s2_256", batch=2, seq_len=256)
+    y_ref, _, _ = _ref_fwd(case)
+    outs = []
+    for chunk in (16, 32, 64):
+        o = gla_forward(case, chunk)
+        outs.append(to_f64(o["y"]))
+        assert maxrel(outs[-1], y_ref) <= TOL["bf16"]
+    for a in outs[1:]:
+        assert maxrel(a, outs[0]) <= TOL["bf16"]
+    a = to_f64(gla_forward(case, 64, seg_chunks=1)["y"])
+    b = to_f64(gla_forward(case, 64, seg_chunks=1)["y"])
+    assert np.array_equal(a, b), "two identical runs differ"
+
+
+def test_fwd_config_dig_s2_256_full():
+    announce("fwd dig_s2_256 full B=8 L=256")
+    case = _case("dig_s2_256")
+    out = gla_forward(case, 64)
+    _check_fwd(case, out, TOL["bf16"], what="dig_s2_256")
+
+
+def test_fwd_config_dig_s2_1792_full():
+    announce("fwd dig_s2_1792 full B=1 L=12544")
+    case = _case("dig_s2_1792")
+    out = gla_forward(case, 64)
+    _check_fwd(case, out, TOL["bf16"], what="dig_s2_1792")
+
+
+def test_fwd_config_dig_xl2_1024_four_directions():
+    cfg = W.CONFIGS["dig_xl2_1024"]
+    base = W.make_gla_case(cfg)
+    for d in W.SCHEDULE:
+        announce("fwd dig_xl2_1024 full direction=%s" % W.SCAN_NAMES[d])
+        # the same image tokens, stored in scan order d
+        re = lambda a: oracle.reorient(a.reshape(cfg.batch, cfg.seq_len, -1), cfg.grid_h, cfg.grid_w,
+                                       W.ROW, d).reshape(a.shape)
+        case = W.GLACase(cfg, re(base.q), re(base.k), re(base.v), re(base.z), re(base.r),
+                         base.gamma, re(base.dy))
+        out = gla_forward(case, 64, want_opre=False)
+        _check_fwd(case, out, TOL["bf16"], what="xl2_1024 dir %d" % d)
+
+
+# ---------------------------------------------------------------------- backward
+GRADS = ("dq", "dk", "dv", "dz", "dr")
+
+
+def _check_bwd(case, g, tol, what=""):
+    ref = oracle.gla_bwd(case.q, case.k, case.v, case.z, case.r, case.dy, case.gamma)
+    errs = {n: maxrel(to_f64(g[n]), ref[n]) for n in GRADS}
+    if g.get("dgamma") is not None:
+        errs["dgamma"] = maxrel(g["dgamma"].cpu().numpy().astype(np.float64), ref["dgamma"])
+    print("  %s " % what + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("seg", [0, 1])
+def test_bwd_tiny_f32(chunk, seg):
+    announce("bwd tiny_f32 chunk=%d seg=%d" % (chunk, seg))
+    case = _case("tiny_f32", random_gamma=True)
+    f = gla_forward(case, chunk, seg_chunks=seg, want_saved=True)
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["f32"])
+
+
+@pytest.mark.parametrize("name,batch,seq_len,chunk,seg", [
+    ("dig_s2_256", 2, 256, 64, 0),
+    ("dig_s2_256", 1, 333, 64, 2),
+    ("dig_s2_256", 1, 100, 16, 1),
+    ("dig_xl2_2048", 1, 256, 64, 0),   # the 16x16 crop of the 2048-px config
+    ("dig_xl2_2048", 1, 256, 64, 1),
+    ("dig_xl2_2048", 1, 999, 32, 3),
+])
+def test_bwd_bf16_shapes(name, batch, seq_len, chunk, seg):
+    announce("bwd %s B=%d L=%d chunk=%d seg=%d" % (name, batch, seq_len, chunk, seg))
+    case = _case(name, batch=batch, seq_len=seq_len, random_gamma=True)
+    f = gla_forward(case, chunk, seg_chunks=seg, want_saved=True)
+    _check_fwd(case, f, TOL["bf16"])
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["bf16"])
+
+
+@pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
+def test_bwd_gate_stress(stress):
+    kw = {"long_memory": dict(gate_bias=6.0), "fast_decay": dict(gate_bias=-6.0),
+          "wide_logits": dict(z_std=4.0), "extreme_decay": dict(gate_bias=-40.0, z_std=1.0)}[stress]
+    announce("bwd stress %s" % stress)
+    case = _case("dig_s2_256", batch=1, seq_len=300, **kw)
+    f = gla_forward(case, 64, seg_chunks=2, want_saved=True)
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_cancelling_first_token(dtype):
+    """With o_0 parallel to v_0 the RMSNorm gradient makes do_0.v_0 cancel; the gradients of
+    the first token must still match."""
+    announce("bwd cancelling first token %s" % dtype)
+    case = _case("dig_xl2_2048", batch=1, seq_len=96, dtype=dtype)
+    q0, k0 = case.q[:, 0], case.k[:, 0]
+    proj = np.sum(q0 * k0, -1, keepdims=True) / np.sum(q0 * q0, -1, keepdims=True)
+    case.k[:, 0] = W.quantize(k0 - 0.98 * proj * q0, dtype)   # small but not zero q_0.k_0
+    f = gla_forward(case, 32 if dtype == "f32" else 64, want_saved=True)
+    _check_fwd(case, f, TOL[dtype])
+    _check_bwd(case, gla_backward(case, f), TOL[dtype])
+
+
+def test_bwd_determinism():
+    announce("bwd determinism")
+    case = _case("dig_xl2_2048", batch=1, seq_len=512)
+    f = gla_forward(case, 64, seg_chunks=2, want_saved=True)
+    g1 = gla_backward(case, f)
+    g2 = gla_backward(case, f)
+    for n in GRADS + ("dgamma",):
+        assert np.array_equal(to_f64(g1[n]), to_f64(g2[n])), n
+
+
+def test_fwd_bwd_config_dig_xl2_2048_full():
+    announce("fwd+bwd dig_xl2_2048 full B=1 L=16384")
+    case = _case("dig_xl2_2048")
+    f = gla_forward(case, 64, want_saved=True)
+    _check_fwd(case, f, TOL["bf16"], what="xl2_2048")
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["bf16"], what="xl2_2048")
