@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the DiG hot path on one MI355X: GLA token mixer + SREM, forward and backward.
+
+One step = one pass of the whole path over one batch of synthetic DiG-S/2 256-px input:
+for each of the 12 blocks (scan directions cycling row, row_rev, col, col_rev)
+    dig_gla_fwd (saving chunk states) -> dig_dwconv3x3 (fused reorient to the next direction)
+then, blocks in reverse,
+    dig_dwconv3x3_bwd -> dig_gla_bwd.
+Inputs are generated on the GPU before timing (seeded, x ~ N(0,1), weights ~ N(0, 1/D)).
+The metric is GLA-layer tokens/s: batch * tokens * blocks / step time.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dig_s2_256", choices=sorted(W.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seg-chunks", type=int, default=0)
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def gen_blocks(cfg, nblocks, seed):
+    """Per-block bf16 operands on the GPU: projections of x ~ N(0,1) by weights ~ N(0,1/D)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    B, L, D, H, dk, dv = cfg.batch, cfg.seq_len, cfg.d_model, cfg.heads, cfg.d_k, cfg.d_v
+    s = 1.0 / np.sqrt(D)
+    blocks = []
+    for _ in range(nblocks):
+        x = torch.randn(B * L, D, device="cuda", generator=g)
+        w = lambda n, m: torch.randn(n, m, device="cuda", generator=g) * s
+        q = (x @ w(D, H * dk)).view(B, L, H, dk)
+        k = (x @ w(D, H * dk)).view(B, L, H, dk)
+        v = (x @ w(D, H * dv)).view(B, L, H, dv)
+        z = ((x @ w(D, cfg.rank)) @ w(cfg.rank, H * dk)).view(B, L, H, dk)
+        r = (x @ w(D, H * dv)).view(B, L, H, dv)
+        cw = torch.randn(D, 3, 3, device="cuda", generator=g) / 3.0
+        dy = torch.randn(B, L, H, dv, device="cuda", generator=g)
+        dys = torch.randn(B, L, D, device="cuda", generator=g)
+        bf = lambda t: t.to(torch.bfloat16).contiguous()
+        blocks.append(dict(q=bf(q), k=bf(k), v=bf(v), z=bf(z), r=bf(r), x=bf(x.view(B, L, D)),
+                           cw=cw.contiguous(), dy=bf(dy), dys=bf(dys),
+                           gamma=torch.ones(dv, device="cuda")))
+    return blocks
+
+
+class Path:
+    """Buffers and the library calls of one step."""
+
+    def __init__(self, cfg, blocks, seg_chunks):
+        import torch
+        import diffusion_backbone_amd as dig
+        self.dig, self.cfg, self.blocks = dig, cfg, blocks
+        B, L, H, dk, dv, D = cfg.batch, cfg.seq_len, cfg.heads, cfg.d_k, cfg.d_v, cfg.d_model
+        self.desc = dig.make_desc(B, L, H, dk, dv, cfg.chunk, cfg.tau, 1.0, 1e-5, dig.DIG_BF16,
+                                  seg_chunks)
+        bt = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+        by = lambda n: torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+        self.fws_b = dig.dig_gla_fwd_workspace_bytes(self.desc)
+        self.bws_b = dig.dig_gla_bwd_workspace_bytes(self.desc)
+        self.cws_b = dig.dig_dwconv3x3_bwd_workspace_bytes(B, cfg.grid_h, cfg.grid_w, D)
+        self.fws, self.bws, self.cws = by(self.fws_b), by(self.bws_b), by(self.cws_b)
+        n = len(blocks)
+        self.saved = [by(dig.dig_gla_saved_bytes(self.desc)) for _ in range(n)]
+        self.y = [bt(B, L, H, dv) for _ in range(n)]
+        self.xs = [bt(B, L, D) for _ in range(n)]
+        self.g = {k: bt(B, L, H, dk) for k in ("dq", "dk", "dz")}
+        self.g.update({k: bt(B, L, H, dv) for k in ("dv", "dr")})
+        self.dgamma = torch.empty(dv, device="cuda")
+        self.dxs = bt(B, L, D)
+        self.dw = torch.empty(D, 3, 3, device="cuda")
+        self.db = torch.empty(D, device="cuda")
+        self.sched = [W.SCHEDULE[l % 4] for l in range(n + 1)]
+
+    def gla_fwd(self, l):
+        b = self.blocks[l]
+        self.dig.dig_gla_fwd(self.desc, b["q"], b["k"], b["v"], b["z"], b["r"], b["gamma"],
+                             self.y[l], None, self.saved[l], self.fws, self.fws_b)
+
+    def srem_fwd(self, l):
+        c, b = self.cfg, self.blocks[l]
+        self.dig.dig_dwconv3x3(c.batch, c.grid_h, c.grid_w, c.d_model, self.dig.DIG_BF16,
+                               self.sched[l], self.sched[l + 1], b["x"], b["cw"], None, self.xs[l])
+
+    def srem_bwd(self, l):
+        c, b = self.cfg, self.blocks[l]
+        self.dig.dig_dwconv3x3_bwd(c.batch, c.grid_h, c.grid_w, c.d_model, self.dig.DIG_BF16,
+                                   self.sched[l], self.sched[l + 1], b["x"], b["cw"], b["dys"],
+                                   self.dxs, self.dw, self.db, self.cws, self.cws_b)
+
+    def gla_bwd(self, l):
+        b, g = self.blocks[l], self.g
+        self.dig.dig_gla_bwd(self.desc, b["q"], b["k"], b["v"], b["z"], b["r"], b["gamma"],
+                             b["dy"], self.saved[l], g["dq"], g["dk"], g["dv"], g["dz"], g["dr"],
+                             self.dgamma, self.bws, self.bws_b)
+
+    def step(self, ev=None):
+        n = len(self.blocks)
+        for l in range(n):
+            if ev is not None:
+                ev.record_pair("gla_fwd", lambda: self.gla_fwd(l))
+            else:
+                self.gla_fwd(l)
+            self.srem_fwd(l)
+        for l in reversed(range(n)):
+            self.srem_bwd(l)
+            if ev is not None:
+                ev.record_pair("gla_bwd", lambda: self.gla_bwd(l))
+            else:
+                self.gla_bwd(l)
+
+    def step_fwd(self):
+        for l in range(len(self.blocks)):
+            self.gla_fwd(l)
+            self.srem_fwd(l)
+
+
+class EventTimer:
+    """HIP events around chosen calls on torch's current stream (the stream they run on)."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def record_pair(self, name, fn):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def avg_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ps) / max(len(ps), 1)
+
+
+def gla_bytes_per_token_head(cfg, which):
+    """Algorithmic HBM bytes per (token, head) of one mixer call (bf16 I/O)."""
+    dk, dv = cfg.d_k, cfg.d_v
+    if which == "fwd":   # read q, k, z, v, r; write y
+        return 2 * (3 * dk + 3 * dv)
+    # bwd: read q, k, z, v, r, dy; write dq, dk, dz, dv, dr
+    return 2 * (6 * dk + 5 * dv)
+
+
+def cpu_baseline(cfg, nblocks):
+    """The fp64 oracle on the host: one full step (fwd + bwd of every block) of a bounded
+    sample of the batch, scaled to GLA-layer tokens/s."""
+    import oracle
+    sample_batch = max(1, min(cfg.batch, 2))
+    scfg = W.cfg_replace(cfg, batch=sample_batch)
+    case = W.make_gla_case(scfg)
+    srem = W.make_srem_case(scfg)
+    gh, gw = cfg.grid_h, cfg.grid_w
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for l in range(nblocks):
+            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
+            oracle.gla_fwd(case.q, case.k, case.v, case.z, case.r, case.gamma)
+            oracle.dwconv3x3(srem.x, srem.w, gh, gw, d0, d1)
+        for l in reversed(range(nblocks)):
+            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
+            oracle.dwconv3x3_bwd(srem.x, srem.w, srem.dy, gh, gw, d0, d1)
+            oracle.gla_bwd(case.q, case.k, case.v, case.z, case.r, case.dy, case.gamma)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 200:
+            break
+    tokens = sample_batch * cfg.seq_len * nblocks * reps
+    return {"value": tokens / el, "unit": "GLA-layer tokens/s (fwd+bwd)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d full fwd+bwd step(s) of %d of %d images (%d blocks, %d tokens each), %.1f s"
+                      % (reps, sample_batch, cfg.batch, nblocks, cfg.seq_len, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path here has no multi-GPU leg "
+              "(data-parallel sharding is a design note, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    cfg = W.CONFIGS[args.workload]
+    nblocks = cfg.blocks
+    blocks = gen_blocks(cfg, nblocks, cfg.seed)
+    path = Path(cfg, blocks, args.seg_chunks)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    ev = EventTimer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        path.step(ev)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tokens = cfg.batch * cfg.seq_len * nblocks
+    value = tokens / (ms / 1e3)
+
+    # forward-only figure (same calls without the backward), reported beside the main value
+    for _ in range(3):
+        path.step_fwd()
+    torch.cuda.synchronize()
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for _ in range(args.steps):
+        path.step_fwd()
+    e2.record()
+    torch.cuda.synchronize()
+    ms_fwd = s2.elapsed_time(e2) / args.steps
+
+    th = cfg.batch * cfg.seq_len * cfg.heads
+    rl = {}
+    for name, which in (("gla_fwd", "fwd"), ("gla_bwd", "bwd")):
+        t = ev.avg_ms(name)
+        byts = gla_bytes_per_token_head(cfg, which) * th
+        rl[name] = {"ms": t, "bytes": byts, "gbs": byts / (t / 1e3) / 1e9}
+    dom = max(rl, key=lambda n: rl[n]["ms"])
+    roof = {"bound": "hbm", "achieved": round(rl[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(rl[dom]["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gla_bwd_kernel" if dom == "gla_bwd" else "gla_fwd_kernel",
+            "call": "dig_" + dom, "avg_call_us": round(rl[dom]["ms"] * 1e3, 2),
+            "algorithmic_bytes_per_launch": rl[dom]["bytes"]}
+    other = [n for n in rl if n != dom][0]
+    out = {
+        "metric": "GLA-layer tokens/s (fwd+bwd)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "grid": [cfg.grid_h, cfg.grid_w],
+                   "seq_len": cfg.seq_len, "d_model": cfg.d_model, "heads": cfg.heads,
+                   "d_k": cfg.d_k, "d_v": cfg.d_v, "chunk": cfg.chunk, "blocks": nblocks,
+                   "step": "12 x (gla_fwd + dwconv3x3 reorient) + 12 x (dwconv3x3_bwd + gla_bwd)"},
+        "fwd_only": {"value": round(tokens / (ms_fwd / 1e3), 1), "unit": "tokens/s",
+                     "ms_per_step": round(ms_fwd, 4)},
+        "roofline": roof,
+        "roofline_other_call": {"call": "dig_" + other, "avg_call_us": round(rl[other]["ms"] * 1e3, 2),
+                                "achieved_gbs": round(rl[other]["gbs"], 1),
+                                "frac": round(rl[other]["gbs"] / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, nblocks)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

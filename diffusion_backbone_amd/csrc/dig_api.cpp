@@ -82,8 +82,9 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
     return fail(DIG_ERR_SHAPE, "norm_eps must be finite and >= 0");
   if (!std::isfinite(d->q_scale)) return fail(DIG_ERR_SHAPE, "q_scale must be finite");
   if (d->seg_chunks < 0) return fail(DIG_ERR_SHAPE, "seg_chunks must be >= 0");
-  if (d->d_k > 128 || d->d_v > 128)
-    return fail(DIG_ERR_UNSUPPORTED, "d_k (%d) and d_v (%d) must be <= 128", d->d_k, d->d_v);
+  int ndk = 0, ndv = 0;
+  if (!dig::gla_dim_class(d->d_k, d->d_v, &ndk, &ndv))
+    return fail(DIG_ERR_UNSUPPORTED, "d_k (%d) must be <= 64 and d_v (%d) <= 128", d->d_k, d->d_v);
   const long long rows = (long long)d->batch * d->seq_len * d->heads;
   if (rows * (d->d_k > d->d_v ? d->d_k : d->d_v) > (1LL << 40))
     return fail(DIG_ERR_UNSUPPORTED, "tensor too large");
@@ -91,12 +92,6 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
     return fail(DIG_ERR_UNSUPPORTED, "batch * heads too large");
   *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, d->chunk,
                      d->dtype == DIG_BF16, d->seg_chunks);
-  const int dk16 = (d->d_k + 15) / 16, dv16 = (d->d_v + 15) / 16;
-  if (dk16 * dv16 > dig::gla_max_state_tiles())
-    return fail(DIG_ERR_UNSUPPORTED, "d_k/16 * d_v/16 = %d state tiles exceeds %d", dk16 * dv16,
-                dig::gla_max_state_tiles());
-  if ((d->chunk / 16) * dk16 > 16)
-    return fail(DIG_ERR_UNSUPPORTED, "chunk/16 * d_k/16 must be <= 16 (backward tiles)");
   const int lds = pass == kFwd ? dig::gla_fwd_lds(*s, true).bytes : dig::gla_bwd_lds(*s, true).bytes;
   if (lds > kLdsLimit)
     return fail(DIG_ERR_UNSUPPORTED, "%s needs %d bytes of LDS for this shape (limit %d)",
@@ -155,7 +150,7 @@ size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
 size_t dig_gla_fwd_workspace_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;
   if (check_desc(d, &s, kFwd) != DIG_OK) return 0;
-  if (s.nseg == 1) return 0;  // one segment per sequence: no cross-segment scan
+  if (s.nseg == 1 || s.prefix) return 0;  // no cross-segment scan
   return a256(dig::gla_states_bytes(s)) + a256(dig::gla_seglg_bytes(s));
 }
 

@@ -22,6 +22,35 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }  // RNE
 
+// Hardware transcendental units (about 1 ulp): 2^x, log2(x), 1/x.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log2(sigmoid(z)) = min(z, 0) log2(e) - log2(1 + 2^(-|z| log2(e))): no overflow for any z.
+__device__ __forceinline__ float log2_sigmoid(float z) {
+  return fminf(z, 0.f) * 1.4426950408889634f - flog2(1.f + fexp2(-fabsf(z) * 1.4426950408889634f));
+}
+__device__ __forceinline__ float fast_sigmoid(float z) {
+  return frcp(1.f + fexp2(-z * 1.4426950408889634f));
+}
+
+// Element-type-specific math: bf16 I/O uses the hardware units above; fp32 I/O keeps the
+// correctly rounded library forms so that its tighter accuracy holds on ill-conditioned rows.
+template <typename T> struct Fm;
+template <> struct Fm<bf16> {
+  __device__ static __forceinline__ float exp2(float x) { return fexp2(x); }
+  __device__ static __forceinline__ float lsig2(float z) { return log2_sigmoid(z); }
+  __device__ static __forceinline__ float sig(float z) { return fast_sigmoid(z); }
+};
+template <> struct Fm<float> {
+  __device__ static __forceinline__ float exp2(float x) { return exp2f(x); }
+  __device__ static __forceinline__ float lsig2(float z) {
+    return (fminf(z, 0.f) - log1pf(expf(-fabsf(z)))) * 1.4426950408889634f;
+  }
+  __device__ static __forceinline__ float sig(float z) { return 1.f / (1.f + expf(-z)); }
+};
+
 // logsigmoid(z) = min(z, 0) - log1p(exp(-|z|)), no overflow for any finite z.
 __device__ __forceinline__ float logsigmoid_f(float z) {
   return fminf(z, 0.0f) - log1pf(expf(-fabsf(z)));
@@ -194,5 +223,104 @@ __device__ __forceinline__ void store_rows(T* gdst, long gstride, const T* src, 
 }
 
 __device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// ------------------------------------------------------- direct global -> LDS copies
+// gfx950 LDS DMA: lane i of a wave writes its PS-byte piece to (wave-uniform LDS base) + i*PS.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+template <int PS>
+__device__ __forceinline__ void dma_pieces(unsigned char* lds_dst, const unsigned char* gsrc,
+                                           long gstride, int ppr, int npieces, int wave,
+                                           int nwaves, int lane) {
+  for (int base = wave * 64; base < npieces; base += nwaves * 64) {
+    const int e = base + lane;
+    if (e < npieces) {
+      const int r = e / ppr, c = e - r * ppr;
+      gbl_ptr_t g = (gbl_ptr_t)(gsrc + (long)r * gstride + c * PS);
+      lds_ptr_t l = (lds_ptr_t)(lds_dst + base * PS);
+      if constexpr (PS == 16)
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      else if constexpr (PS == 4)
+        __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+    }
+  }
+}
+
+// Lane -> piece mapping of a tile with `cols` elements per row, copied with one DMA
+// instruction covering rpi whole rows (pieces of ps bytes, ppr pieces per row).
+struct DmaMap {
+  int ps, ppr, rpi, lr, lc, rowbytes;
+};
+
+template <typename T>
+__device__ __forceinline__ DmaMap dma_map(int cols, int lane) {
+  DmaMap m;
+  m.rowbytes = cols * (int)sizeof(T);
+  m.ps = (m.rowbytes & 15) == 0 ? 16 : ((m.rowbytes & 3) == 0 ? 4 : 2);
+  m.ppr = m.rowbytes / m.ps;
+  m.rpi = m.ppr <= 64 ? 64 / m.ppr : 0;
+  m.lr = m.rpi ? lane / m.ppr : 0;
+  m.lc = lane - m.lr * m.ppr;
+  return m;
+}
+
+// Rows [0, valid) of a token-major tile into packed LDS rows, whole rows per instruction.
+template <typename T>
+__device__ __forceinline__ void dma_rows(const DmaMap& m, T* lds_dst, const T* gsrc, long gstride,
+                                         int valid, int wave, int nwaves, int lane) {
+  unsigned char* d = reinterpret_cast<unsigned char*>(lds_dst);
+  const unsigned char* s = reinterpret_cast<const unsigned char*>(gsrc);
+  const long gs = gstride * (long)sizeof(T);
+  if (m.rpi == 0) {  // rows wider than one instruction: piecewise
+    if (m.ps == 16) dma_pieces<16>(d, s, gs, m.ppr, valid * m.ppr, wave, nwaves, lane);
+    else if (m.ps == 4) dma_pieces<4>(d, s, gs, m.ppr, valid * m.ppr, wave, nwaves, lane);
+    else dma_pieces<2>(d, s, gs, m.ppr, valid * m.ppr, wave, nwaves, lane);
+    return;
+  }
+  for (int rb = wave * m.rpi; rb < valid; rb += nwaves * m.rpi) {
+    const int r = rb + m.lr;
+    if (m.lr < m.rpi && r < valid) {
+      gbl_ptr_t g = (gbl_ptr_t)(s + (long)r * gs + m.lc * m.ps);
+      lds_ptr_t l = (lds_ptr_t)(d + rb * m.rowbytes);
+      if (m.ps == 16)
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      else if (m.ps == 4)
+        __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+    }
+  }
+}
+
+// Starts an asynchronous copy of rows [0, valid) of a token-major tile (row r at gsrc + r *
+// gstride elements, `cols` elements per row) into LDS as packed rows (pitch = cols).  The
+// caller waits with dma_wait() + a barrier, and zero-fills rows >= valid itself.
+template <typename T>
+__device__ __forceinline__ void dma_tile(T* lds_dst, const T* gsrc, long gstride, int valid,
+                                         int cols, int wave, int nwaves, int lane) {
+  const int rowbytes = cols * (int)sizeof(T);
+  const long gs = gstride * (long)sizeof(T);
+  unsigned char* d = reinterpret_cast<unsigned char*>(lds_dst);
+  const unsigned char* s = reinterpret_cast<const unsigned char*>(gsrc);
+  if ((rowbytes & 15) == 0)
+    dma_pieces<16>(d, s, gs, rowbytes >> 4, valid * (rowbytes >> 4), wave, nwaves, lane);
+  else if ((rowbytes & 3) == 0)
+    dma_pieces<4>(d, s, gs, rowbytes >> 2, valid * (rowbytes >> 2), wave, nwaves, lane);
+  else
+    dma_pieces<2>(d, s, gs, rowbytes >> 1, valid * (rowbytes >> 1), wave, nwaves, lane);
+}
+
+// Waits for this wave's outstanding memory operations (LDS DMA included).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Zero rows [valid, rows) of a packed LDS tile.
+template <typename T>
+__device__ __forceinline__ void zero_rows(T* dst, int valid, int rows, int cols, int tid,
+                                          int nthr) {
+  for (int i = valid * cols + tid; i < rows * cols; i += nthr) dst[i] = from_f<T>(0.f);
+}
 
 }  // namespace dig

@@ -15,16 +15,23 @@ struct GlaShape {
   int NC;                   // chunks per sequence = ceil(L / C)
   int sc;                   // chunks per segment
   int nseg;                 // segments per sequence = ceil(NC / sc)
+  int prefix;               // 1: each segment recomputes its incoming state (short sequences)
+  int ndk, ndv;             // compiled head-dim class: d_k <= 16*ndk, d_v <= 16*ndv
 };
+
+// Head-dim classes the kernels are compiled for (16-wide tiles of d_k and d_v).
+bool gla_dim_class(int dk, int dv, int* ndk, int* ndv);
 
 // LDS carve-up of the chunk kernels (byte offsets; 0-sized arrays are unused).
 struct GlaLds {
   int DKP, DK16, DV16, DVP, CK;
-  int off_q, off_k, off_kbt, off_vt, off_s, off_b, off_raw, off_r, off_gam, off_misc;
+  int off_q, off_k, off_kbt, off_vt, off_s, off_b, off_raw, off_rv, off_r, off_gam, off_qk,
+      off_misc;
   int bytes;
 };
 
 struct GlaFwdParams {
+  int C, prefix;
   const void* q;
   const void* k;
   const void* v;
@@ -46,7 +53,6 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
 GlaLds gla_fwd_lds(const GlaShape& s, bool out_pass);
 size_t gla_states_bytes(const GlaShape& s);
 size_t gla_seglg_bytes(const GlaShape& s);
-int gla_max_state_tiles();
 
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
 
@@ -54,11 +60,12 @@ hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
 struct GlaBwdLds {
   int DKP, DK16, DV16, DVP, DVK, CK;
   int off_q, off_k, off_kb, off_v, off_do, off_s0, off_g, off_p, off_d, off_w, off_b, off_raw,
-      off_rdy, off_part, off_gam, off_misc;
+      off_rdy, off_qk, off_part, off_gam, off_misc;
   int bytes;
 };
 
 struct GlaBwdParams {
+  int C, prefix;
   const void* q;
   const void* k;
   const void* v;

@@ -71,7 +71,7 @@ typedef struct {
   int32_t batch;      /* B >= 0 */
   int32_t seq_len;    /* L >= 0 tokens per image, in the current scan order */
   int32_t heads;      /* H >= 1 */
-  int32_t d_k;        /* key dim per head, 1..128 (true size; MFMA padding is internal) */
+  int32_t d_k;        /* key dim per head, 1..64 (true size; MFMA padding is internal) */
   int32_t d_v;        /* value dim per head, 1..128 */
   int32_t chunk;      /* 16, 32 or 64 tokens per chunk (the pages' M) */
   float tau;          /* gate temperature, > 0 (DiG uses 16) */

@@ -54,7 +54,7 @@ def _fwd(desc, q=BAD_PTR, ws=None, wsb=0, y=BAD_PTR + 0x100000000, saved=None):
     (dict(batch=-1), dig.DIG_ERR_SHAPE),
     (dict(heads=0), dig.DIG_ERR_SHAPE),
     (dict(d_k=0), dig.DIG_ERR_SHAPE),
-    (dict(d_k=129), dig.DIG_ERR_UNSUPPORTED),
+    (dict(d_k=65), dig.DIG_ERR_UNSUPPORTED),
     (dict(d_v=200), dig.DIG_ERR_UNSUPPORTED),
     (dict(chunk=48), dig.DIG_ERR_UNSUPPORTED),
     (dict(dtype=7), dig.DIG_ERR_UNSUPPORTED),

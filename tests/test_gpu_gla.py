@@ -91,7 +91,7 @@ def test_fwd_cancelling_first_token(dtype):
     q0, k0 = case.q[:, 0], case.k[:, 0]                       # [B, H, dk]
     proj = np.sum(q0 * k0, -1, keepdims=True) / np.sum(q0 * q0, -1, keepdims=True)
     case.k[:, 0] = W.quantize(k0 - proj * q0, dtype)          # q_0.k_0 ~ rounding level
-    out = gla_forward(case, 64)
+    out = gla_forward(case, 64 if dtype == "bf16" else 32)   # fp32 XL tiles fit LDS at 32
     _check_fwd(case, out, TOL[dtype])
 
 
@@ -208,7 +208,7 @@ def test_bwd_cancelling_first_token(dtype):
     q0, k0 = case.q[:, 0], case.k[:, 0]
     proj = np.sum(q0 * k0, -1, keepdims=True) / np.sum(q0 * q0, -1, keepdims=True)
     case.k[:, 0] = W.quantize(k0 - 0.98 * proj * q0, dtype)   # small but not zero q_0.k_0
-    f = gla_forward(case, 32 if dtype == "f32" else 64, want_saved=True)
+    f = gla_forward(case, 16 if dtype == "f32" else 64, want_saved=True)  # fp32 XL: LDS fit
     _check_fwd(case, f, TOL[dtype])
     _check_bwd(case, gla_backward(case, f), TOL[dtype])
 
