@@ -271,12 +271,209 @@ __global__ __launch_bounds__(256) void dwconv_dw_reduce(const float* __restrict_
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= 10L * D) return;
   const int t = (int)(idx / D), c = (int)(idx - (long)t * D);
-  float s = 0.f;
-  for (int i = 0; i < nblk; ++i) s += part[((long)i * 10 + t) * D + c];
+  // eight independent partial sums (loads in flight together), combined in a fixed order
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = 0;
+  for (; i + 8 <= nblk; i += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s8[u] += part[((long)(i + u) * 10 + t) * D + c];
+  for (; i < nblk; ++i) s8[0] += part[((long)i * 10 + t) * D + c];
+  float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   if (t < 9)
     dw[c * 9 + t] = s;
   else if (dbias)
     dbias[c] = s;
+}
+
+// ------------------------------------------------------------ LDS-tiled conv
+// One block: an 8 x 8 tile of current-grid positions x one 128-byte channel slab.  The
+// 10 x 10 halo tile arrives through global->LDS DMA (one round trip); positions outside the
+// grid are zero-filled.  Used when the slab divides the channel count.
+constexpr int kTile = 8, kHalo = kTile + 2, kSlabBytes = 128;
+
+template <typename T, bool GATHER>
+__device__ __forceinline__ void load_halo(T* tile, const T* x, long bL, int D, int c0, int i0,
+                                          int j0, int rows, int cols, int gh, int gw, long L,
+                                          int layout, int out_layout, int wave, int lane) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = kSlabBytes / 16;  // 16-byte pieces per position
+  constexpr int NP = kHalo * kHalo * NG;
+  unsigned char* tb = reinterpret_cast<unsigned char*>(tile);
+  for (int base = wave * 64; base < NP; base += 4 * 64) {
+    const int e = base + lane;
+    if (e < NP) {
+      const int pos = e / NG, k = e - pos * NG;
+      const int hi = pos / kHalo, hj = pos - hi * kHalo;
+      const int ii = i0 - 1 + hi, jj = j0 - 1 + hj;
+      if (ii >= 0 && ii < rows && jj >= 0 && jj < cols) {
+        const long p = (long)ii * cols + jj;
+        const long row = GATHER ? scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L) : p;
+        const T* g = x + (bL + row) * D + c0 + k * VEC;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)(tb + base * 16), 16, 0, 0);
+      } else {
+        *reinterpret_cast<uint4*>(tb + (long)e * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+//   forward:  out[p'] = sum_taps w x, written at the position of p's token in out_layout;
+//   backward (dx): input is dy gathered back to the current order, taps rotated 180 degrees,
+//             output in the current order.
+template <typename T, bool BWD>
+__global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           T* __restrict__ y, int gh, int gw,
+                                                           int D, int layout, int out_layout,
+                                                           int rows, int cols, int ntr, int ntc,
+                                                           int nslab) {
+  constexpr int CS = kSlabBytes / sizeof(T);  // channels per slab
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = CS / VEC;                // = 8 pieces per position
+  __shared__ __align__(16) T tile[kHalo * kHalo * CS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int tc = blk % ntc; blk /= ntc;
+  const int tr = blk % ntr;
+  const int b = blk / ntr;
+  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
+  const long L = (long)gh * gw, bL = (long)b * L;
+
+  load_halo<T, BWD>(tile, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout, wave,
+                    lane);
+
+  const int g = tid % NG, pl = tid / NG;  // channel group, first output position
+  float wr[9][VEC], bs[VEC];
+#pragma unroll
+  for (int t = 0; t < 9; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+      wr[t][v] = w[(c0 + g * VEC + v) * 9 + (BWD ? 8 - t : t)];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) bs[v] = (!BWD && bias) ? bias[c0 + g * VEC + v] : 0.f;
+  dma_wait();
+  __syncthreads();
+
+#pragma unroll
+  for (int task = 0; task < 2; ++task) {
+    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
+    const int i = i0 + oi, j = j0 + oj;
+    if (i < rows && j < cols) {
+      float acc[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = bs[v];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          const Vec<T, VEC> xv =
+              *reinterpret_cast<const Vec<T, VEC>*>(tile + ((oi + a) * kHalo + oj + s2) * CS + g * VEC);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wr[a * 3 + s2][v], to_f(xv.v[v]), acc[v]);
+        }
+      Vec<T, VEC> o;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
+      const long p = (long)i * cols + j;
+      const long orow = BWD ? p : scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L);
+      *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c0 + g * VEC) = o;
+    }
+  }
+}
+
+// dw / dbias partial sums over a column of up to `tpb` row tiles; dy tile gathered back to
+// the current order.  part[blk][tap][D] with tap 9 = bias, blk over (b, tile column, row group).
+template <typename T>
+__global__ __launch_bounds__(256) void dwconv_dw_tiled_kernel(const T* __restrict__ x,
+                                                              const T* __restrict__ dy,
+                                                              float* __restrict__ part, int gh,
+                                                              int gw, int D, int layout,
+                                                              int out_layout, int rows, int cols,
+                                                              int ntr, int ntc, int nslab, int tpb,
+                                                              int nrg) {
+  constexpr int CS = kSlabBytes / sizeof(T);
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = CS / VEC;
+  __shared__ __align__(16) T xt[kHalo * kHalo * CS];
+  __shared__ __align__(16) T dt[kTile * kTile * CS];
+  __shared__ float red[32 * CS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int tc = blk % ntc; blk /= ntc;
+  const int rg = blk % nrg;
+  const int b = blk / nrg;
+  const int j0 = tc * kTile, c0 = slab * CS;
+  const long L = (long)gh * gw, bL = (long)b * L;
+  const int g = tid % NG, pl = tid / NG;
+
+  float acc[10][VEC];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
+
+  const int tr_end = min(ntr, (rg + 1) * tpb);
+  for (int tr = rg * tpb; tr < tr_end; ++tr) {
+    const int i0 = tr * kTile;
+    load_halo<T, false>(xt, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout, wave,
+                        lane);
+    {  // dy tile (no halo), gathered from out_layout order
+      unsigned char* db = reinterpret_cast<unsigned char*>(dt);
+      constexpr int NP = kTile * kTile * NG;
+      for (int base = wave * 64; base < NP; base += 4 * 64) {
+        const int e = base + lane;
+        const int pos = e / NG, k = e - pos * NG;
+        const int oi = pos / kTile, oj = pos - oi * kTile;
+        const int i = i0 + oi, j = j0 + oj;
+        if (i < rows && j < cols) {
+          const long p = (long)i * cols + j;
+          const long row = scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L);
+          const T* gp = dy + (bL + row) * D + c0 + k * VEC;
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)gp, (lds_ptr_t)(db + base * 16), 16, 0, 0);
+        } else {
+          *reinterpret_cast<uint4*>(db + (long)e * 16) = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    dma_wait();
+    __syncthreads();
+#pragma unroll
+    for (int task = 0; task < 2; ++task) {
+      const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
+      const Vec<T, VEC> gv = *reinterpret_cast<const Vec<T, VEC>*>(dt + q * CS + g * VEC);
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          const Vec<T, VEC> xv =
+              *reinterpret_cast<const Vec<T, VEC>*>(xt + ((oi + a) * kHalo + oj + s2) * CS + g * VEC);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+            acc[a * 3 + s2][v] = fmaf(to_f(gv.v[v]), to_f(xv.v[v]), acc[a * 3 + s2][v]);
+        }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[9][v] += to_f(gv.v[v]);
+    }
+    __syncthreads();
+  }
+
+  // fixed-order reduction over the 32 position lanes of each channel group
+  const long pblk = ((long)b * ntc + tc) * nrg + rg;
+#pragma unroll
+  for (int t = 0; t < 10; ++t) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[pl * CS + g * VEC + v] = acc[t][v];
+    __syncthreads();
+    if (tid < CS) {
+      float s2 = 0.f;
+      for (int q = 0; q < 32; ++q) s2 += red[q * CS + tid];
+      part[(pblk * 10 + t) * D + c0 + tid] = s2;
+    }
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------ planning
@@ -310,10 +507,47 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 constexpr int kConvSR = 16;
 constexpr int kDwSR = 64;
 
+// Plan of the LDS-tiled path: 8 x 8 position tiles x 128-byte channel slabs.
+struct TilePlan {
+  bool ok;
+  int rows, cols, ntr, ntc, nslab, tpb, nrg;
+  long conv_blocks, dw_blocks, dw_partials;
+};
+
+static TilePlan tile_plan(int B, int gh, int gw, int D, int elt, int layout) {
+  TilePlan t{};
+  const bool col = layout == kCol || layout == kColRev;
+  t.rows = col ? gw : gh;
+  t.cols = col ? gh : gw;
+  t.ok = ((long)D * elt) % kSlabBytes == 0;
+  if (!t.ok) return t;
+  t.nslab = (int)((long)D * elt / kSlabBytes);
+  t.ntr = (t.rows + kTile - 1) / kTile;
+  t.ntc = (t.cols + kTile - 1) / kTile;
+  t.conv_blocks = (long)B * t.ntr * t.ntc * t.nslab;
+  // dw: enough row groups to give about 1024 blocks, each walking tpb row tiles
+  const long per_rg = (long)B * t.ntc * t.nslab;
+  long want = (1024 + per_rg - 1) / per_rg;
+  if (want > t.ntr) want = t.ntr;
+  if (want < 1) want = 1;
+  t.tpb = (int)((t.ntr + want - 1) / want);
+  t.nrg = (t.ntr + t.tpb - 1) / t.tpb;
+  t.dw_blocks = per_rg * t.nrg;
+  t.dw_partials = (long)B * t.ntc * t.nrg;
+  return t;
+}
+
 template <typename T, bool BWD>
 static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int out_layout,
                                 const void* x, const float* w, const float* bias, void* y,
                                 hipStream_t st) {
+  const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
+  if (tp.ok) {
+    hipLaunchKernelGGL((dwconv_tiled_kernel<T, BWD>), dim3((unsigned)tp.conv_blocks), dim3(256),
+                       0, st, static_cast<const T*>(x), w, bias, static_cast<T*>(y), gh, gw, D,
+                       layout, out_layout, tp.rows, tp.cols, tp.ntr, tp.ntc, tp.nslab);
+    return hipGetLastError();
+  }
   const ConvPlan c = conv_plan(B, gh, gw, D, sizeof(T), layout, kConvSR, 16 / sizeof(T));
   dim3 blk(c.cgs, c.nj), grd(c.nblocks);
 #define DIG_CONV_CASE(V)                                                                       \
@@ -344,12 +578,19 @@ static ConvPlan dw_plan(int B, int gh, int gw, int D, int elt, int layout) {
   return conv_plan(B, gh, gw, D, elt, layout, kDwSR, 16 / elt);
 }
 
+// Number of [10][D] partial-sum slices the dw pass writes for one dtype and layout.
+static long dw_partials(int B, int gh, int gw, int D, int elt, int layout) {
+  const TilePlan tp = tile_plan(B, gh, gw, D, elt, layout);
+  if (tp.ok) return tp.dw_partials;
+  const ConvPlan c = dw_plan(B, gh, gw, D, elt, layout);
+  return c.nblocks / c.nchb;
+}
+
 size_t dwconv_bwd_workspace(int B, int gh, int gw, int D) {
   size_t best = 0;
   for (int elt = 2; elt <= 4; elt += 2)
     for (int lay = 0; lay < 4; lay += 2) {
-      const ConvPlan c = dw_plan(B, gh, gw, D, elt, lay);
-      const size_t b = (size_t)(c.nblocks / c.nchb) * 10 * D * sizeof(float);
+      const size_t b = (size_t)dw_partials(B, gh, gw, D, elt, lay) * 10 * D * sizeof(float);
       if (b > best) best = b;
     }
   return best;
@@ -359,6 +600,17 @@ template <typename T>
 static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_layout,
                               const void* x, const void* dy, float* dw, float* dbias,
                               float* part, hipStream_t st) {
+  const long n = 10L * D;
+  const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
+  if (tp.ok) {
+    hipLaunchKernelGGL((dwconv_dw_tiled_kernel<T>), dim3((unsigned)tp.dw_blocks), dim3(256), 0, st,
+                       static_cast<const T*>(x), static_cast<const T*>(dy), part, gh, gw, D,
+                       layout, out_layout, tp.rows, tp.cols, tp.ntr, tp.ntc, tp.nslab, tp.tpb,
+                       tp.nrg);
+    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       part, (int)tp.dw_partials, D, dw, dbias);
+    return hipGetLastError();
+  }
   const ConvPlan c = dw_plan(B, gh, gw, D, sizeof(T), layout);
   dim3 blk(c.cgs, c.nj), grd(c.nblocks);
   const size_t shm = (size_t)c.nj * c.cgs * c.VW * sizeof(float);
@@ -376,7 +628,6 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
     default: return hipErrorInvalidValue;
   }
 #undef DIG_DW_CASE
-  const long n = 10L * D;
   hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
                      c.nblocks / c.nchb, D, dw, dbias);
   return hipGetLastError();
