@@ -46,12 +46,16 @@ struct GlaFwdParams {
   float g2scale;   // log2(e) / tau
   float q_scale, eps;
   int write_states;
+  unsigned* done_counter;  // backward's workgroup counter inside `saved`: zeroed here, or null
   GlaLds lds;
 };
 
 GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks);
 GlaLds gla_fwd_lds(const GlaShape& s, bool out_pass);
 size_t gla_states_bytes(const GlaShape& s);
+// `saved` = chunk-entry states, then (at a 256-byte boundary) one counter word.
+size_t gla_saved_bytes(const GlaShape& s);
+size_t gla_counter_offset(const GlaShape& s);
 size_t gla_seglg_bytes(const GlaShape& s);
 
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
@@ -83,6 +87,7 @@ struct GlaBwdParams {
   float* gstates;       // [B*H][nseg][dk][dv] gradient entering each segment's end
   float* seg_lg;        // [B*H][nseg][dk]
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
+  unsigned* done_counter;  // finished final-pass workgroups (in `saved`; 0 between calls)
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
   GlaBwdLds lds;

@@ -100,6 +100,8 @@ GlaLds gla_fwd_lds(const GlaShape& s, bool out) {
 size_t gla_states_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.NC * s.dk * s.dv * sizeof(float);
 }
+size_t gla_counter_offset(const GlaShape& s) { return (gla_states_bytes(s) + 255) / 256 * 256; }
+size_t gla_saved_bytes(const GlaShape& s) { return gla_counter_offset(s) + 256; }
 size_t gla_seglg_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.nseg * s.dk * sizeof(float);
 }
@@ -143,6 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_fwd_kernel(GlaFwdParams p) {
 
   for (int i = tid; i < Ld.bytes / 16; i += kThreads)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  if (OUT && p.done_counter && blockIdx.x == 0 && tid == 0) *p.done_counter = 0u;
   __syncthreads();
 
   const int c_first = seg * p.sc;
