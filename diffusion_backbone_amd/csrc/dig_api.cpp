@@ -92,7 +92,7 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
     return fail(DIG_ERR_UNSUPPORTED, "batch * heads too large");
   *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, d->chunk,
                      d->dtype == DIG_BF16, d->seg_chunks);
-  const int lds = pass == kFwd ? dig::gla_fwd_lds(*s, true).bytes : dig::gla_bwd_lds(*s, true).bytes;
+  const int lds = pass == kFwd ? dig::gla_fwd_lds_bytes(*s) : dig::gla_bwd_lds(*s, true).bytes;
   if (lds > kLdsLimit)
     return fail(DIG_ERR_UNSUPPORTED, "%s needs %d bytes of LDS for this shape (limit %d)",
                 pass == kFwd ? "forward" : "backward", lds, kLdsLimit);
@@ -139,12 +139,12 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 101; }
+int32_t dig_abi_version(void) { return 100; }
 
 size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;
   if (check_desc(d, &s, kFwd) != DIG_OK) return 0;
-  return dig::gla_saved_bytes(s);
+  return dig::gla_states_bytes(s);
 }
 
 size_t dig_gla_fwd_workspace_bytes(const dig_gla_desc* d) {
@@ -185,7 +185,7 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
                       rng("gate_logit", gate_logit, bk), rng("r", r, bv),
                       rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0)};
   const Range out[] = {rng("y", y, bv), rng("o_pre", o_pre_opt, o_pre_opt ? bv : 0),
-                       rng("saved", saved_opt, saved_opt ? dig::gla_saved_bytes(s) : 0),
+                       rng("saved", saved_opt, saved_opt ? sb : 0),
                        rng("workspace", workspace, workspace ? need : 0)};
   st = check_alias(in, 6, out, 4);
   if (st != DIG_OK) return st;
@@ -197,9 +197,6 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
   p.states = saved_opt ? static_cast<float*>(saved_opt) : reinterpret_cast<float*>(ws);
   p.seg_lg = reinterpret_cast<float*>(ws + a256(sb));
   p.write_states = saved_opt != nullptr;
-  p.done_counter = saved_opt ? reinterpret_cast<unsigned*>(static_cast<char*>(saved_opt) +
-                                                           dig::gla_counter_offset(s))
-                             : nullptr;
   p.g2scale = 1.4426950408889634f / d->tau;
   p.q_scale = d->q_scale;
   p.eps = d->norm_eps;
@@ -208,7 +205,7 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
 
 dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
                        const void* gate_logit, const void* r, const float* norm_w,
-                       const void* dy, void* saved, void* dq, void* dk, void* dv,
+                       const void* dy, const void* saved, void* dq, void* dk, void* dv,
                        void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
   dig::GlaShape s;
@@ -239,7 +236,7 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
                       rng("gate_logit", gate_logit, bk), rng("r", r, bv),
                       rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0), rng("dy", dy, bv),
-                      rng("saved", saved, dig::gla_saved_bytes(s))};
+                      rng("saved", saved, dig::gla_states_bytes(s))};
   const Range out[] = {rng("dq", dq, bk), rng("dk", dk, bk), rng("dv", dv, bv),
                        rng("d_gate_logit", d_gate_logit, bk), rng("dr", dr, bv),
                        rng("d_norm_w", d_norm_w, d_norm_w ? d->d_v * 4 : 0),
@@ -252,8 +249,6 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   dig::GlaBwdParams p{};
   p.q = q; p.k = k; p.v = v; p.z = gate_logit; p.r = r; p.norm_w = norm_w; p.dy = dy;
   p.states = static_cast<const float*>(saved);
-  p.done_counter =
-      reinterpret_cast<unsigned*>(static_cast<char*>(saved) + dig::gla_counter_offset(s));
   p.dq = dq; p.dk_ = dk; p.dv_ = dv; p.dz = d_gate_logit; p.dr = dr; p.d_norm_w = d_norm_w;
   p.gstates = reinterpret_cast<float*>(ws);
   size_t off = a256(BH * s.nseg * s.dk * s.dv * sizeof(float));

@@ -160,6 +160,154 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// ---------------------------------------------------- DPP (register-only) lane ops
+// gfx9 data-parallel primitives: row_shr:k = 0x110+k, row_ror:k = 0x120+k, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143 (a "row" is 16 lanes).  Lanes whose source is outside the row,
+// or whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum over groups of W consecutive lanes (W = 16, 32 or 64).
+template <int W>
+__device__ __forceinline__ float scan_dpp(float x) {
+  static_assert(W == 16 || W == 32 || W == 64, "scan width");
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  if constexpr (W >= 32) x += dpp_f<0x142, 0xa>(x);  // row r-1's last lane into rows 1, 3
+  if constexpr (W == 64) x += dpp_f<0x143, 0xc>(x);  // lane 31 into rows 2, 3
+  return x;
+}
+
+// Sum over the 16 lanes of this lane's row, returned in every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x122>(x);
+  x += dpp_f<0x121>(x);
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Value held by the last lane of this lane's group of W consecutive lanes.
+template <int W>
+__device__ __forceinline__ float group_last(float x, int lane) {
+  if constexpr (W == 64) {
+    return readlane_f(x, 63);
+  } else {
+    float r = 0.f;
+#pragma unroll
+    for (int g = 0; g < 64 / W; ++g) {
+      const float v = readlane_f(x, g * W + W - 1);
+      if (lane / W == g) r = v;
+    }
+    return r;
+  }
+}
+
+// Maximum over the whole wave (uniform result).
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x122>(x));
+  x = fmaxf(x, dpp_f<0x121>(x));
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+
+// N consecutive elements c0..c0+N-1 of a packed LDS row with `cols` elements; columns past
+// the row end, and every column of an invalid row, read as zero.  Whole 16- or 8-byte
+// vectors when the row pitch and the range allow it.
+template <typename T, int N>
+__device__ __forceinline__ void lds_row_read(T (&out)[N], const T* row, int c0, int cols,
+                                             bool valid) {
+  constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T);
+  const int pitch = cols * (int)sizeof(T);
+  if (N % V16 == 0 && (pitch & 15) == 0 && c0 + N <= cols) {
+#pragma unroll
+    for (int j = 0; j < N; j += V16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + c0 + j);
+      const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int i = 0; i < V16; ++i) out[j + i] = e[i];
+    }
+  } else if (N % V8 == 0 && (pitch & 7) == 0 && c0 + N <= cols) {
+#pragma unroll
+    for (int j = 0; j < N; j += V8) {
+      const uint2 u = *reinterpret_cast<const uint2*>(row + c0 + j);
+      const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int i = 0; i < V8; ++i) out[j + i] = e[i];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = (c0 + j < cols) ? row[c0 + j] : from_f<T>(0.f);
+  }
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = from_f<T>(0.f);
+  }
+}
+
+// Same with the row width known at compile time and the range inside the row (c0 + N <=
+// COLS, c0 a multiple of N): whole 16-byte vectors whenever the widths allow.
+template <typename T, int N, int COLS>
+__device__ __forceinline__ void lds_row_read_k(T (&out)[N], const T* row, int c0, bool valid) {
+  constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T);
+  constexpr int PB = COLS * (int)sizeof(T), NB = N * (int)sizeof(T);
+  if constexpr (PB % 16 == 0 && NB % 16 == 0) {
+#pragma unroll
+    for (int j = 0; j < N; j += V16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + c0 + j);
+      const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int i = 0; i < V16; ++i) out[j + i] = e[i];
+    }
+  } else if constexpr (PB % 8 == 0 && NB % 8 == 0) {
+#pragma unroll
+    for (int j = 0; j < N; j += V8) {
+      const uint2 u = *reinterpret_cast<const uint2*>(row + c0 + j);
+      const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int i = 0; i < V8; ++i) out[j + i] = e[i];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = row[c0 + j];
+  }
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = from_f<T>(0.f);
+  }
+}
+
+// Store N consecutive elements to an LDS row at element offset c0 (16-byte vectors when
+// the byte offset is 16-aligned and N fills whole vectors).
+template <typename T, int N>
+__device__ __forceinline__ void lds_row_write(T* row, int c0, const T (&in)[N]) {
+  constexpr int V16 = 16 / (int)sizeof(T);
+  if constexpr (N % V16 == 0) {
+    if (((reinterpret_cast<uintptr_t>(row + c0)) & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < N; j += V16) {
+        uint4 u;
+        T* e = reinterpret_cast<T*>(&u);
+#pragma unroll
+        for (int i = 0; i < V16; ++i) e[i] = in[j + i];
+        *reinterpret_cast<uint4*>(row + c0 + j) = u;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) row[c0 + j] = in[j];
+}
+
 // ------------------------------------------------------------ tile staging
 // Copy rows [0, rows) of a token-major tile (row r at gsrc + r*gstride elements, `cols`
 // elements each) into LDS dst (row pitch ld elements).  Rows >= valid are zero-filled.
@@ -295,6 +443,32 @@ __device__ __forceinline__ void dma_rows(const DmaMap& m, T* lds_dst, const T* g
   }
 }
 
+// Compact form of dma_rows (one loop for every row width; small code): rows [0, valid) of
+// `rowbytes` bytes each, row r at gsrc + r*gstride_bytes, into packed LDS rows at lds_dst.
+// Piece size 16, 4 or 2 bytes: the largest dividing the row.  Waves [0, nwaves) share the
+// pieces; lane i of an instruction writes LDS at (instruction base) + i*piece.
+__device__ __forceinline__ void dma_rows_c(unsigned char* lds_dst, const unsigned char* gsrc,
+                                           long gstride_bytes, int rowbytes, int valid,
+                                           int wave, int nwaves, int lane) {
+  const int lg = (rowbytes & 15) == 0 ? 4 : ((rowbytes & 3) == 0 ? 2 : 1);
+  const int ppr = rowbytes >> lg;
+  const int npieces = valid * ppr;
+  for (int base = wave * 64; base < npieces; base += nwaves * 64) {
+    const int e = base + lane;
+    if (e < npieces) {
+      const int r = e / ppr, c = e - r * ppr;
+      gbl_ptr_t g = (gbl_ptr_t)(gsrc + (long)r * gstride_bytes + (c << lg));
+      lds_ptr_t l = (lds_ptr_t)(lds_dst + (base << lg));
+      if (lg == 4)
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      else if (lg == 2)
+        __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(g, l, 2, 0, 0);
+    }
+  }
+}
+
 // Starts an asynchronous copy of rows [0, valid) of a token-major tile (row r at gsrc + r *
 // gstride elements, `cols` elements per row) into LDS as packed rows (pitch = cols).  The
 // caller waits with dma_wait() + a barrier, and zero-fills rows >= valid itself.
@@ -315,6 +489,18 @@ __device__ __forceinline__ void dma_tile(T* lds_dst, const T* gsrc, long gstride
 
 // Waits for this wave's outstanding memory operations (LDS DMA included).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt = 0; s_waitcnt encoding 0xC07F leaves vmcnt/expcnt unconstrained) and keeps the
+// compiler from moving memory accesses across it.  Unlike __syncthreads() it does not wait
+// for this wave's global->LDS copies still in flight, so a wave that prefetches can pass it.
+// Callers must not rely on it for LDS written by such copies.
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Zero rows [valid, rows) of a packed LDS tile.
 template <typename T>

@@ -22,14 +22,6 @@ struct GlaShape {
 // Head-dim classes the kernels are compiled for (16-wide tiles of d_k and d_v).
 bool gla_dim_class(int dk, int dv, int* ndk, int* ndv);
 
-// LDS carve-up of the chunk kernels (byte offsets; 0-sized arrays are unused).
-struct GlaLds {
-  int DKP, DK16, DV16, DVP, CK;
-  int off_q, off_k, off_kbt, off_vt, off_s, off_b, off_raw, off_rv, off_r, off_gam, off_qk,
-      off_misc;
-  int bytes;
-};
-
 struct GlaFwdParams {
   int C, prefix;
   const void* q;
@@ -46,19 +38,18 @@ struct GlaFwdParams {
   float g2scale;   // log2(e) / tau
   float q_scale, eps;
   int write_states;
-  unsigned* done_counter;  // backward's workgroup counter inside `saved`: zeroed here, or null
-  GlaLds lds;
 };
 
 GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks);
-GlaLds gla_fwd_lds(const GlaShape& s, bool out_pass);
+// LDS bytes of the forward's output pass for this shape (0 if no kernel exists for it).
+int gla_fwd_lds_bytes(const GlaShape& s);
 size_t gla_states_bytes(const GlaShape& s);
-// `saved` = chunk-entry states, then (at a 256-byte boundary) one counter word.
-size_t gla_saved_bytes(const GlaShape& s);
-size_t gla_counter_offset(const GlaShape& s);
 size_t gla_seglg_bytes(const GlaShape& s);
 
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
+// Pass B of the three-pass forward: exclusive scan of segment states.
+hipError_t launch_gla_state_scan(const GlaShape& s, float* states, const float* seg_lg,
+                                 hipStream_t st);
 
 // ----------------------------------------------------------------- GLA backward
 struct GlaBwdLds {
@@ -87,7 +78,6 @@ struct GlaBwdParams {
   float* gstates;       // [B*H][nseg][dk][dv] gradient entering each segment's end
   float* seg_lg;        // [B*H][nseg][dk]
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
-  unsigned* done_counter;  // finished final-pass workgroups (in `saved`; 0 between calls)
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
   GlaBwdLds lds;

@@ -614,42 +614,9 @@ __global__ __launch_bounds__(kBThreads) void gla_bwd_kernel(GlaBwdParams p) {
       if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
     }
     __syncthreads();
-    if (p.d_norm_w) {
-      // Publish this workgroup's partial; the last workgroup to finish sums all partials in
-      // a fixed order (agent-scope atomics and fences: partials come from every XCD).
-      for (int e = tid; e < dv; e += kBThreads)
-        __hip_atomic_store(p.dgamma_part + (long)blockIdx.x * dv + e,
-                           ((sDg[e] + sDg[DVP + e]) + sDg[2 * DVP + e]) + sDg[3 * DVP + e],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
-      __syncthreads();
-      int* sLast = reinterpret_cast<int*>(sMax);
-      if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(p.done_counter, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        sLast[0] = prev == gridDim.x - 1;
-      }
-      __syncthreads();
-      if (sLast[0]) {
-        __threadfence();
-        const int nparts = (int)gridDim.x;
-        for (int e = tid; e < dv; e += kBThreads) {
-          float acc[4] = {0.f, 0.f, 0.f, 0.f};
-          int i = 0;
-          for (; i + 4 <= nparts; i += 4)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              acc[u] += __hip_atomic_load(p.dgamma_part + (long)(i + u) * dv + e,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          for (; i < nparts; ++i)
-            acc[0] += __hip_atomic_load(p.dgamma_part + (long)i * dv + e, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-          p.d_norm_w[e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        }
-        if (tid == 0)
-          __hip_atomic_store(p.done_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    for (int e = tid; e < dv; e += kBThreads)
+      p.dgamma_part[(long)blockIdx.x * dv + e] =
+          ((sDg[e] + sDg[DVP + e]) + sDg[2 * DVP + e]) + sDg[3 * DVP + e];
   } else {
     float* dst = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
 #pragma unroll
@@ -689,6 +656,23 @@ __global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const f
   base[0] = G;
 }
 
+// out[e] = sum over parts of part[i][e]: one block per column e, a fixed-order tree (the
+// same bits on every run).
+__global__ __launch_bounds__(kBThreads) void gla_dgamma_reduce(const float* part, int nparts,
+                                                              int dv, float* out) {
+  __shared__ float red[kBThreads];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float s = 0.f;
+  for (int i = tid; i < nparts; i += kBThreads) s += part[(long)i * dv + e];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = kBThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) out[e] = red[0];
+}
+
 template <typename T, int NDK, int NDV>
 static hipError_t launch_bt(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   const long BH = (long)s.B * s.H;
@@ -704,6 +688,9 @@ static hipError_t launch_bt(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.lds = gla_bwd_lds(s, true);
   hipLaunchKernelGGL((gla_bwd_kernel<T, NDK, NDV, true>), dim3((unsigned)(BH * s.nseg)),
                      dim3(kBThreads), p.lds.bytes, st, p);
+  if (p.d_norm_w)
+    hipLaunchKernelGGL(gla_dgamma_reduce, dim3(s.dv), dim3(kBThreads), 0, st, p.dgamma_part,
+                       (int)(BH * s.nseg), s.dv, p.d_norm_w);
   return hipGetLastError();
 }
 

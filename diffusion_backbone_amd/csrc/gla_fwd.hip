@@ -1,36 +1,20 @@
-// gla_fwd.hip -- chunkwise forward of DiG's gated linear attention on gfx950.
-//
-// What is computed (DiG study-group slides, eqs. (5)-(10); write-up section 3,
-// "Efficiency Analysis": chunks of M tokens computed on-chip), per image b and head h:
-//   g_t = logsigmoid(z_t)/tau,  S_t = diag(exp g_t) S_{t-1} + k_t^T v_t,  o_t = q_t S_t,
-//   y_t = RMSNorm_head(o_t) * w * Swish(r_t).
-// Chunk form, with b_i = sum of g over the chunk up to token i (inclusive) and S0 the state
-// entering the chunk:
-//   o_i = sum_{j<=i} [sum_c q_ic e^{b_ic} k_jc e^{-b_jc}] v_j + (q_i e^{b_i}) S0
-//   S_next = diag(e^{b_last}) S0 + sum_j (k_j e^{b_last - b_j})^T v_j
-// The bracket (the gated Q K^T of the chunk) and both products with V/S run on matrix cores
-// (bf16 16x16x32 or fp32 16x16x4, fp32 accumulation).  Gates live in log2 space in fp32.
-// When a chunk's total decay is so strong that k e^{-b} could overflow, that chunk's gated
-// Q K^T is evaluated elementwise as sum_c q_ic k_jc exp(b_ic - b_jc) instead.
+// gla_fwd.hip -- host side of the GLA forward: launch planning (segments, LDS layout), the
+// cross-segment state scan (pass B), and dispatch to the chunk kernels compiled per element
+// type in gla_fwd_bf16.hip / gla_fwd_f32.hip (kernel in gla_fwd_kernel.h).
 //
 // The sequence is cut into segments of `sc` chunks, one workgroup per (image, head,
 // segment).  A segment's incoming state comes either
 //   - from recomputing the state over all earlier chunks inside the same workgroup
 //     (short sequences: one launch), or
-//   - from three passes: pass A (gla_fwd_kernel<OUT=false>) carries each segment's local
+//   - from three passes: pass A (chunk kernel, OUT=false) carries each segment's local
 //     state from zero and records it with the segment's log2 decay; pass B
 //     (gla_state_scan) scans those per state element; pass C (OUT=true) emits outputs.
 // Head dims are compiled in 16-wide tile classes (NDK x NDV tiles); smaller dims are padded
 // with zeros inside LDS, which leaves every product unchanged.
-#include <type_traits>
-
 #include "dig_device.h"
 #include "dig_internal.h"
 
 namespace dig {
-
-constexpr int kThreads = 256;
-constexpr float kSlowDecayLog2 = 96.0f;  // e^{-b} factors up to 2^96 stay finite in bf16/fp32
 
 static int rup(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -67,403 +51,21 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   return s;
 }
 
-// LDS carve-up.  Matrix-core operands are stored with rows padded by 8 elements so that the
-// 16 rows a fragment load touches fall on different banks.
-GlaLds gla_fwd_lds(const GlaShape& s, bool out) {
-  GlaLds l;
-  const int T = s.bf16 ? 2 : 4;
-  l.DKP = rup(16 * s.ndk, 32);
-  l.DK16 = s.ndk;
-  l.DV16 = s.ndv;
-  l.DVP = 16 * s.ndv;
-  l.CK = s.bf16 ? rup(s.C, 32) : s.C;
-  const int QP = l.DKP + 8, TP = l.CK + 8;
-  const int cpad = s.ndk <= 2 ? 32 : 64;
-  int off = 0;
-  auto take = [&](int bytes) { int o = off; off += rup(bytes, 16); return o; };
-  l.off_q = take(out ? s.C * QP * T : 0);            // q e^{b}            [C][QP]
-  l.off_k = take(out ? s.C * QP * T : 0);            // k e^{-b}           [C][QP]
-  l.off_kbt = take(16 * s.ndk * TP * T);             // (k e^{blast-b})^T  [16 NDK][TP]
-  l.off_vt = take(l.DVP * TP * T);                   // v^T                [DVP][TP]
-  l.off_s = take(out ? l.DVP * QP * T : 0);          // S^T (bf16 copy)    [DVP][QP]
-  l.off_b = take(s.C * s.dk * 4);                    // log2 cumsum        [C][dk] fp32
-  l.off_raw = take(3 * s.C * s.dk * T);              // raw q, k, z (packed rows, LDS DMA)
-  l.off_rv = take(s.C * s.dv * T);                   // raw v
-  l.off_r = take(out ? s.C * s.dv * T : 0);          // raw r, then y
-  l.off_gam = take(l.DKP * 4);                       // e^{b_last}
-  l.off_qk = take((256 / cpad) * cpad * 4);          // per-segment gate sums [seg][col]
-  l.off_misc = take(l.DKP * 4 + 16 * 4);
-  l.bytes = off;
-  return l;
-}
-
 size_t gla_states_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.NC * s.dk * s.dv * sizeof(float);
 }
-size_t gla_counter_offset(const GlaShape& s) { return (gla_states_bytes(s) + 255) / 256 * 256; }
-size_t gla_saved_bytes(const GlaShape& s) { return gla_counter_offset(s) + 256; }
 size_t gla_seglg_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.nseg * s.dk * sizeof(float);
 }
 
-template <typename T, int NDK, int NDV, bool OUT>
-__global__ __launch_bounds__(kThreads, 2) void gla_fwd_kernel(GlaFwdParams p) {
-  constexpr int DKP = ((NDK * 16 + 31) / 32) * 32;
-  constexpr int DVP = NDV * 16;
-  constexpr int QP = DKP + 8;                   // row pitch of sQ, sK, sS
-  constexpr int NST = NDK * NDV;                // state tiles
-  constexpr int STW = (NST + 3) / 4;            // state tiles per wave
-  constexpr int CPAD = NDK <= 2 ? 32 : 64;      // gate pass: lanes over key columns
-  constexpr int NSEGT = kThreads / CPAD;        // ... and token segments
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int C = p.C, NT = C >> 4;
-  const int nseg_launch = OUT ? p.nseg : p.nseg - 1;
-  const int seg = blockIdx.x % nseg_launch;
-  const int bh = blockIdx.x / nseg_launch;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int H = p.H, dk = p.dk, dv = p.dv;
-  const GlaLds& Ld = p.lds;
-  const int CK = Ld.CK, TP = CK + 8;  // row pitch of the token-indexed transposes
-
-  T* sQ = reinterpret_cast<T*>(smem + Ld.off_q);
-  T* sK = reinterpret_cast<T*>(smem + Ld.off_k);
-  T* sKbT = reinterpret_cast<T*>(smem + Ld.off_kbt);
-  T* sVt = reinterpret_cast<T*>(smem + Ld.off_vt);
-  T* sS = reinterpret_cast<T*>(smem + Ld.off_s);
-  float* sB = reinterpret_cast<float*>(smem + Ld.off_b);
-  T* rawq = reinterpret_cast<T*>(smem + Ld.off_raw);
-  T* rawk = rawq + C * dk;
-  T* rawz = rawk + C * dk;
-  T* rawv = reinterpret_cast<T*>(smem + Ld.off_rv);
-  T* sR = reinterpret_cast<T*>(smem + Ld.off_r);
-  float* sGam = reinterpret_cast<float*>(smem + Ld.off_gam);
-  float* sTot = reinterpret_cast<float*>(smem + Ld.off_qk);
-  float* sLg = reinterpret_cast<float*>(smem + Ld.off_misc);
-  float* sMax = sLg + DKP;
-
-  for (int i = tid; i < Ld.bytes / 16; i += kThreads)
-    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
-  if (OUT && p.done_counter && blockIdx.x == 0 && tid == 0) *p.done_counter = 0u;
-  __syncthreads();
-
-  const int c_first = seg * p.sc;
-  const int c_end = min(p.NC, c_first + p.sc);
-  const int n_begin = (OUT && p.prefix) ? 0 : c_first;
-  const bool scanned = !p.prefix && p.nseg > 1;  // incoming state comes from pass B
-  const long sbase = (long)bh * p.NC;             // chunk-slot base for this (b,h)
-  const DmaMap mk = dma_map<T>(dk, lane), mv = dma_map<T>(dv, lane);
-  // gate pass mapping: column gc over token segment gs of length TL
-  const int gc = tid % CPAD, gs = tid / CPAD, TL = C / NSEGT;
-  const float inv_tau = p.g2scale * 0.69314718055994531f;  // g2scale = log2(e) / tau
-
-  f32x4 sacc[STW];
-#pragma unroll
-  for (int m = 0; m < STW; ++m) sacc[m] = zero4();
-
-  if (OUT && scanned && seg > 0) {
-    const float* src = p.states + (sbase + c_first) * dk * dv;
-#pragma unroll
-    for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
-        const int ct = u / NDV, et = u - ct * NDV;
-        const int e = et * 16 + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = ct * 16 + g4 * 4 + i;
-          const float val = (c < dk && e < dv) ? src[c * dv + e] : 0.f;
-          sacc[m][i] = val;
-          sS[e * QP + c] = from_f<T>(val);
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  const T* gq = static_cast<const T*>(p.q);
-  const T* gk = static_cast<const T*>(p.k);
-  const T* gv = static_cast<const T*>(p.v);
-  const T* gz = static_cast<const T*>(p.z);
-  const T* gr = static_cast<const T*>(p.r);
-  T* gy = static_cast<T*>(p.y);
-  T* gop = static_cast<T*>(p.o_pre);
-
-  float gm[NDV];  // norm weight of the output column this lane touches in tile E
-#pragma unroll
-  for (int E = 0; E < NDV; ++E) {
-    const int e = E * 16 + r16;
-    gm[E] = (OUT && e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
-  }
-
-  for (int n = n_begin; n < c_end; ++n) {
-    const bool emit = OUT && n >= c_first;
-    const int t0 = n * C;
-    const int valid = min(C, p.L - t0);
-    const long row0 = ((long)b * p.L + t0) * H + h;  // (b, t0, h) as a token-head row
-
-    // ---- stage the chunk's raw operands: asynchronous global->LDS copies, one round trip
-    if (emit) dma_rows<T>(mk, rawq, gq + row0 * dk, (long)H * dk, valid, wave, 4, lane);
-    dma_rows<T>(mk, rawk, gk + row0 * dk, (long)H * dk, valid, wave, 4, lane);
-    dma_rows<T>(mk, rawz, gz + row0 * dk, (long)H * dk, valid, wave, 4, lane);
-    dma_rows<T>(mv, rawv, gv + row0 * dv, (long)H * dv, valid, wave, 4, lane);
-    if (emit) dma_rows<T>(mv, sR, gr + row0 * dv, (long)H * dv, valid, wave, 4, lane);
-
-    if (emit && p.write_states && !(scanned && n == c_first)) {
-      float* dst = p.states + (sbase + n) * dk * dv;
-#pragma unroll
-      for (int m = 0; m < STW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NST) {
-          const int ct = u / NDV, et = u - ct * NDV;
-          const int e = et * 16 + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = ct * 16 + g4 * 4 + i;
-            if (c < dk && e < dv) dst[c * dv + e] = sacc[m][i];
-          }
-        }
-      }
-    }
-    dma_wait();
-    __syncthreads();
-    if (valid < C) {  // ragged last chunk: rows past the sequence are zero
-      zero_rows<T>(rawq, valid, C, dk, tid, kThreads);
-      zero_rows<T>(rawk, valid, C, dk, tid, kThreads);
-      zero_rows<T>(rawz, valid, C, dk, tid, kThreads);
-      zero_rows<T>(rawv, valid, C, dv, tid, kThreads);
-      if (emit) zero_rows<T>(sR, valid, C, dv, tid, kThreads);
-      __syncthreads();
-    }
-
-    // ---- gate, pass 1: g = log2(sigmoid(z))/tau per element and its running sum along each
-    // column's token segment (lanes run over key columns: conflict-free LDS rows); V^T
-    {
-      float run = 0.f;
-      if (gc < dk) {
-        for (int j = 0; j < TL; ++j) {
-          const int t = gs * TL + j;
-          const float g2 = t < valid ? Fm<T>::lsig2(to_f(rawz[t * dk + gc])) * inv_tau : 0.f;
-          run += g2;
-          sB[t * dk + gc] = run;
-        }
-      }
-      sTot[gs * CPAD + gc] = run;
-      for (int i = tid; i < C * DVP; i += kThreads) {
-        const int e = i % DVP, t = i / DVP;
-        if (e < dv) sVt[e * TP + t] = rawv[t * dv + e];
-      }
-    }
-    __syncthreads();
-
-    // ---- gate, pass 2: segment offsets complete the inclusive cumsum b; scaled operands
-    {
-      float off = 0.f, blast = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < NSEGT; ++s2) {
-        const float tv = sTot[s2 * CPAD + gc];
-        if (s2 < gs) off += tv;
-        blast += tv;
-      }
-      if (gc < dk) {
-        for (int j = 0; j < TL; ++j) {
-          const int t = gs * TL + j;
-          const float bb = sB[t * dk + gc] + off;
-          const float kf = to_f(rawk[t * dk + gc]);
-          sKbT[gc * TP + t] = from_f<T>(kf * Fm<T>::exp2(blast - bb));
-          if (emit) {
-            const float qf = to_f(rawq[t * dk + gc]) * p.q_scale;
-            sQ[t * QP + gc] = from_f<T>(qf * Fm<T>::exp2(bb));
-            sK[t * QP + gc] = from_f<T>(kf * Fm<T>::exp2(-bb));
-            sB[t * dk + gc] = bb;
-          }
-        }
-        if (gs == 0) {
-          sGam[gc] = Fm<T>::exp2(blast);
-          if (!OUT) sLg[gc] += blast;
-        }
-      }
-      if (emit && wave == 0) {  // wave 0 holds segment 0 of every column
-        const float md = wave_max((gs == 0 && gc < dk) ? -blast : 0.f);
-        if (lane == 0) sMax[0] = md;
-      }
-    }
-    __syncthreads();
-
-    if (emit && wave < NT) {
-      const int I = wave;  // this wave's 16 query rows
-      const bool slow = sMax[0] > kSlowDecayLog2;
-      // exact diagonal q_i.k_i (gate factor 1) in fp32 from the unscaled inputs, so that a
-      // cancelling dot product keeps its relative accuracy: 16 rows x 4 column groups
-      float diag;
-      {
-        const int ir = 16 * I + r16, cq = (dk + 3) >> 2;
-        // fp32 I/O accumulates in fp64: the sum can cancel far below its terms
-        using Acc = typename std::conditional<sizeof(T) == 4, double, float>::type;
-        Acc acc = 0;
-        for (int c = g4 * cq; c < min(dk, g4 * cq + cq); ++c)
-          acc += (Acc)to_f(rawq[ir * dk + c]) * (Acc)to_f(rawk[ir * dk + c]);
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
-        diag = (float)acc * p.q_scale;
-      }
-      // P^T tiles: pt[J][i] = P[16I + r16][16J + 4*g4 + i]
-      f32x4 pt[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        pt[J] = zero4();
-        if (J <= I) {
-          if (!slow) {
-            pt[J] = Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane);
-          } else {
-            const int ir = 16 * I + r16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = 16 * J + 4 * g4 + i;
-              float acc = 0.f;
-              if (j <= ir) {
-                for (int c = 0; c < dk; ++c)
-                  acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
-                         Fm<T>::exp2(sB[ir * dk + c] - sB[j * dk + c]);
-                acc *= p.q_scale;
-              }
-              pt[J][i] = acc;
-            }
-          }
-          if (J == I) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (4 * g4 + i > r16) pt[J][i] = 0.f;
-              if (4 * g4 + i == r16) pt[J][i] = diag;
-            }
-          }
-        }
-      }
-
-      f32x4 oacc[NDV];
-#pragma unroll
-      for (int E = 0; E < NDV; ++E) oacc[E] = zero4();
-
-      // intra-chunk: O += P V   (P straight from the accumulators above)
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          if (2 * pp <= I) {
-            const bool hi_on = 2 * pp + 1 <= I;
-            bf16x8 a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              a[i] = from_f<bf16>(pt[2 * pp][i]);
-              a[4 + i] = from_f<bf16>(hi_on ? pt[2 * pp + 1][i] : 0.f);
-            }
-#pragma unroll
-            for (int E = 0; E < NDV; ++E) {
-              const T* vb = sVt + (E * 16 + r16) * TP + 32 * pp + 4 * g4;
-              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vb);
-              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vb + 16);
-              bf16x8 bv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) { bv[i] = lo[i]; bv[4 + i] = hi[i]; }
-              oacc[E] = mfma_bf16(a, bv, oacc[E]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          if (J <= I) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-              for (int E = 0; E < NDV; ++E) {
-                const float bv = to_f(sVt[(E * 16 + r16) * TP + 16 * J + 4 * g4 + s4]);
-                oacc[E] = mfma_f32(pt[J][s4], bv, oacc[E]);
-              }
-            }
-          }
-        }
-      }
-      // inter-chunk: O += (q e^{b}) S0
-#pragma unroll
-      for (int E = 0; E < NDV; ++E)
-        oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
-
-      // output stage: head-wise RMSNorm x weight x Swish(r); y staged over r in LDS
-      float ss[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int E = 0; E < NDV; ++E)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ss[i] += oacc[E][i] * oacc[E][i];
-      float rstd[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(sum16(ss[i]) / (float)dv + p.eps);
-#pragma unroll
-      for (int E = 0; E < NDV; ++E) {
-        const int e = E * 16 + r16;
-        if (e < dv) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * I + 4 * g4 + i;
-            const float o = oacc[E][i];
-            if (gop && row < valid) gop[(row0 + (long)row * H) * dv + e] = from_f<T>(o);
-            const float rv = to_f(sR[row * dv + e]);
-            sR[row * dv + e] = from_f<T>(o * rstd[i] * gm[E] * rv * Fm<T>::sig(rv));
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    if (emit) store_rows<T>(gy + row0 * dv, (long)H * dv, sR, dv, valid, dv, tid, kThreads);
-
-    // ---- state carry: S = diag(e^{b_last}) S + (k e^{b_last - b})^T V
-#pragma unroll
-    for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
-        const int ct = u / NDV, et = u - ct * NDV;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = ct * 16 + g4 * 4 + i;
-          sacc[m][i] *= (c < dk) ? sGam[c] : 1.f;
-        }
-        sacc[m] = Mma<T>::kc(sacc[m], sKbT, TP, 16 * ct, sVt, TP, 16 * et, CK, lane);
-        if (OUT) {
-          const int e = et * 16 + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sS[e * QP + ct * 16 + g4 * 4 + i] = from_f<T>(sacc[m][i]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (!OUT) {
-    float* dst = p.states + (sbase + c_first) * dk * dv;
-#pragma unroll
-    for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
-        const int ct = u / NDV, et = u - ct * NDV;
-        const int e = et * 16 + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = ct * 16 + g4 * 4 + i;
-          if (c < dk && e < dv) dst[c * dv + e] = sacc[m][i];
-        }
-      }
-    }
-    for (int c = tid; c < dk; c += kThreads) p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
-  }
-}
-
 // Exclusive scan over segments, in place: slot(p) <- state entering segment p.
 // Forward direction: S(0) = 0, S(p+1) = 2^{lg(p)} S(p) + dS(p).
-__global__ __launch_bounds__(kThreads) void gla_state_scan(float* states, const float* seg_lg,
-                                                          int BH, int NC, int sc, int nseg,
-                                                          int dk, int dv) {
-  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void gla_state_scan(float* states,
+                                                              const float* seg_lg, int BH,
+                                                              int NC, int sc, int nseg, int dk,
+                                                              int dv) {
+  const long idx = (long)blockIdx.x * kScanThreads + threadIdx.x;
   const long per = (long)dk * dv;
   if (idx >= (long)BH * per) return;
   const long bh = idx / per, ce = idx - bh * per;
@@ -492,41 +94,37 @@ __global__ __launch_bounds__(kThreads) void gla_state_scan(float* states, const 
   base[(long)(nseg - 1) * sc * per] = S;
 }
 
-template <typename T, int NDK, int NDV>
-static hipError_t launch_t(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
+hipError_t launch_gla_state_scan(const GlaShape& s, float* states, const float* seg_lg,
+                                 hipStream_t st) {
   const long BH = (long)s.B * s.H;
-  if (!s.prefix && s.nseg > 1) {
-    GlaFwdParams pa = p;
-    pa.lds = gla_fwd_lds(s, false);
-    hipLaunchKernelGGL((gla_fwd_kernel<T, NDK, NDV, false>), dim3((unsigned)(BH * (s.nseg - 1))),
-                       dim3(kThreads), pa.lds.bytes, st, pa);
-    const long nthreads = BH * s.dk * s.dv;
-    hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)((nthreads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, p.states, p.seg_lg, (int)BH, s.NC, s.sc, s.nseg,
-                       s.dk, s.dv);
-  }
-  p.lds = gla_fwd_lds(s, true);
-  hipLaunchKernelGGL((gla_fwd_kernel<T, NDK, NDV, true>), dim3((unsigned)(BH * s.nseg)),
-                     dim3(kThreads), p.lds.bytes, st, p);
+  const long nthreads = BH * s.dk * s.dv;
+  hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)((nthreads + kScanThreads - 1) / kScanThreads)),
+                     dim3(kScanThreads), 0, st, states, seg_lg, (int)BH, s.NC, s.sc, s.nseg, s.dk,
+                     s.dv);
   return hipGetLastError();
 }
 
+// Chunk kernels, instantiated per element type in their own translation units.
 template <typename T>
-static hipError_t launch_cls(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
-  switch (s.ndk * 16 + s.ndv) {
-    case 1 * 16 + 2: return launch_t<T, 1, 2>(s, p, st);
-    case 2 * 16 + 4: return launch_t<T, 2, 4>(s, p, st);
-    case 3 * 16 + 5: return launch_t<T, 3, 5>(s, p, st);
-    case 4 * 16 + 8: return launch_t<T, 4, 8>(s, p, st);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_gla_fwd_t(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out);
+extern template hipError_t launch_gla_fwd_t<bf16>(const GlaShape&, GlaFwdParams, hipStream_t,
+                                                  int*);
+extern template hipError_t launch_gla_fwd_t<float>(const GlaShape&, GlaFwdParams, hipStream_t,
+                                                   int*);
+
+int gla_fwd_lds_bytes(const GlaShape& s) {
+  int bytes = 0;
+  const hipError_t e = s.bf16 ? launch_gla_fwd_t<bf16>(s, GlaFwdParams{}, nullptr, &bytes)
+                              : launch_gla_fwd_t<float>(s, GlaFwdParams{}, nullptr, &bytes);
+  return e == hipSuccess ? bytes : 0;
 }
 
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.prefix;
-  return s.bf16 ? launch_cls<bf16>(s, p, st) : launch_cls<float>(s, p, st);
+  return s.bf16 ? launch_gla_fwd_t<bf16>(s, p, st, nullptr)
+                : launch_gla_fwd_t<float>(s, p, st, nullptr);
 }
 
 }  // namespace dig

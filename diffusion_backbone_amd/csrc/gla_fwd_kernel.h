@@ -1,0 +1,542 @@
+// gla_fwd_kernel.h -- the chunk kernel of the GLA forward on gfx950 (included by the
+// per-element-type translation units gla_fwd_bf16.hip and gla_fwd_f32.hip).
+//
+// What is computed (DiG study-group slides, eqs. (5)-(10); write-up section 3,
+// "Efficiency Analysis": chunks of M tokens computed on-chip), per image b and head h:
+//   g_t = logsigmoid(z_t)/tau,  S_t = diag(exp g_t) S_{t-1} + k_t^T v_t,  o_t = q_t S_t,
+//   y_t = RMSNorm_head(o_t) * w * Swish(r_t).
+// Chunk form, with b_i = sum of g over the chunk up to token i (inclusive) and S0 the state
+// entering the chunk:
+//   o_i = sum_{j<=i} [sum_c q_ic e^{b_ic} k_jc e^{-b_jc}] v_j + (q_i e^{b_i}) S0
+//   S_next = diag(e^{b_last}) S0 + sum_j (k_j e^{b_last - b_j})^T v_j
+// The bracket (the gated Q K^T of the chunk) and both products with V/S run on matrix cores
+// (bf16 16x16x32 or fp32 16x16x4, fp32 accumulation).  Gates live in log2 space in fp32.
+// When a chunk's total decay is so strong that k e^{-b} could overflow, that chunk's gated
+// Q K^T is evaluated elementwise as sum_c q_ic k_jc exp(b_ic - b_jc) instead.
+//
+// Per chunk, one workgroup of four waves runs two phases separated by barriers:
+//   gate    lanes = tokens of the chunk, each lane a run of key columns: log-sigmoid, the
+//           in-chunk cumulative sum as a DPP lane scan, the scaled operands q e^{b},
+//           k e^{-b}, (k e^{b_last-b})^T and V^T written to LDS;
+//   product every wave advances its share of the fp32 state tiles; wave I owns query rows
+//           16I..16I+15: gated Q K^T (kept in registers), P V, (q e^{b}) S0, the RMSNorm x
+//           Swish epilogue (y written over r in LDS, then stored as whole rows).
+// The raw rows of the next chunk are copied global->LDS (LDS DMA) while the current one is
+// being processed (two staging slots when LDS allows).
+//
+// Head dims: DK x DV is either the exact shape (compile-time dims, no guards) or a 16-wide
+// tile class holding any smaller runtime shape (EXACT = false), zero-padded inside LDS.
+// The LDS layout is a compile-time function of the template parameters.
+#pragma once
+
+#include <type_traits>
+
+#include "dig_device.h"
+#include "dig_internal.h"
+
+namespace dig {
+
+constexpr int kFwdThreads = 256;
+constexpr float kSlowDecayLog2 = 96.0f;  // e^{-b} factors up to 2^96 stay finite in bf16/fp32
+constexpr int kFwdLdsBudget = 160 * 1024;
+
+constexpr int al16(int x) { return (x + 15) / 16 * 16; }
+
+template <typename T, int DK, int DV, int C, bool OUT>
+struct FwdLayout {
+  static constexpr int SZ = (int)sizeof(T);
+  static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
+  static constexpr int DKP = ((NDK * 16 + 31) / 32) * 32;  // key dim padded to the K step
+  static constexpr int DVP = NDV * 16;
+  static constexpr int CK = SZ == 2 ? ((C + 31) / 32) * 32 : C;  // token dim padded
+  static constexpr int QP = DKP + 8, TP = CK + 8;              // padded LDS row pitches
+  // byte offsets: operands, state copy, gates, misc; the raw staging slots come last
+  static constexpr int O_Q = 0;                                         // q e^{b}  [C][QP]
+  static constexpr int O_K = O_Q + al16(OUT ? C * QP * SZ : 0);          // k e^{-b} [C][QP]
+  static constexpr int O_KBT = O_K + al16(OUT ? C * QP * SZ : 0);        // kbar^T [16NDK][TP]
+  static constexpr int O_VT = O_KBT + al16(16 * NDK * TP * SZ);          // v^T    [DVP][TP]
+  static constexpr int O_S = O_VT + al16(DVP * TP * SZ);                 // S^T    [DVP][QP]
+  static constexpr int O_B = O_S + al16(OUT ? DVP * QP * SZ : 0);        // b fp32 [C][DK]
+  static constexpr int O_GAM = O_B + al16(OUT ? C * DK * 4 : 0);         // e^{b_last} [DKP]
+  static constexpr int O_LG = O_GAM + al16(DKP * 4);                     // segment decay
+  static constexpr int O_MAX = O_LG + al16(DKP * 4);                     // per-wave decay
+  static constexpr int O_P = O_MAX + 64;                                 // slow P [4][16][C]
+  static constexpr int O_RAW = O_P + al16(OUT ? 4 * 16 * C * 4 : 0);
+  // one staging slot: raw k, z, v (+ q, r) rows, packed with the runtime row length
+  static constexpr int R_K = 0;
+  static constexpr int R_Z = R_K + al16(C * DK * SZ);
+  static constexpr int R_V = R_Z + al16(C * DK * SZ);
+  static constexpr int R_Q = R_V + al16(C * DV * SZ);
+  static constexpr int R_R = R_Q + al16(OUT ? C * DK * SZ : 0);
+  static constexpr int SLOT = R_R + al16(OUT ? C * DV * SZ : 0);
+  static constexpr int bytes(int nbuf) { return O_RAW + nbuf * SLOT; }
+};
+
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
+__global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
+  using Lo = FwdLayout<T, DK, DV, C, OUT>;
+  constexpr bool kBf = sizeof(T) == 2;
+  constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
+  constexpr int QP = Lo::QP, TP = Lo::TP;
+  constexpr int NT = C / 16;                            // query row tiles
+  constexpr int NST = NDK * NDV, STW = (NST + 3) / 4;   // state tiles, per wave
+  constexpr int NCL = DKP * C / kFwdThreads;            // gate pass: key columns per lane
+  constexpr int NEL = DVP * C / kFwdThreads;            // V transpose: value columns per lane
+  // every gate/transpose column is a real one: no per-column guards
+  constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
+  static_assert(NCL >= 1 && NEL >= 1, "tile split");
+  using Acc = typename std::conditional<kBf, float, double>::type;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nseg_launch = OUT ? p.nseg : p.nseg - 1;
+  const int seg = blockIdx.x % nseg_launch;
+  const int bh = blockIdx.x / nseg_launch;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int H = p.H;
+  const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
+
+  T* sQ = reinterpret_cast<T*>(smem + Lo::O_Q);
+  T* sK = reinterpret_cast<T*>(smem + Lo::O_K);
+  T* sKbT = reinterpret_cast<T*>(smem + Lo::O_KBT);
+  T* sVt = reinterpret_cast<T*>(smem + Lo::O_VT);
+  T* sS = reinterpret_cast<T*>(smem + Lo::O_S);
+  float* sB = reinterpret_cast<float*>(smem + Lo::O_B);
+  float* sGam = reinterpret_cast<float*>(smem + Lo::O_GAM);
+  float* sLg = reinterpret_cast<float*>(smem + Lo::O_LG);
+  float* sMax = reinterpret_cast<float*>(smem + Lo::O_MAX);
+  float* sP = reinterpret_cast<float*>(smem + Lo::O_P);
+
+  const int c_first = seg * p.sc;
+  const int c_end = min(p.NC, c_first + p.sc);
+  const int n_begin = (OUT && p.prefix) ? 0 : c_first;
+  const bool scanned = !p.prefix && p.nseg > 1;  // incoming state comes from pass B
+  const long sbase = (long)bh * p.NC;             // chunk-slot base for this (b,h)
+  const float inv_tau = p.g2scale * 0.69314718055994531f;  // g2scale = log2(e) / tau
+
+  const T* gq = static_cast<const T*>(p.q);
+  const T* gk = static_cast<const T*>(p.k);
+  const T* gv = static_cast<const T*>(p.v);
+  const T* gz = static_cast<const T*>(p.z);
+  const T* gr = static_cast<const T*>(p.r);
+  T* gy = static_cast<T*>(p.y);
+  T* gop = static_cast<T*>(p.o_pre);
+
+  // staging slot s: k, z, v, then q, r (output chunks only)
+  auto issue = [&](int n, int s) {
+    unsigned char* base = smem + Lo::O_RAW + s * Lo::SLOT;
+    const int t0 = n * C, valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;
+    const long gsk = (long)H * dk * sizeof(T), gsv = (long)H * dv * sizeof(T);
+    const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
+    dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
+               valid, wave, 4, lane);
+    if (OUT && n >= c_first) {
+      dma_rows_c(base + Lo::R_Q, reinterpret_cast<const unsigned char*>(gq + row0 * dk), gsk,
+                 rbk, valid, wave, 4, lane);
+      dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv,
+                 rbv, valid, wave, 4, lane);
+    }
+  };
+  issue(n_begin, 0);  // the first chunk's copy overlaps the set-up below
+
+  // zero everything but the staging slots: padding rows/columns of the MFMA operands must
+  // read as zero and are never written afterwards
+  for (int i = tid; i < Lo::O_RAW / 16; i += kFwdThreads)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+
+  f32x4 sacc[STW];
+#pragma unroll
+  for (int m = 0; m < STW; ++m) sacc[m] = zero4();
+  if (OUT && scanned && seg > 0) {
+    const float* src = p.states + (sbase + c_first) * dk * dv;
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ct * 16 + g4 * 4 + i;
+          sacc[m][i] = (c < dk && e < dv) ? src[c * dv + e] : 0.f;
+        }
+      }
+    }
+  }
+
+  float gm[NDV];  // norm weight of the output column this lane touches in tile E
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = E * 16 + r16;
+    gm[E] = (OUT && e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
+  }
+
+  // gate-pass lane roles: token tg of the chunk, key columns c0.., value columns e0..
+  const int tg = tid % C, cg = tid / C;
+  const int c0 = cg * NCL, e0 = cg * NEL;
+
+  for (int n = n_begin; n < c_end; ++n) {
+    const int it = n - n_begin;
+    const int slot = nbuf == 2 ? (it & 1) : 0;
+    unsigned char* raw = smem + Lo::O_RAW + slot * Lo::SLOT;
+    const T* rawk = reinterpret_cast<const T*>(raw + Lo::R_K);
+    const T* rawz = reinterpret_cast<const T*>(raw + Lo::R_Z);
+    const T* rawv = reinterpret_cast<const T*>(raw + Lo::R_V);
+    const T* rawq = reinterpret_cast<const T*>(raw + Lo::R_Q);
+    T* sR = reinterpret_cast<T*>(raw + Lo::R_R);
+    const bool emit = OUT && n >= c_first;
+    const int t0 = n * C;
+    const int valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;  // (b, t0, h) as a token-head row
+
+    if (nbuf == 1 && it > 0) {  // single slot: wait until the previous chunk left it
+      __syncthreads();
+      issue(n, 0);
+    }
+    // the state entering this chunk: saved for the backward, bf16 copy for (q e^b) S0
+    if (emit && p.write_states && !(scanned && n == c_first)) {
+      float* dst = p.states + (sbase + n) * dk * dv;
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NST) {
+          const int ct = u / NDV, et = u - ct * NDV;
+          const int e = et * 16 + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = ct * 16 + g4 * 4 + i;
+            if (c < dk && e < dv) dst[c * dv + e] = sacc[m][i];
+          }
+        }
+      }
+    }
+    if (emit) {
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NST) {
+          const int ct = u / NDV, et = u - ct * NDV;
+          const int e = et * 16 + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sS[e * QP + ct * 16 + g4 * 4 + i] = from_f<T>(sacc[m][i]);
+        }
+      }
+    }
+    dma_wait();
+    __syncthreads();
+    if (nbuf == 2 && n + 1 < c_end) issue(n + 1, slot ^ 1);
+
+    // ---------------------------------------------------------------- gate phase
+    // (every LDS read first, then the arithmetic, then every write: one LDS round trip)
+    {
+      const bool tv = tg < valid;
+      T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
+      if constexpr (FULLK) {
+        lds_row_read_k<T, NCL, DK>(zr, rawz + tg * DK, c0, tv);
+        lds_row_read_k<T, NCL, DK>(kr, rawk + tg * DK, c0, tv);
+        if (emit) lds_row_read_k<T, NCL, DK>(qr, rawq + tg * DK, c0, tv);
+      } else {
+        lds_row_read<T, NCL>(zr, rawz + tg * dk, c0, dk, tv);
+        lds_row_read<T, NCL>(kr, rawk + tg * dk, c0, dk, tv);
+        if (emit) lds_row_read<T, NCL>(qr, rawq + tg * dk, c0, dk, tv);
+      }
+      if constexpr (FULLV) lds_row_read_k<T, NEL, DV>(vr, rawv + tg * DV, e0, tv);
+      else lds_row_read<T, NEL>(vr, rawv + tg * dv, e0, dv, tv);
+
+      float bb[NCL], bl[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        const bool on = FULLK ? tv : (tv && c0 + j < dk);
+        bb[j] = on ? Fm<T>::lsig2(to_f(zr[j])) * inv_tau : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) bl[j] = group_last<C>(bb[j], lane);
+      T kb[NCL], qs[NCL], ks[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        const float kf = to_f(kr[j]);
+        kb[j] = from_f<T>(kf * Fm<T>::exp2(bl[j] - bb[j]));
+        if (emit) {
+          qs[j] = from_f<T>(to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]));
+          ks[j] = from_f<T>(kf * Fm<T>::exp2(-bb[j]));
+        }
+      }
+      float md = 0.f;  // strongest decay over this wave's columns -> slow-path test
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) md = fmaxf(md, -bl[j]);
+      if (emit) md = wave_max_dpp(md);
+
+#pragma unroll
+      for (int j = 0; j < NCL; ++j)
+        if (FULLK || c0 + j < 16 * NDK) sKbT[(c0 + j) * TP + tg] = kb[j];
+#pragma unroll
+      for (int j = 0; j < NEL; ++j) sVt[(e0 + j) * TP + tg] = vr[j];  // V^T, zero past the end
+      if (emit) {
+        lds_row_write<T, NCL>(sQ + tg * QP, c0, qs);
+        lds_row_write<T, NCL>(sK + tg * QP, c0, ks);
+#pragma unroll
+        for (int j = 0; j < NCL; ++j)
+          if (FULLK || c0 + j < dk) sB[tg * DK + c0 + j] = bb[j];
+        if (lane == 0) sMax[wave] = md;
+      }
+      if (tg == C - 1) {
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+          sGam[c0 + j] = Fm<T>::exp2(bl[j]);
+          if (!OUT) sLg[c0 + j] += bl[j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------- product phase
+    // state carry first (independent of the outputs): S = diag(e^{b_last}) S + Kbar^T V
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[m][i] *= gam[i];
+        sacc[m] = Mma<T>::kc(sacc[m], sKbT, TP, 16 * ct, sVt, TP, 16 * et, CK, lane);
+      }
+    }
+
+    if (emit && wave < NT) {
+      const int I = wave;  // this wave's 16 query rows
+      const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
+      const bool slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kSlowDecayLog2;
+      // exact diagonal q_i.k_i (gate factor 1) from the unscaled inputs, so that a
+      // cancelling dot product keeps its relative accuracy: 16 rows x 4 column groups
+      float diag;
+      {
+        constexpr int DQ = DKP / 4;
+        const int ir = 16 * I + r16;
+        T qd[DQ], kd[DQ];
+        if constexpr (FULLK) {
+          lds_row_read_k<T, DQ, DK>(qd, rawq + ir * DK, g4 * DQ, true);
+          lds_row_read_k<T, DQ, DK>(kd, rawk + ir * DK, g4 * DQ, true);
+        } else {
+          lds_row_read<T, DQ>(qd, rawq + ir * dk, g4 * DQ, dk, true);
+          lds_row_read<T, DQ>(kd, rawk + ir * dk, g4 * DQ, dk, true);
+        }
+        Acc acc = 0;
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) acc += (Acc)to_f(qd[j]) * (Acc)to_f(kd[j]);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        diag = (float)acc * p.q_scale;
+      }
+      // P^T tiles: pt[J][i] = P[16I + r16][16J + 4*g4 + i]
+      f32x4 pt[NT];
+      if (!slow) {
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+          pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
+      } else {
+        // strong decay: P_ij = sum_c q_ic k_jc 2^{b_ic - b_jc} elementwise (no overflow), via a
+        // per-wave LDS tile (rare path, kept compact)
+        float* sPw = sP + wave * 16 * C;
+        for (int idx = lane; idx < 16 * C; idx += 64) {
+          const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
+          float acc = 0.f;
+          if (j <= ir) {
+            for (int c = 0; c < dk; ++c)
+              acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
+                     Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
+            acc *= p.q_scale;
+          }
+          sPw[idx] = acc;
+        }
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pt[J][i] = sPw[r16 * C + 16 * J + 4 * g4 + i];
+      }
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {  // diagonal tile: causal mask and the exact diagonal
+        if (J == I) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (4 * g4 + i > r16) pt[J][i] = 0.f;
+            if (4 * g4 + i == r16) pt[J][i] = diag;
+          }
+        }
+      }
+
+      f32x4 oacc[NDV];
+#pragma unroll
+      for (int E = 0; E < NDV; ++E) oacc[E] = zero4();
+      // inter-chunk: O = (q e^{b}) S0
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+        oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
+
+      // intra-chunk: O += P V   (P straight from the accumulators above)
+      if constexpr (kBf) {
+#pragma unroll
+        for (int pp = 0; pp < (NT + 1) / 2; ++pp) {
+          if (2 * pp <= I) {
+            const bool hi_on = 2 * pp + 1 <= I;
+            bf16x8 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              a[i] = from_f<bf16>(pt[2 * pp][i]);
+              a[4 + i] = from_f<bf16>(hi_on ? pt[min(2 * pp + 1, NT - 1)][i] : 0.f);
+            }
+#pragma unroll
+            for (int E = 0; E < NDV; ++E) {
+              const T* vb = sVt + (E * 16 + r16) * TP + 32 * pp + 4 * g4;
+              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vb);
+              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vb + 16);
+              bf16x8 bv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) { bv[i] = lo[i]; bv[4 + i] = hi[i]; }
+              oacc[E] = mfma_bf16(a, bv, oacc[E]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          if (J <= I) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+              for (int E = 0; E < NDV; ++E) {
+                const float bv = to_f(sVt[(E * 16 + r16) * TP + 16 * J + 4 * g4 + s4]);
+                oacc[E] = mfma_f32(pt[J][s4], bv, oacc[E]);
+              }
+            }
+          }
+        }
+      }
+
+      // output stage: head-wise RMSNorm x weight x Swish(r); y written over r in LDS
+      T rr[NDV][4];  // all of this lane's r first (one LDS round trip)
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = E * 16 + r16;
+          rr[E][i] = (FULLV || e < dv) ? sR[(16 * I + 4 * g4 + i) * dv + e] : from_f<T>(0.f);
+        }
+      float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss[i] += oacc[E][i] * oacc[E][i];
+      float rstd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) / (float)dv + p.eps);
+#pragma unroll
+      for (int E = 0; E < NDV; ++E) {
+        const int e = E * 16 + r16;
+        if (FULLV || e < dv) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * I + 4 * g4 + i;
+            const float o = oacc[E][i];
+            if (gop && row < valid) gop[(row0 + (long)row * H) * dv + e] = from_f<T>(o);
+            const float rv = to_f(rr[E][i]);
+            sR[row * dv + e] = from_f<T>(o * rstd[i] * gm[E] * rv * Fm<T>::sig(rv));
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    if (emit) store_rows<T>(gy + row0 * dv, (long)H * dv, sR, dv, valid, dv, tid, kFwdThreads);
+  }
+
+  if (!OUT) {
+    float* dst = p.states + (sbase + c_first) * dk * dv;
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ct * 16 + g4 * 4 + i;
+          if (c < dk && e < dv) dst[c * dv + e] = sacc[m][i];
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < dk; c += kFwdThreads)
+      p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
+  }
+}
+
+// LDS bytes and staging slots of one launch.  Two slots (prefetch of the next chunk) when a
+// workgroup walks more than one chunk and they fit.
+template <typename T, int DK, int DV, int C, bool OUT>
+static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
+  using Lo = FwdLayout<T, DK, DV, C, OUT>;
+  const int walk = (OUT && s.prefix) ? s.NC : s.sc;
+  *nbuf = (walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
+  *bytes = Lo::bytes(*nbuf);
+}
+
+template <typename T, int DK, int DV, bool EXACT, int C>
+static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
+  const long BH = (long)s.B * s.H;
+  int bytes_c, nbuf_c;
+  fwd_lds<T, DK, DV, C, true>(s, &bytes_c, &nbuf_c);
+  if (lds_out) {  // size query only
+    *lds_out = bytes_c;
+    return hipSuccess;
+  }
+  if (!s.prefix && s.nseg > 1) {
+    int bytes_a, nbuf_a;
+    fwd_lds<T, DK, DV, C, false>(s, &bytes_a, &nbuf_a);
+    hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false>),
+                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(kFwdThreads), bytes_a, st, p,
+                       nbuf_a);
+    const hipError_t e = launch_gla_state_scan(s, p.states, p.seg_lg, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true>), dim3((unsigned)(BH * s.nseg)),
+                     dim3(kFwdThreads), bytes_c, st, p, nbuf_c);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, bool EXACT>
+static hipError_t launch_fwd_dims(const GlaShape& s, GlaFwdParams p, hipStream_t st,
+                                  int* lds_out) {
+  switch (s.C) {
+    case 16: return launch_fwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out);
+    case 32: return launch_fwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out);
+    case 64: return launch_fwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Exact DiG head shapes (S: 32/64, XL: 36/72, and 16/32), else the enclosing tile class.
+// lds_out != nullptr: only report the LDS bytes of the output pass.
+template <typename T>
+hipError_t launch_gla_fwd_t(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
+  if (s.dk == 32 && s.dv == 64) return launch_fwd_dims<T, 32, 64, true>(s, p, st, lds_out);
+  if (s.dk == 36 && s.dv == 72) return launch_fwd_dims<T, 36, 72, true>(s, p, st, lds_out);
+  if (s.dk == 16 && s.dv == 32) return launch_fwd_dims<T, 16, 32, true>(s, p, st, lds_out);
+  switch (s.ndk * 16 + s.ndv) {
+    case 1 * 16 + 2: return launch_fwd_dims<T, 16, 32, false>(s, p, st, lds_out);
+    case 2 * 16 + 4: return launch_fwd_dims<T, 32, 64, false>(s, p, st, lds_out);
+    case 3 * 16 + 5: return launch_fwd_dims<T, 48, 80, false>(s, p, st, lds_out);
+    case 4 * 16 + 8: return launch_fwd_dims<T, 64, 128, false>(s, p, st, lds_out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dig

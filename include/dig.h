@@ -83,9 +83,7 @@ typedef struct {
 
 /*
  * Bytes of the forward->backward buffer `saved`: the fp32 state entering every chunk,
- * [B][H][ceil(L/chunk)][d_k][d_v], then, at the next 256-byte boundary, one 32-bit counter
- * that dig_gla_fwd zeroes and dig_gla_bwd uses (and leaves at zero) to find its last
- * workgroup.  0 for an invalid descriptor.
+ * [B][H][ceil(L/chunk)][d_k][d_v].  0 for an invalid descriptor.
  */
 size_t dig_gla_saved_bytes(const dig_gla_desc* desc);
 
@@ -120,13 +118,11 @@ size_t dig_gla_bwd_workspace_bytes(const dig_gla_desc* desc);
  *   dq, dk, d_gate_logit : [B, L, H, d_k];  dv, dr : [B, L, H, d_v]   (overwritten)
  *   d_norm_w             : [d_v] fp32 sum over batch, tokens and heads (overwritten), or NULL
  * d_gate_logit = dlog(alpha) * sigmoid(-z) / tau.  The d_norm_w reduction runs in a fixed
- * order, so repeated calls give identical bits.  The chunk states in `saved` are only read;
- * its counter word is updated and returned to zero, so two backward calls that share one
- * `saved` buffer must not run at the same time.
+ * order, so repeated calls give identical bits.
  */
 dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, const void* v,
                        const void* gate_logit, const void* r, const float* norm_w,
-                       const void* dy, void* saved, void* dq, void* dk, void* dv,
+                       const void* dy, const void* saved, void* dq, void* dk, void* dv,
                        void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 

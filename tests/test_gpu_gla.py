@@ -221,22 +221,12 @@ def test_bwd_determinism():
     g2 = gla_backward(case, f)
     for n in GRADS + ("dgamma",):
         assert np.array_equal(to_f64(g1[n]), to_f64(g2[n])), n
-    _assert_counter_zero(f)
-    # the single-launch short-sequence path (last workgroup reduces d_norm_w) as well
+    # the single-launch short-sequence path as well
     case = _case("dig_s2_256", batch=3, seq_len=200)
     f = gla_forward(case, 64, want_saved=True)
     g1 = gla_backward(case, f)
     g2 = gla_backward(case, f)
     assert np.array_equal(to_f64(g1["dgamma"]), to_f64(g2["dgamma"]))
-    _assert_counter_zero(f)
-
-
-def _assert_counter_zero(f):
-    """The backward leaves the counter word at the end of `saved` at zero."""
-    import diffusion_backbone_amd as dig
-    nbytes = dig.dig_gla_saved_bytes(f["desc"])
-    word = f["saved"].view(-1)[nbytes - 256:nbytes - 252].cpu().numpy().view(np.uint32)[0]
-    assert word == 0
 
 
 def test_fwd_bwd_config_dig_xl2_2048_full():
