@@ -13,8 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdig.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["dig_api.cpp", "gla_fwd.hip", "gla_fwd_bf16.hip", "gla_fwd_f32.hip", "gla_bwd.hip", "srem.hip"]
-HEADERS = ["dig_device.h", "dig_internal.h", "gla_fwd_kernel.h"]
+SOURCES = ["dig_api.cpp", "gla_fwd.hip", "gla_fwd_bf16.hip", "gla_fwd_f32.hip", "gla_bwd.hip",
+           "gla_bwd_bf16.hip", "gla_bwd_f32.hip", "srem.hip"]
+HEADERS = ["dig_device.h", "dig_internal.h", "gla_fwd_kernel.h", "gla_bwd_kernel.h"]
 
 ARCH = "gfx950"
 FLAGS = [

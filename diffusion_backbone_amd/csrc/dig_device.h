@@ -68,6 +68,7 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+
 template <typename T> struct Mma;
 
 // Operand access: KC ("K-contiguous") means element (row, k) sits at base[row * ld + k];
@@ -88,14 +89,40 @@ template <> struct Mma<bf16> {
       return v;
     }
   }
-  // acc += sum_{k<K} A(m0 + m, k) * B(k, n0 + n)
+  template <bool KC>
+  __device__ static __forceinline__ bf16x4 frag4(const bf16* base, int ld, int row, int k) {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x4*>(base + row * ld + k);
+    } else {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = base[(k + i) * ld + row];
+      return v;
+    }
+  }
+  // acc += sum_{k<K} A(m0 + m, k) * B(k, n0 + n); K a multiple of 16 (a final 16 runs as a
+  // 16x16x32 step with half of each lane's slots zero)
   template <bool AKC, bool BKC>
   __device__ static __forceinline__ f32x4 mm(f32x4 acc, const bf16* A, int lda, int m0,
                                              const bf16* B, int ldb, int n0, int K, int lane) {
-    const int r = lane & 15, g8 = (lane >> 4) * 8;
-
-    for (int k = 0; k < K; k += 32)
-      acc = mfma_bf16(frag<AKC>(A, lda, m0 + r, k + g8), frag<BKC>(B, ldb, n0 + r, k + g8), acc);
+    const int r = lane & 15, g = lane >> 4;
+    int k = 0;
+    for (; k + 32 <= K; k += 32)
+      acc = mfma_bf16(frag<AKC>(A, lda, m0 + r, k + 8 * g), frag<BKC>(B, ldb, n0 + r, k + 8 * g),
+                      acc);
+    if (k < K) {  // K tail of 16: each lane group's 4 live k in slots 0-3, zeros in 4-7
+      const bf16x4 a4 = frag4<AKC>(A, lda, m0 + r, k + 4 * g);
+      const bf16x4 b4 = frag4<BKC>(B, ldb, n0 + r, k + 4 * g);
+      bf16x8 a, b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = a4[i];
+        b[i] = b4[i];
+        a[4 + i] = from_f<bf16>(0.f);
+        b[4 + i] = from_f<bf16>(0.f);
+      }
+      acc = mfma_bf16(a, b, acc);
+    }
     return acc;
   }
   __device__ static __forceinline__ f32x4 kc(f32x4 acc, const bf16* A, int lda, int m0,
@@ -290,7 +317,7 @@ __device__ __forceinline__ void lds_row_read_k(T (&out)[N], const T* row, int c0
 // the byte offset is 16-aligned and N fills whole vectors).
 template <typename T, int N>
 __device__ __forceinline__ void lds_row_write(T* row, int c0, const T (&in)[N]) {
-  constexpr int V16 = 16 / (int)sizeof(T);
+  constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T);
   if constexpr (N % V16 == 0) {
     if (((reinterpret_cast<uintptr_t>(row + c0)) & 15) == 0) {
 #pragma unroll
@@ -300,6 +327,19 @@ __device__ __forceinline__ void lds_row_write(T* row, int c0, const T (&in)[N]) 
 #pragma unroll
         for (int i = 0; i < V16; ++i) e[i] = in[j + i];
         *reinterpret_cast<uint4*>(row + c0 + j) = u;
+      }
+      return;
+    }
+  }
+  if constexpr (N % V8 == 0) {
+    if (((reinterpret_cast<uintptr_t>(row + c0)) & 7) == 0) {
+#pragma unroll
+      for (int j = 0; j < N; j += V8) {
+        uint2 u;
+        T* e = reinterpret_cast<T*>(&u);
+#pragma unroll
+        for (int i = 0; i < V8; ++i) e[i] = in[j + i];
+        *reinterpret_cast<uint2*>(row + c0 + j) = u;
       }
       return;
     }

@@ -52,13 +52,6 @@ hipError_t launch_gla_state_scan(const GlaShape& s, float* states, const float* 
                                  hipStream_t st);
 
 // ----------------------------------------------------------------- GLA backward
-struct GlaBwdLds {
-  int DKP, DK16, DV16, DVP, DVK, CK;
-  int off_q, off_k, off_kb, off_v, off_do, off_s0, off_g, off_p, off_d, off_w, off_b, off_raw,
-      off_rdy, off_qk, off_part, off_gam, off_misc;
-  int bytes;
-};
-
 struct GlaBwdParams {
   int C, prefix;
   const void* q;
@@ -80,10 +73,13 @@ struct GlaBwdParams {
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
-  GlaBwdLds lds;
 };
 
-GlaBwdLds gla_bwd_lds(const GlaShape& s, bool final_pass);
+// LDS bytes of the backward's final pass for this shape (0 if no kernel exists for it).
+int gla_bwd_lds_bytes(const GlaShape& s);
+// Pass B of the three-pass backward: reverse scan of segment gradient states.
+hipError_t launch_gla_gstate_scan(const GlaShape& s, float* gstates, const float* seg_lg,
+                                  hipStream_t st);
 size_t gla_bwd_workspace(const GlaShape& s);
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 

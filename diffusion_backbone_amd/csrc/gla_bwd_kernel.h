@@ -1,0 +1,857 @@
+// gla_bwd_kernel.h -- the chunk kernel of the GLA backward on gfx950 (included by the
+// per-element-type translation units gla_bwd_bf16.hip and gla_bwd_f32.hip).
+//
+// Gradients of <dy, y> through the forward (DiG study-group slides, eqs. (5)-(10), by the
+// chain rule).  Per image and head, with do the gradient at the pre-norm output o, S_t the
+// state after token t and dS_t the gradient flowing into S_t:
+//   dq_t = S_t do_t,   dk_t = dS_t v_t,   dv_t = k_t dS_t,
+//   dlog(alpha_u) = sum_{t >= u} (q_t.dq_t - k_t.dk_t)          (elementwise per key dim)
+// Chunk form: b = in-chunk inclusive cumsum of log(alpha), S0 = state entering the chunk
+// (saved by the forward), G = gradient reaching the chunk's end state from later chunks,
+// D = dO V^T and P = gated Q K^T (both causal inside the chunk):
+//   dq_i = e^{b_i} (do_i S0^T + sum_{j<=i} D_ij k_j e^{-b_j})
+//   dk_j = e^{-b_j} sum_{i>=j} D_ij q_i e^{b_i} + e^{b_last-b_j} (G v_j)
+//   dv_j = sum_{i>=j} P_ij do_i + (k_j e^{-b_j}) (e^{b_last} G)
+//   dlog(alpha_u) = sum_{t>=u in chunk} (q.dq - k.dk)_t + sum_e (S_end (.) G)[:, e]
+//   G_prev = diag(e^{b_last}) G + sum_i (q_i e^{b_i})^T do_i
+// S_end, the state leaving the chunk, is the saved state entering the next chunk (and G is
+// zero after the last chunk).  The output-stage backward (head-wise RMSNorm x weight x
+// Swish) recomputes o from S0.
+//
+// Phases of one chunk (four waves, barriers between):
+//   gate      lanes = tokens: log-sigmoid, DPP cumulative sum, q e^{b}, k e^{-b} in row and
+//             transposed layouts, V in a padded row layout;
+//   recompute wave I: gated Q K^T rows 16I.., o = P V + (q e^b) S0, RMSNorm x Swish
+//             backward -> dO (row and transposed), dr, dgamma;
+//   D         dO V^T tiles (row and transposed), the boundary term of dlog(alpha);
+//   grads     dq, dk (row tile x key tile pairs), dv, and the carried G;
+//   dlog      lanes = tokens in reverse: suffix sums of q.dq - k.dk as a DPP scan -> dz.
+// Chunks that only carry G (later chunks recomputed in the same workgroup, or pass A of the
+// three-pass scheme) run gate, recompute and the G update only.
+#pragma once
+
+#include <type_traits>
+
+#include "dig_device.h"
+#include "dig_internal.h"
+
+namespace dig {
+
+constexpr int kBwdThreads = 256;
+constexpr float kBwdSlowDecayLog2 = 96.0f;
+
+constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
+
+// LDS layout (compile time).  LEAN drops the row-layout copies of dO, S0 and D (their
+// products then read the transposed copies with strided fragments) when the full layout
+// would not fit.
+template <typename T, int DK, int DV, int C, bool FIN, bool LEAN>
+struct BwdLayout {
+  static constexpr int SZ = (int)sizeof(T);
+  static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
+  static constexpr int DKP = 16 * NDK, DVP = 16 * NDV;           // contraction pads (K 16)
+  static constexpr int QP = DKP + 8, VP = DVP + 8, TP = C + 8;    // padded row pitches
+  // row layouts [token][dim]
+  static constexpr int O_Q = 0;                                          // q e^{b}   [C][QP]
+  static constexpr int O_K = O_Q + bal16(C * QP * SZ);                   // k e^{-b}  [C][QP]
+  static constexpr int O_V = O_K + bal16(C * QP * SZ);                   // v         [C][VP]
+  static constexpr int O_DO = O_V + bal16(C * VP * SZ);                  // dO        [C][VP]
+  static constexpr int O_S0 = O_DO + bal16(LEAN ? 0 : C * VP * SZ);      // S0      [DKP][VP]
+  static constexpr int O_D = O_S0 + bal16(LEAN ? 0 : DKP * VP * SZ);     // dO V^T    [C][TP]
+  // transposed layouts [dim][token] and [value][key]
+  static constexpr int O_QT = O_D + bal16(FIN && !LEAN ? C * TP * SZ : 0);  // (q e^b)^T [DKP][TP]
+  static constexpr int O_KT = O_QT + bal16(DKP * TP * SZ);               // (k e^-b)^T [DKP][TP]
+  static constexpr int O_DOT = O_KT + bal16(FIN ? DKP * TP * SZ : 0);    // dO^T     [DVP][TP]
+  static constexpr int O_S0T = O_DOT + bal16(DVP * TP * SZ);             // S0^T     [DVP][QP]
+  static constexpr int O_GT = O_S0T + bal16(DVP * QP * SZ);              // G^T      [DVP][QP]
+  static constexpr int O_PT = O_GT + bal16(FIN ? DVP * QP * SZ : 0);     // P^T        [C][TP]
+  // D^T [C][TP]; during the recompute phase the strong-decay P rows [4][16][C] live here
+  static constexpr int DT_BYTES = (FIN ? C * TP * SZ : 0) > 4 * 16 * C * SZ
+                                      ? (FIN ? C * TP * SZ : 0) : 4 * 16 * C * SZ;
+  static constexpr int O_DT = O_PT + bal16(FIN ? C * TP * SZ : 0);
+  // fp32 scratch
+  static constexpr int O_B = O_DT + bal16(DT_BYTES);                 // b, then q.dq-k.dk [C][DK]
+  static constexpr int O_GAM = O_B + bal16(C * DK * 4);              // e^{b_last}  [DKP]
+  static constexpr int O_LG = O_GAM + bal16(DKP * 4);                // b_last / segment decay
+  static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [4]
+  static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
+  static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [4][DVP]
+  static constexpr int O_DIAG = O_DG + bal16(4 * DVP * 4);           // [C]
+  static constexpr int O_RAW = O_DIAG + bal16(C * 4);
+  // raw staging: q, k, z, v, r, dy rows packed with the runtime row length
+  static constexpr int R_Q = 0;
+  static constexpr int R_K = R_Q + bal16(C * DK * SZ);
+  static constexpr int R_Z = R_K + bal16(C * DK * SZ);
+  static constexpr int R_V = R_Z + bal16(C * DK * SZ);
+  static constexpr int R_R = R_V + bal16(C * DV * SZ);
+  static constexpr int R_DY = R_R + bal16(C * DV * SZ);
+  static constexpr int SLOT = R_DY + bal16(C * DV * SZ);
+  static constexpr int bytes = O_RAW + SLOT;
+};
+constexpr int kBwdLdsBudget = 160 * 1024;
+template <typename T, int DK, int DV, int C, bool FIN>
+constexpr bool bwd_lean() {
+  return BwdLayout<T, DK, DV, C, FIN, false>::bytes > kBwdLdsBudget;
+}
+
+template <typename T, int DK, int DV, bool EXACT, int C, bool FIN>
+__global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
+  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN>();
+  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN>;
+  constexpr bool kBf = sizeof(T) == 2;
+  constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP;
+  constexpr int QP = Lo::QP, VP = Lo::VP, TP = Lo::TP;
+  constexpr int NT = C / 16;
+  constexpr int NST = NDK * NDV, STW = (NST + 3) / 4;
+  constexpr int NPAIR = NT * NDK, PRW = (NPAIR + 3) / 4;     // dq/dk (row tile, key tile)
+  constexpr int NDVT = NT * NDV, DVW = (NDVT + 3) / 4;       // dv (row tile, value tile)
+  constexpr int NCL = DKP * C / kBwdThreads;                 // gate: key columns per lane
+  constexpr int NEL = DVP * C / kBwdThreads;                 // gate: value columns per lane
+  constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
+  static_assert(NCL >= 1 && NEL >= 1, "tile split");
+  using Acc = typename std::conditional<kBf, float, double>::type;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nseg_launch = FIN ? p.nseg : p.nseg - 1;
+  const int seg = (FIN ? 0 : 1) + (int)(blockIdx.x % nseg_launch);
+  const int bh = blockIdx.x / nseg_launch;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int H = p.H;
+  const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
+
+  T* sQ = reinterpret_cast<T*>(smem + Lo::O_Q);
+  T* sK = reinterpret_cast<T*>(smem + Lo::O_K);
+  T* sV = reinterpret_cast<T*>(smem + Lo::O_V);
+  T* sdO = reinterpret_cast<T*>(smem + Lo::O_DO);
+  T* sS0 = reinterpret_cast<T*>(smem + Lo::O_S0);
+  T* sD = reinterpret_cast<T*>(smem + Lo::O_D);
+  T* sQt = reinterpret_cast<T*>(smem + Lo::O_QT);
+  T* sKt = reinterpret_cast<T*>(smem + Lo::O_KT);
+  T* sdOt = reinterpret_cast<T*>(smem + Lo::O_DOT);
+  T* sS0t = reinterpret_cast<T*>(smem + Lo::O_S0T);
+  T* sGt = reinterpret_cast<T*>(smem + Lo::O_GT);
+  T* sPt = reinterpret_cast<T*>(smem + Lo::O_PT);
+  T* sDt = reinterpret_cast<T*>(smem + Lo::O_DT);
+  float* sB = reinterpret_cast<float*>(smem + Lo::O_B);
+  float* sW = sB;  // q.dq - k.dk replaces b once dq, dk are formed
+  float* sGam = reinterpret_cast<float*>(smem + Lo::O_GAM);
+  float* sLg = reinterpret_cast<float*>(smem + Lo::O_LG);
+  float* sMax = reinterpret_cast<float*>(smem + Lo::O_MAX);
+  float* sPart = reinterpret_cast<float*>(smem + Lo::O_PART);
+  float* sDg = reinterpret_cast<float*>(smem + Lo::O_DG);
+  float* sDiag = reinterpret_cast<float*>(smem + Lo::O_DIAG);
+  T* sSlow = reinterpret_cast<T*>(smem + Lo::O_DT);  // strong-decay P rows (recompute only)
+  T* rawq = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Q);  // then dq
+  T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);  // then dk
+  T* rawz = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Z);  // then dz
+  T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);
+  T* sRr = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_R);   // r, then dr
+  T* sDy = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_DY);  // dy, then dv
+
+  const int c_first = seg * p.sc;
+  const int c_end = min(p.NC, c_first + p.sc);
+  const int n_top = (FIN && p.prefix) ? p.NC : c_end;  // later chunks recomputed for G
+  const bool scanned = !p.prefix && p.nseg > 1;
+  const long sbase = (long)bh * p.NC;
+  const float inv_tau = p.g2scale * 0.69314718055994531f;  // g2scale = log2(e) / tau
+
+  const T* gq = static_cast<const T*>(p.q);
+  const T* gk = static_cast<const T*>(p.k);
+  const T* gv = static_cast<const T*>(p.v);
+  const T* gz = static_cast<const T*>(p.z);
+  const T* gr = static_cast<const T*>(p.r);
+  const T* gdy = static_cast<const T*>(p.dy);
+
+  auto issue = [&](int n) {
+    unsigned char* base = smem + Lo::O_RAW;
+    const int t0 = n * C, valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;
+    const long gsk = (long)H * dk * sizeof(T), gsv = (long)H * dv * sizeof(T);
+    const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
+    dma_rows_c(base + Lo::R_Q, reinterpret_cast<const unsigned char*>(gq + row0 * dk), gsk, rbk,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv, rbv,
+               valid, wave, 4, lane);
+    dma_rows_c(base + Lo::R_DY, reinterpret_cast<const unsigned char*>(gdy + row0 * dv), gsv,
+               rbv, valid, wave, 4, lane);
+  };
+  // this lane's elements of the fp32 state tiles of chunk n (the saved forward states)
+  auto load_state = [&](int n, f32x4 (&dst)[STW]) {
+    const float* src = p.states + (sbase + n) * dk * dv;
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      dst[m] = zero4();
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ct * 16 + g4 * 4 + i;
+          if ((FULLK || c < dk) && (FULLV || e < dv)) dst[m][i] = src[c * dv + e];
+        }
+      }
+    }
+  };
+
+  issue(n_top - 1);
+  for (int i = tid; i < Lo::O_RAW / 16; i += kBwdThreads)
+    reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();  // the zero fill is complete before anything below writes LDS
+
+  // gradient state G (fp32, tile u = wave + 4m -> (key tile, value tile))
+  f32x4 gacc[STW];
+#pragma unroll
+  for (int m = 0; m < STW; ++m) gacc[m] = zero4();
+  if (FIN && scanned) {
+    const float* src = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ct * 16 + g4 * 4 + i;
+          gacc[m][i] = (c < dk && e < dv) ? src[c * dv + e] : 0.f;
+        }
+      }
+    }
+  }
+  // S0 of the current chunk, and the state leaving it (S0 of the next chunk) for the
+  // boundary term; the latter is needed only where G is nonzero
+  f32x4 s0c[STW], s0n[STW];
+  load_state(n_top - 1, s0c);
+#pragma unroll
+  for (int m = 0; m < STW; ++m) s0n[m] = zero4();
+  if (FIN && n_top < p.NC) load_state(n_top, s0n);
+
+  float gm[NDV], dgam[NDV];
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = E * 16 + r16;
+    gm[E] = (e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
+    dgam[E] = 0.f;
+  }
+  const int tg = tid % C, cg = tid / C;
+  const int c0 = cg * NCL, e0 = cg * NEL;
+
+  for (int n = n_top - 1; n >= c_first; --n) {
+    const bool own = FIN && n < c_end;  // gradients of this chunk are this workgroup's output
+    const int t0 = n * C;
+    const int valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;
+    if (n < n_top - 1) {
+      __syncthreads();  // the single staging slot is free again
+      issue(n);
+    }
+
+    // ---- S0 (transposed, and row unless LEAN) as bf16 operands; G^T follows the gate
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+        T sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = from_f<T>(s0c[m][i]);
+          if constexpr (!LEAN) sS0[(ct * 16 + g4 * 4 + i) * VP + e] = sv[i];
+        }
+        lds_row_write<T, 4>(sS0t + e * QP, ct * 16 + g4 * 4, sv);
+      }
+    }
+    dma_wait();
+    __syncthreads();
+    f32x4 s0p[STW];  // prefetch S0 of the next chunk down (consumed at the next top)
+    if (n > c_first) load_state(n - 1, s0p);
+
+    // ---------------------------------------------------------------- gate phase
+    {
+      const bool tv = tg < valid;
+      T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
+      if constexpr (FULLK) {
+        lds_row_read_k<T, NCL, DK>(zr, rawz + tg * DK, c0, tv);
+        lds_row_read_k<T, NCL, DK>(kr, rawk + tg * DK, c0, tv);
+        lds_row_read_k<T, NCL, DK>(qr, rawq + tg * DK, c0, tv);
+      } else {
+        lds_row_read<T, NCL>(zr, rawz + tg * dk, c0, dk, tv);
+        lds_row_read<T, NCL>(kr, rawk + tg * dk, c0, dk, tv);
+        lds_row_read<T, NCL>(qr, rawq + tg * dk, c0, dk, tv);
+      }
+      if constexpr (FULLV) lds_row_read_k<T, NEL, DV>(vr, rawv + tg * DV, e0, tv);
+      else lds_row_read<T, NEL>(vr, rawv + tg * dv, e0, dv, tv);
+
+      float bb[NCL], bl[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        const bool on = FULLK ? tv : (tv && c0 + j < dk);
+        bb[j] = on ? Fm<T>::lsig2(to_f(zr[j])) * inv_tau : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) bl[j] = group_last<C>(bb[j], lane);
+      T qs[NCL], ks[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        qs[j] = from_f<T>(to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]));
+        ks[j] = from_f<T>(to_f(kr[j]) * Fm<T>::exp2(-bb[j]));
+      }
+      float md = 0.f;
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) md = fmaxf(md, -bl[j]);
+      md = wave_max_dpp(md);
+
+      lds_row_write<T, NCL>(sQ + tg * QP, c0, qs);
+      lds_row_write<T, NCL>(sK + tg * QP, c0, ks);
+      lds_row_write<T, NEL>(sV + tg * VP, e0, vr);
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        if (FULLK || c0 + j < 16 * NDK) {
+          sQt[(c0 + j) * TP + tg] = qs[j];
+          if (own) sKt[(c0 + j) * TP + tg] = ks[j];
+        }
+        if (FULLK || c0 + j < dk) sB[tg * DK + c0 + j] = bb[j];
+      }
+      if (lane == 0) sMax[wave] = md;
+      if (tg == C - 1) {
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+          sGam[c0 + j] = Fm<T>::exp2(bl[j]);
+          if (FIN)
+            sLg[c0 + j] = bl[j];  // this chunk's log2 decay, for the e^{b_last - b} factors
+          else
+            sLg[c0 + j] += bl[j];  // segment's log2 decay
+        }
+      }
+    }
+    __syncthreads();
+    const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
+    const bool slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kBwdSlowDecayLog2;
+
+    // G^T as (e^{b_last} G)^T: it enters dv as k e^{-b} (e^{b_last} G) and dk as
+    // e^{-b} V (e^{b_last} G)^T; with strong decay (elementwise paths) G itself
+    if (own) {
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NST) {
+          const int ct = u / NDV, et = u - ct * NDV;
+          const int e = et * 16 + r16;
+          const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
+          T gv4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv4[i] = from_f<T>(slow ? gacc[m][i] : gacc[m][i] * gam[i]);
+          lds_row_write<T, 4>(sGt + e * QP, ct * 16 + g4 * 4, gv4);
+        }
+      }
+    }
+
+    // ------------------------------------------------------------ recompute phase
+    if (wave < NT) {
+      const int I = wave;
+      float diag;  // exact q_i.k_i from the unscaled inputs (gate factor 1)
+      {
+        constexpr int DQ = DKP / 4;
+        const int ir = 16 * I + r16;
+        T qd[DQ], kd[DQ];
+        if constexpr (FULLK) {
+          lds_row_read_k<T, DQ, DK>(qd, rawq + ir * DK, g4 * DQ, true);
+          lds_row_read_k<T, DQ, DK>(kd, rawk + ir * DK, g4 * DQ, true);
+        } else {
+          lds_row_read<T, DQ>(qd, rawq + ir * dk, g4 * DQ, dk, true);
+          lds_row_read<T, DQ>(kd, rawk + ir * dk, g4 * DQ, dk, true);
+        }
+        Acc acc = 0;
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) acc += (Acc)to_f(qd[j]) * (Acc)to_f(kd[j]);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        // rows past the sequence end hold stale staging data: they must stay exactly zero
+        diag = ir < valid ? (float)acc * p.q_scale : 0.f;
+      }
+      f32x4 pt[NT];  // pt[J][i] = P[16I + r16][16J + 4 g4 + i]
+      if (!slow) {
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+          pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
+      } else {
+        T* sPw = sSlow + wave * 16 * C;
+        for (int idx = lane; idx < 16 * C; idx += 64) {
+          const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
+          float acc = 0.f;
+          if (j <= ir && ir < valid) {
+            for (int c = 0; c < dk; ++c)
+              acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
+                     Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
+            acc *= p.q_scale;
+          }
+          sPw[idx] = from_f<T>(acc);
+        }
+#pragma unroll
+        for (int J = 0; J < NT; ++J)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pt[J][i] = to_f(sPw[r16 * C + 16 * J + 4 * g4 + i]);
+      }
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J == I) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (4 * g4 + i > r16) pt[J][i] = 0.f;
+            if (4 * g4 + i == r16) pt[J][i] = diag;
+          }
+        }
+        if (own && J <= I) {  // P^T for dv (tiles above the diagonal stay zero)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sPt[(16 * J + 4 * g4 + i) * TP + 16 * I + r16] = from_f<T>(pt[J][i]);
+        }
+      }
+      f32x4 oacc[NDV];
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+        oacc[E] = Mma<T>::kc(zero4(), sQ, QP, 16 * I, sS0t, QP, 16 * E, DKP, lane);
+      if constexpr (kBf) {
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp) {  // token tiles in pairs: one K = 32 step
+          if (2 * pp <= I) {
+            const bool hi_on = 2 * pp + 1 <= I;
+            bf16x8 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              a[i] = from_f<bf16>(pt[2 * pp][i]);
+              a[4 + i] = from_f<bf16>(hi_on ? pt[2 * pp + 1][i] : 0.f);
+            }
+#pragma unroll
+            for (int E = 0; E < NDV; ++E) {
+              const int e = E * 16 + r16;
+              bf16x8 bv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                bv[i] = sV[(32 * pp + 4 * g4 + i) * VP + e];
+                bv[4 + i] = sV[(32 * pp + 16 + 4 * g4 + i) * VP + e];
+              }
+              oacc[E] = mfma_bf16(a, bv, oacc[E]);
+            }
+          }
+        }
+        if constexpr (NT % 2 == 1) {  // last token tile alone: half-filled K = 32 step
+          constexpr int J = NT - 1;
+          if (J <= I) {
+            bf16x8 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              a[i] = from_f<bf16>(pt[J][i]);
+              a[4 + i] = from_f<bf16>(0.f);
+            }
+#pragma unroll
+            for (int E = 0; E < NDV; ++E) {
+              bf16x8 bv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                bv[i] = sV[(16 * J + 4 * g4 + i) * VP + E * 16 + r16];
+                bv[4 + i] = from_f<bf16>(0.f);
+              }
+              oacc[E] = mfma_bf16(a, bv, oacc[E]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          if (J <= I) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+              for (int E = 0; E < NDV; ++E) {
+                const float bv = to_f(sV[(16 * J + 4 * g4 + s4) * VP + E * 16 + r16]);
+                oacc[E] = mfma_f32(pt[J][s4], bv, oacc[E]);
+              }
+            }
+          }
+        }
+      }
+
+      // output-stage backward: r, dy first (one LDS round trip)
+      T rr[NDV][4], dyr[NDV][4];
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = E * 16 + r16, row = 16 * I + 4 * g4 + i;
+          const bool on = (FULLV || e < dv) && row < valid;  // stale rows past the end: 0
+          rr[E][i] = on ? sRr[row * dv + e] : from_f<T>(0.f);
+          dyr[E][i] = on ? sDy[row * dv + e] : from_f<T>(0.f);
+        }
+      float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss[i] += oacc[E][i] * oacc[E][i];
+      float rstd[4], md[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) / (float)dv + p.eps);
+      // oacc becomes the normalised output, dn = dy * w * swish(r)
+      float dn[NDV][4];
+#pragma unroll
+      for (int E = 0; E < NDV; ++E) {
+        const int e = E * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          oacc[E][i] *= rstd[i];
+          const int row = 16 * I + 4 * g4 + i;
+          const float nv = oacc[E][i], rv = to_f(rr[E][i]), dyv = to_f(dyr[E][i]);
+          const float sg = Fm<T>::sig(rv), sw = rv * sg;
+          if (own && (FULLV || e < dv)) {
+            dgam[E] += dyv * nv * sw;
+            sRr[row * dv + e] = from_f<T>(dyv * nv * gm[E] * sg * (1.f + rv * (1.f - sg)));
+          }
+          dn[E][i] = dyv * gm[E] * sw;
+          md[i] += dn[E][i] * nv;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) md[i] = row_sum16(md[i]) / (float)dv;
+      Acc dvd[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int E = 0; E < NDV; ++E) {
+        const int e = E * 16 + r16;
+        T dov4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * I + 4 * g4 + i;
+          const float dov = (FULLV || e < dv) ? rstd[i] * (dn[E][i] - oacc[E][i] * md[i]) : 0.f;
+          dov4[i] = from_f<T>(dov);
+          if constexpr (!LEAN) sdO[row * VP + e] = dov4[i];
+          dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
+        }
+        lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
+      }
+      // do_i is orthogonal to the normalised o_i (up to eps); when o_i is parallel to v_i
+      // (the first token) do_i.v_i cancels, so it is formed here from the fp32 do_i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Acc dd = dvd[i];
+        dd += __shfl_xor(dd, 1);
+        dd += __shfl_xor(dd, 2);
+        dd += __shfl_xor(dd, 4);
+        dd += __shfl_xor(dd, 8);
+        if (own && r16 == 0) sDiag[16 * I + 4 * g4 + i] = (float)dd;
+      }
+    }
+    __syncthreads();
+
+    if (own) {
+      // ---- D = dO V^T (causal, row and transposed) and the dlog(alpha) boundary term
+      for (int q = wave; q < NT * NT; q += 4) {
+        const int I = q / NT, J = q - I * NT;
+        if (J <= I) {
+          f32x4 d;
+          if constexpr (LEAN)
+            d = Mma<T>::template mm<false, true>(zero4(), sdOt, TP, 16 * I, sV, VP, 16 * J, DVP,
+                                                 lane);
+          else
+            d = Mma<T>::kc(zero4(), sdO, VP, 16 * I, sV, VP, 16 * J, DVP, lane);
+          T dt4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ii = 16 * I + 4 * g4 + i, jj = 16 * J + r16;
+            dt4[i] = from_f<T>(jj < ii ? d[i] : (jj == ii ? sDiag[ii] : 0.f));
+            if constexpr (!LEAN) sD[ii * TP + jj] = dt4[i];
+          }
+          lds_row_write<T, 4>(sDt + (16 * J + r16) * TP, 16 * I + 4 * g4, dt4);
+        }
+      }
+      // sum_e S_end (.) G per key column (S_end = S0 of the next chunk; G = 0 after the last)
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NST) {
+          const int ct = u / NDV, et = u - ct * NDV;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float part = row_sum16(s0n[m][i] * gacc[m][i]);
+            if (r16 == 0) sPart[et * DKP + ct * 16 + g4 * 4 + i] = part;
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- dq, dk (registers), dv (staged over dy)
+      f32x4 dqa[PRW], dka[PRW];
+#pragma unroll
+      for (int m = 0; m < PRW; ++m) {
+        dqa[m] = zero4();
+        dka[m] = zero4();
+        const int u = wave + 4 * m;
+        if (u < NPAIR) {
+          const int I = u / NDK, ct = u - I * NDK;
+          f32x4 a1, a2 = zero4(), a4 = zero4();
+          if constexpr (LEAN)
+            a1 = Mma<T>::template mm<false, false>(zero4(), sdOt, TP, 16 * I, sS0t, QP, 16 * ct,
+                                                   DVP, lane);
+          else
+            a1 = Mma<T>::kc(zero4(), sdO, VP, 16 * I, sS0, VP, 16 * ct, DVP, lane);
+          const f32x4 a3 = Mma<T>::template mm<true, false>(zero4(), sV, VP, 16 * I, sGt, QP,
+                                                            16 * ct, DVP, lane);
+          if (!slow) {
+            if constexpr (LEAN)
+              a2 = Mma<T>::template mm<false, true>(zero4(), sDt, TP, 16 * I, sKt, TP, 16 * ct, C,
+                                                    lane);
+            else
+              a2 = Mma<T>::kc(zero4(), sD, TP, 16 * I, sKt, TP, 16 * ct, C, lane);
+            a4 = Mma<T>::kc(zero4(), sDt, TP, 16 * I, sQt, TP, 16 * ct, C, lane);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * I + 4 * g4 + i, c = ct * 16 + r16;
+            float dq = 0.f, dkk = 0.f;
+            if (FULLK || c < dk) {
+              const float bt = sB[t * DK + c];
+              const float blast = sLg[c];
+              if (!slow) {  // a3 holds V (e^{b_last} G)^T here
+                dq = Fm<T>::exp2(bt) * (a1[i] + a2[i]);
+                dkk = Fm<T>::exp2(-bt) * (a4[i] + a3[i]);
+              } else {  // a3 holds V G^T here
+                float s1 = 0.f, s2 = 0.f;
+                for (int j = 0; j <= t && j < valid; ++j)
+                  s1 += to_f(LEAN ? sDt[j * TP + t] : sD[t * TP + j]) * to_f(rawk[j * dk + c]) *
+                        Fm<T>::exp2(bt - sB[j * DK + c]);
+                for (int i2 = t; i2 < valid; ++i2)
+                  s2 += to_f(sDt[t * TP + i2]) * to_f(rawq[i2 * dk + c]) * p.q_scale *
+                        Fm<T>::exp2(sB[i2 * DK + c] - bt);
+                dq = Fm<T>::exp2(bt) * a1[i] + s1;
+                dkk = s2 + Fm<T>::exp2(blast - bt) * a3[i];
+              }
+            }
+            dqa[m][i] = dq;
+            dka[m][i] = dkk;
+          }
+        }
+      }
+      f32x4 dva[DVW];
+#pragma unroll
+      for (int m = 0; m < DVW; ++m) {
+        dva[m] = zero4();
+        const int u = wave + 4 * m;
+        if (u < NDVT) {
+          const int J = u / NDV, et = u - J * NDV;
+          dva[m] = Mma<T>::kc(zero4(), sPt, TP, 16 * J, sdOt, TP, 16 * et, C, lane);
+          if (!slow) {
+            dva[m] = Mma<T>::kc(dva[m], sK, QP, 16 * J, sGt, QP, 16 * et, DKP, lane);
+          } else {  // k_j e^{b_last - b_j} G elementwise (no overflow)
+            const int e = et * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = 16 * J + 4 * g4 + i;
+              float acc = 0.f;
+              for (int c = 0; c < dk; ++c)
+                acc += to_f(rawk[j * dk + c]) * Fm<T>::exp2(sLg[c] - sB[j * DK + c]) *
+                       to_f(sGt[e * QP + c]);
+              dva[m][i] += acc;
+            }
+          }
+        }
+      }
+      __syncthreads();  // all reads of sB, raw q/k and dy done
+
+      // ---- q.dq - k.dk over b; dq, dk over raw q, k; dv over dy
+#pragma unroll
+      for (int m = 0; m < PRW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NPAIR) {
+          const int I = u / NDK, ct = u - I * NDK;
+          const int c = ct * 16 + r16;
+          if (FULLK || c < dk) {
+            T qv[4], kv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * I + 4 * g4 + i;
+              qv[i] = rawq[t * dk + c];
+              kv[i] = rawk[t * dk + c];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * I + 4 * g4 + i;
+              sW[t * DK + c] = to_f(qv[i]) * p.q_scale * dqa[m][i] - to_f(kv[i]) * dka[m][i];
+              rawq[t * dk + c] = from_f<T>(p.q_scale * dqa[m][i]);
+              rawk[t * dk + c] = from_f<T>(dka[m][i]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < DVW; ++m) {
+        const int u = wave + 4 * m;
+        if (u < NDVT) {
+          const int J = u / NDV, et = u - J * NDV;
+          const int e = et * 16 + r16;
+          if (FULLV || e < dv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * dv + e] = from_f<T>(dva[m][i]);
+          }
+        }
+      }
+    }
+
+    // gradient state: G <- diag(e^{b_last}) G + (q e^{b})^T dO
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gacc[m][i] *= gam[i];
+        gacc[m] = Mma<T>::kc(gacc[m], sQt, TP, 16 * ct, sdOt, TP, 16 * et, C, lane);
+      }
+    }
+    __syncthreads();
+
+    if (own) {
+      // ---- dlog(alpha) = suffix sums of q.dq - k.dk (lanes = tokens in reverse order, DPP
+      // prefix scan) + the boundary term; dz = dlog(alpha) sigmoid(-z) / tau, over raw z
+      const int tr = C - 1 - tg;
+      const bool tv = tr < valid;
+      float w[NCL];
+      T zr[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        const int c = c0 + j;
+        const bool on = tv && (FULLK || c < dk);
+        w[j] = on ? sW[tr * DK + c] : 0.f;
+        zr[j] = on ? rawz[tr * dk + c] : from_f<T>(0.f);
+      }
+      float bterm[NCL];
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int et = 0; et < NDV; ++et) s += sPart[et * DKP + c0 + j];
+        bterm[j] = s;
+      }
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) w[j] = scan_dpp<C>(w[j]);
+#pragma unroll
+      for (int j = 0; j < NCL; ++j) {
+        const int c = c0 + j;
+        if (tv && (FULLK || c < dk)) {
+          float dla = w[j] + bterm[j];
+          if (n == 0 && tr == 0) dla = 0.f;  // alpha_0 multiplies the zero initial state
+          rawz[tr * dk + c] = from_f<T>(dla * Fm<T>::sig(-to_f(zr[j])) * inv_tau);
+        }
+      }
+      __syncthreads();
+      T* gdq = static_cast<T*>(p.dq);
+      T* gdk = static_cast<T*>(p.dk_);
+      T* gdz = static_cast<T*>(p.dz);
+      T* gdv = static_cast<T*>(p.dv_);
+      T* gdr = static_cast<T*>(p.dr);
+      store_rows<T>(gdq + row0 * dk, (long)H * dk, rawq, dk, valid, dk, tid, kBwdThreads);
+      store_rows<T>(gdk + row0 * dk, (long)H * dk, rawk, dk, valid, dk, tid, kBwdThreads);
+      store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, kBwdThreads);
+      store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, kBwdThreads);
+      store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, kBwdThreads);
+    }
+    // the state bookkeeping moves one chunk down
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      s0n[m] = s0c[m];
+      if (n > c_first) s0c[m] = s0p[m];
+    }
+  }
+
+  if (FIN) {
+    // per-workgroup partial of dgamma, reduced in a fixed order by a second kernel
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      float v = dgam[E];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
+    }
+    __syncthreads();
+    for (int e = tid; e < dv; e += kBwdThreads)
+      p.dgamma_part[(long)blockIdx.x * dv + e] =
+          ((sDg[e] + sDg[DVP + e]) + sDg[2 * DVP + e]) + sDg[3 * DVP + e];
+  } else {
+    float* dst = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
+#pragma unroll
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = et * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ct * 16 + g4 * 4 + i;
+          if (c < dk && e < dv) dst[c * dv + e] = gacc[m][i];
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < dk; c += kBwdThreads)
+      p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
+  }
+}
+
+template <typename T, int DK, int DV, bool EXACT, int C>
+static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
+  const long BH = (long)s.B * s.H;
+  constexpr int fin_bytes = BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true>()>::bytes;
+  constexpr int a_bytes = BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false>()>::bytes;
+  if (lds_out) {
+    *lds_out = fin_bytes;
+    return hipSuccess;
+  }
+  if (!s.prefix && s.nseg > 1) {
+    hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false>),
+                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(kBwdThreads), a_bytes, st,
+                       p);
+    const hipError_t e = launch_gla_gstate_scan(s, p.gstates, p.seg_lg, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true>), dim3((unsigned)(BH * s.nseg)),
+                     dim3(kBwdThreads), fin_bytes, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, bool EXACT>
+static hipError_t launch_bwd_dims(const GlaShape& s, GlaBwdParams p, hipStream_t st,
+                                  int* lds_out) {
+  switch (s.C) {
+    case 16: return launch_bwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out);
+    case 32: return launch_bwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out);
+    case 64: return launch_bwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Same shape dispatch as the forward; lds_out != nullptr: only report the final pass's LDS.
+template <typename T>
+hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
+  if (s.dk == 32 && s.dv == 64) return launch_bwd_dims<T, 32, 64, true>(s, p, st, lds_out);
+  if (s.dk == 36 && s.dv == 72) return launch_bwd_dims<T, 36, 72, true>(s, p, st, lds_out);
+  if (s.dk == 16 && s.dv == 32) return launch_bwd_dims<T, 16, 32, true>(s, p, st, lds_out);
+  switch (s.ndk * 16 + s.ndv) {
+    case 1 * 16 + 2: return launch_bwd_dims<T, 16, 32, false>(s, p, st, lds_out);
+    case 2 * 16 + 4: return launch_bwd_dims<T, 32, 64, false>(s, p, st, lds_out);
+    case 3 * 16 + 5: return launch_bwd_dims<T, 48, 80, false>(s, p, st, lds_out);
+    case 4 * 16 + 8: return launch_bwd_dims<T, 64, 128, false>(s, p, st, lds_out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dig

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
   // read as zero and are never written afterwards
   for (int i = tid; i < Lo::O_RAW / 16; i += kFwdThreads)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();  // the zero fill is complete before anything below writes LDS
 
   f32x4 sacc[STW];
 #pragma unroll
