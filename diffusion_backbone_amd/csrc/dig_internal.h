@@ -15,7 +15,8 @@ struct GlaShape {
   int NC;                   // chunks per sequence = ceil(L / C)
   int sc;                   // chunks per segment
   int nseg;                 // segments per sequence = ceil(NC / sc)
-  int prefix;               // 1: each segment recomputes its incoming state (short sequences)
+  int prefix;               // forward: 1 = each segment recomputes its incoming state
+  int bprefix;              // backward: the same choice (its recompute is costlier)
   int ndk, ndv;             // compiled head-dim class: d_k <= 16*ndk, d_v <= 16*ndv
 };
 

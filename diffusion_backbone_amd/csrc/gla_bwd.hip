@@ -101,7 +101,7 @@ int gla_bwd_lds_bytes(const GlaShape& s) {
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
-  p.C = s.C; p.prefix = s.prefix;
+  p.C = s.C; p.prefix = s.bprefix;
   hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr)
                         : launch_gla_bwd_t<float>(s, p, st, nullptr);
   if (e != hipSuccess) return e;

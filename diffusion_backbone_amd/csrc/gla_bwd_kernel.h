@@ -816,7 +816,7 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
     *lds_out = fin_bytes;
     return hipSuccess;
   }
-  if (!s.prefix && s.nseg > 1) {
+  if (!s.bprefix && s.nseg > 1) {
     hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false>),
                        dim3((unsigned)(BH * (s.nseg - 1))), dim3(kBwdThreads), a_bytes, st,
                        p);

@@ -47,7 +47,12 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   if (sc < 1) sc = 1;
   s.sc = sc;
   s.nseg = (s.NC + sc - 1) / sc;
-  s.prefix = s.nseg <= 4;
+  // Recomputing earlier chunks in-workgroup beats the extra launches of the three-pass
+  // scheme only while the grid is at most one workgroup per compute unit (latency-bound)
+  // and there are few segments; the backward's recompute (a full output-stage backward per
+  // chunk) never pays off.
+  s.prefix = s.nseg <= 4 && (long)B * H * s.nseg <= 256;
+  s.bprefix = s.nseg <= 1;
   return s;
 }
 
