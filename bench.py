@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--quiet", action="store_true")
+    # profiling helpers (rocprofv3 counter runs): run only one library call of the step, or a
+    # plain device copy of known size that calibrates the byte counters
+    ap.add_argument("--pmc-target", choices=["gla_fwd", "gla_bwd", "srem_fwd", "srem_bwd"],
+                    default=None)
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
     return ap.parse_args()
 
 
@@ -159,6 +164,53 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ps) / max(len(ps), 1)
 
 
+# HBM traffic of one dig_gla_bwd call on the default workload, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (summed over the call's kernels) divided by the counters' reading per byte
+# of a plain copy; valid only for the kernel sources it was measured on (sha256 below).
+TRAFFIC = {
+    "call": "dig_gla_bwd",
+    "workload": "dig_s2_256",
+    "bytes": None,
+    "sources_sha256": None,
+}
+TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
+                   "diffusion_backbone_amd/csrc/gla_bwd.hip",
+                   "diffusion_backbone_amd/csrc/dig_device.h")
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Counter-derived bytes per call, or None when the kernels changed since the run."""
+    if TRAFFIC["bytes"] is None or workload != TRAFFIC["workload"]:
+        return None
+    return TRAFFIC["bytes"] if TRAFFIC["sources_sha256"] == sources_sha256() else None
+
+
+def copy_probe(mib, reps):
+    """A plain copy of known size through dig_srem_reorient (identity order): the reference
+    for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes."""
+    import torch
+    import diffusion_backbone_amd as dig
+    n = mib * 1024 * 1024 // 2
+    D = 1024
+    rows = n // D
+    x = torch.ones(rows * D, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dig.dig_srem_reorient(1, 1, rows, D, dig.DIG_BF16, dig.DIG_SCAN_ROW, dig.DIG_SCAN_ROW, x, y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": rows * D * 2, "reps": reps}), flush=True)
+
+
 def gla_bytes_per_token_head(cfg, which):
     """Algorithmic HBM bytes per (token, head) of one mixer call (bf16 I/O)."""
     dk, dv = cfg.d_k, cfg.d_v
@@ -207,11 +259,23 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, max(1, args.steps))
+        return
     cfg = W.CONFIGS[args.workload]
     nblocks = cfg.blocks
     blocks = gen_blocks(cfg, nblocks, cfg.seed)
     path = Path(cfg, blocks, args.seg_chunks)
     torch.cuda.synchronize()
+    if args.pmc_target:  # one library call per block, `steps` times (for counter runs)
+        fn = getattr(path, args.pmc_target)
+        for _ in range(args.steps):
+            for l in range(nblocks):
+                fn(l)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": args.pmc_target, "calls": args.steps * nblocks}),
+              flush=True)
+        return
 
     for _ in range(args.warmup):
         path.step()
@@ -249,11 +313,15 @@ def main():
         byts = gla_bytes_per_token_head(cfg, which) * th
         rl[name] = {"ms": t, "bytes": byts, "gbs": byts / (t / 1e3) / 1e9}
     dom = max(rl, key=lambda n: rl[n]["ms"])
+    traffic = measured_traffic(cfg.name) if dom == "gla_bwd" else None
     roof = {"bound": "hbm", "achieved": round(rl[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(rl[dom]["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gla_bwd_kernel" if dom == "gla_bwd" else "gla_fwd_kernel",
+            "unit": "GB/s", "frac": round(rl[dom]["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": ("gla_bwd_kernel (pass A + final pass) + gla_gstate_scan + gla_dgamma_reduce"
+                       if dom == "gla_bwd" else "gla_fwd_kernel"),
             "call": "dig_" + dom, "avg_call_us": round(rl[dom]["ms"] * 1e3, 2),
-            "algorithmic_bytes_per_launch": rl[dom]["bytes"]}
+            "algorithmic_bytes_per_launch": rl[dom]["bytes"],
+            "note": "per library call: HIP events bracket the whole call on its stream"}
     other = [n for n in rl if n != dom][0]
     out = {
         "metric": "GLA-layer tokens/s (fwd+bwd)",

@@ -154,6 +154,15 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// The same value, opaque to the optimiser (an empty asm statement that claims to modify the
+// register; no instruction is emitted).  Deriving a loop body's lane-dependent LDS addresses
+// from it keeps them from being hoisted out of the loop, where hundreds of them would stay
+// live across every phase and spill.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // ------------------------------------------------------------ wave primitives
 // Inclusive prefix sum over groups of `width` consecutive lanes (width a power of 2 <= 64).
 __device__ __forceinline__ float group_inclusive_scan(float x, int width, int lane_in_group) {

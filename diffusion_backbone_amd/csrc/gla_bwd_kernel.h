@@ -70,8 +70,9 @@ struct BwdLayout {
                                       ? (FIN ? C * TP * SZ : 0) : 4 * 16 * C * SZ;
   static constexpr int O_DT = O_PT + bal16(FIN ? C * TP * SZ : 0);
   // fp32 scratch
-  static constexpr int O_B = O_DT + bal16(DT_BYTES);                 // b, then q.dq-k.dk [C][DK]
-  static constexpr int O_GAM = O_B + bal16(C * DK * 4);              // e^{b_last}  [DKP]
+  static constexpr int O_B = O_DT + bal16(DT_BYTES);                 // b        [C][DK]
+  static constexpr int O_W = O_B + bal16(C * DK * 4);                // q.dq-k.dk [C][DK]
+  static constexpr int O_GAM = O_W + bal16(FIN ? C * DK * 4 : 0);    // e^{b_last}  [DKP]
   static constexpr int O_LG = O_GAM + bal16(DKP * 4);                // b_last / segment decay
   static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [4]
   static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
@@ -83,7 +84,7 @@ struct BwdLayout {
   static constexpr int R_K = R_Q + bal16(C * DK * SZ);
   static constexpr int R_Z = R_K + bal16(C * DK * SZ);
   static constexpr int R_V = R_Z + bal16(C * DK * SZ);
-  static constexpr int R_R = R_V + bal16(C * DV * SZ);
+  static constexpr int R_R = R_V + bal16(C * (DV > 2 * DK ? DV : 2 * DK) * SZ);  // v; dq|dk
   static constexpr int R_DY = R_R + bal16(C * DV * SZ);
   static constexpr int SLOT = R_DY + bal16(C * DV * SZ);
   static constexpr int bytes = O_RAW + SLOT;
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   T* sPt = reinterpret_cast<T*>(smem + Lo::O_PT);
   T* sDt = reinterpret_cast<T*>(smem + Lo::O_DT);
   float* sB = reinterpret_cast<float*>(smem + Lo::O_B);
-  float* sW = sB;  // q.dq - k.dk replaces b once dq, dk are formed
+  float* sW = reinterpret_cast<float*>(smem + Lo::O_W);  // q.dq - k.dk [C][DK]
   float* sGam = reinterpret_cast<float*>(smem + Lo::O_GAM);
   float* sLg = reinterpret_cast<float*>(smem + Lo::O_LG);
   float* sMax = reinterpret_cast<float*>(smem + Lo::O_MAX);
@@ -143,10 +144,12 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   float* sDg = reinterpret_cast<float*>(smem + Lo::O_DG);
   float* sDiag = reinterpret_cast<float*>(smem + Lo::O_DIAG);
   T* sSlow = reinterpret_cast<T*>(smem + Lo::O_DT);  // strong-decay P rows (recompute only)
-  T* rawq = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Q);  // then dq
-  T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);  // then dk
+  T* rawq = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Q);
+  T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);
   T* rawz = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Z);  // then dz
-  T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);
+  T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);  // then dq | dk
+  T* sdqs = rawv;
+  T* sdks = rawv + C * dk;
   T* sRr = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_R);   // r, then dr
   T* sDy = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_DY);  // dy, then dv
 
@@ -227,13 +230,30 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
   }
-  // S0 of the current chunk, and the state leaving it (S0 of the next chunk) for the
-  // boundary term; the latter is needed only where G is nonzero
-  f32x4 s0c[STW], s0n[STW];
-  load_state(n_top - 1, s0c);
+  // sum_e S_end (.) G per key column, the boundary term of dlog(alpha) of the chunk about to
+  // be processed: S_end is the saved state entering the next chunk up, G the gradient
+  // carried into the chunk's end (zero after the last chunk)
+  auto write_part = [&](const f32x4 (&se)[STW]) {
 #pragma unroll
-  for (int m = 0; m < STW; ++m) s0n[m] = zero4();
-  if (FIN && n_top < p.NC) load_state(n_top, s0n);
+    for (int m = 0; m < STW; ++m) {
+      const int u = wave + 4 * m;
+      if (u < NST) {
+        const int ct = u / NDV, et = u - ct * NDV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float part = row_sum16(se[m][i] * gacc[m][i]);
+          if (r16 == 0) sPart[et * DKP + ct * 16 + g4 * 4 + i] = part;
+        }
+      }
+    }
+  };
+  if (FIN && n_top < p.NC) {
+    f32x4 se[STW];
+    load_state(n_top, se);
+    write_part(se);
+  }
+  f32x4 s0c[STW];  // S0 of the current chunk
+  load_state(n_top - 1, s0c);
 
   float gm[NDV], dgam[NDV];
 #pragma unroll
@@ -246,6 +266,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   const int c0 = cg * NCL, e0 = cg * NEL;
 
   for (int n = n_top - 1; n >= c_first; --n) {
+    // per-iteration copies of the lane-dependent indices (see opaque())
+    const int lane = opaque(tid & 63);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int tg = (wave * 64 + lane) % C, cg = (wave * 64 + lane) / C;
+    const int c0 = cg * NCL, e0 = cg * NEL;
     const bool own = FIN && n < c_end;  // gradients of this chunk are this workgroup's output
     const int t0 = n * C;
     const int valid = min(C, p.L - t0);
@@ -392,6 +417,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
           const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
           float acc = 0.f;
           if (j <= ir && ir < valid) {
+#pragma unroll 1
             for (int c = 0; c < dk; ++c)
               acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
                      Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
@@ -574,27 +600,15 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
           lds_row_write<T, 4>(sDt + (16 * J + r16) * TP, 16 * I + 4 * g4, dt4);
         }
       }
-      // sum_e S_end (.) G per key column (S_end = S0 of the next chunk; G = 0 after the last)
-#pragma unroll
-      for (int m = 0; m < STW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NST) {
-          const int ct = u / NDV, et = u - ct * NDV;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float part = row_sum16(s0n[m][i] * gacc[m][i]);
-            if (r16 == 0) sPart[et * DKP + ct * 16 + g4 * 4 + i] = part;
-          }
-        }
-      }
       __syncthreads();
 
-      // ---- dq, dk (registers), dv (staged over dy)
-      f32x4 dqa[PRW], dka[PRW];
+      // ---- dq, dk, q.dq - k.dk (staged as soon as each (row tile, key tile) pair is done:
+      // dq | dk over the raw v rows, which are no longer read) and dv (over dy, read only in
+      // the recompute phase)
 #pragma unroll
       for (int m = 0; m < PRW; ++m) {
-        dqa[m] = zero4();
-        dka[m] = zero4();
+        // one pair at a time: keeps later pairs' operand fragments from being hoisted
+        __builtin_amdgcn_sched_barrier(0);
         const int u = wave + 4 * m;
         if (u < NPAIR) {
           const int I = u / NDK, ct = u - I * NDK;
@@ -614,93 +628,63 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
               a2 = Mma<T>::kc(zero4(), sD, TP, 16 * I, sKt, TP, 16 * ct, C, lane);
             a4 = Mma<T>::kc(zero4(), sDt, TP, 16 * I, sQt, TP, 16 * ct, C, lane);
           }
+          const int c = ct * 16 + r16;
+          if (FULLK || c < dk) {
+            const float blast = sLg[c];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * I + 4 * g4 + i, c = ct * 16 + r16;
-            float dq = 0.f, dkk = 0.f;
-            if (FULLK || c < dk) {
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * I + 4 * g4 + i;
               const float bt = sB[t * DK + c];
-              const float blast = sLg[c];
+              float dq, dkk;
               if (!slow) {  // a3 holds V (e^{b_last} G)^T here
                 dq = Fm<T>::exp2(bt) * (a1[i] + a2[i]);
                 dkk = Fm<T>::exp2(-bt) * (a4[i] + a3[i]);
               } else {  // a3 holds V G^T here
                 float s1 = 0.f, s2 = 0.f;
+#pragma unroll 1
                 for (int j = 0; j <= t && j < valid; ++j)
                   s1 += to_f(LEAN ? sDt[j * TP + t] : sD[t * TP + j]) * to_f(rawk[j * dk + c]) *
                         Fm<T>::exp2(bt - sB[j * DK + c]);
+#pragma unroll 1
                 for (int i2 = t; i2 < valid; ++i2)
                   s2 += to_f(sDt[t * TP + i2]) * to_f(rawq[i2 * dk + c]) * p.q_scale *
                         Fm<T>::exp2(sB[i2 * DK + c] - bt);
                 dq = Fm<T>::exp2(bt) * a1[i] + s1;
                 dkk = s2 + Fm<T>::exp2(blast - bt) * a3[i];
               }
+              const float qf = to_f(rawq[t * dk + c]) * p.q_scale, kf = to_f(rawk[t * dk + c]);
+              sW[t * DK + c] = qf * dq - kf * dkk;
+              sdqs[t * dk + c] = from_f<T>(p.q_scale * dq);
+              sdks[t * dk + c] = from_f<T>(dkk);
             }
-            dqa[m][i] = dq;
-            dka[m][i] = dkk;
           }
         }
       }
-      f32x4 dva[DVW];
 #pragma unroll
       for (int m = 0; m < DVW; ++m) {
-        dva[m] = zero4();
+        __builtin_amdgcn_sched_barrier(0);
         const int u = wave + 4 * m;
         if (u < NDVT) {
           const int J = u / NDV, et = u - J * NDV;
-          dva[m] = Mma<T>::kc(zero4(), sPt, TP, 16 * J, sdOt, TP, 16 * et, C, lane);
+          f32x4 dva = Mma<T>::kc(zero4(), sPt, TP, 16 * J, sdOt, TP, 16 * et, C, lane);
+          const int e = et * 16 + r16;
           if (!slow) {
-            dva[m] = Mma<T>::kc(dva[m], sK, QP, 16 * J, sGt, QP, 16 * et, DKP, lane);
+            dva = Mma<T>::kc(dva, sK, QP, 16 * J, sGt, QP, 16 * et, DKP, lane);
           } else {  // k_j e^{b_last - b_j} G elementwise (no overflow)
-            const int e = et * 16 + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int j = 16 * J + 4 * g4 + i;
               float acc = 0.f;
+#pragma unroll 1
               for (int c = 0; c < dk; ++c)
                 acc += to_f(rawk[j * dk + c]) * Fm<T>::exp2(sLg[c] - sB[j * DK + c]) *
                        to_f(sGt[e * QP + c]);
-              dva[m][i] += acc;
+              dva[i] += acc;
             }
           }
-        }
-      }
-      __syncthreads();  // all reads of sB, raw q/k and dy done
-
-      // ---- q.dq - k.dk over b; dq, dk over raw q, k; dv over dy
-#pragma unroll
-      for (int m = 0; m < PRW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NPAIR) {
-          const int I = u / NDK, ct = u - I * NDK;
-          const int c = ct * 16 + r16;
-          if (FULLK || c < dk) {
-            T qv[4], kv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 16 * I + 4 * g4 + i;
-              qv[i] = rawq[t * dk + c];
-              kv[i] = rawk[t * dk + c];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 16 * I + 4 * g4 + i;
-              sW[t * DK + c] = to_f(qv[i]) * p.q_scale * dqa[m][i] - to_f(kv[i]) * dka[m][i];
-              rawq[t * dk + c] = from_f<T>(p.q_scale * dqa[m][i]);
-              rawk[t * dk + c] = from_f<T>(dka[m][i]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < DVW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NDVT) {
-          const int J = u / NDV, et = u - J * NDV;
-          const int e = et * 16 + r16;
           if (FULLV || e < dv) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * dv + e] = from_f<T>(dva[m][i]);
+            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * dv + e] = from_f<T>(dva[i]);
           }
         }
       }
@@ -759,17 +743,19 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       T* gdz = static_cast<T*>(p.dz);
       T* gdv = static_cast<T*>(p.dv_);
       T* gdr = static_cast<T*>(p.dr);
-      store_rows<T>(gdq + row0 * dk, (long)H * dk, rawq, dk, valid, dk, tid, kBwdThreads);
-      store_rows<T>(gdk + row0 * dk, (long)H * dk, rawk, dk, valid, dk, tid, kBwdThreads);
+      store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, kBwdThreads);
+      store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, kBwdThreads);
       store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, kBwdThreads);
       store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, kBwdThreads);
       store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, kBwdThreads);
     }
-    // the state bookkeeping moves one chunk down
+    // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
+    // its S0 (read by nobody before the next top barrier; sPart's last reader, this chunk's
+    // dlog phase, is behind the barrier above)
+    if (n > c_first) {
+      if (FIN) write_part(s0c);
 #pragma unroll
-    for (int m = 0; m < STW; ++m) {
-      s0n[m] = s0c[m];
-      if (n > c_first) s0c[m] = s0p[m];
+      for (int m = 0; m < STW; ++m) s0c[m] = s0p[m];
     }
   }
 

@@ -183,6 +183,11 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
   const int c0 = cg * NCL, e0 = cg * NEL;
 
   for (int n = n_begin; n < c_end; ++n) {
+    // per-iteration copies of the lane-dependent indices (see opaque())
+    const int lane = opaque(tid & 63);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int tg = (wave * 64 + lane) % C, cg = (wave * 64 + lane) / C;
+    const int c0 = cg * NCL, e0 = cg * NEL;
     const int it = n - n_begin;
     const int slot = nbuf == 2 ? (it & 1) : 0;
     unsigned char* raw = smem + Lo::O_RAW + slot * Lo::SLOT;
@@ -351,6 +356,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
           const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
           float acc = 0.f;
           if (j <= ir) {
+#pragma unroll 1
             for (int c = 0; c < dk; ++c)
               acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
                      Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
