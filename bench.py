@@ -170,8 +170,10 @@ class EventTimer:
 TRAFFIC = {
     "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    "bytes": None,
-    "sources_sha256": None,
+    # FETCH_SIZE 12006.1 KiB / 0.50017 (copy: 131116.8 KiB read per 262144 KiB moved) +
+    # WRITE_SIZE 8132.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
+    "bytes": 32907259,
+    "sources_sha256": "a4e2e60c31b7174876bb1c23036c2d8ee9ee3881959c4017c8094f7c473df557",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
