@@ -536,6 +536,47 @@ __device__ __forceinline__ void dma_tile(T* lds_dst, const T* gsrc, long gstride
     dma_pieces<2>(d, s, gs, rowbytes >> 1, valid * (rowbytes >> 1), wave, nwaves, lane);
 }
 
+// ------------------------------------------------------- register prefetch of raw rows
+// ROWS rows of RB bytes each (row r at gsrc + r * gstride bytes) held in VGPRs, shared by NTH
+// threads in pieces of 16, 8 or 4 bytes (the largest dividing RB).  load() starts ordinary
+// vector loads (rows >= valid read as zero); put() writes the rows packed (pitch RB) to LDS.
+// Unlike an LDS DMA, nothing in between has to wait for these loads: the wait lands at put().
+template <int PB> struct PieceType;
+template <> struct PieceType<16> { using type = uint4; };
+template <> struct PieceType<8> { using type = uint2; };
+template <> struct PieceType<4> { using type = unsigned; };
+
+template <int RB, int ROWS, int NTH>
+struct RowRegs {
+  static_assert(RB % 4 == 0, "rows must be a whole number of dwords");
+  static constexpr int PB = RB % 16 == 0 ? 16 : (RB % 8 == 0 ? 8 : 4);
+  static constexpr int PR = RB / PB;                     // pieces per row
+  static constexpr int NPC = ROWS * PR;                  // pieces in the tile
+  static constexpr int NP = (NPC + NTH - 1) / NTH;       // pieces per thread
+  using P = typename PieceType<PB>::type;
+  P v[NP];
+  // Branch-free on purpose (a branch around a load makes the compiler's wait analysis
+  // pessimistic): threads past the last piece repeat it, and rows >= valid load row valid-1
+  // and are replaced by zeros in put().
+  __device__ __forceinline__ void load(const unsigned char* gsrc, long gstride, int valid,
+                                       int tid) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int e = min(tid + NTH * m, NPC - 1), r = e / PR, c = e - r * PR;
+      v[m] = *reinterpret_cast<const P*>(gsrc + (long)min(r, valid - 1) * gstride + c * PB);
+    }
+  }
+  __device__ __forceinline__ void put(unsigned char* lds, int valid, int tid) const {
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+      const int e = min(tid + NTH * m, NPC - 1), r = e / PR, c = e - r * PR;
+      P x = v[m];
+      if (r >= valid) x = P{};
+      *reinterpret_cast<P*>(lds + r * RB + c * PB) = x;
+    }
+  }
+};
+
 // Waits for this wave's outstanding memory operations (LDS DMA included).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -20,9 +20,11 @@
 //           k e^{-b}, (k e^{b_last-b})^T and V^T written to LDS;
 //   product every wave advances its share of the fp32 state tiles; wave I owns query rows
 //           16I..16I+15: gated Q K^T (kept in registers), P V, (q e^{b}) S0, the RMSNorm x
-//           Swish epilogue (y written over r in LDS, then stored as whole rows).
-// The raw rows of the next chunk are copied global->LDS (LDS DMA) while the current one is
-// being processed (two staging slots when LDS allows).
+//           Swish epilogue, y stored straight from the accumulators.
+// Exact head shapes load the raw rows of the next chunk into registers while the current one
+// is processed and write them to the one staging slot at the top of the next iteration (an
+// LDS DMA would make every LDS read of the current chunk wait for the copy).  Tile classes
+// copy global->LDS by DMA (two staging slots when LDS allows).
 //
 // Head dims: DK x DV is either the exact shape (compile-time dims, no guards) or a 16-wide
 // tile class holding any smaller runtime shape (EXACT = false), zero-padded inside LDS.
@@ -56,12 +58,15 @@ struct FwdLayout {
   static constexpr int O_KBT = O_K + al16(OUT ? C * QP * SZ : 0);        // kbar^T [16NDK][TP]
   static constexpr int O_VT = O_KBT + al16(16 * NDK * TP * SZ);          // v^T    [DVP][TP]
   static constexpr int O_S = O_VT + al16(DVP * TP * SZ);                 // S^T    [DVP][QP]
-  static constexpr int O_B = O_S + al16(OUT ? DVP * QP * SZ : 0);        // b fp32 [C][DK]
-  static constexpr int O_GAM = O_B + al16(OUT ? C * DK * 4 : 0);         // e^{b_last} [DKP]
+  // b fp32 [C][DK], written only for strong-decay chunks, which do not read k e^{-b}: it
+  // takes that tile's place when it fits there
+  static constexpr bool B_IN_K = C * DK * 4 <= C * QP * SZ;
+  static constexpr int O_B = B_IN_K ? O_K : O_S + al16(OUT ? DVP * QP * SZ : 0);
+  static constexpr int O_GAM = O_S + al16(OUT ? DVP * QP * SZ : 0) +
+                               al16(OUT && !B_IN_K ? C * DK * 4 : 0);  // e^{b_last} [DKP]
   static constexpr int O_LG = O_GAM + al16(DKP * 4);                     // segment decay
   static constexpr int O_MAX = O_LG + al16(DKP * 4);                     // per-wave decay
-  static constexpr int O_P = O_MAX + 64;                                 // slow P [4][16][C]
-  static constexpr int O_RAW = O_P + al16(OUT ? 4 * 16 * C * 4 : 0);
+  static constexpr int O_RAW = O_MAX + 64;
   // one staging slot: raw k, z, v (+ q, r) rows, packed with the runtime row length
   static constexpr int R_K = 0;
   static constexpr int R_Z = R_K + al16(C * DK * SZ);
@@ -86,6 +91,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
   using Acc = typename std::conditional<kBf, float, double>::type;
+  constexpr bool PF = EXACT;  // register prefetch (one staging slot) for exact head shapes
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -106,7 +112,6 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
   float* sGam = reinterpret_cast<float*>(smem + Lo::O_GAM);
   float* sLg = reinterpret_cast<float*>(smem + Lo::O_LG);
   float* sMax = reinterpret_cast<float*>(smem + Lo::O_MAX);
-  float* sP = reinterpret_cast<float*>(smem + Lo::O_P);
 
   const int c_first = seg * p.sc;
   const int c_end = min(p.NC, c_first + p.sc);
@@ -143,7 +148,33 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
                  rbv, valid, wave, 4, lane);
     }
   };
-  issue(n_begin, 0);  // the first chunk's copy overlaps the set-up below
+  // exact shapes: the raw rows of a chunk in registers (loaded one iteration ahead)
+  RowRegs<DK * (int)sizeof(T), C, kFwdThreads> pk, pz, pq;
+  RowRegs<DV * (int)sizeof(T), C, kFwdThreads> pv, pr;
+  auto pf_load = [&](int n) {
+    const int t0 = n * C, valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;
+    const long gsk = (long)H * DK * sizeof(T), gsv = (long)H * DV * sizeof(T);
+    pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
+    pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
+    pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
+    if (OUT && n >= c_first) {
+      pq.load(reinterpret_cast<const unsigned char*>(gq + row0 * DK), gsk, valid, tid);
+      pr.load(reinterpret_cast<const unsigned char*>(gr + row0 * DV), gsv, valid, tid);
+    }
+  };
+  auto pf_put = [&](int n, unsigned char* base) {
+    const int valid = min(C, p.L - n * C);
+    pk.put(base + Lo::R_K, valid, tid);
+    pz.put(base + Lo::R_Z, valid, tid);
+    pv.put(base + Lo::R_V, valid, tid);
+    if (OUT && n >= c_first) {
+      pq.put(base + Lo::R_Q, valid, tid);
+      pr.put(base + Lo::R_R, valid, tid);
+    }
+  };
+  if constexpr (PF) pf_load(n_begin);
+  else issue(n_begin, 0);  // the first chunk's copy overlaps the set-up below
 
   // zero everything but the staging slots: padding rows/columns of the MFMA operands must
   // read as zero and are never written afterwards
@@ -177,6 +208,9 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     const int e = E * 16 + r16;
     gm[E] = (OUT && e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
   }
+  // Every load above (and the first chunk's rows) has landed before the loop: otherwise the
+  // compiler's wait for them, placed inside the loop, would also wait for the prefetch.
+  if constexpr (PF) dma_wait();
 
   // gate-pass lane roles: token tg of the chunk, key columns c0.., value columns e0..
   const int tg = tid % C, cg = tid / C;
@@ -195,13 +229,15 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     const T* rawz = reinterpret_cast<const T*>(raw + Lo::R_Z);
     const T* rawv = reinterpret_cast<const T*>(raw + Lo::R_V);
     const T* rawq = reinterpret_cast<const T*>(raw + Lo::R_Q);
-    T* sR = reinterpret_cast<T*>(raw + Lo::R_R);
+    const T* sR = reinterpret_cast<const T*>(raw + Lo::R_R);
     const bool emit = OUT && n >= c_first;
     const int t0 = n * C;
     const int valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;  // (b, t0, h) as a token-head row
 
-    if (nbuf == 1 && it > 0) {  // single slot: wait until the previous chunk left it
+    if constexpr (PF) {
+      pf_put(n, raw);  // the previous chunk's last reads of the slot preceded the last barrier
+    } else if (nbuf == 1 && it > 0) {  // single slot: wait until the previous chunk left it
       __syncthreads();
       issue(n, 0);
     }
@@ -234,12 +270,17 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
         }
       }
     }
-    dma_wait();
+    if constexpr (!PF) dma_wait();
     __syncthreads();
-    if (nbuf == 2 && n + 1 < c_end) issue(n + 1, slot ^ 1);
+    if constexpr (PF) {
+      if (n + 1 < c_end) pf_load(n + 1);
+    } else if (nbuf == 2 && n + 1 < c_end) {
+      issue(n + 1, slot ^ 1);
+    }
 
     // ---------------------------------------------------------------- gate phase
     // (every LDS read first, then the arithmetic, then every write: one LDS round trip)
+    float bb[NCL];  // in-chunk cumulative log2 gates of token tg, key columns c0..
     {
       const bool tv = tg < valid;
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
@@ -255,7 +296,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
       if constexpr (FULLV) lds_row_read_k<T, NEL, DV>(vr, rawv + tg * DV, e0, tv);
       else lds_row_read<T, NEL>(vr, rawv + tg * dv, e0, dv, tv);
 
-      float bb[NCL], bl[NCL];
+      float bl[NCL];
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
         const bool on = FULLK ? tv : (tv && c0 + j < dk);
@@ -288,9 +329,6 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
       if (emit) {
         lds_row_write<T, NCL>(sQ + tg * QP, c0, qs);
         lds_row_write<T, NCL>(sK + tg * QP, c0, ks);
-#pragma unroll
-        for (int j = 0; j < NCL; ++j)
-          if (FULLK || c0 + j < dk) sB[tg * DK + c0 + j] = bb[j];
         if (lane == 0) sMax[wave] = md;
       }
       if (tg == C - 1) {
@@ -302,6 +340,20 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
       }
     }
     __syncthreads();
+
+    // strong decay somewhere in the chunk (uniform over the workgroup): the gated Q K^T is
+    // evaluated elementwise from b, which is written now (over k e^{-b} when it fits there)
+    bool slow = false;
+    if (emit) {
+      const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
+      slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kSlowDecayLog2;
+    }
+    if (slow) {
+#pragma unroll
+      for (int j = 0; j < NCL; ++j)
+        if (FULLK || c0 + j < dk) sB[tg * DK + c0 + j] = bb[j];
+      __syncthreads();
+    }
 
     // ------------------------------------------------------------- product phase
     // state carry first (independent of the outputs): S = diag(e^{b_last}) S + Kbar^T V
@@ -319,8 +371,6 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
 
     if (emit && wave < NT) {
       const int I = wave;  // this wave's 16 query rows
-      const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
-      const bool slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kSlowDecayLog2;
       // exact diagonal q_i.k_i (gate factor 1) from the unscaled inputs, so that a
       // cancelling dot product keeps its relative accuracy: 16 rows x 4 column groups
       float diag;
@@ -349,25 +399,25 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
         for (int J = 0; J < NT; ++J)
           pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
       } else {
-        // strong decay: P_ij = sum_c q_ic k_jc 2^{b_ic - b_jc} elementwise (no overflow), via a
-        // per-wave LDS tile (rare path, kept compact)
-        float* sPw = sP + wave * 16 * C;
-        for (int idx = lane; idx < 16 * C; idx += 64) {
-          const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
-          float acc = 0.f;
-          if (j <= ir) {
+        // strong decay: P_ij = sum_c q_ic k_jc 2^{b_ic - b_jc} elementwise (no overflow), each
+        // lane its own elements (rare path, kept compact); j > i is masked below
+        const int ir = 16 * I + r16;
+#pragma unroll
+        for (int J = 0; J < NT; ++J) pt[J] = zero4();
 #pragma unroll 1
-            for (int c = 0; c < dk; ++c)
-              acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
-                     Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
-            acc *= p.q_scale;
+        for (int c = 0; c < dk; ++c) {
+          const float qc = to_f(rawq[ir * dk + c]) * p.q_scale, bq = sB[ir * DK + c];
+#pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            if (J <= I) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int j = 16 * J + 4 * g4 + i;
+                pt[J][i] += qc * to_f(rawk[j * dk + c]) * Fm<T>::exp2(bq - sB[j * DK + c]);
+              }
+            }
           }
-          sPw[idx] = acc;
         }
-#pragma unroll
-        for (int J = 0; J < NT; ++J)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pt[J][i] = sPw[r16 * C + 16 * J + 4 * g4 + i];
       }
 #pragma unroll
       for (int J = 0; J < NT; ++J) {  // diagonal tile: causal mask and the exact diagonal
@@ -428,7 +478,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
         }
       }
 
-      // output stage: head-wise RMSNorm x weight x Swish(r); y written over r in LDS
+      // output stage: head-wise RMSNorm x weight x Swish(r), stored from the accumulators
       T rr[NDV][4];  // all of this lane's r first (one LDS round trip)
 #pragma unroll
       for (int E = 0; E < NDV; ++E)
@@ -453,16 +503,17 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
           for (int i = 0; i < 4; ++i) {
             const int row = 16 * I + 4 * g4 + i;
             const float o = oacc[E][i];
-            if (gop && row < valid) gop[(row0 + (long)row * H) * dv + e] = from_f<T>(o);
             const float rv = to_f(rr[E][i]);
-            sR[row * dv + e] = from_f<T>(o * rstd[i] * gm[E] * rv * Fm<T>::sig(rv));
+            if (row < valid) {
+              const long off = (row0 + (long)row * H) * dv + e;
+              if (gop) gop[off] = from_f<T>(o);
+              gy[off] = from_f<T>(o * rstd[i] * gm[E] * rv * Fm<T>::sig(rv));
+            }
           }
         }
       }
     }
-    __syncthreads();
-
-    if (emit) store_rows<T>(gy + row0 * dv, (long)H * dv, sR, dv, valid, dv, tid, kFwdThreads);
+    __syncthreads();  // every read of the staging slot and of S^T is done
   }
 
   if (!OUT) {
@@ -486,13 +537,13 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
   }
 }
 
-// LDS bytes and staging slots of one launch.  Two slots (prefetch of the next chunk) when a
-// workgroup walks more than one chunk and they fit.
-template <typename T, int DK, int DV, int C, bool OUT>
+// LDS bytes and staging slots of one launch.  Exact shapes prefetch into registers (one
+// slot); tile classes use two DMA slots when a workgroup walks more than one chunk and they fit.
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
 static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
   using Lo = FwdLayout<T, DK, DV, C, OUT>;
   const int walk = (OUT && s.prefix) ? s.NC : s.sc;
-  *nbuf = (walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
+  *nbuf = (!EXACT && walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
   *bytes = Lo::bytes(*nbuf);
 }
 
@@ -500,14 +551,14 @@ template <typename T, int DK, int DV, bool EXACT, int C>
 static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
   const long BH = (long)s.B * s.H;
   int bytes_c, nbuf_c;
-  fwd_lds<T, DK, DV, C, true>(s, &bytes_c, &nbuf_c);
+  fwd_lds<T, DK, DV, EXACT, C, true>(s, &bytes_c, &nbuf_c);
   if (lds_out) {  // size query only
     *lds_out = bytes_c;
     return hipSuccess;
   }
   if (!s.prefix && s.nseg > 1) {
     int bytes_a, nbuf_a;
-    fwd_lds<T, DK, DV, C, false>(s, &bytes_a, &nbuf_a);
+    fwd_lds<T, DK, DV, EXACT, C, false>(s, &bytes_a, &nbuf_a);
     hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false>),
                        dim3((unsigned)(BH * (s.nseg - 1))), dim3(kFwdThreads), bytes_a, st, p,
                        nbuf_a);
