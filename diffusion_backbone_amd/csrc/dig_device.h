@@ -577,6 +577,24 @@ struct RowRegs {
   }
 };
 
+// Rows [0, valid) of a packed LDS tile (pitch RB bytes) stored to global rows `gstride`
+// bytes apart, branch-free with a fixed number of stores per thread (so the compiler can
+// count them when it waits for loads issued earlier): threads past the last piece repeat it
+// and rows >= valid repeat row valid-1, i.e. the same bytes to the same address.
+template <int RB, int ROWS, int NTH>
+__device__ __forceinline__ void store_rows_fixed(unsigned char* gdst, long gstride,
+                                                 const unsigned char* lds, int valid, int tid) {
+  using R = RowRegs<RB, ROWS, NTH>;
+  using P = typename R::P;
+#pragma unroll
+  for (int m = 0; m < R::NP; ++m) {
+    const int e = min(tid + NTH * m, R::NPC - 1), c = e % R::PR;
+    const int r = min(e / R::PR, valid - 1);
+    *reinterpret_cast<P*>(gdst + (long)r * gstride + c * R::PB) =
+        *reinterpret_cast<const P*>(lds + r * RB + c * R::PB);
+  }
+}
+
 // Waits for this wave's outstanding memory operations (LDS DMA included).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -26,8 +26,9 @@
 //   D         dO V^T tiles (row and transposed), the boundary term of dlog(alpha);
 //   grads     dq, dk (row tile x key tile pairs), dv, and the carried G;
 //   dlog      lanes = tokens in reverse: suffix sums of q.dq - k.dk as a DPP scan -> dz.
-// Chunks that only carry G (later chunks recomputed in the same workgroup, or pass A of the
-// three-pass scheme) run gate, recompute and the G update only.
+// Pass A of the three-pass scheme (chunks that only carry G) runs gate, recompute and the G
+// update only.  Exact head shapes load the next chunk's raw rows into registers while the
+// current one is processed; tile classes copy them global->LDS after the chunk is done.
 #pragma once
 
 #include <type_traits>
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
   using Acc = typename std::conditional<kBf, float, double>::type;
+  constexpr bool PF = EXACT;  // register prefetch of the next chunk's raw rows
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
 
   const int c_first = seg * p.sc;
   const int c_end = min(p.NC, c_first + p.sc);
-  const int n_top = (FIN && p.prefix) ? p.NC : c_end;  // later chunks recomputed for G
-  const bool scanned = !p.prefix && p.nseg > 1;
+  const int n_top = c_end;
+  const bool scanned = p.nseg > 1;  // G entering the segment's end comes from the scan
   const long sbase = (long)bh * p.NC;
   const float inv_tau = p.g2scale * 0.69314718055994531f;  // g2scale = log2(e) / tau
 
@@ -187,8 +189,21 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
                rbv, valid, wave, 4, lane);
   };
   // this lane's elements of the fp32 state tiles of chunk n (the saved forward states)
+  // (exact shapes: branch-free, padding positions hold clamped copies that are masked where
+  // the state becomes an MFMA operand; they only meet zeros elsewhere)
   auto load_state = [&](int n, f32x4 (&dst)[STW]) {
     const float* src = p.states + (sbase + n) * dk * dv;
+    if constexpr (PF) {
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = min(wave + 4 * m, NST - 1);
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = min(et * 16 + r16, DV - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[m][i] = src[min(ct * 16 + g4 * 4 + i, DK - 1) * DV + e];
+      }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
       dst[m] = zero4();
@@ -205,7 +220,31 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     }
   };
 
-  issue(n_top - 1);
+  RowRegs<DK * (int)sizeof(T), C, kBwdThreads> pq, pk, pz;
+  RowRegs<DV * (int)sizeof(T), C, kBwdThreads> pv, pr, pdy;
+  auto pf_load = [&](int n) {
+    const int t0 = n * C, valid = min(C, p.L - t0);
+    const long row0 = ((long)b * p.L + t0) * H + h;
+    const long gsk = (long)H * DK * sizeof(T), gsv = (long)H * DV * sizeof(T);
+    pq.load(reinterpret_cast<const unsigned char*>(gq + row0 * DK), gsk, valid, tid);
+    pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
+    pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
+    pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
+    pr.load(reinterpret_cast<const unsigned char*>(gr + row0 * DV), gsv, valid, tid);
+    pdy.load(reinterpret_cast<const unsigned char*>(gdy + row0 * DV), gsv, valid, tid);
+  };
+  auto pf_put = [&](int n) {
+    unsigned char* base = smem + Lo::O_RAW;
+    const int valid = min(C, p.L - n * C);
+    pq.put(base + Lo::R_Q, valid, tid);
+    pk.put(base + Lo::R_K, valid, tid);
+    pz.put(base + Lo::R_Z, valid, tid);
+    pv.put(base + Lo::R_V, valid, tid);
+    pr.put(base + Lo::R_R, valid, tid);
+    pdy.put(base + Lo::R_DY, valid, tid);
+  };
+  if constexpr (PF) pf_load(n_top - 1);
+  else issue(n_top - 1);
   for (int i = tid; i < Lo::O_RAW / 16; i += kBwdThreads)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
@@ -264,6 +303,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   }
   const int tg = tid % C, cg = tid / C;
   const int c0 = cg * NCL, e0 = cg * NEL;
+  // Every load above has landed before the loop: otherwise the compiler's wait for them,
+  // placed inside the loop, would also wait for the prefetch.
+  if constexpr (PF) dma_wait();
 
   for (int n = n_top - 1; n >= c_first; --n) {
     // per-iteration copies of the lane-dependent indices (see opaque())
@@ -271,11 +313,14 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     const int r16 = lane & 15, g4 = lane >> 4;
     const int tg = (wave * 64 + lane) % C, cg = (wave * 64 + lane) / C;
     const int c0 = cg * NCL, e0 = cg * NEL;
-    const bool own = FIN && n < c_end;  // gradients of this chunk are this workgroup's output
+    constexpr bool own = FIN;  // the final pass emits every chunk it walks
     const int t0 = n * C;
     const int valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
-    if (n < n_top - 1) {
+    if constexpr (PF) {
+      if (n < n_top - 1) __syncthreads();  // the single staging slot is free again
+      pf_put(n);
+    } else if (n < n_top - 1) {
       __syncthreads();  // the single staging slot is free again
       issue(n);
     }
@@ -290,16 +335,20 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
         T sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sv[i] = from_f<T>(s0c[m][i]);
+          const bool in = FULLK && FULLV ? true : (ct * 16 + g4 * 4 + i < dk && e < dv);
+          sv[i] = from_f<T>(in ? s0c[m][i] : 0.f);
           if constexpr (!LEAN) sS0[(ct * 16 + g4 * 4 + i) * VP + e] = sv[i];
         }
         lds_row_write<T, 4>(sS0t + e * QP, ct * 16 + g4 * 4, sv);
       }
     }
-    dma_wait();
+    if constexpr (!PF) dma_wait();
     __syncthreads();
     f32x4 s0p[STW];  // prefetch S0 of the next chunk down (consumed at the next top)
-    if (n > c_first) load_state(n - 1, s0p);
+    if (n > c_first) {
+      if constexpr (PF) pf_load(n - 1);
+      load_state(n - 1, s0p);
+    }
 
     // ---------------------------------------------------------------- gate phase
     {
@@ -743,11 +792,26 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       T* gdz = static_cast<T*>(p.dz);
       T* gdv = static_cast<T*>(p.dv_);
       T* gdr = static_cast<T*>(p.dr);
-      store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, kBwdThreads);
-      store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, kBwdThreads);
-      store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, kBwdThreads);
-      store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, kBwdThreads);
-      store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, kBwdThreads);
+      if constexpr (PF) {
+        constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
+        using UC = unsigned char;
+        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
+                                             reinterpret_cast<const UC*>(sdqs), valid, tid);
+        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
+                                             reinterpret_cast<const UC*>(sdks), valid, tid);
+        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
+                                             reinterpret_cast<const UC*>(rawz), valid, tid);
+        store_rows_fixed<RV, C, kBwdThreads>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
+                                             reinterpret_cast<const UC*>(sDy), valid, tid);
+        store_rows_fixed<RV, C, kBwdThreads>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
+                                             reinterpret_cast<const UC*>(sRr), valid, tid);
+      } else {
+        store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, kBwdThreads);
+        store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, kBwdThreads);
+        store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, kBwdThreads);
+        store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, kBwdThreads);
+        store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, kBwdThreads);
+      }
     }
     // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
     // its S0 (read by nobody before the next top barrier; sPart's last reader, this chunk's
