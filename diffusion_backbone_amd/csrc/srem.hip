@@ -476,6 +476,126 @@ __global__ __launch_bounds__(256) void dwconv_dw_tiled_kernel(const T* __restric
   }
 }
 
+// ------------------------------------------------------------ column-strip conv
+// Position of the token at current-grid (i, j) in another scan order: an affine function
+// A + Bi i + Bj j of the grid indices (each scan order is a flip and/or transpose of the
+// canonical row-major grid), so the fused reorient costs no division in the kernel.
+struct GridMap {
+  long A, Bi, Bj;
+};
+static GridMap grid_map(int gh, int gw, int layout, int out_layout) {
+  const long L = (long)gh * gw;
+  // canonical (ci, cj) of current-grid (i, j): ci = c0 + cii i + cij j, cj = d0 + dji i + djj j
+  long c0 = 0, cii = 0, cij = 0, d0 = 0, dji = 0, djj = 0;
+  switch (layout) {
+    case kRow: cii = 1; djj = 1; break;
+    case kRowRev: c0 = gh - 1; cii = -1; d0 = gw - 1; djj = -1; break;
+    case kCol: cij = 1; dji = 1; break;
+    default: c0 = gh - 1; cij = -1; d0 = gw - 1; dji = -1; break;
+  }
+  // position in out_layout of canonical (ci, cj): o0 + oi ci + oj cj
+  long o0 = 0, oi = 0, oj = 0;
+  switch (out_layout) {
+    case kRow: oi = gw; oj = 1; break;
+    case kRowRev: o0 = L - 1; oi = -gw; oj = -1; break;
+    case kCol: oi = 1; oj = gh; break;
+    default: o0 = L - 1; oi = -1; oj = -gh; break;
+  }
+  return GridMap{o0 + oi * c0 + oj * d0, oi * cii + oj * dji, oi * cij + oj * djj};
+}
+
+// One block: a strip of 16 current-grid columns x RH rows x one slab of 16 channel groups
+// (16 bytes each, so one token's slab is 256 contiguous bytes).  Thread (group g, column j)
+// loads its 16-byte vectors of columns j-1, j, j+1 for the RH + 2 input rows (the side
+// columns are the adjacent lanes' centre loads and come from L1), then forms its RH outputs
+// with the taps in registers.  There is no branch: a conditional store would let the
+// compiler sink the loads next to their first use (one memory round trip per output row).
+// Out-of-grid rows and columns are loaded clamped and scaled by zero (rows) or get zero taps
+// (columns); columns past the grid repeat the last one and the last row group overlaps its
+// neighbour, both writing identical values.  Needs at least RH rows.
+//   forward:  input row of (i, j) is its current position; output row is its position in
+//             out_layout (map m);
+//   backward (dx): input is dy at the position in out_layout (map m), taps rotated by 180
+//             degrees, output in the current order.
+constexpr int kStripG = 16, kStripW = 256 / kStripG;
+
+template <typename T, bool BWD, int RH>
+__global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           T* __restrict__ y, int rows, int cols,
+                                                           int D, long L, GridMap m,
+                                                           float bscale, int nslab, int nstrip,
+                                                           int nrg) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int tid = threadIdx.x, g = tid % kStripG, jc = tid / kStripG;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int strip = blk % nstrip; blk /= nstrip;
+  const int rg = blk % nrg;
+  const int b = blk / nrg;
+  const int c = (slab * kStripG + g) * VEC;
+  const int i0 = min(rg * RH, rows - RH);
+  const int j = min(strip * kStripW + jc, cols - 1);
+  const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
+  const long bL = (long)b * L;
+
+  float wr[3][3][VEC];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        wr[a][s][v] = BWD ? w[(c + v) * 9 + (2 - a) * 3 + (2 - s)] : w[(c + v) * 9 + a * 3 + s];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      if (j == 0) wr[a][0][v] = 0.f;
+      if (j == cols - 1) wr[a][2][v] = 0.f;
+    }
+  // bias: `bscale` is 0 when there is none (then `bias` points at any readable D floats)
+  float bs[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) bs[v] = bscale * bias[c + v];
+
+  auto in_row = [&](int ii, int jj) -> long {
+    return BWD ? m.A + m.Bi * ii + m.Bj * jj : (long)ii * cols + jj;
+  };
+  Vec<T, VEC> win[RH + 2][3];
+#pragma unroll
+  for (int r = 0; r < RH + 2; ++r) {
+    const int ii = min(max(i0 - 1 + r, 0), rows - 1);
+    win[r][0] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, jm)) * D + c);
+    win[r][1] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, j)) * D + c);
+    win[r][2] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, jp)) * D + c);
+  }
+  // only the window's first and last rows can lie outside the grid
+  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
+#pragma unroll
+  for (int r = 0; r < RH; ++r) {
+    const int i = i0 + r;
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = bs[v];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float on = r + a == 0 ? m_top : (r + a == RH + 1 ? m_bot : 1.f);
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+          acc[v] = fmaf(wr[a][s][v], on * to_f(win[r + a][s].v[v]), acc[v]);
+    }
+    Vec<T, VEC> o;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
+    const long orow = BWD ? (long)i * cols + j : m.A + m.Bi * i + m.Bj * j;
+    *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c) = o;
+  }
+}
+
 // ------------------------------------------------------------------ planning
 struct ConvPlan {
   int VW, cgs, nchb, nj, rows, cols, SR, ncolb, nstrip, nblocks;
@@ -505,6 +625,8 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 }
 
 constexpr int kConvSR = 16;
+constexpr int kStripRows = 16;  // output rows per strip block
+constexpr long kStripMinBlocks = 64;
 constexpr int kDwSR = 64;
 
 // Plan of the LDS-tiled path: 8 x 8 position tiles x 128-byte channel slabs.
@@ -541,6 +663,22 @@ template <typename T, bool BWD>
 static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int out_layout,
                                 const void* x, const float* w, const float* bias, void* y,
                                 hipStream_t st) {
+  constexpr int kSlabC = kStripG * 16 / (int)sizeof(T);  // channels of one slab
+  const bool col = layout == kCol || layout == kColRev;
+  const int rows = col ? gw : gh, cols = col ? gh : gw;
+  constexpr int RH = kStripRows;
+  const int nslab = D / kSlabC, nstrip = (cols + kStripW - 1) / kStripW;
+  const int nrg = (rows + RH - 1) / RH;
+  const long blocks = (long)B * nrg * nstrip * nslab;
+  // small grids (a few dozen strips) go to the 8 x 8 tiles, which give more blocks
+  if (D % kSlabC == 0 && rows >= RH && blocks >= kStripMinBlocks) {
+    hipLaunchKernelGGL((dwconv_strip_kernel<T, BWD, RH>), dim3((unsigned)blocks), dim3(256), 0,
+                       st, static_cast<const T*>(x), w, (!BWD && bias) ? bias : w,
+                       static_cast<T*>(y), rows, cols, D, (long)gh * gw,
+                       grid_map(gh, gw, layout, out_layout), (!BWD && bias) ? 1.f : 0.f, nslab,
+                       nstrip, nrg);
+    return hipGetLastError();
+  }
   const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
   if (tp.ok) {
     hipLaunchKernelGGL((dwconv_tiled_kernel<T, BWD>), dim3((unsigned)tp.conv_blocks), dim3(256),

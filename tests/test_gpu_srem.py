@@ -53,6 +53,8 @@ def test_reorient_bit_exact(B, gh, gw, D, dtype):
     (1, 8, 8, 64, "f32", False), (1, 8, 8, 64, "f32", True), (2, 16, 16, 384, "bf16", False),
     (1, 5, 7, 12, "bf16", True), (2, 3, 4, 5, "f32", True), (1, 1, 1, 8, "bf16", False),
     (1, 9, 2, 1152, "bf16", False),
+    # column-strip path (>= 64 strip blocks): ragged rows and columns, overlapping last row group
+    (4, 37, 29, 384, "bf16", True), (6, 29, 37, 128, "f32", False),
 ])
 def test_dwconv_all_layout_pairs(B, gh, gw, D, dtype, bias):
     dig = _dig()
@@ -103,6 +105,7 @@ def test_dwconv_full_configs(name):
 @pytest.mark.parametrize("B,gh,gw,D,dtype", [
     (1, 8, 8, 64, "f32"), (2, 16, 16, 384, "bf16"), (1, 5, 7, 12, "bf16"), (2, 3, 4, 5, "f32"),
     (1, 16, 16, 1152, "bf16"),
+    (4, 37, 29, 384, "bf16"), (6, 29, 37, 128, "f32"),  # column-strip dx path, ragged
 ])
 def test_dwconv_bwd(B, gh, gw, D, dtype):
     dig = _dig()
