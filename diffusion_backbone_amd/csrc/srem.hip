@@ -596,6 +596,87 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
   }
 }
 
+// Weight/bias gradient partials on the same strips: thread (group g, column j) accumulates
+// dy_cur(i, j) * x(i+a-1, j+s-1) for its RH rows (taps 0..8) and dy_cur (tap 9, the bias);
+// the 16 columns are then summed in a fixed order into part[blk][tap][D], blk over
+// (b, strip, row group).  Clamped duplicate columns and the rows of an overlapping last row
+// group that the previous group owns contribute zero.
+template <typename T, int RH>
+__global__ __launch_bounds__(256) void dwconv_dw_strip_kernel(const T* __restrict__ x,
+                                                              const T* __restrict__ dy,
+                                                              float* __restrict__ part, int rows,
+                                                              int cols, int D, long L, GridMap m,
+                                                              int nslab, int nstrip, int nrg) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CS = kStripG * VEC;  // channels of the slab
+  __shared__ float red[kStripW * CS];
+  const int tid = threadIdx.x, g = tid % kStripG, jc = tid / kStripG;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int strip = blk % nstrip; blk /= nstrip;
+  const int rg = blk % nrg;
+  const int b = blk / nrg;
+  const int c = (slab * kStripG + g) * VEC;
+  const int i0 = min(rg * RH, rows - RH), first_own = rg * RH;
+  const int jr = strip * kStripW + jc, j = min(jr, cols - 1);
+  const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
+  const long bL = (long)b * L;
+  const float mj = jr < cols ? 1.f : 0.f;
+  const float ms[3] = {j > 0 ? 1.f : 0.f, 1.f, j < cols - 1 ? 1.f : 0.f};
+
+  Vec<T, VEC> xw[RH + 2][3], dv[RH];
+#pragma unroll
+  for (int r = 0; r < RH + 2; ++r) {
+    const int ii = min(max(i0 - 1 + r, 0), rows - 1);
+    xw[r][0] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + jm) * D + c);
+    xw[r][1] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + j) * D + c);
+    xw[r][2] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + jp) * D + c);
+  }
+#pragma unroll
+  for (int r = 0; r < RH; ++r)
+    dv[r] = *reinterpret_cast<const Vec<T, VEC>*>(
+        dy + (bL + m.A + m.Bi * (i0 + r) + m.Bj * j) * D + c);
+  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
+
+  float acc[10][VEC];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
+#pragma unroll
+  for (int r = 0; r < RH; ++r) {
+    const float md = i0 + r >= first_own ? mj : 0.f;
+    float d[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) d[v] = md * to_f(dv[r].v[v]);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float on = r + a == 0 ? m_top : (r + a == RH + 1 ? m_bot : 1.f);
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+          acc[a * 3 + s][v] = fmaf(d[v], on * ms[s] * to_f(xw[r + a][s].v[v]), acc[a * 3 + s][v]);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[9][v] += d[v];
+  }
+
+  const long pblk = ((long)b * nstrip + strip) * nrg + rg;
+#pragma unroll
+  for (int t = 0; t < 10; ++t) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[jc * CS + g * VEC + v] = acc[t][v];
+    __syncthreads();
+    if (tid < CS) {
+      float sum = 0.f;
+      for (int q = 0; q < kStripW; ++q) sum += red[q * CS + tid];
+      part[(pblk * 10 + t) * D + slab * CS + tid] = sum;
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ planning
 struct ConvPlan {
   int VW, cgs, nchb, nj, rows, cols, SR, ncolb, nstrip, nblocks;
@@ -627,6 +708,29 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 constexpr int kConvSR = 16;
 constexpr int kStripRows = 16;  // output rows per strip block
 constexpr long kStripMinBlocks = 64;
+constexpr int kDwStripRows = 16;  // rows per block of the weight-gradient strips
+
+// Column-strip plan: 16-column strips x RH-row groups x slabs of 16 channel groups.  Used
+// when the slab divides the channels, the grid has at least RH rows and there are enough
+// blocks (small grids go to the 8 x 8 tiles).
+struct StripPlan {
+  bool ok;
+  int rows, cols, nslab, nstrip, nrg;
+  long blocks;
+};
+static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout, int RH) {
+  StripPlan p{};
+  const bool col = layout == kCol || layout == kColRev;
+  p.rows = col ? gw : gh;
+  p.cols = col ? gh : gw;
+  const int slabc = kStripG * 16 / elt;
+  p.nslab = D / slabc;
+  p.nstrip = (p.cols + kStripW - 1) / kStripW;
+  p.nrg = (p.rows + RH - 1) / RH;
+  p.blocks = (long)B * p.nrg * p.nstrip * p.nslab;
+  p.ok = D % slabc == 0 && p.rows >= RH && p.blocks >= kStripMinBlocks;
+  return p;
+}
 constexpr int kDwSR = 64;
 
 // Plan of the LDS-tiled path: 8 x 8 position tiles x 128-byte channel slabs.
@@ -663,15 +767,11 @@ template <typename T, bool BWD>
 static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int out_layout,
                                 const void* x, const float* w, const float* bias, void* y,
                                 hipStream_t st) {
-  constexpr int kSlabC = kStripG * 16 / (int)sizeof(T);  // channels of one slab
-  const bool col = layout == kCol || layout == kColRev;
-  const int rows = col ? gw : gh, cols = col ? gh : gw;
   constexpr int RH = kStripRows;
-  const int nslab = D / kSlabC, nstrip = (cols + kStripW - 1) / kStripW;
-  const int nrg = (rows + RH - 1) / RH;
-  const long blocks = (long)B * nrg * nstrip * nslab;
-  // small grids (a few dozen strips) go to the 8 x 8 tiles, which give more blocks
-  if (D % kSlabC == 0 && rows >= RH && blocks >= kStripMinBlocks) {
+  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, RH);
+  if (sp.ok) {
+    const int rows = sp.rows, cols = sp.cols, nslab = sp.nslab, nstrip = sp.nstrip, nrg = sp.nrg;
+    const long blocks = sp.blocks;
     hipLaunchKernelGGL((dwconv_strip_kernel<T, BWD, RH>), dim3((unsigned)blocks), dim3(256), 0,
                        st, static_cast<const T*>(x), w, (!BWD && bias) ? bias : w,
                        static_cast<T*>(y), rows, cols, D, (long)gh * gw,
@@ -718,6 +818,8 @@ static ConvPlan dw_plan(int B, int gh, int gw, int D, int elt, int layout) {
 
 // Number of [10][D] partial-sum slices the dw pass writes for one dtype and layout.
 static long dw_partials(int B, int gh, int gw, int D, int elt, int layout) {
+  const StripPlan sp = strip_plan(B, gh, gw, D, elt, layout, kDwStripRows);
+  if (sp.ok) return (long)B * sp.nstrip * sp.nrg;
   const TilePlan tp = tile_plan(B, gh, gw, D, elt, layout);
   if (tp.ok) return tp.dw_partials;
   const ConvPlan c = dw_plan(B, gh, gw, D, elt, layout);
@@ -739,6 +841,16 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
                               const void* x, const void* dy, float* dw, float* dbias,
                               float* part, hipStream_t st) {
   const long n = 10L * D;
+  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kDwStripRows);
+  if (sp.ok) {
+    hipLaunchKernelGGL((dwconv_dw_strip_kernel<T, kDwStripRows>), dim3((unsigned)sp.blocks),
+                       dim3(256), 0, st, static_cast<const T*>(x), static_cast<const T*>(dy), part,
+                       sp.rows, sp.cols, D, (long)gh * gw, grid_map(gh, gw, layout, out_layout),
+                       sp.nslab, sp.nstrip, sp.nrg);
+    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       part, (int)((long)B * sp.nstrip * sp.nrg), D, dw, dbias);
+    return hipGetLastError();
+  }
   const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
   if (tp.ok) {
     hipLaunchKernelGGL((dwconv_dw_tiled_kernel<T>), dim3((unsigned)tp.dw_blocks), dim3(256), 0, st,
