@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dig_s2_256", choices=sorted(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the steady-state probes (larger shapes, outside the timed step)")
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--quiet", action="store_true")
     # profiling helpers (rocprofv3 counter runs): run only one library call of the step, or a
@@ -173,10 +175,10 @@ class EventTimer:
 TRAFFIC = {
     "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    # FETCH_SIZE 12006.1 KiB / 0.50017 (copy: 131116.8 KiB read per 262144 KiB moved) +
+    # FETCH_SIZE 11994.8 KiB / 0.50016 (copy: 131113.3 KiB read per 262144 KiB moved) +
     # WRITE_SIZE 8132.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-    "bytes": 32907259,
-    "sources_sha256": "a4e2e60c31b7174876bb1c23036c2d8ee9ee3881959c4017c8094f7c473df557",
+    "bytes": 32884669,
+    "sources_sha256": "5e12c6639d87830d91473997747e8622191304f770dfb28e47c6c9cca12305f8",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
@@ -254,6 +256,86 @@ def cpu_baseline(cfg, nblocks):
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d full fwd+bwd step(s) of %d of %d images (%d blocks, %d tokens each), %.1f s"
                       % (reps, sample_batch, cfg.batch, nblocks, cfg.seq_len, el)}
+
+
+def _time_us(fn, reps=10):
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e3
+
+
+def probes():
+    """Steady-state probes, outside the timed step: one library call at a time, back to back,
+    on inputs large enough that launch latency does not dominate.  Labelled as probes: they
+    are not the step's workload."""
+    import torch
+    import diffusion_backbone_amd as dig
+    out = {}
+
+    def gla(label, B, L, H, dk, dv, chunk=64):
+        bt = lambda *sh: torch.randn(*sh, device="cuda").to(torch.bfloat16)
+        q, k, v, r = bt(B, L, H, dk), bt(B, L, H, dk), bt(B, L, H, dv), bt(B, L, H, dv)
+        z = (torch.randn(B, L, H, dk, device="cuda") * 0.2).to(torch.bfloat16)
+        dy = bt(B, L, H, dv)
+        desc = dig.make_desc(B, L, H, dk, dv, chunk, 16.0, 1.0, 1e-5, dig.DIG_BF16, 0)
+        by = lambda n: torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+        fwb, bwb = dig.dig_gla_fwd_workspace_bytes(desc), dig.dig_gla_bwd_workspace_bytes(desc)
+        fws, bws, saved = by(fwb), by(bwb), by(dig.dig_gla_saved_bytes(desc))
+        y = torch.empty_like(r)
+        g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z),
+             torch.empty_like(r)]
+        dgam = torch.empty(dv, device="cuda")
+        tf = _time_us(lambda: dig.dig_gla_fwd(desc, q, k, v, z, r, None, y, None, saved, fws, fwb))
+        tb = _time_us(lambda: dig.dig_gla_bwd(desc, q, k, v, z, r, None, dy, saved, *g, dgam,
+                                              bws, bwb))
+        th = B * L * H
+        for name, t, byts in (("fwd", tf, 2 * (3 * dk + 3 * dv) * th),
+                              ("bwd", tb, 2 * (6 * dk + 5 * dv) * th)):
+            gbs = byts / (t / 1e6) / 1e9
+            out["%s_%s" % (label, name)] = {
+                "call": "dig_gla_" + name, "shape": [B, L, H, dk, dv], "us": round(t, 1),
+                "tokens_per_s": round(B * L / (t / 1e6), 1), "achieved_gbs": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del q, k, v, r, z, dy, y, g, fws, bws, saved
+
+    def srem(label, B, gh, gw, D):
+        x = torch.randn(B, gh * gw, D, device="cuda").to(torch.bfloat16)
+        dy = torch.randn_like(x)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        w = torch.randn(D, 3, 3, device="cuda") / 3.0
+        dw, db = torch.empty_like(w), torch.empty(D, device="cuda")
+        wsb = dig.dig_dwconv3x3_bwd_workspace_bytes(B, gh, gw, D)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        nb = x.numel() * 2
+        R, C = dig.DIG_SCAN_ROW, dig.DIG_SCAN_COL
+        cases = (
+            ("reorient", lambda: dig.dig_srem_reorient(B, gh, gw, D, dig.DIG_BF16, R, C, x, y), 2 * nb),
+            ("dwconv3x3", lambda: dig.dig_dwconv3x3(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, None, y),
+             2 * nb),
+            ("dwconv3x3_bwd", lambda: dig.dig_dwconv3x3_bwd(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, dy,
+                                                           dx, dw, db, ws, wsb), 3 * nb))
+        for name, fn, byts in cases:
+            t = _time_us(fn)
+            gbs = byts / (t / 1e6) / 1e9
+            out["%s_%s" % (label, name)] = {
+                "call": "dig_" + ("srem_" + name if name == "reorient" else name),
+                "shape": [B, gh, gw, D], "us": round(t, 1), "achieved_gbs": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    gla("s2_b256", 256, 256, 6, 32, 64)
+    c5 = W.CONFIGS["dig_xl2_2048"]
+    gla("xl2_2048", c5.batch, c5.seq_len, c5.heads, c5.d_k, c5.d_v)
+    srem("xl2_2048", c5.batch, c5.grid_h, c5.grid_w, c5.d_model)
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -365,6 +447,8 @@ def main():
                                 "achieved_gbs": round(rl[other]["gbs"], 1),
                                 "frac": round(rl[other]["gbs"] / HBM_PEAK_GBS, 4)},
     }
+    if not args.no_probes:
+        out["probes"] = probes()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, nblocks)
     print(json.dumps(out), flush=True)
