@@ -383,94 +383,100 @@ __global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__
   }
 }
 
-// dw / dbias partial sums over a column of up to `tpb` row tiles; dy tile gathered back to
-// the current order.  part[blk][tap][D] with tap 9 = bias, blk over (b, tile column, row group).
+// Backward of one 8 x 8 tile x 128-byte slab in one pass: the dy halo tile (gathered back to
+// the current order) and the x halo tile arrive by LDS DMA; each thread forms dx at its two
+// positions (taps rotated by 180 degrees) and accumulates dy(i, j) * x(i+a-1, j+s-1) (taps
+// 0..8) and dy(i, j) (tap 9, the bias), then the 32 position lanes are summed in a fixed
+// order into part[tile][tap][D], tile over (b, tile row, tile column).
 template <typename T>
-__global__ __launch_bounds__(256) void dwconv_dw_tiled_kernel(const T* __restrict__ x,
-                                                              const T* __restrict__ dy,
-                                                              float* __restrict__ part, int gh,
-                                                              int gw, int D, int layout,
-                                                              int out_layout, int rows, int cols,
-                                                              int ntr, int ntc, int nslab, int tpb,
-                                                              int nrg) {
+__global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               const T* __restrict__ dy,
+                                                               T* __restrict__ dx,
+                                                               float* __restrict__ part, int gh,
+                                                               int gw, int D, int layout,
+                                                               int out_layout, int rows,
+                                                               int cols, int ntr, int ntc,
+                                                               int nslab) {
   constexpr int CS = kSlabBytes / sizeof(T);
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NG = CS / VEC;
+  __shared__ __align__(16) T dyt[kHalo * kHalo * CS];
   __shared__ __align__(16) T xt[kHalo * kHalo * CS];
-  __shared__ __align__(16) T dt[kTile * kTile * CS];
   __shared__ float red[32 * CS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int blk = blockIdx.x;
   const int slab = blk % nslab; blk /= nslab;
   const int tc = blk % ntc; blk /= ntc;
-  const int rg = blk % nrg;
-  const int b = blk / nrg;
-  const int j0 = tc * kTile, c0 = slab * CS;
+  const int tr = blk % ntr;
+  const int b = blk / ntr;
+  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
   const long L = (long)gh * gw, bL = (long)b * L;
-  const int g = tid % NG, pl = tid / NG;
 
+  load_halo<T, true>(dyt, dy, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout,
+                     wave, lane);
+  load_halo<T, false>(xt, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout,
+                      wave, lane);
+  const int g = tid % NG, pl = tid / NG;  // channel group, first position
+  float wr[9][VEC];
+#pragma unroll
+  for (int t = 0; t < 9; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) wr[t][v] = w[(c0 + g * VEC + v) * 9 + 8 - t];
   float acc[10][VEC];
 #pragma unroll
   for (int t = 0; t < 10; ++t)
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
+  dma_wait();
+  __syncthreads();
 
-  const int tr_end = min(ntr, (rg + 1) * tpb);
-  for (int tr = rg * tpb; tr < tr_end; ++tr) {
-    const int i0 = tr * kTile;
-    load_halo<T, false>(xt, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout, wave,
-                        lane);
-    {  // dy tile (no halo), gathered from out_layout order
-      unsigned char* db = reinterpret_cast<unsigned char*>(dt);
-      constexpr int NP = kTile * kTile * NG;
-      for (int base = wave * 64; base < NP; base += 4 * 64) {
-        const int e = base + lane;
-        const int pos = e / NG, k = e - pos * NG;
-        const int oi = pos / kTile, oj = pos - oi * kTile;
-        const int i = i0 + oi, j = j0 + oj;
-        if (i < rows && j < cols) {
-          const long p = (long)i * cols + j;
-          const long row = scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L);
-          const T* gp = dy + (bL + row) * D + c0 + k * VEC;
-          __builtin_amdgcn_global_load_lds((gbl_ptr_t)gp, (lds_ptr_t)(db + base * 16), 16, 0, 0);
-        } else {
-          *reinterpret_cast<uint4*>(db + (long)e * 16) = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-    dma_wait();
-    __syncthreads();
 #pragma unroll
-    for (int task = 0; task < 2; ++task) {
-      const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
-      const Vec<T, VEC> gv = *reinterpret_cast<const Vec<T, VEC>*>(dt + q * CS + g * VEC);
+  for (int task = 0; task < 2; ++task) {
+    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
+    const int i = i0 + oi, j = j0 + oj;
+    if (i < rows && j < cols) {
+      float o[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[v] = 0.f;
 #pragma unroll
       for (int a = 0; a < 3; ++a)
 #pragma unroll
         for (int s2 = 0; s2 < 3; ++s2) {
-          const Vec<T, VEC> xv =
-              *reinterpret_cast<const Vec<T, VEC>*>(xt + ((oi + a) * kHalo + oj + s2) * CS + g * VEC);
+          const int h = ((oi + a) * kHalo + oj + s2) * CS + g * VEC;
+          const Vec<T, VEC> dv = *reinterpret_cast<const Vec<T, VEC>*>(dyt + h);
+          const Vec<T, VEC> xv = *reinterpret_cast<const Vec<T, VEC>*>(xt + h);
+          const Vec<T, VEC> gc = *reinterpret_cast<const Vec<T, VEC>*>(
+              dyt + ((oi + 1) * kHalo + oj + 1) * CS + g * VEC);
 #pragma unroll
-          for (int v = 0; v < VEC; ++v)
-            acc[a * 3 + s2][v] = fmaf(to_f(gv.v[v]), to_f(xv.v[v]), acc[a * 3 + s2][v]);
+          for (int v = 0; v < VEC; ++v) {
+            o[v] = fmaf(wr[a * 3 + s2][v], to_f(dv.v[v]), o[v]);
+            acc[a * 3 + s2][v] = fmaf(to_f(gc.v[v]), to_f(xv.v[v]), acc[a * 3 + s2][v]);
+          }
         }
+      const Vec<T, VEC> gc =
+          *reinterpret_cast<const Vec<T, VEC>*>(dyt + ((oi + 1) * kHalo + oj + 1) * CS + g * VEC);
+      Vec<T, VEC> ov;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[9][v] += to_f(gv.v[v]);
+      for (int v = 0; v < VEC; ++v) {
+        acc[9][v] += to_f(gc.v[v]);
+        ov.v[v] = from_f<T>(o[v]);
+      }
+      *reinterpret_cast<Vec<T, VEC>*>(dx + (bL + (long)i * cols + j) * D + c0 + g * VEC) = ov;
     }
-    __syncthreads();
   }
 
   // fixed-order reduction over the 32 position lanes of each channel group
-  const long pblk = ((long)b * ntc + tc) * nrg + rg;
+  const long pblk = ((long)b * ntr + tr) * ntc + tc;
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) red[pl * CS + g * VEC + v] = acc[t][v];
     __syncthreads();
     if (tid < CS) {
-      float s2 = 0.f;
-      for (int q = 0; q < 32; ++q) s2 += red[q * CS + tid];
-      part[(pblk * 10 + t) * D + c0 + tid] = s2;
+      float s3 = 0.f;
+      for (int q = 0; q < 32; ++q) s3 += red[q * CS + tid];
+      part[(pblk * 10 + t) * D + c0 + tid] = s3;
     }
     __syncthreads();
   }
@@ -708,7 +714,6 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 constexpr int kConvSR = 16;
 constexpr int kStripRows = 16;  // output rows per strip block
 constexpr long kStripMinBlocks = 64;
-constexpr int kDwStripRows = 16;  // rows per block of the weight-gradient strips
 
 // Column-strip plan: 16-column strips x RH-row groups x slabs of 16 channel groups.  Used
 // when the slab divides the channels, the grid has at least RH rows and there are enough
@@ -736,8 +741,8 @@ constexpr int kDwSR = 64;
 // Plan of the LDS-tiled path: 8 x 8 position tiles x 128-byte channel slabs.
 struct TilePlan {
   bool ok;
-  int rows, cols, ntr, ntc, nslab, tpb, nrg;
-  long conv_blocks, dw_blocks, dw_partials;
+  int rows, cols, ntr, ntc, nslab;
+  long conv_blocks;
 };
 
 static TilePlan tile_plan(int B, int gh, int gw, int D, int elt, int layout) {
@@ -751,15 +756,6 @@ static TilePlan tile_plan(int B, int gh, int gw, int D, int elt, int layout) {
   t.ntr = (t.rows + kTile - 1) / kTile;
   t.ntc = (t.cols + kTile - 1) / kTile;
   t.conv_blocks = (long)B * t.ntr * t.ntc * t.nslab;
-  // dw: enough row groups to give about 1024 blocks, each walking tpb row tiles
-  const long per_rg = (long)B * t.ntc * t.nslab;
-  long want = (1024 + per_rg - 1) / per_rg;
-  if (want > t.ntr) want = t.ntr;
-  if (want < 1) want = 1;
-  t.tpb = (int)((t.ntr + want - 1) / want);
-  t.nrg = (t.ntr + t.tpb - 1) / t.tpb;
-  t.dw_blocks = per_rg * t.nrg;
-  t.dw_partials = (long)B * t.ntc * t.nrg;
   return t;
 }
 
@@ -818,10 +814,10 @@ static ConvPlan dw_plan(int B, int gh, int gw, int D, int elt, int layout) {
 
 // Number of [10][D] partial-sum slices the dw pass writes for one dtype and layout.
 static long dw_partials(int B, int gh, int gw, int D, int elt, int layout) {
-  const StripPlan sp = strip_plan(B, gh, gw, D, elt, layout, kDwStripRows);
+  const StripPlan sp = strip_plan(B, gh, gw, D, elt, layout, kStripRows);
   if (sp.ok) return (long)B * sp.nstrip * sp.nrg;
   const TilePlan tp = tile_plan(B, gh, gw, D, elt, layout);
-  if (tp.ok) return tp.dw_partials;
+  if (tp.ok) return (long)B * tp.ntr * tp.ntc;
   const ConvPlan c = dw_plan(B, gh, gw, D, elt, layout);
   return c.nblocks / c.nchb;
 }
@@ -841,24 +837,14 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
                               const void* x, const void* dy, float* dw, float* dbias,
                               float* part, hipStream_t st) {
   const long n = 10L * D;
-  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kDwStripRows);
+  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kStripRows);
   if (sp.ok) {
-    hipLaunchKernelGGL((dwconv_dw_strip_kernel<T, kDwStripRows>), dim3((unsigned)sp.blocks),
+    hipLaunchKernelGGL((dwconv_dw_strip_kernel<T, kStripRows>), dim3((unsigned)sp.blocks),
                        dim3(256), 0, st, static_cast<const T*>(x), static_cast<const T*>(dy), part,
                        sp.rows, sp.cols, D, (long)gh * gw, grid_map(gh, gw, layout, out_layout),
                        sp.nslab, sp.nstrip, sp.nrg);
     hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        part, (int)((long)B * sp.nstrip * sp.nrg), D, dw, dbias);
-    return hipGetLastError();
-  }
-  const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
-  if (tp.ok) {
-    hipLaunchKernelGGL((dwconv_dw_tiled_kernel<T>), dim3((unsigned)tp.dw_blocks), dim3(256), 0, st,
-                       static_cast<const T*>(x), static_cast<const T*>(dy), part, gh, gw, D,
-                       layout, out_layout, tp.rows, tp.cols, tp.ntr, tp.ntc, tp.nslab, tp.tpb,
-                       tp.nrg);
-    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       part, (int)tp.dw_partials, D, dw, dbias);
     return hipGetLastError();
   }
   const ConvPlan c = dw_plan(B, gh, gw, D, sizeof(T), layout);
@@ -883,20 +869,39 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
   return hipGetLastError();
 }
 
+// dx and the dW/dbias partials: column strips (two kernels) on large grids, one fused pass
+// over 8 x 8 tiles on small ones, the per-channel sums of the partials last.
+template <typename T>
+static hipError_t launch_dwconv_bwd_t(int B, int gh, int gw, int D, int layout, int out_layout,
+                                      const void* x, const float* w, const void* dy, void* dx,
+                                      float* dw, float* dbias, float* part, hipStream_t st) {
+  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kStripRows);
+  const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
+  if (!sp.ok && tp.ok) {
+    hipLaunchKernelGGL((dwconv_bwd_tiled_kernel<T>), dim3((unsigned)tp.conv_blocks), dim3(256), 0,
+                       st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
+                       static_cast<T*>(dx), part, gh, gw, D, layout, out_layout, tp.rows, tp.cols,
+                       tp.ntr, tp.ntc, tp.nslab);
+    const long n = 10L * D;
+    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       part, (int)((long)B * tp.ntr * tp.ntc), D, dw, dbias);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_conv_t<T, true>(B, gh, gw, D, layout, out_layout, dy, w, nullptr,
+                                              dx, st);
+  if (e != hipSuccess) return e;
+  return launch_dw_t<T>(B, gh, gw, D, layout, out_layout, x, dy, dw, dbias, part, st);
+}
+
 hipError_t launch_dwconv_bwd(int B, int gh, int gw, int D, int bf16v, int layout, int out_layout,
                              const void* x, const float* w, const void* dy, void* dx, float* dw,
                              float* dbias, void* workspace, hipStream_t st) {
-  hipError_t e;
-  if (bf16v) {
-    e = launch_conv_t<bf16, true>(B, gh, gw, D, layout, out_layout, dy, w, nullptr, dx, st);
-    if (e != hipSuccess) return e;
-    return launch_dw_t<bf16>(B, gh, gw, D, layout, out_layout, x, dy, dw, dbias,
-                             static_cast<float*>(workspace), st);
-  }
-  e = launch_conv_t<float, true>(B, gh, gw, D, layout, out_layout, dy, w, nullptr, dx, st);
-  if (e != hipSuccess) return e;
-  return launch_dw_t<float>(B, gh, gw, D, layout, out_layout, x, dy, dw, dbias,
-                            static_cast<float*>(workspace), st);
+  float* part = static_cast<float*>(workspace);
+  if (bf16v)
+    return launch_dwconv_bwd_t<bf16>(B, gh, gw, D, layout, out_layout, x, w, dy, dx, dw, dbias,
+                                     part, st);
+  return launch_dwconv_bwd_t<float>(B, gh, gw, D, layout, out_layout, x, w, dy, dx, dw, dbias,
+                                    part, st);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t n) {
