@@ -38,7 +38,9 @@
 
 namespace dig {
 
-constexpr int kBwdThreads = 256;
+#ifndef DIG_BWD_WAVES8
+#define DIG_BWD_WAVES8 8
+#endif
 constexpr float kBwdSlowDecayLog2 = 96.0f;
 
 constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
@@ -46,7 +48,7 @@ constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
 // LDS layout (compile time).  LEAN drops the row-layout copies of dO, S0 and D (their
 // products then read the transposed copies with strided fragments) when the full layout
 // would not fit.
-template <typename T, int DK, int DV, int C, bool FIN, bool LEAN>
+template <typename T, int DK, int DV, int C, bool FIN, bool LEAN, int NW = 4>
 struct BwdLayout {
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
@@ -75,10 +77,10 @@ struct BwdLayout {
   static constexpr int O_W = O_B + bal16(C * DK * 4);                // q.dq-k.dk [C][DK]
   static constexpr int O_GAM = O_W + bal16(FIN ? C * DK * 4 : 0);    // e^{b_last}  [DKP]
   static constexpr int O_LG = O_GAM + bal16(DKP * 4);                // b_last / segment decay
-  static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [4]
+  static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [NW]
   static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
-  static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [4][DVP]
-  static constexpr int O_DIAG = O_DG + bal16(4 * DVP * 4);           // [C]
+  static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [NW][DVP]
+  static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [C]
   static constexpr int O_RAW = O_DIAG + bal16(C * 4);
   // raw staging: q, k, z, v, r, dy rows packed with the runtime row length
   static constexpr int R_Q = 0;
@@ -91,24 +93,25 @@ struct BwdLayout {
   static constexpr int bytes = O_RAW + SLOT;
 };
 constexpr int kBwdLdsBudget = 160 * 1024;
-template <typename T, int DK, int DV, int C, bool FIN>
+template <typename T, int DK, int DV, int C, bool FIN, int NW = 4>
 constexpr bool bwd_lean() {
-  return BwdLayout<T, DK, DV, C, FIN, false>::bytes > kBwdLdsBudget;
+  return BwdLayout<T, DK, DV, C, FIN, false, NW>::bytes > kBwdLdsBudget;
 }
 
-template <typename T, int DK, int DV, bool EXACT, int C, bool FIN>
-__global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
-  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN>();
-  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN>;
+template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW>
+__global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
+  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW>();
+  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW>;
+  constexpr int NTH = 64 * NW;  // NW waves
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP;
   constexpr int QP = Lo::QP, VP = Lo::VP, TP = Lo::TP;
   constexpr int NT = C / 16;
-  constexpr int NST = NDK * NDV, STW = (NST + 3) / 4;
-  constexpr int NPAIR = NT * NDK, PRW = (NPAIR + 3) / 4;     // dq/dk (row tile, key tile)
-  constexpr int NDVT = NT * NDV, DVW = (NDVT + 3) / 4;       // dv (row tile, value tile)
-  constexpr int NCL = DKP * C / kBwdThreads;                 // gate: key columns per lane
-  constexpr int NEL = DVP * C / kBwdThreads;                 // gate: value columns per lane
+  constexpr int NST = NDK * NDV, STW = (NST + NW - 1) / NW;
+  constexpr int NPAIR = NT * NDK, PRW = (NPAIR + NW - 1) / NW;  // dq/dk (row tile, key tile)
+  constexpr int NDVT = NT * NDV, DVW = (NDVT + NW - 1) / NW;    // dv (row tile, value tile)
+  constexpr int NCL = DKP * C / NTH;                         // gate: key columns per lane
+  constexpr int NEL = DVP * C / NTH;                         // gate: value columns per lane
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
   using Acc = typename std::conditional<kBf, float, double>::type;
@@ -176,17 +179,17 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     const long gsk = (long)H * dk * sizeof(T), gsv = (long)H * dv * sizeof(T);
     const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
     dma_rows_c(base + Lo::R_Q, reinterpret_cast<const unsigned char*>(gq + row0 * dk), gsk, rbk,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv, rbv,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_DY, reinterpret_cast<const unsigned char*>(gdy + row0 * dv), gsv,
-               rbv, valid, wave, 4, lane);
+               rbv, valid, wave, NW, lane);
   };
   // this lane's elements of the fp32 state tiles of chunk n (the saved forward states)
   // (exact shapes: branch-free, padding positions hold clamped copies that are masked where
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     if constexpr (PF) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
-        const int u = min(wave + 4 * m, NST - 1);
+        const int u = min(wave + NW * m, NST - 1);
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = min(et * 16 + r16, DV - 1);
 #pragma unroll
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
       dst[m] = zero4();
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     }
   };
 
-  RowRegs<DK * (int)sizeof(T), C, kBwdThreads> pq, pk, pz;
-  RowRegs<DV * (int)sizeof(T), C, kBwdThreads> pv, pr, pdy;
+  RowRegs<DK * (int)sizeof(T), C, NTH> pq, pk, pz;
+  RowRegs<DV * (int)sizeof(T), C, NTH> pv, pr, pdy;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   };
   if constexpr (PF) pf_load(n_top - 1);
   else issue(n_top - 1);
-  for (int i = tid; i < Lo::O_RAW / 16; i += kBwdThreads)
+  for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
 
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     const float* src = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
   auto write_part = [&](const f32x4 (&se)[STW]) {
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
 #pragma unroll
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     // ---- S0 (transposed, and row unless LEAN) as bf16 operands; G^T follows the gate
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
@@ -411,15 +414,17 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
     __syncthreads();
-    const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
-    const bool slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kBwdSlowDecayLog2;
+    float mxa = sMax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mxa = fmaxf(mxa, sMax[w]);
+    const bool slow = mxa > kBwdSlowDecayLog2;
 
     // G^T as (e^{b_last} G)^T: it enters dv as k e^{-b} (e^{b_last} G) and dk as
     // e^{-b} V (e^{b_last} G)^T; with strong decay (elementwise paths) G itself
     if (own) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
-        const int u = wave + 4 * m;
+        const int u = wave + NW * m;
         if (u < NST) {
           const int ct = u / NDV, et = u - ct * NDV;
           const int e = et * 16 + r16;
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
 
     if (own) {
       // ---- D = dO V^T (causal, row and transposed) and the dlog(alpha) boundary term
-      for (int q = wave; q < NT * NT; q += 4) {
+      for (int q = wave; q < NT * NT; q += NW) {
         const int I = q / NT, J = q - I * NT;
         if (J <= I) {
           f32x4 d;
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       for (int m = 0; m < PRW; ++m) {
         // one pair at a time: keeps later pairs' operand fragments from being hoisted
         __builtin_amdgcn_sched_barrier(0);
-        const int u = wave + 4 * m;
+        const int u = wave + NW * m;
         if (u < NPAIR) {
           const int I = u / NDK, ct = u - I * NDK;
           f32x4 a1, a2 = zero4(), a4 = zero4();
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
       for (int m = 0; m < DVW; ++m) {
         __builtin_amdgcn_sched_barrier(0);
-        const int u = wave + 4 * m;
+        const int u = wave + NW * m;
         if (u < NDVT) {
           const int J = u / NDV, et = u - J * NDV;
           f32x4 dva = Mma<T>::kc(zero4(), sPt, TP, 16 * J, sdOt, TP, 16 * et, C, lane);
@@ -742,7 +747,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
     // gradient state: G <- diag(e^{b_last}) G + (q e^{b})^T dO
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
@@ -795,22 +800,22 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       if constexpr (PF) {
         constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
         using UC = unsigned char;
-        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
+        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
                                              reinterpret_cast<const UC*>(sdqs), valid, tid);
-        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
+        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
                                              reinterpret_cast<const UC*>(sdks), valid, tid);
-        store_rows_fixed<RK, C, kBwdThreads>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
+        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
                                              reinterpret_cast<const UC*>(rawz), valid, tid);
-        store_rows_fixed<RV, C, kBwdThreads>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
+        store_rows_fixed<RV, C, NTH>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
                                              reinterpret_cast<const UC*>(sDy), valid, tid);
-        store_rows_fixed<RV, C, kBwdThreads>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
+        store_rows_fixed<RV, C, NTH>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
                                              reinterpret_cast<const UC*>(sRr), valid, tid);
       } else {
-        store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, kBwdThreads);
-        store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, kBwdThreads);
-        store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, kBwdThreads);
-        store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, kBwdThreads);
-        store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, kBwdThreads);
+        store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, NTH);
+        store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, NTH);
+        store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, NTH);
+        store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, NTH);
+        store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, NTH);
       }
     }
     // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
@@ -833,14 +838,17 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
     }
     __syncthreads();
-    for (int e = tid; e < dv; e += kBwdThreads)
-      p.dgamma_part[(long)blockIdx.x * dv + e] =
-          ((sDg[e] + sDg[DVP + e]) + sDg[2 * DVP + e]) + sDg[3 * DVP + e];
+    for (int e = tid; e < dv; e += NTH) {
+      float sum = sDg[e];  // waves in order (waves past the row tiles add exact zeros)
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += sDg[w * DVP + e];
+      p.dgamma_part[(long)blockIdx.x * dv + e] = sum;
+    }
   } else {
     float* dst = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
+      const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
@@ -852,29 +860,38 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
     __syncthreads();
-    for (int c = tid; c < dk; c += kBwdThreads)
+    for (int c = tid; c < dk; c += NTH)
       p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
   }
+}
+
+// Waves per workgroup: eight where the head shape leaves every phase at least one column per
+// lane and the registers fit two waves per SIMD, else four.
+template <typename T, int DK, int DV, bool EXACT>
+constexpr int bwd_waves() {
+  return (EXACT && sizeof(T) == 2 && DK == 32 && DV == 64) ? DIG_BWD_WAVES8 : 4;
 }
 
 template <typename T, int DK, int DV, bool EXACT, int C>
 static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
   const long BH = (long)s.B * s.H;
-  constexpr int fin_bytes = BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true>()>::bytes;
-  constexpr int a_bytes = BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false>()>::bytes;
+  constexpr int NW = bwd_waves<T, DK, DV, EXACT>();
+  constexpr int fin_bytes =
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW>(), NW>::bytes;
+  constexpr int a_bytes =
+      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW>(), NW>::bytes;
   if (lds_out) {
     *lds_out = fin_bytes;
     return hipSuccess;
   }
   if (!s.bprefix && s.nseg > 1) {
-    hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false>),
-                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(kBwdThreads), a_bytes, st,
-                       p);
+    hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW>),
+                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(64 * NW), a_bytes, st, p);
     const hipError_t e = launch_gla_gstate_scan(s, p.gstates, p.seg_lg, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true>), dim3((unsigned)(BH * s.nseg)),
-                     dim3(kBwdThreads), fin_bytes, st, p);
+  hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW>),
+                     dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
   return hipGetLastError();
 }
 
