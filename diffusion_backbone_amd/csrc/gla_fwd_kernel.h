@@ -38,7 +38,9 @@
 
 namespace dig {
 
-constexpr int kFwdThreads = 256;
+#ifndef DIG_FWD_WAVES8
+#define DIG_FWD_WAVES8 8
+#endif
 constexpr float kSlowDecayLog2 = 96.0f;  // e^{-b} factors up to 2^96 stay finite in bf16/fp32
 constexpr int kFwdLdsBudget = 160 * 1024;
 
@@ -77,16 +79,21 @@ struct FwdLayout {
   static constexpr int bytes(int nbuf) { return O_RAW + nbuf * SLOT; }
 };
 
-template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
-__global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW>
+__global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
+  constexpr int NTH = 64 * NW;  // NW waves
   using Lo = FwdLayout<T, DK, DV, C, OUT>;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
   constexpr int QP = Lo::QP, TP = Lo::TP;
   constexpr int NT = C / 16;                            // query row tiles
-  constexpr int NST = NDK * NDV, STW = (NST + 3) / 4;   // state tiles, per wave
-  constexpr int NCL = DKP * C / kFwdThreads;            // gate pass: key columns per lane
-  constexpr int NEL = DVP * C / kFwdThreads;            // V transpose: value columns per lane
+  constexpr int NST = NDK * NDV;                        // fp32 state tiles
+  // state tiles are owned by waves SW0..NW-1: the waves past the query row tiles when there
+  // are more waves than row tiles (they advance the state while the others form outputs)
+  constexpr int SW0 = (OUT && NW > NT) ? NT : 0, NSW = NW - SW0;
+  constexpr int STW = (NST + NSW - 1) / NSW;            // state tiles per owning wave
+  constexpr int NCL = DKP * C / NTH;                    // gate pass: key columns per lane
+  constexpr int NEL = DVP * C / NTH;                    // V transpose: value columns per lane
   // every gate/transpose column is a real one: no per-column guards
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
@@ -136,21 +143,21 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     const long gsk = (long)H * dk * sizeof(T), gsv = (long)H * dv * sizeof(T);
     const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
     dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
-               valid, wave, 4, lane);
+               valid, wave, NW, lane);
     if (OUT && n >= c_first) {
       dma_rows_c(base + Lo::R_Q, reinterpret_cast<const unsigned char*>(gq + row0 * dk), gsk,
-                 rbk, valid, wave, 4, lane);
+                 rbk, valid, wave, NW, lane);
       dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv,
-                 rbv, valid, wave, 4, lane);
+                 rbv, valid, wave, NW, lane);
     }
   };
   // exact shapes: the raw rows of a chunk in registers (loaded one iteration ahead)
-  RowRegs<DK * (int)sizeof(T), C, kFwdThreads> pk, pz, pq;
-  RowRegs<DV * (int)sizeof(T), C, kFwdThreads> pv, pr;
+  RowRegs<DK * (int)sizeof(T), C, NTH> pk, pz, pq;
+  RowRegs<DV * (int)sizeof(T), C, NTH> pv, pr;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
 
   // zero everything but the staging slots: padding rows/columns of the MFMA operands must
   // read as zero and are never written afterwards
-  for (int i = tid; i < Lo::O_RAW / 16; i += kFwdThreads)
+  for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
 
@@ -189,8 +196,8 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     const float* src = p.states + (sbase + c_first) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
+      const int u = wave - SW0 + NSW * m;
+      if (wave >= SW0 && u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
 #pragma unroll
@@ -246,8 +253,8 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
       float* dst = p.states + (sbase + n) * dk * dv;
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NST) {
+        const int u = wave - SW0 + NSW * m;
+        if (wave >= SW0 && u < NST) {
           const int ct = u / NDV, et = u - ct * NDV;
           const int e = et * 16 + r16;
 #pragma unroll
@@ -261,8 +268,8 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     if (emit) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
-        const int u = wave + 4 * m;
-        if (u < NST) {
+        const int u = wave - SW0 + NSW * m;
+        if (wave >= SW0 && u < NST) {
           const int ct = u / NDV, et = u - ct * NDV;
           const int e = et * 16 + r16;
 #pragma unroll
@@ -345,8 +352,10 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     // evaluated elementwise from b, which is written now (over k e^{-b} when it fits there)
     bool slow = false;
     if (emit) {
-      const f32x4 mx = *reinterpret_cast<const f32x4*>(sMax);
-      slow = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])) > kSlowDecayLog2;
+      float mxa = sMax[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mxa = fmaxf(mxa, sMax[w]);
+      slow = mxa > kSlowDecayLog2;
     }
     if (slow) {
 #pragma unroll
@@ -359,8 +368,8 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     // state carry first (independent of the outputs): S = diag(e^{b_last}) S + Kbar^T V
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
+      const int u = wave - SW0 + NSW * m;
+      if (wave >= SW0 && u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
 #pragma unroll
@@ -520,8 +529,8 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
     float* dst = p.states + (sbase + c_first) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
-      const int u = wave + 4 * m;
-      if (u < NST) {
+      const int u = wave - SW0 + NSW * m;
+      if (wave >= SW0 && u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const int e = et * 16 + r16;
 #pragma unroll
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(kFwdThreads) void gla_fwd_kernel(GlaFwdParams p, in
       }
     }
     __syncthreads();
-    for (int c = tid; c < dk; c += kFwdThreads)
+    for (int c = tid; c < dk; c += NTH)
       p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
   }
 }
@@ -547,9 +556,17 @@ static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
   *bytes = Lo::bytes(*nbuf);
 }
 
+// Waves per workgroup: eight for the DiG-S head shape (the query-row waves and the state
+// waves then run side by side), else four.
+template <typename T, int DK, int DV, bool EXACT>
+constexpr int fwd_waves() {
+  return (EXACT && sizeof(T) == 2 && DK == 32 && DV == 64) ? DIG_FWD_WAVES8 : 4;
+}
+
 template <typename T, int DK, int DV, bool EXACT, int C>
 static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
   const long BH = (long)s.B * s.H;
+  constexpr int NW = fwd_waves<T, DK, DV, EXACT>();
   int bytes_c, nbuf_c;
   fwd_lds<T, DK, DV, EXACT, C, true>(s, &bytes_c, &nbuf_c);
   if (lds_out) {  // size query only
@@ -559,14 +576,14 @@ static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st
   if (!s.prefix && s.nseg > 1) {
     int bytes_a, nbuf_a;
     fwd_lds<T, DK, DV, EXACT, C, false>(s, &bytes_a, &nbuf_a);
-    hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false>),
-                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(kFwdThreads), bytes_a, st, p,
+    hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false, NW>),
+                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(64 * NW), bytes_a, st, p,
                        nbuf_a);
     const hipError_t e = launch_gla_state_scan(s, p.states, p.seg_lg, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true>), dim3((unsigned)(BH * s.nseg)),
-                     dim3(kFwdThreads), bytes_c, st, p, nbuf_c);
+  hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW>),
+                     dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), bytes_c, st, p, nbuf_c);
   return hipGetLastError();
 }
 
