@@ -256,14 +256,14 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
-// N consecutive elements c0..c0+N-1 of a packed LDS row with `cols` elements; columns past
-// the row end, and every column of an invalid row, read as zero.  Whole 16- or 8-byte
-// vectors when the row pitch and the range allow it.
+// N consecutive elements c0..c0+N-1 of an LDS row with `cols` elements (row pitch
+// pitch_elems, default cols); columns past the row end, and every column of an invalid row,
+// read as zero.  Whole 16- or 8-byte vectors when the row pitch and the range allow it.
 template <typename T, int N>
 __device__ __forceinline__ void lds_row_read(T (&out)[N], const T* row, int c0, int cols,
-                                             bool valid) {
+                                             bool valid, int pitch_elems = -1) {
   constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T);
-  const int pitch = cols * (int)sizeof(T);
+  const int pitch = (pitch_elems < 0 ? cols : pitch_elems) * (int)sizeof(T);
   if (N % V16 == 0 && (pitch & 15) == 0 && c0 + N <= cols) {
 #pragma unroll
     for (int j = 0; j < N; j += V16) {
@@ -546,14 +546,18 @@ template <> struct PieceType<16> { using type = uint4; };
 template <> struct PieceType<8> { using type = uint2; };
 template <> struct PieceType<4> { using type = unsigned; };
 
-template <int RB, int ROWS, int NTH>
+// LDS row pitch LP bytes (>= RB; a padded pitch keeps accesses that walk rows conflict-free):
+// each piece is written as one store when LP keeps it aligned, else as 8- or 4-byte parts.
+template <int RB, int ROWS, int NTH, int LP = RB>
 struct RowRegs {
-  static_assert(RB % 4 == 0, "rows must be a whole number of dwords");
+  static_assert(RB % 4 == 0 && LP % 4 == 0 && LP >= RB, "row and pitch in dwords");
   static constexpr int PB = RB % 16 == 0 ? 16 : (RB % 8 == 0 ? 8 : 4);
   static constexpr int PR = RB / PB;                     // pieces per row
   static constexpr int NPC = ROWS * PR;                  // pieces in the tile
   static constexpr int NP = (NPC + NTH - 1) / NTH;       // pieces per thread
+  static constexpr int WB = LP % PB == 0 ? PB : (LP % 8 == 0 && PB % 8 == 0 ? 8 : 4);
   using P = typename PieceType<PB>::type;
+  using PW = typename PieceType<WB>::type;
   P v[NP];
   // Branch-free on purpose (a branch around a load makes the compiler's wait analysis
   // pessimistic): threads past the last piece repeat it, and rows >= valid load row valid-1
@@ -572,7 +576,10 @@ struct RowRegs {
       const int e = min(tid + NTH * m, NPC - 1), r = e / PR, c = e - r * PR;
       P x = v[m];
       if (r >= valid) x = P{};
-      *reinterpret_cast<P*>(lds + r * RB + c * PB) = x;
+      const PW* xs = reinterpret_cast<const PW*>(&x);
+#pragma unroll
+      for (int k = 0; k < PB / WB; ++k)
+        *reinterpret_cast<PW*>(lds + r * LP + c * PB + k * WB) = xs[k];
     }
   }
 };
@@ -581,18 +588,40 @@ struct RowRegs {
 // bytes apart, branch-free with a fixed number of stores per thread (so the compiler can
 // count them when it waits for loads issued earlier): threads past the last piece repeat it
 // and rows >= valid repeat row valid-1, i.e. the same bytes to the same address.
-template <int RB, int ROWS, int NTH>
+template <int RB, int ROWS, int NTH, int LP = RB>
 __device__ __forceinline__ void store_rows_fixed(unsigned char* gdst, long gstride,
                                                  const unsigned char* lds, int valid, int tid) {
-  using R = RowRegs<RB, ROWS, NTH>;
+  using R = RowRegs<RB, ROWS, NTH, LP>;
   using P = typename R::P;
+  using PW = typename R::PW;
 #pragma unroll
   for (int m = 0; m < R::NP; ++m) {
     const int e = min(tid + NTH * m, R::NPC - 1), c = e % R::PR;
     const int r = min(e / R::PR, valid - 1);
-    *reinterpret_cast<P*>(gdst + (long)r * gstride + c * R::PB) =
-        *reinterpret_cast<const P*>(lds + r * RB + c * R::PB);
+    P x;
+    PW* xs = reinterpret_cast<PW*>(&x);
+#pragma unroll
+    for (int k = 0; k < R::PB / R::WB; ++k)
+      xs[k] = *reinterpret_cast<const PW*>(lds + r * LP + c * R::PB + k * R::WB);
+    *reinterpret_cast<P*>(gdst + (long)r * gstride + c * R::PB) = x;
   }
+}
+
+// Row pitch (bytes, >= rb) at which one lane per row reading nb bytes of the row, with the
+// widest vector reads the pitch allows (16 or 8 bytes, as lds_row_read_k does), hits distinct
+// banks: P / w odd for the read width w.  Among the widths nb allows, the smallest such pitch
+// (wider reads on ties); rows of other widths fall back to 4-byte alignment.
+constexpr int odd_multiple_pitch(int rb, int w) {
+  int p = (rb + w - 1) / w * w;
+  if ((p / w) % 2 == 0) p += w;
+  return p;
+}
+constexpr int row_pitch(int rb, int nb) {
+  const int p16 = nb % 16 == 0 ? odd_multiple_pitch(rb, 16) : 1 << 30;
+  const int p8 = nb % 8 == 0 ? odd_multiple_pitch(rb, 8) : 1 << 30;
+  if (p16 <= p8 && p16 < (1 << 30)) return p16;
+  if (p8 < (1 << 30)) return p8;
+  return odd_multiple_pitch(rb, 4);
 }
 
 // Waits for this wave's outstanding memory operations (LDS DMA included).

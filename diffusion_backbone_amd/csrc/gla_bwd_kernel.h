@@ -47,13 +47,19 @@ constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
 
 // LDS layout (compile time).  LEAN drops the row-layout copies of dO, S0 and D (their
 // products then read the transposed copies with strided fragments) when the full layout
-// would not fit.
-template <typename T, int DK, int DV, int C, bool FIN, bool LEAN, int NW = 4>
+// would not fit.  PAD gives the raw staging rows pitches at which the gate pass (one lane
+// per token) reads without bank conflicts (register-staged rows only; LDS DMA writes rows
+// packed).  The fp32 per-token rows (b, q.dq - k.dk) have an odd pitch for the same reason.
+template <typename T, int DK, int DV, int C, bool FIN, bool LEAN, int NW = 4, bool PAD = false>
 struct BwdLayout {
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
   static constexpr int DKP = 16 * NDK, DVP = 16 * NDV;           // contraction pads (K 16)
   static constexpr int QP = DKP + 8, VP = DVP + 8, TP = C + 8;    // padded row pitches
+  static constexpr int NCL = DKP * C / (64 * NW), NEL = DVP * C / (64 * NW);  // gate columns
+  static constexpr int KPE = PAD ? row_pitch(DK * SZ, NCL * SZ) / SZ : DK;  // raw k pitch
+  static constexpr int VPE = PAD ? row_pitch(DV * SZ, NEL * SZ) / SZ : DV;  // raw v pitch
+  static constexpr int DKB = DK % 2 ? DK : DK + 1;                // fp32 row pitch (odd)
   // row layouts [token][dim]
   static constexpr int O_Q = 0;                                          // q e^{b}   [C][QP]
   static constexpr int O_K = O_Q + bal16(C * QP * SZ);                   // k e^{-b}  [C][QP]
@@ -73,35 +79,37 @@ struct BwdLayout {
                                       ? (FIN ? C * TP * SZ : 0) : 4 * 16 * C * SZ;
   static constexpr int O_DT = O_PT + bal16(FIN ? C * TP * SZ : 0);
   // fp32 scratch
-  static constexpr int O_B = O_DT + bal16(DT_BYTES);                 // b        [C][DK]
-  static constexpr int O_W = O_B + bal16(C * DK * 4);                // q.dq-k.dk [C][DK]
-  static constexpr int O_GAM = O_W + bal16(FIN ? C * DK * 4 : 0);    // e^{b_last}  [DKP]
+  static constexpr int O_B = O_DT + bal16(DT_BYTES);                 // b        [C][DKB]
+  static constexpr int O_W = O_B + bal16(C * DKB * 4);               // q.dq-k.dk [C][DKB]
+  static constexpr int O_GAM = O_W + bal16(FIN ? C * DKB * 4 : 0);   // e^{b_last}  [DKP]
   static constexpr int O_LG = O_GAM + bal16(DKP * 4);                // b_last / segment decay
   static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [NW]
   static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
   static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [NW][DVP]
   static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [C]
   static constexpr int O_RAW = O_DIAG + bal16(C * 4);
-  // raw staging: q, k, z, v, r, dy rows packed with the runtime row length
+  // raw staging: q, k, z (pitch KPE, or the runtime d_k when packed), v, r, dy (pitch VPE)
   static constexpr int R_Q = 0;
-  static constexpr int R_K = R_Q + bal16(C * DK * SZ);
-  static constexpr int R_Z = R_K + bal16(C * DK * SZ);
-  static constexpr int R_V = R_Z + bal16(C * DK * SZ);
-  static constexpr int R_R = R_V + bal16(C * (DV > 2 * DK ? DV : 2 * DK) * SZ);  // v; dq|dk
-  static constexpr int R_DY = R_R + bal16(C * DV * SZ);
-  static constexpr int SLOT = R_DY + bal16(C * DV * SZ);
+  static constexpr int R_K = R_Q + bal16(C * KPE * SZ);
+  static constexpr int R_Z = R_K + bal16(C * KPE * SZ);
+  static constexpr int R_V = R_Z + bal16(C * KPE * SZ);
+  static constexpr int R_R = R_V + bal16(C * (VPE > 2 * KPE ? VPE : 2 * KPE) * SZ);  // v; dq|dk
+  static constexpr int R_DY = R_R + bal16(C * VPE * SZ);
+  static constexpr int SLOT = R_DY + bal16(C * VPE * SZ);
   static constexpr int bytes = O_RAW + SLOT;
 };
 constexpr int kBwdLdsBudget = 160 * 1024;
-template <typename T, int DK, int DV, int C, bool FIN, int NW = 4>
+template <typename T, int DK, int DV, int C, bool FIN, int NW = 4, bool PAD = false>
 constexpr bool bwd_lean() {
-  return BwdLayout<T, DK, DV, C, FIN, false, NW>::bytes > kBwdLdsBudget;
+  return BwdLayout<T, DK, DV, C, FIN, false, NW, PAD>::bytes > kBwdLdsBudget;
 }
 
 template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
-  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW>();
-  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW>;
+  constexpr bool PF = EXACT;  // register prefetch of the next chunk's raw rows
+  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
+  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF>;
+  constexpr int KPE = Lo::KPE, VPE = Lo::VPE, DKB = Lo::DKB;
   constexpr int NTH = 64 * NW;  // NW waves
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP;
@@ -115,7 +123,6 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
   using Acc = typename std::conditional<kBf, float, double>::type;
-  constexpr bool PF = EXACT;  // register prefetch of the next chunk's raw rows
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -153,8 +160,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);
   T* rawz = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Z);  // then dz
   T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);  // then dq | dk
+  // raw row pitches: padded for register-staged rows, the runtime widths for DMA-staged ones
+  const int kp = PF ? KPE : dk, vp = PF ? VPE : dv;
   T* sdqs = rawv;
-  T* sdks = rawv + C * dk;
+  T* sdks = rawv + C * kp;
   T* sRr = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_R);   // r, then dr
   T* sDy = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_DY);  // dy, then dv
 
@@ -223,8 +232,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
   };
 
-  RowRegs<DK * (int)sizeof(T), C, NTH> pq, pk, pz;
-  RowRegs<DV * (int)sizeof(T), C, NTH> pv, pr, pdy;
+  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pq, pk, pz;
+  RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv, pr, pdy;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
@@ -358,16 +367,16 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       const bool tv = tg < valid;
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
       if constexpr (FULLK) {
-        lds_row_read_k<T, NCL, DK>(zr, rawz + tg * DK, c0, tv);
-        lds_row_read_k<T, NCL, DK>(kr, rawk + tg * DK, c0, tv);
-        lds_row_read_k<T, NCL, DK>(qr, rawq + tg * DK, c0, tv);
+        lds_row_read_k<T, NCL, KPE>(zr, rawz + tg * KPE, c0, tv);
+        lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
+        lds_row_read_k<T, NCL, KPE>(qr, rawq + tg * KPE, c0, tv);
       } else {
-        lds_row_read<T, NCL>(zr, rawz + tg * dk, c0, dk, tv);
-        lds_row_read<T, NCL>(kr, rawk + tg * dk, c0, dk, tv);
-        lds_row_read<T, NCL>(qr, rawq + tg * dk, c0, dk, tv);
+        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
+        lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
+        lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
-      if constexpr (FULLV) lds_row_read_k<T, NEL, DV>(vr, rawv + tg * DV, e0, tv);
-      else lds_row_read<T, NEL>(vr, rawv + tg * dv, e0, dv, tv);
+      if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
+      else lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
 
       float bb[NCL], bl[NCL];
 #pragma unroll
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           sQt[(c0 + j) * TP + tg] = qs[j];
           if (own) sKt[(c0 + j) * TP + tg] = ks[j];
         }
-        if (FULLK || c0 + j < dk) sB[tg * DK + c0 + j] = bb[j];
+        if (FULLK || c0 + j < dk) sB[tg * DKB + c0 + j] = bb[j];
       }
       if (lane == 0) sMax[wave] = md;
       if (tg == C - 1) {
@@ -446,11 +455,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         const int ir = 16 * I + r16;
         T qd[DQ], kd[DQ];
         if constexpr (FULLK) {
-          lds_row_read_k<T, DQ, DK>(qd, rawq + ir * DK, g4 * DQ, true);
-          lds_row_read_k<T, DQ, DK>(kd, rawk + ir * DK, g4 * DQ, true);
+          lds_row_read_k<T, DQ, KPE>(qd, rawq + ir * KPE, g4 * DQ, true);
+          lds_row_read_k<T, DQ, KPE>(kd, rawk + ir * KPE, g4 * DQ, true);
         } else {
-          lds_row_read<T, DQ>(qd, rawq + ir * dk, g4 * DQ, dk, true);
-          lds_row_read<T, DQ>(kd, rawk + ir * dk, g4 * DQ, dk, true);
+          lds_row_read<T, DQ>(qd, rawq + ir * kp, g4 * DQ, dk, true, kp);
+          lds_row_read<T, DQ>(kd, rawk + ir * kp, g4 * DQ, dk, true, kp);
         }
         Acc acc = 0;
 #pragma unroll
@@ -473,8 +482,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           if (j <= ir && ir < valid) {
 #pragma unroll 1
             for (int c = 0; c < dk; ++c)
-              acc += to_f(rawq[ir * dk + c]) * to_f(rawk[j * dk + c]) *
-                     Fm<T>::exp2(sB[ir * DK + c] - sB[j * DK + c]);
+              acc += to_f(rawq[ir * kp + c]) * to_f(rawk[j * kp + c]) *
+                     Fm<T>::exp2(sB[ir * DKB + c] - sB[j * DKB + c]);
             acc *= p.q_scale;
           }
           sPw[idx] = from_f<T>(acc);
@@ -572,8 +581,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int e = E * 16 + r16, row = 16 * I + 4 * g4 + i;
           const bool on = (FULLV || e < dv) && row < valid;  // stale rows past the end: 0
-          rr[E][i] = on ? sRr[row * dv + e] : from_f<T>(0.f);
-          dyr[E][i] = on ? sDy[row * dv + e] : from_f<T>(0.f);
+          rr[E][i] = on ? sRr[row * vp + e] : from_f<T>(0.f);
+          dyr[E][i] = on ? sDy[row * vp + e] : from_f<T>(0.f);
         }
       float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -596,7 +605,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           const float sg = Fm<T>::sig(rv), sw = rv * sg;
           if (own && (FULLV || e < dv)) {
             dgam[E] += dyv * nv * sw;
-            sRr[row * dv + e] = from_f<T>(dyv * nv * gm[E] * sg * (1.f + rv * (1.f - sg)));
+            sRr[row * vp + e] = from_f<T>(dyv * nv * gm[E] * sg * (1.f + rv * (1.f - sg)));
           }
           dn[E][i] = dyv * gm[E] * sw;
           md[i] += dn[E][i] * nv;
@@ -688,7 +697,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int t = 16 * I + 4 * g4 + i;
-              const float bt = sB[t * DK + c];
+              const float bt = sB[t * DKB + c];
               float dq, dkk;
               if (!slow) {  // a3 holds V (e^{b_last} G)^T here
                 dq = Fm<T>::exp2(bt) * (a1[i] + a2[i]);
@@ -697,19 +706,19 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
                 float s1 = 0.f, s2 = 0.f;
 #pragma unroll 1
                 for (int j = 0; j <= t && j < valid; ++j)
-                  s1 += to_f(LEAN ? sDt[j * TP + t] : sD[t * TP + j]) * to_f(rawk[j * dk + c]) *
-                        Fm<T>::exp2(bt - sB[j * DK + c]);
+                  s1 += to_f(LEAN ? sDt[j * TP + t] : sD[t * TP + j]) * to_f(rawk[j * kp + c]) *
+                        Fm<T>::exp2(bt - sB[j * DKB + c]);
 #pragma unroll 1
                 for (int i2 = t; i2 < valid; ++i2)
-                  s2 += to_f(sDt[t * TP + i2]) * to_f(rawq[i2 * dk + c]) * p.q_scale *
-                        Fm<T>::exp2(sB[i2 * DK + c] - bt);
+                  s2 += to_f(sDt[t * TP + i2]) * to_f(rawq[i2 * kp + c]) * p.q_scale *
+                        Fm<T>::exp2(sB[i2 * DKB + c] - bt);
                 dq = Fm<T>::exp2(bt) * a1[i] + s1;
                 dkk = s2 + Fm<T>::exp2(blast - bt) * a3[i];
               }
-              const float qf = to_f(rawq[t * dk + c]) * p.q_scale, kf = to_f(rawk[t * dk + c]);
-              sW[t * DK + c] = qf * dq - kf * dkk;
-              sdqs[t * dk + c] = from_f<T>(p.q_scale * dq);
-              sdks[t * dk + c] = from_f<T>(dkk);
+              const float qf = to_f(rawq[t * kp + c]) * p.q_scale, kf = to_f(rawk[t * kp + c]);
+              sW[t * DKB + c] = qf * dq - kf * dkk;
+              sdqs[t * kp + c] = from_f<T>(p.q_scale * dq);
+              sdks[t * kp + c] = from_f<T>(dkk);
             }
           }
         }
@@ -731,14 +740,14 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
               float acc = 0.f;
 #pragma unroll 1
               for (int c = 0; c < dk; ++c)
-                acc += to_f(rawk[j * dk + c]) * Fm<T>::exp2(sLg[c] - sB[j * DK + c]) *
+                acc += to_f(rawk[j * kp + c]) * Fm<T>::exp2(sLg[c] - sB[j * DKB + c]) *
                        to_f(sGt[e * QP + c]);
               dva[i] += acc;
             }
           }
           if (FULLV || e < dv) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * dv + e] = from_f<T>(dva[i]);
+            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * vp + e] = from_f<T>(dva[i]);
           }
         }
       }
@@ -769,8 +778,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       for (int j = 0; j < NCL; ++j) {
         const int c = c0 + j;
         const bool on = tv && (FULLK || c < dk);
-        w[j] = on ? sW[tr * DK + c] : 0.f;
-        zr[j] = on ? rawz[tr * dk + c] : from_f<T>(0.f);
+        w[j] = on ? sW[tr * DKB + c] : 0.f;
+        zr[j] = on ? rawz[tr * kp + c] : from_f<T>(0.f);
       }
       float bterm[NCL];
 #pragma unroll
@@ -788,7 +797,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         if (tv && (FULLK || c < dk)) {
           float dla = w[j] + bterm[j];
           if (n == 0 && tr == 0) dla = 0.f;  // alpha_0 multiplies the zero initial state
-          rawz[tr * dk + c] = from_f<T>(dla * Fm<T>::sig(-to_f(zr[j])) * inv_tau);
+          rawz[tr * kp + c] = from_f<T>(dla * Fm<T>::sig(-to_f(zr[j])) * inv_tau);
         }
       }
       __syncthreads();
@@ -800,16 +809,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       if constexpr (PF) {
         constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
         using UC = unsigned char;
-        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
-                                             reinterpret_cast<const UC*>(sdqs), valid, tid);
-        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
-                                             reinterpret_cast<const UC*>(sdks), valid, tid);
-        store_rows_fixed<RK, C, NTH>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
-                                             reinterpret_cast<const UC*>(rawz), valid, tid);
-        store_rows_fixed<RV, C, NTH>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
-                                             reinterpret_cast<const UC*>(sDy), valid, tid);
-        store_rows_fixed<RV, C, NTH>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
-                                             reinterpret_cast<const UC*>(sRr), valid, tid);
+        constexpr int LK = KPE * (int)sizeof(T), LV = VPE * (int)sizeof(T);
+        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
+                                         reinterpret_cast<const UC*>(sdqs), valid, tid);
+        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
+                                         reinterpret_cast<const UC*>(sdks), valid, tid);
+        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
+                                         reinterpret_cast<const UC*>(rawz), valid, tid);
+        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
+                                         reinterpret_cast<const UC*>(sDy), valid, tid);
+        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
+                                         reinterpret_cast<const UC*>(sRr), valid, tid);
       } else {
         store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, NTH);
         store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, NTH);
@@ -877,9 +887,10 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   const long BH = (long)s.B * s.H;
   constexpr int NW = bwd_waves<T, DK, DV, EXACT>();
   constexpr int fin_bytes =
-      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW>(), NW>::bytes;
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, EXACT>(), NW, EXACT>::bytes;
   constexpr int a_bytes =
-      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW>(), NW>::bytes;
+      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, EXACT>(), NW,
+                EXACT>::bytes;
   if (lds_out) {
     *lds_out = fin_bytes;
     return hipSuccess;

@@ -46,7 +46,9 @@ constexpr int kFwdLdsBudget = 160 * 1024;
 
 constexpr int al16(int x) { return (x + 15) / 16 * 16; }
 
-template <typename T, int DK, int DV, int C, bool OUT>
+// PAD: raw staging rows at pitches the gate pass (one lane per token) reads without bank
+// conflicts (register-staged rows; LDS DMA writes them packed).
+template <typename T, int DK, int DV, int C, bool OUT, int NW = 4, bool PAD = false>
 struct FwdLayout {
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
@@ -54,6 +56,7 @@ struct FwdLayout {
   static constexpr int DVP = NDV * 16;
   static constexpr int CK = SZ == 2 ? ((C + 31) / 32) * 32 : C;  // token dim padded
   static constexpr int QP = DKP + 8, TP = CK + 8;              // padded LDS row pitches
+  static constexpr int NCL = DKP * C / (64 * NW), NEL = DVP * C / (64 * NW);  // gate columns
   // byte offsets: operands, state copy, gates, misc; the raw staging slots come last
   static constexpr int O_Q = 0;                                         // q e^{b}  [C][QP]
   static constexpr int O_K = O_Q + al16(OUT ? C * QP * SZ : 0);          // k e^{-b} [C][QP]
@@ -69,20 +72,35 @@ struct FwdLayout {
   static constexpr int O_LG = O_GAM + al16(DKP * 4);                     // segment decay
   static constexpr int O_MAX = O_LG + al16(DKP * 4);                     // per-wave decay
   static constexpr int O_RAW = O_MAX + 64;
-  // one staging slot: raw k, z, v (+ q, r) rows, packed with the runtime row length
+  // one staging slot: raw k, z, v (+ q, r) rows at pitches KPE, VPE (elements; the runtime
+  // widths when DMA-staged).  A padded pitch is kept only if it does not cost the second
+  // workgroup per CU.
+  static constexpr int slot_bytes(int kpe, int vpe) {
+    return al16(C * kpe * SZ) * 2 + al16(C * vpe * SZ) +
+           (OUT ? al16(C * kpe * SZ) + al16(C * vpe * SZ) : 0);
+  }
+  static constexpr int HALF_CU = 80 * 1024;
+  static constexpr bool fits(int kpe, int vpe) {
+    return O_RAW + slot_bytes(kpe, vpe) <= HALF_CU || O_RAW + slot_bytes(DK, DV) > HALF_CU;
+  }
+  static constexpr int KPAD = row_pitch(DK * SZ, NCL * SZ) / SZ;
+  static constexpr int VPAD = row_pitch(DV * SZ, NEL * SZ) / SZ;
+  static constexpr int KPE = PAD && fits(KPAD, DV) ? KPAD : DK;
+  static constexpr int VPE = PAD && fits(KPE, VPAD) ? VPAD : DV;
   static constexpr int R_K = 0;
-  static constexpr int R_Z = R_K + al16(C * DK * SZ);
-  static constexpr int R_V = R_Z + al16(C * DK * SZ);
-  static constexpr int R_Q = R_V + al16(C * DV * SZ);
-  static constexpr int R_R = R_Q + al16(OUT ? C * DK * SZ : 0);
-  static constexpr int SLOT = R_R + al16(OUT ? C * DV * SZ : 0);
+  static constexpr int R_Z = R_K + al16(C * KPE * SZ);
+  static constexpr int R_V = R_Z + al16(C * KPE * SZ);
+  static constexpr int R_Q = R_V + al16(C * VPE * SZ);
+  static constexpr int R_R = R_Q + al16(OUT ? C * KPE * SZ : 0);
+  static constexpr int SLOT = R_R + al16(OUT ? C * VPE * SZ : 0);
   static constexpr int bytes(int nbuf) { return O_RAW + nbuf * SLOT; }
 };
 
 template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW>
 __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
   constexpr int NTH = 64 * NW;  // NW waves
-  using Lo = FwdLayout<T, DK, DV, C, OUT>;
+  using Lo = FwdLayout<T, DK, DV, C, OUT, NW, EXACT>;
+  constexpr int KPE = Lo::KPE, VPE = Lo::VPE;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
   constexpr int QP = Lo::QP, TP = Lo::TP;
@@ -156,8 +174,8 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     }
   };
   // exact shapes: the raw rows of a chunk in registers (loaded one iteration ahead)
-  RowRegs<DK * (int)sizeof(T), C, NTH> pk, pz, pq;
-  RowRegs<DV * (int)sizeof(T), C, NTH> pv, pr;
+  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pk, pz, pq;
+  RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv, pr;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
@@ -237,6 +255,8 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     const T* rawv = reinterpret_cast<const T*>(raw + Lo::R_V);
     const T* rawq = reinterpret_cast<const T*>(raw + Lo::R_Q);
     const T* sR = reinterpret_cast<const T*>(raw + Lo::R_R);
+    // raw row pitches: padded for register-staged rows, the runtime widths for DMA-staged ones
+    const int kp = PF ? KPE : dk, vp = PF ? VPE : dv;
     const bool emit = OUT && n >= c_first;
     const int t0 = n * C;
     const int valid = min(C, p.L - t0);
@@ -292,16 +312,16 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       const bool tv = tg < valid;
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
       if constexpr (FULLK) {
-        lds_row_read_k<T, NCL, DK>(zr, rawz + tg * DK, c0, tv);
-        lds_row_read_k<T, NCL, DK>(kr, rawk + tg * DK, c0, tv);
-        if (emit) lds_row_read_k<T, NCL, DK>(qr, rawq + tg * DK, c0, tv);
+        lds_row_read_k<T, NCL, KPE>(zr, rawz + tg * KPE, c0, tv);
+        lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
+        if (emit) lds_row_read_k<T, NCL, KPE>(qr, rawq + tg * KPE, c0, tv);
       } else {
-        lds_row_read<T, NCL>(zr, rawz + tg * dk, c0, dk, tv);
-        lds_row_read<T, NCL>(kr, rawk + tg * dk, c0, dk, tv);
-        if (emit) lds_row_read<T, NCL>(qr, rawq + tg * dk, c0, dk, tv);
+        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
+        lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
+        if (emit) lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
-      if constexpr (FULLV) lds_row_read_k<T, NEL, DV>(vr, rawv + tg * DV, e0, tv);
-      else lds_row_read<T, NEL>(vr, rawv + tg * dv, e0, dv, tv);
+      if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
+      else lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
 
       float bl[NCL];
 #pragma unroll
@@ -388,11 +408,11 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         const int ir = 16 * I + r16;
         T qd[DQ], kd[DQ];
         if constexpr (FULLK) {
-          lds_row_read_k<T, DQ, DK>(qd, rawq + ir * DK, g4 * DQ, true);
-          lds_row_read_k<T, DQ, DK>(kd, rawk + ir * DK, g4 * DQ, true);
+          lds_row_read_k<T, DQ, KPE>(qd, rawq + ir * KPE, g4 * DQ, true);
+          lds_row_read_k<T, DQ, KPE>(kd, rawk + ir * KPE, g4 * DQ, true);
         } else {
-          lds_row_read<T, DQ>(qd, rawq + ir * dk, g4 * DQ, dk, true);
-          lds_row_read<T, DQ>(kd, rawk + ir * dk, g4 * DQ, dk, true);
+          lds_row_read<T, DQ>(qd, rawq + ir * kp, g4 * DQ, dk, true, kp);
+          lds_row_read<T, DQ>(kd, rawk + ir * kp, g4 * DQ, dk, true, kp);
         }
         Acc acc = 0;
 #pragma unroll
@@ -415,14 +435,14 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         for (int J = 0; J < NT; ++J) pt[J] = zero4();
 #pragma unroll 1
         for (int c = 0; c < dk; ++c) {
-          const float qc = to_f(rawq[ir * dk + c]) * p.q_scale, bq = sB[ir * DK + c];
+          const float qc = to_f(rawq[ir * kp + c]) * p.q_scale, bq = sB[ir * DK + c];
 #pragma unroll
           for (int J = 0; J < NT; ++J) {
             if (J <= I) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int j = 16 * J + 4 * g4 + i;
-                pt[J][i] += qc * to_f(rawk[j * dk + c]) * Fm<T>::exp2(bq - sB[j * DK + c]);
+                pt[J][i] += qc * to_f(rawk[j * kp + c]) * Fm<T>::exp2(bq - sB[j * DK + c]);
               }
             }
           }
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = E * 16 + r16;
-          rr[E][i] = (FULLV || e < dv) ? sR[(16 * I + 4 * g4 + i) * dv + e] : from_f<T>(0.f);
+          rr[E][i] = (FULLV || e < dv) ? sR[(16 * I + 4 * g4 + i) * vp + e] : from_f<T>(0.f);
         }
       float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -546,21 +566,21 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   }
 }
 
-// LDS bytes and staging slots of one launch.  Exact shapes prefetch into registers (one
-// slot); tile classes use two DMA slots when a workgroup walks more than one chunk and they fit.
-template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
-static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
-  using Lo = FwdLayout<T, DK, DV, C, OUT>;
-  const int walk = (OUT && s.prefix) ? s.NC : s.sc;
-  *nbuf = (!EXACT && walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
-  *bytes = Lo::bytes(*nbuf);
-}
-
 // Waves per workgroup: eight for the DiG-S head shape (the query-row waves and the state
 // waves then run side by side), else four.
 template <typename T, int DK, int DV, bool EXACT>
 constexpr int fwd_waves() {
   return (EXACT && sizeof(T) == 2 && DK == 32 && DV == 64) ? DIG_FWD_WAVES8 : 4;
+}
+
+// LDS bytes and staging slots of one launch.  Exact shapes prefetch into registers (one
+// slot); tile classes use two DMA slots when a workgroup walks more than one chunk and they fit.
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
+static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
+  using Lo = FwdLayout<T, DK, DV, C, OUT, fwd_waves<T, DK, DV, EXACT>(), EXACT>;
+  const int walk = (OUT && s.prefix) ? s.NC : s.sc;
+  *nbuf = (!EXACT && walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
+  *bytes = Lo::bytes(*nbuf);
 }
 
 template <typename T, int DK, int DV, bool EXACT, int C>
