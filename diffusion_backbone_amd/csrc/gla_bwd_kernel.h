@@ -86,8 +86,9 @@ struct BwdLayout {
   static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [NW]
   static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
   static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [NW][DVP]
-  static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [C]
-  static constexpr int O_RAW = O_DIAG + bal16(C * 4);
+  static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [2][C] (halves)
+  static constexpr int O_XCH = O_DIAG + bal16(2 * C * 4);            // [4][C] row sums
+  static constexpr int O_RAW = O_XCH + bal16(4 * C * 4);
   // raw staging: q, k, z (pitch KPE, or the runtime d_k when packed), v, r, dy (pitch VPE)
   static constexpr int R_Q = 0;
   static constexpr int R_K = R_Q + bal16(C * KPE * SZ);
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   float* sPart = reinterpret_cast<float*>(smem + Lo::O_PART);
   float* sDg = reinterpret_cast<float*>(smem + Lo::O_DG);
   float* sDiag = reinterpret_cast<float*>(smem + Lo::O_DIAG);
+  float* sXch = reinterpret_cast<float*>(smem + Lo::O_XCH);
   T* sSlow = reinterpret_cast<T*>(smem + Lo::O_DT);  // strong-decay P rows (recompute only)
   T* rawq = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Q);
   T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);
@@ -447,8 +449,38 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
 
     // ------------------------------------------------------------ recompute phase
-    if (wave < NT) {
-      const int I = wave;
+    // Row tile I = wave % NT; with at least twice as many waves as row tiles, the two waves
+    // of a row tile split its value tiles (half h = wave / NT) and exchange the RMSNorm row
+    // sums through LDS (two extra barriers); the gated Q K^T tile is formed by both.
+    constexpr int SPL = NW >= 2 * NT ? 2 : 1;
+    constexpr int NDVH = (NDV + SPL - 1) / SPL;            // value tiles per half
+    const bool part = wave < NT * SPL;
+    const int I = wave % NT, hh = wave / NT;
+    const int E0 = hh * NDVH;
+    f32x4 pt[NT];  // pt[J][i] = P[16I + r16][16J + 4 g4 + i]
+    f32x4 oacc[NDVH];
+    T rr[NDVH][4], dyr[NDVH][4];
+    float ss[4] = {0.f, 0.f, 0.f, 0.f}, md[4] = {0.f, 0.f, 0.f, 0.f}, rstd[4];
+    float dn[NDVH][4];
+    if (slow) {  // strong decay: P rows elementwise, one copy per row tile (uniform branch)
+      if (part && hh == 0) {
+        T* sPw = sSlow + I * 16 * C;
+        for (int idx = lane; idx < 16 * C; idx += 64) {
+          const int rq = idx / C, j = idx - rq * C, ir = 16 * I + rq;
+          float acc = 0.f;
+          if (j <= ir && ir < valid) {
+#pragma unroll 1
+            for (int c = 0; c < dk; ++c)
+              acc += to_f(rawq[ir * kp + c]) * to_f(rawk[j * kp + c]) *
+                     Fm<T>::exp2(sB[ir * DKB + c] - sB[j * DKB + c]);
+            acc *= p.q_scale;
+          }
+          sPw[idx] = from_f<T>(acc);
+        }
+      }
+      __syncthreads();
+    }
+    if (part) {
       float diag;  // exact q_i.k_i from the unscaled inputs (gate factor 1)
       {
         constexpr int DQ = DKP / 4;
@@ -469,25 +501,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         // rows past the sequence end hold stale staging data: they must stay exactly zero
         diag = ir < valid ? (float)acc * p.q_scale : 0.f;
       }
-      f32x4 pt[NT];  // pt[J][i] = P[16I + r16][16J + 4 g4 + i]
       if (!slow) {
 #pragma unroll
         for (int J = 0; J < NT; ++J)
           pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
       } else {
-        T* sPw = sSlow + wave * 16 * C;
-        for (int idx = lane; idx < 16 * C; idx += 64) {
-          const int rr = idx / C, j = idx - rr * C, ir = 16 * I + rr;
-          float acc = 0.f;
-          if (j <= ir && ir < valid) {
-#pragma unroll 1
-            for (int c = 0; c < dk; ++c)
-              acc += to_f(rawq[ir * kp + c]) * to_f(rawk[j * kp + c]) *
-                     Fm<T>::exp2(sB[ir * DKB + c] - sB[j * DKB + c]);
-            acc *= p.q_scale;
-          }
-          sPw[idx] = from_f<T>(acc);
-        }
+        const T* sPw = sSlow + I * 16 * C;
 #pragma unroll
         for (int J = 0; J < NT; ++J)
 #pragma unroll
@@ -502,16 +521,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             if (4 * g4 + i == r16) pt[J][i] = diag;
           }
         }
-        if (own && J <= I) {  // P^T for dv (tiles above the diagonal stay zero)
+        if (own && hh == 0 && J <= I) {  // P^T for dv (tiles above the diagonal stay zero)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sPt[(16 * J + 4 * g4 + i) * TP + 16 * I + r16] = from_f<T>(pt[J][i]);
         }
       }
-      f32x4 oacc[NDV];
 #pragma unroll
-      for (int E = 0; E < NDV; ++E)
-        oacc[E] = Mma<T>::kc(zero4(), sQ, QP, 16 * I, sS0t, QP, 16 * E, DKP, lane);
+      for (int Eh = 0; Eh < NDVH; ++Eh) {
+        const int E = min(E0 + Eh, NDV - 1);
+        oacc[Eh] = Mma<T>::kc(zero4(), sQ, QP, 16 * I, sS0t, QP, 16 * E, DKP, lane);
+      }
       if constexpr (kBf) {
 #pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {  // token tiles in pairs: one K = 32 step
@@ -524,15 +544,15 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
               a[4 + i] = from_f<bf16>(hi_on ? pt[2 * pp + 1][i] : 0.f);
             }
 #pragma unroll
-            for (int E = 0; E < NDV; ++E) {
-              const int e = E * 16 + r16;
+            for (int Eh = 0; Eh < NDVH; ++Eh) {
+              const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
               bf16x8 bv;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 bv[i] = sV[(32 * pp + 4 * g4 + i) * VP + e];
                 bv[4 + i] = sV[(32 * pp + 16 + 4 * g4 + i) * VP + e];
               }
-              oacc[E] = mfma_bf16(a, bv, oacc[E]);
+              oacc[Eh] = mfma_bf16(a, bv, oacc[Eh]);
             }
           }
         }
@@ -546,14 +566,15 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
               a[4 + i] = from_f<bf16>(0.f);
             }
 #pragma unroll
-            for (int E = 0; E < NDV; ++E) {
+            for (int Eh = 0; Eh < NDVH; ++Eh) {
+              const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
               bf16x8 bv;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                bv[i] = sV[(16 * J + 4 * g4 + i) * VP + E * 16 + r16];
+                bv[i] = sV[(16 * J + 4 * g4 + i) * VP + e];
                 bv[4 + i] = from_f<bf16>(0.f);
               }
-              oacc[E] = mfma_bf16(a, bv, oacc[E]);
+              oacc[Eh] = mfma_bf16(a, bv, oacc[Eh]);
             }
           }
         }
@@ -564,72 +585,119 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-              for (int E = 0; E < NDV; ++E) {
-                const float bv = to_f(sV[(16 * J + 4 * g4 + s4) * VP + E * 16 + r16]);
-                oacc[E] = mfma_f32(pt[J][s4], bv, oacc[E]);
+              for (int Eh = 0; Eh < NDVH; ++Eh) {
+                const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
+                const float bv = to_f(sV[(16 * J + 4 * g4 + s4) * VP + e]);
+                oacc[Eh] = mfma_f32(pt[J][s4], bv, oacc[Eh]);
               }
             }
           }
         }
       }
 
-      // output-stage backward: r, dy first (one LDS round trip)
-      T rr[NDV][4], dyr[NDV][4];
+      // output-stage backward: r, dy first (one LDS round trip); value tiles past this
+      // half's range (an odd tile count) count as zero columns
 #pragma unroll
-      for (int E = 0; E < NDV; ++E)
+      for (int Eh = 0; Eh < NDVH; ++Eh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = E * 16 + r16, row = 16 * I + 4 * g4 + i;
-          const bool on = (FULLV || e < dv) && row < valid;  // stale rows past the end: 0
-          rr[E][i] = on ? sRr[row * vp + e] : from_f<T>(0.f);
-          dyr[E][i] = on ? sDy[row * vp + e] : from_f<T>(0.f);
+          const int e = (E0 + Eh) * 16 + r16, row = 16 * I + 4 * g4 + i;
+          const bool on = E0 + Eh < NDV && (FULLV || e < dv) && row < valid;  // stale rows: 0
+          rr[Eh][i] = on ? sRr[row * vp + e] : from_f<T>(0.f);
+          dyr[Eh][i] = on ? sDy[row * vp + e] : from_f<T>(0.f);
+          if (E0 + Eh >= NDV) oacc[Eh][i] = 0.f;
         }
-      float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int E = 0; E < NDV; ++E)
+      for (int Eh = 0; Eh < NDVH; ++Eh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ss[i] += oacc[E][i] * oacc[E][i];
-      float rstd[4], md[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) ss[i] += oacc[Eh][i] * oacc[Eh][i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) / (float)dv + p.eps);
+      for (int i = 0; i < 4; ++i) ss[i] = row_sum16(ss[i]);
+      if constexpr (SPL > 1) {
+        if (r16 == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sXch[hh * C + 16 * I + 4 * g4 + i] = ss[i];
+        }
+      }
+    }
+    if constexpr (SPL > 1) __syncthreads();  // row sums of both halves
+    if (part) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float tot = ss[i];
+        if constexpr (SPL > 1) {
+          const int row = 16 * I + 4 * g4 + i;
+          tot = sXch[row] + sXch[C + row];
+        }
+        rstd[i] = rsqrtf(tot / (float)dv + p.eps);
+      }
       // oacc becomes the normalised output, dn = dy * w * swish(r)
-      float dn[NDV][4];
 #pragma unroll
-      for (int E = 0; E < NDV; ++E) {
-        const int e = E * 16 + r16;
+      for (int Eh = 0; Eh < NDVH; ++Eh) {
+        const int E = min(E0 + Eh, NDV - 1), e = (E0 + Eh) * 16 + r16;
+        const bool col_on = E0 + Eh < NDV && (FULLV || e < dv);
+        float gmE = gm[0];
+#pragma unroll
+        for (int k = 1; k < NDV; ++k) gmE = k == E ? gm[k] : gmE;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          oacc[E][i] *= rstd[i];
+          oacc[Eh][i] *= rstd[i];
           const int row = 16 * I + 4 * g4 + i;
-          const float nv = oacc[E][i], rv = to_f(rr[E][i]), dyv = to_f(dyr[E][i]);
+          const float nv = oacc[Eh][i], rv = to_f(rr[Eh][i]), dyv = to_f(dyr[Eh][i]);
           const float sg = Fm<T>::sig(rv), sw = rv * sg;
-          if (own && (FULLV || e < dv)) {
-            dgam[E] += dyv * nv * sw;
-            sRr[row * vp + e] = from_f<T>(dyv * nv * gm[E] * sg * (1.f + rv * (1.f - sg)));
+          if (own && col_on) {
+            // register arrays take compile-time indices only (a runtime one sends them to
+            // scratch memory): dgam[E] via a select over every tile
+#pragma unroll
+            for (int k = 0; k < NDV; ++k)
+              if (k == E) dgam[k] += dyv * nv * sw;
+            sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
           }
-          dn[E][i] = dyv * gm[E] * sw;
-          md[i] += dn[E][i] * nv;
+          dn[Eh][i] = dyv * gmE * sw;
+          md[i] += dn[Eh][i] * nv;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) md[i] = row_sum16(md[i]) / (float)dv;
+      for (int i = 0; i < 4; ++i) md[i] = row_sum16(md[i]);
+      if constexpr (SPL > 1) {
+        if (r16 == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sXch[(2 + hh) * C + 16 * I + 4 * g4 + i] = md[i];
+        }
+      }
+    }
+    if constexpr (SPL > 1) __syncthreads();  // dn.o row sums of both halves
+    if (part) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float tot = md[i];
+        if constexpr (SPL > 1) {
+          const int row = 16 * I + 4 * g4 + i;
+          tot = sXch[2 * C + row] + sXch[3 * C + row];
+        }
+        md[i] = tot / (float)dv;
+      }
       Acc dvd[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int E = 0; E < NDV; ++E) {
-        const int e = E * 16 + r16;
-        T dov4[4];
+      for (int Eh = 0; Eh < NDVH; ++Eh) {
+        if (E0 + Eh < NDV) {
+          const int e = (E0 + Eh) * 16 + r16;
+          T dov4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * I + 4 * g4 + i;
-          const float dov = (FULLV || e < dv) ? rstd[i] * (dn[E][i] - oacc[E][i] * md[i]) : 0.f;
-          dov4[i] = from_f<T>(dov);
-          if constexpr (!LEAN) sdO[row * VP + e] = dov4[i];
-          dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * I + 4 * g4 + i;
+            const float dov =
+                (FULLV || e < dv) ? rstd[i] * (dn[Eh][i] - oacc[Eh][i] * md[i]) : 0.f;
+            dov4[i] = from_f<T>(dov);
+            if constexpr (!LEAN) sdO[row * VP + e] = dov4[i];
+            dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
+          }
+          lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
         }
-        lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
       }
       // do_i is orthogonal to the normalised o_i (up to eps); when o_i is parallel to v_i
-      // (the first token) do_i.v_i cancels, so it is formed here from the fp32 do_i
+      // (the first token) do_i.v_i cancels, so it is formed here from the fp32 do_i; the
+      // halves' partial sums are added where the diagonal is used
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         Acc dd = dvd[i];
@@ -637,7 +705,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         dd += __shfl_xor(dd, 2);
         dd += __shfl_xor(dd, 4);
         dd += __shfl_xor(dd, 8);
-        if (own && r16 == 0) sDiag[16 * I + 4 * g4 + i] = (float)dd;
+        if (own && r16 == 0) sDiag[hh * C + 16 * I + 4 * g4 + i] = (float)dd;
       }
     }
     __syncthreads();
@@ -657,7 +725,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ii = 16 * I + 4 * g4 + i, jj = 16 * J + r16;
-            dt4[i] = from_f<T>(jj < ii ? d[i] : (jj == ii ? sDiag[ii] : 0.f));
+            const float dg = NW >= 2 * NT ? sDiag[ii] + sDiag[C + ii] : sDiag[ii];
+            dt4[i] = from_f<T>(jj < ii ? d[i] : (jj == ii ? dg : 0.f));
             if constexpr (!LEAN) sD[ii * TP + jj] = dt4[i];
           }
           lds_row_write<T, 4>(sDt + (16 * J + r16) * TP, 16 * I + 4 * g4, dt4);
