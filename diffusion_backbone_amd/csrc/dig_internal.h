@@ -79,8 +79,7 @@ struct GlaBwdParams {
 // LDS bytes of the backward's final pass for this shape (0 if no kernel exists for it).
 int gla_bwd_lds_bytes(const GlaShape& s);
 // Pass B of the three-pass backward: reverse scan of segment gradient states.
-hipError_t launch_gla_gstate_scan(const GlaShape& s, float* gstates, const float* seg_lg,
-                                  hipStream_t st);
+hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipStream_t st);
 size_t gla_bwd_workspace(const GlaShape& s);
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 

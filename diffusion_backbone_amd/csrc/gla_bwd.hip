@@ -39,11 +39,9 @@ size_t gla_bwd_workspace(const GlaShape& s) {
 
 // Reverse exclusive scan over segments, in place: slot(p) <- gradient reaching the end of
 // segment p from later segments.  G(nseg-1) = 0, G(p-1) = 2^{lg(p)} G(p) + dG(p).
-__global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const float* seg_lg,
-                                                            int BH, int nseg, int dk, int dv) {
-  const long idx = (long)blockIdx.x * kBThreads + threadIdx.x;
+__device__ __forceinline__ void gstate_scan_one(float* gst, const float* seg_lg, long idx,
+                                                int nseg, int dk, int dv) {
   const long per = (long)dk * dv;
-  if (idx >= (long)BH * per) return;
   const long bh = idx / per, ce = idx - bh * per;
   const int c = (int)(ce / dv);
   float* base = gst + bh * nseg * per + ce;
@@ -57,12 +55,12 @@ __global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const f
   base[0] = G;
 }
 
-// out[e] = sum over parts of part[i][e]: one block per column e, a fixed-order tree (the
+// out[e] = sum over parts of part[i][e] for the block's column e: a fixed-order tree (the
 // same bits on every run).
-__global__ __launch_bounds__(kBThreads) void gla_dgamma_reduce(const float* part, int nparts,
-                                                              int dv, float* out) {
+__device__ __forceinline__ void dgamma_reduce_one(const float* part, int nparts, int dv, int e,
+                                                  float* out) {
   __shared__ float red[kBThreads];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   float s = 0.f;
   for (int i = tid; i < nparts; i += kBThreads) s += part[(long)i * dv + e];
   red[tid] = s;
@@ -74,12 +72,34 @@ __global__ __launch_bounds__(kBThreads) void gla_dgamma_reduce(const float* part
   if (tid == 0) out[e] = red[0];
 }
 
-hipError_t launch_gla_gstate_scan(const GlaShape& s, float* gstates, const float* seg_lg,
-                                  hipStream_t st) {
+// Pass B of the backward: blocks [0, nscan) scan the segment gradient states; the next dv
+// blocks (when out is given) reduce the dgamma partials that pass A wrote.
+__global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const float* seg_lg,
+                                                            int BH, int nseg, int dk, int dv,
+                                                            int nscan, const float* part,
+                                                            int nparts, float* out) {
+  if ((int)blockIdx.x >= nscan) {
+    dgamma_reduce_one(part, nparts, dv, (int)blockIdx.x - nscan, out);
+    return;
+  }
+  const long idx = (long)blockIdx.x * kBThreads + threadIdx.x;
+  if (idx < (long)BH * dk * dv) gstate_scan_one(gst, seg_lg, idx, nseg, dk, dv);
+}
+
+// dgamma alone (single-segment backward: the final pass wrote the partials).
+__global__ __launch_bounds__(kBThreads) void gla_dgamma_reduce(const float* part, int nparts,
+                                                              int dv, float* out) {
+  dgamma_reduce_one(part, nparts, dv, (int)blockIdx.x, out);
+}
+
+hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipStream_t st) {
   const long BH = (long)s.B * s.H;
   const long nthreads = BH * s.dk * s.dv;
-  hipLaunchKernelGGL(gla_gstate_scan, dim3((unsigned)((nthreads + kBThreads - 1) / kBThreads)),
-                     dim3(kBThreads), 0, st, gstates, seg_lg, (int)BH, s.nseg, s.dk, s.dv);
+  const int nscan = (int)((nthreads + kBThreads - 1) / kBThreads);
+  const int nred = p.d_norm_w ? s.dv : 0;
+  hipLaunchKernelGGL(gla_gstate_scan, dim3((unsigned)(nscan + nred)), dim3(kBThreads), 0, st,
+                     p.gstates, p.seg_lg, (int)BH, s.nseg, s.dk, s.dv, nscan, p.dgamma_part,
+                     (int)(BH * s.nseg), p.d_norm_w);
   return hipGetLastError();
 }
 
@@ -105,7 +125,7 @@ hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr)
                         : launch_gla_bwd_t<float>(s, p, st, nullptr);
   if (e != hipSuccess) return e;
-  if (p.d_norm_w) {
+  if (p.d_norm_w && s.nseg == 1) {  // with more segments the scan launch reduces dgamma
     const long parts = (long)s.B * s.H * s.nseg;
     hipLaunchKernelGGL(gla_dgamma_reduce, dim3(s.dv), dim3(kBThreads), 0, st, p.dgamma_part,
                        (int)parts, s.dv, p.d_norm_w);

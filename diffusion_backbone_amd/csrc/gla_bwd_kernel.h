@@ -128,9 +128,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int nseg_launch = FIN ? p.nseg : p.nseg - 1;
-  const int seg = (FIN ? 0 : 1) + (int)(blockIdx.x % nseg_launch);
-  const int bh = blockIdx.x / nseg_launch;
+  // pass A covers every segment: segment 0's G is not needed, but its dgamma partial is (with
+  // more than one segment the dgamma partials come from pass A and the scan reduces them)
+  const int seg = (int)(blockIdx.x % p.nseg);
+  const int bh = blockIdx.x / p.nseg;
+  const bool dg_here = FIN ? p.nseg == 1 : true;
   const int b = bh / p.H, h = bh - b * p.H;
   const int H = p.H;
   const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
@@ -645,13 +647,15 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           const int row = 16 * I + 4 * g4 + i;
           const float nv = oacc[Eh][i], rv = to_f(rr[Eh][i]), dyv = to_f(dyr[Eh][i]);
           const float sg = Fm<T>::sig(rv), sw = rv * sg;
-          if (own && col_on) {
+          if (col_on) {
             // register arrays take compile-time indices only (a runtime one sends them to
             // scratch memory): dgam[E] via a select over every tile
+            if (dg_here) {
 #pragma unroll
-            for (int k = 0; k < NDV; ++k)
-              if (k == E) dgam[k] += dyv * nv * sw;
-            sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
+              for (int k = 0; k < NDV; ++k)
+                if (k == E) dgam[k] += dyv * nv * sw;
+            }
+            if (own) sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
           }
           dn[Eh][i] = dyv * gmE * sw;
           md[i] += dn[Eh][i] * nv;
@@ -907,8 +911,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
   }
 
-  if (FIN) {
-    // per-workgroup partial of dgamma, reduced in a fixed order by a second kernel
+  if (dg_here) {
+    // per-workgroup partial of dgamma, reduced in a fixed order by a later kernel
 #pragma unroll
     for (int E = 0; E < NDV; ++E) {
       float v = dgam[E];
@@ -923,7 +927,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       for (int w = 1; w < NW; ++w) sum += sDg[w * DVP + e];
       p.dgamma_part[(long)blockIdx.x * dv + e] = sum;
     }
-  } else {
+  }
+  if (!FIN) {
     float* dst = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
@@ -966,8 +971,8 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   }
   if (!s.bprefix && s.nseg > 1) {
     hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW>),
-                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(64 * NW), a_bytes, st, p);
-    const hipError_t e = launch_gla_gstate_scan(s, p.gstates, p.seg_lg, st);
+                       dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
+    const hipError_t e = launch_gla_gstate_scan(s, p, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW>),
