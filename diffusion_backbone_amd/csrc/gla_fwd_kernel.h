@@ -56,7 +56,9 @@ struct FwdLayout {
   static constexpr int DVP = NDV * 16;
   static constexpr int CK = SZ == 2 ? ((C + 31) / 32) * 32 : C;  // token dim padded
   static constexpr int QP = DKP + 8, TP = CK + 8;              // padded LDS row pitches
-  static constexpr int NCL = DKP * C / (64 * NW), NEL = DVP * C / (64 * NW);  // gate columns
+  // gate columns per lane: the key columns up to the last 16-wide tile (the K-step padding
+  // past it stays zero and is never touched), the value columns
+  static constexpr int NCL = 16 * NDK * C / (64 * NW), NEL = DVP * C / (64 * NW);
   // byte offsets: operands, state copy, gates, misc; the raw staging slots come last
   static constexpr int O_Q = 0;                                         // q e^{b}  [C][QP]
   static constexpr int O_K = O_Q + al16(OUT ? C * QP * SZ : 0);          // k e^{-b} [C][QP]
@@ -110,8 +112,8 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   // are more waves than row tiles (they advance the state while the others form outputs)
   constexpr int SW0 = (OUT && NW > NT) ? NT : 0, NSW = NW - SW0;
   constexpr int STW = (NST + NSW - 1) / NSW;            // state tiles per owning wave
-  constexpr int NCL = DKP * C / NTH;                    // gate pass: key columns per lane
-  constexpr int NEL = DVP * C / NTH;                    // V transpose: value columns per lane
+  constexpr int NCL = Lo::NCL;                          // gate pass: key columns per lane
+  constexpr int NEL = Lo::NEL;                          // V transpose: value columns per lane
   // every gate/transpose column is a real one: no per-column guards
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
