@@ -406,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       // cancelling dot product keeps its relative accuracy: 16 rows x 4 column groups
       float diag;
       {
-        constexpr int DQ = DKP / 4;
+        constexpr int DQ = 4 * NDK;  // four column groups over the 16-wide key tiles
         const int ir = 16 * I + r16;
         T qd[DQ], kd[DQ];
         if constexpr (FULLK) {
