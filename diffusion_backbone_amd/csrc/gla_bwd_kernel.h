@@ -953,7 +953,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 // lane and the registers fit two waves per SIMD, else four.
 template <typename T, int DK, int DV, bool EXACT>
 constexpr int bwd_waves() {
-  return (EXACT && sizeof(T) == 2 && DK == 32 && DV == 64) ? DIG_BWD_WAVES8 : 4;
+  return (EXACT && sizeof(T) == 2 && ((DK == 32 && DV == 64) || (DK == 36 && DV == 72))) ? DIG_BWD_WAVES8 : 4;
 }
 
 template <typename T, int DK, int DV, bool EXACT, int C>
