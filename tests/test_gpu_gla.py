@@ -76,6 +76,9 @@ def test_fwd_gate_stress(stress, dtype):
     case = _case("dig_s2_256", batch=1, seq_len=300, dtype=dtype, **kw)
     out = gla_forward(case, 64, seg_chunks=2)
     _check_fwd(case, out, TOL[dtype])
+    if dtype == "bf16":  # the XL head shape (padded key tiles, four waves) on the same gates
+        cx = _case("dig_xl2_2048", batch=1, seq_len=300, dtype=dtype, **kw)
+        _check_fwd(cx, gla_forward(cx, 64, seg_chunks=2), TOL[dtype])
     if dtype == "f32":  # fp32 backward at these head dims fits LDS with 32-token chunks
         f = gla_forward(case, 32, seg_chunks=3, want_saved=True)
         _check_fwd(case, f, TOL[dtype])
@@ -189,11 +192,12 @@ def test_bwd_bf16_shapes(name, batch, seq_len, chunk, seg):
 
 
 @pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
-def test_bwd_gate_stress(stress):
+@pytest.mark.parametrize("name", ["dig_s2_256", "dig_xl2_2048"])
+def test_bwd_gate_stress(stress, name):
     kw = {"long_memory": dict(gate_bias=6.0), "fast_decay": dict(gate_bias=-6.0),
           "wide_logits": dict(z_std=4.0), "extreme_decay": dict(gate_bias=-40.0, z_std=1.0)}[stress]
-    announce("bwd stress %s" % stress)
-    case = _case("dig_s2_256", batch=1, seq_len=300, **kw)
+    announce("bwd stress %s %s" % (stress, name))
+    case = _case(name, batch=1, seq_len=300, **kw)
     f = gla_forward(case, 64, seg_chunks=2, want_saved=True)
     g = gla_backward(case, f)
     _check_bwd(case, g, TOL["bf16"])
