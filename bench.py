@@ -175,10 +175,10 @@ class EventTimer:
 TRAFFIC = {
     "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    # FETCH_SIZE 11994.8 KiB / 0.50016 (copy: 131113.3 KiB read per 262144 KiB moved) +
-    # WRITE_SIZE 8132.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-    "bytes": 32884669,
-    "sources_sha256": "5e12c6639d87830d91473997747e8622191304f770dfb28e47c6c9cca12305f8",
+    # FETCH_SIZE 13214.3 KiB / 0.50018 (copy: 131120.1 KiB read per 262144 KiB moved) +
+    # WRITE_SIZE 8522.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
+    "bytes": 35779433,
+    "sources_sha256": "320bc2b313e8966982eaee831aa82acd18f3becd9b8c3e67bcce78036c67a461",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
