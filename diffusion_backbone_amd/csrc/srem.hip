@@ -271,13 +271,23 @@ __global__ __launch_bounds__(256) void dwconv_dw_reduce(const float* __restrict_
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= 10L * D) return;
   const int t = (int)(idx / D), c = (int)(idx - (long)t * D);
-  // eight independent partial sums (loads in flight together), combined in a fixed order
+  // eight running sums combined in a fixed order; 32 partials are loaded before any is added,
+  // so up to 32 partials cost one memory round trip
   float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* pc = part + (long)t * D + c;
+  const long step = 10L * D;
   int i = 0;
+  for (; i + 32 <= nblk; i += 32) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = pc[(long)(i + u) * step];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s8[u & 7] += v[u];
+  }
   for (; i + 8 <= nblk; i += 8)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s8[u] += part[((long)(i + u) * 10 + t) * D + c];
-  for (; i < nblk; ++i) s8[0] += part[((long)i * 10 + t) * D + c];
+    for (int u = 0; u < 8; ++u) s8[u] += pc[(long)(i + u) * step];
+  for (; i < nblk; ++i) s8[0] += pc[(long)i * step];
   float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   if (t < 9)
     dw[c * 9 + t] = s;
@@ -285,204 +295,7 @@ __global__ __launch_bounds__(256) void dwconv_dw_reduce(const float* __restrict_
     dbias[c] = s;
 }
 
-// ------------------------------------------------------------ LDS-tiled conv
-// One block: an 8 x 8 tile of current-grid positions x one 128-byte channel slab.  The
-// 10 x 10 halo tile arrives through global->LDS DMA (one round trip); positions outside the
-// grid are zero-filled.  Used when the slab divides the channel count.
-constexpr int kTile = 8, kHalo = kTile + 2, kSlabBytes = 128;
-
-template <typename T, bool GATHER>
-__device__ __forceinline__ void load_halo(T* tile, const T* x, long bL, int D, int c0, int i0,
-                                          int j0, int rows, int cols, int gh, int gw, long L,
-                                          int layout, int out_layout, int wave, int lane) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int NG = kSlabBytes / 16;  // 16-byte pieces per position
-  constexpr int NP = kHalo * kHalo * NG;
-  unsigned char* tb = reinterpret_cast<unsigned char*>(tile);
-  for (int base = wave * 64; base < NP; base += 4 * 64) {
-    const int e = base + lane;
-    if (e < NP) {
-      const int pos = e / NG, k = e - pos * NG;
-      const int hi = pos / kHalo, hj = pos - hi * kHalo;
-      const int ii = i0 - 1 + hi, jj = j0 - 1 + hj;
-      if (ii >= 0 && ii < rows && jj >= 0 && jj < cols) {
-        const long p = (long)ii * cols + jj;
-        const long row = GATHER ? scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L) : p;
-        const T* g = x + (bL + row) * D + c0 + k * VEC;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)(tb + base * 16), 16, 0, 0);
-      } else {
-        *reinterpret_cast<uint4*>(tb + (long)e * 16) = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-}
-
-//   forward:  out[p'] = sum_taps w x, written at the position of p's token in out_layout;
-//   backward (dx): input is dy gathered back to the current order, taps rotated 180 degrees,
-//             output in the current order.
-template <typename T, bool BWD>
-__global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__ x,
-                                                           const float* __restrict__ w,
-                                                           const float* __restrict__ bias,
-                                                           T* __restrict__ y, int gh, int gw,
-                                                           int D, int layout, int out_layout,
-                                                           int rows, int cols, int ntr, int ntc,
-                                                           int nslab) {
-  constexpr int CS = kSlabBytes / sizeof(T);  // channels per slab
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int NG = CS / VEC;                // = 8 pieces per position
-  __shared__ __align__(16) T tile[kHalo * kHalo * CS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int blk = blockIdx.x;
-  const int slab = blk % nslab; blk /= nslab;
-  const int tc = blk % ntc; blk /= ntc;
-  const int tr = blk % ntr;
-  const int b = blk / ntr;
-  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
-  const long L = (long)gh * gw, bL = (long)b * L;
-
-  load_halo<T, BWD>(tile, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout, wave,
-                    lane);
-
-  const int g = tid % NG, pl = tid / NG;  // channel group, first output position
-  float wr[9][VEC], bs[VEC];
-#pragma unroll
-  for (int t = 0; t < 9; ++t)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v)
-      wr[t][v] = w[(c0 + g * VEC + v) * 9 + (BWD ? 8 - t : t)];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) bs[v] = (!BWD && bias) ? bias[c0 + g * VEC + v] : 0.f;
-  dma_wait();
-  __syncthreads();
-
-#pragma unroll
-  for (int task = 0; task < 2; ++task) {
-    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
-    const int i = i0 + oi, j = j0 + oj;
-    if (i < rows && j < cols) {
-      float acc[VEC];
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] = bs[v];
-#pragma unroll
-      for (int a = 0; a < 3; ++a)
-#pragma unroll
-        for (int s2 = 0; s2 < 3; ++s2) {
-          const Vec<T, VEC> xv =
-              *reinterpret_cast<const Vec<T, VEC>*>(tile + ((oi + a) * kHalo + oj + s2) * CS + g * VEC);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wr[a * 3 + s2][v], to_f(xv.v[v]), acc[v]);
-        }
-      Vec<T, VEC> o;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
-      const long p = (long)i * cols + j;
-      const long orow = BWD ? p : scan_inv(out_layout, scan_pi(layout, p, gh, gw, L), gh, gw, L);
-      *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c0 + g * VEC) = o;
-    }
-  }
-}
-
-// Backward of one 8 x 8 tile x 128-byte slab in one pass: the dy halo tile (gathered back to
-// the current order) and the x halo tile arrive by LDS DMA; each thread forms dx at its two
-// positions (taps rotated by 180 degrees) and accumulates dy(i, j) * x(i+a-1, j+s-1) (taps
-// 0..8) and dy(i, j) (tap 9, the bias), then the 32 position lanes are summed in a fixed
-// order into part[tile][tap][D], tile over (b, tile row, tile column).
-template <typename T>
-__global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restrict__ x,
-                                                               const float* __restrict__ w,
-                                                               const T* __restrict__ dy,
-                                                               T* __restrict__ dx,
-                                                               float* __restrict__ part, int gh,
-                                                               int gw, int D, int layout,
-                                                               int out_layout, int rows,
-                                                               int cols, int ntr, int ntc,
-                                                               int nslab) {
-  constexpr int CS = kSlabBytes / sizeof(T);
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int NG = CS / VEC;
-  __shared__ __align__(16) T dyt[kHalo * kHalo * CS];
-  __shared__ __align__(16) T xt[kHalo * kHalo * CS];
-  __shared__ float red[32 * CS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int blk = blockIdx.x;
-  const int slab = blk % nslab; blk /= nslab;
-  const int tc = blk % ntc; blk /= ntc;
-  const int tr = blk % ntr;
-  const int b = blk / ntr;
-  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
-  const long L = (long)gh * gw, bL = (long)b * L;
-
-  load_halo<T, true>(dyt, dy, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout,
-                     wave, lane);
-  load_halo<T, false>(xt, x, bL, D, c0, i0, j0, rows, cols, gh, gw, L, layout, out_layout,
-                      wave, lane);
-  const int g = tid % NG, pl = tid / NG;  // channel group, first position
-  float wr[9][VEC];
-#pragma unroll
-  for (int t = 0; t < 9; ++t)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) wr[t][v] = w[(c0 + g * VEC + v) * 9 + 8 - t];
-  float acc[10][VEC];
-#pragma unroll
-  for (int t = 0; t < 10; ++t)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
-  dma_wait();
-  __syncthreads();
-
-#pragma unroll
-  for (int task = 0; task < 2; ++task) {
-    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
-    const int i = i0 + oi, j = j0 + oj;
-    if (i < rows && j < cols) {
-      float o[VEC];
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) o[v] = 0.f;
-#pragma unroll
-      for (int a = 0; a < 3; ++a)
-#pragma unroll
-        for (int s2 = 0; s2 < 3; ++s2) {
-          const int h = ((oi + a) * kHalo + oj + s2) * CS + g * VEC;
-          const Vec<T, VEC> dv = *reinterpret_cast<const Vec<T, VEC>*>(dyt + h);
-          const Vec<T, VEC> xv = *reinterpret_cast<const Vec<T, VEC>*>(xt + h);
-          const Vec<T, VEC> gc = *reinterpret_cast<const Vec<T, VEC>*>(
-              dyt + ((oi + 1) * kHalo + oj + 1) * CS + g * VEC);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            o[v] = fmaf(wr[a * 3 + s2][v], to_f(dv.v[v]), o[v]);
-            acc[a * 3 + s2][v] = fmaf(to_f(gc.v[v]), to_f(xv.v[v]), acc[a * 3 + s2][v]);
-          }
-        }
-      const Vec<T, VEC> gc =
-          *reinterpret_cast<const Vec<T, VEC>*>(dyt + ((oi + 1) * kHalo + oj + 1) * CS + g * VEC);
-      Vec<T, VEC> ov;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        acc[9][v] += to_f(gc.v[v]);
-        ov.v[v] = from_f<T>(o[v]);
-      }
-      *reinterpret_cast<Vec<T, VEC>*>(dx + (bL + (long)i * cols + j) * D + c0 + g * VEC) = ov;
-    }
-  }
-
-  // fixed-order reduction over the 32 position lanes of each channel group
-  const long pblk = ((long)b * ntr + tr) * ntc + tc;
-#pragma unroll
-  for (int t = 0; t < 10; ++t) {
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) red[pl * CS + g * VEC + v] = acc[t][v];
-    __syncthreads();
-    if (tid < CS) {
-      float s3 = 0.f;
-      for (int q = 0; q < 32; ++q) s3 += red[q * CS + tid];
-      part[(pblk * 10 + t) * D + c0 + tid] = s3;
-    }
-    __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------ column-strip conv
+// ---------------------------------------------------- scan-order map of the grid
 // Position of the token at current-grid (i, j) in another scan order: an affine function
 // A + Bi i + Bj j of the grid indices (each scan order is a flip and/or transpose of the
 // canonical row-major grid), so the fused reorient costs no division in the kernel.
@@ -510,6 +323,231 @@ static GridMap grid_map(int gh, int gw, int layout, int out_layout) {
   return GridMap{o0 + oi * c0 + oj * d0, oi * cii + oj * dji, oi * cij + oj * djj};
 }
 
+// ------------------------------------------------------------ LDS-tiled conv
+// One block: an 8 x 8 tile of current-grid positions x one 128-byte channel slab.  The
+// 10 x 10 halo tile arrives through global->LDS DMA (one round trip); positions outside the
+// grid are zero-filled.  Used when the slab divides the channel count.
+constexpr int kTile = 8, kHalo = kTile + 2, kSlabBytes = 128;
+
+template <typename T, bool GATHER>
+__device__ __forceinline__ void load_halo(T* tile, const T* x, long bL, int D, int c0, int i0,
+                                          int j0, int rows, int cols, GridMap m, int wave,
+                                          int lane) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = kSlabBytes / 16;  // 16-byte pieces per position
+  constexpr int NP = kHalo * kHalo * NG;
+  unsigned char* tb = reinterpret_cast<unsigned char*>(tile);
+  for (int base = wave * 64; base < NP; base += 4 * 64) {
+    const int e = base + lane;
+    if (e < NP) {
+      const int pos = e / NG, k = e - pos * NG;
+      const int hi = pos / kHalo, hj = pos - hi * kHalo;
+      const int ii = i0 - 1 + hi, jj = j0 - 1 + hj;
+      if (ii >= 0 && ii < rows && jj >= 0 && jj < cols) {
+        const long row = GATHER ? m.A + m.Bi * ii + m.Bj * jj : (long)ii * cols + jj;
+        const T* g = x + (bL + row) * D + c0 + k * VEC;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)(tb + base * 16), 16, 0, 0);
+      } else {
+        *reinterpret_cast<uint4*>(tb + (long)e * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The slab's taps, w[c0 .. c0+CS)[9] (contiguous), staged into LDS tap-major, wl[tap][CS],
+// with coalesced loads; read back after the block's barrier as 16-byte runs of channels.
+template <int CS>
+__device__ __forceinline__ void stage_taps(float* wl, const float* w, int c0, int tid) {
+  for (int e = tid; e < 9 * CS; e += 256) {
+    const int ch = e / 9, t = e - ch * 9;
+    wl[t * CS + ch] = w[(long)c0 * 9 + e];
+  }
+}
+template <int CS, int VEC>
+__device__ __forceinline__ void read_taps(float (&wr)[9][VEC], const float* wl, int cl, bool rot) {
+#pragma unroll
+  for (int t = 0; t < 9; ++t) {
+    const float4* src = reinterpret_cast<const float4*>(wl + (rot ? 8 - t : t) * CS + cl);
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const float4 f = src[q];
+      wr[t][4 * q] = f.x; wr[t][4 * q + 1] = f.y; wr[t][4 * q + 2] = f.z; wr[t][4 * q + 3] = f.w;
+    }
+  }
+}
+
+//   forward:  out[p'] = sum_taps w x, written at the position of p's token in out_layout;
+//   backward (dx): input is dy gathered back to the current order, taps rotated 180 degrees,
+//             output in the current order.
+template <typename T, bool BWD>
+__global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           T* __restrict__ y, int D, long L,
+                                                           GridMap m, int rows, int cols,
+                                                           int ntr, int ntc, int nslab) {
+  constexpr int CS = kSlabBytes / sizeof(T);  // channels per slab
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = CS / VEC;                // = 8 pieces per position
+  __shared__ __align__(16) T tile[kHalo * kHalo * CS];
+  __shared__ __align__(16) float wl[9 * CS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int tc = blk % ntc; blk /= ntc;
+  const int tr = blk % ntr;
+  const int b = blk / ntr;
+  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
+  const long bL = (long)b * L;
+
+  load_halo<T, BWD>(tile, x, bL, D, c0, i0, j0, rows, cols, m, wave, lane);
+
+  const int g = tid % NG, pl = tid / NG;  // channel group, first output position
+  stage_taps<CS>(wl, w, c0, tid);
+  float bs[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) bs[v] = (!BWD && bias) ? bias[c0 + g * VEC + v] : 0.f;
+  dma_wait();
+  __syncthreads();
+  float wr[9][VEC];
+  read_taps<CS, VEC>(wr, wl, g * VEC, BWD);
+
+#pragma unroll
+  for (int task = 0; task < 2; ++task) {
+    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
+    const int i = i0 + oi, j = j0 + oj;
+    if (i < rows && j < cols) {
+      float acc[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[v] = bs[v];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          const Vec<T, VEC> xv =
+              *reinterpret_cast<const Vec<T, VEC>*>(tile + ((oi + a) * kHalo + oj + s2) * CS + g * VEC);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wr[a * 3 + s2][v], to_f(xv.v[v]), acc[v]);
+        }
+      Vec<T, VEC> o;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
+      const long orow = BWD ? (long)i * cols + j : m.A + m.Bi * i + m.Bj * j;
+      *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c0 + g * VEC) = o;
+    }
+  }
+}
+
+// Backward of one 8 x 8 tile x 128-byte slab in one pass: the dy halo tile (gathered back to
+// the current order) and the x halo tile arrive by LDS DMA; each thread forms dx at its two
+// positions (taps rotated by 180 degrees) and accumulates dy(i, j) * x(i+a-1, j+s-1) (taps
+// 0..8) and dy(i, j) (tap 9, the bias).  The 32 position lanes of a channel group are then
+// summed in a fixed order: lane pairs of a 16-lane row by DPP, the 16 row partials through
+// LDS (reusing the tile space), all taps behind one barrier, into part[tile][tap][D], tile
+// over (b, tile row, tile column).
+template <typename T>
+__global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               const T* __restrict__ dy,
+                                                               T* __restrict__ dx,
+                                                               float* __restrict__ part, int D,
+                                                               long L, GridMap m, int rows,
+                                                               int cols, int ntr, int ntc,
+                                                               int nslab) {
+  constexpr int CS = kSlabBytes / sizeof(T);
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NG = CS / VEC;
+  static_assert(NG == 8, "a 16-lane row holds two positions of one channel group");
+  constexpr int NRP = 16, RP = NRP + 1;  // row partials per channel, odd pitch
+  constexpr int TILE_BYTES = 2 * kHalo * kHalo * CS * (int)sizeof(T) + 9 * CS * (int)sizeof(float);
+  constexpr int RED_BYTES = 10 * CS * RP * (int)sizeof(float);
+  __shared__ __align__(16) unsigned char sm[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
+  T* dyt = reinterpret_cast<T*>(sm);
+  T* xt = dyt + kHalo * kHalo * CS;
+  float* wl = reinterpret_cast<float*>(xt + kHalo * kHalo * CS);
+  float* red = reinterpret_cast<float*>(sm);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int slab = blk % nslab; blk /= nslab;
+  const int tc = blk % ntc; blk /= ntc;
+  const int tr = blk % ntr;
+  const int b = blk / ntr;
+  const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
+  const long bL = (long)b * L;
+
+  load_halo<T, true>(dyt, dy, bL, D, c0, i0, j0, rows, cols, m, wave, lane);
+  load_halo<T, false>(xt, x, bL, D, c0, i0, j0, rows, cols, m, wave, lane);
+  const int g = tid % NG, pl = tid / NG;  // channel group, first position
+  stage_taps<CS>(wl, w, c0, tid);
+  float acc[10][VEC];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
+  dma_wait();
+  __syncthreads();
+  float wr[9][VEC];
+  read_taps<CS, VEC>(wr, wl, g * VEC, true);
+
+#pragma unroll
+  for (int task = 0; task < 2; ++task) {
+    const int q = pl + 32 * task, oi = q / kTile, oj = q - oi * kTile;
+    const int i = i0 + oi, j = j0 + oj;
+    if (i < rows && j < cols) {
+      const Vec<T, VEC> gc =
+          *reinterpret_cast<const Vec<T, VEC>*>(dyt + ((oi + 1) * kHalo + oj + 1) * CS + g * VEC);
+      float o[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[v] = 0.f;
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          const int h = ((oi + a) * kHalo + oj + s2) * CS + g * VEC;
+          const Vec<T, VEC> dv = *reinterpret_cast<const Vec<T, VEC>*>(dyt + h);
+          const Vec<T, VEC> xv = *reinterpret_cast<const Vec<T, VEC>*>(xt + h);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            o[v] = fmaf(wr[a * 3 + s2][v], to_f(dv.v[v]), o[v]);
+            acc[a * 3 + s2][v] = fmaf(to_f(gc.v[v]), to_f(xv.v[v]), acc[a * 3 + s2][v]);
+          }
+        }
+      Vec<T, VEC> ov;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        acc[9][v] += to_f(gc.v[v]);
+        ov.v[v] = from_f<T>(o[v]);
+      }
+      *reinterpret_cast<Vec<T, VEC>*>(dx + (bL + (long)i * cols + j) * D + c0 + g * VEC) = ov;
+    }
+  }
+
+  // lanes l and l ^ 8 of a row hold positions pl and pl ^ 1 of the same channel group
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[t][v] += dpp_f<0x128>(acc[t][v]);
+  __syncthreads();  // tiles and taps are dead: their space becomes red[tap][channel][row partial]
+  if ((tid & 8) == 0) {
+    const int rp = tid >> 4;
+#pragma unroll
+    for (int t = 0; t < 10; ++t)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) red[(t * CS + g * VEC + v) * RP + rp] = acc[t][v];
+  }
+  __syncthreads();
+  const long pblk = ((long)b * ntr + tr) * ntc + tc;
+  for (int o = tid; o < 10 * CS; o += 256) {
+    const float* r = red + o * RP;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NRP; ++q) s4[q & 3] += r[q];
+    const int t = o / CS, ch = o - t * CS;
+    part[(pblk * 10 + t) * D + c0 + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  }
+}
+
+// ------------------------------------------------------------ column-strip conv
 // One block: a strip of 16 current-grid columns x RH rows x one slab of 16 channel groups
 // (16 bytes each, so one token's slab is 256 contiguous bytes).  Thread (group g, column j)
 // loads its 16-byte vectors of columns j-1, j, j+1 for the RH + 2 input rows (the side
@@ -778,8 +816,9 @@ static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int ou
   const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
   if (tp.ok) {
     hipLaunchKernelGGL((dwconv_tiled_kernel<T, BWD>), dim3((unsigned)tp.conv_blocks), dim3(256),
-                       0, st, static_cast<const T*>(x), w, bias, static_cast<T*>(y), gh, gw, D,
-                       layout, out_layout, tp.rows, tp.cols, tp.ntr, tp.ntc, tp.nslab);
+                       0, st, static_cast<const T*>(x), w, bias, static_cast<T*>(y), D,
+                       (long)gh * gw, grid_map(gh, gw, layout, out_layout), tp.rows, tp.cols,
+                       tp.ntr, tp.ntc, tp.nslab);
     return hipGetLastError();
   }
   const ConvPlan c = conv_plan(B, gh, gw, D, sizeof(T), layout, kConvSR, 16 / sizeof(T));
@@ -880,8 +919,9 @@ static hipError_t launch_dwconv_bwd_t(int B, int gh, int gw, int D, int layout, 
   if (!sp.ok && tp.ok) {
     hipLaunchKernelGGL((dwconv_bwd_tiled_kernel<T>), dim3((unsigned)tp.conv_blocks), dim3(256), 0,
                        st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
-                       static_cast<T*>(dx), part, gh, gw, D, layout, out_layout, tp.rows, tp.cols,
-                       tp.ntr, tp.ntc, tp.nslab);
+                       static_cast<T*>(dx), part, D, (long)gh * gw,
+                       grid_map(gh, gw, layout, out_layout), tp.rows, tp.cols, tp.ntr, tp.ntc,
+                       tp.nslab);
     const long n = 10L * D;
     hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        part, (int)((long)B * tp.ntr * tp.ntc), D, dw, dbias);
