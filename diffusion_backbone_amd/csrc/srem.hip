@@ -376,10 +376,8 @@ __device__ __forceinline__ void read_taps(float (&wr)[9][VEC], const float* wl, 
   }
 }
 
-//   forward:  out[p'] = sum_taps w x, written at the position of p's token in out_layout;
-//   backward (dx): input is dy gathered back to the current order, taps rotated 180 degrees,
-//             output in the current order.
-template <typename T, bool BWD>
+// Forward: out[p'] = sum_taps w x + b, written at the position of p's token in out_layout.
+template <typename T>
 __global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias,
@@ -400,17 +398,17 @@ __global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__
   const int i0 = tr * kTile, j0 = tc * kTile, c0 = slab * CS;
   const long bL = (long)b * L;
 
-  load_halo<T, BWD>(tile, x, bL, D, c0, i0, j0, rows, cols, m, wave, lane);
+  load_halo<T, false>(tile, x, bL, D, c0, i0, j0, rows, cols, m, wave, lane);
 
   const int g = tid % NG, pl = tid / NG;  // channel group, first output position
   stage_taps<CS>(wl, w, c0, tid);
   float bs[VEC];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) bs[v] = (!BWD && bias) ? bias[c0 + g * VEC + v] : 0.f;
+  for (int v = 0; v < VEC; ++v) bs[v] = bias ? bias[c0 + g * VEC + v] : 0.f;
   dma_wait();
   __syncthreads();
   float wr[9][VEC];
-  read_taps<CS, VEC>(wr, wl, g * VEC, BWD);
+  read_taps<CS, VEC>(wr, wl, g * VEC, false);
 
 #pragma unroll
   for (int task = 0; task < 2; ++task) {
@@ -432,7 +430,7 @@ __global__ __launch_bounds__(256) void dwconv_tiled_kernel(const T* __restrict__
       Vec<T, VEC> o;
 #pragma unroll
       for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
-      const long orow = BWD ? (long)i * cols + j : m.A + m.Bi * i + m.Bj * j;
+      const long orow = m.A + m.Bi * i + m.Bj * j;
       *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c0 + g * VEC) = o;
     }
   }
@@ -556,14 +554,11 @@ __global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restri
 // compiler sink the loads next to their first use (one memory round trip per output row).
 // Out-of-grid rows and columns are loaded clamped and scaled by zero (rows) or get zero taps
 // (columns); columns past the grid repeat the last one and the last row group overlaps its
-// neighbour, both writing identical values.  Needs at least RH rows.
-//   forward:  input row of (i, j) is its current position; output row is its position in
-//             out_layout (map m);
-//   backward (dx): input is dy at the position in out_layout (map m), taps rotated by 180
-//             degrees, output in the current order.
+// neighbour, both writing identical values.  Needs at least RH rows.  The input row of (i, j)
+// is its current position, the output row its position in out_layout (map m).
 constexpr int kStripG = 16, kStripW = 256 / kStripG;
 
-template <typename T, bool BWD, int RH>
+template <typename T, int RH>
 __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias,
@@ -591,7 +586,7 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
     for (int s = 0; s < 3; ++s)
 #pragma unroll
       for (int v = 0; v < VEC; ++v)
-        wr[a][s][v] = BWD ? w[(c + v) * 9 + (2 - a) * 3 + (2 - s)] : w[(c + v) * 9 + a * 3 + s];
+        wr[a][s][v] = w[(c + v) * 9 + a * 3 + s];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -604,9 +599,7 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
 #pragma unroll
   for (int v = 0; v < VEC; ++v) bs[v] = bscale * bias[c + v];
 
-  auto in_row = [&](int ii, int jj) -> long {
-    return BWD ? m.A + m.Bi * ii + m.Bj * jj : (long)ii * cols + jj;
-  };
+  auto in_row = [&](int ii, int jj) -> long { return (long)ii * cols + jj; };
   Vec<T, VEC> win[RH + 2][3];
 #pragma unroll
   for (int r = 0; r < RH + 2; ++r) {
@@ -635,89 +628,144 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
     Vec<T, VEC> o;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
-    const long orow = BWD ? (long)i * cols + j : m.A + m.Bi * i + m.Bj * j;
+    const long orow = m.A + m.Bi * i + m.Bj * j;
     *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c) = o;
   }
 }
 
-// Weight/bias gradient partials on the same strips: thread (group g, column j) accumulates
-// dy_cur(i, j) * x(i+a-1, j+s-1) for its RH rows (taps 0..8) and dy_cur (tap 9, the bias);
-// the 16 columns are then summed in a fixed order into part[blk][tap][D], blk over
-// (b, strip, row group).  Clamped duplicate columns and the rows of an overlapping last row
-// group that the previous group owns contribute zero.
+// Backward of the conv in one pass over column strips: dx and the dW/dbias partials.  Thread
+// (group g, column j) owns VEC channels of one current-grid column and walks RH rows.  With
+// the dy window win[u][v] = dy(i-1+u, j-1+v) around the input position (i, j), dy being zero
+// outside the grid, the adjoint of y(i, j) = sum_{a,s} w[a][s] x(i+a-1, j+s-1) + b is
+//   dx(i, j) = sum_{u,v} w[2-u][2-v] win[u][v],   dw[2-u][2-v] += x(i, j) win[u][v],
+//   dbias += win[1][1]
+// so one window serves both, and dy is read once per position (x and dx once each).
+// Out-of-grid dy rows are loaded clamped and scaled by zero; out-of-grid dy columns get zero
+// dx taps and have their dW sums cleared at the end (a lane's column is fixed).  Positions a
+// thread does not own (columns past the grid repeating the last one, rows of an overlapping
+// last row group that the previous group owns) add nothing to dW and rewrite identical dx.
+// The block's W columns are summed in a fixed order through LDS into part[blk][tap][D], blk
+// over (b, strip, row group).  No branch before the stores (loads stay in flight together).
+constexpr int kBwdVec = 2, kBwdSlabBytes = 128, kBwdRows = 16;
+
 template <typename T, int RH>
-__global__ __launch_bounds__(256) void dwconv_dw_strip_kernel(const T* __restrict__ x,
-                                                              const T* __restrict__ dy,
-                                                              float* __restrict__ part, int rows,
-                                                              int cols, int D, long L, GridMap m,
-                                                              int nslab, int nstrip, int nrg) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int CS = kStripG * VEC;  // channels of the slab
-  __shared__ float red[kStripW * CS];
-  const int tid = threadIdx.x, g = tid % kStripG, jc = tid / kStripG;
+__global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
+    const T* __restrict__ x, const float* __restrict__ w, const T* __restrict__ dy,
+    T* __restrict__ dx, float* __restrict__ part, int rows, int cols, int D, long L, GridMap m,
+    int nslab, int nstrip, int nrg) {
+  constexpr int VEC = kBwdVec;
+  constexpr int G = kBwdSlabBytes / (VEC * (int)sizeof(T));  // channel groups per slab
+  constexpr int W = 256 / G;                                  // columns per strip
+  constexpr int CS = G * VEC;                                 // channels per slab
+  using V = Vec<T, VEC>;
+  __shared__ float red[W * 10 * CS];
+  const int tid = threadIdx.x, g = tid % G, jc = tid / G;
   int blk = blockIdx.x;
   const int slab = blk % nslab; blk /= nslab;
   const int strip = blk % nstrip; blk /= nstrip;
   const int rg = blk % nrg;
   const int b = blk / nrg;
-  const int c = (slab * kStripG + g) * VEC;
+  const int c0 = slab * CS, c = c0 + g * VEC;
   const int i0 = min(rg * RH, rows - RH), first_own = rg * RH;
-  const int jr = strip * kStripW + jc, j = min(jr, cols - 1);
+  const int jr = strip * W + jc, j = min(jr, cols - 1);
   const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
   const long bL = (long)b * L;
   const float mj = jr < cols ? 1.f : 0.f;
-  const float ms[3] = {j > 0 ? 1.f : 0.f, 1.f, j < cols - 1 ? 1.f : 0.f};
+  const float ml = j > 0 ? 1.f : 0.f, mr = j < cols - 1 ? 1.f : 0.f;
 
-  Vec<T, VEC> xw[RH + 2][3], dv[RH];
+  // the lane's taps w[c .. c+VEC)[9]: 9 VEC contiguous floats, 8-byte aligned (VEC even)
+  float wv[9 * VEC];
+  {
+    const float2* wp = reinterpret_cast<const float2*>(w + (long)c * 9);
+#pragma unroll
+    for (int q = 0; q < 9 * VEC / 2; ++q) {
+      const float2 f = wp[q];
+      wv[2 * q] = f.x;
+      wv[2 * q + 1] = f.y;
+    }
+  }
+  V dr[RH + 2][3], xr[RH];
 #pragma unroll
   for (int r = 0; r < RH + 2; ++r) {
     const int ii = min(max(i0 - 1 + r, 0), rows - 1);
-    xw[r][0] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + jm) * D + c);
-    xw[r][1] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + j) * D + c);
-    xw[r][2] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + (long)ii * cols + jp) * D + c);
+    const long base = bL + m.A + m.Bi * ii;
+    dr[r][0] = *reinterpret_cast<const V*>(dy + (base + m.Bj * jm) * D + c);
+    dr[r][1] = *reinterpret_cast<const V*>(dy + (base + m.Bj * j) * D + c);
+    dr[r][2] = *reinterpret_cast<const V*>(dy + (base + m.Bj * jp) * D + c);
   }
 #pragma unroll
   for (int r = 0; r < RH; ++r)
-    dv[r] = *reinterpret_cast<const Vec<T, VEC>*>(
-        dy + (bL + m.A + m.Bi * (i0 + r) + m.Bj * j) * D + c);
-  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
+    xr[r] = *reinterpret_cast<const V*>(x + (bL + (long)(i0 + r) * cols + j) * D + c);
 
+  // dx taps, rotated by 180 degrees; out-of-grid side columns get zero taps
+  float wr[3][3][VEC];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int v = 0; v < 3; ++v)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        wr[u][v][e] = wv[e * 9 + (2 - u) * 3 + (2 - v)] * (v == 0 ? ml : (v == 2 ? mr : 1.f));
+  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
+  float fr[RH + 2][3][VEC];
+  auto cvt = [&](int r) {
+    const float sc = r == 0 ? m_top : (r == RH + 1 ? m_bot : 1.f);
+#pragma unroll
+    for (int v = 0; v < 3; ++v)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) fr[r][v][e] = sc * to_f(dr[r][v].v[e]);
+  };
   float acc[10][VEC];
 #pragma unroll
   for (int t = 0; t < 10; ++t)
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[t][v] = 0.f;
+    for (int e = 0; e < VEC; ++e) acc[t][e] = 0.f;
+  cvt(0);
+  cvt(1);
 #pragma unroll
   for (int r = 0; r < RH; ++r) {
+    cvt(r + 2);
     const float md = i0 + r >= first_own ? mj : 0.f;
-    float d[VEC];
+    float xm[VEC], o[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) d[v] = md * to_f(dv[r].v[v]);
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const float on = r + a == 0 ? m_top : (r + a == RH + 1 ? m_bot : 1.f);
-#pragma unroll
-      for (int s = 0; s < 3; ++s)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v)
-          acc[a * 3 + s][v] = fmaf(d[v], on * ms[s] * to_f(xw[r + a][s].v[v]), acc[a * 3 + s][v]);
+    for (int e = 0; e < VEC; ++e) {
+      xm[e] = md * to_f(xr[r].v[e]);
+      o[e] = 0.f;
     }
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[9][v] += d[v];
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int v = 0; v < 3; ++v)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          o[e] = fmaf(wr[u][v][e], fr[r + u][v][e], o[e]);
+          acc[u * 3 + v][e] = fmaf(xm[e], fr[r + u][v][e], acc[u * 3 + v][e]);
+        }
+    V ov;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      acc[9][e] = fmaf(md, fr[r + 1][1][e], acc[9][e]);
+      ov.v[e] = from_f<T>(o[e]);
+    }
+    *reinterpret_cast<V*>(dx + (bL + (long)(i0 + r) * cols + j) * D + c) = ov;
   }
 
-  const long pblk = ((long)b * nstrip + strip) * nrg + rg;
+  // tap t = a*3 + s of dw is window slot 8 - t; clear the sums of out-of-grid side columns
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
+    const int k = t < 9 ? 8 - t : 9;
+    const float mk = k % 3 == 0 && k < 9 ? ml : (k % 3 == 2 ? mr : 1.f);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) red[jc * CS + g * VEC + v] = acc[t][v];
-    __syncthreads();
-    if (tid < CS) {
-      float sum = 0.f;
-      for (int q = 0; q < kStripW; ++q) sum += red[q * CS + tid];
-      part[(pblk * 10 + t) * D + slab * CS + tid] = sum;
-    }
-    __syncthreads();
+    for (int e = 0; e < VEC; ++e) red[(jc * 10 + t) * CS + g * VEC + e] = mk * acc[k][e];
+  }
+  __syncthreads();
+  const long pblk = ((long)b * nstrip + strip) * nrg + rg;
+  for (int o = tid; o < 10 * CS; o += 256) {
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < W; ++q) s4[q & 3] += red[q * 10 * CS + o];
+    const int t = o / CS, ch = o - t * CS;
+    part[(pblk * 10 + t) * D + c0 + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   }
 }
 
@@ -761,14 +809,15 @@ struct StripPlan {
   int rows, cols, nslab, nstrip, nrg;
   long blocks;
 };
-static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout, int RH) {
+static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout, int RH,
+                            int slab_bytes = kStripG * 16, int width = kStripW) {
   StripPlan p{};
   const bool col = layout == kCol || layout == kColRev;
   p.rows = col ? gw : gh;
   p.cols = col ? gh : gw;
-  const int slabc = kStripG * 16 / elt;
+  const int slabc = slab_bytes / elt;
   p.nslab = D / slabc;
-  p.nstrip = (p.cols + kStripW - 1) / kStripW;
+  p.nstrip = (p.cols + width - 1) / width;
   p.nrg = (p.rows + RH - 1) / RH;
   p.blocks = (long)B * p.nrg * p.nstrip * p.nslab;
   p.ok = D % slabc == 0 && p.rows >= RH && p.blocks >= kStripMinBlocks;
@@ -797,29 +846,31 @@ static TilePlan tile_plan(int B, int gh, int gw, int D, int elt, int layout) {
   return t;
 }
 
+// Forward (column strips on large grids, 8 x 8 tiles on small ones, the generic kernel for
+// channel counts no slab divides); the backward's dx uses the generic kernel only (its strip
+// and tile paths are fused with the weight gradient).
 template <typename T, bool BWD>
 static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int out_layout,
                                 const void* x, const float* w, const float* bias, void* y,
                                 hipStream_t st) {
-  constexpr int RH = kStripRows;
-  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, RH);
-  if (sp.ok) {
-    const int rows = sp.rows, cols = sp.cols, nslab = sp.nslab, nstrip = sp.nstrip, nrg = sp.nrg;
-    const long blocks = sp.blocks;
-    hipLaunchKernelGGL((dwconv_strip_kernel<T, BWD, RH>), dim3((unsigned)blocks), dim3(256), 0,
-                       st, static_cast<const T*>(x), w, (!BWD && bias) ? bias : w,
-                       static_cast<T*>(y), rows, cols, D, (long)gh * gw,
-                       grid_map(gh, gw, layout, out_layout), (!BWD && bias) ? 1.f : 0.f, nslab,
-                       nstrip, nrg);
-    return hipGetLastError();
-  }
-  const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
-  if (tp.ok) {
-    hipLaunchKernelGGL((dwconv_tiled_kernel<T, BWD>), dim3((unsigned)tp.conv_blocks), dim3(256),
-                       0, st, static_cast<const T*>(x), w, bias, static_cast<T*>(y), D,
-                       (long)gh * gw, grid_map(gh, gw, layout, out_layout), tp.rows, tp.cols,
-                       tp.ntr, tp.ntc, tp.nslab);
-    return hipGetLastError();
+  if constexpr (!BWD) {
+    constexpr int RH = kStripRows;
+    const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, RH);
+    if (sp.ok) {
+      hipLaunchKernelGGL((dwconv_strip_kernel<T, RH>), dim3((unsigned)sp.blocks), dim3(256), 0,
+                         st, static_cast<const T*>(x), w, bias ? bias : w, static_cast<T*>(y),
+                         sp.rows, sp.cols, D, (long)gh * gw, grid_map(gh, gw, layout, out_layout),
+                         bias ? 1.f : 0.f, sp.nslab, sp.nstrip, sp.nrg);
+      return hipGetLastError();
+    }
+    const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
+    if (tp.ok) {
+      hipLaunchKernelGGL((dwconv_tiled_kernel<T>), dim3((unsigned)tp.conv_blocks), dim3(256), 0,
+                         st, static_cast<const T*>(x), w, bias, static_cast<T*>(y), D,
+                         (long)gh * gw, grid_map(gh, gw, layout, out_layout), tp.rows, tp.cols,
+                         tp.ntr, tp.ntc, tp.nslab);
+      return hipGetLastError();
+    }
   }
   const ConvPlan c = conv_plan(B, gh, gw, D, sizeof(T), layout, kConvSR, 16 / sizeof(T));
   dim3 blk(c.cgs, c.nj), grd(c.nblocks);
@@ -851,9 +902,16 @@ static ConvPlan dw_plan(int B, int gh, int gw, int D, int elt, int layout) {
   return conv_plan(B, gh, gw, D, elt, layout, kDwSR, 16 / elt);
 }
 
+// Plan of the fused column-strip backward: 128-byte channel slabs of kBwdVec-channel groups,
+// 256 / groups columns per strip.
+static StripPlan bwd_strip_plan(int B, int gh, int gw, int D, int elt, int layout) {
+  const int groups = kBwdSlabBytes / (kBwdVec * elt);
+  return strip_plan(B, gh, gw, D, elt, layout, kBwdRows, kBwdSlabBytes, 256 / groups);
+}
+
 // Number of [10][D] partial-sum slices the dw pass writes for one dtype and layout.
 static long dw_partials(int B, int gh, int gw, int D, int elt, int layout) {
-  const StripPlan sp = strip_plan(B, gh, gw, D, elt, layout, kStripRows);
+  const StripPlan sp = bwd_strip_plan(B, gh, gw, D, elt, layout);
   if (sp.ok) return (long)B * sp.nstrip * sp.nrg;
   const TilePlan tp = tile_plan(B, gh, gw, D, elt, layout);
   if (tp.ok) return (long)B * tp.ntr * tp.ntc;
@@ -876,16 +934,6 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
                               const void* x, const void* dy, float* dw, float* dbias,
                               float* part, hipStream_t st) {
   const long n = 10L * D;
-  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kStripRows);
-  if (sp.ok) {
-    hipLaunchKernelGGL((dwconv_dw_strip_kernel<T, kStripRows>), dim3((unsigned)sp.blocks),
-                       dim3(256), 0, st, static_cast<const T*>(x), static_cast<const T*>(dy), part,
-                       sp.rows, sp.cols, D, (long)gh * gw, grid_map(gh, gw, layout, out_layout),
-                       sp.nslab, sp.nstrip, sp.nrg);
-    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       part, (int)((long)B * sp.nstrip * sp.nrg), D, dw, dbias);
-    return hipGetLastError();
-  }
   const ConvPlan c = dw_plan(B, gh, gw, D, sizeof(T), layout);
   dim3 blk(c.cgs, c.nj), grd(c.nblocks);
   const size_t shm = (size_t)c.nj * c.cgs * c.VW * sizeof(float);
@@ -908,21 +956,31 @@ static hipError_t launch_dw_t(int B, int gh, int gw, int D, int layout, int out_
   return hipGetLastError();
 }
 
-// dx and the dW/dbias partials: column strips (two kernels) on large grids, one fused pass
-// over 8 x 8 tiles on small ones, the per-channel sums of the partials last.
+// dx and the dW/dbias partials in one pass (column strips on large grids, 8 x 8 tiles on
+// small ones; two generic kernels for channel counts no slab divides), then the per-channel
+// sums of the partials.
 template <typename T>
 static hipError_t launch_dwconv_bwd_t(int B, int gh, int gw, int D, int layout, int out_layout,
                                       const void* x, const float* w, const void* dy, void* dx,
                                       float* dw, float* dbias, float* part, hipStream_t st) {
-  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, kStripRows);
+  const long n = 10L * D;
+  const StripPlan sp = bwd_strip_plan(B, gh, gw, D, sizeof(T), layout);
+  if (sp.ok) {
+    hipLaunchKernelGGL((dwconv_bwd_strip_kernel<T, kBwdRows>), dim3((unsigned)sp.blocks),
+                       dim3(256), 0, st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
+                       static_cast<T*>(dx), part, sp.rows, sp.cols, D, (long)gh * gw,
+                       grid_map(gh, gw, layout, out_layout), sp.nslab, sp.nstrip, sp.nrg);
+    hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       part, (int)((long)B * sp.nstrip * sp.nrg), D, dw, dbias);
+    return hipGetLastError();
+  }
   const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
-  if (!sp.ok && tp.ok) {
+  if (tp.ok) {
     hipLaunchKernelGGL((dwconv_bwd_tiled_kernel<T>), dim3((unsigned)tp.conv_blocks), dim3(256), 0,
                        st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
                        static_cast<T*>(dx), part, D, (long)gh * gw,
                        grid_map(gh, gw, layout, out_layout), tp.rows, tp.cols, tp.ntr, tp.ntc,
                        tp.nslab);
-    const long n = 10L * D;
     hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        part, (int)((long)B * tp.ntr * tp.ntc), D, dw, dbias);
     return hipGetLastError();
