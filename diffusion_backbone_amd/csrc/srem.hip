@@ -41,6 +41,18 @@ struct __attribute__((aligned(VW * sizeof(T)))) Vec {
   T v[VW];
 };
 
+// Vector access at a wave-uniform base plus a per-lane 32-bit byte offset: the address form
+// global memory instructions take directly (base in scalar registers, offset in one vector
+// register), so an access costs no per-lane 64-bit address arithmetic.
+template <typename V>
+__device__ __forceinline__ V ld_at(const void* base, unsigned off) {
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + off);
+}
+template <typename V>
+__device__ __forceinline__ void st_at(void* base, unsigned off, const V& v) {
+  *reinterpret_cast<V*>(static_cast<char*>(base) + off) = v;
+}
+
 // ------------------------------------------------------------------ reorient
 template <typename V>
 __global__ __launch_bounds__(256) void reorient_kernel(const V* __restrict__ x, V* __restrict__ y,
@@ -546,18 +558,33 @@ __global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------ column-strip conv
-// One block: a strip of 16 current-grid columns x RH rows x one slab of 16 channel groups
-// (16 bytes each, so one token's slab is 256 contiguous bytes).  Thread (group g, column j)
-// loads its 16-byte vectors of columns j-1, j, j+1 for the RH + 2 input rows (the side
-// columns are the adjacent lanes' centre loads and come from L1), then forms its RH outputs
-// with the taps in registers.  There is no branch: a conditional store would let the
+// One block: a strip of W current-grid columns x RH rows x one 128-byte channel slab of G
+// groups of kStripVec channels (4 bytes per lane in bf16, 8 in fp32; G W = 256).  Thread
+// (group g, column j) loads its vectors of columns j-1, j, j+1 for the RH + 2 input rows (the
+// side columns are the adjacent lanes' centre loads and come from L1), then forms its RH
+// outputs with the taps in registers.  There is no branch: a conditional store would let the
 // compiler sink the loads next to their first use (one memory round trip per output row).
 // Out-of-grid rows and columns are loaded clamped and scaled by zero (rows) or get zero taps
 // (columns); columns past the grid repeat the last one and the last row group overlaps its
-// neighbour, both writing identical values.  Needs at least RH rows.  The input row of (i, j)
-// is its current position, the output row its position in out_layout (map m).
-constexpr int kStripG = 16, kStripW = 256 / kStripG;
+// neighbour, both writing identical values.  Needs at least RH rows.  Row bases are uniform
+// and lane offsets 32-bit (one image is below 2^31 bytes).
+constexpr int kStripVec = 2, kStripSlabBytes = 128;
 
+// Byte offset from a uniform row base of the token at map position Bj jj: with Bj < 0 the
+// lane term is taken over the reflected column so that it stays non-negative, the constant
+// Bj (cols - 1) moving into the base (see map_base).
+__device__ __forceinline__ unsigned map_lane_off(const GridMap& m, int jj, int cols, int D, int c,
+                                                 int elt) {
+  const bool rev = m.Bj < 0;
+  return (unsigned)(((rev ? cols - 1 - jj : jj) * (rev ? -m.Bj : m.Bj) * D + c) * (long)elt);
+}
+__device__ __forceinline__ long map_base(const GridMap& m, int cols) {
+  return m.A + (m.Bj < 0 ? m.Bj * (cols - 1) : 0);
+}
+
+// Forward: y at the position of (i, j) in out_layout (map m) = sum_{a,s} w[a][s] x(i+a-1,
+// j+s-1) + b, x read in the current order.  `bscale` is 0 when there is no bias (then `bias`
+// points at any readable D floats).
 template <typename T, int RH>
 __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ w,
@@ -566,70 +593,87 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
                                                            int D, long L, GridMap m,
                                                            float bscale, int nslab, int nstrip,
                                                            int nrg) {
-  constexpr int VEC = 16 / sizeof(T);
-  const int tid = threadIdx.x, g = tid % kStripG, jc = tid / kStripG;
+  constexpr int VEC = kStripVec;
+  constexpr int G = kStripSlabBytes / (VEC * (int)sizeof(T));
+  constexpr int W = 256 / G;
+  constexpr int CS = G * VEC;
+  using V = Vec<T, VEC>;
+  const int tid = threadIdx.x, g = tid % G, jc = tid / G;
   int blk = blockIdx.x;
   const int slab = blk % nslab; blk /= nslab;
   const int strip = blk % nstrip; blk /= nstrip;
   const int rg = blk % nrg;
   const int b = blk / nrg;
-  const int c = (slab * kStripG + g) * VEC;
+  const int c = slab * CS + g * VEC;
   const int i0 = min(rg * RH, rows - RH);
-  const int j = min(strip * kStripW + jc, cols - 1);
+  const int j = min(strip * W + jc, cols - 1);
   const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
   const long bL = (long)b * L;
+  const float ml = j > 0 ? 1.f : 0.f, mr = j < cols - 1 ? 1.f : 0.f;
+
+  // the lane's taps w[c .. c+VEC)[9]: 9 VEC contiguous floats, 8-byte aligned (VEC even)
+  float wv[9 * VEC];
+  {
+    const float2* wp = reinterpret_cast<const float2*>(w + (long)c * 9);
+#pragma unroll
+    for (int q = 0; q < 9 * VEC / 2; ++q) {
+      const float2 f = wp[q];
+      wv[2 * q] = f.x;
+      wv[2 * q + 1] = f.y;
+    }
+  }
+  const float2 bb = *reinterpret_cast<const float2*>(bias + c);
+  const T* xb = x + bL * D;
+  const unsigned oM = (unsigned)(((long)jm * D + c) * (long)sizeof(T));
+  const unsigned oC = (unsigned)(((long)j * D + c) * (long)sizeof(T));
+  const unsigned oP = (unsigned)(((long)jp * D + c) * (long)sizeof(T));
+  V xr[RH + 2][3];
+#pragma unroll
+  for (int r = 0; r < RH + 2; ++r) {
+    const T* rp = xb + (long)min(max(i0 - 1 + r, 0), rows - 1) * cols * D;
+    xr[r][0] = ld_at<V>(rp, oM);
+    xr[r][1] = ld_at<V>(rp, oC);
+    xr[r][2] = ld_at<V>(rp, oP);
+  }
 
   float wr[3][3][VEC];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
+    for (int s2 = 0; s2 < 3; ++s2)
 #pragma unroll
-      for (int v = 0; v < VEC; ++v)
-        wr[a][s][v] = w[(c + v) * 9 + a * 3 + s];
-#pragma unroll
-  for (int a = 0; a < 3; ++a)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      if (j == 0) wr[a][0][v] = 0.f;
-      if (j == cols - 1) wr[a][2][v] = 0.f;
-    }
-  // bias: `bscale` is 0 when there is none (then `bias` points at any readable D floats)
-  float bs[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) bs[v] = bscale * bias[c + v];
-
-  auto in_row = [&](int ii, int jj) -> long { return (long)ii * cols + jj; };
-  Vec<T, VEC> win[RH + 2][3];
-#pragma unroll
-  for (int r = 0; r < RH + 2; ++r) {
-    const int ii = min(max(i0 - 1 + r, 0), rows - 1);
-    win[r][0] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, jm)) * D + c);
-    win[r][1] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, j)) * D + c);
-    win[r][2] = *reinterpret_cast<const Vec<T, VEC>*>(x + (bL + in_row(ii, jp)) * D + c);
-  }
+      for (int e = 0; e < VEC; ++e)
+        wr[a][s2][e] = wv[e * 9 + a * 3 + s2] * (s2 == 0 ? ml : (s2 == 2 ? mr : 1.f));
+  const float bs[2] = {bscale * bb.x, bscale * bb.y};
+  static_assert(VEC == 2, "bias pair");
+  T* yb = y + (bL + map_base(m, cols)) * D;
+  const unsigned oY = map_lane_off(m, j, cols, D, c, (int)sizeof(T));
   // only the window's first and last rows can lie outside the grid
   const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
+  float fr[RH + 2][3][VEC];
+  auto cvt = [&](int r) {
+    const float sc = r == 0 ? m_top : (r == RH + 1 ? m_bot : 1.f);
+#pragma unroll
+    for (int s2 = 0; s2 < 3; ++s2)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) fr[r][s2][e] = sc * to_f(xr[r][s2].v[e]);
+  };
+  cvt(0);
+  cvt(1);
 #pragma unroll
   for (int r = 0; r < RH; ++r) {
-    const int i = i0 + r;
-    float acc[VEC];
+    cvt(r + 2);
+    V o;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = bs[v];
+    for (int e = 0; e < VEC; ++e) {
+      float acc = bs[e];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const float on = r + a == 0 ? m_top : (r + a == RH + 1 ? m_bot : 1.f);
+      for (int a = 0; a < 3; ++a)
 #pragma unroll
-      for (int s = 0; s < 3; ++s)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v)
-          acc[v] = fmaf(wr[a][s][v], on * to_f(win[r + a][s].v[v]), acc[v]);
+        for (int s2 = 0; s2 < 3; ++s2) acc = fmaf(wr[a][s2][e], fr[r + a][s2][e], acc);
+      o.v[e] = from_f<T>(acc);
     }
-    Vec<T, VEC> o;
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) o.v[v] = from_f<T>(acc[v]);
-    const long orow = m.A + m.Bi * i + m.Bj * j;
-    *reinterpret_cast<Vec<T, VEC>*>(y + (bL + orow) * D + c) = o;
+    st_at<V>(yb + m.Bi * (i0 + r) * D, oY, o);
   }
 }
 
@@ -646,15 +690,13 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
 // last row group that the previous group owns) add nothing to dW and rewrite identical dx.
 // The block's W columns are summed in a fixed order through LDS into part[blk][tap][D], blk
 // over (b, strip, row group).  No branch before the stores (loads stay in flight together).
-constexpr int kBwdVec = 2, kBwdSlabBytes = 128, kBwdRows = 16;
-
 template <typename T, int RH>
 __global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
     const T* __restrict__ x, const float* __restrict__ w, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ part, int rows, int cols, int D, long L, GridMap m,
     int nslab, int nstrip, int nrg) {
-  constexpr int VEC = kBwdVec;
-  constexpr int G = kBwdSlabBytes / (VEC * (int)sizeof(T));  // channel groups per slab
+  constexpr int VEC = kStripVec;
+  constexpr int G = kStripSlabBytes / (VEC * (int)sizeof(T));  // channel groups per slab
   constexpr int W = 256 / G;                                  // columns per strip
   constexpr int CS = G * VEC;                                 // channels per slab
   using V = Vec<T, VEC>;
@@ -684,18 +726,25 @@ __global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
       wv[2 * q + 1] = f.y;
     }
   }
+  // dy's position of (ii, jj) is A + Bi ii + Bj jj: a uniform row base plus a lane offset
+  const T* dyb = dy + (bL + map_base(m, cols)) * D;
+  const unsigned oM = map_lane_off(m, jm, cols, D, c, (int)sizeof(T));
+  const unsigned oC = map_lane_off(m, j, cols, D, c, (int)sizeof(T));
+  const unsigned oP = map_lane_off(m, jp, cols, D, c, (int)sizeof(T));
+  const unsigned oX = (unsigned)(((long)j * D + c) * (long)sizeof(T));
+  const T* xb = x + bL * D;
+  T* dxb = dx + bL * D;
   V dr[RH + 2][3], xr[RH];
 #pragma unroll
   for (int r = 0; r < RH + 2; ++r) {
     const int ii = min(max(i0 - 1 + r, 0), rows - 1);
-    const long base = bL + m.A + m.Bi * ii;
-    dr[r][0] = *reinterpret_cast<const V*>(dy + (base + m.Bj * jm) * D + c);
-    dr[r][1] = *reinterpret_cast<const V*>(dy + (base + m.Bj * j) * D + c);
-    dr[r][2] = *reinterpret_cast<const V*>(dy + (base + m.Bj * jp) * D + c);
+    const T* rp = dyb + m.Bi * ii * D;
+    dr[r][0] = ld_at<V>(rp, oM);
+    dr[r][1] = ld_at<V>(rp, oC);
+    dr[r][2] = ld_at<V>(rp, oP);
   }
 #pragma unroll
-  for (int r = 0; r < RH; ++r)
-    xr[r] = *reinterpret_cast<const V*>(x + (bL + (long)(i0 + r) * cols + j) * D + c);
+  for (int r = 0; r < RH; ++r) xr[r] = ld_at<V>(xb + (long)(i0 + r) * cols * D, oX);
 
   // dx taps, rotated by 180 degrees; out-of-grid side columns get zero taps
   float wr[3][3][VEC];
@@ -747,7 +796,7 @@ __global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
       acc[9][e] = fmaf(md, fr[r + 1][1][e], acc[9][e]);
       ov.v[e] = from_f<T>(o[e]);
     }
-    *reinterpret_cast<V*>(dx + (bL + (long)(i0 + r) * cols + j) * D + c) = ov;
+    st_at<V>(dxb + (long)(i0 + r) * cols * D, oX, ov);
   }
 
   // tap t = a*3 + s of dw is window slot 8 - t; clear the sums of out-of-grid side columns
@@ -799,28 +848,31 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 
 constexpr int kConvSR = 16;
 constexpr int kStripRows = 16;  // output rows per strip block
-constexpr long kStripMinBlocks = 64;
+constexpr long kStripMinBlocks = 256;
 
-// Column-strip plan: 16-column strips x RH-row groups x slabs of 16 channel groups.  Used
-// when the slab divides the channels, the grid has at least RH rows and there are enough
-// blocks (small grids go to the 8 x 8 tiles).
+// Column-strip plan (forward and backward): W-column strips x kStripRows-row groups x
+// 128-byte channel slabs.  Used when the slab divides the channels, the grid has at least
+// kStripRows rows, one image is below 2^31 bytes and there is at least one block per compute
+// unit (smaller grids go to the 8 x 8 tiles).
 struct StripPlan {
   bool ok;
   int rows, cols, nslab, nstrip, nrg;
   long blocks;
 };
-static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout, int RH,
-                            int slab_bytes = kStripG * 16, int width = kStripW) {
+static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout) {
+  constexpr int RH = kStripRows;
+  const int width = 256 / (kStripSlabBytes / (kStripVec * elt));
   StripPlan p{};
   const bool col = layout == kCol || layout == kColRev;
   p.rows = col ? gw : gh;
   p.cols = col ? gh : gw;
-  const int slabc = slab_bytes / elt;
+  const int slabc = kStripSlabBytes / elt;
   p.nslab = D / slabc;
   p.nstrip = (p.cols + width - 1) / width;
   p.nrg = (p.rows + RH - 1) / RH;
   p.blocks = (long)B * p.nrg * p.nstrip * p.nslab;
-  p.ok = D % slabc == 0 && p.rows >= RH && p.blocks >= kStripMinBlocks;
+  p.ok = D % slabc == 0 && p.rows >= RH && p.blocks >= kStripMinBlocks &&
+         (long)p.rows * p.cols * D * elt < (1L << 31);
   return p;
 }
 constexpr int kDwSR = 64;
@@ -855,7 +907,7 @@ static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int ou
                                 hipStream_t st) {
   if constexpr (!BWD) {
     constexpr int RH = kStripRows;
-    const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout, RH);
+    const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout);
     if (sp.ok) {
       hipLaunchKernelGGL((dwconv_strip_kernel<T, RH>), dim3((unsigned)sp.blocks), dim3(256), 0,
                          st, static_cast<const T*>(x), w, bias ? bias : w, static_cast<T*>(y),
@@ -902,16 +954,9 @@ static ConvPlan dw_plan(int B, int gh, int gw, int D, int elt, int layout) {
   return conv_plan(B, gh, gw, D, elt, layout, kDwSR, 16 / elt);
 }
 
-// Plan of the fused column-strip backward: 128-byte channel slabs of kBwdVec-channel groups,
-// 256 / groups columns per strip.
-static StripPlan bwd_strip_plan(int B, int gh, int gw, int D, int elt, int layout) {
-  const int groups = kBwdSlabBytes / (kBwdVec * elt);
-  return strip_plan(B, gh, gw, D, elt, layout, kBwdRows, kBwdSlabBytes, 256 / groups);
-}
-
 // Number of [10][D] partial-sum slices the dw pass writes for one dtype and layout.
 static long dw_partials(int B, int gh, int gw, int D, int elt, int layout) {
-  const StripPlan sp = bwd_strip_plan(B, gh, gw, D, elt, layout);
+  const StripPlan sp = strip_plan(B, gh, gw, D, elt, layout);
   if (sp.ok) return (long)B * sp.nstrip * sp.nrg;
   const TilePlan tp = tile_plan(B, gh, gw, D, elt, layout);
   if (tp.ok) return (long)B * tp.ntr * tp.ntc;
@@ -964,9 +1009,9 @@ static hipError_t launch_dwconv_bwd_t(int B, int gh, int gw, int D, int layout, 
                                       const void* x, const float* w, const void* dy, void* dx,
                                       float* dw, float* dbias, float* part, hipStream_t st) {
   const long n = 10L * D;
-  const StripPlan sp = bwd_strip_plan(B, gh, gw, D, sizeof(T), layout);
+  const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout);
   if (sp.ok) {
-    hipLaunchKernelGGL((dwconv_bwd_strip_kernel<T, kBwdRows>), dim3((unsigned)sp.blocks),
+    hipLaunchKernelGGL((dwconv_bwd_strip_kernel<T, kStripRows>), dim3((unsigned)sp.blocks),
                        dim3(256), 0, st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
                        static_cast<T*>(dx), part, sp.rows, sp.cols, D, (long)gh * gw,
                        grid_map(gh, gw, layout, out_layout), sp.nslab, sp.nstrip, sp.nrg);
