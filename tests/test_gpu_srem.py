@@ -53,8 +53,10 @@ def test_reorient_bit_exact(B, gh, gw, D, dtype):
     (1, 8, 8, 64, "f32", False), (1, 8, 8, 64, "f32", True), (2, 16, 16, 384, "bf16", False),
     (1, 5, 7, 12, "bf16", True), (2, 3, 4, 5, "f32", True), (1, 1, 1, 8, "bf16", False),
     (1, 9, 2, 1152, "bf16", False),
-    # column-strip path (>= 64 strip blocks): ragged rows and columns, overlapping last row group
-    (4, 37, 29, 384, "bf16", True), (6, 29, 37, 128, "f32", False),
+    # column-strip path (>= 256 strip blocks in every orientation: bf16 8-column strips x
+    # 64-channel slabs, fp32 16-column strips x 32-channel slabs, 16-row groups): ragged rows
+    # (overlapping last row group) and columns (repeated last column)
+    (6, 37, 29, 384, "bf16", True), (11, 29, 37, 128, "f32", False),
 ])
 def test_dwconv_all_layout_pairs(B, gh, gw, D, dtype, bias):
     dig = _dig()
@@ -105,7 +107,7 @@ def test_dwconv_full_configs(name):
 @pytest.mark.parametrize("B,gh,gw,D,dtype", [
     (1, 8, 8, 64, "f32"), (2, 16, 16, 384, "bf16"), (1, 5, 7, 12, "bf16"), (2, 3, 4, 5, "f32"),
     (1, 16, 16, 1152, "bf16"),
-    (4, 37, 29, 384, "bf16"), (6, 29, 37, 128, "f32"),  # column-strip dx path, ragged
+    (6, 37, 29, 384, "bf16"), (11, 29, 37, 128, "f32"),  # column-strip path, ragged
 ])
 def test_dwconv_bwd(B, gh, gw, D, dtype):
     dig = _dig()
@@ -128,3 +130,25 @@ def test_dwconv_bwd(B, gh, gw, D, dtype):
         dw2 = torch.empty_like(dw)
         dig.dig_dwconv3x3_bwd(B, gh, gw, D, DT[dtype], lay, out, xd, wd, dyd, dx, dw2, None, ws, wsb)
         assert torch.equal(dw, dw2), "dw not deterministic"
+
+
+@pytest.mark.parametrize("name", ["dig_s2_1792", "dig_xl2_2048"])
+def test_dwconv_bwd_full_configs(name):
+    dig = _dig()
+    cfg = W.CONFIGS[name]
+    case = W.make_srem_case(cfg)
+    B, gh, gw, D = cfg.batch, cfg.grid_h, cfg.grid_w, cfg.d_model
+    xd, dyd = to_dev(case.x, "bf16"), to_dev(case.dy, "bf16")
+    wd = torch.from_numpy(case.w.astype(np.float32)).cuda()
+    wsb = dig.dig_dwconv3x3_bwd_workspace_bytes(B, gh, gw, D)
+    ws = nbytes_buf(wsb)
+    lay, out = W.COL, W.ROW_REV
+    announce("dwconv bwd full %s %d->%d" % (name, lay, out))
+    dx = empty(xd.shape, "bf16")
+    dw = torch.empty((D, 3, 3), device="cuda")
+    db = torch.empty((D,), device="cuda")
+    dig.dig_dwconv3x3_bwd(B, gh, gw, D, 1, lay, out, xd, wd, dyd, dx, dw, db, ws, wsb)
+    rdx, rdw, rdb = oracle.dwconv3x3_bwd(case.x, case.w, case.dy, gh, gw, lay, out)
+    assert maxrel(to_f64(dx), rdx) <= TOL["bf16"], "dx"
+    assert maxrel(dw.cpu().numpy().astype(np.float64), rdw) <= TOL["bf16"], "dw"
+    assert maxrel(db.cpu().numpy().astype(np.float64), rdb) <= TOL["bf16"], "dbias"
