@@ -209,7 +209,22 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   // the state becomes an MFMA operand; they only meet zeros elsewhere)
   auto load_state = [&](int n, f32x4 (&dst)[STW]) {
     const float* src = p.states + (sbase + n) * dk * dv;
-    if constexpr (PF) {
+    if constexpr (PF && DK % 4 == 0) {
+      // A lane's four rows lie all inside d_k or all in the padding (where any rows do): one
+      // 32-bit offset per tile, the rows at immediate offsets from it.
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = min(wave + NW * m, NST - 1);
+        const int ct = u / NDV, et = u - ct * NDV;
+        const int e = min(et * 16 + r16, DV - 1);
+        const unsigned off = (unsigned)((min(ct * 16 + g4 * 4, DK - 4) * DV + e) * (int)sizeof(float));
+        const char* sp = reinterpret_cast<const char*>(src) + off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[m][i] = *reinterpret_cast<const float*>(sp + i * DV * (int)sizeof(float));
+      }
+      return;
+    } else if constexpr (PF) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
         const int u = min(wave + NW * m, NST - 1);
