@@ -105,9 +105,18 @@ constexpr bool bwd_lean() {
   return BwdLayout<T, DK, DV, C, FIN, false, NW, PAD>::bytes > kBwdLdsBudget;
 }
 
+// Register prefetch of the next chunk's raw rows (exact head shapes).  The final pass drops it
+// when a wave holds more than one state tile: those registers then go to the tiles (with the
+// prefetch the compiler spills inside the chunk loop).
+template <int DK, int DV, bool EXACT, bool FIN, int NW>
+constexpr bool bwd_prefetch() {
+  constexpr int stw = ((DK + 15) / 16 * ((DV + 15) / 16) + NW - 1) / NW;
+  return EXACT && !(FIN && stw > 1);
+}
+
 template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
-  constexpr bool PF = EXACT;  // register prefetch of the next chunk's raw rows
+  constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW>();
   constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
   using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF>;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE, DKB = Lo::DKB;
@@ -975,11 +984,12 @@ template <typename T, int DK, int DV, bool EXACT, int C>
 static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
   const long BH = (long)s.B * s.H;
   constexpr int NW = bwd_waves<T, DK, DV, EXACT>();
+  constexpr bool PF_FIN = bwd_prefetch<DK, DV, EXACT, true, NW>();
+  constexpr bool PF_A = bwd_prefetch<DK, DV, EXACT, false, NW>();
   constexpr int fin_bytes =
-      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, EXACT>(), NW, EXACT>::bytes;
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_FIN>(), NW, PF_FIN>::bytes;
   constexpr int a_bytes =
-      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, EXACT>(), NW,
-                EXACT>::bytes;
+      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, PF_A>(), NW, PF_A>::bytes;
   if (lds_out) {
     *lds_out = fin_bytes;
     return hipSuccess;
