@@ -91,7 +91,7 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
   if ((long long)d->batch * d->heads > (1LL << 30))
     return fail(DIG_ERR_UNSUPPORTED, "batch * heads too large");
   *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, d->chunk,
-                     d->dtype == DIG_BF16, d->seg_chunks);
+                     d->dtype == DIG_BF16, d->seg_chunks, pass == kBwd);
   const int lds = pass == kFwd ? dig::gla_fwd_lds_bytes(*s) : dig::gla_bwd_lds_bytes(*s);
   if (lds > kLdsLimit)
     return fail(DIG_ERR_UNSUPPORTED, "%s needs %d bytes of LDS for this shape (limit %d)",

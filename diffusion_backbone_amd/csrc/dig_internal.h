@@ -41,7 +41,8 @@ struct GlaFwdParams {
   int write_states;
 };
 
-GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks);
+// Launch plan of one pass (bwd selects the backward's automatic segment length).
+GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks, bool bwd);
 // LDS bytes of the forward's output pass for this shape (0 if no kernel exists for it).
 int gla_fwd_lds_bytes(const GlaShape& s);
 size_t gla_states_bytes(const GlaShape& s);

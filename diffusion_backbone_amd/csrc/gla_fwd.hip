@@ -29,7 +29,13 @@ bool gla_dim_class(int dk, int dv, int* ndk, int* ndv) {
   return false;
 }
 
-GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks) {
+// Compute units of the target GPU; the automatic segment length aims at one round of
+// workgroups over them: two co-resident workgroups per unit for the forward's chunk kernels,
+// one for the backward's (their registers allow no second workgroup).
+constexpr long kComputeUnits = 256;
+
+GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks,
+                  bool bwd) {
   GlaShape s;
   s.B = B; s.L = L; s.H = H; s.dk = dk; s.dv = dv; s.C = C; s.bf16 = bf16;
   s.ndk = s.ndv = 0;
@@ -37,11 +43,12 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   s.NC = (L + C - 1) / C;
   int sc = seg_chunks;
   if (sc <= 0) {
-    // aim for about 1024 segment workgroups; one segment per sequence when the (image,
-    // head) units alone already fill the chip
+    // as many segments per sequence as fill that round; one segment when the (image, head)
+    // units alone already do
     const long units = (long)B * H;
-    const long total = units * s.NC;
-    sc = units >= 512 ? s.NC : (int)(total / 1024);
+    const long target = kComputeUnits * (bwd ? 1 : 2);
+    const long nseg = units >= target || units < 1 ? 1 : target / units;
+    sc = (int)(((long)s.NC + nseg - 1) / nseg);
   }
   if (sc > s.NC) sc = s.NC;
   if (sc < 1) sc = 1;
