@@ -53,6 +53,43 @@ __device__ __forceinline__ void st_at(void* base, unsigned off, const V& v) {
   *reinterpret_cast<V*>(static_cast<char*>(base) + off) = v;
 }
 
+// Buffer-resource access: a per-image resource (base, byte size) in scalar registers, the
+// lane's byte offset in one vector register and a uniform byte offset (a row) in a scalar
+// register, so stepping to the next row costs no vector instruction.  Every access here lies
+// inside the resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const void* base, long bytes) {
+  constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: no format conversion
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
+}
+template <typename V>
+__device__ __forceinline__ V buf_ld(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  static_assert(sizeof(V) == 4 || sizeof(V) == 8, "4- or 8-byte lanes");
+  V v;
+  if constexpr (sizeof(V) == 4) {
+    const unsigned u = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    __builtin_memcpy(&v, &u, 4);
+  } else {
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    __builtin_memcpy(&v, &u, 8);
+  }
+  return v;
+}
+template <typename V>
+__device__ __forceinline__ void buf_st(const V& v, __amdgpu_buffer_rsrc_t r, unsigned voff,
+                                       unsigned soff) {
+  static_assert(sizeof(V) == 4 || sizeof(V) == 8, "4- or 8-byte lanes");
+  if constexpr (sizeof(V) == 4) {
+    unsigned u;
+    __builtin_memcpy(&u, &v, 4);
+    __builtin_amdgcn_raw_buffer_store_b32(u, r, voff, soff, 0);
+  } else {
+    unsigned __attribute__((ext_vector_type(2))) u;
+    __builtin_memcpy(&u, &v, 8);
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, voff, soff, 0);
+  }
+}
+
 // ------------------------------------------------------------------ reorient
 template <typename V>
 __global__ __launch_bounds__(256) void reorient_kernel(const V* __restrict__ x, V* __restrict__ y,
@@ -558,17 +595,18 @@ __global__ __launch_bounds__(256) void dwconv_bwd_tiled_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------ column-strip conv
-// One block: a strip of W current-grid columns x RH rows x one 128-byte channel slab of G
+// One block: a strip of W current-grid columns x rh rows x one 128-byte channel slab of G
 // groups of kStripVec channels (4 bytes per lane in bf16, 8 in fp32; G W = 256).  Thread
-// (group g, column j) loads its vectors of columns j-1, j, j+1 for the RH + 2 input rows (the
-// side columns are the adjacent lanes' centre loads and come from L1), then forms its RH
-// outputs with the taps in registers.  There is no branch: a conditional store would let the
-// compiler sink the loads next to their first use (one memory round trip per output row).
-// Out-of-grid rows and columns are loaded clamped and scaled by zero (rows) or get zero taps
-// (columns); columns past the grid repeat the last one and the last row group overlaps its
-// neighbour, both writing identical values.  Needs at least RH rows.  Row bases are uniform
-// and lane offsets 32-bit (one image is below 2^31 bytes).
-constexpr int kStripVec = 2, kStripSlabBytes = 128;
+// (group g, column j) streams down its column: input rows arrive in groups of kStripK, two
+// groups in flight while the previous ones are consumed, and each row's three vectors
+// (columns j-1, j, j+1; the side columns are the adjacent lanes' centre loads and come from
+// L1) enter a rolling 3-row window of floats.  No branch surrounds a load or store (the
+// compiler would then wait for every outstanding access): rows and columns outside the grid
+// are loaded clamped and scaled by zero (rows) or get zero taps (columns); columns past the
+// grid repeat the last one and the last row group overlaps its neighbour, both writing
+// identical values.  rh is a multiple of 2 kStripK and at most the row count.  Row bases are
+// uniform and lane offsets 32-bit (one image is below 2^31 bytes).
+constexpr int kStripVec = 2, kStripSlabBytes = 128, kStripK = 4;
 
 // Byte offset from a uniform row base of the token at map position Bj jj: with Bj < 0 the
 // lane term is taken over the reflected column so that it stays non-negative, the constant
@@ -582,60 +620,137 @@ __device__ __forceinline__ long map_base(const GridMap& m, int cols) {
   return m.A + (m.Bj < 0 ? m.Bj * (cols - 1) : 0);
 }
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) in turn, workgroup i to XCD
+// i mod 8.  Tiles are ordered slab fastest, then strip, and XCD x takes the x-th contiguous
+// eighth of them: the slabs of a strip run together (whole token rows are read and written
+// at about the same time) and the halo columns a block reads from its neighbour strips are
+// mostly in its own XCD's L2.
+__device__ __forceinline__ int xcd_tile(int blk, int nblk) {
+  constexpr int kXcds = 8;
+  const int x = blk % kXcds, local = blk / kXcds;
+  const int n8 = nblk / kXcds, rem = nblk % kXcds;
+  return x * n8 + min(x, rem) + local;
+}
+
+// Lane geometry shared by the strip kernels.
+template <typename T>
+struct StripLane {
+  static constexpr int VEC = kStripVec;
+  static constexpr int G = kStripSlabBytes / (VEC * (int)sizeof(T));  // groups per slab
+  static constexpr int W = 256 / G;                                   // columns per strip
+  static constexpr int CS = G * VEC;                                  // channels per slab
+  int g, jc, slab, strip, rg, b, c0, c, i0, jr, j, jm, jp;
+  long bL;
+  float ml, mr;  // 0 where the left / right neighbour column is outside the grid
+  __device__ StripLane(int rows, int cols, long L, int nslab, int nstrip, int nrg, int rh) {
+    const int tid = threadIdx.x;
+    g = tid % G; jc = tid / G;
+    int blk = xcd_tile(blockIdx.x, gridDim.x);
+    slab = blk % nslab; blk /= nslab;
+    strip = blk % nstrip; blk /= nstrip;
+    rg = blk % nrg;
+    b = blk / nrg;
+    c0 = slab * CS; c = c0 + g * VEC;
+    i0 = min(rg * rh, rows - rh);
+    jr = strip * W + jc; j = min(jr, cols - 1);
+    jm = max(j - 1, 0); jp = min(j + 1, cols - 1);
+    bL = (long)b * L;
+    ml = j > 0 ? 1.f : 0.f; mr = j < cols - 1 ? 1.f : 0.f;
+  }
+};
+
+// The lane's taps w[c .. c+VEC)[9]: 9 VEC contiguous floats, 8-byte aligned (VEC even).
+template <int VEC>
+__device__ __forceinline__ void lane_taps(float (&wv)[9 * VEC], const float* w, int c) {
+  const float2* wp = reinterpret_cast<const float2*>(w + (long)c * 9);
+#pragma unroll
+  for (int q = 0; q < 9 * VEC / 2; ++q) {
+    const float2 f = wp[q];
+    wv[2 * q] = f.x;
+    wv[2 * q + 1] = f.y;
+  }
+}
+
+// A channel pair as floats.  bf16 pairs are widened with byte permutes of the loaded dword
+// (a shift or mask of it lets the compiler re-load the upper half as a separate 16-bit load).
+template <typename T>
+__device__ __forceinline__ void pair_f(const Vec<T, 2>& p, float& lo, float& hi) {
+  if constexpr (sizeof(T) == 2) {
+    const unsigned u = *reinterpret_cast<const unsigned*>(&p);
+    lo = __uint_as_float(__builtin_amdgcn_perm(0u, u, 0x01000c0cu));
+    hi = __uint_as_float(__builtin_amdgcn_perm(0u, u, 0x03020c0cu));
+  } else {
+    lo = to_f(p.v[0]);
+    hi = to_f(p.v[1]);
+  }
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void vec_f(const Vec<T, VEC>& p, float (&f)[VEC]) {
+  static_assert(VEC % 2 == 0, "channel pairs");
+#pragma unroll
+  for (int q = 0; q < VEC / 2; ++q)
+    pair_f<T>(reinterpret_cast<const Vec<T, 2>*>(&p)[q], f[2 * q], f[2 * q + 1]);
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void cvt3(float (&dst)[3][VEC], const Vec<T, VEC> (&src)[3], float sc) {
+#pragma unroll
+  for (int s2 = 0; s2 < 3; ++s2) {
+    float f[VEC];
+    vec_f<T, VEC>(src[s2], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[s2][e] = sc * f[e];
+  }
+}
+template <int VEC>
+__device__ __forceinline__ void copy3(float (&dst)[3][VEC], const float (&src)[3][VEC]) {
+#pragma unroll
+  for (int s2 = 0; s2 < 3; ++s2)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dst[s2][e] = src[s2][e];
+}
+
 // Forward: y at the position of (i, j) in out_layout (map m) = sum_{a,s} w[a][s] x(i+a-1,
 // j+s-1) + b, x read in the current order.  `bscale` is 0 when there is no bias (then `bias`
 // points at any readable D floats).
-template <typename T, int RH>
+template <typename T>
 __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias,
                                                            T* __restrict__ y, int rows, int cols,
                                                            int D, long L, GridMap m,
                                                            float bscale, int nslab, int nstrip,
-                                                           int nrg) {
-  constexpr int VEC = kStripVec;
-  constexpr int G = kStripSlabBytes / (VEC * (int)sizeof(T));
-  constexpr int W = 256 / G;
-  constexpr int CS = G * VEC;
+                                                           int nrg, int rh) {
+  using Ln = StripLane<T>;
+  constexpr int VEC = Ln::VEC, K = kStripK;
   using V = Vec<T, VEC>;
-  const int tid = threadIdx.x, g = tid % G, jc = tid / G;
-  int blk = blockIdx.x;
-  const int slab = blk % nslab; blk /= nslab;
-  const int strip = blk % nstrip; blk /= nstrip;
-  const int rg = blk % nrg;
-  const int b = blk / nrg;
-  const int c = slab * CS + g * VEC;
-  const int i0 = min(rg * RH, rows - RH);
-  const int j = min(strip * W + jc, cols - 1);
-  const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
-  const long bL = (long)b * L;
-  const float ml = j > 0 ? 1.f : 0.f, mr = j < cols - 1 ? 1.f : 0.f;
+  const Ln ln(rows, cols, L, nslab, nstrip, nrg, rh);
+  const int i0 = ln.i0;
 
-  // the lane's taps w[c .. c+VEC)[9]: 9 VEC contiguous floats, 8-byte aligned (VEC even)
+  const long ibytes = L * D * (long)sizeof(T), rowb = (long)cols * D * (long)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rx = image_rsrc(x + ln.bL * D, ibytes);
+  const unsigned oM = (unsigned)(((long)ln.jm * D + ln.c) * (long)sizeof(T));
+  const unsigned oC = (unsigned)(((long)ln.j * D + ln.c) * (long)sizeof(T));
+  const unsigned oP = (unsigned)(((long)ln.jp * D + ln.c) * (long)sizeof(T));
+  auto load_row = [&](V (&dst)[3], int ii) {
+    const unsigned ro = (unsigned)(min(max(ii, 0), rows - 1) * rowb);
+    dst[0] = buf_ld<V>(rx, oM, ro);
+    dst[1] = buf_ld<V>(rx, oC, ro);
+    dst[2] = buf_ld<V>(rx, oP, ro);
+  };
+  // group q holds input rows i0 + qK + 1 .. i0 + qK + K (the row below each output row)
+  V bufA[K][3], bufB[K][3];
+  auto load_group = [&](V (&buf)[K][3], int q) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) load_row(buf[k], i0 + q * K + 1 + k);
+  };
+  V top[2][3];
+  load_row(top[0], i0 - 1);
+  load_row(top[1], i0);
+  load_group(bufA, 0);
+  load_group(bufB, 1);
+
   float wv[9 * VEC];
-  {
-    const float2* wp = reinterpret_cast<const float2*>(w + (long)c * 9);
-#pragma unroll
-    for (int q = 0; q < 9 * VEC / 2; ++q) {
-      const float2 f = wp[q];
-      wv[2 * q] = f.x;
-      wv[2 * q + 1] = f.y;
-    }
-  }
-  const float2 bb = *reinterpret_cast<const float2*>(bias + c);
-  const T* xb = x + bL * D;
-  const unsigned oM = (unsigned)(((long)jm * D + c) * (long)sizeof(T));
-  const unsigned oC = (unsigned)(((long)j * D + c) * (long)sizeof(T));
-  const unsigned oP = (unsigned)(((long)jp * D + c) * (long)sizeof(T));
-  V xr[RH + 2][3];
-#pragma unroll
-  for (int r = 0; r < RH + 2; ++r) {
-    const T* rp = xb + (long)min(max(i0 - 1 + r, 0), rows - 1) * cols * D;
-    xr[r][0] = ld_at<V>(rp, oM);
-    xr[r][1] = ld_at<V>(rp, oC);
-    xr[r][2] = ld_at<V>(rp, oP);
-  }
-
+  lane_taps<VEC>(wv, w, ln.c);
   float wr[3][3][VEC];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
@@ -643,44 +758,64 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
     for (int s2 = 0; s2 < 3; ++s2)
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
-        wr[a][s2][e] = wv[e * 9 + a * 3 + s2] * (s2 == 0 ? ml : (s2 == 2 ? mr : 1.f));
-  const float bs[2] = {bscale * bb.x, bscale * bb.y};
-  static_assert(VEC == 2, "bias pair");
-  T* yb = y + (bL + map_base(m, cols)) * D;
-  const unsigned oY = map_lane_off(m, j, cols, D, c, (int)sizeof(T));
-  // only the window's first and last rows can lie outside the grid
-  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
-  float fr[RH + 2][3][VEC];
-  auto cvt = [&](int r) {
-    const float sc = r == 0 ? m_top : (r == RH + 1 ? m_bot : 1.f);
+        wr[a][s2][e] = wv[e * 9 + a * 3 + s2] * (s2 == 0 ? ln.ml : (s2 == 2 ? ln.mr : 1.f));
+  float bs[VEC];
 #pragma unroll
-    for (int s2 = 0; s2 < 3; ++s2)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) fr[r][s2][e] = sc * to_f(xr[r][s2].v[e]);
-  };
-  cvt(0);
-  cvt(1);
-#pragma unroll
-  for (int r = 0; r < RH; ++r) {
-    cvt(r + 2);
-    V o;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float acc = bs[e];
-#pragma unroll
-      for (int a = 0; a < 3; ++a)
-#pragma unroll
-        for (int s2 = 0; s2 < 3; ++s2) acc = fmaf(wr[a][s2][e], fr[r + a][s2][e], acc);
-      o.v[e] = from_f<T>(acc);
-    }
-    st_at<V>(yb + m.Bi * (i0 + r) * D, oY, o);
+  for (int q = 0; q < VEC / 2; ++q) {
+    const float2 bb = reinterpret_cast<const float2*>(bias + ln.c)[q];
+    bs[2 * q] = bscale * bb.x;
+    bs[2 * q + 1] = bscale * bb.y;
   }
+  // y's position of (i, j) is A + Bi i + Bj j: a uniform row offset (a valid position, so
+  // non-negative) plus a lane offset
+  const __amdgpu_buffer_rsrc_t ry = image_rsrc(y + ln.bL * D, ibytes);
+  const long ybase = map_base(m, cols);
+  const unsigned oY = map_lane_off(m, ln.j, cols, D, ln.c, (int)sizeof(T));
+
+  float fa[3][VEC], fb[3][VEC];  // window rows i-1 and i
+  cvt3<T, VEC>(fa, top[0], i0 > 0 ? 1.f : 0.f);
+  cvt3<T, VEC>(fb, top[1], 1.f);
+  // only the block's last row can have its lower neighbour outside the grid
+  const float m_bot = i0 + rh < rows ? 1.f : 0.f;
+  auto process = [&](const V (&buf)[K][3], int q, auto last) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = i0 + q * K + k;
+      float fc[3][VEC];
+      cvt3<T, VEC>(fc, buf[k], decltype(last)::value && k == K - 1 ? m_bot : 1.f);
+      V o;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float acc = bs[e];
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+          acc = fmaf(wr[0][s2][e], fa[s2][e], acc);
+          acc = fmaf(wr[1][s2][e], fb[s2][e], acc);
+          acc = fmaf(wr[2][s2][e], fc[s2][e], acc);
+        }
+        o.v[e] = from_f<T>(acc);
+      }
+      buf_st<V>(o, ry, oY, (unsigned)((ybase + m.Bi * i) * D * (long)sizeof(T)));
+      copy3<VEC>(fa, fb);
+      copy3<VEC>(fb, fc);
+    }
+  };
+  const int ng = rh / K;  // even, >= 2
+  for (int q = 0; q < ng - 2; q += 2) {
+    process(bufA, q, std::false_type{});
+    load_group(bufA, q + 2);
+    process(bufB, q + 1, std::false_type{});
+    load_group(bufB, q + 3);
+  }
+  process(bufA, ng - 2, std::false_type{});
+  process(bufB, ng - 1, std::true_type{});
 }
 
 // Backward of the conv in one pass over column strips: dx and the dW/dbias partials.  Thread
-// (group g, column j) owns VEC channels of one current-grid column and walks RH rows.  With
-// the dy window win[u][v] = dy(i-1+u, j-1+v) around the input position (i, j), dy being zero
-// outside the grid, the adjoint of y(i, j) = sum_{a,s} w[a][s] x(i+a-1, j+s-1) + b is
+// (group g, column j) owns VEC channels of one current-grid column and streams its rh rows as
+// the forward does.  With the dy window win[u][v] = dy(i-1+u, j-1+v) around the input
+// position (i, j), dy being zero outside the grid, the adjoint of y(i, j) = sum_{a,s} w[a][s]
+// x(i+a-1, j+s-1) + b is
 //   dx(i, j) = sum_{u,v} w[2-u][2-v] win[u][v],   dw[2-u][2-v] += x(i, j) win[u][v],
 //   dbias += win[1][1]
 // so one window serves both, and dy is read once per position (x and dx once each).
@@ -689,63 +824,58 @@ __global__ __launch_bounds__(256) void dwconv_strip_kernel(const T* __restrict__
 // thread does not own (columns past the grid repeating the last one, rows of an overlapping
 // last row group that the previous group owns) add nothing to dW and rewrite identical dx.
 // The block's W columns are summed in a fixed order through LDS into part[blk][tap][D], blk
-// over (b, strip, row group).  No branch before the stores (loads stay in flight together).
-template <typename T, int RH>
+// over (b, strip, row group).
+template <typename T>
 __global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
     const T* __restrict__ x, const float* __restrict__ w, const T* __restrict__ dy,
     T* __restrict__ dx, float* __restrict__ part, int rows, int cols, int D, long L, GridMap m,
-    int nslab, int nstrip, int nrg) {
-  constexpr int VEC = kStripVec;
-  constexpr int G = kStripSlabBytes / (VEC * (int)sizeof(T));  // channel groups per slab
-  constexpr int W = 256 / G;                                  // columns per strip
-  constexpr int CS = G * VEC;                                 // channels per slab
+    int nslab, int nstrip, int nrg, int rh) {
+  using Ln = StripLane<T>;
+  constexpr int VEC = Ln::VEC, K = kStripK, W = Ln::W, CS = Ln::CS;
   using V = Vec<T, VEC>;
   __shared__ float red[W * 10 * CS];
-  const int tid = threadIdx.x, g = tid % G, jc = tid / G;
-  int blk = blockIdx.x;
-  const int slab = blk % nslab; blk /= nslab;
-  const int strip = blk % nstrip; blk /= nstrip;
-  const int rg = blk % nrg;
-  const int b = blk / nrg;
-  const int c0 = slab * CS, c = c0 + g * VEC;
-  const int i0 = min(rg * RH, rows - RH), first_own = rg * RH;
-  const int jr = strip * W + jc, j = min(jr, cols - 1);
-  const int jm = max(j - 1, 0), jp = min(j + 1, cols - 1);
-  const long bL = (long)b * L;
-  const float mj = jr < cols ? 1.f : 0.f;
-  const float ml = j > 0 ? 1.f : 0.f, mr = j < cols - 1 ? 1.f : 0.f;
+  const Ln ln(rows, cols, L, nslab, nstrip, nrg, rh);
+  const int i0 = ln.i0, first_own = ln.rg * rh;
+  const float mj = ln.jr < cols ? 1.f : 0.f;
 
-  // the lane's taps w[c .. c+VEC)[9]: 9 VEC contiguous floats, 8-byte aligned (VEC even)
-  float wv[9 * VEC];
-  {
-    const float2* wp = reinterpret_cast<const float2*>(w + (long)c * 9);
+  // dy's position of (ii, jj) is A + Bi ii + Bj jj: a uniform row offset (a valid position,
+  // so non-negative) plus a lane offset
+  const long ibytes = L * D * (long)sizeof(T), rowb = (long)cols * D * (long)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rdy = image_rsrc(dy + ln.bL * D, ibytes);
+  const __amdgpu_buffer_rsrc_t rx = image_rsrc(x + ln.bL * D, ibytes);
+  const __amdgpu_buffer_rsrc_t rdx = image_rsrc(dx + ln.bL * D, ibytes);
+  const long dybase = map_base(m, cols);
+  const unsigned oM = map_lane_off(m, ln.jm, cols, D, ln.c, (int)sizeof(T));
+  const unsigned oC = map_lane_off(m, ln.j, cols, D, ln.c, (int)sizeof(T));
+  const unsigned oP = map_lane_off(m, ln.jp, cols, D, ln.c, (int)sizeof(T));
+  const unsigned oX = (unsigned)(((long)ln.j * D + ln.c) * (long)sizeof(T));
+  auto load_dy = [&](V (&dst)[3], int ii) {
+    const unsigned ro =
+        (unsigned)((dybase + m.Bi * min(max(ii, 0), rows - 1)) * D * (long)sizeof(T));
+    dst[0] = buf_ld<V>(rdy, oM, ro);
+    dst[1] = buf_ld<V>(rdy, oC, ro);
+    dst[2] = buf_ld<V>(rdy, oP, ro);
+  };
+  // group q: dy rows i0 + qK + 1 .. i0 + qK + K (slots 0..2) and x rows i0 + qK .. (slot 3)
+  V bufA[K][4], bufB[K][4];
+  auto load_group = [&](V (&buf)[K][4], int q) {
 #pragma unroll
-    for (int q = 0; q < 9 * VEC / 2; ++q) {
-      const float2 f = wp[q];
-      wv[2 * q] = f.x;
-      wv[2 * q + 1] = f.y;
+    for (int k = 0; k < K; ++k) {
+      const int i = i0 + q * K + k;
+      V t[3];
+      load_dy(t, i + 1);
+      buf[k][0] = t[0]; buf[k][1] = t[1]; buf[k][2] = t[2];
+      buf[k][3] = buf_ld<V>(rx, oX, (unsigned)(i * rowb));
     }
-  }
-  // dy's position of (ii, jj) is A + Bi ii + Bj jj: a uniform row base plus a lane offset
-  const T* dyb = dy + (bL + map_base(m, cols)) * D;
-  const unsigned oM = map_lane_off(m, jm, cols, D, c, (int)sizeof(T));
-  const unsigned oC = map_lane_off(m, j, cols, D, c, (int)sizeof(T));
-  const unsigned oP = map_lane_off(m, jp, cols, D, c, (int)sizeof(T));
-  const unsigned oX = (unsigned)(((long)j * D + c) * (long)sizeof(T));
-  const T* xb = x + bL * D;
-  T* dxb = dx + bL * D;
-  V dr[RH + 2][3], xr[RH];
-#pragma unroll
-  for (int r = 0; r < RH + 2; ++r) {
-    const int ii = min(max(i0 - 1 + r, 0), rows - 1);
-    const T* rp = dyb + m.Bi * ii * D;
-    dr[r][0] = ld_at<V>(rp, oM);
-    dr[r][1] = ld_at<V>(rp, oC);
-    dr[r][2] = ld_at<V>(rp, oP);
-  }
-#pragma unroll
-  for (int r = 0; r < RH; ++r) xr[r] = ld_at<V>(xb + (long)(i0 + r) * cols * D, oX);
+  };
+  V top[2][3];
+  load_dy(top[0], i0 - 1);
+  load_dy(top[1], i0);
+  load_group(bufA, 0);
+  load_group(bufB, 1);
 
+  float wv[9 * VEC];
+  lane_taps<VEC>(wv, w, ln.c);
   // dx taps, rotated by 180 degrees; out-of-grid side columns get zero taps
   float wr[3][3][VEC];
 #pragma unroll
@@ -754,67 +884,82 @@ __global__ __launch_bounds__(256) void dwconv_bwd_strip_kernel(
     for (int v = 0; v < 3; ++v)
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
-        wr[u][v][e] = wv[e * 9 + (2 - u) * 3 + (2 - v)] * (v == 0 ? ml : (v == 2 ? mr : 1.f));
-  const float m_top = i0 > 0 ? 1.f : 0.f, m_bot = i0 + RH < rows ? 1.f : 0.f;
-  float fr[RH + 2][3][VEC];
-  auto cvt = [&](int r) {
-    const float sc = r == 0 ? m_top : (r == RH + 1 ? m_bot : 1.f);
-#pragma unroll
-    for (int v = 0; v < 3; ++v)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) fr[r][v][e] = sc * to_f(dr[r][v].v[e]);
-  };
+        wr[u][v][e] = wv[e * 9 + (2 - u) * 3 + (2 - v)] * (v == 0 ? ln.ml : (v == 2 ? ln.mr : 1.f));
   float acc[10][VEC];
 #pragma unroll
   for (int t = 0; t < 10; ++t)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[t][e] = 0.f;
-  cvt(0);
-  cvt(1);
+
+  float fa[3][VEC], fb[3][VEC];  // dy window rows i-1 and i
+  cvt3<T, VEC>(fa, top[0], i0 > 0 ? 1.f : 0.f);
+  cvt3<T, VEC>(fb, top[1], 1.f);
+  // only the block's last row can have its lower neighbour outside the grid
+  const float m_bot = i0 + rh < rows ? 1.f : 0.f;
+  auto process = [&](const V (&buf)[K][4], int q, auto last) {
 #pragma unroll
-  for (int r = 0; r < RH; ++r) {
-    cvt(r + 2);
-    const float md = i0 + r >= first_own ? mj : 0.f;
-    float xm[VEC], o[VEC];
+    for (int k = 0; k < K; ++k) {
+      const int i = i0 + q * K + k;
+      float fc[3][VEC];
+      const V dr[3] = {buf[k][0], buf[k][1], buf[k][2]};
+      cvt3<T, VEC>(fc, dr, decltype(last)::value && k == K - 1 ? m_bot : 1.f);
+      const float md = i >= first_own ? mj : 0.f;
+      float xm[VEC], o[VEC];
+      vec_f<T, VEC>(buf[k][3], xm);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      xm[e] = md * to_f(xr[r].v[e]);
-      o[e] = 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 3; ++u)
+      for (int e = 0; e < VEC; ++e) {
+        xm[e] *= md;
+        o[e] = 0.f;
+      }
 #pragma unroll
       for (int v = 0; v < 3; ++v)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          o[e] = fmaf(wr[u][v][e], fr[r + u][v][e], o[e]);
-          acc[u * 3 + v][e] = fmaf(xm[e], fr[r + u][v][e], acc[u * 3 + v][e]);
+          o[e] = fmaf(wr[0][v][e], fa[v][e], o[e]);
+          o[e] = fmaf(wr[1][v][e], fb[v][e], o[e]);
+          o[e] = fmaf(wr[2][v][e], fc[v][e], o[e]);
+          acc[v][e] = fmaf(xm[e], fa[v][e], acc[v][e]);
+          acc[3 + v][e] = fmaf(xm[e], fb[v][e], acc[3 + v][e]);
+          acc[6 + v][e] = fmaf(xm[e], fc[v][e], acc[6 + v][e]);
         }
-    V ov;
+      V ov;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      acc[9][e] = fmaf(md, fr[r + 1][1][e], acc[9][e]);
-      ov.v[e] = from_f<T>(o[e]);
+      for (int e = 0; e < VEC; ++e) {
+        acc[9][e] = fmaf(md, fb[1][e], acc[9][e]);
+        ov.v[e] = from_f<T>(o[e]);
+      }
+      buf_st<V>(ov, rdx, oX, (unsigned)(i * rowb));
+      copy3<VEC>(fa, fb);
+      copy3<VEC>(fb, fc);
     }
-    st_at<V>(dxb + (long)(i0 + r) * cols * D, oX, ov);
+  };
+  const int ng = rh / K;  // even, >= 2
+  for (int q = 0; q < ng - 2; q += 2) {
+    process(bufA, q, std::false_type{});
+    load_group(bufA, q + 2);
+    process(bufB, q + 1, std::false_type{});
+    load_group(bufB, q + 3);
   }
+  process(bufA, ng - 2, std::false_type{});
+  process(bufB, ng - 1, std::true_type{});
 
   // tap t = a*3 + s of dw is window slot 8 - t; clear the sums of out-of-grid side columns
+  const int jc = ln.jc, g = ln.g;
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
     const int k = t < 9 ? 8 - t : 9;
-    const float mk = k % 3 == 0 && k < 9 ? ml : (k % 3 == 2 ? mr : 1.f);
+    const float mk = k % 3 == 0 && k < 9 ? ln.ml : (k % 3 == 2 ? ln.mr : 1.f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) red[(jc * 10 + t) * CS + g * VEC + e] = mk * acc[k][e];
   }
   __syncthreads();
-  const long pblk = ((long)b * nstrip + strip) * nrg + rg;
-  for (int o = tid; o < 10 * CS; o += 256) {
+  const long pblk = ((long)ln.b * nstrip + ln.strip) * nrg + ln.rg;
+  for (int o = threadIdx.x; o < 10 * CS; o += 256) {
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < W; ++q) s4[q & 3] += red[q * 10 * CS + o];
     const int t = o / CS, ch = o - t * CS;
-    part[(pblk * 10 + t) * D + c0 + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    part[(pblk * 10 + t) * D + ln.c0 + ch] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   }
 }
 
@@ -847,20 +992,21 @@ static ConvPlan conv_plan(int B, int gh, int gw, int D, int elt, int layout, int
 }
 
 constexpr int kConvSR = 16;
-constexpr int kStripRows = 16;  // output rows per strip block
 constexpr long kStripMinBlocks = 256;
+constexpr long kStripTargetBlocks = 1024;
 
-// Column-strip plan (forward and backward): W-column strips x kStripRows-row groups x
-// 128-byte channel slabs.  Used when the slab divides the channels, the grid has at least
-// kStripRows rows, one image is below 2^31 bytes and there is at least one block per compute
-// unit (smaller grids go to the 8 x 8 tiles).
+// Column-strip plan (forward and backward): W-column strips x rh-row groups x 128-byte
+// channel slabs, rh a multiple of 2 kStripK chosen for about kStripTargetBlocks blocks (longer
+// row runs when the strips and slabs alone give many).  Used when the slab divides the
+// channels, the grid has at least 2 kStripK rows, one image is below 2^31 bytes and there is at
+// least one block per compute unit (smaller grids go to the 8 x 8 tiles).
 struct StripPlan {
   bool ok;
-  int rows, cols, nslab, nstrip, nrg;
+  int rows, cols, nslab, nstrip, nrg, rh;
   long blocks;
 };
 static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout) {
-  constexpr int RH = kStripRows;
+  constexpr int unit = 2 * kStripK;
   const int width = 256 / (kStripSlabBytes / (kStripVec * elt));
   StripPlan p{};
   const bool col = layout == kCol || layout == kColRev;
@@ -869,10 +1015,17 @@ static StripPlan strip_plan(int B, int gh, int gw, int D, int elt, int layout) {
   const int slabc = kStripSlabBytes / elt;
   p.nslab = D / slabc;
   p.nstrip = (p.cols + width - 1) / width;
-  p.nrg = (p.rows + RH - 1) / RH;
-  p.blocks = (long)B * p.nrg * p.nstrip * p.nslab;
-  p.ok = D % slabc == 0 && p.rows >= RH && p.blocks >= kStripMinBlocks &&
-         (long)p.rows * p.cols * D * elt < (1L << 31);
+  if (p.rows < unit || D % slabc != 0 || B < 1) return p;
+  const long base = (long)B * p.nstrip * p.nslab;
+  long want = (kStripTargetBlocks + base - 1) / base;  // row groups wanted
+  if (want < 1) want = 1;
+  long rh = ((p.rows + want - 1) / want + unit - 1) / unit * unit;
+  const int rmax = p.rows / unit * unit;
+  if (rh > rmax) rh = rmax;
+  p.rh = (int)rh;
+  p.nrg = (p.rows + p.rh - 1) / p.rh;
+  p.blocks = base * p.nrg;
+  p.ok = p.blocks >= kStripMinBlocks && (long)p.rows * p.cols * D * elt < (1L << 31);
   return p;
 }
 constexpr int kDwSR = 64;
@@ -906,13 +1059,12 @@ static hipError_t launch_conv_t(int B, int gh, int gw, int D, int layout, int ou
                                 const void* x, const float* w, const float* bias, void* y,
                                 hipStream_t st) {
   if constexpr (!BWD) {
-    constexpr int RH = kStripRows;
     const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout);
     if (sp.ok) {
-      hipLaunchKernelGGL((dwconv_strip_kernel<T, RH>), dim3((unsigned)sp.blocks), dim3(256), 0,
-                         st, static_cast<const T*>(x), w, bias ? bias : w, static_cast<T*>(y),
+      hipLaunchKernelGGL((dwconv_strip_kernel<T>), dim3((unsigned)sp.blocks), dim3(256), 0, st,
+                         static_cast<const T*>(x), w, bias ? bias : w, static_cast<T*>(y),
                          sp.rows, sp.cols, D, (long)gh * gw, grid_map(gh, gw, layout, out_layout),
-                         bias ? 1.f : 0.f, sp.nslab, sp.nstrip, sp.nrg);
+                         bias ? 1.f : 0.f, sp.nslab, sp.nstrip, sp.nrg, sp.rh);
       return hipGetLastError();
     }
     const TilePlan tp = tile_plan(B, gh, gw, D, sizeof(T), layout);
@@ -1011,10 +1163,10 @@ static hipError_t launch_dwconv_bwd_t(int B, int gh, int gw, int D, int layout, 
   const long n = 10L * D;
   const StripPlan sp = strip_plan(B, gh, gw, D, sizeof(T), layout);
   if (sp.ok) {
-    hipLaunchKernelGGL((dwconv_bwd_strip_kernel<T, kStripRows>), dim3((unsigned)sp.blocks),
-                       dim3(256), 0, st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
+    hipLaunchKernelGGL((dwconv_bwd_strip_kernel<T>), dim3((unsigned)sp.blocks), dim3(256), 0,
+                       st, static_cast<const T*>(x), w, static_cast<const T*>(dy),
                        static_cast<T*>(dx), part, sp.rows, sp.cols, D, (long)gh * gw,
-                       grid_map(gh, gw, layout, out_layout), sp.nslab, sp.nstrip, sp.nrg);
+                       grid_map(gh, gw, layout, out_layout), sp.nslab, sp.nstrip, sp.nrg, sp.rh);
     hipLaunchKernelGGL(dwconv_dw_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        part, (int)((long)B * sp.nstrip * sp.nrg), D, dw, dbias);
     return hipGetLastError();
