@@ -329,11 +329,20 @@ def probes():
                 "call": "dig_" + ("srem_" + name if name == "reorient" else name),
                 "shape": [B, gh, gw, D], "us": round(t, 1), "achieved_gbs": round(gbs, 1),
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        # reference ceiling: the runtime's own device copy of the same bytes (torch copy_)
+        t = _time_us(lambda: y.copy_(x))
+        gbs = 2 * nb / (t / 1e6) / 1e9
+        out["%s_copy_ref" % label] = {
+            "call": "torch copy_ (reference, not the library)", "shape": [B, gh, gw, D],
+            "us": round(t, 1), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del x, dy, y, dx, ws
 
     gla("s2_b256", 256, 256, 6, 32, 64)
     c5 = W.CONFIGS["dig_xl2_2048"]
     gla("xl2_2048", c5.batch, c5.seq_len, c5.heads, c5.d_k, c5.d_v)
     srem("xl2_2048", c5.batch, c5.grid_h, c5.grid_w, c5.d_model)
+    # 16 images: 604 MB per tensor, past the 256 MB Infinity Cache (HBM streaming regime)
+    srem("xl2_2048_b16", 16, c5.grid_h, c5.grid_w, c5.d_model)
     torch.cuda.empty_cache()
     return out
 

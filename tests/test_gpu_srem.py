@@ -52,10 +52,10 @@ def test_reorient_bit_exact(B, gh, gw, D, dtype):
 @pytest.mark.parametrize("B,gh,gw,D,dtype,bias", [
     (1, 8, 8, 64, "f32", False), (1, 8, 8, 64, "f32", True), (2, 16, 16, 384, "bf16", False),
     (1, 5, 7, 12, "bf16", True), (2, 3, 4, 5, "f32", True), (1, 1, 1, 8, "bf16", False),
-    (1, 9, 2, 1152, "bf16", False),
-    # column-strip path (>= 256 strip blocks in every orientation: bf16 8-column strips x
-    # 64-channel slabs, fp32 16-column strips x 32-channel slabs, 16-row groups): ragged rows
-    # (overlapping last row group) and columns (repeated last column)
+    (1, 9, 2, 1152, "bf16", False), (2, 5, 6, 64, "f32", True),  # fewer than 8 rows: tiles
+    # column-strip path (bf16 8-column strips x 64-channel slabs, fp32 16-column strips x
+    # 32-channel slabs, row runs of multiples of 8): ragged rows (overlapping last row
+    # group) and columns (repeated last column)
     (6, 37, 29, 384, "bf16", True), (11, 29, 37, 128, "f32", False),
 ])
 def test_dwconv_all_layout_pairs(B, gh, gw, D, dtype, bias):
@@ -106,7 +106,7 @@ def test_dwconv_full_configs(name):
 
 @pytest.mark.parametrize("B,gh,gw,D,dtype", [
     (1, 8, 8, 64, "f32"), (2, 16, 16, 384, "bf16"), (1, 5, 7, 12, "bf16"), (2, 3, 4, 5, "f32"),
-    (1, 16, 16, 1152, "bf16"),
+    (1, 16, 16, 1152, "bf16"), (1, 9, 2, 1152, "bf16"), (2, 5, 6, 64, "f32"),
     (6, 37, 29, 384, "bf16"), (11, 29, 37, 128, "f32"),  # column-strip path, ragged
 ])
 def test_dwconv_bwd(B, gh, gw, D, dtype):
