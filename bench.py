@@ -175,10 +175,10 @@ class EventTimer:
 TRAFFIC = {
     "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    # FETCH_SIZE 13214.3 KiB / 0.50018 (copy: 131120.1 KiB read per 262144 KiB moved) +
+    # FETCH_SIZE 13204.1 KiB / 0.50017 (copy: 131117.6 KiB read per 262144 KiB moved) +
     # WRITE_SIZE 8522.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-    "bytes": 35779433,
-    "sources_sha256": "320bc2b313e8966982eaee831aa82acd18f3becd9b8c3e67bcce78036c67a461",
+    "bytes": 35759120,
+    "sources_sha256": "98b82adb408fcf944dcba2ff2e57777f8231d56266aea9f155d02163b277b15e",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
