@@ -90,56 +90,6 @@ __device__ __forceinline__ void buf_st(const V& v, __amdgpu_buffer_rsrc_t r, uns
   }
 }
 
-// ------------------------------------------------------------------ reorient
-template <typename V>
-__global__ __launch_bounds__(256) void reorient_kernel(const V* __restrict__ x, V* __restrict__ y,
-                                                       long rows, long L, int nv, int gh, int gw,
-                                                       int from, int to) {
-  const long total = rows * nv;
-  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (long)gridDim.x * blockDim.x) {
-    const long row = i / nv;
-    const int v = (int)(i - row * nv);
-    const long b = row / L, p = row - b * L;
-    const long src = scan_inv(from, scan_pi(to, p, gh, gw, L), gh, gw, L);
-    y[i] = x[(b * L + src) * nv + v];
-  }
-}
-
-hipError_t launch_reorient(int B, int gh, int gw, int D, int elt, int from, int to,
-                           const void* x, void* y, hipStream_t st) {
-  const long L = (long)gh * gw, rows = (long)B * L;
-  const long rowbytes = (long)D * elt;
-  const long total_bytes = rows * rowbytes;
-  long blocks_cap = 256L * 16;
-  auto grid = [&](long items) {
-    long g = (items + 255) / 256;
-    return (unsigned)(g < blocks_cap ? g : blocks_cap);
-  };
-  if (rowbytes % 16 == 0) {
-    const int nv = (int)(rowbytes / 16);
-    hipLaunchKernelGGL(reorient_kernel<uint4>, dim3(grid(total_bytes / 16)), dim3(256), 0, st,
-                       static_cast<const uint4*>(x), static_cast<uint4*>(y), rows, L, nv, gh, gw,
-                       from, to);
-  } else if (rowbytes % 8 == 0) {
-    const int nv = (int)(rowbytes / 8);
-    hipLaunchKernelGGL(reorient_kernel<uint2>, dim3(grid(total_bytes / 8)), dim3(256), 0, st,
-                       static_cast<const uint2*>(x), static_cast<uint2*>(y), rows, L, nv, gh, gw,
-                       from, to);
-  } else if (rowbytes % 4 == 0) {
-    const int nv = (int)(rowbytes / 4);
-    hipLaunchKernelGGL(reorient_kernel<uint32_t>, dim3(grid(total_bytes / 4)), dim3(256), 0, st,
-                       static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), rows, L, nv,
-                       gh, gw, from, to);
-  } else {
-    const int nv = (int)(rowbytes / 2);
-    hipLaunchKernelGGL(reorient_kernel<uint16_t>, dim3(grid(total_bytes / 2)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), rows, L, nv,
-                       gh, gw, from, to);
-  }
-  return hipGetLastError();
-}
-
 // -------------------------------------------------------------- depthwise conv
 // One thread owns VW channels of one current-grid column j and walks a strip of rows,
 // keeping a 3x3 window of input vectors in registers (3 new loads per output).
@@ -370,6 +320,116 @@ static GridMap grid_map(int gh, int gw, int layout, int out_layout) {
     default: o0 = L - 1; oi = -1; oj = -gh; break;
   }
   return GridMap{o0 + oi * c0 + oj * d0, oi * cii + oj * dji, oi * cij + oj * djj};
+}
+
+// ------------------------------------------------------------------ reorient
+// Whole token rows move: the row of current position s goes to its position in the target
+// order, the affine map A + Bi i + Bj j of its grid indices (i, j) = (s / cols, s mod cols).
+// One wave per row at a time, the row index and its destination wave-uniform (scalar
+// arithmetic); each lane moves CPR 16-byte pieces of U rows, all loads before the stores.
+// Pieces past the row end and rows past the end repeat the last ones (identical values
+// written twice), so no branch surrounds a load or store.
+template <int CPR>
+__global__ __launch_bounds__(256) void reorient_rows_kernel(const uint4* __restrict__ x,
+                                                            uint4* __restrict__ y, int nrows,
+                                                            int L, int cols, int nv, GridMap m) {
+  constexpr int U = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nw = (int)gridDim.x * 4;
+  for (int r0 = (int)blockIdx.x * 4 + wave; r0 < nrows; r0 += nw * U) {
+    uint4 buf[U][CPR];
+    long dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(r0 + u * nw, nrows - 1);
+      const int b = r / L, s = r - b * L;
+      const int i = s / cols, j = s - i * cols;
+      dst[u] = ((long)b * L + m.A + m.Bi * i + m.Bj * j) * nv;
+      const uint4* src = x + (long)r * nv;
+#pragma unroll
+      for (int c = 0; c < CPR; ++c) buf[u][c] = src[min(lane + 64 * c, nv - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CPR; ++c) y[dst[u] + min(lane + 64 * c, nv - 1)] = buf[u][c];
+  }
+}
+
+// Fallback for rows that are not whole 16-byte pieces or longer than 8 KiB: a grid-stride
+// loop over elements.
+template <typename V>
+__global__ __launch_bounds__(256) void reorient_kernel(const V* __restrict__ x, V* __restrict__ y,
+                                                       long rows, long L, int nv, int gh, int gw,
+                                                       int from, int to) {
+  const long total = rows * nv;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    const long row = i / nv;
+    const int v = (int)(i - row * nv);
+    const long b = row / L, p = row - b * L;
+    const long src = scan_inv(from, scan_pi(to, p, gh, gw, L), gh, gw, L);
+    y[i] = x[(b * L + src) * nv + v];
+  }
+}
+
+hipError_t launch_reorient(int B, int gh, int gw, int D, int elt, int from, int to,
+                           const void* x, void* y, hipStream_t st) {
+  const long L = (long)gh * gw, rows = (long)B * L;
+  const long rowbytes = (long)D * elt;
+  const long total_bytes = rows * rowbytes;
+  long blocks_cap = 256L * 16;
+  auto grid = [&](long items) {
+    long g = (items + 255) / 256;
+    return (unsigned)(g < blocks_cap ? g : blocks_cap);
+  };
+  if (rowbytes % 16 == 0 && rowbytes <= 16 * 64 * 8 && rows < (1L << 31)) {
+    const int nv = (int)(rowbytes / 16), cpr = (nv + 63) / 64;
+    const bool col = from == kCol || from == kColRev;
+    const GridMap m = grid_map(gh, gw, from, to);
+    long g = (rows + 7) / 8;  // 4 waves x 2 rows per block step
+    if (g > blocks_cap) g = blocks_cap;
+#define DIG_REO_CASE(N)                                                                       \
+  case N:                                                                                     \
+    hipLaunchKernelGGL(reorient_rows_kernel<N>, dim3((unsigned)g), dim3(256), 0, st,           \
+                       static_cast<const uint4*>(x), static_cast<uint4*>(y), (int)rows, (int)L, \
+                       col ? gh : gw, nv, m);                                                  \
+    break;
+    switch (cpr) {
+      DIG_REO_CASE(1)
+      DIG_REO_CASE(2)
+      DIG_REO_CASE(3)
+      DIG_REO_CASE(4)
+      DIG_REO_CASE(5)
+      DIG_REO_CASE(6)
+      DIG_REO_CASE(7)
+      DIG_REO_CASE(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef DIG_REO_CASE
+  } else if (rowbytes % 16 == 0) {
+    const int nv = (int)(rowbytes / 16);
+    hipLaunchKernelGGL(reorient_kernel<uint4>, dim3(grid(total_bytes / 16)), dim3(256), 0, st,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(y), rows, L, nv, gh, gw,
+                       from, to);
+  } else if (rowbytes % 8 == 0) {
+    const int nv = (int)(rowbytes / 8);
+    hipLaunchKernelGGL(reorient_kernel<uint2>, dim3(grid(total_bytes / 8)), dim3(256), 0, st,
+                       static_cast<const uint2*>(x), static_cast<uint2*>(y), rows, L, nv, gh, gw,
+                       from, to);
+  } else if (rowbytes % 4 == 0) {
+    const int nv = (int)(rowbytes / 4);
+    hipLaunchKernelGGL(reorient_kernel<uint32_t>, dim3(grid(total_bytes / 4)), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), rows, L, nv,
+                       gh, gw, from, to);
+  } else {
+    const int nv = (int)(rowbytes / 2);
+    hipLaunchKernelGGL(reorient_kernel<uint16_t>, dim3(grid(total_bytes / 2)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), rows, L, nv,
+                       gh, gw, from, to);
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ LDS-tiled conv
