@@ -255,6 +255,11 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   p.seg_lg = reinterpret_cast<float*>(ws + off);
   off += a256(BH * s.nseg * s.dk * sizeof(float));
   p.dgamma_part = reinterpret_cast<float*>(ws + off);
+  off += a256(BH * s.nseg * s.dv * sizeof(float));
+  if (dig::gla_bwd_reuse_bytes(s)) {  // pass A's dO for the final pass
+    p.dofrag = ws + off;
+    p.diagws = reinterpret_cast<float*>(ws + off + dig::gla_bwd_reuse_diag_offset(s));
+  }
   p.g2scale = 1.4426950408889634f / d->tau;
   p.inv_tau = 1.f / d->tau;
   p.q_scale = d->q_scale;

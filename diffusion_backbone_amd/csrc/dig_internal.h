@@ -73,6 +73,8 @@ struct GlaBwdParams {
   float* gstates;       // [B*H][nseg][dk][dv] gradient entering each segment's end
   float* seg_lg;        // [B*H][nseg][dk]
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
+  void* dofrag;         // [B*H][NC] chunks of pass A's dO in fragment order (reuse), or null
+  float* diagws;        // [B*H][NC][2][C] pass A's dO.v diagonals (reuse), or null
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
 };
@@ -82,6 +84,9 @@ int gla_bwd_lds_bytes(const GlaShape& s);
 // Pass B of the three-pass backward: reverse scan of segment gradient states.
 hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipStream_t st);
 size_t gla_bwd_workspace(const GlaShape& s);
+// Bytes of the final pass's reuse buffers (dO fragments, then diagonals), 0 when it recomputes.
+size_t gla_bwd_reuse_bytes(const GlaShape& s);
+size_t gla_bwd_reuse_diag_offset(const GlaShape& s);
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
 // ------------------------------------------------------------------------- misc

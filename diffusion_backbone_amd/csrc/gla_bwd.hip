@@ -34,7 +34,7 @@ size_t gla_bwd_workspace(const GlaShape& s) {
   size_t lg = BH * s.nseg * s.dk * sizeof(float);
   size_t part = BH * s.nseg * s.dv * sizeof(float);
   auto a = [](size_t x) { return (x + 255) / 256 * 256; };
-  return a(g) + a(lg) + a(part);
+  return a(g) + a(lg) + a(part) + gla_bwd_reuse_bytes(s);
 }
 
 // Reverse exclusive scan over segments, in place: slot(p) <- gradient reaching the end of
@@ -105,25 +105,44 @@ hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipS
 
 // Chunk kernels, instantiated per element type in their own translation units.
 template <typename T>
-hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out);
+hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
+                            size_t* ru_out);
 extern template hipError_t launch_gla_bwd_t<bf16>(const GlaShape&, GlaBwdParams, hipStream_t,
-                                                  int*);
+                                                  int*, size_t*);
 extern template hipError_t launch_gla_bwd_t<float>(const GlaShape&, GlaBwdParams, hipStream_t,
-                                                   int*);
+                                                   int*, size_t*);
 
 int gla_bwd_lds_bytes(const GlaShape& s) {
   int bytes = 0;
-  const hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, GlaBwdParams{}, nullptr, &bytes)
-                              : launch_gla_bwd_t<float>(s, GlaBwdParams{}, nullptr, &bytes);
+  const hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, GlaBwdParams{}, nullptr, &bytes, nullptr)
+                              : launch_gla_bwd_t<float>(s, GlaBwdParams{}, nullptr, &bytes, nullptr);
   return e == hipSuccess ? bytes : 0;
+}
+
+static void reuse_sizes(const GlaShape& s, size_t (&b)[2]) {
+  b[0] = b[1] = 0;
+  const hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, GlaBwdParams{}, nullptr, nullptr, b)
+                              : launch_gla_bwd_t<float>(s, GlaBwdParams{}, nullptr, nullptr, b);
+  if (e != hipSuccess) b[0] = b[1] = 0;
+}
+static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+size_t gla_bwd_reuse_bytes(const GlaShape& s) {
+  size_t b[2];
+  reuse_sizes(s, b);
+  return b[0] ? a256(b[0]) + a256(b[1]) : 0;
+}
+size_t gla_bwd_reuse_diag_offset(const GlaShape& s) {
+  size_t b[2];
+  reuse_sizes(s, b);
+  return a256(b[0]);
 }
 
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.bprefix;
-  hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr)
-                        : launch_gla_bwd_t<float>(s, p, st, nullptr);
+  hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr, nullptr)
+                        : launch_gla_bwd_t<float>(s, p, st, nullptr, nullptr);
   if (e != hipSuccess) return e;
   if (p.d_norm_w && s.nseg == 1) {  // with more segments the scan launch reduces dgamma
     const long parts = (long)s.B * s.H * s.nseg;

@@ -45,6 +45,12 @@ constexpr float kBwdSlowDecayLog2 = 96.0f;
 
 constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
 
+// Four elements moved as one vector (a lane's share of one dO fragment row group).
+template <typename T>
+struct alignas(4 * sizeof(T)) Quad {
+  T v[4];
+};
+
 // LDS layout (compile time).  LEAN drops the row-layout copies of dO, S0 and D (their
 // products then read the transposed copies with strided fragments) when the full layout
 // would not fit.  PAD gives the raw staging rows pitches at which the gate pass (one lane
@@ -114,8 +120,29 @@ constexpr bool bwd_prefetch() {
   return EXACT && !(FIN && stw > 1);
 }
 
-template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW>
+// Reuse of pass A's output-stage backward (RU, three-pass calls): pass A stores dO in its
+// register-fragment order (Vec4 per lane, [chunk][wave][value tile][lane]), the rows' exact
+// dO.v diagonal and dr; the final pass then reads dO and the diagonal instead of recomputing
+// o = P V + (q e^b) S0 and the RMSNorm x Swish backward, and reads neither r nor dy.  Needs
+// every wave in the recompute phase (row tiles x value halves = waves).
+template <int C, int NW>
+constexpr int bwd_spl() {
+  return NW >= 2 * (C / 16) ? 2 : 1;
+}
+template <int DK, int DV, bool EXACT, int C, int NW>
+constexpr bool bwd_reuse_ok() {
+  return EXACT && (C / 16) * bwd_spl<C, NW>() == NW;
+}
+template <typename T, int DV, int C, int NW>
+constexpr size_t bwd_reuse_chunk_bytes() {
+  constexpr int NDVH = ((DV + 15) / 16 + bwd_spl<C, NW>() - 1) / bwd_spl<C, NW>();
+  return (size_t)NW * NDVH * 64 * 4 * sizeof(T) + 2 * C * sizeof(float);
+}
+
+template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool RU = false>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
+  static_assert(!RU || bwd_reuse_ok<DK, DV, EXACT, C, NW>(), "reuse needs every wave in the recompute phase");
+  constexpr bool RD = FIN && RU;  // the final pass reads dO (skips the output-stage backward)
   constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW>();
   constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
   using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF>;
@@ -133,6 +160,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
   using Acc = typename std::conditional<kBf, float, double>::type;
+  constexpr int RNDVH = (NDV + bwd_spl<C, NW>() - 1) / bwd_spl<C, NW>();  // reuse fragments
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -208,10 +236,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
                valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
                valid, wave, NW, lane);
-    dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv, rbv,
-               valid, wave, NW, lane);
-    dma_rows_c(base + Lo::R_DY, reinterpret_cast<const unsigned char*>(gdy + row0 * dv), gsv,
-               rbv, valid, wave, NW, lane);
+    if constexpr (!RD) {
+      dma_rows_c(base + Lo::R_R, reinterpret_cast<const unsigned char*>(gr + row0 * dv), gsv,
+                 rbv, valid, wave, NW, lane);
+      dma_rows_c(base + Lo::R_DY, reinterpret_cast<const unsigned char*>(gdy + row0 * dv), gsv,
+                 rbv, valid, wave, NW, lane);
+    }
   };
   // this lane's elements of the fp32 state tiles of chunk n (the saved forward states)
   // (exact shapes: branch-free, padding positions hold clamped copies that are masked where
@@ -270,8 +300,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
     pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
     pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
-    pr.load(reinterpret_cast<const unsigned char*>(gr + row0 * DV), gsv, valid, tid);
-    pdy.load(reinterpret_cast<const unsigned char*>(gdy + row0 * DV), gsv, valid, tid);
+    if constexpr (!RD) {
+      pr.load(reinterpret_cast<const unsigned char*>(gr + row0 * DV), gsv, valid, tid);
+      pdy.load(reinterpret_cast<const unsigned char*>(gdy + row0 * DV), gsv, valid, tid);
+    }
   };
   auto pf_put = [&](int n) {
     unsigned char* base = smem + Lo::O_RAW;
@@ -280,8 +312,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     pk.put(base + Lo::R_K, valid, tid);
     pz.put(base + Lo::R_Z, valid, tid);
     pv.put(base + Lo::R_V, valid, tid);
-    pr.put(base + Lo::R_R, valid, tid);
-    pdy.put(base + Lo::R_DY, valid, tid);
+    if constexpr (!RD) {
+      pr.put(base + Lo::R_R, valid, tid);
+      pdy.put(base + Lo::R_DY, valid, tid);
+    }
   };
   if constexpr (PF) pf_load(n_top - 1);
   else issue(n_top - 1);
@@ -384,8 +418,23 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
     if constexpr (!PF) dma_wait();
     __syncthreads();
+    // the reading final pass: this chunk's dO fragments and diagonal from pass A (consumed in
+    // the recompute phase, after the gate phase has covered their latency)
+    Quad<T> dofr[RD ? RNDVH : 1];
+    float dgw = 0.f;
+    if constexpr (RD) {
+      const Quad<T>* fb = static_cast<const Quad<T>*>(p.dofrag) +
+                          ((sbase + n) * NW + wave) * RNDVH * 64 + lane;
+#pragma unroll
+      for (int Eh = 0; Eh < RNDVH; ++Eh) dofr[Eh] = fb[Eh * 64];
+      dgw = p.diagws[(sbase + n) * 2 * C + min(tid, 2 * C - 1)];
+    }
     f32x4 s0p[STW];  // prefetch S0 of the next chunk down (consumed at the next top)
-    if (n > c_first) {
+    if constexpr (RD) {  // fixed load counts keep the compiler's wait for the loads above exact
+      const int nn = max(n - 1, c_first);
+      if constexpr (PF) pf_load(nn);
+      load_state(nn, s0p);
+    } else if (n > c_first) {
       if constexpr (PF) pf_load(n - 1);
       load_state(n - 1, s0p);
     }
@@ -553,6 +602,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             sPt[(16 * J + 4 * g4 + i) * TP + 16 * I + r16] = from_f<T>(pt[J][i]);
         }
       }
+      if constexpr (!RD) {  // the reading final pass skips o and the output-stage backward
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh) {
         const int E = min(E0 + Eh, NDV - 1);
@@ -645,9 +695,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           for (int i = 0; i < 4; ++i) sXch[hh * C + 16 * I + 4 * g4 + i] = ss[i];
         }
       }
+      }  // !RD
     }
-    if constexpr (SPL > 1) __syncthreads();  // row sums of both halves
-    if (part) {
+    if constexpr (SPL > 1 && !RD) __syncthreads();  // row sums of both halves
+    if (part && !RD) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float tot = ss[i];
@@ -679,7 +730,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
               for (int k = 0; k < NDV; ++k)
                 if (k == E) dgam[k] += dyv * nv * sw;
             }
-            if (own) sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
+            if (own || RU) sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
           }
           dn[Eh][i] = dyv * gmE * sw;
           md[i] += dn[Eh][i] * nv;
@@ -694,8 +745,24 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         }
       }
     }
-    if constexpr (SPL > 1) __syncthreads();  // dn.o row sums of both halves
-    if (part) {
+    if constexpr (SPL > 1 && !RD) __syncthreads();  // dn.o row sums of both halves
+    if (part && RD) {
+      // dO and the dO.v diagonal as pass A formed them
+#pragma unroll
+      for (int Eh = 0; Eh < NDVH; ++Eh) {
+        if (E0 + Eh < NDV) {
+          const int e = (E0 + Eh) * 16 + r16;
+          T dov4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dov4[i] = dofr[Eh].v[i];
+            if constexpr (!LEAN) sdO[(16 * I + 4 * g4 + i) * VP + e] = dov4[i];
+          }
+          lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
+        }
+      }
+      if (tid < 2 * C) sDiag[tid] = dgw;
+    } else if (part) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float tot = md[i];
@@ -706,8 +773,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         md[i] = tot / (float)dv;
       }
       Acc dvd[4] = {0, 0, 0, 0};
+      Quad<T> dof[NDVH];  // pass A with reuse: dO in fragment order for the final pass
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dof[Eh].v[i] = from_f<T>(0.f);
         if (E0 + Eh < NDV) {
           const int e = (E0 + Eh) * 16 + r16;
           T dov4[4];
@@ -717,11 +787,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             const float dov =
                 (FULLV || e < dv) ? rstd[i] * (dn[Eh][i] - oacc[Eh][i] * md[i]) : 0.f;
             dov4[i] = from_f<T>(dov);
+            dof[Eh].v[i] = dov4[i];
             if constexpr (!LEAN) sdO[row * VP + e] = dov4[i];
             dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
           }
           lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
         }
+      }
+      if constexpr (RU && !FIN) {
+        Quad<T>* fb = static_cast<Quad<T>*>(p.dofrag) + ((sbase + n) * NW + wave) * NDVH * 64 + lane;
+#pragma unroll
+        for (int Eh = 0; Eh < NDVH; ++Eh) fb[Eh * 64] = dof[Eh];
       }
       // do_i is orthogonal to the normalised o_i (up to eps); when o_i is parallel to v_i
       // (the first token) do_i.v_i cancels, so it is formed here from the fp32 do_i; the
@@ -733,10 +809,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         dd += __shfl_xor(dd, 2);
         dd += __shfl_xor(dd, 4);
         dd += __shfl_xor(dd, 8);
-        if (own && r16 == 0) sDiag[hh * C + 16 * I + 4 * g4 + i] = (float)dd;
+        if ((own || RU) && r16 == 0) sDiag[hh * C + 16 * I + 4 * g4 + i] = (float)dd;
       }
     }
     __syncthreads();
+    if constexpr (RU && !FIN) {
+      if (tid < 2 * C) p.diagws[(sbase + n) * 2 * C + tid] = sDiag[tid];
+    }
 
     if (own) {
       // ---- D = dO V^T (causal, row and transposed) and the dlog(alpha) boundary term
@@ -863,6 +942,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
     __syncthreads();
+    if constexpr (RU && !FIN) {  // pass A emits dr (the reading final pass has no r)
+      T* gdr = static_cast<T*>(p.dr);
+      if constexpr (PF) {
+        constexpr int RV = DV * (int)sizeof(T), LV = VPE * (int)sizeof(T);
+        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<unsigned char*>(gdr + row0 * DV),
+                                         (long)H * RV, reinterpret_cast<const unsigned char*>(sRr),
+                                         valid, tid);
+      } else {
+        store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, NTH);
+      }
+    }
 
     if (own) {
       // ---- dlog(alpha) = suffix sums of q.dq - k.dk (lanes = tokens in reverse order, DPP
@@ -915,14 +1005,15 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
                                          reinterpret_cast<const UC*>(rawz), valid, tid);
         store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
                                          reinterpret_cast<const UC*>(sDy), valid, tid);
-        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
-                                         reinterpret_cast<const UC*>(sRr), valid, tid);
+        if constexpr (!RD)
+          store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
+                                           reinterpret_cast<const UC*>(sRr), valid, tid);
       } else {
         store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, NTH);
         store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, NTH);
         store_rows<T>(gdz + row0 * dk, (long)H * dk, rawz, dk, valid, dk, tid, NTH);
         store_rows<T>(gdv + row0 * dv, (long)H * dv, sDy, dv, valid, dv, tid, NTH);
-        store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, NTH);
+        if constexpr (!RD) store_rows<T>(gdr + row0 * dv, (long)H * dv, sRr, dv, valid, dv, tid, NTH);
       }
     }
     // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
@@ -981,9 +1072,17 @@ constexpr int bwd_waves() {
 }
 
 template <typename T, int DK, int DV, bool EXACT, int C>
-static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
+static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
+                               size_t* ru_out) {
   const long BH = (long)s.B * s.H;
   constexpr int NW = bwd_waves<T, DK, DV, EXACT>();
+  constexpr bool RU = bwd_reuse_ok<DK, DV, EXACT, C, NW>();
+  const bool three = !s.bprefix && s.nseg > 1;
+  if (ru_out) {  // reuse buffers: dO fragments of every chunk, then the diagonals
+    ru_out[0] = RU && three ? (size_t)BH * s.NC * (bwd_reuse_chunk_bytes<T, DV, C, NW>() - 2 * C * sizeof(float)) : 0;
+    ru_out[1] = RU && three ? (size_t)BH * s.NC * 2 * C * sizeof(float) : 0;
+    return hipSuccess;
+  }
   constexpr bool PF_FIN = bwd_prefetch<DK, DV, EXACT, true, NW>();
   constexpr bool PF_A = bwd_prefetch<DK, DV, EXACT, false, NW>();
   constexpr int fin_bytes =
@@ -994,11 +1093,22 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
     *lds_out = fin_bytes;
     return hipSuccess;
   }
-  if (!s.bprefix && s.nseg > 1) {
-    hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW>),
-                       dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
+  if (three) {
+    if constexpr (RU) {
+      if (!p.dofrag || !p.diagws) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW, true>),
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
+    } else {
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW>),
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
+    }
     const hipError_t e = launch_gla_gstate_scan(s, p, st);
     if (e != hipSuccess) return e;
+    if constexpr (RU) {
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, true>),
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW>),
                      dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
@@ -1007,26 +1117,28 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
 
 template <typename T, int DK, int DV, bool EXACT>
 static hipError_t launch_bwd_dims(const GlaShape& s, GlaBwdParams p, hipStream_t st,
-                                  int* lds_out) {
+                                  int* lds_out, size_t* ru_out) {
   switch (s.C) {
-    case 16: return launch_bwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out);
-    case 32: return launch_bwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out);
-    case 64: return launch_bwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out);
+    case 16: return launch_bwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out, ru_out);
+    case 32: return launch_bwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out, ru_out);
+    case 64: return launch_bwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out, ru_out);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Same shape dispatch as the forward; lds_out != nullptr: only report the final pass's LDS.
+// Same shape dispatch as the forward.  Queries: lds_out != nullptr reports the final pass's
+// LDS bytes, ru_out != nullptr the reuse buffers' bytes ({dO fragments, diagonals}).
 template <typename T>
-hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out) {
-  if (s.dk == 32 && s.dv == 64) return launch_bwd_dims<T, 32, 64, true>(s, p, st, lds_out);
-  if (s.dk == 36 && s.dv == 72) return launch_bwd_dims<T, 36, 72, true>(s, p, st, lds_out);
-  if (s.dk == 16 && s.dv == 32) return launch_bwd_dims<T, 16, 32, true>(s, p, st, lds_out);
+hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
+                            size_t* ru_out) {
+  if (s.dk == 32 && s.dv == 64) return launch_bwd_dims<T, 32, 64, true>(s, p, st, lds_out, ru_out);
+  if (s.dk == 36 && s.dv == 72) return launch_bwd_dims<T, 36, 72, true>(s, p, st, lds_out, ru_out);
+  if (s.dk == 16 && s.dv == 32) return launch_bwd_dims<T, 16, 32, true>(s, p, st, lds_out, ru_out);
   switch (s.ndk * 16 + s.ndv) {
-    case 1 * 16 + 2: return launch_bwd_dims<T, 16, 32, false>(s, p, st, lds_out);
-    case 2 * 16 + 4: return launch_bwd_dims<T, 32, 64, false>(s, p, st, lds_out);
-    case 3 * 16 + 5: return launch_bwd_dims<T, 48, 80, false>(s, p, st, lds_out);
-    case 4 * 16 + 8: return launch_bwd_dims<T, 64, 128, false>(s, p, st, lds_out);
+    case 1 * 16 + 2: return launch_bwd_dims<T, 16, 32, false>(s, p, st, lds_out, ru_out);
+    case 2 * 16 + 4: return launch_bwd_dims<T, 32, 64, false>(s, p, st, lds_out, ru_out);
+    case 3 * 16 + 5: return launch_bwd_dims<T, 48, 80, false>(s, p, st, lds_out, ru_out);
+    case 4 * 16 + 8: return launch_bwd_dims<T, 64, 128, false>(s, p, st, lds_out, ru_out);
     default: return hipErrorInvalidValue;
   }
 }
