@@ -111,13 +111,14 @@ constexpr bool bwd_lean() {
   return BwdLayout<T, DK, DV, C, FIN, false, NW, PAD>::bytes > kBwdLdsBudget;
 }
 
-// Register prefetch of the next chunk's raw rows (exact head shapes).  The final pass drops it
-// when a wave holds more than one state tile: those registers then go to the tiles (with the
-// prefetch the compiler spills inside the chunk loop).
-template <int DK, int DV, bool EXACT, bool FIN, int NW>
+// Register prefetch of the next chunk's raw rows (exact head shapes).  The recomputing final
+// pass drops it when a wave holds more than one state tile: those registers then go to the
+// tiles (with the prefetch the compiler spills inside the chunk loop).  The final pass that
+// reads pass A's dO (RD) has the registers to keep it.
+template <int DK, int DV, bool EXACT, bool FIN, int NW, bool RD = false>
 constexpr bool bwd_prefetch() {
   constexpr int stw = ((DK + 15) / 16 * ((DV + 15) / 16) + NW - 1) / NW;
-  return EXACT && !(FIN && stw > 1);
+  return EXACT && !(FIN && !RD && stw > 1);
 }
 
 // Reuse of pass A's output-stage backward (RU, three-pass calls): pass A stores dO in its
@@ -143,7 +144,7 @@ template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool 
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   static_assert(!RU || bwd_reuse_ok<DK, DV, EXACT, C, NW>(), "reuse needs every wave in the recompute phase");
   constexpr bool RD = FIN && RU;  // the final pass reads dO (skips the output-stage backward)
-  constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW>();
+  constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW, RD>();
   constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
   using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF>;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE, DKB = Lo::DKB;
@@ -1084,13 +1085,16 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
     return hipSuccess;
   }
   constexpr bool PF_FIN = bwd_prefetch<DK, DV, EXACT, true, NW>();
+  constexpr bool PF_RD = bwd_prefetch<DK, DV, EXACT, true, NW, true>();
   constexpr bool PF_A = bwd_prefetch<DK, DV, EXACT, false, NW>();
   constexpr int fin_bytes =
       BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_FIN>(), NW, PF_FIN>::bytes;
+  constexpr int rd_bytes =
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_RD>(), NW, PF_RD>::bytes;
   constexpr int a_bytes =
       BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, PF_A>(), NW, PF_A>::bytes;
   if (lds_out) {
-    *lds_out = fin_bytes;
+    *lds_out = RU && three && rd_bytes > fin_bytes ? rd_bytes : fin_bytes;
     return hipSuccess;
   }
   if (three) {
@@ -1106,7 +1110,7 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
     if (e != hipSuccess) return e;
     if constexpr (RU) {
       hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, true>),
-                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), rd_bytes, st, p);
       return hipGetLastError();
     }
   }
