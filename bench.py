@@ -175,10 +175,10 @@ class EventTimer:
 TRAFFIC = {
     "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    # FETCH_SIZE 13204.1 KiB / 0.50017 (copy: 131117.6 KiB read per 262144 KiB moved) +
-    # WRITE_SIZE 8522.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-    "bytes": 35759120,
-    "sources_sha256": "98b82adb408fcf944dcba2ff2e57777f8231d56266aea9f155d02163b277b15e",
+    # FETCH_SIZE 12467.8 KiB / 0.50006 (copy: 131088.3 KiB read per 262144 KiB moved) +
+    # WRITE_SIZE 10154.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
+    "bytes": 35928476,
+    "sources_sha256": "5b632107880f6485b4183885e2418f66f2829babf4662e00f7984d8d2e7a170e",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
