@@ -41,18 +41,6 @@ struct __attribute__((aligned(VW * sizeof(T)))) Vec {
   T v[VW];
 };
 
-// Vector access at a wave-uniform base plus a per-lane 32-bit byte offset: the address form
-// global memory instructions take directly (base in scalar registers, offset in one vector
-// register), so an access costs no per-lane 64-bit address arithmetic.
-template <typename V>
-__device__ __forceinline__ V ld_at(const void* base, unsigned off) {
-  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + off);
-}
-template <typename V>
-__device__ __forceinline__ void st_at(void* base, unsigned off, const V& v) {
-  *reinterpret_cast<V*>(static_cast<char*>(base) + off) = v;
-}
-
 // Buffer-resource access: a per-image resource (base, byte size) in scalar registers, the
 // lane's byte offset in one vector register and a uniform byte offset (a row) in a scalar
 // register, so stepping to the next row costs no vector instruction.  Every access here lies
