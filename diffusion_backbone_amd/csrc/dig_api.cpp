@@ -144,7 +144,7 @@ int32_t dig_abi_version(void) { return 100; }
 size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;
   if (check_desc(d, &s, kFwd) != DIG_OK) return 0;
-  return dig::gla_states_bytes(s);
+  return dig::gla_saved_bytes(s);
 }
 
 size_t dig_gla_fwd_workspace_bytes(const dig_gla_desc* d) {
@@ -185,7 +185,7 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
                       rng("gate_logit", gate_logit, bk), rng("r", r, bv),
                       rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0)};
   const Range out[] = {rng("y", y, bv), rng("o_pre", o_pre_opt, o_pre_opt ? bv : 0),
-                       rng("saved", saved_opt, saved_opt ? sb : 0),
+                       rng("saved", saved_opt, saved_opt ? dig::gla_saved_bytes(s) : 0),
                        rng("workspace", workspace, workspace ? need : 0)};
   st = check_alias(in, 6, out, 4);
   if (st != DIG_OK) return st;
@@ -195,6 +195,10 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
   p.y = y; p.o_pre = o_pre_opt;
   char* ws = static_cast<char*>(workspace);
   p.states = saved_opt ? static_cast<float*>(saved_opt) : reinterpret_cast<float*>(ws);
+  if (saved_opt) {
+    p.obar = static_cast<char*>(saved_opt) + dig::gla_saved_obar_offset(s);
+    p.rstd = reinterpret_cast<float*>(static_cast<char*>(saved_opt) + dig::gla_saved_rstd_offset(s));
+  }
   p.seg_lg = reinterpret_cast<float*>(ws + a256(sb));
   p.write_states = saved_opt != nullptr;
   p.g2scale = 1.4426950408889634f / d->tau;
@@ -236,7 +240,7 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
                       rng("gate_logit", gate_logit, bk), rng("r", r, bv),
                       rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0), rng("dy", dy, bv),
-                      rng("saved", saved, dig::gla_states_bytes(s))};
+                      rng("saved", saved, dig::gla_saved_bytes(s))};
   const Range out[] = {rng("dq", dq, bk), rng("dk", dk, bk), rng("dv", dv, bv),
                        rng("d_gate_logit", d_gate_logit, bk), rng("dr", dr, bv),
                        rng("d_norm_w", d_norm_w, d_norm_w ? d->d_v * 4 : 0),
@@ -249,6 +253,9 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   dig::GlaBwdParams p{};
   p.q = q; p.k = k; p.v = v; p.z = gate_logit; p.r = r; p.norm_w = norm_w; p.dy = dy;
   p.states = static_cast<const float*>(saved);
+  p.obar = static_cast<const char*>(saved) + dig::gla_saved_obar_offset(s);
+  p.rstd = reinterpret_cast<const float*>(static_cast<const char*>(saved) +
+                                          dig::gla_saved_rstd_offset(s));
   p.dq = dq; p.dk_ = dk; p.dv_ = dv; p.dz = d_gate_logit; p.dr = dr; p.d_norm_w = d_norm_w;
   p.gstates = reinterpret_cast<float*>(ws);
   size_t off = a256(BH * s.nseg * s.dk * s.dv * sizeof(float));

@@ -196,6 +196,12 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Four elements moved as one vector: a lane's four rows of one 16 x 16 MFMA result tile.
+template <typename T>
+struct alignas(4 * sizeof(T)) Quad {
+  T v[4];
+};
+
 // ---------------------------------------------------- DPP (register-only) lane ops
 // gfx9 data-parallel primitives: row_shr:k = 0x110+k, row_ror:k = 0x120+k, row_bcast:15 =
 // 0x142, row_bcast:31 = 0x143 (a "row" is 16 lanes).  Lanes whose source is outside the row,

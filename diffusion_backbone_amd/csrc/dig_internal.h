@@ -35,6 +35,8 @@ struct GlaFwdParams {
   void* o_pre;
   float* states;   // [B*H][NC][dk][dv] fp32: state entering each chunk
   float* seg_lg;   // [B*H][nseg][dk] fp32: log2 of each segment's total decay
+  void* obar;      // saved for the backward, or null: normalised o in fragment order
+  float* rstd;     // saved for the backward, or null: [B*H][NC][C] RMSNorm reciprocal rms
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale;   // log2(e) / tau
   float q_scale, eps;
@@ -46,6 +48,12 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
 // LDS bytes of the forward's output pass for this shape (0 if no kernel exists for it).
 int gla_fwd_lds_bytes(const GlaShape& s);
 size_t gla_states_bytes(const GlaShape& s);
+// The forward->backward buffer: chunk states, then the normalised output ō of every token
+// (bf16/fp32 as the I/O, [B*H][NC][C/16][NDV] 16 x 16 tiles in MFMA fragment order, NDV =
+// ceil(d_v/16)), then the rows' rsqrt(mean o^2 + eps) (fp32 [B*H][NC][C]); offsets 256-aligned.
+size_t gla_saved_bytes(const GlaShape& s);
+size_t gla_saved_obar_offset(const GlaShape& s);
+size_t gla_saved_rstd_offset(const GlaShape& s);
 size_t gla_seglg_bytes(const GlaShape& s);
 
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st);
@@ -64,6 +72,8 @@ struct GlaBwdParams {
   const float* norm_w;
   const void* dy;
   const float* states;  // forward's chunk-entry states [B*H][NC][dk][dv]
+  const void* obar;     // forward's normalised output, fragment order (see gla_saved_bytes)
+  const float* rstd;    // forward's per-row rsqrt(mean o^2 + eps) [B*H][NC][C]
   void* dq;
   void* dk_;
   void* dv_;

@@ -45,11 +45,6 @@ constexpr float kBwdSlowDecayLog2 = 96.0f;
 
 constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
 
-// Four elements moved as one vector (a lane's share of one dO fragment row group).
-template <typename T>
-struct alignas(4 * sizeof(T)) Quad {
-  T v[4];
-};
 
 // LDS layout (compile time).  LEAN drops the row-layout copies of dO, S0 and D (their
 // products then read the transposed copies with strided fragments) when the full layout
@@ -423,6 +418,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // the recompute phase, after the gate phase has covered their latency)
     Quad<T> dofr[RD ? RNDVH : 1];
     float dgw = 0.f;
+    // the passes that form dO: this chunk's normalised output o rstd and rstd as the forward
+    // saved them (the recompute phase's row tile I, value tiles E0.. of half hh)
+    Quad<T> obr[RD ? 1 : RNDVH];
+    float4 rsv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (!RD) {
+      const int I = wave % NT, E0 = (wave / NT) * RNDVH;
+      const Quad<T>* ob = static_cast<const Quad<T>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane;
+#pragma unroll
+      for (int Eh = 0; Eh < RNDVH; ++Eh) obr[Eh] = ob[min(E0 + Eh, NDV - 1) * 64];
+      rsv = *reinterpret_cast<const float4*>(p.rstd + (sbase + n) * C + 16 * I + 4 * g4);
+    }
     if constexpr (RD) {
       const Quad<T>* fb = static_cast<const Quad<T>*>(p.dofrag) +
                           ((sbase + n) * NW + wave) * RNDVH * 64 + lane;
@@ -538,7 +544,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     T rr[NDVH][4], dyr[NDVH][4];
     float ss[4] = {0.f, 0.f, 0.f, 0.f}, md[4] = {0.f, 0.f, 0.f, 0.f}, rstd[4];
     float dn[NDVH][4];
-    if (slow) {  // strong decay: P rows elementwise, one copy per row tile (uniform branch)
+    if (FIN && slow) {  // strong decay: P rows elementwise, one copy per row tile (uniform branch)
       if (part && hh == 0) {
         T* sPw = sSlow + I * 16 * C;
         for (int idx = lane; idx < 16 * C; idx += 64) {
@@ -557,6 +563,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       __syncthreads();
     }
     if (part) {
+      if constexpr (FIN) {  // P (for dv) in the final pass only
       float diag;  // exact q_i.k_i from the unscaled inputs (gate factor 1)
       {
         constexpr int DQ = DKP / 4;
@@ -603,74 +610,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             sPt[(16 * J + 4 * g4 + i) * TP + 16 * I + r16] = from_f<T>(pt[J][i]);
         }
       }
-      if constexpr (!RD) {  // the reading final pass skips o and the output-stage backward
+      }  // FIN
+      if constexpr (!RD) {  // the reading final pass skips the output-stage backward
+      // o rstd as the forward saved it (its rows are the rows of this tile)
 #pragma unroll
-      for (int Eh = 0; Eh < NDVH; ++Eh) {
-        const int E = min(E0 + Eh, NDV - 1);
-        oacc[Eh] = Mma<T>::kc(zero4(), sQ, QP, 16 * I, sS0t, QP, 16 * E, DKP, lane);
-      }
-      if constexpr (kBf) {
+      for (int Eh = 0; Eh < NDVH; ++Eh)
 #pragma unroll
-        for (int pp = 0; pp < NT / 2; ++pp) {  // token tiles in pairs: one K = 32 step
-          if (2 * pp <= I) {
-            const bool hi_on = 2 * pp + 1 <= I;
-            bf16x8 a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              a[i] = from_f<bf16>(pt[2 * pp][i]);
-              a[4 + i] = from_f<bf16>(hi_on ? pt[2 * pp + 1][i] : 0.f);
-            }
-#pragma unroll
-            for (int Eh = 0; Eh < NDVH; ++Eh) {
-              const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
-              bf16x8 bv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                bv[i] = sV[(32 * pp + 4 * g4 + i) * VP + e];
-                bv[4 + i] = sV[(32 * pp + 16 + 4 * g4 + i) * VP + e];
-              }
-              oacc[Eh] = mfma_bf16(a, bv, oacc[Eh]);
-            }
-          }
-        }
-        if constexpr (NT % 2 == 1) {  // last token tile alone: half-filled K = 32 step
-          constexpr int J = NT - 1;
-          if (J <= I) {
-            bf16x8 a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              a[i] = from_f<bf16>(pt[J][i]);
-              a[4 + i] = from_f<bf16>(0.f);
-            }
-#pragma unroll
-            for (int Eh = 0; Eh < NDVH; ++Eh) {
-              const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
-              bf16x8 bv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                bv[i] = sV[(16 * J + 4 * g4 + i) * VP + e];
-                bv[4 + i] = from_f<bf16>(0.f);
-              }
-              oacc[Eh] = mfma_bf16(a, bv, oacc[Eh]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int J = 0; J < NT; ++J) {
-          if (J <= I) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-              for (int Eh = 0; Eh < NDVH; ++Eh) {
-                const int e = min(E0 + Eh, NDV - 1) * 16 + r16;
-                const float bv = to_f(sV[(16 * J + 4 * g4 + s4) * VP + e]);
-                oacc[Eh] = mfma_f32(pt[J][s4], bv, oacc[Eh]);
-              }
-            }
-          }
-        }
-      }
+        for (int i = 0; i < 4; ++i) oacc[Eh][i] = to_f(obr[Eh].v[i]);
 
       // output-stage backward: r, dy first (one LDS round trip); value tiles past this
       // half's range (an odd tile count) count as zero columns
@@ -684,32 +630,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           dyr[Eh][i] = on ? sDy[row * vp + e] : from_f<T>(0.f);
           if (E0 + Eh >= NDV) oacc[Eh][i] = 0.f;
         }
-#pragma unroll
-      for (int Eh = 0; Eh < NDVH; ++Eh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ss[i] += oacc[Eh][i] * oacc[Eh][i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss[i] = row_sum16(ss[i]);
-      if constexpr (SPL > 1) {
-        if (r16 == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sXch[hh * C + 16 * I + 4 * g4 + i] = ss[i];
-        }
-      }
       }  // !RD
     }
-    if constexpr (SPL > 1 && !RD) __syncthreads();  // row sums of both halves
     if (part && !RD) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float tot = ss[i];
-        if constexpr (SPL > 1) {
-          const int row = 16 * I + 4 * g4 + i;
-          tot = sXch[row] + sXch[C + row];
-        }
-        rstd[i] = rsqrtf(tot / (float)dv + p.eps);
-      }
-      // oacc becomes the normalised output, dn = dy * w * swish(r)
+      rstd[0] = rsv.x; rstd[1] = rsv.y; rstd[2] = rsv.z; rstd[3] = rsv.w;
+      // oacc is the normalised output, dn = dy * w * swish(r)
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh) {
         const int E = min(E0 + Eh, NDV - 1), e = (E0 + Eh) * 16 + r16;
@@ -719,7 +644,6 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         for (int k = 1; k < NDV; ++k) gmE = k == E ? gm[k] : gmE;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          oacc[Eh][i] *= rstd[i];
           const int row = 16 * I + 4 * g4 + i;
           const float nv = oacc[Eh][i], rv = to_f(rr[Eh][i]), dyv = to_f(dyr[Eh][i]);
           const float sg = Fm<T>::sig(rv), sw = rv * sg;

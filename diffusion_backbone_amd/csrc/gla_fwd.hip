@@ -66,6 +66,15 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
 size_t gla_states_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.NC * s.dk * s.dv * sizeof(float);
 }
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+size_t gla_saved_obar_offset(const GlaShape& s) { return al256(gla_states_bytes(s)); }
+size_t gla_saved_rstd_offset(const GlaShape& s) {
+  const size_t ob = (size_t)s.B * s.H * s.NC * s.C * 16 * s.ndv * (s.bf16 ? 2 : 4);
+  return gla_saved_obar_offset(s) + al256(ob);
+}
+size_t gla_saved_bytes(const GlaShape& s) {
+  return gla_saved_rstd_offset(s) + al256((size_t)s.B * s.H * s.NC * s.C * sizeof(float));
+}
 size_t gla_seglg_bytes(const GlaShape& s) {
   return (size_t)s.B * s.H * s.nseg * s.dk * sizeof(float);
 }

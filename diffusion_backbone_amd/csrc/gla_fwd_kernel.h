@@ -526,23 +526,31 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       float rstd[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) / (float)dv + p.eps);
+      // y, and for the backward (when saved) o rstd in fragment order and rstd per row
+      Quad<T>* ob = p.obar ? static_cast<Quad<T>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane
+                           : nullptr;
 #pragma unroll
       for (int E = 0; E < NDV; ++E) {
         const int e = E * 16 + r16;
-        if (FULLV || e < dv) {
+        Quad<T> q4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * I + 4 * g4 + i;
-            const float o = oacc[E][i];
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * I + 4 * g4 + i;
+          const float o = oacc[E][i];
+          const float nv = o * rstd[i];
+          q4.v[i] = from_f<T>(nv);
+          if ((FULLV || e < dv) && row < valid) {
             const float rv = to_f(rr[E][i]);
-            if (row < valid) {
-              const long off = (row0 + (long)row * H) * dv + e;
-              if (gop) gop[off] = from_f<T>(o);
-              gy[off] = from_f<T>(o * rstd[i] * gm[E] * rv * Fm<T>::sig(rv));
-            }
+            const long off = (row0 + (long)row * H) * dv + e;
+            if (gop) gop[off] = from_f<T>(o);
+            gy[off] = from_f<T>(nv * gm[E] * rv * Fm<T>::sig(rv));
           }
         }
+        if (ob) ob[E * 64] = q4;
       }
+      if (ob && r16 == 0)
+        *reinterpret_cast<float4*>(p.rstd + (sbase + n) * C + 16 * I + 4 * g4) =
+            make_float4(rstd[0], rstd[1], rstd[2], rstd[3]);
     }
     __syncthreads();  // every read of the staging slot and of S^T is done
   }
