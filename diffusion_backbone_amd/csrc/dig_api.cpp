@@ -267,6 +267,7 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
     p.dofrag = ws + off;
     p.diagws = reinterpret_cast<float*>(ws + off + dig::gla_bwd_reuse_diag_offset(s));
   }
+  if (s.lookback) p.lb_flag = reinterpret_cast<unsigned*>(ws + dig::gla_bwd_flag_offset(s));
   p.g2scale = 1.4426950408889634f / d->tau;
   p.inv_tau = 1.f / d->tau;
   p.q_scale = d->q_scale;

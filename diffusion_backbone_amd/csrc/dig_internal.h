@@ -17,6 +17,7 @@ struct GlaShape {
   int nseg;                 // segments per sequence = ceil(NC / sc)
   int prefix;               // forward: 1 = each segment recomputes its incoming state
   int bprefix;              // backward: the same choice (its recompute is costlier)
+  int lookback;             // backward: one chunk per workgroup, G via a look-back (1 launch)
   int ndk, ndv;             // compiled head-dim class: d_k <= 16*ndk, d_v <= 16*ndv
 };
 
@@ -85,6 +86,8 @@ struct GlaBwdParams {
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
   void* dofrag;         // [B*H][NC] chunks of pass A's dO in fragment order (reuse), or null
   float* diagws;        // [B*H][NC][2][C] pass A's dO.v diagonals (reuse), or null
+  unsigned* lb_flag;    // [B*H][nseg] look-back: segment published (== lb_tag)
+  unsigned lb_tag;      // this call's flag value (differs from every earlier call's)
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
 };
@@ -97,6 +100,8 @@ size_t gla_bwd_workspace(const GlaShape& s);
 // Bytes of the final pass's reuse buffers (dO fragments, then diagonals), 0 when it recomputes.
 size_t gla_bwd_reuse_bytes(const GlaShape& s);
 size_t gla_bwd_reuse_diag_offset(const GlaShape& s);
+// Offset of the look-back flags in the workspace ([B*H][nseg] unsigned).
+size_t gla_bwd_flag_offset(const GlaShape& s);
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
 // ------------------------------------------------------------------------- misc

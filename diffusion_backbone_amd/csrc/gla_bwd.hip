@@ -16,10 +16,14 @@
 //   dv_j = sum_{i>=j} P_ij do_i + (k_j e^{b_last-b_j}) G
 //   dlog(alpha_u) = sum_{t>=u in chunk} (q.dq - k.dk)_t + sum_e (S_end (.) G)[:, e]
 //   G_prev = diag(e^{b_last}) G + sum_i (q_i e^{b_i})^T do_i
-// The last identity carries G backwards.  A segment's incoming G comes either from
-// recomputing it over all later chunks in the same workgroup (short sequences), or from
-// pass A (per-segment local G from zero) + a reverse scan over segments.  The output-stage
-// backward (head-wise RMSNorm x weight x Swish) recomputes o from the saved S0.
+// The last identity carries G backwards.  A segment's incoming G comes from one of:
+//  - the look-back (short sequences, one chunk per workgroup, one launch): each workgroup
+//    publishes its chunk's (q e^b)^T dO and decay and sums the later chunks' ones;
+//  - one segment per sequence (the workgroup walks every chunk itself);
+//  - pass A (per-segment local G from zero) + a reverse scan over segments + the final pass.
+// The output-stage backward (head-wise RMSNorm x weight x Swish) starts from the normalised
+// output o rstd and rstd that the forward saved.
+#include <atomic>
 #include <type_traits>
 
 #include "dig_device.h"
@@ -34,7 +38,14 @@ size_t gla_bwd_workspace(const GlaShape& s) {
   size_t lg = BH * s.nseg * s.dk * sizeof(float);
   size_t part = BH * s.nseg * s.dv * sizeof(float);
   auto a = [](size_t x) { return (x + 255) / 256 * 256; };
-  return a(g) + a(lg) + a(part) + gla_bwd_reuse_bytes(s);
+  return a(g) + a(lg) + a(part) + gla_bwd_reuse_bytes(s) +
+         (s.lookback ? a(BH * s.nseg * sizeof(unsigned)) : 0);
+}
+size_t gla_bwd_flag_offset(const GlaShape& s) {
+  const size_t BH = (size_t)s.B * s.H;
+  auto a = [](size_t x) { return (x + 255) / 256 * 256; };
+  return a(BH * s.nseg * s.dk * s.dv * sizeof(float)) + a(BH * s.nseg * s.dk * sizeof(float)) +
+         a(BH * s.nseg * s.dv * sizeof(float)) + gla_bwd_reuse_bytes(s);
 }
 
 // Reverse exclusive scan over segments, in place: slot(p) <- gradient reaching the end of
@@ -137,8 +148,17 @@ size_t gla_bwd_reuse_diag_offset(const GlaShape& s) {
   return a256(b[0]);
 }
 
+// Look-back flag values: a fresh one per call (a bijective hash of a call counter), so that
+// flags left in a reused workspace by earlier calls never match.
+static unsigned next_lb_tag() {
+  static std::atomic<unsigned> calls{0};
+  const unsigned t = (calls.fetch_add(1, std::memory_order_relaxed) + 1u) * 0x9E3779B1u;
+  return t ? t : 1u;
+}
+
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
+  p.lb_tag = next_lb_tag();
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.bprefix;
   hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr, nullptr)

@@ -135,9 +135,45 @@ constexpr size_t bwd_reuse_chunk_bytes() {
   return (size_t)NW * NDVH * 64 * 4 * sizeof(T) + 2 * C * sizeof(float);
 }
 
-template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool RU = false>
+// Look-back (LB, short sequences, one chunk per workgroup, one launch): each workgroup
+// publishes its chunk's own contribution to the gradient state, U = (q e^b)^T dO, with the
+// chunk's log2 decay and its dgamma partial, then raises its flag; the gradient reaching its
+// chunk's end is the decayed sum of the later chunks' U:
+//   G(n) = U(n+1) + diag(e^{b_last(n+1)}) U(n+2) + diag(e^{b_last(n+1) + b_last(n+2)}) U(n+3) ...
+// Later chunks get lower workgroup indices, so every workgroup waited on was dispatched
+// before the waiter (in-order dispatch): the waits cannot deadlock.  The last workgroup
+// reduces the dgamma partials in a fixed order once every flag is up.  Flags hold this
+// call's tag, so values left by earlier calls never match; each wait is bounded.
+// Every exchanged value goes through device-scope loads and stores, which the L2 of each
+// XCD does not hold back; the stores have completed (waited for) before the flag is
+// written, and the values are loaded only after the flag is seen.  No L2 write-back or
+// invalidation is needed (fences would do both, over the whole L2, per wave).
+constexpr unsigned kLbSpinLimit = 1u << 18;  // polls of at least ~1 us: a bound far past any real wait
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).
+__device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, unsigned tag,
+                                            int lane) {
+  if (lane < count) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(const_cast<unsigned*>(flags + lane), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
+           ++spins < kLbSpinLimit)
+      __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool RU = false,
+          bool LB = false>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   static_assert(!RU || bwd_reuse_ok<DK, DV, EXACT, C, NW>(), "reuse needs every wave in the recompute phase");
+  static_assert(!LB || (FIN && !RU), "the look-back runs the recomputing final pass");
   constexpr bool RD = FIN && RU;  // the final pass reads dO (skips the output-stage backward)
   constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW, RD>();
   constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
@@ -163,9 +199,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   const int r16 = lane & 15, g4 = lane >> 4;
   // pass A covers every segment: segment 0's G is not needed, but its dgamma partial is (with
   // more than one segment the dgamma partials come from pass A and the scan reduces them)
-  const int seg = (int)(blockIdx.x % p.nseg);
+  // (look-back: later segments first, so that a workgroup waits only on earlier ones)
+  const int seg = LB ? p.nseg - 1 - (int)(blockIdx.x % p.nseg) : (int)(blockIdx.x % p.nseg);
   const int bh = blockIdx.x / p.nseg;
-  const bool dg_here = FIN ? p.nseg == 1 : true;
+  const bool dg_here = FIN ? (p.nseg == 1 || LB) : true;
   const int b = bh / p.H, h = bh - b * p.H;
   const int H = p.H;
   const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
@@ -315,6 +352,18 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   };
   if constexpr (PF) pf_load(n_top - 1);
   else issue(n_top - 1);
+  // the look-back's single chunk: its saved o rstd and rstd are loaded with its rows (where
+  // a wave holds one state tile: with two, the registers are not there)
+  constexpr bool LBPF = LB && STW == 1;
+  Quad<T> obr_lb[LBPF ? RNDVH : 1];
+  float4 rsv_lb = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (LBPF) {
+    const int I = wave % NT, E0 = (wave / NT) * RNDVH;
+    const Quad<T>* ob = static_cast<const Quad<T>*>(p.obar) + ((sbase + n_top - 1) * NT + I) * NDV * 64 + lane;
+#pragma unroll
+    for (int Eh = 0; Eh < RNDVH; ++Eh) obr_lb[Eh] = ob[min(E0 + Eh, NDV - 1) * 64];
+    rsv_lb = *reinterpret_cast<const float4*>(p.rstd + (sbase + n_top - 1) * C + 16 * I + 4 * g4);
+  }
   for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
@@ -323,7 +372,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   f32x4 gacc[STW];
 #pragma unroll
   for (int m = 0; m < STW; ++m) gacc[m] = zero4();
-  if (FIN && scanned) {
+  if (FIN && scanned && !LB) {
     const float* src = p.gstates + ((long)bh * p.nseg + seg) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
@@ -356,10 +405,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
   };
+  // look-back: S_end waits for G (the look-back below); loaded here where a wave holds one
+  // state tile, after the look-back where it holds two (registers)
+  f32x4 se_lb[LB ? STW : 1];
   if (FIN && n_top < p.NC) {
-    f32x4 se[STW];
-    load_state(n_top, se);
-    write_part(se);
+    if constexpr (LB) {
+      if constexpr (STW == 1) load_state(n_top, se_lb);
+    } else {
+      f32x4 se[STW];
+      load_state(n_top, se);
+      write_part(se);
+    }
   }
   f32x4 s0c[STW];  // S0 of the current chunk
   load_state(n_top - 1, s0c);
@@ -422,7 +478,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // saved them (the recompute phase's row tile I, value tiles E0.. of half hh)
     Quad<T> obr[RD ? 1 : RNDVH];
     float4 rsv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (!RD) {
+    if constexpr (LBPF) {
+#pragma unroll
+      for (int Eh = 0; Eh < RNDVH; ++Eh) obr[Eh] = obr_lb[Eh];
+      rsv = rsv_lb;
+    } else if constexpr (!RD) {
       const int I = wave % NT, E0 = (wave / NT) * RNDVH;
       const Quad<T>* ob = static_cast<const Quad<T>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane;
 #pragma unroll
@@ -441,7 +501,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       const int nn = max(n - 1, c_first);
       if constexpr (PF) pf_load(nn);
       load_state(nn, s0p);
-    } else if (n > c_first) {
+    } else if (!LB && n > c_first) {  // (the look-back's workgroups hold one chunk)
       if constexpr (PF) pf_load(n - 1);
       load_state(n - 1, s0p);
     }
@@ -514,7 +574,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 
     // G^T as (e^{b_last} G)^T: it enters dv as k e^{-b} (e^{b_last} G) and dk as
     // e^{-b} V (e^{b_last} G)^T; with strong decay (elementwise paths) G itself
-    if (own) {
+    auto write_gt = [&]() {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
         const int u = wave + NW * m;
@@ -528,7 +588,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           lds_row_write<T, 4>(sGt + e * QP, ct * 16 + g4 * 4, gv4);
         }
       }
-    }
+    };
+    if (own && !LB) write_gt();  // the look-back writes it once G is known
 
     // ------------------------------------------------------------ recompute phase
     // Row tile I = wave % NT; with at least twice as many waves as row tiles, the two waves
@@ -737,9 +798,44 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         if ((own || RU) && r16 == 0) sDiag[hh * C + 16 * I + 4 * g4 + i] = (float)dd;
       }
     }
+    if constexpr (LB) {  // the dgamma partial is complete: per-wave sums
+#pragma unroll
+      for (int E = 0; E < NDV; ++E) {
+        float v = dgam[E];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
+      }
+    }
     __syncthreads();
     if constexpr (RU && !FIN) {
       if (tid < 2 * C) p.diagws[(sbase + n) * 2 * C + tid] = sDiag[tid];
+    }
+    if constexpr (LB) {
+      // publish this chunk's U = (q e^b)^T dO, its log2 decay and the dgamma partial (the
+      // flag follows the D phase, which covers the stores' latency)
+      const long slot = (long)bh * p.nseg + seg;
+      float* dst = p.gstates + slot * dk * dv;
+#pragma unroll
+      for (int m = 0; m < STW; ++m) {
+        const int u = wave + NW * m;
+        if (u < NST) {
+          const int ct = u / NDV, et = u - ct * NDV;
+          const f32x4 ua = Mma<T>::kc(zero4(), sQt, TP, 16 * ct, sdOt, TP, 16 * et, C, lane);
+          const int e = et * 16 + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = ct * 16 + g4 * 4 + i;
+            if ((FULLK || c < dk) && (FULLV || e < dv)) st_dev(dst + c * dv + e, ua[i]);
+          }
+        }
+      }
+      for (int c = tid; c < dk; c += NTH) st_dev(p.seg_lg + slot * dk + c, sLg[c]);
+      for (int e = tid; e < dv; e += NTH) {
+        float sum = sDg[e];  // waves in order
+        for (int w = 1; w < NW; ++w) sum += sDg[w * DVP + e];
+        st_dev(p.dgamma_part + (long)blockIdx.x * dv + e, sum);
+      }
     }
 
     if (own) {
@@ -764,7 +860,69 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           lds_row_write<T, 4>(sDt + (16 * J + r16) * TP, 16 * I + 4 * g4, dt4);
         }
       }
+      if constexpr (LB) __builtin_amdgcn_s_waitcnt(0);  // the values published above are out
       __syncthreads();
+      if constexpr (LB) {
+        const long slot0 = (long)bh * p.nseg;
+        if (tid == 0)
+          __hip_atomic_store(p.lb_flag + slot0 + seg, p.lb_tag, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        // G reaching this chunk's end: the later chunks' U, each decayed by the chunks
+        // between (gacc is zero here)
+        float fac[STW][4];
+#pragma unroll
+        for (int m = 0; m < STW; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fac[m][i] = 1.f;
+        lb_wait_all(p.lb_flag + slot0 + seg + 1, p.nseg - 1 - seg, p.lb_tag, lane);
+        // LBU later segments per step, their loads in flight together (a step past the
+        // last segment re-reads it and adds nothing)
+        constexpr int LBU = STW == 1 ? 4 : 1;
+        for (int s0 = seg + 1; s0 < p.nseg; s0 += LBU) {
+          float uv[LBU][STW][4], gv[LBU][STW][4];
+#pragma unroll
+          for (int a = 0; a < LBU; ++a) {
+            const long sl = slot0 + min(s0 + a, p.nseg - 1);
+            const float* src = p.gstates + sl * dk * dv;
+            const float* lg = p.seg_lg + sl * dk;
+#pragma unroll
+            for (int m = 0; m < STW; ++m) {
+              const int u = min(wave + NW * m, NST - 1);
+              const int ct = u / NDV, et = u - ct * NDV;
+              const int e = min(et * 16 + r16, dv - 1);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int c = min(ct * 16 + g4 * 4 + i, dk - 1);
+                uv[a][m][i] = ld_dev(src + c * dv + e);
+                gv[a][m][i] = ld_dev(lg + c);
+              }
+            }
+          }
+#pragma unroll
+          for (int a = 0; a < LBU; ++a) {
+            const bool on = s0 + a < p.nseg;
+#pragma unroll
+            for (int m = 0; m < STW; ++m) {
+              const int u = wave + NW * m;
+              const int ct = u / NDV, et = u - ct * NDV;
+              const int e = et * 16 + r16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int c = ct * 16 + g4 * 4 + i;
+                const bool in = on && u < NST && (FULLK || c < dk) && (FULLV || e < dv);
+                gacc[m][i] += in ? fac[m][i] * uv[a][m][i] : 0.f;
+                fac[m][i] *= on ? Fm<T>::exp2(gv[a][m][i]) : 1.f;
+              }
+            }
+          }
+        }
+        write_gt();
+        if (n_top < p.NC) {
+          if constexpr (STW > 1) load_state(n_top, se_lb);
+          write_part(se_lb);
+        }
+        __syncthreads();
+      }
 
       // ---- dq, dk, q.dq - k.dk (staged as soon as each (row tile, key tile) pair is done:
       // dq | dk over the raw v rows, which are no longer read) and dv (over dy, read only in
@@ -854,11 +1012,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
 
-    // gradient state: G <- diag(e^{b_last}) G + (q e^{b})^T dO
+    // gradient state: G <- diag(e^{b_last}) G + (q e^{b})^T dO (the look-back's single chunk
+    // has no chunk below it)
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
       const int u = wave + NW * m;
-      if (u < NST) {
+      if (!LB && u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
         const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
 #pragma unroll
@@ -944,14 +1103,14 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
     // its S0 (read by nobody before the next top barrier; sPart's last reader, this chunk's
     // dlog phase, is behind the barrier above)
-    if (n > c_first) {
+    if (!LB && n > c_first) {
       if (FIN) write_part(s0c);
 #pragma unroll
       for (int m = 0; m < STW; ++m) s0c[m] = s0p[m];
     }
   }
 
-  if (dg_here) {
+  if (dg_here && !LB) {
     // per-workgroup partial of dgamma, reduced in a fixed order by a later kernel
 #pragma unroll
     for (int E = 0; E < NDV; ++E) {
@@ -987,6 +1146,44 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     for (int c = tid; c < dk; c += NTH)
       p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
   }
+  if constexpr (LB) {
+    // the last workgroup: once every flag is up, d_norm_w = the partials added in a fixed
+    // order (parts strided over NG groups per column, then the groups in order)
+    if (p.d_norm_w && blockIdx.x == gridDim.x - 1) {
+      const int nparts = (int)gridDim.x;
+      for (int i = tid; i < nparts; i += NTH) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(p.lb_flag + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                   p.lb_tag &&
+               ++spins < kLbSpinLimit)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      __syncthreads();
+      constexpr int NG = NTH / DVP < NW ? NTH / DVP : NW;
+      const int g = tid / DVP, e = tid - g * DVP;
+      if (g < NG && e < dv) {
+        // parts g, g + NG, ... in increasing order, eight loads in flight at a time
+        constexpr int U8 = 8;
+        float sum = 0.f;
+        for (int i0 = g; i0 < nparts; i0 += U8 * NG) {
+          float v8[U8];
+#pragma unroll
+          for (int j = 0; j < U8; ++j)
+            v8[j] = ld_dev(p.dgamma_part + (long)min(i0 + j * NG, nparts - 1) * dv + e);
+#pragma unroll
+          for (int j = 0; j < U8; ++j) sum += i0 + j * NG < nparts ? v8[j] : 0.f;
+        }
+        sDg[g * DVP + e] = sum;
+      }
+      __syncthreads();
+      for (int e2 = tid; e2 < dv; e2 += NTH) {
+        float sum = sDg[e2];
+#pragma unroll
+        for (int g2 = 1; g2 < NG; ++g2) sum += sDg[g2 * DVP + e2];
+        p.d_norm_w[e2] = sum;
+      }
+    }
+  }
 }
 
 // Waves per workgroup: eight where the head shape leaves every phase at least one column per
@@ -1002,7 +1199,8 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   const long BH = (long)s.B * s.H;
   constexpr int NW = bwd_waves<T, DK, DV, EXACT>();
   constexpr bool RU = bwd_reuse_ok<DK, DV, EXACT, C, NW>();
-  const bool three = !s.bprefix && s.nseg > 1;
+  const bool lb = RU && s.lookback;  // the look-back shares the reuse condition
+  const bool three = !s.bprefix && s.nseg > 1 && !lb;
   if (ru_out) {  // reuse buffers: dO fragments of every chunk, then the diagonals
     ru_out[0] = RU && three ? (size_t)BH * s.NC * (bwd_reuse_chunk_bytes<T, DV, C, NW>() - 2 * C * sizeof(float)) : 0;
     ru_out[1] = RU && three ? (size_t)BH * s.NC * 2 * C * sizeof(float) : 0;
@@ -1020,6 +1218,14 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   if (lds_out) {
     *lds_out = RU && three && rd_bytes > fin_bytes ? rd_bytes : fin_bytes;
     return hipSuccess;
+  }
+  if constexpr (RU) {
+    if (lb) {
+      if (!p.lb_flag) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, false, true>),
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
+      return hipGetLastError();
+    }
   }
   if (three) {
     if constexpr (RU) {

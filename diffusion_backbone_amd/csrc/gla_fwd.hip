@@ -33,6 +33,9 @@ bool gla_dim_class(int dk, int dv, int* ndk, int* ndv) {
 // workgroups over them: two co-resident workgroups per unit for the forward's chunk kernels,
 // one for the backward's (their registers allow no second workgroup).
 constexpr long kComputeUnits = 256;
+// Longest sequence (in chunks) whose backward runs as one launch with the look-back: every
+// workgroup reads the contributions of all later chunks of its sequence.
+constexpr int kLookbackMaxChunks = 8;
 
 GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_chunks,
                   bool bwd) {
@@ -42,6 +45,11 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   gla_dim_class(dk, dv, &s.ndk, &s.ndv);
   s.NC = (L + C - 1) / C;
   int sc = seg_chunks;
+  // backward of a short sequence whose chunks all fit one round of workgroups: one chunk
+  // per workgroup, the gradient state carried by the look-back (a single launch)
+  if (bwd && sc <= 0 && s.NC >= 2 && s.NC <= kLookbackMaxChunks &&
+      (long)B * H * s.NC <= kComputeUnits)
+    sc = 1;
   if (sc <= 0) {
     // as many segments per sequence as fill that round; one segment when the (image, head)
     // units alone already do
@@ -60,6 +68,8 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   // chunk) never pays off.
   s.prefix = s.nseg <= 4 && (long)B * H * s.nseg <= 256;
   s.bprefix = s.nseg <= 1;
+  s.lookback = bwd && s.sc == 1 && s.nseg >= 2 && s.nseg <= kLookbackMaxChunks &&
+               (long)B * H * s.nseg <= kComputeUnits;
   return s;
 }
 

@@ -94,7 +94,7 @@ def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved:
     return d
 
 
-def gla_backward(case: W.GLACase, fwd: dict, *, dgamma: bool = True):
+def gla_backward(case: W.GLACase, fwd: dict, *, dgamma: bool = True, ws=None):
     import torch
     import diffusion_backbone_amd as dig
     dt = case.cfg.dtype
@@ -106,7 +106,8 @@ def gla_backward(case: W.GLACase, fwd: dict, *, dgamma: bool = True):
         g[n] = empty((B, L, H, d), dt)
     g["dgamma"] = torch.full((dv,), float("nan"), dtype=torch.float32, device="cuda") if dgamma else None
     wsb = dig.dig_gla_bwd_workspace_bytes(desc)
-    g["ws"] = nbytes_buf(wsb)
+    g["ws"] = nbytes_buf(wsb) if ws is None else ws   # a caller's workspace may be reused
+    assert g["ws"].numel() >= wsb
     dig.dig_gla_bwd(desc, fwd["q"], fwd["k"], fwd["v"], fwd["z"], fwd["r"], fwd["gamma"], g["dy"],
                     fwd["saved"], g["dq"], g["dk"], g["dv"], g["dz"], g["dr"], g["dgamma"],
                     g["ws"], wsb)

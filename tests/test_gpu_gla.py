@@ -193,12 +193,13 @@ def test_bwd_bf16_shapes(name, batch, seq_len, chunk, seg):
 
 @pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
 @pytest.mark.parametrize("name", ["dig_s2_256", "dig_xl2_2048"])
-def test_bwd_gate_stress(stress, name):
+@pytest.mark.parametrize("seg", [2, 0])   # 0: five chunks, one per workgroup (look-back)
+def test_bwd_gate_stress(stress, name, seg):
     kw = {"long_memory": dict(gate_bias=6.0), "fast_decay": dict(gate_bias=-6.0),
           "wide_logits": dict(z_std=4.0), "extreme_decay": dict(gate_bias=-40.0, z_std=1.0)}[stress]
-    announce("bwd stress %s %s" % (stress, name))
+    announce("bwd stress %s %s seg=%d" % (stress, name, seg))
     case = _case(name, batch=1, seq_len=300, **kw)
-    f = gla_forward(case, 64, seg_chunks=2, want_saved=True)
+    f = gla_forward(case, 64, seg_chunks=seg, want_saved=True)
     g = gla_backward(case, f)
     _check_bwd(case, g, TOL["bf16"])
 
@@ -231,6 +232,46 @@ def test_bwd_determinism():
     g1 = gla_backward(case, f)
     g2 = gla_backward(case, f)
     assert np.array_equal(to_f64(g1["dgamma"]), to_f64(g2["dgamma"]))
+
+
+# Short sequences whose chunks fit one round of workgroups run the backward as one launch:
+# a workgroup per chunk, the gradient state from the later chunks through the look-back
+# (published per chunk, read through flags tagged per call).
+@pytest.mark.parametrize("name,dtype,batch,seq_len,chunk", [
+    ("dig_s2_256", "bf16", 8, 256, 64),     # the benchmarked block: 4 chunks, 192 workgroups
+    ("dig_s2_256", "bf16", 1, 130, 64),     # 3 chunks, a ragged tail of 2 tokens
+    ("dig_s2_256", "bf16", 5, 512, 64),     # 8 chunks, the longest look-back
+    ("dig_xl2_2048", "bf16", 1, 450, 64),   # padded head tiles (36, 72), 8 chunks, ragged
+    ("dig_xl2_2048", "bf16", 2, 65, 64),    # 2 chunks, the second holds one token
+    ("tiny_f32", "bf16", 3, 200, 64),       # (16, 32) heads, four waves
+    ("tiny_f32", "bf16", 2, 200, 32),       # (16, 32) heads, 32-token chunks, 7 chunks
+])
+@pytest.mark.parametrize("dgamma", [True, False])
+def test_bwd_lookback_shapes(name, dtype, batch, seq_len, chunk, dgamma):
+    announce("bwd lookback %s B=%d L=%d chunk=%d dgamma=%d" % (name, batch, seq_len, chunk, dgamma))
+    case = _case(name, batch=batch, seq_len=seq_len, dtype=dtype, random_gamma=True)
+    f = gla_forward(case, chunk, want_saved=True)
+    g = gla_backward(case, f, dgamma=dgamma)
+    _check_bwd(case, g, TOL["bf16"])
+
+
+def test_bwd_lookback_workspace_reuse():
+    """One workspace across calls with other inputs: flags left by an earlier call must not
+    be taken for this call's, and a repeated call gives the same bits."""
+    announce("bwd lookback workspace reuse")
+    a = _case("dig_s2_256", batch=4, seq_len=256, random_gamma=True)
+    b = W.make_gla_case(W.CONFIGS["dig_s2_256"], seed=1234, batch=4, seq_len=256,
+                        random_gamma=True)
+    fa = gla_forward(a, 64, want_saved=True)
+    fb = gla_forward(b, 64, want_saved=True)
+    ga = gla_backward(a, fa)
+    ws = ga["ws"]
+    gb = gla_backward(b, fb, ws=ws)
+    _check_bwd(b, gb, TOL["bf16"], what="second call")
+    ga2 = gla_backward(a, fa, ws=ws)
+    _check_bwd(a, ga2, TOL["bf16"], what="third call")
+    for n in GRADS + ("dgamma",):
+        assert np.array_equal(to_f64(ga[n]), to_f64(ga2[n])), n
 
 
 def test_fwd_bwd_config_dig_xl2_2048_full():
