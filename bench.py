@@ -169,20 +169,33 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ps) / max(len(ps), 1)
 
 
-# HBM traffic of one dig_gla_bwd call on the default workload, from rocprofv3 FETCH_SIZE and
+# HBM traffic of one GLA call on the default workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (summed over the call's kernels) divided by the counters' reading per byte
 # of a plain copy; valid only for the kernel sources it was measured on (sha256 below).
 TRAFFIC = {
-    "call": "dig_gla_bwd",
     "workload": "dig_s2_256",
-    # FETCH_SIZE 12467.8 KiB / 0.50006 (copy: 131088.3 KiB read per 262144 KiB moved) +
-    # WRITE_SIZE 10154.0 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-    "bytes": 35928476,
-    "sources_sha256": "5b632107880f6485b4183885e2418f66f2829babf4662e00f7984d8d2e7a170e",
+    "bytes": {
+        # FETCH_SIZE 8115.4 KiB / 0.50006 (copy: 131088.1 KiB read per 262144 KiB moved) +
+        # WRITE_SIZE 6990.2 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
+        "dig_gla_bwd": 23776381,
+        # FETCH_SIZE 7402.7 KiB / 0.50006 + WRITE_SIZE 4656.0 KiB / 1.0
+        "dig_gla_fwd": 19926597,
+    },
+    "sources_sha256": "65baaf6db75c289a5e93807a649761765068d1814bfd16b2c4650754e5f6e3c6",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
+                   "diffusion_backbone_amd/csrc/gla_fwd_kernel.h",
+                   "diffusion_backbone_amd/csrc/gla_fwd.hip",
                    "diffusion_backbone_amd/csrc/dig_device.h")
+
+
+# The kernels one call runs on the default workload (B=8, 16x16 grid, 6 heads: 4 chunks of 64
+# tokens per image and head).
+KERNEL_OF_CALL = {
+    "gla_bwd": "gla_bwd_kernel, look-back (one chunk per workgroup, one launch)",
+    "gla_fwd": "gla_fwd_kernel, in-workgroup prefix (one launch)",
+}
 
 
 def sources_sha256():
@@ -194,11 +207,12 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, call):
     """Counter-derived bytes per call, or None when the kernels changed since the run."""
-    if TRAFFIC["bytes"] is None or workload != TRAFFIC["workload"]:
+    byts = TRAFFIC["bytes"].get(call)
+    if byts is None or workload != TRAFFIC["workload"]:
         return None
-    return TRAFFIC["bytes"] if TRAFFIC["sources_sha256"] == sources_sha256() else None
+    return byts if TRAFFIC["sources_sha256"] == sources_sha256() else None
 
 
 def copy_probe(mib, reps):
@@ -420,18 +434,18 @@ def main():
         byts = gla_bytes_per_token_head(cfg, which) * th
         rl[name] = {"ms": t, "bytes": byts, "gbs": byts / (t / 1e3) / 1e9}
     dom = max(rl, key=lambda n: rl[n]["ms"])
-    traffic = measured_traffic(cfg.name) if dom == "gla_bwd" else None
+    traffic = measured_traffic(cfg.name, "dig_" + dom)
     roof = {"bound": "hbm", "achieved": round(rl[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(rl[dom]["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": ("gla_bwd_kernel (pass A + final pass) + gla_gstate_scan + gla_dgamma_reduce"
-                       if dom == "gla_bwd" else "gla_fwd_kernel"),
+            "kernel": KERNEL_OF_CALL[dom],
             "call": "dig_" + dom, "avg_call_us": round(rl[dom]["ms"] * 1e3, 2),
             "algorithmic_bytes_per_launch": rl[dom]["bytes"],
             "note": "per library call: HIP events bracket the whole call on its stream, "
                     "in a second timed pass of the same K steps (%.4f ms/step with the events)"
                     % ms_ev}
     other = [n for n in rl if n != dom][0]
+    traffic_other = measured_traffic(cfg.name, "dig_" + other)
     out = {
         "metric": "GLA-layer tokens/s (fwd+bwd)",
         "value": round(value, 1),
@@ -454,7 +468,8 @@ def main():
         "roofline": roof,
         "roofline_other_call": {"call": "dig_" + other, "avg_call_us": round(rl[other]["ms"] * 1e3, 2),
                                 "achieved_gbs": round(rl[other]["gbs"], 1),
-                                "frac": round(rl[other]["gbs"] / HBM_PEAK_GBS, 4)},
+                                "frac": round(rl[other]["gbs"] / HBM_PEAK_GBS, 4),
+                                "kernel": KERNEL_OF_CALL[other], "traffic": traffic_other},
     }
     if not args.no_probes:
         out["probes"] = probes()

@@ -6,7 +6,10 @@
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers on the current HIP device, 16-byte aligned,
  *     contiguous.  The caller owns every buffer; the library never allocates or frees
- *     device memory and keeps no state between calls.
+ *     device memory and keeps no device state between calls (its only state is a host-side
+ *     call counter that tags the backward's look-back flags).
+ *   - A workspace holds scratch only: it needs no initialisation and may be reused by later
+ *     calls, but two calls that may run at the same time (other streams) must not share one.
  *   - Work is enqueued on `stream` and the call returns without synchronising.
  *   - Arguments are checked on the host before anything is enqueued.  A non-OK status
  *     means nothing was written; dig_last_error() gives a thread-local description.
@@ -121,7 +124,10 @@ size_t dig_gla_bwd_workspace_bytes(const dig_gla_desc* desc);
  *   dq, dk, d_gate_logit : [B, L, H, d_k];  dv, dr : [B, L, H, d_v]   (overwritten)
  *   d_norm_w             : [d_v] fp32 sum over batch, tokens and heads (overwritten), or NULL
  * d_gate_logit = dlog(alpha) * sigmoid(-z) / tau.  The d_norm_w reduction runs in a fixed
- * order, so repeated calls give identical bits.
+ * order, so repeated calls give identical bits.  Sequences of 2..8 chunks whose chunks all
+ * fit one round of workgroups (batch * heads * chunks <= 256) run as one launch in which
+ * each chunk's workgroup reads the later chunks' gradient contributions through flags in
+ * the workspace (bounded waits; the flags carry a per-call tag).
  */
 dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, const void* v,
                        const void* gate_logit, const void* r, const float* norm_w,
