@@ -150,8 +150,9 @@ size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
 size_t dig_gla_fwd_workspace_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;
   if (check_desc(d, &s, kFwd) != DIG_OK) return 0;
-  if (s.nseg == 1 || s.prefix) return 0;  // no cross-segment scan
-  return a256(dig::gla_states_bytes(s)) + a256(dig::gla_seglg_bytes(s));
+  const size_t flags = s.lookback ? a256((size_t)s.B * s.H * s.nseg * sizeof(unsigned)) : 0;
+  if (!s.lookback && (s.nseg == 1 || s.prefix)) return 0;  // no cross-segment exchange
+  return a256(dig::gla_states_bytes(s)) + a256(dig::gla_seglg_bytes(s)) + flags;
 }
 
 size_t dig_gla_bwd_workspace_bytes(const dig_gla_desc* d) {
@@ -200,6 +201,10 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
     p.rstd = reinterpret_cast<float*>(static_cast<char*>(saved_opt) + dig::gla_saved_rstd_offset(s));
   }
   p.seg_lg = reinterpret_cast<float*>(ws + a256(sb));
+  if (s.lookback) {  // chunk contributions, decays and flags
+    p.lb_u = reinterpret_cast<float*>(ws);
+    p.lb_flag = reinterpret_cast<unsigned*>(ws + a256(sb) + a256(dig::gla_seglg_bytes(s)));
+  }
   p.write_states = saved_opt != nullptr;
   p.g2scale = 1.4426950408889634f / d->tau;
   p.q_scale = d->q_scale;

@@ -652,4 +652,30 @@ __device__ __forceinline__ void zero_rows(T* dst, int valid, int rows, int cols,
   for (int i = valid * cols + tid; i < rows * cols; i += nthr) dst[i] = from_f<T>(0.f);
 }
 
+// Cross-workgroup exchange inside one launch (the GLA look-back kernels).  Every exchanged
+// value goes through device-scope loads and stores, which the L2 of each
+// XCD does not hold back; the stores have completed (waited for) before the flag is
+// written, and the values are loaded only after the flag is seen.  No L2 write-back or
+// invalidation is needed (fences would do both, over the whole L2, per wave).
+constexpr unsigned kLbSpinLimit = 1u << 18;  // polls of at least ~1 us: a bound far past any real wait
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).
+__device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, unsigned tag,
+                                            int lane) {
+  if (lane < count) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(const_cast<unsigned*>(flags + lane), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
+           ++spins < kLbSpinLimit)
+      __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 }  // namespace dig

@@ -17,7 +17,8 @@ struct GlaShape {
   int nseg;                 // segments per sequence = ceil(NC / sc)
   int prefix;               // forward: 1 = each segment recomputes its incoming state
   int bprefix;              // backward: the same choice (its recompute is costlier)
-  int lookback;             // backward: one chunk per workgroup, G via a look-back (1 launch)
+  int lookback;             // one chunk per workgroup, the carried state through a look-back
+                            // over flags (forward: S0; backward: G), one launch
   int ndk, ndv;             // compiled head-dim class: d_k <= 16*ndk, d_v <= 16*ndv
 };
 
@@ -35,7 +36,11 @@ struct GlaFwdParams {
   void* y;
   void* o_pre;
   float* states;   // [B*H][NC][dk][dv] fp32: state entering each chunk
-  float* seg_lg;   // [B*H][nseg][dk] fp32: log2 of each segment's total decay
+  float* seg_lg;   // [B*H][nseg][dk] fp32: log2 of each segment's total decay (look-back:
+                   // each chunk's decay factor)
+  float* lb_u;     // look-back: [B*H][NC][dk][dv] each chunk's own state contribution
+  unsigned* lb_flag;  // look-back: [B*H][NC] chunk published (== lb_tag)
+  unsigned lb_tag;    // this call's flag value
   void* obar;      // saved for the backward, or null: normalised o in fragment order
   float* rstd;     // saved for the backward, or null: [B*H][NC][C] RMSNorm reciprocal rms
   int B, L, H, dk, dv, NC, sc, nseg;
@@ -102,6 +107,8 @@ size_t gla_bwd_reuse_bytes(const GlaShape& s);
 size_t gla_bwd_reuse_diag_offset(const GlaShape& s);
 // Offset of the look-back flags in the workspace ([B*H][nseg] unsigned).
 size_t gla_bwd_flag_offset(const GlaShape& s);
+// Look-back flag value for one call: differs from every earlier call's in this process.
+unsigned next_call_tag();
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
 // ------------------------------------------------------------------------- misc

@@ -150,7 +150,7 @@ size_t gla_bwd_reuse_diag_offset(const GlaShape& s) {
 
 // Look-back flag values: a fresh one per call (a bijective hash of a call counter), so that
 // flags left in a reused workspace by earlier calls never match.
-static unsigned next_lb_tag() {
+unsigned next_call_tag() {
   static std::atomic<unsigned> calls{0};
   const unsigned t = (calls.fetch_add(1, std::memory_order_relaxed) + 1u) * 0x9E3779B1u;
   return t ? t : 1u;
@@ -158,7 +158,7 @@ static unsigned next_lb_tag() {
 
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
-  p.lb_tag = next_lb_tag();
+  p.lb_tag = next_call_tag();
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.bprefix;
   hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr, nullptr)

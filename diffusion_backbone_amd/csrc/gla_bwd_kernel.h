@@ -144,31 +144,6 @@ constexpr size_t bwd_reuse_chunk_bytes() {
 // before the waiter (in-order dispatch): the waits cannot deadlock.  The last workgroup
 // reduces the dgamma partials in a fixed order once every flag is up.  Flags hold this
 // call's tag, so values left by earlier calls never match; each wait is bounded.
-// Every exchanged value goes through device-scope loads and stores, which the L2 of each
-// XCD does not hold back; the stores have completed (waited for) before the flag is
-// written, and the values are loaded only after the flag is seen.  No L2 write-back or
-// invalidation is needed (fences would do both, over the whole L2, per wave).
-constexpr unsigned kLbSpinLimit = 1u << 18;  // polls of at least ~1 us: a bound far past any real wait
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-// Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).
-__device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, unsigned tag,
-                                            int lane) {
-  if (lane < count) {
-    unsigned spins = 0;
-    while (__hip_atomic_load(const_cast<unsigned*>(flags + lane), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
-           ++spins < kLbSpinLimit)
-      __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool RU = false,
           bool LB = false>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {

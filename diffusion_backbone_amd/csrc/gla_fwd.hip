@@ -45,9 +45,12 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   gla_dim_class(dk, dv, &s.ndk, &s.ndv);
   s.NC = (L + C - 1) / C;
   int sc = seg_chunks;
-  // backward of a short sequence whose chunks all fit one round of workgroups: one chunk
-  // per workgroup, the gradient state carried by the look-back (a single launch)
-  if (bwd && sc <= 0 && s.NC >= 2 && s.NC <= kLookbackMaxChunks &&
+  // a short sequence whose chunks all fit one round of workgroups: one chunk per workgroup,
+  // the carried state through the look-back (a single launch); the forward's look-back
+  // kernel exists for the exact head shapes
+  const bool exact = (dk == 32 && dv == 64) || (dk == 36 && dv == 72) || (dk == 16 && dv == 32);
+  const bool lb_ok = bwd || exact;
+  if (lb_ok && sc <= 0 && s.NC >= 2 && s.NC <= kLookbackMaxChunks &&
       (long)B * H * s.NC <= kComputeUnits)
     sc = 1;
   if (sc <= 0) {
@@ -66,10 +69,10 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   // scheme only while the grid is at most one workgroup per compute unit (latency-bound)
   // and there are few segments; the backward's recompute (a full output-stage backward per
   // chunk) never pays off.
-  s.prefix = s.nseg <= 4 && (long)B * H * s.nseg <= 256;
-  s.bprefix = s.nseg <= 1;
-  s.lookback = bwd && s.sc == 1 && s.nseg >= 2 && s.nseg <= kLookbackMaxChunks &&
+  s.lookback = lb_ok && s.sc == 1 && s.nseg >= 2 && s.nseg <= kLookbackMaxChunks &&
                (long)B * H * s.nseg <= kComputeUnits;
+  s.prefix = !s.lookback && s.nseg <= 4 && (long)B * H * s.nseg <= 256;
+  s.bprefix = s.nseg <= 1;
   return s;
 }
 
@@ -154,6 +157,7 @@ hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.prefix;
+  p.lb_tag = next_call_tag();
   return s.bf16 ? launch_gla_fwd_t<bf16>(s, p, st, nullptr)
                 : launch_gla_fwd_t<float>(s, p, st, nullptr);
 }

@@ -98,8 +98,16 @@ struct FwdLayout {
   static constexpr int bytes(int nbuf) { return O_RAW + nbuf * SLOT; }
 };
 
-template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW>
+// Look-back (LB: short sequences, one chunk per workgroup, one launch).  The state waves form
+// the chunk's own contribution U = Kbar^T V (the carry from a zero state), publish it with the
+// chunk's decay factors and raise the chunk's flag, while the query-row waves form P V; then
+// the state waves wait for the earlier chunks' flags of the sequence and sum
+//   S0(n) = U(n-1) + diag(e^{b_last(n-1)}) U(n-2) + diag(e^{b_last(n-1) + b_last(n-2)}) U(n-3) ...
+// which the query-row waves then use for (q e^b) S0.  Earlier chunks have lower workgroup
+// indices (dispatched first), every wait is bounded, and flags carry a per-call tag.
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW, bool LB = false>
 __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
+  static_assert(!LB || OUT, "the look-back runs the output kernel");
   constexpr int NTH = 64 * NW;  // NW waves
   using Lo = FwdLayout<T, DK, DV, C, OUT, NW, EXACT>;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   const int c_first = seg * p.sc;
   const int c_end = min(p.NC, c_first + p.sc);
   const int n_begin = (OUT && p.prefix) ? 0 : c_first;
-  const bool scanned = !p.prefix && p.nseg > 1;  // incoming state comes from pass B
+  const bool scanned = !LB && !p.prefix && p.nseg > 1;  // incoming state comes from pass B
   const long sbase = (long)bh * p.NC;             // chunk-slot base for this (b,h)
   const float inv_tau = p.g2scale * 0.69314718055994531f;  // g2scale = log2(e) / tau
 
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   f32x4 sacc[STW];
 #pragma unroll
   for (int m = 0; m < STW; ++m) sacc[m] = zero4();
-  if (OUT && scanned && seg > 0) {
+  if (OUT && scanned && seg > 0) {  // (never with the look-back: scanned is false there)
     const float* src = p.states + (sbase + c_first) * dk * dv;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       issue(n, 0);
     }
     // the state entering this chunk: saved for the backward, bf16 copy for (q e^b) S0
-    if (emit && p.write_states && !(scanned && n == c_first)) {
+    if (!LB && emit && p.write_states && !(scanned && n == c_first)) {
       float* dst = p.states + (sbase + n) * dk * dv;
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
@@ -287,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         }
       }
     }
-    if (emit) {
+    if (!LB && emit) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
         const int u = wave - SW0 + NSW * m;
@@ -399,7 +407,30 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         sacc[m] = Mma<T>::kc(sacc[m], sKbT, TP, 16 * ct, sVt, TP, 16 * et, CK, lane);
       }
     }
+    if constexpr (LB) {  // publish U (sacc started from zero) and the chunk's decay factors
+      if (wave >= SW0) {
+        const long slot = (long)bh * p.nseg + seg;
+        float* dst = p.lb_u + slot * dk * dv;
+#pragma unroll
+        for (int m = 0; m < STW; ++m) {
+          const int u = wave - SW0 + NSW * m;
+          if (u < NST) {
+            const int ct = u / NDV, et = u - ct * NDV;
+            const int e = et * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = ct * 16 + g4 * 4 + i;
+              if ((FULLK || c < dk) && (FULLV || e < dv)) st_dev(dst + c * dv + e, sacc[m][i]);
+            }
+          }
+        }
+        for (int c = tid - 64 * SW0; c < dk; c += 64 * NSW) st_dev(p.seg_lg + slot * dk + c, sGam[c]);
+      }
+    }
 
+    f32x4 oacc[NDV];
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) oacc[E] = zero4();
     if (emit && wave < NT) {
       const int I = wave;  // this wave's 16 query rows
       // exact diagonal q_i.k_i (gate factor 1) from the unscaled inputs, so that a
@@ -461,13 +492,12 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         }
       }
 
-      f32x4 oacc[NDV];
+      // inter-chunk: O = (q e^{b}) S0 (the look-back adds it once S0 is known)
+      if constexpr (!LB) {
 #pragma unroll
-      for (int E = 0; E < NDV; ++E) oacc[E] = zero4();
-      // inter-chunk: O = (q e^{b}) S0
-#pragma unroll
-      for (int E = 0; E < NDV; ++E)
-        oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
+        for (int E = 0; E < NDV; ++E)
+          oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
+      }
 
       // intra-chunk: O += P V   (P straight from the accumulators above)
       if constexpr (kBf) {
@@ -509,6 +539,90 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         }
       }
 
+    }
+    if constexpr (LB) {
+      __builtin_amdgcn_s_waitcnt(0);  // U and the decay factors are out
+      __syncthreads();
+      const long slot0 = (long)bh * p.nseg;
+      if (tid == 0)
+        __hip_atomic_store(p.lb_flag + slot0 + seg, p.lb_tag, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (wave >= SW0) {
+        // S0 = the earlier chunks' U, each decayed by the chunks between; the state tiles are
+        // reused for it (U has been published)
+#pragma unroll
+        for (int m = 0; m < STW; ++m) sacc[m] = zero4();
+        if (seg > 0) {
+          lb_wait_all(p.lb_flag + slot0, seg, p.lb_tag, lane);
+          float fac[STW][4];
+#pragma unroll
+          for (int m = 0; m < STW; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fac[m][i] = 1.f;
+          constexpr int LBU = STW <= 2 ? 2 : 1;  // chunks whose loads are in flight together
+          for (int m0 = seg - 1; m0 >= 0; m0 -= LBU) {
+            float uv[LBU][STW][4], gv[LBU][STW][4];
+#pragma unroll
+            for (int a = 0; a < LBU; ++a) {
+              const long sl = slot0 + max(m0 - a, 0);
+#pragma unroll
+              for (int m = 0; m < STW; ++m) {
+                const int u = min(wave - SW0 + NSW * m, NST - 1);
+                const int ct = u / NDV, et = u - ct * NDV;
+                const int e = min(et * 16 + r16, dv - 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int c = min(ct * 16 + g4 * 4 + i, dk - 1);
+                  uv[a][m][i] = ld_dev(p.lb_u + sl * dk * dv + c * dv + e);
+                  gv[a][m][i] = ld_dev(p.seg_lg + sl * dk + c);
+                }
+              }
+            }
+#pragma unroll
+            for (int a = 0; a < LBU; ++a) {
+              const bool on = m0 - a >= 0;
+#pragma unroll
+              for (int m = 0; m < STW; ++m) {
+                const int u = wave - SW0 + NSW * m;
+                const int ct = u / NDV, et = u - ct * NDV;
+                const int e = et * 16 + r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int c = ct * 16 + g4 * 4 + i;
+                  const bool in = on && u < NST && (FULLK || c < dk) && (FULLV || e < dv);
+                  sacc[m][i] += in ? fac[m][i] * uv[a][m][i] : 0.f;
+                  fac[m][i] *= on ? gv[a][m][i] : 1.f;
+                }
+              }
+            }
+          }
+        }
+        // S0: saved for the backward, bf16 copy for (q e^b) S0
+        float* dst = p.states + (sbase + n) * dk * dv;
+#pragma unroll
+        for (int m = 0; m < STW; ++m) {
+          const int u = wave - SW0 + NSW * m;
+          if (u < NST) {
+            const int ct = u / NDV, et = u - ct * NDV;
+            const int e = et * 16 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = ct * 16 + g4 * 4 + i;
+              if (p.write_states && c < dk && e < dv) dst[c * dv + e] = sacc[m][i];
+              sS[e * QP + c] = from_f<T>(sacc[m][i]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (emit && wave < NT) {
+      const int I = wave;
+      if constexpr (LB) {
+#pragma unroll
+        for (int E = 0; E < NDV; ++E)
+          oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
+      }
       // output stage: head-wise RMSNorm x weight x Swish(r), stored from the accumulators
       T rr[NDV][4];  // all of this lane's r first (one LDS round trip)
 #pragma unroll
@@ -602,6 +716,14 @@ static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st
   if (lds_out) {  // size query only
     *lds_out = bytes_c;
     return hipSuccess;
+  }
+  if constexpr (EXACT) {
+    if (s.lookback) {
+      if (!p.lb_u || !p.lb_flag) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW, true>),
+                         dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), bytes_c, st, p, nbuf_c);
+      return hipGetLastError();
+    }
   }
   if (!s.prefix && s.nseg > 1) {
     int bytes_a, nbuf_a;

@@ -72,7 +72,7 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved: bool = False,
                 want_opre: bool = True, gamma=True, tau: float = 16.0, q_scale: float = 1.0,
-                eps: float = 1e-5):
+                eps: float = 1e-5, ws=None):
     """Runs dig_gla_fwd on the case; returns dict of device tensors."""
     import torch
     import diffusion_backbone_amd as dig
@@ -87,7 +87,8 @@ def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved:
     d["o_pre"] = empty((B, L, H, dv), dt) if want_opre else None
     d["saved"] = nbytes_buf(dig.dig_gla_saved_bytes(desc)) if want_saved else None
     wsb = dig.dig_gla_fwd_workspace_bytes(desc)
-    d["ws"] = nbytes_buf(wsb) if wsb else None
+    d["ws"] = (nbytes_buf(wsb) if wsb else None) if ws is None else ws  # may be reused
+    assert d["ws"] is None or d["ws"].numel() >= wsb
     dig.dig_gla_fwd(desc, d["q"], d["k"], d["v"], d["z"], d["r"], d["gamma"], d["y"],
                     d["o_pre"], d["saved"], d["ws"], wsb)
     d["desc"] = desc

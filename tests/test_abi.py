@@ -74,8 +74,11 @@ def test_fwd_null_alias_align_workspace():
     d = _desc()
     assert _fwd(d, q=None) == dig.DIG_ERR_NULL
     assert _fwd(d, q=BAD_PTR + 8) == dig.DIG_ERR_ALIGN
-    # y overlapping q
-    assert _fwd(d, y=BAD_PTR + 64) == dig.DIG_ERR_ALIAS
+    # y overlapping q (with the workspace this short sequence's look-back needs)
+    nd = dig.dig_gla_fwd_workspace_bytes(d)
+    assert nd > 0
+    assert _fwd(d, y=BAD_PTR + 64, ws=BAD_PTR + 0x200000000, wsb=nd) == dig.DIG_ERR_ALIAS
+    assert _fwd(d, ws=None) == dig.DIG_ERR_WORKSPACE
     # a long sequence needs a workspace for the cross-segment scan
     dl = _desc(batch=1, heads=6, seq_len=12544)
     need = dig.dig_gla_fwd_workspace_bytes(dl)

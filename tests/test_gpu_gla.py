@@ -122,6 +122,54 @@ def test_fwd_chunk_invariance_and_determinism():
     assert np.array_equal(a, b), "two identical runs differ"
 
 
+# Short sequences whose chunks fit one round of workgroups run the forward as one launch: a
+# workgroup per chunk, the state entering it from the earlier chunks through the look-back.
+@pytest.mark.parametrize("name,dtype,batch,seq_len,chunk", [
+    ("dig_s2_256", "bf16", 8, 256, 64),     # the benchmarked block: 4 chunks, 192 workgroups
+    ("dig_s2_256", "bf16", 1, 130, 64),     # 3 chunks, a ragged tail of 2 tokens
+    ("dig_s2_256", "bf16", 5, 512, 64),     # 8 chunks, the longest look-back
+    ("dig_xl2_2048", "bf16", 1, 450, 64),   # padded head tiles (36, 72), 8 chunks, ragged
+    ("dig_xl2_2048", "bf16", 2, 65, 64),    # 2 chunks, the second holds one token
+    ("tiny_f32", "bf16", 3, 200, 64),       # (16, 32) heads, four waves
+    ("tiny_f32", "f32", 2, 200, 32),        # fp32, 32-token chunks, 7 chunks
+])
+@pytest.mark.parametrize("saved", [True, False])
+def test_fwd_lookback_shapes(name, dtype, batch, seq_len, chunk, saved):
+    announce("fwd lookback %s %s B=%d L=%d chunk=%d saved=%d" % (name, dtype, batch, seq_len,
+                                                                 chunk, saved))
+    case = _case(name, batch=batch, seq_len=seq_len, dtype=dtype, random_gamma=True)
+    f = gla_forward(case, chunk, want_saved=saved)
+    _check_fwd(case, f, TOL[dtype])
+    if saved and dtype == "bf16":  # the saved states feed the backward
+        _check_bwd(case, gla_backward(case, f), TOL[dtype])
+
+
+@pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
+def test_fwd_lookback_gate_stress(stress):
+    kw = {"long_memory": dict(gate_bias=6.0), "fast_decay": dict(gate_bias=-6.0),
+          "wide_logits": dict(z_std=4.0), "extreme_decay": dict(gate_bias=-40.0, z_std=1.0)}[stress]
+    announce("fwd lookback stress %s" % stress)
+    for name in ("dig_s2_256", "dig_xl2_2048"):
+        case = _case(name, batch=1, seq_len=300, **kw)   # five chunks
+        _check_fwd(case, gla_forward(case, 64), TOL["bf16"], what=name)
+
+
+def test_fwd_lookback_workspace_reuse():
+    """One workspace across forward calls with other inputs (stale flags must not match), and
+    a repeated call gives the same bits."""
+    announce("fwd lookback workspace reuse")
+    a = _case("dig_s2_256", batch=4, seq_len=256, random_gamma=True)
+    b = W.make_gla_case(W.CONFIGS["dig_s2_256"], seed=4321, batch=4, seq_len=256,
+                        random_gamma=True)
+    fa = gla_forward(a, 64, want_saved=True)
+    ws = fa["ws"]
+    fb = gla_forward(b, 64, want_saved=True, ws=ws)
+    _check_fwd(b, fb, TOL["bf16"], what="second call")
+    fa2 = gla_forward(a, 64, want_saved=True, ws=ws)
+    _check_fwd(a, fa2, TOL["bf16"], what="third call")
+    assert np.array_equal(to_f64(fa["y"]), to_f64(fa2["y"]))
+
+
 def test_fwd_config_dig_s2_256_full():
     announce("fwd dig_s2_256 full B=8 L=256")
     case = _case("dig_s2_256")
