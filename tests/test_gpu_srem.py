@@ -108,6 +108,7 @@ def test_dwconv_full_configs(name):
     (1, 8, 8, 64, "f32"), (2, 16, 16, 384, "bf16"), (1, 5, 7, 12, "bf16"), (2, 3, 4, 5, "f32"),
     (1, 16, 16, 1152, "bf16"), (1, 9, 2, 1152, "bf16"), (2, 5, 6, 64, "f32"),
     (6, 37, 29, 384, "bf16"), (11, 29, 37, 128, "f32"),  # column-strip path, ragged
+    (8, 16, 16, 384, "bf16"),  # the benchmarked block (sums finished in the same launch)
 ])
 def test_dwconv_bwd(B, gh, gw, D, dtype):
     dig = _dig()
