@@ -150,7 +150,8 @@ size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
 size_t dig_gla_fwd_workspace_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;
   if (check_desc(d, &s, kFwd) != DIG_OK) return 0;
-  const size_t flags = s.lookback ? a256((size_t)s.B * s.H * s.nseg * sizeof(unsigned)) : 0;
+  const size_t flags =  // look-back flags: published, done
+      s.lookback ? a256(2 * (size_t)s.B * s.H * s.nseg * sizeof(unsigned)) : 0;
   if (!s.lookback && (s.nseg == 1 || s.prefix)) return 0;  // no cross-segment exchange
   return a256(dig::gla_states_bytes(s)) + a256(dig::gla_seglg_bytes(s)) + flags;
 }

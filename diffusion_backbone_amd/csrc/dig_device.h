@@ -666,6 +666,12 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+// Each launch also clears its flags before it ends: every workgroup raises a second ("done")
+// flag once its own waits are over, and the last workgroup waits for all of those and then
+// zeroes both arrays.  A launch therefore never sees flags raised by an earlier one, also when
+// the same arguments (the same tag) are replayed, as from a captured graph; the per-call tag
+// covers a workspace that has never been used.
+//
 // Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).
 __device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, unsigned tag,
                                             int lane) {
@@ -676,6 +682,22 @@ __device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, un
            ++spins < kLbSpinLimit)
       __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Every thread: waits until flags[0..n) all hold tag, n any size (the workgroup's threads
+// share the flags; a workgroup barrier follows in the caller).
+__device__ __forceinline__ void lb_wait_each(const unsigned* flags, int n, unsigned tag, int tid,
+                                             int nthreads) {
+  for (int i = tid; i < n; i += nthreads) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(const_cast<unsigned*>(flags + i), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
+           ++spins < kLbSpinLimit)
+      __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ void lb_raise(unsigned* flag, unsigned tag) {
+  __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dig

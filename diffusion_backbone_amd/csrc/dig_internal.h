@@ -39,7 +39,7 @@ struct GlaFwdParams {
   float* seg_lg;   // [B*H][nseg][dk] fp32: log2 of each segment's total decay (look-back:
                    // each chunk's decay factor)
   float* lb_u;     // look-back: [B*H][NC][dk][dv] each chunk's own state contribution
-  unsigned* lb_flag;  // look-back: [B*H][NC] chunk published (== lb_tag)
+  unsigned* lb_flag;  // look-back: [2][B*H][NC] chunk published, chunk done (== lb_tag)
   unsigned lb_tag;    // this call's flag value
   void* obar;      // saved for the backward, or null: normalised o in fragment order
   float* rstd;     // saved for the backward, or null: [B*H][NC][C] RMSNorm reciprocal rms
@@ -91,7 +91,7 @@ struct GlaBwdParams {
   float* dgamma_part;   // [B*H*nseg][dv] per-workgroup partial sums
   void* dofrag;         // [B*H][NC] chunks of pass A's dO in fragment order (reuse), or null
   float* diagws;        // [B*H][NC][2][C] pass A's dO.v diagonals (reuse), or null
-  unsigned* lb_flag;    // [B*H][nseg] look-back: segment published (== lb_tag)
+  unsigned* lb_flag;    // look-back: [2][B*H][nseg] segment published, segment done (== lb_tag)
   unsigned lb_tag;      // this call's flag value (differs from every earlier call's)
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;

@@ -39,7 +39,7 @@ size_t gla_bwd_workspace(const GlaShape& s) {
   size_t part = BH * s.nseg * s.dv * sizeof(float);
   auto a = [](size_t x) { return (x + 255) / 256 * 256; };
   return a(g) + a(lg) + a(part) + gla_bwd_reuse_bytes(s) +
-         (s.lookback ? a(BH * s.nseg * sizeof(unsigned)) : 0);
+         (s.lookback ? a(2 * BH * s.nseg * sizeof(unsigned)) : 0);  // published, done
 }
 size_t gla_bwd_flag_offset(const GlaShape& s) {
   const size_t BH = (size_t)s.B * s.H;

@@ -897,6 +897,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           write_part(se_lb);
         }
         __syncthreads();
+        if (tid == 0) lb_raise(p.lb_flag + (long)gridDim.x + slot0 + seg, p.lb_tag);  // done
       }
 
       // ---- dq, dk, q.dq - k.dk (staged as soon as each (row tile, key tile) pair is done:
@@ -1122,18 +1123,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       p.seg_lg[((long)bh * p.nseg + seg) * dk + c] = sLg[c];
   }
   if constexpr (LB) {
-    // the last workgroup: once every flag is up, d_norm_w = the partials added in a fixed
-    // order (parts strided over NG groups per column, then the groups in order)
+    // the last workgroup: once every workgroup is done with its waits (each had published
+    // before), d_norm_w = the partials added in a fixed order (parts strided over NG groups per
+    // column, then the groups in order), and the flags are cleared for the next launch
+    if (blockIdx.x == gridDim.x - 1) {
+      const int nparts = (int)gridDim.x;
+      lb_wait_each(p.lb_flag + nparts, nparts, p.lb_tag, tid, NTH);
+      __syncthreads();
+      for (int i = tid; i < 2 * nparts; i += NTH) lb_raise(p.lb_flag + i, 0u);
+    }
     if (p.d_norm_w && blockIdx.x == gridDim.x - 1) {
       const int nparts = (int)gridDim.x;
-      for (int i = tid; i < nparts; i += NTH) {
-        unsigned spins = 0;
-        while (__hip_atomic_load(p.lb_flag + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-                   p.lb_tag &&
-               ++spins < kLbSpinLimit)
-          __builtin_amdgcn_s_sleep(1);
-      }
-      __syncthreads();
       constexpr int NG = NTH / DVP < NW ? NTH / DVP : NW;
       const int g = tid / DVP, e = tid - g * DVP;
       if (g < NG && e < dv) {

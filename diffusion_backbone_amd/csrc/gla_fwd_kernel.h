@@ -615,6 +615,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         }
       }
       __syncthreads();
+      if (tid == 0) lb_raise(p.lb_flag + (long)gridDim.x + slot0 + seg, p.lb_tag);  // done
     }
     if (emit && wave < NT) {
       const int I = wave;
@@ -667,6 +668,16 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
             make_float4(rstd[0], rstd[1], rstd[2], rstd[3]);
     }
     __syncthreads();  // every read of the staging slot and of S^T is done
+  }
+  if constexpr (LB) {
+    // the last workgroup: once every workgroup is done with its waits, clear the flags for
+    // the next launch
+    if (blockIdx.x == gridDim.x - 1) {
+      const int n = (int)gridDim.x;
+      lb_wait_each(p.lb_flag + n, n, p.lb_tag, tid, NTH);
+      __syncthreads();
+      for (int i = tid; i < 2 * n; i += NTH) lb_raise(p.lb_flag + i, 0u);
+    }
   }
 
   if (!OUT) {

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import TOL, announce, gla_backward, gla_forward, has_gpu, maxrel, to_f64
+from gpu_util import (TOL, announce, gla_backward, gla_forward, has_gpu, maxrel, nbytes_buf,
+                      to_dev, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
@@ -168,6 +169,74 @@ def test_fwd_lookback_workspace_reuse():
     fa2 = gla_forward(a, 64, want_saved=True, ws=ws)
     _check_fwd(a, fa2, TOL["bf16"], what="third call")
     assert np.array_equal(to_f64(fa["y"]), to_f64(fa2["y"]))
+
+
+def test_lookback_graph_replay():
+    """dig_gla_fwd + dig_gla_bwd captured once in a HIP graph (the same look-back tag on every
+    replay) and replayed over new inputs, with eager work and synchronisation between the
+    replays: each replay must give the eager call's bits for the same inputs (each launch
+    clears its flags, so a replay never meets flags raised by an earlier one)."""
+    import torch
+    import diffusion_backbone_amd as dig
+    announce("look-back fwd+bwd graph replay")
+    cfg = W.CONFIGS["dig_s2_256"]
+    cases = [W.make_gla_case(cfg, seed=sd, batch=4, seq_len=256, random_gamma=True)
+             for sd in (11, 12, 13, 11)]
+    c0 = cases[0]
+    B, L, H, dk = c0.q.shape
+    dv = c0.v.shape[-1]
+    desc = dig.make_desc(B, L, H, dk, dv, 64, 16.0, 1.0, 1e-5, "bf16", 0)
+    names = ("q", "k", "v", "z", "r", "dy")
+    inp = {n: to_dev(getattr(c0, n), "bf16") for n in names}
+    gam = torch.from_numpy(c0.gamma.astype(np.float32)).cuda()
+    y = torch.empty(B, L, H, dv, dtype=torch.bfloat16, device="cuda")
+    saved = nbytes_buf(dig.dig_gla_saved_bytes(desc))
+    fwb, bwb = dig.dig_gla_fwd_workspace_bytes(desc), dig.dig_gla_bwd_workspace_bytes(desc)
+    fws, bws = nbytes_buf(fwb), nbytes_buf(bwb)
+    grads = {n: torch.empty(B, L, H, dk, dtype=torch.bfloat16, device="cuda") for n in ("dq", "dk", "dz")}
+    grads.update({n: torch.empty(B, L, H, dv, dtype=torch.bfloat16, device="cuda") for n in ("dv", "dr")})
+    dgm = torch.empty(dv, device="cuda")
+
+    def step():
+        dig.dig_gla_fwd(desc, inp["q"], inp["k"], inp["v"], inp["z"], inp["r"], gam, y, None,
+                        saved, fws, fwb)
+        dig.dig_gla_bwd(desc, inp["q"], inp["k"], inp["v"], inp["z"], inp["r"], gam, inp["dy"],
+                        saved, grads["dq"], grads["dk"], grads["dv"], grads["dz"], grads["dr"],
+                        dgm, bws, bwb)
+
+    def load(case):
+        for n in names:
+            inp[n].copy_(to_dev(getattr(case, n), "bf16"))
+        gam.copy_(torch.from_numpy(case.gamma.astype(np.float32)))
+
+    def outputs():
+        return [to_f64(y)] + [to_f64(grads[n]) for n in GRADS] + [dgm.cpu().numpy().copy()]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i, case in enumerate(cases):
+        load(case)
+        step()                      # eager reference for these inputs
+        torch.cuda.synchronize()
+        want = outputs()
+        y.fill_(float("nan"))
+        dgm.fill_(float("nan"))
+        for n in GRADS:
+            grads[n].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outputs()
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), "replay %d differs from the eager call" % i
+    _check_fwd(cases[-1], {"y": y}, TOL["bf16"], what="last replay")
 
 
 def test_fwd_config_dig_s2_256_full():
