@@ -127,7 +127,9 @@ size_t dig_gla_bwd_workspace_bytes(const dig_gla_desc* desc);
  * order, so repeated calls give identical bits.  Sequences of 2..8 chunks whose chunks all
  * fit one round of workgroups (batch * heads * chunks <= 256) run as one launch in which
  * each chunk's workgroup reads the later chunks' gradient contributions through flags in
- * the workspace (bounded waits; the flags carry a per-call tag).
+ * the workspace (bounded waits; the flags carry a per-call tag and every launch clears
+ * them before it ends, so a call captured in a HIP graph may be replayed).  dig_gla_fwd
+ * does the same for the state entering each chunk (exact head shapes 32/64, 36/72, 16/32).
  */
 dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, const void* v,
                        const void* gate_logit, const void* r, const float* norm_w,
