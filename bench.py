@@ -175,13 +175,13 @@ class EventTimer:
 TRAFFIC = {
     "workload": "dig_s2_256",
     "bytes": {
-        # FETCH_SIZE 8115.4 KiB / 0.50006 (copy: 131088.1 KiB read per 262144 KiB moved) +
-        # WRITE_SIZE 6990.2 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 23776381,
-        # FETCH_SIZE 7402.7 KiB / 0.50006 + WRITE_SIZE 4656.0 KiB / 1.0
-        "dig_gla_fwd": 19926597,
+        # FETCH_SIZE 8118.8 KiB / 0.50006 (copy: 131087.9 KiB read per 262144 KiB moved) +
+        # WRITE_SIZE 6997.8 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
+        "dig_gla_bwd": 23791021,
+        # FETCH_SIZE 5145.6 KiB / 0.50006 + WRITE_SIZE 6229.5 KiB / 1.0
+        "dig_gla_fwd": 16915945,
     },
-    "sources_sha256": "65baaf6db75c289a5e93807a649761765068d1814bfd16b2c4650754e5f6e3c6",
+    "sources_sha256": "112808d8113af1ca98880fca12b02a66c7a5ea60a005e481ff0e8310f17d1f07",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
@@ -194,7 +194,7 @@ TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
 # tokens per image and head).
 KERNEL_OF_CALL = {
     "gla_bwd": "gla_bwd_kernel, look-back (one chunk per workgroup, one launch)",
-    "gla_fwd": "gla_fwd_kernel, in-workgroup prefix (one launch)",
+    "gla_fwd": "gla_fwd_kernel, look-back (one chunk per workgroup, one launch)",
 }
 
 
