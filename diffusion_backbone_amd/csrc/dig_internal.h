@@ -55,7 +55,9 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
 int gla_fwd_lds_bytes(const GlaShape& s);
 size_t gla_states_bytes(const GlaShape& s);
 // The forward->backward buffer: chunk states, then the normalised output ō of every token
-// (bf16/fp32 as the I/O, [B*H][NC][C/16][NDV] 16 x 16 tiles in MFMA fragment order, NDV =
+// (fp32 whatever the I/O type: dO = rstd (dn - o rstd mean(dn . o rstd)) must stay orthogonal
+// to o to fp32 precision, or dO . v at the first token, where o is parallel to v, loses its
+// cancellation; [B*H][NC][C/16][NDV] 16 x 16 tiles in MFMA fragment order, NDV =
 // ceil(d_v/16)), then the rows' rsqrt(mean o^2 + eps) (fp32 [B*H][NC][C]); offsets 256-aligned.
 size_t gla_saved_bytes(const GlaShape& s);
 size_t gla_saved_obar_offset(const GlaShape& s);

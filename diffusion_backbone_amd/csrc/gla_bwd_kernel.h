@@ -330,11 +330,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   // the look-back's single chunk: its saved o rstd and rstd are loaded with its rows (where
   // a wave holds one state tile: with two, the registers are not there)
   constexpr bool LBPF = LB && STW == 1;
-  Quad<T> obr_lb[LBPF ? RNDVH : 1];
+  Quad<float> obr_lb[LBPF ? RNDVH : 1];
   float4 rsv_lb = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (LBPF) {
     const int I = wave % NT, E0 = (wave / NT) * RNDVH;
-    const Quad<T>* ob = static_cast<const Quad<T>*>(p.obar) + ((sbase + n_top - 1) * NT + I) * NDV * 64 + lane;
+    const Quad<float>* ob = static_cast<const Quad<float>*>(p.obar) + ((sbase + n_top - 1) * NT + I) * NDV * 64 + lane;
 #pragma unroll
     for (int Eh = 0; Eh < RNDVH; ++Eh) obr_lb[Eh] = ob[min(E0 + Eh, NDV - 1) * 64];
     rsv_lb = *reinterpret_cast<const float4*>(p.rstd + (sbase + n_top - 1) * C + 16 * I + 4 * g4);
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     float dgw = 0.f;
     // the passes that form dO: this chunk's normalised output o rstd and rstd as the forward
     // saved them (the recompute phase's row tile I, value tiles E0.. of half hh)
-    Quad<T> obr[RD ? 1 : RNDVH];
+    Quad<float> obr[RD ? 1 : RNDVH];
     float4 rsv = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (LBPF) {
 #pragma unroll
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       rsv = rsv_lb;
     } else if constexpr (!RD) {
       const int I = wave % NT, E0 = (wave / NT) * RNDVH;
-      const Quad<T>* ob = static_cast<const Quad<T>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane;
+      const Quad<float>* ob = static_cast<const Quad<float>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane;
 #pragma unroll
       for (int Eh = 0; Eh < RNDVH; ++Eh) obr[Eh] = ob[min(E0 + Eh, NDV - 1) * 64];
       rsv = *reinterpret_cast<const float4*>(p.rstd + (sbase + n) * C + 16 * I + 4 * g4);
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[Eh][i] = to_f(obr[Eh].v[i]);
+        for (int i = 0; i < 4; ++i) oacc[Eh][i] = obr[Eh].v[i];
 
       // output-stage backward: r, dy first (one LDS round trip); value tiles past this
       // half's range (an odd tile count) count as zero columns

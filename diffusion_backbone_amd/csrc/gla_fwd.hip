@@ -82,7 +82,7 @@ size_t gla_states_bytes(const GlaShape& s) {
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 size_t gla_saved_obar_offset(const GlaShape& s) { return al256(gla_states_bytes(s)); }
 size_t gla_saved_rstd_offset(const GlaShape& s) {
-  const size_t ob = (size_t)s.B * s.H * s.NC * s.C * 16 * s.ndv * (s.bf16 ? 2 : 4);
+  const size_t ob = (size_t)s.B * s.H * s.NC * s.C * 16 * s.ndv * sizeof(float);
   return gla_saved_obar_offset(s) + al256(ob);
 }
 size_t gla_saved_bytes(const GlaShape& s) {

@@ -642,18 +642,18 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
 #pragma unroll
       for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) / (float)dv + p.eps);
       // y, and for the backward (when saved) o rstd in fragment order and rstd per row
-      Quad<T>* ob = p.obar ? static_cast<Quad<T>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane
+      Quad<float>* ob = p.obar ? static_cast<Quad<float>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane
                            : nullptr;
 #pragma unroll
       for (int E = 0; E < NDV; ++E) {
         const int e = E * 16 + r16;
-        Quad<T> q4;
+        Quad<float> q4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * I + 4 * g4 + i;
           const float o = oacc[E][i];
           const float nv = o * rstd[i];
-          q4.v[i] = from_f<T>(nv);
+          q4.v[i] = nv;
           if ((FULLV || e < dv) && row < valid) {
             const float rv = to_f(rr[E][i]);
             const long off = (row0 + (long)row * H) * dv + e;

@@ -87,9 +87,9 @@ typedef struct {
 /*
  * Bytes of the forward->backward buffer `saved` (opaque to the caller; each region starts
  * 256-byte aligned): the fp32 state entering every chunk, [B][H][ceil(L/chunk)][d_k][d_v];
- * the normalised output o * rsqrt(mean o^2 + eps) of every token in the I/O dtype, as
- * 16 x 16 (token x value) tiles over d_v rounded up to 16; the fp32 rsqrt(mean o^2 + eps) of
- * every token.  0 for an invalid descriptor.
+ * the normalised output o * rsqrt(mean o^2 + eps) of every token in fp32 (the backward's
+ * RMSNorm gradient cancels against it), as 16 x 16 (token x value) tiles over d_v rounded up
+ * to 16; the fp32 rsqrt(mean o^2 + eps) of every token.  0 for an invalid descriptor.
  */
 size_t dig_gla_saved_bytes(const dig_gla_desc* desc);
 

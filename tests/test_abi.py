@@ -95,7 +95,7 @@ def test_sizes_match_layout():
     nchunks = (1000 + 63) // 64
     a256 = lambda x: (x + 255) // 256 * 256
     states = 1 * 16 * nchunks * 36 * 72 * 4             # fp32 state entering each chunk
-    obar = 1 * 16 * nchunks * 64 * 80 * 2               # normalised output, 16-wide d_v tiles
+    obar = 1 * 16 * nchunks * 64 * 80 * 4               # normalised output (fp32), 16-wide d_v tiles
     rstd = 1 * 16 * nchunks * 64 * 4                    # per-row rsqrt(mean o^2 + eps)
     assert dig.dig_gla_saved_bytes(d) == a256(states) + a256(obar) + a256(rstd)
     assert dig.dig_gla_bwd_workspace_bytes(d) > 0

@@ -171,6 +171,19 @@ def test_fwd_lookback_workspace_reuse():
     assert np.array_equal(to_f64(fa["y"]), to_f64(fa2["y"]))
 
 
+@pytest.mark.parametrize("batch,seq_len", [
+    (16, 512),   # 2 heads x 8 chunks x 16 images = 256 workgroups: the largest look-back grid
+    (17, 512),   # 272: one past it (segments and a scan instead)
+    (1, 577),    # 10 chunks: past the look-back's longest sequence
+])
+def test_lookback_plan_boundary(batch, seq_len):
+    announce("look-back plan boundary B=%d L=%d" % (batch, seq_len))
+    case = _case("tiny_f32", batch=batch, seq_len=seq_len, dtype="bf16", random_gamma=True)
+    f = gla_forward(case, 64, want_saved=True)
+    _check_fwd(case, f, TOL["bf16"])
+    _check_bwd(case, gla_backward(case, f), TOL["bf16"])
+
+
 def test_lookback_graph_replay():
     """dig_gla_fwd + dig_gla_bwd captured once in a HIP graph (the same look-back tag on every
     replay) and replayed over new inputs, with eager work and synchronisation between the
