@@ -175,13 +175,13 @@ class EventTimer:
 TRAFFIC = {
     "workload": "dig_s2_256",
     "bytes": {
-        # FETCH_SIZE 8118.8 KiB / 0.50006 (copy: 131087.9 KiB read per 262144 KiB moved) +
+        # FETCH_SIZE 8886.1 KiB / 0.50006 (copy: 131088.0 KiB read per 262144 KiB moved) +
         # WRITE_SIZE 6997.8 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 23791021,
-        # FETCH_SIZE 5145.6 KiB / 0.50006 + WRITE_SIZE 6229.5 KiB / 1.0
-        "dig_gla_fwd": 16915945,
+        "dig_gla_bwd": 25362253,
+        # FETCH_SIZE 5145.2 KiB / 0.50006 + WRITE_SIZE 7765.5 KiB / 1.0
+        "dig_gla_fwd": 18487983,
     },
-    "sources_sha256": "112808d8113af1ca98880fca12b02a66c7a5ea60a005e481ff0e8310f17d1f07",
+    "sources_sha256": "834f09c8cae3003b695a888b3be3d3f76831e6e85b8238bc8e8beeea36dc9391",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
