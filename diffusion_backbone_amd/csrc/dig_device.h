@@ -154,6 +154,90 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ------------------------------------------------- split-precision operands on bf16 MFMA
+// An fp32 operand x is carried as x_hi + x_lo, x_hi = bf16(x), x_lo = bf16(x - x_hi) (the
+// difference is exact in fp32).  The pair holds about 16 significant bits, so a product
+// accumulated as A_hi B_hi + A_hi B_lo + A_lo B_hi on the bf16 matrix cores is accurate to
+// about 2^-16 of each term (the dropped A_lo B_lo is below that), against 2^-8 with one bf16
+// rounding per operand.
+struct SplitFrag {
+  bf16x8 hi, lo;
+};
+
+// Split fragment of row `row`, columns k..k+7 (k a multiple of 8) of a K-contiguous fp32 tile
+// with COLS stored columns (a multiple of 4) at pitch LD floats (a multiple of 4).  Columns at
+// or past COLS read as zero; FULL asserts that k + 8 <= COLS for every lane.  Both 16-byte
+// reads are always issued (from a clamped address where masked): no branch around them.
+template <int COLS, int LD, bool FULL>
+__device__ __forceinline__ SplitFrag split_frag(const float* base, int row, int k) {
+  static_assert(COLS % 4 == 0 && LD % 4 == 0 && COLS <= LD, "fp32 tile layout");
+  float x[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = k + 4 * h;
+    const bool in = FULL || c + 4 <= COLS;
+    const float4 v = *reinterpret_cast<const float4*>(base + row * LD + (in ? c : COLS - 4));
+    x[4 * h + 0] = in ? v.x : 0.f;
+    x[4 * h + 1] = in ? v.y : 0.f;
+    x[4 * h + 2] = in ? v.z : 0.f;
+    x[4 * h + 3] = in ? v.w : 0.f;
+  }
+  SplitFrag f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16 hi = from_f<bf16>(x[i]);
+    f.hi[i] = hi;
+    f.lo[i] = from_f<bf16>(x[i] - to_f(hi));
+  }
+  return f;
+}
+
+// acc += A B over one 32-wide K step from split operands (lo products first).
+__device__ __forceinline__ f32x4 mfma_split(const SplitFrag& a, const SplitFrag& b, f32x4 acc) {
+  acc = mfma_bf16(a.lo, b.hi, acc);
+  acc = mfma_bf16(a.hi, b.lo, acc);
+  return mfma_bf16(a.hi, b.hi, acc);
+}
+
+// acc(m, n) += sum_k A(m0 + m, k) B(n0 + n, k) over the COLS stored columns of two K-contiguous
+// fp32 tiles (pitches LDA, LDB floats), both split into hi + lo bf16 parts.
+template <int COLS, int LDA, int LDB>
+__device__ __forceinline__ f32x4 mm_split(f32x4 acc, const float* A, int m0, const float* B,
+                                          int n0, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  acc = mfma_split(split_frag<COLS, LDA, (32 <= COLS)>(A, m0 + r, 8 * g),
+                   split_frag<COLS, LDB, (32 <= COLS)>(B, n0 + r, 8 * g), acc);
+  if constexpr (COLS > 32)
+    acc = mfma_split(split_frag<COLS, LDA, (64 <= COLS)>(A, m0 + r, 32 + 8 * g),
+                     split_frag<COLS, LDB, (64 <= COLS)>(B, n0 + r, 32 + 8 * g), acc);
+  static_assert(COLS <= 64, "two K steps");
+  return acc;
+}
+
+// The same with a bf16 K-contiguous B tile (pitch LDB elements): A enters as hi + lo parts, B as
+// stored.  A lane group whose first column lies past COLS takes B as zero (its A part is zero);
+// one whose first column lies inside reads eight B columns, so rows of B must hold
+// (COLS + 7) / 8 * 8 readable, finite columns.
+template <int COLS, int LDA, int LDB>
+__device__ __forceinline__ f32x4 mm_split_b(f32x4 acc, const float* A, int m0, const bf16* B,
+                                            int n0, int lane) {
+  static_assert(COLS <= 64 && (COLS + 7) / 8 * 8 <= LDB, "bf16 operand rows");
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < (COLS + 31) / 32; ++s) {
+    const int k = 32 * s + 8 * g;
+    const bool in = k < COLS;
+    bf16x8 b = *reinterpret_cast<const bf16x8*>(B + (n0 + r) * LDB + (in ? k : 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = in ? b[i] : from_f<bf16>(0.f);
+    const SplitFrag a = s == 0 ? split_frag<COLS, LDA, (32 <= COLS)>(A, m0 + r, k)
+                               : split_frag<COLS, LDA, (64 <= COLS)>(A, m0 + r, k);
+    acc = mfma_bf16(a.lo, b, acc);
+    acc = mfma_bf16(a.hi, b, acc);
+  }
+  return acc;
+}
+
 // The same value, opaque to the optimiser (an empty asm statement that claims to modify the
 // register; no instruction is emitted).  Deriving a loop body's lane-dependent LDS addresses
 // from it keeps them from being hoisted out of the loop, where hundreds of them would stay

@@ -58,13 +58,18 @@ struct BwdLayout {
   static constexpr int DKP = 16 * NDK, DVP = 16 * NDV;           // contraction pads (K 16)
   static constexpr int QP = DKP + 8, VP = DVP + 8, TP = C + 8;    // padded row pitches
   static constexpr int NCL = DKP * C / (64 * NW), NEL = DVP * C / (64 * NW);  // gate columns
+  // the row layouts of q e^{b}, k e^{-b} are fp32 for either element type (bf16 I/O splits
+  // them into hi + lo bf16 fragments for the gated Q K^T): QKC stored columns (d_k rounded up
+  // to 4) at pitch QKP floats; the transposed copies are of the element type
+  static constexpr int QKC = SZ == 2 ? (DK + 3) / 4 * 4 : DKP;
+  static constexpr int QKP = SZ == 2 ? (QKC % 32 == 0 ? QKC + 4 : QKC) : QP;
   static constexpr int KPE = PAD ? row_pitch(DK * SZ, NCL * SZ) / SZ : DK;  // raw k pitch
   static constexpr int VPE = PAD ? row_pitch(DV * SZ, NEL * SZ) / SZ : DV;  // raw v pitch
   static constexpr int DKB = DK % 2 ? DK : DK + 1;                // fp32 row pitch (odd)
   // row layouts [token][dim]
-  static constexpr int O_Q = 0;                                          // q e^{b}   [C][QP]
-  static constexpr int O_K = O_Q + bal16(C * QP * SZ);                   // k e^{-b}  [C][QP]
-  static constexpr int O_V = O_K + bal16(C * QP * SZ);                   // v         [C][VP]
+  static constexpr int O_Q = 0;                                          // q e^{b}  [C][QKP]
+  static constexpr int O_K = O_Q + bal16(C * QKP * 4);                   // k e^{-b} [C][QKP]
+  static constexpr int O_V = O_K + bal16(C * QKP * 4);                   // v         [C][VP]
   static constexpr int O_DO = O_V + bal16(C * VP * SZ);                  // dO        [C][VP]
   static constexpr int O_S0 = O_DO + bal16(LEAN ? 0 : C * VP * SZ);      // S0      [DKP][VP]
   static constexpr int O_D = O_S0 + bal16(LEAN ? 0 : DKP * VP * SZ);     // dO V^T    [C][TP]
@@ -158,6 +163,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP;
   constexpr int QP = Lo::QP, VP = Lo::VP, TP = Lo::TP;
+  constexpr int QKC = Lo::QKC, QKP = Lo::QKP;  // fp32 q e^{b}, k e^{-b} row tiles
   constexpr int NT = C / 16;
   constexpr int NST = NDK * NDV, STW = (NST + NW - 1) / NW;
   constexpr int NPAIR = NT * NDK, PRW = (NPAIR + NW - 1) / NW;  // dq/dk (row tile, key tile)
@@ -166,6 +172,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr int NEL = DVP * C / NTH;                         // gate: value columns per lane
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
+  static_assert(QKC % NCL == 0 || QKC >= DKP, "gate column runs end at the stored columns");
   using Acc = typename std::conditional<kBf, float, double>::type;
   constexpr int RNDVH = (NDV + bwd_spl<C, NW>() - 1) / bwd_spl<C, NW>();  // reuse fragments
 
@@ -182,8 +189,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   const int H = p.H;
   const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
 
-  T* sQ = reinterpret_cast<T*>(smem + Lo::O_Q);
-  T* sK = reinterpret_cast<T*>(smem + Lo::O_K);
+  float* sQ = reinterpret_cast<float*>(smem + Lo::O_Q);
+  float* sK = reinterpret_cast<float*>(smem + Lo::O_K);
   T* sV = reinterpret_cast<T*>(smem + Lo::O_V);
   T* sdO = reinterpret_cast<T*>(smem + Lo::O_DO);
   T* sS0 = reinterpret_cast<T*>(smem + Lo::O_S0);
@@ -507,19 +514,24 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
 #pragma unroll
       for (int j = 0; j < NCL; ++j) bl[j] = group_last<C>(bb[j], lane);
+      float qf[NCL], kf[NCL];
       T qs[NCL], ks[NCL];
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
-        qs[j] = from_f<T>(to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]));
-        ks[j] = from_f<T>(to_f(kr[j]) * Fm<T>::exp2(-bb[j]));
+        qf[j] = to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]);
+        kf[j] = to_f(kr[j]) * Fm<T>::exp2(-bb[j]);
+        qs[j] = from_f<T>(qf[j]);
+        ks[j] = from_f<T>(kf[j]);
       }
       float md = 0.f;
 #pragma unroll
       for (int j = 0; j < NCL; ++j) md = fmaxf(md, -bl[j]);
       md = wave_max_dpp(md);
 
-      lds_row_write<T, NCL>(sQ + tg * QP, c0, qs);
-      lds_row_write<T, NCL>(sK + tg * QP, c0, ks);
+      if (c0 < QKC) {  // a lane's column run lies wholly inside or past the stored columns
+        lds_row_write<float, NCL>(sQ + tg * QKP, c0, qf);
+        lds_row_write<float, NCL>(sK + tg * QKP, c0, kf);
+      }
       lds_row_write<T, NEL>(sV + tg * VP, e0, vr);
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
@@ -621,9 +633,15 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         diag = ir < valid ? (float)acc * p.q_scale : 0.f;
       }
       if (!slow) {
+        // bf16 I/O: split operands (dv takes P_ij times do_i, which is large where rstd_i is,
+        // so P_ij is needed to the accuracy of its own magnitude there)
 #pragma unroll
-        for (int J = 0; J < NT; ++J)
-          pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
+        for (int J = 0; J < NT; ++J) {
+          if constexpr (kBf)
+            pt[J] = J <= I ? mm_split<QKC, QKP, QKP>(zero4(), sK, 16 * J, sQ, 16 * I, lane) : zero4();
+          else
+            pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QKP, 16 * J, sQ, QKP, 16 * I, DKP, lane) : zero4();
+        }
       } else {
         const T* sPw = sSlow + I * 16 * C;
 #pragma unroll
@@ -967,7 +985,10 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           f32x4 dva = Mma<T>::kc(zero4(), sPt, TP, 16 * J, sdOt, TP, 16 * et, C, lane);
           const int e = et * 16 + r16;
           if (!slow) {
-            dva = Mma<T>::kc(dva, sK, QP, 16 * J, sGt, QP, 16 * et, DKP, lane);
+            if constexpr (kBf)
+              dva = mm_split_b<QKC, QKP, QP>(dva, sK, 16 * J, sGt, 16 * et, lane);
+            else
+              dva = Mma<T>::kc(dva, sK, QKP, 16 * J, sGt, QP, 16 * et, DKP, lane);
           } else {  // k_j e^{b_last - b_j} G elementwise (no overflow)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

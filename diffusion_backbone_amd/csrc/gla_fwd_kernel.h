@@ -59,15 +59,20 @@ struct FwdLayout {
   // gate columns per lane: the key columns up to the last 16-wide tile (the K-step padding
   // past it stays zero and is never touched), the value columns
   static constexpr int NCL = 16 * NDK * C / (64 * NW), NEL = DVP * C / (64 * NW);
+  // q e^{b} and k e^{-b} are kept in fp32 for either element type (bf16 I/O splits them into
+  // hi + lo bf16 fragments for the gated Q K^T): QKC stored columns (the true d_k for exact
+  // head shapes, the 16-wide tile class otherwise) at pitch QKP floats
+  static constexpr int QKC = SZ == 2 ? (PAD ? (DK + 3) / 4 * 4 : 16 * NDK) : DKP;
+  static constexpr int QKP = SZ == 2 ? (QKC % 32 == 0 ? QKC + 4 : QKC) : QP;
   // byte offsets: operands, state copy, gates, misc; the raw staging slots come last
-  static constexpr int O_Q = 0;                                         // q e^{b}  [C][QP]
-  static constexpr int O_K = O_Q + al16(OUT ? C * QP * SZ : 0);          // k e^{-b} [C][QP]
-  static constexpr int O_KBT = O_K + al16(OUT ? C * QP * SZ : 0);        // kbar^T [16NDK][TP]
+  static constexpr int O_Q = 0;                                         // q e^{b}  [C][QKP]
+  static constexpr int O_K = O_Q + al16(OUT ? C * QKP * 4 : 0);          // k e^{-b} [C][QKP]
+  static constexpr int O_KBT = O_K + al16(OUT ? C * QKP * 4 : 0);        // kbar^T [16NDK][TP]
   static constexpr int O_VT = O_KBT + al16(16 * NDK * TP * SZ);          // v^T    [DVP][TP]
   static constexpr int O_S = O_VT + al16(DVP * TP * SZ);                 // S^T    [DVP][QP]
   // b fp32 [C][DK], written only for strong-decay chunks, which do not read k e^{-b}: it
   // takes that tile's place when it fits there
-  static constexpr bool B_IN_K = C * DK * 4 <= C * QP * SZ;
+  static constexpr bool B_IN_K = C * DK * 4 <= C * QKP * 4;
   static constexpr int O_B = B_IN_K ? O_K : O_S + al16(OUT ? DVP * QP * SZ : 0);
   static constexpr int O_GAM = O_S + al16(OUT ? DVP * QP * SZ : 0) +
                                al16(OUT && !B_IN_K ? C * DK * 4 : 0);  // e^{b_last} [DKP]
@@ -114,6 +119,8 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
   constexpr int QP = Lo::QP, TP = Lo::TP;
+  constexpr int QKC = Lo::QKC, QKP = Lo::QKP;  // fp32 q e^{b}, k e^{-b} tiles
+  constexpr int NKS = DKP / 32;                 // bf16 K steps over the key dim
   constexpr int NT = C / 16;                            // query row tiles
   constexpr int NST = NDK * NDV;                        // fp32 state tiles
   // state tiles are owned by waves SW0..NW-1: the waves past the query row tiles when there
@@ -125,6 +132,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   // every gate/transpose column is a real one: no per-column guards
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
+  static_assert(QKC % NCL == 0 || QKC >= 16 * NDK, "gate column runs end at the stored columns");
   using Acc = typename std::conditional<kBf, float, double>::type;
   constexpr bool PF = EXACT;  // register prefetch (one staging slot) for exact head shapes
 
@@ -138,8 +146,8 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   const int H = p.H;
   const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
 
-  T* sQ = reinterpret_cast<T*>(smem + Lo::O_Q);
-  T* sK = reinterpret_cast<T*>(smem + Lo::O_K);
+  float* sQ = reinterpret_cast<float*>(smem + Lo::O_Q);
+  float* sK = reinterpret_cast<float*>(smem + Lo::O_K);
   T* sKbT = reinterpret_cast<T*>(smem + Lo::O_KBT);
   T* sVt = reinterpret_cast<T*>(smem + Lo::O_VT);
   T* sS = reinterpret_cast<T*>(smem + Lo::O_S);
@@ -243,6 +251,38 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     const int e = E * 16 + r16;
     gm[E] = (OUT && e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
   }
+  // bf16 I/O: split fragments of q e^{b}, rows 16I.. (the B operand of the gated K Q^T tiles
+  // and the A operand of (q e^{b}) S0 share the lane layout: row = lane % 16, K slice 8g)
+  auto q_frags = [&](SplitFrag (&qf)[NKS], int I) {
+    const int l = opaque(tid & 63);
+    qf[0] = split_frag<QKC, QKP, (32 <= QKC)>(sQ, 16 * I + (l & 15), 8 * (l >> 4));
+    if constexpr (NKS > 1)
+      qf[1] = split_frag<QKC, QKP, (64 <= QKC)>(sQ, 16 * I + (l & 15), 32 + 8 * (l >> 4));
+  };
+  // oacc += (q e^{b}) S0 for query rows 16I..: S0 is the bf16 copy in sS; q e^{b} enters as
+  // hi + lo parts (bf16 I/O)
+  auto q_s0 = [&](f32x4 (&oacc)[NDV], int I) {
+    const int l = opaque(tid & 63);
+    if constexpr (kBf) {
+      SplitFrag qf[NKS];
+      q_frags(qf, I);
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 sb = Mma<bf16>::frag<true>(reinterpret_cast<const bf16*>(sS), QP,
+                                                  16 * E + (l & 15), 32 * s + 8 * (l >> 4));
+          oacc[E] = mfma_bf16(qf[s].lo, sb, oacc[E]);
+          oacc[E] = mfma_bf16(qf[s].hi, sb, oacc[E]);
+        }
+    } else {
+#pragma unroll
+      for (int E = 0; E < NDV; ++E)
+        oacc[E] = Mma<T>::kc(oacc[E], sQ, QKP, 16 * I, sS, QP, 16 * E, DKP, l);
+    }
+  };
+  static_assert(NKS >= 1 && NKS <= 2, "key dim up to 64");
+
   // Every load above (and the first chunk's rows) has landed before the loop: otherwise the
   // compiler's wait for them, placed inside the loop, would also wait for the prefetch.
   if constexpr (PF) dma_wait();
@@ -343,14 +383,15 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
 #pragma unroll
       for (int j = 0; j < NCL; ++j) bl[j] = group_last<C>(bb[j], lane);
-      T kb[NCL], qs[NCL], ks[NCL];
+      T kb[NCL];
+      float qs[NCL], ks[NCL];
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
         const float kf = to_f(kr[j]);
         kb[j] = from_f<T>(kf * Fm<T>::exp2(bl[j] - bb[j]));
         if (emit) {
-          qs[j] = from_f<T>(to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]));
-          ks[j] = from_f<T>(kf * Fm<T>::exp2(-bb[j]));
+          qs[j] = to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]);
+          ks[j] = kf * Fm<T>::exp2(-bb[j]);
         }
       }
       float md = 0.f;  // strongest decay over this wave's columns -> slow-path test
@@ -364,8 +405,10 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
 #pragma unroll
       for (int j = 0; j < NEL; ++j) sVt[(e0 + j) * TP + tg] = vr[j];  // V^T, zero past the end
       if (emit) {
-        lds_row_write<T, NCL>(sQ + tg * QP, c0, qs);
-        lds_row_write<T, NCL>(sK + tg * QP, c0, ks);
+        if (c0 < QKC) {  // a lane's column run lies wholly inside or past the stored columns
+          lds_row_write<float, NCL>(sQ + tg * QKP, c0, qs);
+          lds_row_write<float, NCL>(sK + tg * QKP, c0, ks);
+        }
         if (lane == 0) sMax[wave] = md;
       }
       if (tg == C - 1) {
@@ -457,9 +500,27 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       // P^T tiles: pt[J][i] = P[16I + r16][16J + 4*g4 + i]
       f32x4 pt[NT];
       if (!slow) {
+        if constexpr (kBf) {
+          // split operands: where o_i cancels to a small vector its relative error is that of
+          // these sums, and the RMSNorm gradient magnifies it by rstd_i
+          SplitFrag qf[NKS];
+          q_frags(qf, I);
 #pragma unroll
-        for (int J = 0; J < NT; ++J)
-          pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QP, 16 * J, sQ, QP, 16 * I, DKP, lane) : zero4();
+          for (int J = 0; J < NT; ++J) {
+            pt[J] = zero4();
+            if (J <= I) {
+              pt[J] = mfma_split(split_frag<QKC, QKP, (32 <= QKC)>(sK, 16 * J + r16, 8 * g4),
+                                 qf[0], pt[J]);
+              if constexpr (NKS > 1)
+                pt[J] = mfma_split(split_frag<QKC, QKP, (64 <= QKC)>(sK, 16 * J + r16, 32 + 8 * g4),
+                                   qf[1], pt[J]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int J = 0; J < NT; ++J)
+            pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QKP, 16 * J, sQ, QKP, 16 * I, DKP, lane) : zero4();
+        }
       } else {
         // strong decay: P_ij = sum_c q_ic k_jc 2^{b_ic - b_jc} elementwise (no overflow), each
         // lane its own elements (rare path, kept compact); j > i is masked below
@@ -493,11 +554,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       }
 
       // inter-chunk: O = (q e^{b}) S0 (the look-back adds it once S0 is known)
-      if constexpr (!LB) {
-#pragma unroll
-        for (int E = 0; E < NDV; ++E)
-          oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
-      }
+      if constexpr (!LB) q_s0(oacc, I);
 
       // intra-chunk: O += P V   (P straight from the accumulators above)
       if constexpr (kBf) {
@@ -619,11 +676,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     }
     if (emit && wave < NT) {
       const int I = wave;
-      if constexpr (LB) {
-#pragma unroll
-        for (int E = 0; E < NDV; ++E)
-          oacc[E] = Mma<T>::kc(oacc[E], sQ, QP, 16 * I, sS, QP, 16 * E, DKP, lane);
-      }
+      if constexpr (LB) q_s0(oacc, I);
       // output stage: head-wise RMSNorm x weight x Swish(r), stored from the accumulators
       T rr[NDV][4];  // all of this lane's r first (one LDS round trip)
 #pragma unroll
