@@ -26,7 +26,7 @@ EXPORTS = (
     "dig_gla_saved_bytes", "dig_gla_fwd_workspace_bytes", "dig_gla_fwd",
     "dig_gla_bwd_workspace_bytes", "dig_gla_bwd", "dig_srem_reorient", "dig_dwconv3x3",
     "dig_dwconv3x3_bwd_workspace_bytes", "dig_dwconv3x3_bwd", "dig_status_str",
-    "dig_last_error", "dig_abi_version",
+    "dig_last_error", "dig_abi_version", "dig_lookback_status", "dig_debug_lookback",
 )
 
 
@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.dig_last_error.argtypes = []
         L.dig_last_error.restype = ctypes.c_char_p
         L.dig_abi_version.restype = I
+        L.dig_lookback_status.argtypes = [P]
+        L.dig_lookback_status.restype = ctypes.c_int
+        L.dig_debug_lookback.argtypes = [ctypes.c_uint32, I]
+        L.dig_debug_lookback.restype = None
         _lib = L
     return _lib
 
@@ -189,3 +193,12 @@ def dig_dwconv3x3_bwd(batch, grid_h, grid_w, channels, dtype, layout, out_layout
 
 def dig_abi_version() -> int:
     return lib().dig_abi_version()
+
+
+def dig_lookback_status(stream=None):
+    """Raises DigError(DIG_ERR_DEVICE) if a look-back wait gave up since the last query."""
+    _check(lib().dig_lookback_status(_stream(stream)), "dig_lookback_status")
+
+
+def dig_debug_lookback(spins: int, never_match: bool):
+    lib().dig_debug_lookback(int(spins), 1 if never_match else 0)

@@ -139,7 +139,28 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 100; }
+int32_t dig_abi_version(void) { return 101; }
+
+dig_status dig_lookback_status(hipStream_t stream) {
+  unsigned* word = dig::lookback_status_word();
+  if (!word) return fail(DIG_ERR_DEVICE, "look-back status word unavailable on this device");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return check_dev(e, "dig_lookback_status: stream synchronize");
+  unsigned v = 0;
+  e = hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return check_dev(e, "dig_lookback_status: read");
+  if (v == 0) return ok();
+  const unsigned zero = 0;
+  e = hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return check_dev(e, "dig_lookback_status: clear");
+  return fail(DIG_ERR_DEVICE,
+              "a look-back wait gave up before the values it waited for arrived; the outputs "
+              "of the affected calls hold NaN");
+}
+
+void dig_debug_lookback(uint32_t spins, int32_t never_match) {
+  dig::set_lookback_wait(spins, never_match != 0);
+}
 
 size_t dig_gla_saved_bytes(const dig_gla_desc* d) {
   dig::GlaShape s;

@@ -199,18 +199,44 @@ __device__ __forceinline__ f32x4 mfma_split(const SplitFrag& a, const SplitFrag&
   return mfma_bf16(a.hi, b.hi, acc);
 }
 
+// A four-column K tail (columns 32..35) packed into one 32-wide step: the three products
+// hi.hi, hi.lo and lo.hi of the four columns take 12 of the step's 32 slots.  Lane group 0
+// holds A = [hi, hi], B = [hi, lo]; lane group 1 A = [lo, 0], B = [hi, 0]; the others zero.
+// TAIL_B selects the B role.  (The element index inside a lane's eight slots is the K index
+// within its group, so A and B only have to agree slot by slot.)
+template <int LD, bool TAIL_B>
+__device__ __forceinline__ bf16x8 tail4_frag(const float* base, int row, int g) {
+  const float4 v = *reinterpret_cast<const float4*>(base + row * LD + 32);
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 hi = from_f<bf16>(x[i]);
+    const bf16 lo = from_f<bf16>(x[i] - to_f(hi));
+    const bf16 z = from_f<bf16>(0.f);
+    f[i] = g == 0 ? hi : (g == 1 ? (TAIL_B ? hi : lo) : z);
+    f[4 + i] = g == 0 ? (TAIL_B ? lo : hi) : z;
+  }
+  return f;
+}
+
 // acc(m, n) += sum_k A(m0 + m, k) B(n0 + n, k) over the COLS stored columns of two K-contiguous
 // fp32 tiles (pitches LDA, LDB floats), both split into hi + lo bf16 parts.
 template <int COLS, int LDA, int LDB>
 __device__ __forceinline__ f32x4 mm_split(f32x4 acc, const float* A, int m0, const float* B,
                                           int n0, int lane) {
+  static_assert(COLS <= 64, "two K steps");
   const int r = lane & 15, g = lane >> 4;
+  if constexpr (COLS == 36) {  // 32 columns split, then the packed four-column tail
+    acc = mfma_bf16(tail4_frag<LDA, false>(A, m0 + r, g), tail4_frag<LDB, true>(B, n0 + r, g), acc);
+    return mfma_split(split_frag<COLS, LDA, true>(A, m0 + r, 8 * g),
+                      split_frag<COLS, LDB, true>(B, n0 + r, 8 * g), acc);
+  }
   acc = mfma_split(split_frag<COLS, LDA, (32 <= COLS)>(A, m0 + r, 8 * g),
                    split_frag<COLS, LDB, (32 <= COLS)>(B, n0 + r, 8 * g), acc);
   if constexpr (COLS > 32)
     acc = mfma_split(split_frag<COLS, LDA, (64 <= COLS)>(A, m0 + r, 32 + 8 * g),
                      split_frag<COLS, LDB, (64 <= COLS)>(B, n0 + r, 32 + 8 * g), acc);
-  static_assert(COLS <= 64, "two K steps");
   return acc;
 }
 
@@ -223,8 +249,23 @@ __device__ __forceinline__ f32x4 mm_split_b(f32x4 acc, const float* A, int m0, c
                                             int n0, int lane) {
   static_assert(COLS <= 64 && (COLS + 7) / 8 * 8 <= LDB, "bf16 operand rows");
   const int r = lane & 15, g = lane >> 4;
+  if constexpr (COLS == 36) {  // packed four-column tail: lane group 0 A = [hi, lo], B = [b, b]
+    const float4 v = *reinterpret_cast<const float4*>(A + (m0 + r) * LDA + 32);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(B + (n0 + r) * LDB + 32);
+    bf16x8 a, b;
 #pragma unroll
-  for (int s = 0; s < (COLS + 31) / 32; ++s) {
+    for (int i = 0; i < 4; ++i) {
+      const bf16 hi = from_f<bf16>(x[i]), z = from_f<bf16>(0.f);
+      a[i] = g == 0 ? hi : z;
+      a[4 + i] = g == 0 ? from_f<bf16>(x[i] - to_f(hi)) : z;
+      b[i] = g == 0 ? b4[i] : z;
+      b[4 + i] = g == 0 ? b4[i] : z;
+    }
+    acc = mfma_bf16(a, b, acc);
+  }
+#pragma unroll
+  for (int s = 0; s < (COLS == 36 ? 1 : (COLS + 31) / 32); ++s) {
     const int k = 32 * s + 8 * g;
     const bool in = k < COLS;
     bf16x8 b = *reinterpret_cast<const bf16x8*>(B + (n0 + r) * LDB + (in ? k : 0));
@@ -741,7 +782,7 @@ __device__ __forceinline__ void zero_rows(T* dst, int valid, int rows, int cols,
 // XCD does not hold back; the stores have completed (waited for) before the flag is
 // written, and the values are loaded only after the flag is seen.  No L2 write-back or
 // invalidation is needed (fences would do both, over the whole L2, per wave).
-constexpr unsigned kLbSpinLimit = 1u << 18;  // polls of at least ~1 us: a bound far past any real wait
+constexpr unsigned kLbSpinLimit = 1u << 18;  // default bound: polls of at least ~1 us, far past any real wait
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -756,32 +797,54 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 // the same arguments (the same tag) are replayed, as from a captured graph; the per-call tag
 // covers a workspace that has never been used.
 //
-// Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).
-__device__ __forceinline__ void lb_wait_all(const unsigned* flags, int count, unsigned tag,
-                                            int lane) {
+// Every wait is bounded (spin_limit polls).  A wait that gives up returns true; the caller
+// then records it in the sticky status word (lb_fail) and poisons what the missing values fed
+// with NaN, so that the output is visibly wrong and the host can ask for the status.
+//
+// Waits until flags[0..count) all hold tag (lane j polls flag j; count <= 64).  Returns true
+// on every lane of the wave if any lane gave up.
+__device__ __forceinline__ bool lb_wait_all(const unsigned* flags, int count, unsigned tag,
+                                            int lane, unsigned spin_limit) {
+  bool expired = false;
   if (lane < count) {
     unsigned spins = 0;
     while (__hip_atomic_load(const_cast<unsigned*>(flags + lane), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
-           ++spins < kLbSpinLimit)
+                             __HIP_MEMORY_SCOPE_AGENT) != tag) {
+      if (++spins >= spin_limit) {
+        expired = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
+    }
   }
+  return __any(expired);
 }
 
 // Every thread: waits until flags[0..n) all hold tag, n any size (the workgroup's threads
-// share the flags; a workgroup barrier follows in the caller).
-__device__ __forceinline__ void lb_wait_each(const unsigned* flags, int n, unsigned tag, int tid,
-                                             int nthreads) {
+// share the flags; a workgroup barrier follows in the caller).  Returns true on the threads
+// whose own wait gave up.
+__device__ __forceinline__ bool lb_wait_each(const unsigned* flags, int n, unsigned tag, int tid,
+                                             int nthreads, unsigned spin_limit) {
+  bool expired = false;
   for (int i = tid; i < n; i += nthreads) {
     unsigned spins = 0;
     while (__hip_atomic_load(const_cast<unsigned*>(flags + i), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) != tag &&
-           ++spins < kLbSpinLimit)
+                             __HIP_MEMORY_SCOPE_AGENT) != tag) {
+      if (++spins >= spin_limit) {
+        expired = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
+    }
   }
+  return expired;
 }
 __device__ __forceinline__ void lb_raise(unsigned* flag, unsigned tag) {
   __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Records an expired wait in the sticky status word (kept until the host reads and clears it).
+__device__ __forceinline__ void lb_fail(unsigned* status) {
+  __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace dig

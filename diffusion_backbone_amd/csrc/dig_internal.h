@@ -41,6 +41,9 @@ struct GlaFwdParams {
   float* lb_u;     // look-back: [B*H][NC][dk][dv] each chunk's own state contribution
   unsigned* lb_flag;  // look-back: [2][B*H][NC] chunk published, chunk done (== lb_tag)
   unsigned lb_tag;    // this call's flag value
+  unsigned lb_wait_tag;  // the value the waits look for (lb_tag; another only under test)
+  unsigned lb_spins;     // bound on the polls of one wait
+  unsigned* lb_status;   // sticky status word: set when a wait gives up
   void* obar;      // saved for the backward, or null: normalised o in fragment order
   float* rstd;     // saved for the backward, or null: [B*H][NC][C] RMSNorm reciprocal rms
   int B, L, H, dk, dv, NC, sc, nseg;
@@ -95,6 +98,9 @@ struct GlaBwdParams {
   float* diagws;        // [B*H][NC][2][C] pass A's dO.v diagonals (reuse), or null
   unsigned* lb_flag;    // look-back: [2][B*H][nseg] segment published, segment done (== lb_tag)
   unsigned lb_tag;      // this call's flag value (differs from every earlier call's)
+  unsigned lb_wait_tag; // the value the waits look for (lb_tag; another only under test)
+  unsigned lb_spins;    // bound on the polls of one wait
+  unsigned* lb_status;  // sticky status word: set when a wait gives up
   int B, L, H, dk, dv, NC, sc, nseg;
   float g2scale, inv_tau, q_scale, eps;
 };
@@ -111,6 +117,16 @@ size_t gla_bwd_reuse_diag_offset(const GlaShape& s);
 size_t gla_bwd_flag_offset(const GlaShape& s);
 // Look-back flag value for one call: differs from every earlier call's in this process.
 unsigned next_call_tag();
+// Look-back wait settings for the next launches: the bound on one wait's polls, and whether
+// the waits look for a value no flag ever holds (a test of the expiry path).
+struct LookbackWait {
+  unsigned spins;
+  bool never_match;
+};
+LookbackWait lookback_wait();
+void set_lookback_wait(unsigned spins, bool never_match);
+// The current device's sticky look-back status word (device address), or null on failure.
+unsigned* lookback_status_word();
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
 // ------------------------------------------------------------------------- misc

@@ -159,6 +159,13 @@ unsigned next_call_tag() {
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.lb_tag = next_call_tag();
+  const LookbackWait w = lookback_wait();
+  p.lb_wait_tag = w.never_match ? ((p.lb_tag ^ 0x5A5A5A5Au) | 1u) : p.lb_tag;
+  p.lb_spins = w.spins;
+  if (s.lookback) {
+    p.lb_status = lookback_status_word();
+    if (!p.lb_status) return hipErrorInvalidSymbol;
+  }
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.bprefix;
   hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr, nullptr)

@@ -867,7 +867,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         for (int m = 0; m < STW; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i) fac[m][i] = 1.f;
-        lb_wait_all(p.lb_flag + slot0 + seg + 1, p.nseg - 1 - seg, p.lb_tag, lane);
+        const bool expired =
+            lb_wait_all(p.lb_flag + slot0 + seg + 1, p.nseg - 1 - seg, p.lb_wait_tag, lane, p.lb_spins);
         // LBU later segments per step, their loads in flight together (a step past the
         // last segment re-reads it and adds nothing)
         constexpr int LBU = STW == 1 ? 4 : 1;
@@ -908,6 +909,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
               }
             }
           }
+        }
+        if (expired) {  // a later chunk's contribution never arrived: poison G, record it
+#pragma unroll
+          for (int m = 0; m < STW; ++m) gacc[m] = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                        __builtin_nanf(""), __builtin_nanf("")};
+          if (lane == 0) lb_fail(p.lb_status);
         }
         write_gt();
         if (n_top < p.NC) {
@@ -1147,10 +1154,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // the last workgroup: once every workgroup is done with its waits (each had published
     // before), d_norm_w = the partials added in a fixed order (parts strided over NG groups per
     // column, then the groups in order), and the flags are cleared for the next launch
+    bool partial = false;  // some workgroup's done flag never arrived
     if (blockIdx.x == gridDim.x - 1) {
       const int nparts = (int)gridDim.x;
-      lb_wait_each(p.lb_flag + nparts, nparts, p.lb_tag, tid, NTH);
-      __syncthreads();
+      const bool ex = lb_wait_each(p.lb_flag + nparts, nparts, p.lb_wait_tag, tid, NTH, p.lb_spins);
+      if (ex) lb_fail(p.lb_status);
+      partial = __syncthreads_or(ex) != 0;
       for (int i = tid; i < 2 * nparts; i += NTH) lb_raise(p.lb_flag + i, 0u);
     }
     if (p.d_norm_w && blockIdx.x == gridDim.x - 1) {
@@ -1176,7 +1185,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         float sum = sDg[e2];
 #pragma unroll
         for (int g2 = 1; g2 < NG; ++g2) sum += sDg[g2 * DVP + e2];
-        p.d_norm_w[e2] = sum;
+        p.d_norm_w[e2] = partial ? __builtin_nanf("") : sum;
       }
     }
   }

@@ -11,6 +11,9 @@
 //     (gla_state_scan) scans those per state element; pass C (OUT=true) emits outputs.
 // Head dims are compiled in 16-wide tile classes (NDK x NDV tiles); smaller dims are padded
 // with zeros inside LDS, which leaves every product unchanged.
+#include <atomic>
+#include <mutex>
+
 #include "dig_device.h"
 #include "dig_internal.h"
 
@@ -153,11 +156,49 @@ int gla_fwd_lds_bytes(const GlaShape& s) {
   return e == hipSuccess ? bytes : 0;
 }
 
+// Sticky look-back status: one word per GPU (every device holds its own copy of the variable,
+// zero when the code object is loaded).  A look-back wait that gives up sets it; the host reads
+// and clears it (dig_lookback_status).  Host code reaches each device's copy through the
+// address hipGetSymbolAddress returns with that device current.
+__device__ unsigned g_lb_status;
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_status_mu;
+unsigned* g_status_ptr[kMaxDevices];
+std::atomic<unsigned> g_lb_spins{kLbSpinLimit};
+std::atomic<bool> g_lb_never{false};
+}  // namespace
+
+unsigned* lookback_status_word() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_status_mu);
+  if (!g_status_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_lb_status)) != hipSuccess || !ptr) return nullptr;
+    g_status_ptr[dev] = static_cast<unsigned*>(ptr);
+  }
+  return g_status_ptr[dev];
+}
+
+LookbackWait lookback_wait() { return {g_lb_spins.load(), g_lb_never.load()}; }
+void set_lookback_wait(unsigned spins, bool never_match) {
+  g_lb_spins.store(spins ? spins : kLbSpinLimit);
+  g_lb_never.store(never_match);
+}
+
 hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
   p.B = s.B; p.L = s.L; p.H = s.H; p.dk = s.dk; p.dv = s.dv;
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.prefix;
   p.lb_tag = next_call_tag();
+  const LookbackWait w = lookback_wait();
+  p.lb_wait_tag = w.never_match ? ((p.lb_tag ^ 0x5A5A5A5Au) | 1u) : p.lb_tag;
+  p.lb_spins = w.spins;
+  if (s.lookback) {
+    p.lb_status = lookback_status_word();
+    if (!p.lb_status) return hipErrorInvalidSymbol;
+  }
   return s.bf16 ? launch_gla_fwd_t<bf16>(s, p, st, nullptr)
                 : launch_gla_fwd_t<float>(s, p, st, nullptr);
 }

@@ -120,7 +120,6 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
   constexpr int QP = Lo::QP, TP = Lo::TP;
   constexpr int QKC = Lo::QKC, QKP = Lo::QKP;  // fp32 q e^{b}, k e^{-b} tiles
-  constexpr int NKS = DKP / 32;                 // bf16 K steps over the key dim
   constexpr int NT = C / 16;                            // query row tiles
   constexpr int NST = NDK * NDV;                        // fp32 state tiles
   // state tiles are owned by waves SW0..NW-1: the waves past the query row tiles when there
@@ -251,37 +250,21 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     const int e = E * 16 + r16;
     gm[E] = (OUT && e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
   }
-  // bf16 I/O: split fragments of q e^{b}, rows 16I.. (the B operand of the gated K Q^T tiles
-  // and the A operand of (q e^{b}) S0 share the lane layout: row = lane % 16, K slice 8g)
-  auto q_frags = [&](SplitFrag (&qf)[NKS], int I) {
-    const int l = opaque(tid & 63);
-    qf[0] = split_frag<QKC, QKP, (32 <= QKC)>(sQ, 16 * I + (l & 15), 8 * (l >> 4));
-    if constexpr (NKS > 1)
-      qf[1] = split_frag<QKC, QKP, (64 <= QKC)>(sQ, 16 * I + (l & 15), 32 + 8 * (l >> 4));
-  };
   // oacc += (q e^{b}) S0 for query rows 16I..: S0 is the bf16 copy in sS; q e^{b} enters as
   // hi + lo parts (bf16 I/O)
   auto q_s0 = [&](f32x4 (&oacc)[NDV], int I) {
     const int l = opaque(tid & 63);
     if constexpr (kBf) {
-      SplitFrag qf[NKS];
-      q_frags(qf, I);
 #pragma unroll
       for (int E = 0; E < NDV; ++E)
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const bf16x8 sb = Mma<bf16>::frag<true>(reinterpret_cast<const bf16*>(sS), QP,
-                                                  16 * E + (l & 15), 32 * s + 8 * (l >> 4));
-          oacc[E] = mfma_bf16(qf[s].lo, sb, oacc[E]);
-          oacc[E] = mfma_bf16(qf[s].hi, sb, oacc[E]);
-        }
+        oacc[E] = mm_split_b<QKC, QKP, QP>(oacc[E], sQ, 16 * I, reinterpret_cast<const bf16*>(sS),
+                                           16 * E, l);
     } else {
 #pragma unroll
       for (int E = 0; E < NDV; ++E)
         oacc[E] = Mma<T>::kc(oacc[E], sQ, QKP, 16 * I, sS, QP, 16 * E, DKP, l);
     }
   };
-  static_assert(NKS >= 1 && NKS <= 2, "key dim up to 64");
 
   // Every load above (and the first chunk's rows) has landed before the loop: otherwise the
   // compiler's wait for them, placed inside the loop, would also wait for the prefetch.
@@ -503,19 +486,9 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         if constexpr (kBf) {
           // split operands: where o_i cancels to a small vector its relative error is that of
           // these sums, and the RMSNorm gradient magnifies it by rstd_i
-          SplitFrag qf[NKS];
-          q_frags(qf, I);
 #pragma unroll
-          for (int J = 0; J < NT; ++J) {
-            pt[J] = zero4();
-            if (J <= I) {
-              pt[J] = mfma_split(split_frag<QKC, QKP, (32 <= QKC)>(sK, 16 * J + r16, 8 * g4),
-                                 qf[0], pt[J]);
-              if constexpr (NKS > 1)
-                pt[J] = mfma_split(split_frag<QKC, QKP, (64 <= QKC)>(sK, 16 * J + r16, 32 + 8 * g4),
-                                   qf[1], pt[J]);
-            }
-          }
+          for (int J = 0; J < NT; ++J)
+            pt[J] = J <= I ? mm_split<QKC, QKP, QKP>(zero4(), sK, 16 * J, sQ, 16 * I, lane) : zero4();
         } else {
 #pragma unroll
           for (int J = 0; J < NT; ++J)
@@ -610,7 +583,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
 #pragma unroll
         for (int m = 0; m < STW; ++m) sacc[m] = zero4();
         if (seg > 0) {
-          lb_wait_all(p.lb_flag + slot0, seg, p.lb_tag, lane);
+          const bool expired = lb_wait_all(p.lb_flag + slot0, seg, p.lb_wait_tag, lane, p.lb_spins);
           float fac[STW][4];
 #pragma unroll
           for (int m = 0; m < STW; ++m)
@@ -652,6 +625,12 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
                 }
               }
             }
+          }
+          if (expired) {  // an earlier chunk's contribution never arrived: poison S0, record it
+#pragma unroll
+            for (int m = 0; m < STW; ++m) sacc[m] = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                          __builtin_nanf(""), __builtin_nanf("")};
+            if (lane == 0) lb_fail(p.lb_status);
           }
         }
         // S0: saved for the backward, bf16 copy for (q e^b) S0
@@ -727,7 +706,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     // the next launch
     if (blockIdx.x == gridDim.x - 1) {
       const int n = (int)gridDim.x;
-      lb_wait_each(p.lb_flag + n, n, p.lb_tag, tid, NTH);
+      if (lb_wait_each(p.lb_flag + n, n, p.lb_wait_tag, tid, NTH, p.lb_spins)) lb_fail(p.lb_status);
       __syncthreads();
       for (int i = tid; i < 2 * n; i += NTH) lb_raise(p.lb_flag + i, 0u);
     }

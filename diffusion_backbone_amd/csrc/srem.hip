@@ -372,7 +372,8 @@ hipError_t launch_reorient(int B, int gh, int gw, int D, int elt, int from, int 
     long g = (items + 255) / 256;
     return (unsigned)(g < blocks_cap ? g : blocks_cap);
   };
-  if (rowbytes % 16 == 0 && rowbytes <= 16 * 64 * 8 && rows < (1L << 31)) {
+  // (the row loop's indices reach rows + 3 * 4 * blocks_cap in int: kept below 2^31)
+  if (rowbytes % 16 == 0 && rowbytes <= 16 * 64 * 8 && rows < (1L << 31) - (1L << 17)) {
     const int nv = (int)(rowbytes / 16), cpr = (nv + 63) / 64;
     const bool col = from == kCol || from == kColRev;
     const GridMap m = grid_map(gh, gw, from, to);

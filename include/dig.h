@@ -6,8 +6,8 @@
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers on the current HIP device, 16-byte aligned,
  *     contiguous.  The caller owns every buffer; the library never allocates or frees
- *     device memory and keeps no device state between calls (its only state is a host-side
- *     call counter that tags the backward's look-back flags).
+ *     device memory.  Its state between calls: a host-side call counter that tags the
+ *     look-back flags, and one device word per GPU (dig_lookback_status).
  *   - A workspace holds scratch only: it needs no initialisation and may be reused by later
  *     calls, but two calls that may run at the same time (other streams) must not share one.
  *   - Work is enqueued on `stream` and the call returns without synchronising.
@@ -187,6 +187,27 @@ const char* dig_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t dig_abi_version(void);
+
+/*
+ * dig_lookback_status -- status of the look-back waits on the current device.
+ * Short sequences run dig_gla_fwd / dig_gla_bwd as one launch in which a chunk's workgroup
+ * waits (bounded: about 2^18 polls, far past any real wait) for values published by the
+ * workgroups of the other chunks of its sequence.  A wait that gives up leaves NaN in what the
+ * missing values fed (y of that chunk; dq, dk, dv, d_gate_logit of that chunk; d_norm_w) and
+ * sets a sticky status word of the device (a library-held device variable, one per GPU).
+ * This call synchronises `stream`, then returns DIG_OK if no wait has given up since the last
+ * call, else clears the word and returns DIG_ERR_DEVICE.  A wait can only give up when other
+ * work keeps the earlier-dispatched workgroups from running for that long.
+ */
+dig_status dig_lookback_status(hipStream_t stream);
+
+/*
+ * dig_debug_lookback -- test hook for the path above: the launches that follow bound each
+ * look-back wait by `spins` polls (0 restores the default) and, if never_match != 0, wait for a
+ * flag value no workgroup ever raises, so every wait gives up (and every kernel still ends).
+ * Process-wide; not for production use.
+ */
+void dig_debug_lookback(uint32_t spins, int32_t never_match);
 
 #ifdef __cplusplus
 }

@@ -449,3 +449,42 @@ def test_bwd_seed_sweep(name, batch, seq_len, seg):
         for n, e in errs.items():
             worst[n] = max(worst.get(n, 0.0), e)
     print("  worst over seeds: " + " ".join("%s=%.2e" % kv for kv in worst.items()), flush=True)
+
+
+def test_lookback_expired_wait_is_reported():
+    """A look-back wait that gives up leaves NaN where the values it waited for would have gone
+    and makes dig_lookback_status report DIG_ERR_DEVICE.  Forced from the host: the waits look
+    for a flag value no workgroup raises and give up after a few polls, so every kernel still
+    ends.  Afterwards normal calls are correct and the status is clean again."""
+    import torch
+    import diffusion_backbone_amd as dig
+    announce("look-back expired wait: forward, then backward")
+    case = _case("dig_s2_256", batch=2, seq_len=256, random_gamma=True)   # 4 chunks
+    dig.dig_lookback_status()  # nothing pending from earlier tests
+    f_ok = gla_forward(case, 64, want_saved=True)
+    torch.cuda.synchronize()
+    try:
+        dig.dig_debug_lookback(8, True)
+        f = gla_forward(case, 64, want_saved=False)
+        torch.cuda.synchronize()
+        with pytest.raises(dig.DigError) as ei:
+            dig.dig_lookback_status()
+        assert ei.value.status == dig.DIG_ERR_DEVICE
+        y = to_f64(f["y"])
+        assert np.isfinite(y[:, :64]).all()      # the first chunk waits for nothing
+        assert np.isnan(y[:, 64:]).all()         # every later chunk's state never arrived
+        g = gla_backward(case, f_ok)
+        torch.cuda.synchronize()
+        with pytest.raises(dig.DigError):
+            dig.dig_lookback_status()
+        dk = to_f64(g["dk"])
+        assert np.isfinite(dk[:, 192:]).all()    # the last chunk waits for nothing
+        assert np.isnan(dk[:, :192]).all()
+        assert np.isnan(g["dgamma"].cpu().numpy()).all()
+    finally:
+        dig.dig_debug_lookback(0, False)
+    dig.dig_lookback_status()  # cleared by the query above
+    f2 = gla_forward(case, 64, want_saved=True)
+    _check_fwd(case, f2, TOL["bf16"], what="after")
+    _check_bwd(case, gla_backward(case, f2), TOL["bf16"], what="after")
+    dig.dig_lookback_status()

@@ -33,6 +33,11 @@ def _raw_bits(t):
 @pytest.mark.parametrize("B,gh,gw,D,dtype", [
     (1, 8, 8, 64, "f32"), (2, 16, 16, 384, "bf16"), (1, 3, 5, 6, "bf16"), (2, 7, 4, 5, "bf16"),
     (1, 5, 3, 3, "f32"), (1, 112, 112, 384, "bf16"), (1, 1, 1, 8, "bf16"),
+    # row kernel with several 16-byte pieces per lane: 2304-byte rows (3 per lane, DiG-XL/2
+    # D = 1152 in bf16), 4608-byte rows (5 per lane, fp32); rows past 8 KiB take the
+    # element-wise fallback (D = 2304 fp32: 9216-byte rows)
+    (1, 16, 16, 1152, "bf16"), (1, 4, 4, 1152, "f32"), (1, 3, 3, 2304, "f32"),
+    (2, 5, 7, 1152, "bf16"),
 ])
 def test_reorient_bit_exact(B, gh, gw, D, dtype):
     dig = _dig()

@@ -204,3 +204,37 @@ def make_srem_case(cfg: Config, seed: int | None = None, *, batch: int | None = 
 def crop_config(cfg: Config, grid: int = 16) -> Config:
     """The same layer shapes on a grid x grid crop of the token grid (one image)."""
     return cfg_replace(cfg, name=cfg.name + "_crop%d" % grid, batch=1, grid_h=grid, grid_w=grid)
+
+
+# ------------------------------------------------------------- multi-block chain
+@dataclass
+class BlockWeights:
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wa1: np.ndarray
+    wa2: np.ndarray
+    wr: np.ndarray
+    wo: np.ndarray      # [H * d_v, D]: the mixer's output projection
+    conv_w: np.ndarray  # [D, 3, 3]
+
+
+def make_block_weights(cfg: Config, rng) -> BlockWeights:
+    """One block's projection weights ~ N(0, 1/D) and DWConv weights ~ N(0, 1/9) (fp32)."""
+    D, H, dk, dv = cfg.d_model, cfg.heads, cfg.d_k, cfg.d_v
+    s = 1.0 / np.sqrt(D)
+    f = lambda shape, std: (rng.standard_normal(shape) * std).astype(np.float32).astype(np.float64)
+    return BlockWeights(f((D, H * dk), s), f((D, H * dk), s), f((D, H * dv), s),
+                        f((D, cfg.rank), s), f((cfg.rank, H * dk), s), f((D, H * dv), s),
+                        f((H * dv, D), s), f((D, 3, 3), 1.0 / 3.0))
+
+
+def project(cfg: Config, x: np.ndarray, wts: BlockWeights):
+    """The mixer's operands from block input x [B, L, D] (fp64 matmuls, quantised once):
+    q, k, z = (x W_a1) W_a2, v, r, each [B, L, H, d]."""
+    B, L, _ = x.shape
+    H, dk, dv = cfg.heads, cfg.d_k, cfg.d_v
+    x2 = x.reshape(B * L, -1)
+    qz = lambda a, d: quantize(a.reshape(B, L, H, d), cfg.dtype)
+    return (qz(x2 @ wts.wq, dk), qz(x2 @ wts.wk, dk), qz(x2 @ wts.wv, dv),
+            qz((x2 @ wts.wa1) @ wts.wa2, dk), qz(x2 @ wts.wr, dv))
