@@ -27,6 +27,7 @@ EXPORTS = (
     "dig_gla_bwd_workspace_bytes", "dig_gla_bwd", "dig_srem_reorient", "dig_dwconv3x3",
     "dig_dwconv3x3_bwd_workspace_bytes", "dig_dwconv3x3_bwd", "dig_status_str",
     "dig_last_error", "dig_abi_version", "dig_lookback_status", "dig_debug_lookback",
+    "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes",
 )
 
 
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.dig_lookback_status.restype = ctypes.c_int
         L.dig_debug_lookback.argtypes = [ctypes.c_uint32, I]
         L.dig_debug_lookback.restype = None
+        L.dig_dwconv3x3_bwd_noalloc.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.dig_dwconv3x3_bwd_noalloc.restype = ctypes.c_int
+        L.dig_dwconv3x3_bwd_noalloc_max_bytes.argtypes = []
+        L.dig_dwconv3x3_bwd_noalloc_max_bytes.restype = S
         _lib = L
     return _lib
 
@@ -202,3 +207,15 @@ def dig_lookback_status(stream=None):
 
 def dig_debug_lookback(spins: int, never_match: bool):
     lib().dig_debug_lookback(int(spins), 1 if never_match else 0)
+
+
+def dig_dwconv3x3_bwd_noalloc(batch, grid_h, grid_w, channels, dtype, layout, out_layout, x, w,
+                              dy, dx, dw, dbias=None, stream=None):
+    st = lib().dig_dwconv3x3_bwd_noalloc(batch, grid_h, grid_w, channels, dtype, layout,
+                                         out_layout, _ptr(x), _ptr(w), _ptr(dy), _ptr(dx),
+                                         _ptr(dw), _ptr(dbias), _stream(stream))
+    _check(st, "dig_dwconv3x3_bwd_noalloc")
+
+
+def dig_dwconv3x3_bwd_noalloc_max_bytes() -> int:
+    return lib().dig_dwconv3x3_bwd_noalloc_max_bytes()

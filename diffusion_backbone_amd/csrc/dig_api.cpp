@@ -351,26 +351,49 @@ size_t dig_dwconv3x3_bwd_workspace_bytes(int32_t batch, int32_t grid_h, int32_t 
   return dig::dwconv_bwd_workspace(batch, grid_h, grid_w, channels);
 }
 
-dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int32_t channels,
-                             int32_t dtype, int32_t layout, int32_t out_layout, const void* x,
-                             const float* w, const void* dy, void* dx, float* dw,
-                             float* dbias_opt, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the conv backward entry points (the workspace aside).  *empty is
+// set for an empty problem, whose dw (and dbias) have then been zero-filled on the stream.
+dig_status check_dwconv_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int32_t channels,
+                            int32_t dtype, int32_t layout, int32_t out_layout, const void* x,
+                            const float* w, const void* dy, void* dx, float* dw, float* dbias_opt,
+                            hipStream_t stream, bool* empty) {
+  *empty = false;
   dig_status st = check_srem(batch, grid_h, grid_w, channels, dtype, layout, out_layout);
   if (st != DIG_OK) return st;
-  const size_t L = (size_t)grid_h * grid_w;
-  if (batch == 0 || L == 0) {
+  if (batch == 0 || (size_t)grid_h * grid_w == 0) {
     if (!dw) return fail(DIG_ERR_NULL, "dw is required");
     if (!aligned16(dw) || (dbias_opt && !aligned16(dbias_opt)))
       return fail(DIG_ERR_ALIGN, "dw, dbias must be 16-byte aligned");
+    *empty = true;
     hipError_t e = dig::launch_fill_zero(dw, (size_t)channels * 9, stream);
     if (e == hipSuccess && dbias_opt) e = dig::launch_fill_zero(dbias_opt, (size_t)channels, stream);
     return check_dev(e, "dig_dwconv3x3_bwd fill");
   }
   if (!x || !w || !dy || !dx || !dw) return fail(DIG_ERR_NULL, "x, w, dy, dx and dw are required");
-  const void* ptrs[] = {x, w, dy, dx, dw, dbias_opt, workspace};
+  const void* ptrs[] = {x, w, dy, dx, dw, dbias_opt};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  return DIG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int32_t channels,
+                             int32_t dtype, int32_t layout, int32_t out_layout, const void* x,
+                             const float* w, const void* dy, void* dx, float* dw,
+                             float* dbias_opt, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  bool empty = false;
+  dig_status st = check_dwconv_bwd(batch, grid_h, grid_w, channels, dtype, layout, out_layout, x,
+                                   w, dy, dx, dw, dbias_opt, stream, &empty);
+  if (st != DIG_OK || empty) return st;
+  const size_t L = (size_t)grid_h * grid_w;
+  if (workspace && !aligned16(workspace))
+    return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   const size_t need = dig_dwconv3x3_bwd_workspace_bytes(batch, grid_h, grid_w, channels);
   if (need && (!workspace || workspace_bytes < need))
     return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
@@ -387,6 +410,36 @@ dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int3
                                           layout, out_layout, x, w, dy, dx, dw, dbias_opt,
                                           workspace, stream),
                    "dig_dwconv3x3_bwd launch");
+}
+
+size_t dig_dwconv3x3_bwd_noalloc_max_bytes(void) { return dig::kNoAllocScratchBytes; }
+
+dig_status dig_dwconv3x3_bwd_noalloc(int32_t batch, int32_t grid_h, int32_t grid_w,
+                                     int32_t channels, int32_t dtype, int32_t layout,
+                                     int32_t out_layout, const void* x, const float* w,
+                                     const void* dy, void* dx, float* dw, float* dbias_opt,
+                                     hipStream_t stream) {
+  bool empty = false;
+  dig_status st = check_dwconv_bwd(batch, grid_h, grid_w, channels, dtype, layout, out_layout, x,
+                                   w, dy, dx, dw, dbias_opt, stream, &empty);
+  if (st != DIG_OK || empty) return st;
+  const size_t need = dig_dwconv3x3_bwd_workspace_bytes(batch, grid_h, grid_w, channels);
+  if (need > dig::kNoAllocScratchBytes)
+    return fail(DIG_ERR_WORKSPACE,
+                "the partial sums need %zu bytes; the allocation-free call holds at most %zu "
+                "(use dig_dwconv3x3_bwd with a workspace)",
+                need, dig::kNoAllocScratchBytes);
+  const size_t elt = dtype == DIG_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)batch * grid_h * grid_w * channels * elt;
+  const Range in[] = {rng("x", x, bytes), rng("w", w, (size_t)channels * 36), rng("dy", dy, bytes)};
+  const Range out[] = {rng("dx", dx, bytes), rng("dw", dw, (size_t)channels * 36),
+                       rng("dbias", dbias_opt, dbias_opt ? (size_t)channels * 4 : 0)};
+  st = check_alias(in, 3, out, 3);
+  if (st != DIG_OK) return st;
+  return check_dev(dig::launch_dwconv_bwd_noalloc(batch, grid_h, grid_w, channels,
+                                                  dtype == DIG_BF16, layout, out_layout, x, w, dy,
+                                                  dx, dw, dbias_opt, stream),
+                   "dig_dwconv3x3_bwd_noalloc launch");
 }
 
 }  // extern "C"

@@ -143,5 +143,11 @@ size_t dwconv_bwd_workspace(int B, int gh, int gw, int D);
 hipError_t launch_dwconv_bwd(int B, int gh, int gw, int D, int bf16, int layout, int out_layout,
                              const void* x, const float* w, const void* dy, void* dx, float* dw,
                              float* dbias, void* workspace, hipStream_t st);
+// The same with the partials in the library's per-GPU scratch array (no allocation); fails
+// with hipErrorInvalidValue if they need more than kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t launch_dwconv_bwd_noalloc(int B, int gh, int gw, int D, int bf16, int layout,
+                                     int out_layout, const void* x, const float* w, const void* dy,
+                                     void* dx, float* dw, float* dbias, hipStream_t st);
 
 }  // namespace dig

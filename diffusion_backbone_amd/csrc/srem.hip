@@ -10,6 +10,8 @@
 // Tensors are [B, L, D] with D channels contiguous per token, so one token row is one
 // contiguous run: every access below is a vector load/store of a channel group, with
 // consecutive threads on consecutive channel groups of the same token (coalesced).
+#include <mutex>
+
 #include "dig_device.h"
 #include "dig_internal.h"
 
@@ -1246,6 +1248,46 @@ hipError_t launch_dwconv_bwd(int B, int gh, int gw, int D, int bf16v, int layout
                                      part, st);
   return launch_dwconv_bwd_t<float>(B, gh, gw, D, layout, out_layout, x, w, dy, dx, dw, dbias,
                                     part, st);
+}
+
+// The allocation-free conv backward keeps its dW/dbias partials in this array, one copy per
+// GPU for the life of the process.  Every call on a GPU shares that GPU's copy (calls that
+// overlap on one GPU race); each call writes every partial it later reads, so nothing needs
+// clearing between calls.  Host code never passes the array's name to a kernel: it passes the
+// device address hipGetSymbolAddress gives for the current device.
+__device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_dwconv_bwd_noalloc(int B, int gh, int gw, int D, int bf16v, int layout,
+                                     int out_layout, const void* x, const float* w, const void* dy,
+                                     void* dx, float* dw, float* dbias, hipStream_t st) {
+  if (dwconv_bwd_workspace(B, gh, gw, D) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  float* part = nullptr;
+  const hipError_t e = noalloc_scratch(&part);
+  if (e != hipSuccess) return e;
+  return launch_dwconv_bwd(B, gh, gw, D, bf16v, layout, out_layout, x, w, dy, dx, dw, dbias, part,
+                           st);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t n) {

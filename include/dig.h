@@ -177,6 +177,25 @@ dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int3
                              float* dbias_opt, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/*
+ * dig_dwconv3x3_bwd_noalloc -- dig_dwconv3x3_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and results.  The
+ * dw/dbias partial sums go to a scratch array the library holds on each GPU for the life of
+ * the process (dig_dwconv3x3_bwd_noalloc_max_bytes() bytes, 8 MiB).  Problems whose partials
+ * need more (dig_dwconv3x3_bwd_workspace_bytes() larger than that) return DIG_ERR_WORKSPACE.
+ * Nothing is allocated or freed.  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be serialised.
+ */
+dig_status dig_dwconv3x3_bwd_noalloc(int32_t batch, int32_t grid_h, int32_t grid_w,
+                                     int32_t channels, int32_t dtype, int32_t layout,
+                                     int32_t out_layout, const void* x, const float* w,
+                                     const void* dy, void* dx, float* dw, float* dbias_opt,
+                                     hipStream_t stream);
+
+/* Bytes of the per-GPU scratch array of dig_dwconv3x3_bwd_noalloc. */
+size_t dig_dwconv3x3_bwd_noalloc_max_bytes(void);
+
 /* ------------------------------------------------------------------------ misc */
 
 /* Static name of a status code. */
