@@ -1,13 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of the DiG hot path on one MI355X: GLA token mixer + SREM, forward and backward.
 
-One step = one pass of the whole path over one batch of synthetic DiG-S/2 256-px input:
-for each of the 12 blocks (scan directions cycling row, row_rev, col, col_rev)
-    dig_gla_fwd (saving chunk states) -> dig_dwconv3x3 (fused reorient to the next direction)
-then, blocks in reverse,
-    dig_dwconv3x3_bwd -> dig_gla_bwd.
-Inputs are generated on the GPU before timing (seeded, x ~ N(0,1), weights ~ N(0, 1/D)).
-The metric is GLA-layer tokens/s: batch * tokens * blocks / step time.
+Headline (``value``): the DiG-XL/2 2048-px training step (batch 1, 128 x 128 tokens, 16 heads,
+d_k 36, d_v 72, chunk 64).  One step = four blocks in the four scan directions (row, row_rev,
+col, col_rev), each ``dig_gla_fwd`` (saving what the backward needs) -> ``dig_dwconv3x3``
+(fused reorient to the next direction), then, blocks in reverse, ``dig_dwconv3x3_bwd`` ->
+``dig_gla_bwd``.  Inputs are generated on the GPU before timing (seeded; x ~ N(0,1), weights
+~ N(0, 1/D), upstream gradients ~ N(0,1)) and are resident in HBM.  The metric is GLA-layer
+tokens/s: batch * tokens * blocks / step time.
+
+Beside it, in the same JSON line: the other configurations (DiG-S/2 256 px, 12 blocks,
+forward and forward+backward; S/2 1792 px; XL/2 1024 px over the four directions), the
+roofline of the dominant call, an LDS-resident contraction microbenchmark (MFMA fraction of
+the contraction phases), steady-state and cold-cache probes against a measured streaming-copy
+ceiling, and the fp64 oracle timed on the host (single thread and all cores).
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
@@ -27,7 +33,8 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+HEADLINE = "dig_xl2_2048"
 
 
 def parse():
@@ -35,18 +42,25 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dig_s2_256", choices=sorted(W.CONFIGS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
-                    help="skip the steady-state probes (larger shapes, outside the timed step)")
+                    help="skip everything outside the headline step (other configs, probes, "
+                         "microbenchmark)")
     ap.add_argument("--seg-chunks", type=int, default=0)
-    ap.add_argument("--quiet", action="store_true")
     # profiling helpers (rocprofv3 counter runs): run only one library call of the step, or a
     # plain device copy of known size that calibrates the byte counters
     ap.add_argument("--pmc-target", choices=["gla_fwd", "gla_bwd", "srem_fwd", "srem_bwd"],
                     default=None)
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--oracle-leg", default=None, help=argparse.SUPPRESS)  # child process
     return ap.parse_args()
+
+
+def n_blocks(cfg):
+    """Blocks per step: the configuration's own count (12 for DiG-S/2 256 px), else one block
+    per scan direction."""
+    return cfg.blocks if cfg.blocks > 1 else 4
 
 
 def gen_blocks(cfg, nblocks, seed):
@@ -72,6 +86,7 @@ def gen_blocks(cfg, nblocks, seed):
         blocks.append(dict(q=bf(q), k=bf(k), v=bf(v), z=bf(z), r=bf(r), x=bf(x.view(B, L, D)),
                            cw=cw.contiguous(), dy=bf(dy), dys=bf(dys),
                            gamma=torch.ones(dv, device="cuda")))
+        del x, q, k, v, z, r, dy, dys
     return blocks
 
 
@@ -147,9 +162,8 @@ class Path:
 
 
 class EventTimer:
-    """HIP events around chosen calls on torch's current stream (the stream they run on).
-    The events are created up front so that recording them adds no allocation to the
-    timed region."""
+    """HIP events around chosen calls on torch's current stream (the stream the library calls
+    run on).  Created up front so that recording them adds no allocation to the timed region."""
 
     def __init__(self, n):
         import torch
@@ -169,33 +183,42 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ps) / max(len(ps), 1)
 
 
-# HBM traffic of one GLA call on the default workload, from rocprofv3 FETCH_SIZE and
+def timed(fn, steps, warmup):
+    """ms per call of fn over exactly `steps` calls after `warmup` untimed ones, with a device
+    synchronisation on both sides of the timed region."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+# HBM traffic of one GLA call on the headline workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (summed over the call's kernels) divided by the counters' reading per byte
 # of a plain copy; valid only for the kernel sources it was measured on (sha256 below).
 TRAFFIC = {
-    "workload": "dig_s2_256",
+    "workload": "dig_xl2_2048",
     "bytes": {
-        # FETCH_SIZE 8886.1 KiB / 0.50006 (copy: 131088.0 KiB read per 262144 KiB moved) +
-        # WRITE_SIZE 6997.8 KiB / 1.0 (copy: 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 25362253,
-        # FETCH_SIZE 5145.2 KiB / 0.50006 + WRITE_SIZE 7765.5 KiB / 1.0
-        "dig_gla_fwd": 18487983,
+        # pass A 145353.7 KiB / 0.50008 + 92162.7 KiB / 1.0, segment scan 1666.6 + 2594.2,
+        # final pass 95190.5 + 94244.6 (FETCH_SIZE, WRITE_SIZE; copy: 131091.9 KiB read per
+        # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
+        "dig_gla_bwd": 689510069,
+        # pass A 79442.9 + 5099.5, state scan 2819.1 + 5184.0, output pass 67650.9 + 156470.6
+        "dig_gla_fwd": 477731438,
     },
-    "sources_sha256": "834f09c8cae3003b695a888b3be3d3f76831e6e85b8238bc8e8beeea36dc9391",
+    "sources_sha256": "81da8ce96e0d08d2c80a5db9a738417eeba256f4acf3cc0ea90fbb34fcfeb312",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
                    "diffusion_backbone_amd/csrc/gla_fwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_fwd.hip",
                    "diffusion_backbone_amd/csrc/dig_device.h")
-
-
-# The kernels one call runs on the default workload (B=8, 16x16 grid, 6 heads: 4 chunks of 64
-# tokens per image and head).
-KERNEL_OF_CALL = {
-    "gla_bwd": "gla_bwd_kernel, look-back (one chunk per workgroup, one launch)",
-    "gla_fwd": "gla_fwd_kernel, look-back (one chunk per workgroup, one launch)",
-}
 
 
 def sources_sha256():
@@ -215,21 +238,48 @@ def measured_traffic(workload, call):
     return byts if TRAFFIC["sources_sha256"] == sources_sha256() else None
 
 
-def copy_probe(mib, reps):
-    """A plain copy of known size through dig_srem_reorient (identity order): the reference
-    for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes."""
+def probe_lib():
+    """libdig_probe.so: measurement kernels (contraction microbenchmark, streaming copy)."""
+    import ctypes
+    path = os.path.join(ROOT, "diffusion_backbone_amd", "libdig_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libdig_probe.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.digp_contraction.argtypes = [I, I, I, P, P]
+    L.digp_contraction.restype = I
+    L.digp_contraction_waves.argtypes = [I]
+    L.digp_contraction_waves.restype = I
+    L.digp_contraction_flops.argtypes = [I, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double)]
+    L.digp_copy.argtypes = [P, P, ctypes.c_size_t, P]
+    L.digp_copy.restype = I
+    return L
+
+
+def _stream():
     import torch
-    import diffusion_backbone_amd as dig
-    n = mib * 1024 * 1024 // 2
-    D = 1024
-    rows = n // D
-    x = torch.ones(rows * D, dtype=torch.bfloat16, device="cuda")
+    return torch.cuda.current_stream().cuda_stream
+
+
+def device_copy(L, src, dst):
+    err = L.digp_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(), _stream())
+    if err:
+        raise RuntimeError("digp_copy failed: %d" % err)
+
+
+def copy_probe(mib, reps):
+    """A plain streaming copy of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE
+    counter readings to bytes."""
+    import torch
+    L = probe_lib()
+    x = torch.ones(mib * 1024 * 1024 // 2, dtype=torch.bfloat16, device="cuda")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     for _ in range(reps):
-        dig.dig_srem_reorient(1, 1, rows, D, dig.DIG_BF16, dig.DIG_SCAN_ROW, dig.DIG_SCAN_ROW, x, y)
+        device_copy(L, x, y)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_each_way": rows * D * 2, "reps": reps}), flush=True)
+    print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 2, "reps": reps}), flush=True)
 
 
 def gla_bytes_per_token_head(cfg, which):
@@ -241,58 +291,115 @@ def gla_bytes_per_token_head(cfg, which):
     return 2 * (6 * dk + 5 * dv)
 
 
-def cpu_baseline(cfg, nblocks):
-    """The fp64 oracle on the host: one full step (fwd + bwd of every block) of a bounded
-    sample of the batch, scaled to GLA-layer tokens/s."""
-    import oracle
-    sample_batch = max(1, min(cfg.batch, 2))
-    scfg = W.cfg_replace(cfg, batch=sample_batch)
-    case = W.make_gla_case(scfg)
-    srem = W.make_srem_case(scfg)
-    gh, gw = cfg.grid_h, cfg.grid_w
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for l in range(nblocks):
-            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
-            oracle.gla_fwd(case.q, case.k, case.v, case.z, case.r, case.gamma)
-            oracle.dwconv3x3(srem.x, srem.w, gh, gw, d0, d1)
-        for l in reversed(range(nblocks)):
-            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
-            oracle.dwconv3x3_bwd(srem.x, srem.w, srem.dy, gh, gw, d0, d1)
-            oracle.gla_bwd(case.q, case.k, case.v, case.z, case.r, case.dy, case.gamma)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 200:
-            break
-    tokens = sample_batch * cfg.seq_len * nblocks * reps
-    return {"value": tokens / el, "unit": "GLA-layer tokens/s (fwd+bwd)",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d full fwd+bwd step(s) of %d of %d images (%d blocks, %d tokens each), %.1f s"
-                      % (reps, sample_batch, cfg.batch, nblocks, cfg.seq_len, el)}
+def srem_bytes_per_token(cfg, which):
+    """Algorithmic bytes per token of the conv with fused reorient: read x, write y (fwd); read
+    x and dy, write dx (bwd)."""
+    return (2 if which == "fwd" else 3) * cfg.d_model * 2
 
 
-def _time_us(fn, reps=10):
+def run_config(cfg, steps, warmup, seg_chunks=0, fwd_only=False, events=False):
+    """Times the step of one configuration; returns a dict (and the Path when events=True)."""
+    import torch
+    nb = n_blocks(cfg)
+    blocks = gen_blocks(cfg, nb, cfg.seed)
+    path = Path(cfg, blocks, seg_chunks)
+    torch.cuda.synchronize()
+    tokens = cfg.batch * cfg.seq_len * nb
+    out = {"workload": cfg.name, "batch": cfg.batch, "grid": [cfg.grid_h, cfg.grid_w],
+           "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "d_model": cfg.d_model,
+           "chunk": cfg.chunk, "blocks": nb,
+           "directions": [W.SCAN_NAMES[d] for d in path.sched[:nb]]}
+    ms_fwd = timed(path.step_fwd, steps, warmup)
+    out["fwd"] = {"tokens_per_s": round(tokens / (ms_fwd / 1e3), 1), "ms_per_step": round(ms_fwd, 4)}
+    if not fwd_only:
+        ms = timed(path.step, steps, warmup)
+        out["fwd_bwd"] = {"tokens_per_s": round(tokens / (ms / 1e3), 1), "ms_per_step": round(ms, 4)}
+    if not events:
+        del path, blocks
+        torch.cuda.empty_cache()
+        return out, None
+    return out, path
+
+
+def contraction_microbench():
+    """The chunk kernel's contraction phases with operands resident in LDS (no global
+    traffic): how busy they can keep the matrix cores.  A microbenchmark, not the step."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    res = {}
+    for shape, label in ((0, "s_heads_32_64"), (1, "xl_heads_36_72")):
+        nwg, iters = 256 * 4, 400
+        waves = L.digp_contraction_waves(shape)
+        sink = torch.empty(nwg * 64 * waves, device="cuda")
+        run = lambda: L.digp_contraction(shape, nwg, iters, sink.data_ptr(), _stream())
+        ms = timed(run, 5, 2)
+        alg, iss = ctypes.c_double(), ctypes.c_double()
+        L.digp_contraction_flops(shape, ctypes.byref(alg), ctypes.byref(iss))
+        chunks = nwg * iters
+        t_alg = alg.value * chunks / (ms / 1e3) / 1e12
+        t_iss = iss.value * chunks / (ms / 1e3) / 1e12
+        res[label] = {
+            "what": "gated Q K^T (split hi/lo), P V, (q e^b) S0 and the state update of one "
+                    "64-token chunk per workgroup iteration, operands in LDS; %d workgroups x "
+                    "%d iterations" % (nwg, iters),
+            "ms": round(ms, 4),
+            "mfma_issued_tflops": round(t_iss, 1),
+            "mfma_frac_of_bf16_peak": round(t_iss / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_tflops": round(t_alg, 1),
+            "algorithmic_frac_of_bf16_peak": round(t_alg / BF16_PEAK_TFLOPS, 4),
+            "issued_flops_per_chunk": iss.value, "algorithmic_flops_per_chunk": alg.value}
+        del sink
+    return res
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _time_us(fn, reps=10, cold=None):
+    """Average µs per call back to back (warm), or with `cold` given: the median of single
+    calls, each after `cold()` (a 1 GiB write, outside the events) has flushed the caches."""
     import torch
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    if cold is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+    ts = []
     for _ in range(reps):
+        cold()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps * 1e3
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return _median(ts)
 
 
 def probes():
-    """Steady-state probes, outside the timed step: one library call at a time, back to back,
-    on inputs large enough that launch latency does not dominate.  Labelled as probes: they
-    are not the step's workload."""
+    """Probes outside the timed step, labelled as such: single library calls on larger inputs
+    (warm: back to back; cold: after a 1 GiB write), and the streaming-copy ceiling of the same
+    bytes (this repository's own copy kernel)."""
     import torch
     import diffusion_backbone_amd as dig
+    PL = probe_lib()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    cold = lambda: flush.fill_(1.0)
     out = {}
+
+    def rec(key, call, shape, us, byts, **kw):
+        gbs = byts / (us / 1e6) / 1e9
+        out[key] = dict(call=call, shape=shape, us=round(us, 1), achieved_gbs=round(gbs, 1),
+                        frac=round(gbs / HBM_PEAK_GBS, 4), **kw)
 
     def gla(label, B, L, H, dk, dv, chunk=64):
         bt = lambda *sh: torch.randn(*sh, device="cuda").to(torch.bfloat16)
@@ -307,17 +414,15 @@ def probes():
         g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z),
              torch.empty_like(r)]
         dgam = torch.empty(dv, device="cuda")
-        tf = _time_us(lambda: dig.dig_gla_fwd(desc, q, k, v, z, r, None, y, None, saved, fws, fwb))
-        tb = _time_us(lambda: dig.dig_gla_bwd(desc, q, k, v, z, r, None, dy, saved, *g, dgam,
-                                              bws, bwb))
+        f = lambda: dig.dig_gla_fwd(desc, q, k, v, z, r, None, y, None, saved, fws, fwb)
+        bw = lambda: dig.dig_gla_bwd(desc, q, k, v, z, r, None, dy, saved, *g, dgam, bws, bwb)
         th = B * L * H
-        for name, t, byts in (("fwd", tf, 2 * (3 * dk + 3 * dv) * th),
-                              ("bwd", tb, 2 * (6 * dk + 5 * dv) * th)):
-            gbs = byts / (t / 1e6) / 1e9
-            out["%s_%s" % (label, name)] = {
-                "call": "dig_gla_" + name, "shape": [B, L, H, dk, dv], "us": round(t, 1),
-                "tokens_per_s": round(B * L / (t / 1e6), 1), "achieved_gbs": round(gbs, 1),
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        for name, fn, byts in (("fwd", f, 2 * (3 * dk + 3 * dv) * th),
+                               ("bwd", bw, 2 * (6 * dk + 5 * dv) * th)):
+            for mode in ("warm", "cold"):
+                us = _time_us(fn, cold=cold if mode == "cold" else None)
+                rec("%s_%s_%s" % (label, name, mode), "dig_gla_" + name, [B, L, H, dk, dv], us,
+                    byts, tokens_per_s=round(B * L / (us / 1e6), 1))
         del q, k, v, r, z, dy, y, g, fws, bws, saved
 
     def srem(label, B, gh, gw, D):
@@ -331,38 +436,120 @@ def probes():
         nb = x.numel() * 2
         R, C = dig.DIG_SCAN_ROW, dig.DIG_SCAN_COL
         cases = (
-            ("reorient", lambda: dig.dig_srem_reorient(B, gh, gw, D, dig.DIG_BF16, R, C, x, y), 2 * nb),
-            ("dwconv3x3", lambda: dig.dig_dwconv3x3(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, None, y),
-             2 * nb),
-            ("dwconv3x3_bwd", lambda: dig.dig_dwconv3x3_bwd(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, dy,
-                                                           dx, dw, db, ws, wsb), 3 * nb))
-        for name, fn, byts in cases:
-            t = _time_us(fn)
-            gbs = byts / (t / 1e6) / 1e9
-            out["%s_%s" % (label, name)] = {
-                "call": "dig_" + ("srem_" + name if name == "reorient" else name),
-                "shape": [B, gh, gw, D], "us": round(t, 1), "achieved_gbs": round(gbs, 1),
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        # reference ceiling: the runtime's own device copy of the same bytes (torch copy_)
-        t = _time_us(lambda: y.copy_(x))
-        gbs = 2 * nb / (t / 1e6) / 1e9
-        out["%s_copy_ref" % label] = {
-            "call": "torch copy_ (reference, not the library)", "shape": [B, gh, gw, D],
-            "us": round(t, 1), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            ("reorient", "dig_srem_reorient",
+             lambda: dig.dig_srem_reorient(B, gh, gw, D, dig.DIG_BF16, R, C, x, y), 2 * nb),
+            ("dwconv3x3", "dig_dwconv3x3",
+             lambda: dig.dig_dwconv3x3(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, None, y), 2 * nb),
+            ("dwconv3x3_bwd", "dig_dwconv3x3_bwd",
+             lambda: dig.dig_dwconv3x3_bwd(B, gh, gw, D, dig.DIG_BF16, R, C, x, w, dy, dx, dw, db,
+                                           ws, wsb), 3 * nb),
+            ("copy_ceiling", "streaming copy (probe kernel, not the library)",
+             lambda: device_copy(PL, x, y), 2 * nb))
+        for mode in ("warm", "cold"):
+            for name, call, fn, byts in cases:
+                us = _time_us(fn, cold=cold if mode == "cold" else None)
+                rec("%s_%s_%s" % (label, name, mode), call, [B, gh, gw, D], us, byts)
+            ceil = out["%s_copy_ceiling_%s" % (label, mode)]["achieved_gbs"]
+            for name, *_ in cases[:3]:
+                e = out["%s_%s_%s" % (label, name, mode)]
+                e["frac_of_copy_ceiling"] = round(e["achieved_gbs"] / ceil, 4)
         del x, dy, y, dx, ws
 
     gla("s2_b256", 256, 256, 6, 32, 64)
     c5 = W.CONFIGS["dig_xl2_2048"]
-    gla("xl2_2048", c5.batch, c5.seq_len, c5.heads, c5.d_k, c5.d_v)
     srem("xl2_2048", c5.batch, c5.grid_h, c5.grid_w, c5.d_model)
     # 16 images: 604 MB per tensor, past the 256 MB Infinity Cache (HBM streaming regime)
     srem("xl2_2048_b16", 16, c5.grid_h, c5.grid_w, c5.d_model)
+    del flush
     torch.cuda.empty_cache()
     return out
 
 
+# ------------------------------------------------------------------ CPU baseline
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_leg(spec):
+    """Child process (no GPU): times the fp64 oracle on a bounded sample of one
+    configuration's step and prints one JSON line.  spec = "<workload>:<blocks>:<div>:<min_s>":
+    `blocks` blocks, each over heads / div of the heads and d_model / div of the channels."""
+    import oracle
+    name, nblk, div, min_s = spec.split(":")
+    cfg, nblk, div, min_s = W.CONFIGS[name], int(nblk), int(div), float(min_s)
+    cfg = W.cfg_replace(cfg, heads=cfg.heads // div, d_model=cfg.d_model // div)
+    case = W.make_gla_case(cfg)
+    srem = W.make_srem_case(cfg)
+    gh, gw = cfg.grid_h, cfg.grid_w
+    best, reps, t_all = None, 0, time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for l in range(nblk):
+            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
+            oracle.gla_fwd(case.q, case.k, case.v, case.z, case.r, case.gamma)
+            oracle.dwconv3x3(srem.x, srem.w, gh, gw, d0, d1)
+        for l in reversed(range(nblk)):
+            d0, d1 = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
+            oracle.dwconv3x3_bwd(srem.x, srem.w, srem.dy, gh, gw, d0, d1)
+            oracle.gla_bwd(case.q, case.k, case.v, case.z, case.r, case.dy, case.gamma)
+        t = time.perf_counter() - t0
+        best = t if best is None else min(best, t)
+        reps += 1
+        if (reps >= 3 and time.perf_counter() - t_all > min_s) or time.perf_counter() - t_all > 3 * min_s:
+            break
+    print(json.dumps({"seconds_best": best, "reps": reps, "threads": oracle.num_threads(),
+                      "wall": time.perf_counter() - t_all}), flush=True)
+
+
+def cpu_baseline(cfg):
+    """The oracle (untuned) on this host: a bounded sample of the headline step (one block in
+    its first scan direction; a quarter of the heads and channels for the single-thread leg),
+    best of at least three repetitions, single-threaded and on every thread OpenMP is given
+    (each leg in a child process); the oracle's work is linear in heads, channels and blocks,
+    so the sample's time is scaled to GLA-layer tokens/s of the full step."""
+    import subprocess
+    nb = n_blocks(cfg)
+    res, divs = {}, {}
+    # the oracle runs its (image, head) units in parallel: the all-threads leg keeps every head
+    for leg, threads, div in (("single_thread", "1", 4), ("all_threads", None, 1)):
+        divs[leg] = div
+        env = dict(os.environ)
+        if threads:
+            env["OMP_NUM_THREADS"] = threads
+        cmd = [sys.executable, os.path.abspath(__file__), "--oracle-leg",
+               "%s:1:%d:4.0" % (cfg.name, div)]
+        p = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+        if p.returncode != 0:
+            raise RuntimeError("oracle leg failed: %s" % p.stderr[-2000:])
+        r = json.loads(p.stdout.strip().splitlines()[-1])
+        step_s = r["seconds_best"] * div * nb          # the full step's time at this rate
+        res[leg] = {"value": round(cfg.batch * cfg.seq_len * nb / step_s, 1),
+                    "cores": r["threads"], "sample_seconds_best": round(r["seconds_best"], 3),
+                    "reps": r["reps"]}
+    allc = res["all_threads"]
+    return {"value": allc["value"], "unit": "GLA-layer tokens/s (fwd+bwd)", "cores": allc["cores"],
+            "kind": "oracle",
+            "sample": "fp64 oracle fwd+bwd (GLA mixer + conv/reorient) of one %s block, best "
+                      "of >= 3 repetitions, scaled to the %d-block step: all threads over all "
+                      "%d heads and %d channels, single thread over %d heads and %d channels"
+                      % (cfg.name, nb, cfg.heads, cfg.d_model, cfg.heads // divs["single_thread"],
+                         cfg.d_model // divs["single_thread"]),
+            "host_cpu": _cpu_model(), "single_thread": res["single_thread"],
+            "all_threads": allc}
+
+
 def main():
     args = parse()
+    if args.oracle_leg:
+        oracle_leg(args.oracle_leg)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path here has no multi-GPU leg "
               "(data-parallel sharding is a design note, not built). Run with --gpus 1.",
@@ -373,11 +560,12 @@ def main():
         copy_probe(args.copy_probe_mib, max(1, args.steps))
         return
     cfg = W.CONFIGS[args.workload]
-    nblocks = cfg.blocks
-    blocks = gen_blocks(cfg, nblocks, cfg.seed)
-    path = Path(cfg, blocks, args.seg_chunks)
-    torch.cuda.synchronize()
+    nblocks = n_blocks(cfg)
     if args.pmc_target:  # one library call per block, `steps` times (for counter runs)
+        path = Path(cfg, gen_blocks(cfg, nblocks, cfg.seed), args.seg_chunks)
+        for l in range(nblocks):  # the forward's saved buffers feed the backward
+            path.gla_fwd(l)
+        torch.cuda.synchronize()
         fn = getattr(path, args.pmc_target)
         for _ in range(args.steps):
             for l in range(nblocks):
@@ -387,6 +575,9 @@ def main():
               flush=True)
         return
 
+    blocks = gen_blocks(cfg, nblocks, cfg.seed)
+    path = Path(cfg, blocks, args.seg_chunks)
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
@@ -400,6 +591,8 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    tokens = cfg.batch * cfg.seq_len * nblocks
+    value = tokens / (ms / 1e3)
 
     # second timed pass of K steps with HIP events around every GLA call (kept out of the
     # first: recording events between calls adds host work and stream markers)
@@ -412,20 +605,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_ev = s1.elapsed_time(e1) / args.steps
-    tokens = cfg.batch * cfg.seq_len * nblocks
-    value = tokens / (ms / 1e3)
-
-    # forward-only figure (same calls without the backward), reported beside the main value
-    for _ in range(3):
-        path.step_fwd()
-    torch.cuda.synchronize()
-    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s2.record()
-    for _ in range(args.steps):
-        path.step_fwd()
-    e2.record()
-    torch.cuda.synchronize()
-    ms_fwd = s2.elapsed_time(e2) / args.steps
+    ms_fwd = timed(path.step_fwd, args.steps, 3)
 
     th = cfg.batch * cfg.seq_len * cfg.heads
     rl = {}
@@ -434,18 +614,19 @@ def main():
         byts = gla_bytes_per_token_head(cfg, which) * th
         rl[name] = {"ms": t, "bytes": byts, "gbs": byts / (t / 1e3) / 1e9}
     dom = max(rl, key=lambda n: rl[n]["ms"])
-    traffic = measured_traffic(cfg.name, "dig_" + dom)
+    other = [n for n in rl if n != dom][0]
     roof = {"bound": "hbm", "achieved": round(rl[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(rl[dom]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": KERNEL_OF_CALL[dom],
+            "traffic": measured_traffic(cfg.name, "dig_" + dom),
             "call": "dig_" + dom, "avg_call_us": round(rl[dom]["ms"] * 1e3, 2),
             "algorithmic_bytes_per_launch": rl[dom]["bytes"],
-            "note": "per library call: HIP events bracket the whole call on its stream, "
-                    "in a second timed pass of the same K steps (%.4f ms/step with the events)"
-                    % ms_ev}
-    other = [n for n in rl if n != dom][0]
-    traffic_other = measured_traffic(cfg.name, "dig_" + other)
+            "bytes_per_token_head": gla_bytes_per_token_head(cfg, dom[4:]),
+            "source": "HIP events around each dig_%s call on the stream its kernels run on, in a "
+                      "second timed pass of the same K steps (%.4f ms/step with the events); the "
+                      "rocprofv3 kernel-trace summary of this command gives the call's kernel "
+                      "durations" % (dom, ms_ev)}
+    del path, blocks
+    torch.cuda.empty_cache()
     out = {
         "metric": "GLA-layer tokens/s (fwd+bwd)",
         "value": round(value, 1),
@@ -462,19 +643,31 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "grid": [cfg.grid_h, cfg.grid_w],
                    "seq_len": cfg.seq_len, "d_model": cfg.d_model, "heads": cfg.heads,
                    "d_k": cfg.d_k, "d_v": cfg.d_v, "chunk": cfg.chunk, "blocks": nblocks,
-                   "step": "12 x (gla_fwd + dwconv3x3 reorient) + 12 x (dwconv3x3_bwd + gla_bwd)"},
+                   "step": "%d x (gla_fwd + dwconv3x3 reorient) + %d x (dwconv3x3_bwd + gla_bwd), "
+                           "scan directions cycling row, row_rev, col, col_rev"
+                           % (nblocks, nblocks)},
         "fwd_only": {"value": round(tokens / (ms_fwd / 1e3), 1), "unit": "tokens/s",
                      "ms_per_step": round(ms_fwd, 4)},
         "roofline": roof,
         "roofline_other_call": {"call": "dig_" + other, "avg_call_us": round(rl[other]["ms"] * 1e3, 2),
                                 "achieved_gbs": round(rl[other]["gbs"], 1),
                                 "frac": round(rl[other]["gbs"] / HBM_PEAK_GBS, 4),
-                                "kernel": KERNEL_OF_CALL[other], "traffic": traffic_other},
+                                "traffic": measured_traffic(cfg.name, "dig_" + other)},
     }
     if not args.no_probes:
+        configs = {}
+        for name in ("dig_s2_256", "dig_s2_1792", "dig_xl2_1024"):
+            if name == cfg.name:
+                continue
+            c = W.CONFIGS[name]
+            configs[name], _ = run_config(c, max(10, args.steps // 2), 3,
+                                          fwd_only=(name == "dig_xl2_1024"))
+            print("[bench] %s done" % name, file=sys.stderr, flush=True)
+        out["configs"] = configs
+        out["mfma_microbench"] = contraction_microbench()
         out["probes"] = probes()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, nblocks)
+        out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)
 
 

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdig.so")
+PROBE_LIB = os.path.join(HERE, "libdig_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["dig_api.cpp", "gla_fwd.hip", "gla_fwd_bf16.hip", "gla_fwd_f32.hip", "gla_bwd.hip",
            "gla_bwd_bf16.hip", "gla_bwd_f32.hip", "srem.hip"]
@@ -64,7 +65,18 @@ def build(verbose: bool = False, force: bool = True) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    build_probe(hipcc)
     return LIB
+
+
+def build_probe(hipcc: str) -> str:
+    """libdig_probe.so: the measurement kernels bench.py times (contraction microbenchmark,
+    streaming copy); not part of libdig.so."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc] + FLAGS + ["-shared", "-o", tmp, os.path.join(CSRC, "probe.hip")],
+                          stderr=subprocess.DEVNULL)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
