@@ -66,6 +66,7 @@ def _load():
         lib.oref_dwconv3x3.argtypes = [i, i64, i64, i, i, i, D, D, D, D]
         lib.oref_dwconv3x3_bwd.argtypes = [i, i64, i64, i, i, i, D, D, D, D, D, D]
         lib.oref_num_threads.restype = i
+        lib.oref_linear.argtypes = [i64, i64, i64, D, D, D, D]
         _lib = lib
     return _lib
 
@@ -213,3 +214,16 @@ def dwconv3x3_bwd(x, w, dy, gh: int, gw: int, layout: int, out_layout: int):
     _load().oref_dwconv3x3_bwd(B, gh, gw, D, int(layout), int(out_layout), _p(x), _p(w), _p(dy),
                                _p(dx), _p(dw), _p(db))
     return dx, dw, db
+
+
+# ------------------------------------------------------------------- projections
+def linear(a, w, bias=None):
+    """c = a w^T (+ bias): a [..., k], w [n, k] (out x in features), bias [n] or None."""
+    a, w = _f64(a), _f64(w)
+    k = a.shape[-1]
+    m = a.size // k if k else 0
+    n = w.shape[0]
+    b = None if bias is None else _f64(bias)
+    c = np.empty(a.shape[:-1] + (n,))
+    _load().oref_linear(m, k, n, _p(a), _p(w), _p(b), _p(c))
+    return c

@@ -449,6 +449,26 @@ void oref_dwconv3x3_bwd(int B, int64_t gh, int64_t gw, int D, int layout, int ou
     free(inv_to);
 }
 
+/*
+ * Linear projection around the token mixer (DiG study-group slides, slide introducing GLA,
+ * eqs. (5), (9), (10): Q = X W_Q, K = X W_K, V = X W_V, the gate logits, R = X W_r + b_r and
+ * Y = (...) W_O), with the weight stored as (out features x in features):
+ *   c[i][j] = sum_l a[i][l] w[j][l] + bias[j]          (bias may be NULL: no bias)
+ * a [m][k], w [n][k], c [m][n], fp64, the plain definition (rows in parallel).
+ */
+void oref_linear(int64_t m, int64_t k, int64_t n, const double *a, const double *w,
+                 const double *bias, double *c)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int64_t l = 0; l < k; ++l)
+                acc += a[(size_t)i * k + l] * w[(size_t)j * k + l];
+            c[(size_t)i * n + j] = acc + (bias ? bias[j] : 0.0);
+        }
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int oref_num_threads(void)
 {
