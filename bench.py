@@ -353,6 +353,64 @@ def contraction_microbench():
     return res
 
 
+def projections(cfg, steps):
+    """The projections around the mixer (dig_linear, bf16 matrix cores) at one configuration's
+    size, timed alone (MFMA-bound: flops against the 2.5 PFLOP/s bf16 peak), and one layer's
+    forward with them: x -> q, k, v, rank-16 gate factor, r (one launch) -> gate logits
+    (rank 16 -> H d_k, + bias) -> dig_gla_fwd -> output projection -> dig_dwconv3x3 (fused
+    reorient).  Random-init weights of the layer's shapes."""
+    import torch
+    import diffusion_backbone_amd as dig
+    B, L, D, H, dk, dv = cfg.batch, cfg.seq_len, cfg.d_model, cfg.heads, cfg.d_k, cfg.d_v
+    M = B * L
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 5)
+    bf = lambda *sh, s=1.0: (torch.randn(*sh, device="cuda", generator=g) * s).to(torch.bfloat16)
+    x = bf(B, L, D)
+    s = 1.0 / np.sqrt(D)
+    wq, wk, wv, wr = bf(H * dk, D, s=s), bf(H * dk, D, s=s), bf(H * dv, D, s=s), bf(H * dv, D, s=s)
+    wa1, wa2 = bf(cfg.rank, D, s=s), bf(H * dk, cfg.rank, s=s)
+    wo = bf(D, H * dv, s=s)
+    b_alpha = torch.zeros(H * dk, device="cuda")
+    q, k, z = bf(B, L, H, dk), bf(B, L, H, dk), bf(B, L, H, dk)
+    v, r, y = bf(B, L, H, dv), bf(B, L, H, dv), bf(B, L, H, dv)
+    zl = bf(B, L, cfg.rank)
+    yo, xs = bf(B, L, D), bf(B, L, D)
+    cw = torch.randn(D, 3, 3, device="cuda", generator=g) / 3.0
+    gamma = torch.ones(dv, device="cuda")
+    desc = dig.make_desc(B, L, H, dk, dv, cfg.chunk, cfg.tau, 1.0, 1e-5, dig.DIG_BF16, 0)
+    fwb = dig.dig_gla_fwd_workspace_bytes(desc)
+    fws = torch.empty(max(fwb, 16), dtype=torch.uint8, device="cuda")
+    proj_in = lambda: dig.dig_linear(M, D, x, [(q, wq, None), (k, wk, None), (v, wv, None),
+                                               (zl, wa1, None), (r, wr, None)])
+    gate_up = lambda: dig.dig_linear(M, cfg.rank, zl, [(z, wa2, b_alpha)])
+    proj_out = lambda: dig.dig_linear(M, H * dv, y, [(yo, wo, None)])
+    n_in = 2 * H * dk + 2 * H * dv + cfg.rank
+    res = {}
+    for name, fn, flops in (("in_projection", proj_in, 2.0 * M * D * n_in),
+                            ("gate_up_projection", gate_up, 2.0 * M * cfg.rank * H * dk),
+                            ("out_projection", proj_out, 2.0 * M * H * dv * D)):
+        ms = timed(fn, steps, 3)
+        tf = flops / (ms / 1e3) / 1e12
+        res[name] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops}
+
+    def layer():
+        proj_in()
+        gate_up()
+        dig.dig_gla_fwd(desc, q, k, v, z, r, gamma, y, None, None, fws, fwb)
+        proj_out()
+        dig.dig_dwconv3x3(B, cfg.grid_h, cfg.grid_w, D, dig.DIG_BF16, W.ROW, W.ROW_REV, yo, cw,
+                          None, xs)
+    ms = timed(layer, steps, 3)
+    res["layer_fwd_with_projections"] = {
+        "what": "in-projection, gate up-projection, dig_gla_fwd, out-projection, dig_dwconv3x3 "
+                "(fused reorient), one block", "ms": round(ms, 4),
+        "tokens_per_s": round(M / (ms / 1e3), 1)}
+    res["workload"] = cfg.name
+    return res
+
+
 def _median(xs):
     xs = sorted(xs)
     return xs[len(xs) // 2]
@@ -664,6 +722,7 @@ def main():
                                           fwd_only=(name == "dig_xl2_1024"))
             print("[bench] %s done" % name, file=sys.stderr, flush=True)
         out["configs"] = configs
+        out["projections"] = projections(cfg, max(10, args.steps // 2))
         out["mfma_microbench"] = contraction_microbench()
         out["probes"] = probes()
     if not args.no_cpu_baseline:

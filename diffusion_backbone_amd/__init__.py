@@ -27,14 +27,20 @@ EXPORTS = (
     "dig_gla_bwd_workspace_bytes", "dig_gla_bwd", "dig_srem_reorient", "dig_dwconv3x3",
     "dig_dwconv3x3_bwd_workspace_bytes", "dig_dwconv3x3_bwd", "dig_status_str",
     "dig_last_error", "dig_abi_version", "dig_lookback_status", "dig_debug_lookback",
-    "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes",
+    "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes", "dig_linear",
 )
+DIG_LINEAR_MAX_OUT = 6
 
 
 class DigError(RuntimeError):
     def __init__(self, status: int, func: str, detail: str):
         self.status = status
         super().__init__("%s failed: %s (%s)" % (func, _status_name(status), detail))
+
+
+class dig_linear_out(ctypes.Structure):
+    _fields_ = [("c", ctypes.c_void_p), ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("n", ctypes.c_int32)]
 
 
 class dig_gla_desc(ctypes.Structure):
@@ -96,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.dig_dwconv3x3_bwd_noalloc.restype = ctypes.c_int
         L.dig_dwconv3x3_bwd_noalloc_max_bytes.argtypes = []
         L.dig_dwconv3x3_bwd_noalloc_max_bytes.restype = S
+        L.dig_linear.argtypes = [I, I, I, P, I, ctypes.POINTER(dig_linear_out), P]
+        L.dig_linear.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -219,3 +227,13 @@ def dig_dwconv3x3_bwd_noalloc(batch, grid_h, grid_w, channels, dtype, layout, ou
 
 def dig_dwconv3x3_bwd_noalloc_max_bytes() -> int:
     return lib().dig_dwconv3x3_bwd_noalloc_max_bytes()
+
+
+
+def dig_linear(m, k, a, outs, stream=None):
+    """outs: sequence of (c, w, bias_or_None) tensors; c [m, n] bf16, w [n, k] bf16."""
+    arr = (dig_linear_out * max(len(outs), 1))()
+    for i, (c, w, b) in enumerate(outs):
+        arr[i] = dig_linear_out(_ptr(c), _ptr(w), _ptr(b), int(w.shape[0]))
+    st = lib().dig_linear(int(m), int(k), DIG_BF16, _ptr(a), len(outs), arr, _stream(stream))
+    _check(st, "dig_linear")

@@ -414,6 +414,42 @@ dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int3
 
 size_t dig_dwconv3x3_bwd_noalloc_max_bytes(void) { return dig::kNoAllocScratchBytes; }
 
+dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                      const dig_linear_out* outs, hipStream_t stream) {
+  if (dtype != DIG_BF16) return fail(DIG_ERR_UNSUPPORTED, "dig_linear runs on bf16 operands");
+  if (m < 0 || k < 1) return fail(DIG_ERR_SHAPE, "m must be >= 0 and k >= 1");
+  if (n_out < 1 || n_out > DIG_LINEAR_MAX_OUT)
+    return fail(DIG_ERR_SHAPE, "n_out must be 1..%d", (int)DIG_LINEAR_MAX_OUT);
+  if (!outs) return fail(DIG_ERR_NULL, "outs is required");
+  if (k % 8) return fail(DIG_ERR_UNSUPPORTED, "k must be a multiple of 8 (16-byte rows)");
+  if ((long long)(m + 127) / 128 > 65535) return fail(DIG_ERR_UNSUPPORTED, "m too large");
+  for (int i = 0; i < n_out; ++i) {
+    if (outs[i].n < 1) return fail(DIG_ERR_SHAPE, "outs[%d].n must be >= 1", i);
+    if (outs[i].n % 8) return fail(DIG_ERR_UNSUPPORTED, "outs[%d].n must be a multiple of 8", i);
+  }
+  if (m == 0) return ok();
+  if (!a) return fail(DIG_ERR_NULL, "a is required");
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i].c || !outs[i].w) return fail(DIG_ERR_NULL, "outs[%d].c and .w are required", i);
+  if (!aligned16(a)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  for (int i = 0; i < n_out; ++i)
+    if (!aligned16(outs[i].c) || !aligned16(outs[i].w) || (outs[i].bias && !aligned16(outs[i].bias)))
+      return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  Range in[1 + 2 * DIG_LINEAR_MAX_OUT], out[DIG_LINEAR_MAX_OUT];
+  int nin = 0;
+  in[nin++] = rng("a", a, (size_t)m * k * 2);
+  for (int i = 0; i < n_out; ++i) {
+    in[nin++] = rng("w", outs[i].w, (size_t)outs[i].n * k * 2);
+    in[nin++] = rng("bias", outs[i].bias, outs[i].bias ? (size_t)outs[i].n * 4 : 0);
+    out[i] = rng("c", outs[i].c, (size_t)m * outs[i].n * 2);
+  }
+  dig_status st = check_alias(in, nin, out, n_out);
+  if (st != DIG_OK) return st;
+  dig::LinearOut lo[DIG_LINEAR_MAX_OUT];
+  for (int i = 0; i < n_out; ++i) lo[i] = {outs[i].c, outs[i].w, outs[i].bias, outs[i].n};
+  return check_dev(dig::launch_linear(m, k, a, n_out, lo, stream), "dig_linear launch");
+}
+
 dig_status dig_dwconv3x3_bwd_noalloc(int32_t batch, int32_t grid_h, int32_t grid_w,
                                      int32_t channels, int32_t dtype, int32_t layout,
                                      int32_t out_layout, const void* x, const float* w,

@@ -129,6 +129,18 @@ void set_lookback_wait(unsigned spins, bool never_match);
 unsigned* lookback_status_word();
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
+// ------------------------------------------------------------------- projections
+constexpr int kLinearMaxOut = 6;
+struct LinearOut {
+  void* c;             // [M][n] bf16
+  const void* w;       // [n][K] bf16 (out features x in features)
+  const float* bias;   // [n] fp32 or null
+  int n;
+};
+// C_o = A W_o^T (+ bias_o) for every output o, A [M][K] bf16, one launch.
+hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
+                         hipStream_t st);
+
 // ------------------------------------------------------------------------- misc
 // Zero n floats with a kernel (usable inside captured graphs, unlike a memset node).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);

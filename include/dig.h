@@ -137,6 +137,32 @@ dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, c
                        void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ projections */
+
+/*
+ * dig_linear -- the projections around the token mixer (slides eqs. (5), (9), (10):
+ * Q = X W_Q, K = X W_K, V = X W_V, the low-rank gate logits (X W_a1) W_a2 + b_alpha,
+ * R = X W_r + b_r, Y = (Swish(R) * Norm(O)) W_O) as one bf16 matrix-core launch:
+ *   outs[o].c[i][j] = sum_l a[i][l] * outs[o].w[j][l]  (+ outs[o].bias[j])
+ * for every output o (up to DIG_LINEAR_MAX_OUT sharing the input a), fp32 accumulation,
+ * result rounded to bf16 (round to nearest even).
+ *   a          : [m][k] bf16, row-major (m rows, e.g. batch * tokens)
+ *   outs[o].w  : [n][k] bf16 (out features x in features, as a linear layer's weight)
+ *   outs[o].bias : [n] fp32 or NULL
+ *   outs[o].c  : [m][n] bf16 output (contiguous: [B, L, H, d] for the mixer's operands)
+ * dtype must be DIG_BF16; k and every n must be multiples of 8.  Outputs may not overlap
+ * inputs or each other (DIG_ERR_ALIAS).
+ */
+#define DIG_LINEAR_MAX_OUT 6
+typedef struct {
+  void* c;
+  const void* w;
+  const float* bias;
+  int32_t n;
+} dig_linear_out;
+dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                      const dig_linear_out* outs, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- SREM */
 
 /*
