@@ -75,30 +75,46 @@ template <typename T> struct Mma;
 // otherwise ("row-contiguous") at base[k * ld + row].  For an A operand the row is M, for a
 // B operand it is N.  KC reads are single vector loads, the other form is strided.
 
+// K-major tiles (element (row, k) at base[k * ld + row]) reach the MFMA lane layout through
+// the gfx950 LDS transpose load: in each 16-lane group, lane L reads the four elements of
+// K row k0 + L/4 at rows m0 + 4 (L % 4) .. +3 (8 bytes), and the load hands lane j the four
+// K rows k0 .. k0+3 of row m0 + j.  The group reads exactly the 16 x 4 elements the lanes
+// need (no other LDS address); ld and m0 are multiples of 4 and the base 8-byte aligned, so
+// every 8-byte read is aligned.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* base, int ld, int m0, int k0, int r) {
+  const bf16* p = base + (k0 + (r >> 2)) * ld + m0 + 4 * (r & 3);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 // bf16: K step 32; lane group g owns k = 8g..8g+7 of each step.
 template <> struct Mma<bf16> {
   static constexpr int KSTEP = 32;
+  // fragment of rows m0 + r (r = lane % 16), K slice k..k+7 (KC: K-contiguous rows; else a
+  // K-major tile read through the transpose load)
   template <bool KC>
-  __device__ static __forceinline__ bf16x8 frag(const bf16* base, int ld, int row, int k) {
+  __device__ static __forceinline__ bf16x8 frag(const bf16* base, int ld, int m0, int r, int k) {
     if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8*>(base + row * ld + k);
+      return *reinterpret_cast<const bf16x8*>(base + (m0 + r) * ld + k);
     } else {
+      const bf16x4 lo = lds_tr4(base, ld, m0, k, r), hi = lds_tr4(base, ld, m0, k + 4, r);
       bf16x8 v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = base[(k + i) * ld + row];
+      for (int i = 0; i < 4; ++i) { v[i] = lo[i]; v[4 + i] = hi[i]; }
       return v;
     }
   }
   template <bool KC>
-  __device__ static __forceinline__ bf16x4 frag4(const bf16* base, int ld, int row, int k) {
-    if constexpr (KC) {
-      return *reinterpret_cast<const bf16x4*>(base + row * ld + k);
-    } else {
-      bf16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = base[(k + i) * ld + row];
-      return v;
-    }
+  __device__ static __forceinline__ bf16x4 frag4(const bf16* base, int ld, int m0, int r, int k) {
+    if constexpr (KC) return *reinterpret_cast<const bf16x4*>(base + (m0 + r) * ld + k);
+    else return lds_tr4(base, ld, m0, k, r);
+  }
+  template <bool KC>
+  __device__ static __forceinline__ bf16x8 frag(const bf16* base, int ld, int row, int k) {
+    static_assert(KC, "K-major fragments take the tile's first row");
+    return *reinterpret_cast<const bf16x8*>(base + row * ld + k);
   }
   // acc += sum_{k<K} A(m0 + m, k) * B(k, n0 + n); K a multiple of 16 (a final 16 runs as a
   // 16x16x32 step with half of each lane's slots zero)
@@ -108,11 +124,11 @@ template <> struct Mma<bf16> {
     const int r = lane & 15, g = lane >> 4;
     int k = 0;
     for (; k + 32 <= K; k += 32)
-      acc = mfma_bf16(frag<AKC>(A, lda, m0 + r, k + 8 * g), frag<BKC>(B, ldb, n0 + r, k + 8 * g),
+      acc = mfma_bf16(frag<AKC>(A, lda, m0, r, k + 8 * g), frag<BKC>(B, ldb, n0, r, k + 8 * g),
                       acc);
     if (k < K) {  // K tail of 16: each lane group's 4 live k in slots 0-3, zeros in 4-7
-      const bf16x4 a4 = frag4<AKC>(A, lda, m0 + r, k + 4 * g);
-      const bf16x4 b4 = frag4<BKC>(B, ldb, n0 + r, k + 4 * g);
+      const bf16x4 a4 = frag4<AKC>(A, lda, m0, r, k + 4 * g);
+      const bf16x4 b4 = frag4<BKC>(B, ldb, n0, r, k + 4 * g);
       bf16x8 a, b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
