@@ -422,7 +422,7 @@ dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_
     return fail(DIG_ERR_SHAPE, "n_out must be 1..%d", (int)DIG_LINEAR_MAX_OUT);
   if (!outs) return fail(DIG_ERR_NULL, "outs is required");
   if (k % 8) return fail(DIG_ERR_UNSUPPORTED, "k must be a multiple of 8 (16-byte rows)");
-  if ((long long)(m + 127) / 128 > 65535) return fail(DIG_ERR_UNSUPPORTED, "m too large");
+  if ((long long)(m + 255) / 256 > 65535) return fail(DIG_ERR_UNSUPPORTED, "m too large");
   for (int i = 0; i < n_out; ++i) {
     if (outs[i].n < 1) return fail(DIG_ERR_SHAPE, "outs[%d].n must be >= 1", i);
     if (outs[i].n % 8) return fail(DIG_ERR_UNSUPPORTED, "outs[%d].n must be a multiple of 8", i);

@@ -6,19 +6,18 @@
 //
 // One launch covers every output: the grid runs over (row tile, column tile of the
 // concatenated outputs), and a tile never straddles two outputs.  Tiles of 128 x 128 outputs,
-// four waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16, K step 32), K blocks of 64 staged in
-// LDS (A rows and W rows, both K-contiguous, 144-byte pitch) with the next block loaded into
-// registers while the current one is multiplied (two LDS buffers).  fp32 accumulation; bias
-// added in fp32; bf16 output stored from LDS in 16-byte row pieces.
+// four waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32, K step 16: on gfx950 the 32x32x16 bf16
+// instruction sustains about 1.7 times the rate of 16x16x32), K blocks of 32 staged in LDS
+// (A rows and W rows, both K-contiguous, 80-byte pitch: conflict-free 16-byte reads) with the
+// next block loaded into registers while the current one is multiplied (two LDS buffers);
+// three workgroups per compute unit.  fp32 accumulation; bias added in fp32; bf16 output
+// stored from LDS in 16-byte row pieces.
 #include "dig_device.h"
 #include "dig_internal.h"
 
 namespace dig {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LPITCH = BK + 8;  // elements
-constexpr int NTHR = 256;
-constexpr int CPITCH = BN + 8;                                 // epilogue staging pitch
 
 struct LinOut {
   bf16* c;
@@ -33,37 +32,58 @@ struct LinParams {
   LinOut out[kLinearMaxOut];
 };
 
-// 128 rows x 64 bf16 (one K block of a tile) of a K-contiguous source into registers: thread
-// t takes rows t / 4 and t / 4 + 64, 16-byte pieces (t % 4) * 2 and (t % 4) * 2 + 1 of each.
-// Rows past `rows` and columns past K read as zero.
-struct BlockRegs {
-  uint4 v[4];
+// Square tiles of BM x BM outputs, (BM / 64)^2 waves of 64 x 64.
+template <int BM>
+struct Tile {
+  static constexpr int BN = BM, NTHR = (BM / 64) * (BM / 64) * 64, CPITCH = BN + 8;
 };
-__device__ __forceinline__ void load_block(BlockRegs& r, const bf16* src, int rows, int K, int r0,
-                                           int k0, int tid) {
+
+// BM rows x BK bf16 (one K block of a tile) of a K-contiguous source into registers: the
+// tile's BM * BK / 8 16-byte pieces, NP per thread (thread t: pieces t + NTHR u, piece q at
+// row q / (BK / 8), K piece q % (BK / 8)).  Rows past `rows` and columns past K read as zero.
+template <int BM, int BK>
+struct BlockRegs {
+  static constexpr int NTHR = Tile<BM>::NTHR, PPR = BK / 8, NP = BM * PPR / NTHR;
+  static_assert(BM * PPR % NTHR == 0, "pieces per thread");
+  uint4 v[NP];
+};
+template <int BM, int BK>
+__device__ __forceinline__ void load_block(BlockRegs<BM, BK>& r, const bf16* src, int rows, int K,
+                                           int r0, int k0, int tid) {
+  constexpr int PPR = BlockRegs<BM, BK>::PPR, NTHR = Tile<BM>::NTHR;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = (tid >> 2) + 64 * (u >> 1), piece = (tid & 3) * 2 + (u & 1);
+  for (int u = 0; u < BlockRegs<BM, BK>::NP; ++u) {
+    const int q = tid + NTHR * u, row = q / PPR, piece = q % PPR;
     const int gr = r0 + row, gk = k0 + piece * 8;
     const bool in = gr < rows && gk < K;
     const uint4 x = *reinterpret_cast<const uint4*>(src + (long)(in ? gr : 0) * K + (in ? gk : 0));
     r.v[u] = in ? x : make_uint4(0, 0, 0, 0);
   }
 }
-__device__ __forceinline__ void store_block(const BlockRegs& r, bf16* lds, int tid) {
+template <int BM, int BK>
+__device__ __forceinline__ void store_block(const BlockRegs<BM, BK>& r, bf16* lds, int tid) {
+  constexpr int PPR = BlockRegs<BM, BK>::PPR, LPITCH = BK + 8, NTHR = Tile<BM>::NTHR;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = (tid >> 2) + 64 * (u >> 1), piece = (tid & 3) * 2 + (u & 1);
+  for (int u = 0; u < BlockRegs<BM, BK>::NP; ++u) {
+    const int q = tid + NTHR * u, row = q / PPR, piece = q % PPR;
     *reinterpret_cast<uint4*>(lds + row * LPITCH + piece * 8) = r.v[u];
   }
 }
 
-__global__ __launch_bounds__(NTHR) void linear_kernel(LinParams p) {
-  __shared__ __align__(16) bf16 sA[2][BM * LPITCH];
-  __shared__ __align__(16) bf16 sB[2][BN * LPITCH];
+template <int BM, int BK>
+__global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
+  constexpr int BN = Tile<BM>::BN, NTHR = Tile<BM>::NTHR, CPITCH = Tile<BM>::CPITCH;
+  constexpr int WPR = BM / 64;    // waves per tile row
+  constexpr int LPITCH = BK + 8;  // elements (16-byte aligned rows, conflict-free reads)
+  // the epilogue stages the 128 x 128 bf16 tile over the operand buffers
+  constexpr int SA = 2 * BM * LPITCH, SB = 2 * BN * LPITCH;
+  constexpr int SLDS = SA + SB > 128 * CPITCH ? SA + SB : 128 * CPITCH;
+  __shared__ __align__(16) bf16 lds[SLDS];
+  auto sA = [&](int b) { return lds + b * (BM * LPITCH); };
+  auto sB = [&](int b) { return lds + SA + b * (BN * LPITCH); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WPR, wn = wave % WPR;  // waves of 64 x 64
   // which output this column tile belongs to (uniform)
   const int nt = blockIdx.x;
   int o = 0;
@@ -75,41 +95,45 @@ __global__ __launch_bounds__(NTHR) void linear_kernel(LinParams p) {
   const int K = p.K;
   const int nkb = (K + BK - 1) / BK;
 
-  f32x4 acc[4][4];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  BlockRegs ra, rb;  // the next K block of the A tile and of the W tile
+  BlockRegs<BM, BK> ra, rb;  // the next K block of the A tile and of the W tile
   auto load = [&](int kb) {
     load_block(ra, p.a, p.M, K, m0, kb * BK, tid);
     load_block(rb, out.w, out.n, K, n0, kb * BK, tid);
   };
   auto put = [&](int buf) {
-    store_block(ra, sA[buf], tid);
-    store_block(rb, sB[buf], tid);
+    store_block(ra, sA(buf), tid);
+    store_block(rb, sB(buf), tid);
   };
+  // 32x32x16 operands: lane l holds row (l % 32) of its 32-row tile, K slice 8 (l / 32)..+7
+  const int r32 = lane & 31, h32 = lane >> 5;
   load(0);
   put(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     if (kb + 1 < nkb) load(kb + 1);  // in flight while this block is multiplied
-    const bf16* A = sA[buf] + (wm * 64 + r16) * LPITCH + 8 * g4;
-    const bf16* B = sB[buf] + (wn * 64 + r16) * LPITCH + 8 * g4;
+    const bf16* A = sA(buf) + (wm * 64 + r32) * LPITCH + 8 * h32;
+    const bf16* B = sB(buf) + (wn * 64 + r32) * LPITCH + 8 * h32;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(A + 16 * i * LPITCH + 32 * ks);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(B + 16 * i * LPITCH + 32 * ks);
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(A + 32 * i * LPITCH + 16 * ks);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(B + 32 * i * LPITCH + 16 * ks);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(af[i], bfr[j], acc[i][j]);
     }
     if (kb + 1 < nkb) {
       put(buf ^ 1);  // the other buffer was last read before the previous barrier
@@ -118,43 +142,44 @@ __global__ __launch_bounds__(NTHR) void linear_kernel(LinParams p) {
   }
   __syncthreads();  // every wave is done with the operand tiles: reuse them for the output
 
-  // epilogue: acc[i][j][v] = C[m0 + wm*64 + 16i + 4g4 + v][n0 + wn*64 + 16j + r16]
-  bf16* sC = sA[0];  // [BM][CPITCH] bf16 (34 816 bytes, within sA)
+  // epilogue, in BM / 128 parts of 128 rows (the staging tile fits the operand buffers):
+  // acc[i][j][v] = C[m0 + wm*64 + 32i + 8(v/4) + 4(l/32) + v%4][n0 + wn*64 + 32j + l%32]
+  bf16* sC = lds;  // [BM / 2][CPITCH] bf16
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = wn * 64 + 16 * j + r16;
-    const float bias = (out.bias && n0 + col < out.n) ? out.bias[n0 + col] : 0.f;
+  for (int half = 0; half < BM / 128; ++half) {
+    if (half) __syncthreads();  // the previous part's rows have been read
+    if ((wm >> 1) == half) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + 32 * j + r32;
+        const float bias = (out.bias && n0 + col < out.n) ? out.bias[n0 + col] : 0.f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        sC[(wm * 64 + 16 * i + 4 * g4 + v) * CPITCH + col] = from_f<bf16>(acc[i][j][v] + bias);
-  }
-  __syncthreads();
-  // rows of 128 columns = 16 pieces of 8 bf16; 2048 pieces over 256 threads
-  const bool full_n = n0 + BN <= out.n && out.n % 8 == 0;
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int piece = tid + NTHR * u;
-    const int row = piece >> 4, cp = (piece & 15) * 8;
-    const int gr = m0 + row, gc = n0 + cp;
-    if (gr >= p.M) continue;
-    const uint4 x = *reinterpret_cast<const uint4*>(sC + row * CPITCH + cp);
-    bf16* dst = out.c + (long)gr * out.n + gc;
-    if (full_n || gc + 8 <= out.n) {
-      *reinterpret_cast<uint4*>(dst) = x;
-    } else if (gc < out.n) {
-      const bf16* e = reinterpret_cast<const bf16*>(&x);
-      for (int q = 0; q < out.n - gc; ++q) dst[q] = e[q];
+          for (int v = 0; v < 16; ++v)
+            sC[((wm & 1) * 64 + 32 * i + 8 * (v >> 2) + 4 * h32 + (v & 3)) * CPITCH + col] =
+                from_f<bf16>(acc[i][j][v] + bias);
+      }
+    }
+    __syncthreads();
+    // 128 rows of BN columns = 128 * BN / 8 pieces of 8 bf16 over the threads
+    constexpr int PPRC = BN / 8, NPC = 128 * PPRC / NTHR;
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int piece = tid + NTHR * u;
+      const int row = piece / PPRC, cp = (piece % PPRC) * 8;
+      const int gr = m0 + 128 * half + row, gc = n0 + cp;
+      if (gr >= p.M || gc >= out.n) continue;  // n is a multiple of 8: whole pieces only
+      *reinterpret_cast<uint4*>(out.c + (long)gr * out.n + gc) =
+          *reinterpret_cast<const uint4*>(sC + row * CPITCH + cp);
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
-                         hipStream_t st) {
-  if (nout < 1 || nout > kLinearMaxOut) return hipErrorInvalidValue;
+// Launch with BM x BM tiles (tile0 of each output counted in BM-wide column tiles).
+template <int BM>
+static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const LinearOut* outs,
+                                   hipStream_t st) {
   LinParams p{};
   p.a = static_cast<const bf16*>(a);
   p.M = M;
@@ -167,12 +192,28 @@ hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut*
     p.out[i].bias = outs[i].bias;
     p.out[i].n = outs[i].n;
     p.out[i].tile0 = tiles;
-    tiles += (outs[i].n + BN - 1) / BN;
+    tiles += (outs[i].n + BM - 1) / BM;
   }
   const long mt = ((long)M + BM - 1) / BM;
   if (mt > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(linear_kernel, dim3((unsigned)tiles, (unsigned)mt), dim3(NTHR), 0, st, p);
+  hipLaunchKernelGGL((linear_kernel<BM, 32>), dim3((unsigned)tiles, (unsigned)mt),
+                     dim3(Tile<BM>::NTHR), 0, st, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// 256 x 256 tiles (sixteen waves, one workgroup per compute unit, twice the flops per byte
+// loaded) when they give at least four rounds of workgroups over the 256 compute units; else
+// 128 x 128 tiles (four waves, three workgroups per unit), which fill smaller problems.
+hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
+                         hipStream_t st) {
+  if (nout < 1 || nout > kLinearMaxOut) return hipErrorInvalidValue;
+  long t256 = 0;
+  for (int i = 0; i < nout; ++i) t256 += (outs[i].n + 255) / 256;
+  t256 *= ((long)M + 255) / 256;
+  if (t256 >= 4 * 256) return launch_linear_bm<256>(M, K, a, nout, outs, st);
+  return launch_linear_bm<128>(M, K, a, nout, outs, st);
 }
 
 }  // namespace dig

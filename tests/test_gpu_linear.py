@@ -40,6 +40,8 @@ def _run(m, k, ns, bias, seed, scale=1.0):
     (1000, 16, [576], True),                  # the rank-16 gate up-projection (K = 16) + bias
     (4096, 1152, [576, 576, 1152, 16, 1152], False),  # DiG-XL/2 in-projection, 4096 tokens
     (4096, 1152, [1152], False),              # DiG-XL/2 out-projection
+    # >= 1024 tiles of 256 x 256: the sixteen-wave tile, ragged rows and column tiles
+    (33000, 64, [1152, 264, 8], True),
 ])
 def test_linear_parity(m, k, ns, bias):
     announce("linear m=%d k=%d n=%s bias=%d" % (m, k, ns, bias))
