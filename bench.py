@@ -254,6 +254,10 @@ def probe_lib():
                                          ctypes.POINTER(ctypes.c_double)]
     L.digp_copy.argtypes = [P, P, ctypes.c_size_t, P]
     L.digp_copy.restype = I
+    L.digp_mfma_rate.argtypes = [I, I, I, P, P]
+    L.digp_mfma_rate.restype = I
+    L.digp_mfma_rate_flops.argtypes = [I, I, I]
+    L.digp_mfma_rate_flops.restype = ctypes.c_double
     return L
 
 
@@ -350,6 +354,16 @@ def contraction_microbench():
             "algorithmic_frac_of_bf16_peak": round(t_alg / BF16_PEAK_TFLOPS, 4),
             "issued_flops_per_chunk": iss.value, "algorithmic_flops_per_chunk": alg.value}
         del sink
+    # the instructions' own ceilings: operands and accumulators in registers, no memory
+    nwg, iters = 2048, 1000
+    sink = torch.empty(nwg * 256, device="cuda")
+    for wide, label in ((0, "mfma_16x16x32_bf16"), (1, "mfma_32x32x16_bf16")):
+        ms = timed(lambda: L.digp_mfma_rate(wide, nwg, iters, sink.data_ptr(), _stream()), 3, 1)
+        tf = L.digp_mfma_rate_flops(wide, nwg, iters) / (ms / 1e3) / 1e12
+        res["register_only_" + label] = {"tflops": round(tf, 1),
+                                         "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    res["note"] = ("the contraction phases use the 16x16x32 instruction; its register-only rate "
+                   "is the ceiling for them on this part")
     return res
 
 

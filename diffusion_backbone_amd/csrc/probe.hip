@@ -11,6 +11,9 @@
 //                     chip) from the memory traffic around them.
 //   digp_copy         a streaming device copy (16-byte vectors, eight in flight per thread):
 //                     the HBM ceiling a read-once/write-once kernel can reach.
+//   digp_mfma_rate    bf16 MFMA instructions with operands and accumulators in registers only
+//                     (independent accumulators, no memory): the rate each instruction shape
+//                     can sustain, the ceiling under the contraction microbenchmark.
 #include <hip/hip_runtime.h>
 
 #include "dig_device.h"
@@ -136,6 +139,42 @@ hipError_t launch_contraction(int nwg, int iters, float* sink, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Register-only MFMA rate: NACC independent accumulators per wave, `iters` rounds.
+template <bool WIDE, int NACC>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* sink, int iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = from_f<bf16>(0.001f * (float)(threadIdx.x + i));
+    b[i] = from_f<bf16>(0.002f * (float)i);
+  }
+  float s = 0.f;
+  if constexpr (WIDE) {
+    f32x16 c[NACC];
+#pragma unroll
+    for (int j = 0; j < NACC; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c[j][v] = 0.f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) c[j] = mfma32_bf16(a, b, c[j]);
+#pragma unroll
+    for (int j = 0; j < NACC; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += c[j][v];
+  } else {
+    f32x4 c[NACC];
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) c[j] = zero4();
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) c[j] = mfma_bf16(a, b, c[j]);
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  }
+  sink[(long)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // Streaming copy: every thread moves 8 16-byte vectors per step, all loads before the stores.
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src,
                                                    uint4* __restrict__ dst, long n) {
@@ -176,6 +215,18 @@ void digp_contraction_flops(int shape, double* algorithmic, double* issued) {
   const long n = shape == 0 ? dig::ProbeShape<32, 64, 8>::mfma_per_chunk()
                             : dig::ProbeShape<36, 72, 4>::mfma_per_chunk();
   *issued = (double)n * 16 * 16 * 32 * 2;
+}
+
+// wide 0: 16x16x32 (16 384 flops per instruction), 1: 32x32x16 (32 768); nwg workgroups of four
+// waves, iters rounds of 4 (2) independent instructions per wave; sink holds nwg * 256 floats.
+int digp_mfma_rate(int wide, int nwg, int iters, float* sink, hipStream_t st) {
+  if (nwg < 1 || iters < 1 || !sink) return (int)hipErrorInvalidValue;
+  if (wide) hipLaunchKernelGGL((dig::mfma_rate_kernel<true, 4>), dim3(nwg), dim3(256), 0, st, sink, iters);
+  else hipLaunchKernelGGL((dig::mfma_rate_kernel<false, 8>), dim3(nwg), dim3(256), 0, st, sink, iters);
+  return (int)hipGetLastError();
+}
+double digp_mfma_rate_flops(int wide, int nwg, int iters) {
+  return wide ? 4.0 * 32768 * 4 * iters * nwg : 8.0 * 16384 * 4 * iters * nwg;
 }
 
 int digp_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {
