@@ -67,6 +67,9 @@ def _load():
         lib.oref_dwconv3x3_bwd.argtypes = [i, i64, i64, i, i, i, D, D, D, D, D, D]
         lib.oref_num_threads.restype = i
         lib.oref_linear.argtypes = [i64, i64, i64, D, D, D, D]
+        lib.oref_rmsnorm_modulate.argtypes = [i64, i64, i64, D, D, D, i64, d, D]
+        lib.oref_gelu.argtypes = [i64, D, D]
+        lib.oref_silu.argtypes = [i64, D, D]
         _lib = lib
     return _lib
 
@@ -227,3 +230,67 @@ def linear(a, w, bias=None):
     c = np.empty(a.shape[:-1] + (n,))
     _load().oref_linear(m, k, n, _p(a), _p(w), _p(b), _p(c))
     return c
+
+
+# --------------------------------------------------------------------- DiG block
+def rmsnorm_modulate(x, scale, shift, eps: float = 1e-5):
+    """h = RMSNorm(x) * scale + shift over the last axis; x [B, L, D], scale/shift [B, D]."""
+    x, scale, shift = _f64(x), _f64(scale), _f64(shift)
+    B, L, D = x.shape
+    h = np.empty_like(x)
+    _load().oref_rmsnorm_modulate(B * L, D, max(L, 1), _p(x), _p(scale), _p(shift), D,
+                                  float(eps), _p(h))
+    return h
+
+
+def gelu(x):
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oref_gelu(x.size, _p(x), _p(y))
+    return y
+
+
+def silu(x):
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oref_silu(x.size, _p(x), _p(y))
+    return y
+
+
+def block_cond(c, w_ada, b_ada=None):
+    """adaLN parameters of every block: SiLU(c) W_ada^T + b_ada, c [B, D] -> [B, 6 D n]."""
+    return linear(silu(c), w_ada, b_ada)
+
+
+def block_forward(x, mod, wts: dict, gh: int, gw: int, heads: int, d_k: int, d_v: int,
+                  layout: int, out_layout: int, tau: float = 16.0, eps: float = 1e-5,
+                  intermediates: bool = False):
+    """One DiG block forward (slides Figure 4; write-up section 3 "DiG Block"):
+        x1 = x  + a1 * (GLA(RMSNorm(x) g1 + b1) W_out + b_out)
+        x2 = x1 + a2 * (GELU((RMSNorm(x1) g2 + b2) W_ffn1 + b_ffn1) W_ffn2 + b_ffn2)
+        x_out = DWConv3x3(x2) in scan order layout, written in out_layout (SREM)
+    x [B, L, D] in scan order `layout`; mod [B, 6 D] = g1 | b1 | a1 | g2 | b2 | a2; wts holds
+    the fields of dig_block_weights as float64 arrays (None for an absent bias).  The GLA
+    layer: [q | k | v | u | r] = h W_in^T + b_in, z = u W_gate^T + b_gate, then gla_fwd."""
+    x, mod = _f64(x), _f64(mod)
+    B, L, D = x.shape
+    HK, HV = heads * d_k, heads * d_v
+    g1, b1, a1, g2, b2, a2 = (mod[:, i * D:(i + 1) * D] for i in range(6))
+    h = rmsnorm_modulate(x, g1, b1, eps)
+    proj = linear(h, wts["w_in"], wts.get("b_in"))
+    cuts = np.cumsum([HK, HK, HV, proj.shape[-1] - 2 * HK - 2 * HV])
+    q, k, v, u, r = np.split(proj, cuts, axis=-1)
+    z = linear(u, wts["w_gate"], wts.get("b_gate"))
+    shp = lambda t, d: t.reshape(B, L, heads, d)
+    y, _, _ = gla_fwd(shp(q, d_k), shp(k, d_k), shp(v, d_v), shp(z, d_k), shp(r, d_v),
+                      wts.get("gla_norm_w"), tau=tau, eps=eps)
+    x1 = x + a1[:, None, :] * linear(y.reshape(B, L, HV), wts["w_out"], wts.get("b_out"))
+    h2 = rmsnorm_modulate(x1, g2, b2, eps)
+    f = linear(gelu(linear(h2, wts["w_ffn1"], wts.get("b_ffn1"))), wts["w_ffn2"],
+               wts.get("b_ffn2"))
+    x2 = x1 + a2[:, None, :] * f
+    out = dwconv3x3(x2, wts["conv_w"], gh, gw, layout, out_layout, wts.get("conv_b"))
+    if intermediates:
+        return out, dict(h=h, q=q, k=k, v=v, u=u, r=r, z=z, y=y.reshape(B, L, HV), x1=x1, h2=h2,
+                         x2=x2)
+    return out

@@ -469,6 +469,42 @@ void oref_linear(int64_t m, int64_t k, int64_t n, const double *a, const double 
         }
 }
 
+/*
+ * The adaptive normalisation of a DiG block (slides Figure 4: RMS Norm, then Scale & Shift by
+ * the gamma, beta regressed from the conditioning; write-up section 3 "DiG Block"), per row i
+ * of D values, image g = i / rows_per_group:
+ *   h[i][j] = x[i][j] / sqrt(mean_l x[i][l]^2 + eps) * scale[g][j] + shift[g][j]
+ * scale and shift rows are mod_ld apart.  fp64, the plain definition.
+ */
+void oref_rmsnorm_modulate(int64_t rows, int64_t D, int64_t rows_per_group, const double *x,
+                           const double *scale, const double *shift, int64_t mod_ld,
+                           double eps, double *h)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const double *xr = x + (size_t)i * D;
+        double ss = 0.0;
+        for (int64_t j = 0; j < D; ++j) ss += xr[j] * xr[j];
+        const double inv = 1.0 / sqrt(ss / (double)D + eps);
+        const int64_t g = i / rows_per_group;
+        for (int64_t j = 0; j < D; ++j)
+            h[(size_t)i * D + j] = xr[j] * inv * scale[(size_t)g * mod_ld + j] +
+                                   shift[(size_t)g * mod_ld + j];
+    }
+}
+
+/* GELU of the DiG feedforward, exact form: y = x Phi(x) = x (1 + erf(x / sqrt(2))) / 2. */
+void oref_gelu(int64_t n, const double *x, double *y)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = 0.5 * x[i] * (1.0 + erf(x[i] / sqrt(2.0)));
+}
+
+/* SiLU applied to the conditioning before the adaLN regression: y = x / (1 + e^{-x}). */
+void oref_silu(int64_t n, const double *x, double *y)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = x[i] / (1.0 + exp(-x[i]));
+}
+
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int oref_num_threads(void)
 {

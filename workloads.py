@@ -238,3 +238,48 @@ def project(cfg: Config, x: np.ndarray, wts: BlockWeights):
     qz = lambda a, d: quantize(a.reshape(B, L, H, d), cfg.dtype)
     return (qz(x2 @ wts.wq, dk), qz(x2 @ wts.wk, dk), qz(x2 @ wts.wv, dv),
             qz((x2 @ wts.wa1) @ wts.wa2, dk), qz(x2 @ wts.wr, dv))
+
+
+# ----------------------------------------------------------------- DiG block stack
+# The full block stack forward (slides Figure 4 and Table 1: S = 12 blocks, XL = 28) on the
+# same image sizes; the feedforward is D -> 4 D -> D.
+STACKS = {
+    "dig_s2_256_stack": (CONFIGS["dig_s2_256"], 12),
+    "dig_xl2_256_stack": (Config("dig_xl2_256", 8, 16, 16, 1152, 16, 36, 72, 64, "bf16",
+                                 blocks=28, index=5,
+                                 note="DiG-XL/2 at 256 px, block stack forward"), 28),
+}
+
+BLOCK_WEIGHT_FIELDS = ("w_in", "b_in", "w_gate", "b_gate", "gla_norm_w", "w_out", "b_out",
+                       "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "conv_w", "conv_b")
+
+
+def make_dig_block_weights(cfg: Config, rng, ffn_mult: int = 4) -> dict:
+    """One DiG block's weights, bf16-representable matrices and fp32 vectors (as float64):
+    projections ~ N(0, 1/fan_in); biases ~ N(0, 0.1^2); head-wise norm weight 1 + N(0, 0.1^2);
+    DWConv kernel = identity (centre tap 1, the initialisation the write-up describes) plus
+    N(0, 1/36); rows of w_in are q | k | v | u (gate factor, rank cfg.rank) | r."""
+    D, H, dk, dv, R = cfg.d_model, cfg.heads, cfg.d_k, cfg.d_v, cfg.rank
+    F = ffn_mult * D
+    nin = 2 * H * dk + 2 * H * dv + R
+    mat = lambda shape, fan: bf16_round(rng.standard_normal(shape) / np.sqrt(fan))
+    vec = lambda n, std=0.1: f32_round(rng.standard_normal(n) * std)
+    conv = rng.standard_normal((D, 3, 3)) / 6.0
+    conv[:, 1, 1] += 1.0
+    return dict(w_in=mat((nin, D), D), b_in=vec(nin), w_gate=mat((H * dk, R), R),
+                b_gate=vec(H * dk, 1.0), gla_norm_w=f32_round(1.0 + rng.standard_normal(dv) * 0.1),
+                w_out=mat((D, H * dv), H * dv), b_out=vec(D), w_ffn1=mat((F, D), D),
+                b_ffn1=vec(F), w_ffn2=mat((D, F), F), b_ffn2=vec(D), conv_w=f32_round(conv),
+                conv_b=vec(D))
+
+
+def make_block_cond(cfg: Config, n_blocks: int, rng) -> dict:
+    """The conditioning vector c [B, D] ~ N(0, 1) (standing in for the summed timestep and
+    label embeddings) and the adaLN regression W_ada [n_blocks * 6 D, D] ~ N(0, 0.1^2 / D),
+    b_ada = (1, 0, 0.5, 1, 0, 0.5) per D-wide part (gamma_1, beta_1, alpha_1, gamma_2, beta_2,
+    alpha_2), so gamma ~ 1, beta ~ 0, alpha ~ 0.5 with a per-image spread."""
+    D = cfg.d_model
+    part = np.concatenate([np.full(D, v) for v in (1.0, 0.0, 0.5, 1.0, 0.0, 0.5)])
+    return dict(c=bf16_round(rng.standard_normal((cfg.batch, D))),
+                w_ada=bf16_round(rng.standard_normal((n_blocks * 6 * D, D)) * (0.1 / np.sqrt(D))),
+                b_ada=f32_round(np.tile(part, n_blocks)))
