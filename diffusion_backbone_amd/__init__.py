@@ -28,8 +28,11 @@ EXPORTS = (
     "dig_dwconv3x3_bwd_workspace_bytes", "dig_dwconv3x3_bwd", "dig_status_str",
     "dig_last_error", "dig_abi_version", "dig_lookback_status", "dig_debug_lookback",
     "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes", "dig_linear",
+    "dig_rmsnorm_modulate", "dig_block_cond_workspace_bytes", "dig_block_cond",
+    "dig_block_fwd_workspace_bytes", "dig_block_fwd",
 )
 DIG_LINEAR_MAX_OUT = 6
+DIG_ACT_NONE, DIG_ACT_GELU = 0, 1
 
 
 class DigError(RuntimeError):
@@ -40,7 +43,23 @@ class DigError(RuntimeError):
 
 class dig_linear_out(ctypes.Structure):
     _fields_ = [("c", ctypes.c_void_p), ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("n", ctypes.c_int32)]
+                ("n", ctypes.c_int32), ("act", ctypes.c_int32), ("res", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p), ("gate_ld", ctypes.c_int64),
+                ("rows_per_gate", ctypes.c_int64)]
+
+
+class dig_block_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("gate_rank", ctypes.c_int32),
+                ("ffn_dim", ctypes.c_int32), ("chunk", ctypes.c_int32), ("tau", ctypes.c_float),
+                ("norm_eps", ctypes.c_float)]
+
+
+class dig_block_weights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "w_in", "b_in", "w_gate", "b_gate", "gla_norm_w", "w_out", "b_out", "w_ffn1", "b_ffn1",
+        "w_ffn2", "b_ffn2", "conv_w", "conv_b")]
 
 
 class dig_gla_desc(ctypes.Structure):
@@ -104,6 +123,19 @@ def lib() -> ctypes.CDLL:
         L.dig_dwconv3x3_bwd_noalloc_max_bytes.restype = S
         L.dig_linear.argtypes = [I, I, I, P, I, ctypes.POINTER(dig_linear_out), P]
         L.dig_linear.restype = ctypes.c_int
+        I64, F = ctypes.c_int64, ctypes.c_float
+        L.dig_rmsnorm_modulate.argtypes = [I64, I, I64, F, P, P, P, I64, P, P]
+        L.dig_rmsnorm_modulate.restype = ctypes.c_int
+        L.dig_block_cond_workspace_bytes.argtypes = [I, I]
+        L.dig_block_cond_workspace_bytes.restype = S
+        L.dig_block_cond.argtypes = [I, I, I, P, P, P, P, P, S, P]
+        L.dig_block_cond.restype = ctypes.c_int
+        BD = ctypes.POINTER(dig_block_desc)
+        L.dig_block_fwd_workspace_bytes.argtypes = [BD]
+        L.dig_block_fwd_workspace_bytes.restype = S
+        L.dig_block_fwd.argtypes = [BD, ctypes.POINTER(dig_block_weights), P, I64, I, I, P, P, P,
+                                    S, P]
+        L.dig_block_fwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -122,6 +154,13 @@ def _ptr(t):
         return t
     if not t.is_contiguous():
         raise ValueError("tensors passed to libdig must be contiguous")
+    return t.data_ptr()
+
+
+def _addr(t):
+    """Device address of a tensor or view (no contiguity needed: strided-row arguments)."""
+    if t is None or isinstance(t, int):
+        return t
     return t.data_ptr()
 
 
@@ -230,10 +269,72 @@ def dig_dwconv3x3_bwd_noalloc_max_bytes() -> int:
 
 
 
+def linear_out(c, w, bias=None, act=DIG_ACT_NONE, res=None, gate=None, gate_ld=0,
+               rows_per_gate=1, n=None) -> dict:
+    """One output of dig_linear.  gate: tensor view or address of gate row 0."""
+    return dict(c=c, w=w, bias=bias, act=act, res=res, gate=gate, gate_ld=gate_ld,
+                rows_per_gate=rows_per_gate, n=n)
+
+
 def dig_linear(m, k, a, outs, stream=None):
-    """outs: sequence of (c, w, bias_or_None) tensors; c [m, n] bf16, w [n, k] bf16."""
+    """outs: sequence of (c, w, bias_or_None) tuples or linear_out(...) dicts;
+    c [m, n] bf16, w [n, k] bf16."""
     arr = (dig_linear_out * max(len(outs), 1))()
-    for i, (c, w, b) in enumerate(outs):
-        arr[i] = dig_linear_out(_ptr(c), _ptr(w), _ptr(b), int(w.shape[0]))
+    for i, o in enumerate(outs):
+        if not isinstance(o, dict):
+            o = linear_out(*o)
+        n = o["n"] if o["n"] is not None else int(o["w"].shape[0])
+        arr[i] = dig_linear_out(_ptr(o["c"]), _ptr(o["w"]), _ptr(o["bias"]), n, int(o["act"]),
+                                _ptr(o["res"]), _addr(o["gate"]), int(o["gate_ld"]),
+                                int(o["rows_per_gate"]))
     st = lib().dig_linear(int(m), int(k), DIG_BF16, _ptr(a), len(outs), arr, _stream(stream))
     _check(st, "dig_linear")
+
+
+# ---------------------------------------------------------------- DiG block
+def dig_rmsnorm_modulate(rows, dim, rows_per_group, eps, x, scale, shift, mod_ld, h,
+                         stream=None):
+    """scale, shift: tensor views or addresses of row 0 (rows mod_ld elements apart)."""
+    st = lib().dig_rmsnorm_modulate(int(rows), int(dim), int(rows_per_group), float(eps), _ptr(x),
+                                    _addr(scale), _addr(shift), int(mod_ld), _ptr(h),
+                                    _stream(stream))
+    _check(st, "dig_rmsnorm_modulate")
+
+
+def make_block_desc(batch, grid_h, grid_w, dim, heads, d_k, d_v, gate_rank=16, ffn_dim=None,
+                    chunk=64, tau=16.0, norm_eps=1e-5) -> dig_block_desc:
+    return dig_block_desc(batch, grid_h, grid_w, dim, heads, d_k, d_v, gate_rank,
+                          4 * dim if ffn_dim is None else ffn_dim, chunk, tau, norm_eps)
+
+
+def make_block_weights(**tensors) -> dig_block_weights:
+    """Keyword arguments named as the fields of dig_block_weights (tensors or None)."""
+    unknown = set(tensors) - {f for f, _ in dig_block_weights._fields_}
+    if unknown:
+        raise ValueError("unknown block weights: %s" % sorted(unknown))
+    return dig_block_weights(*[_ptr(tensors.get(f)) for f, _ in dig_block_weights._fields_])
+
+
+def dig_block_cond_workspace_bytes(batch, dim) -> int:
+    return lib().dig_block_cond_workspace_bytes(int(batch), int(dim))
+
+
+def dig_block_cond(batch, dim, n_blocks, c, w_ada, b_ada, mod, workspace, workspace_bytes=None,
+                   stream=None):
+    st = lib().dig_block_cond(int(batch), int(dim), int(n_blocks), _ptr(c), _ptr(w_ada),
+                              _ptr(b_ada), _ptr(mod), _ptr(workspace),
+                              _nbytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "dig_block_cond")
+
+
+def dig_block_fwd_workspace_bytes(desc: dig_block_desc) -> int:
+    return lib().dig_block_fwd_workspace_bytes(ctypes.byref(desc))
+
+
+def dig_block_fwd(desc, weights, mod, mod_ld, layout, out_layout, x, x_out, workspace,
+                  workspace_bytes=None, stream=None):
+    """mod: tensor view or address of this block's parameters for image 0."""
+    st = lib().dig_block_fwd(ctypes.byref(desc), ctypes.byref(weights), _addr(mod), int(mod_ld),
+                             int(layout), int(out_layout), _ptr(x), _ptr(x_out), _ptr(workspace),
+                             _nbytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "dig_block_fwd")

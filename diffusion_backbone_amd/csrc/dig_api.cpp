@@ -2,6 +2,7 @@
 // (before anything is enqueued), workspace carving, and dispatch to the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -139,7 +140,7 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 101; }
+int32_t dig_abi_version(void) { return 102; }
 
 dig_status dig_lookback_status(hipStream_t stream) {
   unsigned* word = dig::lookback_status_word();
@@ -424,30 +425,294 @@ dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_
   if (k % 8) return fail(DIG_ERR_UNSUPPORTED, "k must be a multiple of 8 (16-byte rows)");
   if ((long long)(m + 255) / 256 > 65535) return fail(DIG_ERR_UNSUPPORTED, "m too large");
   for (int i = 0; i < n_out; ++i) {
-    if (outs[i].n < 1) return fail(DIG_ERR_SHAPE, "outs[%d].n must be >= 1", i);
-    if (outs[i].n % 8) return fail(DIG_ERR_UNSUPPORTED, "outs[%d].n must be a multiple of 8", i);
+    const dig_linear_out& o = outs[i];
+    if (o.n < 1) return fail(DIG_ERR_SHAPE, "outs[%d].n must be >= 1", i);
+    if (o.n % 8) return fail(DIG_ERR_UNSUPPORTED, "outs[%d].n must be a multiple of 8", i);
+    if (o.act != DIG_ACT_NONE && o.act != DIG_ACT_GELU)
+      return fail(DIG_ERR_SHAPE, "outs[%d].act must be DIG_ACT_NONE or DIG_ACT_GELU", i);
+    if (o.res) {
+      if (o.rows_per_gate < 1)
+        return fail(DIG_ERR_SHAPE, "outs[%d].rows_per_gate must be >= 1", i);
+      if (o.gate_ld < o.n) return fail(DIG_ERR_SHAPE, "outs[%d].gate_ld must be >= n", i);
+      if (o.gate_ld % 8)
+        return fail(DIG_ERR_UNSUPPORTED, "outs[%d].gate_ld must be a multiple of 8", i);
+    }
   }
   if (m == 0) return ok();
   if (!a) return fail(DIG_ERR_NULL, "a is required");
-  for (int i = 0; i < n_out; ++i)
+  for (int i = 0; i < n_out; ++i) {
     if (!outs[i].c || !outs[i].w) return fail(DIG_ERR_NULL, "outs[%d].c and .w are required", i);
+    if (outs[i].res && !outs[i].gate)
+      return fail(DIG_ERR_NULL, "outs[%d].gate is required with a residual", i);
+  }
   if (!aligned16(a)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  for (int i = 0; i < n_out; ++i)
-    if (!aligned16(outs[i].c) || !aligned16(outs[i].w) || (outs[i].bias && !aligned16(outs[i].bias)))
-      return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  Range in[1 + 2 * DIG_LINEAR_MAX_OUT], out[DIG_LINEAR_MAX_OUT];
+  for (int i = 0; i < n_out; ++i) {
+    const dig_linear_out& o = outs[i];
+    const void* ptrs[] = {o.c, o.w, o.bias, o.res, o.gate};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  }
+  Range in[1 + 4 * DIG_LINEAR_MAX_OUT], out[DIG_LINEAR_MAX_OUT];
   int nin = 0;
   in[nin++] = rng("a", a, (size_t)m * k * 2);
   for (int i = 0; i < n_out; ++i) {
-    in[nin++] = rng("w", outs[i].w, (size_t)outs[i].n * k * 2);
-    in[nin++] = rng("bias", outs[i].bias, outs[i].bias ? (size_t)outs[i].n * 4 : 0);
-    out[i] = rng("c", outs[i].c, (size_t)m * outs[i].n * 2);
+    const dig_linear_out& o = outs[i];
+    const size_t cbytes = (size_t)m * o.n * 2;
+    in[nin++] = rng("w", o.w, (size_t)o.n * k * 2);
+    in[nin++] = rng("bias", o.bias, o.bias ? (size_t)o.n * 4 : 0);
+    if (o.res) {
+      const size_t groups = ((size_t)m - 1) / (size_t)o.rows_per_gate;
+      in[nin++] = rng("gate", o.gate, (groups * (size_t)o.gate_ld + o.n) * 2);
+      // the residual may be this output itself, and otherwise may not touch it
+      if (o.res != o.c) in[nin++] = rng("res", o.res, cbytes);
+    }
+    out[i] = rng("c", o.c, cbytes);
   }
   dig_status st = check_alias(in, nin, out, n_out);
   if (st != DIG_OK) return st;
   dig::LinearOut lo[DIG_LINEAR_MAX_OUT];
-  for (int i = 0; i < n_out; ++i) lo[i] = {outs[i].c, outs[i].w, outs[i].bias, outs[i].n};
+  for (int i = 0; i < n_out; ++i) {
+    const dig_linear_out& o = outs[i];
+    lo[i] = dig::LinearOut{o.c, o.w, o.bias, o.n, o.act, o.res, o.res ? o.gate : nullptr,
+                           (long)o.gate_ld, o.res ? (int)std::min<int64_t>(o.rows_per_gate, m) : 1};
+  }
   return check_dev(dig::launch_linear(m, k, a, n_out, lo, stream), "dig_linear launch");
+}
+
+dig_status dig_rmsnorm_modulate(int64_t rows, int32_t dim, int64_t rows_per_group, float eps,
+                                const void* x, const void* scale, const void* shift,
+                                int64_t mod_ld, void* h, hipStream_t stream) {
+  if (rows < 0 || dim < 1 || rows_per_group < 1 || mod_ld < dim)
+    return fail(DIG_ERR_SHAPE, "rows >= 0, dim >= 1, rows_per_group >= 1, mod_ld >= dim");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(DIG_ERR_SHAPE, "eps must be finite, >= 0");
+  if (dim % 8 || dim > 2048 || mod_ld % 8)
+    return fail(DIG_ERR_UNSUPPORTED, "dim and mod_ld must be multiples of 8, dim <= 2048");
+  if (rows > (1LL << 32)) return fail(DIG_ERR_UNSUPPORTED, "too many rows");
+  if (rows == 0) return ok();
+  if (!x || !scale || !shift || !h) return fail(DIG_ERR_NULL, "x, scale, shift and h are required");
+  const void* ptrs[] = {x, scale, shift, h};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t bytes = (size_t)rows * dim * 2;
+  const size_t mbytes = ((size_t)(rows - 1) / rows_per_group * mod_ld + dim) * 2;
+  const Range in[] = {rng("x", x, bytes), rng("scale", scale, mbytes), rng("shift", shift, mbytes)};
+  const Range out[] = {rng("h", h, bytes)};
+  dig_status st = check_alias(in, 3, out, 1);
+  if (st != DIG_OK) return st;
+  return check_dev(dig::launch_rmsnorm_modulate(rows, dim, rows_per_group, eps, x, scale, shift,
+                                                mod_ld, h, stream),
+                   "dig_rmsnorm_modulate launch");
+}
+
+size_t dig_block_cond_workspace_bytes(int32_t batch, int32_t dim) {
+  if (batch < 0 || dim < 1) return 0;
+  return a256((size_t)batch * dim * 2);
+}
+
+dig_status dig_block_cond(int32_t batch, int32_t dim, int32_t n_blocks, const void* c,
+                          const void* w_ada, const float* b_ada, void* mod, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 0 || dim < 1 || n_blocks < 1)
+    return fail(DIG_ERR_SHAPE, "batch >= 0, dim >= 1 and n_blocks >= 1 are required");
+  if (dim % 8) return fail(DIG_ERR_UNSUPPORTED, "dim must be a multiple of 8");
+  if ((long long)n_blocks * 6 * dim > (1LL << 30)) return fail(DIG_ERR_UNSUPPORTED, "too large");
+  if (batch == 0) return ok();
+  if (!c || !w_ada || !mod) return fail(DIG_ERR_NULL, "c, w_ada and mod are required");
+  const size_t need = dig_block_cond_workspace_bytes(batch, dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const void* ptrs[] = {c, w_ada, b_ada, mod, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t nm = (size_t)n_blocks * 6 * dim;
+  const Range in[] = {rng("c", c, (size_t)batch * dim * 2), rng("w_ada", w_ada, nm * dim * 2),
+                      rng("b_ada", b_ada, b_ada ? nm * 4 : 0)};
+  const Range out[] = {rng("mod", mod, (size_t)batch * nm * 2), rng("workspace", workspace, need)};
+  dig_status st = check_alias(in, 3, out, 2);
+  if (st != DIG_OK) return st;
+  st = check_dev(dig::launch_silu((long)batch * dim, c, workspace, stream), "dig_block_cond silu");
+  if (st != DIG_OK) return st;
+  const dig_linear_out o{mod, w_ada, b_ada, (int32_t)nm, DIG_ACT_NONE, nullptr, nullptr, 0, 1};
+  return dig_linear(batch, dim, DIG_BF16, workspace, 1, &o, stream);
+}
+
+namespace {
+
+// Carving of dig_block_fwd's workspace (bf16 intermediates, then the GLA call's workspace).
+struct BlockWs {
+  size_t h, q, k, v, u, r, z, y, x1, hid, gla, total;
+};
+
+dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
+  if (!d) return fail(DIG_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->grid_h < 0 || d->grid_w < 0)
+    return fail(DIG_ERR_SHAPE, "batch, grid_h, grid_w must be >= 0");
+  if (d->dim < 1 || d->heads < 1 || d->d_k < 1 || d->d_v < 1 || d->gate_rank < 1 || d->ffn_dim < 1)
+    return fail(DIG_ERR_SHAPE, "dim, heads, d_k, d_v, gate_rank, ffn_dim must be >= 1");
+  if (d->dim % 8 || d->dim > 2048 || (d->heads * d->d_k) % 8 || (d->heads * d->d_v) % 8 ||
+      d->gate_rank % 8 || d->ffn_dim % 8)
+    return fail(DIG_ERR_UNSUPPORTED,
+                "dim (<= 2048), H*d_k, H*d_v, gate_rank and ffn_dim must be multiples of 8");
+  if ((long long)d->grid_h * d->grid_w > (1LL << 31))
+    return fail(DIG_ERR_UNSUPPORTED, "grid too large");
+  *g = dig_gla_desc{};
+  g->batch = d->batch;
+  g->seq_len = d->grid_h * d->grid_w;
+  g->heads = d->heads;
+  g->d_k = d->d_k;
+  g->d_v = d->d_v;
+  g->chunk = d->chunk;
+  g->tau = d->tau;
+  g->q_scale = 1.f;
+  g->norm_eps = d->norm_eps;
+  g->dtype = DIG_BF16;
+  g->seg_chunks = 0;
+  dig::GlaShape s;
+  dig_status st = check_desc(g, &s, kFwd);
+  if (st != DIG_OK) return st;
+  const size_t M = (size_t)d->batch * g->seq_len;
+  if (M > (size_t)65535 * 256) return fail(DIG_ERR_UNSUPPORTED, "too many tokens");
+  const size_t HK = (size_t)d->heads * d->d_k, HV = (size_t)d->heads * d->d_v;
+  size_t off = 0;
+  auto take = [&](size_t cols) { const size_t o = off; off += a256(M * cols * 2); return o; };
+  w->h = take(d->dim);
+  w->q = take(HK);
+  w->k = take(HK);
+  w->v = take(HV);
+  w->u = take(d->gate_rank);
+  w->r = take(HV);
+  w->z = take(HK);
+  w->y = take(HV);
+  w->x1 = take(d->dim);
+  w->hid = take(d->ffn_dim);
+  w->gla = off;
+  off += a256(dig_gla_fwd_workspace_bytes(g));
+  w->total = off;
+  return DIG_OK;
+}
+
+}  // namespace
+
+size_t dig_block_fwd_workspace_bytes(const dig_block_desc* desc) {
+  dig_gla_desc g;
+  BlockWs w;
+  if (block_plan(desc, &g, &w) != DIG_OK) return 0;
+  return w.total;
+}
+
+dig_status dig_block_fwd(const dig_block_desc* d, const dig_block_weights* wt, const void* mod,
+                         int64_t mod_ld, int32_t layout, int32_t out_layout, const void* x,
+                         void* x_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  dig_gla_desc g;
+  BlockWs w;
+  dig_status st = block_plan(d, &g, &w);
+  if (st != DIG_OK) return st;
+  if (!valid_scan(layout) || !valid_scan(out_layout))
+    return fail(DIG_ERR_SHAPE, "scan direction out of range");
+  if (mod_ld < 6LL * d->dim || mod_ld % 8)
+    return fail(DIG_ERR_SHAPE, "mod_ld must be >= 6 * dim and a multiple of 8");
+  const size_t L = (size_t)d->grid_h * d->grid_w, M = (size_t)d->batch * L;
+  if (M == 0) return ok();
+  if (!wt) return fail(DIG_ERR_NULL, "weights are required");
+  if (!x || !x_out || !mod || !wt->w_in || !wt->w_gate || !wt->w_out || !wt->w_ffn1 ||
+      !wt->w_ffn2 || !wt->conv_w)
+    return fail(DIG_ERR_NULL, "x, x_out, mod and every weight matrix are required");
+  if (!workspace || workspace_bytes < w.total)
+    return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  const int D = d->dim, HK = d->heads * d->d_k, HV = d->heads * d->d_v, R = d->gate_rank;
+  const int F = d->ffn_dim, NIN = 2 * HK + 2 * HV + R;
+  const void* ptrs[] = {x, x_out, mod, workspace, wt->w_in, wt->b_in, wt->w_gate, wt->b_gate,
+                        wt->gla_norm_w, wt->w_out, wt->b_out, wt->w_ffn1, wt->b_ffn1, wt->w_ffn2,
+                        wt->b_ffn2, wt->conv_w, wt->conv_b};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  // every bias / row slice handed to the projections must stay 16-byte aligned
+  if ((HK % 8) || (HV % 8) || (R % 8))
+    return fail(DIG_ERR_UNSUPPORTED, "H*d_k, H*d_v and gate_rank must be multiples of 8");
+  const size_t xbytes = M * D * 2;
+  const size_t mbytes = ((size_t)(d->batch - 1) * mod_ld + 6 * (size_t)D) * 2;
+  const Range in[] = {
+      rng("x", x, xbytes), rng("mod", mod, mbytes),
+      rng("w_in", wt->w_in, (size_t)NIN * D * 2), rng("b_in", wt->b_in, wt->b_in ? NIN * 4 : 0),
+      rng("w_gate", wt->w_gate, (size_t)HK * R * 2),
+      rng("b_gate", wt->b_gate, wt->b_gate ? HK * 4 : 0),
+      rng("gla_norm_w", wt->gla_norm_w, wt->gla_norm_w ? d->d_v * 4 : 0),
+      rng("w_out", wt->w_out, (size_t)D * HV * 2), rng("b_out", wt->b_out, wt->b_out ? D * 4 : 0),
+      rng("w_ffn1", wt->w_ffn1, (size_t)F * D * 2),
+      rng("b_ffn1", wt->b_ffn1, wt->b_ffn1 ? F * 4 : 0),
+      rng("w_ffn2", wt->w_ffn2, (size_t)D * F * 2),
+      rng("b_ffn2", wt->b_ffn2, wt->b_ffn2 ? D * 4 : 0),
+      rng("conv_w", wt->conv_w, (size_t)D * 36), rng("conv_b", wt->conv_b, wt->conv_b ? D * 4 : 0)};
+  const Range out[] = {rng("x_out", x_out, xbytes), rng("workspace", workspace, w.total)};
+  st = check_alias(in, 15, out, 2);
+  if (st != DIG_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  void *h = ws + w.h, *q = ws + w.q, *k = ws + w.k, *v = ws + w.v, *u = ws + w.u, *r = ws + w.r;
+  void *z = ws + w.z, *y = ws + w.y, *x1 = ws + w.x1, *hid = ws + w.hid;
+  const char* md = static_cast<const char*>(mod);
+  const int m = (int)M;
+  const float* bi = wt->b_in;
+  const char* wi = static_cast<const char*>(wt->w_in);
+  auto mcol = [&](int part) { return md + (size_t)part * D * 2; };  // gamma_1 .. alpha_2
+  // 1. h = RMSNorm(x) * gamma_1 + beta_1
+  st = dig_rmsnorm_modulate((int64_t)M, D, (int64_t)L, d->norm_eps, x, mcol(0), mcol(1), mod_ld, h,
+                            stream);
+  if (st != DIG_OK) return st;
+  // 2. [q | k | v | u | r] = h W_in^T + b_in, one launch
+  {
+    const int cols[5] = {HK, HK, HV, R, HV};
+    void* dst[5] = {q, k, v, u, r};
+    dig_linear_out o[5];
+    size_t row0 = 0;
+    for (int i = 0; i < 5; ++i) {
+      o[i] = dig_linear_out{dst[i], wi + row0 * D * 2, bi ? bi + row0 : nullptr, cols[i],
+                            DIG_ACT_NONE, nullptr, nullptr, 0, 1};
+      row0 += cols[i];
+    }
+    st = dig_linear(m, D, DIG_BF16, h, 5, o, stream);
+    if (st != DIG_OK) return st;
+  }
+  // 3. z = u W_gate^T + b_gate
+  {
+    const dig_linear_out o{z, wt->w_gate, wt->b_gate, HK, DIG_ACT_NONE, nullptr, nullptr, 0, 1};
+    st = dig_linear(m, R, DIG_BF16, u, 1, &o, stream);
+    if (st != DIG_OK) return st;
+  }
+  // 4. the GLA token mixer, eqs. (5)-(10) up to the output projection
+  st = dig_gla_fwd(&g, q, k, v, z, r, wt->gla_norm_w, y, nullptr, nullptr, ws + w.gla,
+                   w.total - w.gla, stream);
+  if (st != DIG_OK) return st;
+  // 5. x1 = x + alpha_1 * (y W_out^T + b_out)
+  {
+    const dig_linear_out o{x1, wt->w_out, wt->b_out, D, DIG_ACT_NONE, x, mcol(2), mod_ld,
+                           (int64_t)L};
+    st = dig_linear(m, HV, DIG_BF16, y, 1, &o, stream);
+    if (st != DIG_OK) return st;
+  }
+  // 6. h = RMSNorm(x1) * gamma_2 + beta_2
+  st = dig_rmsnorm_modulate((int64_t)M, D, (int64_t)L, d->norm_eps, x1, mcol(3), mcol(4), mod_ld,
+                            h, stream);
+  if (st != DIG_OK) return st;
+  // 7. hid = GELU(h W_ffn1^T + b_ffn1)
+  {
+    const dig_linear_out o{hid, wt->w_ffn1, wt->b_ffn1, F, DIG_ACT_GELU, nullptr, nullptr, 0, 1};
+    st = dig_linear(m, D, DIG_BF16, h, 1, &o, stream);
+    if (st != DIG_OK) return st;
+  }
+  // 8. x1 += alpha_2 * (hid W_ffn2^T + b_ffn2)   (in place)
+  {
+    const dig_linear_out o{x1, wt->w_ffn2, wt->b_ffn2, D, DIG_ACT_NONE, x1, mcol(5), mod_ld,
+                           (int64_t)L};
+    st = dig_linear(m, F, DIG_BF16, hid, 1, &o, stream);
+    if (st != DIG_OK) return st;
+  }
+  // 9. SREM: 3x3 depthwise conv on the current-order grid, written in the next scan order
+  return dig_dwconv3x3(d->batch, d->grid_h, d->grid_w, D, DIG_BF16, layout, out_layout, x1,
+                       wt->conv_w, wt->conv_b, x_out, stream);
 }
 
 dig_status dig_dwconv3x3_bwd_noalloc(int32_t batch, int32_t grid_h, int32_t grid_w,

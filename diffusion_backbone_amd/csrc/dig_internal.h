@@ -131,15 +131,30 @@ hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
 // ------------------------------------------------------------------- projections
 constexpr int kLinearMaxOut = 6;
+enum { kActNone = 0, kActGelu = 1 };
 struct LinearOut {
   void* c;             // [M][n] bf16
   const void* w;       // [n][K] bf16 (out features x in features)
   const float* bias;   // [n] fp32 or null
   int n;
+  int act;             // kActNone | kActGelu, applied to A W^T + bias
+  const void* res;     // null, or R [M][n] bf16 (may be c): C = R + g * (A W^T + bias)
+  const void* gate;    // g rows [M / rows_per_gate][gate_ld] bf16 (with res)
+  long gate_ld;
+  int rows_per_gate;
 };
-// C_o = A W_o^T (+ bias_o) for every output o, A [M][K] bf16, one launch.
+// C_o = epilogue_o(A W_o^T + bias_o) for every output o, A [M][K] bf16, one launch.
 hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
                          hipStream_t st);
+
+// ------------------------------------------------------------------ DiG block
+// h[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * scale[r / rows_per_group] + shift[...], bf16 rows
+// of D (a multiple of 8, at most 2048); scale and shift rows are mod_ld apart.
+hipError_t launch_rmsnorm_modulate(long rows, int D, long rows_per_group, float eps,
+                                   const void* x, const void* scale, const void* shift,
+                                   long mod_ld, void* h, hipStream_t st);
+// y = x * sigmoid(x), n bf16 elements.
+hipError_t launch_silu(long n, const void* x, void* y, hipStream_t st);
 
 // ------------------------------------------------------------------------- misc
 // Zero n floats with a kernel (usable inside captured graphs, unlike a memset node).

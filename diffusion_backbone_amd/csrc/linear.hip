@@ -1,17 +1,21 @@
-// linear.hip -- the projections around the GLA token mixer on gfx950 bf16 matrix cores:
-//   C_o = A W_o^T (+ bias_o)   for up to kLinearMaxOut outputs o sharing the input A
+// linear.hip -- the dense projections of a DiG block on gfx950 bf16 matrix cores:
+//   C_o = epilogue_o(A W_o^T + bias_o)   for up to kLinearMaxOut outputs o sharing the input A
 // (DiG study-group slides, slide introducing GLA, eqs. (5) and (9)-(10): Q = X W_Q,
 // K = X W_K, V = X W_V, the gate logits X W_alpha (here the rank-16 factor X W_a1, then
-// (X W_a1) W_a2 + b_alpha), R = X W_r + b_r, and Y = (Swish(R) * Norm(O)) W_O).
+// (X W_a1) W_a2 + b_alpha), R = X W_r + b_r, and Y = (Swish(R) * Norm(O)) W_O; slides
+// Figure 4 and the write-up's section 3 "DiG Block": the feedforward, and the residual adds
+// scaled by the regressed alpha_1, alpha_2).  Epilogues: none, GELU, and the gated residual
+// C = R + g[row / rows_per_gate] * (A W^T + bias), R possibly C itself.
 //
 // One launch covers every output: the grid runs over (row tile, column tile of the
-// concatenated outputs), and a tile never straddles two outputs.  Tiles of 128 x 128 outputs,
-// four waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32, K step 16: on gfx950 the 32x32x16 bf16
-// instruction sustains about 1.7 times the rate of 16x16x32), K blocks of 32 staged in LDS
-// (A rows and W rows, both K-contiguous, 80-byte pitch: conflict-free 16-byte reads) with the
-// next block loaded into registers while the current one is multiplied (two LDS buffers);
-// three workgroups per compute unit.  fp32 accumulation; bias added in fp32; bf16 output
-// stored from LDS in 16-byte row pieces.
+// concatenated outputs), and a tile never straddles two outputs.  Each wave owns 64 x 64
+// outputs as 2 x 2 MFMA tiles of 32 x 32 (K step 16: on gfx950 the 32x32x16 bf16 instruction
+// sustains about 1.7 times the rate of 16x16x32); K blocks of 32 staged in LDS (A rows and W
+// rows, both K-contiguous, 80-byte pitch: conflict-free 16-byte reads) with the next block
+// loaded into registers while the current one is multiplied (two LDS buffers).  Tiles of
+// 128 x 128 (four waves, three workgroups per compute unit) or 256 x 256 (sixteen waves, one
+// per unit).  fp32 accumulation; bias and GELU in fp32; bf16 output stored from LDS in 16-byte
+// row pieces, where the gated residual is applied.
 #include "dig_device.h"
 #include "dig_internal.h"
 
@@ -23,9 +27,19 @@ struct LinOut {
   bf16* c;
   const bf16* w;
   const float* bias;
-  int n;       // columns of this output (rows of W)
-  int tile0;   // first column tile of this output in the grid
+  const bf16* res;   // gated residual R (may be c), or null
+  const bf16* gate;  // its gate rows g, [M / rows_per_gate][gate_ld]
+  long gate_ld;
+  int rows_per_gate;
+  int act;           // kActNone | kActGelu
+  int n;             // columns of this output (rows of W)
+  int tile0;         // first column tile of this output in the grid
 };
+
+// GELU in its exact form, x Phi(x) = x (1 + erf(x / sqrt 2)) / 2.
+__device__ __forceinline__ float gelu_exact(float x) {
+  return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+}
 struct LinParams {
   const bf16* a;
   int M, K, nout;
@@ -70,7 +84,9 @@ __device__ __forceinline__ void store_block(const BlockRegs<BM, BK>& r, bf16* ld
   }
 }
 
-template <int BM, int BK>
+// EPI: which epilogues this instantiation can apply (bit 0: GELU, bit 1: gated residual); the
+// choice per output is uniform over a workgroup.
+template <int BM, int BK, int EPI>
 __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
   constexpr int BN = Tile<BM>::BN, NTHR = Tile<BM>::NTHR, CPITCH = Tile<BM>::CPITCH;
   constexpr int WPR = BM / 64;    // waves per tile row
@@ -153,12 +169,16 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
       for (int j = 0; j < 2; ++j) {
         const int col = wn * 64 + 32 * j + r32;
         const float bias = (out.bias && n0 + col < out.n) ? out.bias[n0 + col] : 0.f;
+        const bool gelu = (EPI & 1) && out.act == kActGelu;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
+          for (int v = 0; v < 16; ++v) {
+            float t = acc[i][j][v] + bias;
+            if constexpr (EPI & 1) t = gelu ? gelu_exact(t) : t;
             sC[((wm & 1) * 64 + 32 * i + 8 * (v >> 2) + 4 * h32 + (v & 3)) * CPITCH + col] =
-                from_f<bf16>(acc[i][j][v] + bias);
+                from_f<bf16>(t);
+          }
       }
     }
     __syncthreads();
@@ -170,8 +190,16 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
       const int row = piece / PPRC, cp = (piece % PPRC) * 8;
       const int gr = m0 + 128 * half + row, gc = n0 + cp;
       if (gr >= p.M || gc >= out.n) continue;  // n is a multiple of 8: whole pieces only
-      *reinterpret_cast<uint4*>(out.c + (long)gr * out.n + gc) =
-          *reinterpret_cast<const uint4*>(sC + row * CPITCH + cp);
+      bf16x8 val = *reinterpret_cast<const bf16x8*>(sC + row * CPITCH + cp);
+      if ((EPI & 2) && out.res) {  // C = R + g * val, each element read and written here only
+        const bf16x8 rv = *reinterpret_cast<const bf16x8*>(out.res + (long)gr * out.n + gc);
+        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(
+            out.gate + (long)(gr / out.rows_per_gate) * out.gate_ld + gc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          val[e] = from_f<bf16>(fmaf(to_f(gv[e]), to_f(val[e]), to_f(rv[e])));
+      }
+      *reinterpret_cast<bf16x8*>(out.c + (long)gr * out.n + gc) = val;
     }
   }
 }
@@ -190,14 +218,26 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
     p.out[i].c = static_cast<bf16*>(outs[i].c);
     p.out[i].w = static_cast<const bf16*>(outs[i].w);
     p.out[i].bias = outs[i].bias;
+    p.out[i].res = static_cast<const bf16*>(outs[i].res);
+    p.out[i].gate = static_cast<const bf16*>(outs[i].gate);
+    p.out[i].gate_ld = outs[i].gate_ld;
+    p.out[i].rows_per_gate = outs[i].rows_per_gate;
+    p.out[i].act = outs[i].act;
     p.out[i].n = outs[i].n;
     p.out[i].tile0 = tiles;
     tiles += (outs[i].n + BM - 1) / BM;
   }
   const long mt = ((long)M + BM - 1) / BM;
   if (mt > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((linear_kernel<BM, 32>), dim3((unsigned)tiles, (unsigned)mt),
-                     dim3(Tile<BM>::NTHR), 0, st, p);
+  int epi = 0;
+  for (int i = 0; i < nout; ++i) epi |= (outs[i].act == kActGelu ? 1 : 0) | (outs[i].res ? 2 : 0);
+  const dim3 grid((unsigned)tiles, (unsigned)mt), block(Tile<BM>::NTHR);
+  switch (epi) {
+    case 0: hipLaunchKernelGGL((linear_kernel<BM, 32, 0>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((linear_kernel<BM, 32, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((linear_kernel<BM, 32, 2>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((linear_kernel<BM, 32, 3>), grid, block, 0, st, p); break;
+  }
   return hipGetLastError();
 }
 

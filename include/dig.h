@@ -15,7 +15,8 @@
  *     means nothing was written; dig_last_error() gives a thread-local description.
  *     DIG_ERR_DEVICE means a launch failed; faults inside kernels surface at the
  *     caller's next synchronisation.  Nothing throws or aborts across the ABI.
- *   - Outputs may not overlap inputs (DIG_ERR_ALIAS): no in-place operation.
+ *   - Outputs may not overlap inputs (DIG_ERR_ALIAS): no in-place operation (one
+ *     exception: dig_linear's residual may be its own output).
  *   - Empty problems (batch == 0 or seq_len == 0) return DIG_OK and touch nothing.
  *   - Element type of the activations is DIG_BF16 (bfloat16) or DIG_F32; arithmetic is
  *     fp32 throughout.  Norm weights, conv weights/bias and their gradients are fp32.
@@ -30,6 +31,10 @@
  *   SREM: slides "SREM の導入" and write-up section 3 "DiG Block": reshape to 2-D,
  *        3x3 depthwise conv, transpose the token matrix and flip the flattened sequence to
  *        change the next block's scan direction.
+ *   Block: slides Figure 4 (RMS Norm, Scale & Shift, Gated Linear Attention, Scale,
+ *        RMS Norm, Scale & Shift, Feedforward, Scale, SREM; an MLP from the conditioning)
+ *        and write-up section 3 "DiG Block" (adaptive normalisation regressed from the
+ *        summed timestep and label embeddings).
  */
 #ifndef DIG_H_
 #define DIG_H_
@@ -140,28 +145,126 @@ dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, c
 /* ------------------------------------------------------------------ projections */
 
 /*
- * dig_linear -- the projections around the token mixer (slides eqs. (5), (9), (10):
- * Q = X W_Q, K = X W_K, V = X W_V, the low-rank gate logits (X W_a1) W_a2 + b_alpha,
- * R = X W_r + b_r, Y = (Swish(R) * Norm(O)) W_O) as one bf16 matrix-core launch:
- *   outs[o].c[i][j] = sum_l a[i][l] * outs[o].w[j][l]  (+ outs[o].bias[j])
- * for every output o (up to DIG_LINEAR_MAX_OUT sharing the input a), fp32 accumulation,
- * result rounded to bf16 (round to nearest even).
+ * dig_linear -- the dense projections of a DiG block as one bf16 matrix-core launch: the
+ * token mixer's inputs and output (slides eqs. (5), (9), (10): Q = X W_Q, K = X W_K,
+ * V = X W_V, the low-rank gate logits (X W_a1) W_a2 + b_alpha, R = X W_r + b_r,
+ * Y = (Swish(R) * Norm(O)) W_O) and the feedforward with the alpha-scaled residual adds
+ * (slides Figure 4; write-up section 3 "DiG Block").  For every output o (up to
+ * DIG_LINEAR_MAX_OUT sharing the input a):
+ *   t[i][j] = sum_l a[i][l] * w[j][l] + bias[j]              fp32 accumulation
+ *   t = GELU(t) = t * Phi(t)    if act == DIG_ACT_GELU (exact, erf form), then bf16
+ *   c[i][j] = bf16(res[i][j] + gate[i / rows_per_gate][j] * t[i][j])   if res != NULL
+ *   c[i][j] = t[i][j]                                                 otherwise
+ * (bf16 values rounded to nearest even; the gated form rounds t to bf16 first).
  *   a          : [m][k] bf16, row-major (m rows, e.g. batch * tokens)
- *   outs[o].w  : [n][k] bf16 (out features x in features, as a linear layer's weight)
- *   outs[o].bias : [n] fp32 or NULL
- *   outs[o].c  : [m][n] bf16 output (contiguous: [B, L, H, d] for the mixer's operands)
- * dtype must be DIG_BF16; k and every n must be multiples of 8.  Outputs may not overlap
- * inputs or each other (DIG_ERR_ALIAS).
+ *   w          : [n][k] bf16 (out features x in features, as a linear layer's weight)
+ *   bias       : [n] fp32 or NULL
+ *   c          : [m][n] bf16 output (contiguous: [B, L, H, d] for the mixer's operands)
+ *   res        : NULL, or [m][n] bf16; may be c itself (in-place residual add)
+ *   gate       : with res: rows of n bf16 gate values, row g at gate + g * gate_ld, one row
+ *                per rows_per_gate consecutive rows of c (one per image); gate_ld >= n
+ * dtype must be DIG_BF16; k, every n and gate_ld must be multiples of 8.  Outputs may not
+ * overlap a, w, bias, gate, other outputs, or a res other than their own c (DIG_ERR_ALIAS).
  */
 #define DIG_LINEAR_MAX_OUT 6
+#define DIG_ACT_NONE 0
+#define DIG_ACT_GELU 1
 typedef struct {
   void* c;
   const void* w;
   const float* bias;
   int32_t n;
+  int32_t act;
+  const void* res;
+  const void* gate;
+  int64_t gate_ld;
+  int64_t rows_per_gate;
 } dig_linear_out;
 dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
                       const dig_linear_out* outs, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- DiG block */
+
+/*
+ * dig_rmsnorm_modulate -- the adaptive normalisation in front of a DiG block's GLA layer
+ * and feedforward (slides Figure 4: RMS Norm, then Scale & Shift by gamma, beta regressed
+ * from the conditioning; write-up section 3 "DiG Block"):
+ *   h[i][:] = x[i][:] * rsqrt(mean_j x[i][j]^2 + eps) * scale[g][:] + shift[g][:],
+ *   g = i / rows_per_group (the image of row i), scale/shift row g at scale + g * mod_ld.
+ * x, h: [rows][dim] bf16; scale, shift: bf16 rows; dim and mod_ld multiples of 8,
+ * dim <= 2048.  fp32 arithmetic, h rounded to bf16.  h may not overlap the inputs.
+ */
+dig_status dig_rmsnorm_modulate(int64_t rows, int32_t dim, int64_t rows_per_group, float eps,
+                                const void* x, const void* scale, const void* shift,
+                                int64_t mod_ld, void* h, hipStream_t stream);
+
+/*
+ * One DiG block's shapes (slides Figure 4 and Table 1; write-up section 3 "DiG Block" and
+ * "Architecture Details").  The GLA layer's projections read the block's normalised input:
+ *   [q | k | v | u | r] = h W_in^T + b_in     (q, k: H*d_k; v, r: H*d_v; u: gate_rank)
+ *   z = u W_gate^T + b_gate                    (gate logits, H*d_k; b_gate is b_alpha)
+ * and the feedforward is dim -> ffn_dim -> dim with GELU between.
+ */
+typedef struct {
+  int32_t batch, grid_h, grid_w; /* tokens per image L = grid_h * grid_w */
+  int32_t dim;                   /* hidden size D (multiple of 8, <= 2048) */
+  int32_t heads, d_k, d_v;       /* the GLA layer: H * d_k, H * d_v multiples of 8 */
+  int32_t gate_rank;             /* rank of the gate logits' factorisation (multiple of 8) */
+  int32_t ffn_dim;               /* feedforward hidden width (multiple of 8) */
+  int32_t chunk;                 /* GLA chunk: 16 | 32 | 64 */
+  float tau;                     /* gate temperature */
+  float norm_eps;                /* epsilon of the block's RMSNorms and the head-wise one */
+} dig_block_desc;
+
+/* One block's weights: bf16 matrices [out features][in features], fp32 vectors. */
+typedef struct {
+  const void* w_in;         /* [2 H d_k + 2 H d_v + gate_rank][dim]: rows q | k | v | u | r */
+  const float* b_in;        /* the same rows, or NULL */
+  const void* w_gate;       /* [H d_k][gate_rank] */
+  const float* b_gate;      /* [H d_k] or NULL */
+  const float* gla_norm_w;  /* [d_v] head-wise RMSNorm weight, or NULL (ones) */
+  const void* w_out;        /* [dim][H d_v] */
+  const float* b_out;       /* [dim] or NULL */
+  const void* w_ffn1;       /* [ffn_dim][dim] */
+  const float* b_ffn1;      /* [ffn_dim] or NULL */
+  const void* w_ffn2;       /* [dim][ffn_dim] */
+  const float* b_ffn2;      /* [dim] or NULL */
+  const float* conv_w;      /* [dim][3][3] SREM depthwise conv */
+  const float* conv_b;      /* [dim] or NULL */
+} dig_block_weights;
+
+/*
+ * dig_block_cond -- the conditioning regression of a stack of n_blocks DiG blocks (slides
+ * Figure 4: the MLP from the summed timestep and label embeddings to each block's
+ * gamma, beta, alpha):
+ *   mod[b][:] = SiLU(c[b][:]) W_ada^T + b_ada,   c: [batch][dim] bf16,
+ *   W_ada: [n_blocks * 6 * dim][dim] bf16, b_ada: fp32 or NULL, mod: [batch][n_blocks*6*dim].
+ * Block l's parameters are mod[b][6 dim l + ...] in the order
+ *   gamma_1 | beta_1 | alpha_1 | gamma_2 | beta_2 | alpha_2   (dim each),
+ * gamma used as the multiplier itself (h * gamma + beta).  workspace: batch * dim * 2 bytes
+ * (dig_block_cond_workspace_bytes).
+ */
+size_t dig_block_cond_workspace_bytes(int32_t batch, int32_t dim);
+dig_status dig_block_cond(int32_t batch, int32_t dim, int32_t n_blocks, const void* c,
+                          const void* w_ada, const float* b_ada, void* mod, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dig_block_fwd -- one DiG block forward (slides Figure 4; write-up section 3 "DiG Block"),
+ * on x in scan order `layout`, writing the result in scan order `out_layout`:
+ *   x1 = x  + alpha_1 * GLA(RMSNorm(x)  * gamma_1 + beta_1)        GLA: eqs. (5)-(10), W_O
+ *   x2 = x1 + alpha_2 * FFN(RMSNorm(x1) * gamma_2 + beta_2)        FFN: W_ffn2 GELU(W_ffn1 .)
+ *   x_out = DWConv3x3(x2) reoriented from `layout` to `out_layout` (SREM)
+ * x, x_out: [batch][L][dim] bf16; mod: this block's 6*dim parameters of image 0 (see
+ * dig_block_cond), image b's at mod + b * mod_ld.  The GLA layer runs dig_gla_fwd's kernels
+ * with the same limits (d_k <= 64, d_v <= 128).  workspace: dig_block_fwd_workspace_bytes.
+ * x_out may not overlap x, mod, the weights or the workspace.
+ */
+size_t dig_block_fwd_workspace_bytes(const dig_block_desc* desc);
+dig_status dig_block_fwd(const dig_block_desc* desc, const dig_block_weights* wts,
+                         const void* mod, int64_t mod_ld, int32_t layout, int32_t out_layout,
+                         const void* x, void* x_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------- SREM */
 
