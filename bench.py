@@ -400,14 +400,23 @@ def projections(cfg, steps):
     gate_up = lambda: dig.dig_linear(M, cfg.rank, zl, [(z, wa2, b_alpha)])
     proj_out = lambda: dig.dig_linear(M, H * dv, y, [(yo, wo, None)])
     n_in = 2 * H * dk + 2 * H * dv + cfg.rank
+    # the same products through torch's library GEMM (hipBLASLt), as a reference point only
+    w_cat = torch.cat([wq, wk, wv, wa1, wr], dim=0).contiguous()
+    x2, y2 = x.view(M, D), y.view(M, H * dv)
+    lib_in = lambda: torch.nn.functional.linear(x2, w_cat)
+    lib_out = lambda: torch.nn.functional.linear(y2, wo)
     res = {}
-    for name, fn, flops in (("in_projection", proj_in, 2.0 * M * D * n_in),
-                            ("gate_up_projection", gate_up, 2.0 * M * cfg.rank * H * dk),
-                            ("out_projection", proj_out, 2.0 * M * H * dv * D)):
+    for name, fn, flops, ref in (("in_projection", proj_in, 2.0 * M * D * n_in, lib_in),
+                                 ("gate_up_projection", gate_up, 2.0 * M * cfg.rank * H * dk, None),
+                                 ("out_projection", proj_out, 2.0 * M * H * dv * D, lib_out)):
         ms = timed(fn, steps, 3)
         tf = flops / (ms / 1e3) / 1e12
         res[name] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
                      "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops}
+        if ref is not None:
+            ms_ref = timed(ref, steps, 3)
+            res[name]["torch_linear_reference_us"] = round(ms_ref * 1e3, 1)
+            res[name]["torch_linear_reference_tflops"] = round(flops / (ms_ref / 1e3) / 1e12, 1)
 
     def layer():
         proj_in()
@@ -423,6 +432,129 @@ def projections(cfg, steps):
         "tokens_per_s": round(M / (ms / 1e3), 1)}
     res["workload"] = cfg.name
     return res
+
+
+def block_stack(name, steps, warmup=2):
+    """The DiG block stack forward (slides Figure 4, Table 1): the conditioning regression of
+    every block (dig_block_cond), then n blocks of dig_block_fwd cycling the four scan
+    directions, on random-init weights of the model's shapes (projections ~ N(0, 1/fan_in),
+    DWConv identity + noise, adaLN gamma ~ 1, alpha ~ 0.5) and x ~ N(0, 1).  Reported: images/s
+    and tokens/s of the whole forward, the dense-matmul share against the bf16 peak, and one
+    block's steps timed one by one through the public calls the block composes."""
+    import torch
+    import diffusion_backbone_amd as dig
+    if name in W.STACKS:
+        cfg, nb = W.STACKS[name]
+    else:  # the headline image size with the XL/2 stack
+        cfg, nb = W.CONFIGS["dig_xl2_2048"], 28
+    B, L, D, H, dk, dv, R = cfg.batch, cfg.seq_len, cfg.d_model, cfg.heads, cfg.d_k, cfg.d_v, cfg.rank
+    F, M = 4 * D, cfg.batch * cfg.seq_len
+    HK, HV = H * dk, H * dv
+    nin = 2 * HK + 2 * HV + R
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 9)
+    bf = lambda *sh, s=1.0: (torch.randn(*sh, device="cuda", generator=g) * s).to(torch.bfloat16)
+    f32 = lambda n, s=0.1: torch.randn(n, device="cuda", generator=g) * s
+    keep, structs = [], []
+    for _ in range(nb):
+        cw = torch.randn(D, 3, 3, device="cuda", generator=g) / 6.0
+        cw[:, 1, 1] += 1.0
+        t = dict(w_in=bf(nin, D, s=D ** -0.5), b_in=f32(nin), w_gate=bf(HK, R, s=R ** -0.5),
+                 b_gate=f32(HK, 1.0), gla_norm_w=1.0 + f32(dv), w_out=bf(D, HV, s=HV ** -0.5),
+                 b_out=f32(D), w_ffn1=bf(F, D, s=D ** -0.5), b_ffn1=f32(F),
+                 w_ffn2=bf(D, F, s=F ** -0.5), b_ffn2=f32(D), conv_w=cw, conv_b=f32(D))
+        keep.append(t)
+        structs.append(dig.make_block_weights(**t))
+    part = torch.cat([torch.full((D,), v, device="cuda") for v in (1.0, 0.0, 0.5, 1.0, 0.0, 0.5)])
+    c = bf(B, D)
+    w_ada = bf(nb * 6 * D, D, s=0.1 * D ** -0.5)
+    b_ada = part.repeat(nb).contiguous()
+    mod = torch.empty(B, nb * 6 * D, dtype=torch.bfloat16, device="cuda")
+    desc = dig.make_block_desc(B, cfg.grid_h, cfg.grid_w, D, H, dk, dv, R, F, cfg.chunk, cfg.tau)
+    wsb = max(dig.dig_block_fwd_workspace_bytes(desc), dig.dig_block_cond_workspace_bytes(B, D))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    x0 = bf(B, L, D)
+    xa, xb = torch.empty_like(x0), torch.empty_like(x0)
+    mld = nb * 6 * D
+
+    def forward():
+        dig.dig_block_cond(B, D, nb, c, w_ada, b_ada, mod, ws)
+        src, dst = x0, xa
+        for l in range(nb):
+            d, dn = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
+            dig.dig_block_fwd(desc, structs[l], mod[:, 6 * D * l:], mld, d, dn, src, dst, ws)
+            src, dst = dst, (xb if dst is xa else xa)
+    ms = timed(forward, steps, warmup)
+    # the same forward captured once in a HIP graph and replayed (no host launch overhead)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        forward()
+    ms_graph = timed(graph.replay, steps, warmup)
+    del graph
+    gemm = 2.0 * M * (D * nin + R * HK + HV * D + 2 * D * F)
+    out = {"what": "dig_block_cond + %d x dig_block_fwd (four scan directions cycling)" % nb,
+           "batch": B, "grid": [cfg.grid_h, cfg.grid_w], "d_model": D, "heads": H, "d_k": dk,
+           "d_v": dv, "ffn_dim": F, "blocks": nb, "ms_per_forward": round(ms, 4),
+           "images_per_s": round(B / (ms / 1e3), 2),
+           "tokens_per_s": round(M / (ms / 1e3), 1),
+           "matmul_flops_per_forward": gemm * nb,
+           "matmul_tflops_over_whole_forward": round(gemm * nb / (ms / 1e3) / 1e12, 1),
+           "graph_replay": {"ms_per_forward": round(ms_graph, 4),
+                            "images_per_s": round(B / (ms_graph / 1e3), 2),
+                            "tokens_per_s": round(M / (ms_graph / 1e3), 1)}}
+    # one block's steps, each timed alone through the public calls dig_block_fwd composes
+    t = keep[0]
+    h, x1 = torch.empty_like(x0), torch.empty_like(x0)
+    q, k, z = (torch.empty(M, HK, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    v, r, y = (torch.empty(M, HV, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    u = torch.empty(M, R, dtype=torch.bfloat16, device="cuda")
+    hid = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    gdesc = dig.make_desc(B, L, H, dk, dv, cfg.chunk, cfg.tau, 1.0, 1e-5, dig.DIG_BF16, 0)
+    gwb = dig.dig_gla_fwd_workspace_bytes(gdesc)
+    gws = torch.empty(max(gwb, 16), dtype=torch.uint8, device="cuda")
+    rows = [0, HK, 2 * HK, 2 * HK + HV, 2 * HK + HV + R, nin]
+    outs_in = [(o, t["w_in"][rows[i]:rows[i + 1]], t["b_in"][rows[i]:rows[i + 1]])
+               for i, o in enumerate((q, k, v, u, r))]
+    steps_ = (
+        ("rmsnorm_modulate", lambda: dig.dig_rmsnorm_modulate(M, D, L, 1e-5, x0, mod, mod[:, D:],
+                                                              mld, h), 0.0),
+        ("in_projection", lambda: dig.dig_linear(M, D, h, outs_in), 2.0 * M * D * nin),
+        ("gate_up_projection", lambda: dig.dig_linear(M, R, u, [(z, t["w_gate"], t["b_gate"])]),
+         2.0 * M * R * HK),
+        ("gla_fwd", lambda: dig.dig_gla_fwd(gdesc, q, k, v, z, r, t["gla_norm_w"], y, None, None,
+                                            gws, gwb), 0.0),
+        ("out_projection_gated_residual", lambda: dig.dig_linear(M, HV, y, [dig.linear_out(
+            x1, t["w_out"], t["b_out"], res=x0, gate=mod[:, 2 * D:], gate_ld=mld,
+            rows_per_gate=L)]), 2.0 * M * HV * D),
+        ("ffn1_gelu", lambda: dig.dig_linear(M, D, h, [dig.linear_out(
+            hid, t["w_ffn1"], t["b_ffn1"], act=dig.DIG_ACT_GELU)]), 2.0 * M * D * F),
+        ("ffn2_gated_residual", lambda: dig.dig_linear(M, F, hid, [dig.linear_out(
+            x1, t["w_ffn2"], t["b_ffn2"], res=x1, gate=mod[:, 5 * D:], gate_ld=mld,
+            rows_per_gate=L)]), 2.0 * M * F * D),
+        ("dwconv3x3_reorient", lambda: dig.dig_dwconv3x3(B, cfg.grid_h, cfg.grid_w, D,
+                                                         dig.DIG_BF16, W.ROW, W.ROW_REV, x1,
+                                                         t["conv_w"], t["conv_b"], xa), 0.0),
+    )
+    parts = {}
+    for pname, fn, flops in steps_:
+        pm = timed(fn, max(5, steps), 2)
+        e = {"us": round(pm * 1e3, 1)}
+        if flops:
+            tf = flops / (pm / 1e3) / 1e12
+            e.update(tflops=round(tf, 1), frac_of_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4))
+        else:
+            e["gbs_in_out"] = round(2 * M * D * 2 / (pm / 1e3) / 1e9, 1) if pname != "gla_fwd" \
+                else round(gla_bytes_per_token_head(cfg, "fwd") * M * H / (pm / 1e3) / 1e9, 1)
+        parts[pname] = e
+    out["one_block_parts"] = parts
+    out["one_block_us"] = round(ms * 1e3 / nb, 1)
+    return out
 
 
 def _median(xs):
@@ -737,6 +869,11 @@ def main():
             print("[bench] %s done" % name, file=sys.stderr, flush=True)
         out["configs"] = configs
         out["projections"] = projections(cfg, max(10, args.steps // 2))
+        stacks = {}
+        for sname in ("dig_s2_256_stack", "dig_xl2_256_stack", "dig_xl2_2048_stack"):
+            stacks[sname] = block_stack(sname, max(5, args.steps // 10))
+            print("[bench] %s done" % sname, file=sys.stderr, flush=True)
+        out["block_stack_fwd"] = stacks
         out["mfma_microbench"] = contraction_microbench()
         out["probes"] = probes()
     if not args.no_cpu_baseline:

@@ -245,3 +245,57 @@ def test_block_stack_free_running(cfg, n_blocks):
         e = maxrel(got, x_ref)
         print("  block %2d err %.2e %s" % (l, e, _diag(got, x_ref)), flush=True)
         assert e <= TOL["bf16"], (l, e)
+
+
+def test_block_stack_graph_replay():
+    """dig_block_cond + four dig_block_fwd calls captured once in a HIP graph and replayed over
+    new inputs, with eager work and synchronisation between replays: every replay must give the
+    eager calls' bits for the same inputs."""
+    import torch
+    import diffusion_backbone_amd as dig
+    cfg, nb = S16, 4
+    D = cfg.d_model
+    announce("block stack graph replay, %d blocks" % nb)
+    rng = np.random.default_rng(51)
+    devs = [_dev_weights(W.make_dig_block_weights(cfg, rng)) for _ in range(nb)]
+    cond = W.make_block_cond(cfg, nb, rng)
+    c = to_dev(cond["c"], "bf16")
+    w_ada, b_ada = to_dev(cond["w_ada"], "bf16"), _f32(cond["b_ada"])
+    desc = _desc(cfg)
+    ws = nbytes_buf(max(dig.dig_block_fwd_workspace_bytes(desc),
+                        dig.dig_block_cond_workspace_bytes(cfg.batch, D)))
+    mod = torch.empty(cfg.batch, nb * 6 * D, dtype=torch.bfloat16, device="cuda")
+    x0 = torch.empty(cfg.batch, cfg.seq_len, D, dtype=torch.bfloat16, device="cuda")
+    bufs = [torch.empty_like(x0) for _ in range(2)]
+
+    def forward():
+        dig.dig_block_cond(cfg.batch, D, nb, c, w_ada, b_ada, mod, ws)
+        src = x0
+        for l in range(nb):
+            dst = bufs[l % 2]
+            dig.dig_block_fwd(desc, devs[l][1], mod[:, 6 * D * l:], nb * 6 * D, W.SCHEDULE[l % 4],
+                              W.SCHEDULE[(l + 1) % 4], src, dst, ws)
+            src = dst
+        return src
+
+    x0.copy_(to_dev(W.quantize(rng.standard_normal(tuple(x0.shape)), "bf16"), "bf16"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = forward()
+    torch.cuda.synchronize()
+    for i in range(3):
+        x0.copy_(to_dev(W.quantize(rng.standard_normal(tuple(x0.shape)), "bf16"), "bf16"))
+        c.copy_(to_dev(W.quantize(rng.standard_normal(tuple(c.shape)), "bf16"), "bf16"))
+        want = to_f64(forward())
+        torch.cuda.synchronize()
+        for b in bufs:
+            b.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(out), want), "replay %d differs from the eager calls" % i
