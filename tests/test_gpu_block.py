@@ -196,7 +196,7 @@ def test_block_fwd_rejects_bad_arguments():
     assert need > 0
     x = torch.zeros(cfg.batch, cfg.seq_len, cfg.d_model, dtype=torch.bfloat16, device="cuda")
     mod = torch.zeros(cfg.batch, 6 * cfg.d_model, dtype=torch.bfloat16, device="cuda")
-    _, wts = _dev_weights(W.make_dig_block_weights(cfg, np.random.default_rng(1)))
+    wkeep, wts = _dev_weights(W.make_dig_block_weights(cfg, np.random.default_rng(1)))
     ws = nbytes_buf(need)
     with pytest.raises(dig.DigError) as ei:             # output aliasing the input
         dig.dig_block_fwd(desc, wts, mod, 6 * cfg.d_model, 0, 1, x, x, ws)
@@ -299,3 +299,26 @@ def test_block_stack_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_f64(out), want), "replay %d differs from the eager calls" % i
+
+
+def test_block_fwd_full_xl2_2048():
+    """One DiG-XL/2 block at the full 2048-px size (128 x 128 tokens, the launch configuration
+    the bench times), every output element against the oracle."""
+    import torch
+    import diffusion_backbone_amd as dig
+    cfg = W.CONFIGS["dig_xl2_2048"]
+    announce("block_fwd full dig_xl2_2048 col -> col_rev")
+    x, mod, wts = _block_case(cfg, 61)
+    desc = _desc(cfg)
+    wdev, ws_struct = _dev_weights(wts)   # wdev keeps the weights alive
+    ws = nbytes_buf(dig.dig_block_fwd_workspace_bytes(desc))
+    out = _gpu_block(cfg, desc, wdev, ws_struct, to_dev(x, "bf16"), to_dev(mod, "bf16"),
+                     6 * cfg.d_model, W.COL, W.COL_REV, ws)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    announce("  oracle (fp64, about 20 s)")
+    ref = oracle.block_forward(x, mod, wts, cfg.grid_h, cfg.grid_w, cfg.heads, cfg.d_k, cfg.d_v,
+                               W.COL, W.COL_REV, tau=cfg.tau)
+    e = maxrel(got, ref)
+    print("  err %.2e %s" % (e, _diag(got, ref)), flush=True)
+    assert e <= TOL["bf16"]
