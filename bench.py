@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--pmc-target", choices=["gla_fwd", "gla_bwd", "srem_fwd", "srem_bwd"],
                     default=None)
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--stack", default=None,
+                    choices=["dig_s2_256_stack", "dig_xl2_256_stack", "dig_xl2_2048_stack"],
+                    help="time only this DiG block stack forward (for kernel traces)")
     ap.add_argument("--oracle-leg", default=None, help=argparse.SUPPRESS)  # child process
     return ap.parse_args()
 
@@ -205,14 +208,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 145353.7 KiB / 0.50008 + 92162.7 KiB / 1.0, segment scan 1666.6 + 2594.2,
-        # final pass 95190.5 + 94244.6 (FETCH_SIZE, WRITE_SIZE; copy: 131091.9 KiB read per
+        # pass A 145343.5 KiB / 0.50008 + 92098.4 KiB / 1.0, segment scan 1666.7 + 2594.2,
+        # final pass 95169.4 + 94197.1 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 689510069,
-        # pass A 79442.9 + 5099.5, state scan 2819.1 + 5184.0, output pass 67650.9 + 156470.6
-        "dig_gla_fwd": 477731438,
+        "dig_gla_bwd": 689331909,
+        # pass A 79443.0 + 5099.5, state scan 2819.1 + 5184.0, output pass 67650.1 + 156476.2
+        "dig_gla_fwd": 477735727,
     },
-    "sources_sha256": "81da8ce96e0d08d2c80a5db9a738417eeba256f4acf3cc0ea90fbb34fcfeb312",
+    "sources_sha256": "78a45912ba0c9fe80df906d12bf7909ff4fc3da4deed651a746f9fc488ec3e39",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
@@ -762,6 +765,9 @@ def main():
     import torch
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, max(1, args.steps))
+        return
+    if args.stack:
+        print(json.dumps({args.stack: block_stack(args.stack, max(1, args.steps))}), flush=True)
         return
     cfg = W.CONFIGS[args.workload]
     nblocks = n_blocks(cfg)

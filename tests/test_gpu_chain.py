@@ -1,13 +1,13 @@
 """GPU parity of the DiG-S/2 256-px twelve-block chain (the mixer and SREM step of every block,
 four scan directions cycling ROW, ROW_REV, COL, COL_REV).
 
-Block l runs in scan order d(l): the host projects its input x_l to q, k, v, z, r (fp64
-matmuls, bf16 operands), dig_gla_fwd mixes the tokens, the host applies the output projection
-and the residual, x_l + Y_l W_O, and dig_dwconv3x3 convolves that on the current-order grid
-and writes it in the next block's order d(l+1) (DiG write-up, section 3 "DiG Block").  The
-GPU's output of block l is block l+1's input (teacher forcing), and each block's mixer output
-and SREM output are checked against the fp64 oracle on the same inputs.  The whole chain is
-also run through the oracle alone, and the final deviation is logged.
+Block l runs in scan order d(l): its input x_l is projected to q, k, v, z, r (fp64 matmuls,
+bf16 operands), the mixer runs, the output projection and the residual give x_l + Y_l W_O, and
+the 3x3 conv runs on the current-order grid and writes the next block's order d(l+1) (DiG
+write-up, section 3 "DiG Block").  On the GPU the mixer is dig_gla_fwd and the conv
+dig_dwconv3x3; the oracle runs the same chain with its own functions.  The two chains run free:
+each from its own previous block (every block boundary holds bf16 on both sides), so no oracle
+input ever comes from the GPU.  Every block's mixer output and SREM output are compared.
 """
 import numpy as np
 import pytest
@@ -33,12 +33,11 @@ def test_chain_dig_s2_256_twelve_blocks():
     for l in range(cfg.blocks):
         d, dn = W.SCHEDULE[l % 4], W.SCHEDULE[(l + 1) % 4]
         announce("chain block %d: %s -> %s" % (l, W.SCAN_NAMES[d], W.SCAN_NAMES[dn]))
+        # GPU chain, from the GPU's previous block
         q, k, v, z, r = W.project(cfg, x, wts[l])
         case = W.GLACase(cfg, q, k, v, z, r, gamma, None)
         f = gla_forward(case, cfg.chunk, want_opre=False)
         y = to_f64(f["y"])
-        y_ref, _, _ = oracle.gla_fwd(q, k, v, z, r, gamma)
-        ey = maxrel(y, y_ref)
         res = W.quantize(x + y.reshape(B, cfg.seq_len, -1) @ wts[l].wo, "bf16")
         xd = to_dev(res, "bf16")
         wd = torch.from_numpy(wts[l].conv_w.astype(np.float32)).cuda()
@@ -46,15 +45,14 @@ def test_chain_dig_s2_256_twelve_blocks():
         dig.dig_dwconv3x3(B, gh, gw, D, dig.DIG_BF16, d, dn, xd, wd, None, out)
         torch.cuda.synchronize()
         x_next = to_f64(out)
-        ec = maxrel(x_next, oracle.dwconv3x3(res, wts[l].conv_w, gh, gw, d, dn))
-        # the oracle alone, from the oracle's own previous block
+        # oracle chain, from the oracle's previous block
         qr, kr, vr, zr, rr = W.project(cfg, x_ref, wts[l])
         yr, _, _ = oracle.gla_fwd(qr, kr, vr, zr, rr, gamma)
         res_r = W.quantize(x_ref + yr.reshape(B, cfg.seq_len, -1) @ wts[l].wo, "bf16")
         x_ref = W.quantize(oracle.dwconv3x3(res_r, wts[l].conv_w, gh, gw, d, dn), "bf16")
-        drift = maxrel(x_next, x_ref)
-        print("  block %2d %-7s y=%.2e srem=%.2e  free-running drift %.2e"
-              % (l, W.SCAN_NAMES[d], ey, ec, drift), flush=True)
+        ey = maxrel(y, yr)
+        ec = maxrel(x_next, x_ref)
+        print("  block %2d %-7s y=%.2e srem=%.2e" % (l, W.SCAN_NAMES[d], ey, ec), flush=True)
         assert ey <= TOL["bf16"], ("y", l, ey)
         assert ec <= TOL["bf16"], ("srem", l, ec)
         x = x_next
