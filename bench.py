@@ -544,6 +544,21 @@ def block_stack(name, steps, warmup=2):
                                                          dig.DIG_BF16, W.ROW, W.ROW_REV, x1,
                                                          t["conv_w"], t["conv_b"], xa), 0.0),
     )
+    # the one-output products as dig_block_fwd issues them: K split over a workspace where the
+    # grid of tiles would not fill the GPU
+    lws = torch.empty(max(dig.dig_block_fwd_workspace_bytes(desc), 16), dtype=torch.uint8,
+                      device="cuda")
+    split = {
+        "out_projection_gated_residual": lambda: dig.dig_linear_ws(M, HV, y, [dig.linear_out(
+            x1, t["w_out"], t["b_out"], res=x0, gate=mod[:, 2 * D:], gate_ld=mld,
+            rows_per_gate=L)], lws),
+        "ffn1_gelu": lambda: dig.dig_linear_ws(M, D, h, [dig.linear_out(
+            hid, t["w_ffn1"], t["b_ffn1"], act=dig.DIG_ACT_GELU)], lws),
+        "ffn2_gated_residual": lambda: dig.dig_linear_ws(M, F, hid, [dig.linear_out(
+            x1, t["w_ffn2"], t["b_ffn2"], res=x1, gate=mod[:, 5 * D:], gate_ld=mld,
+            rows_per_gate=L)], lws),
+    }
+    steps_ = tuple((n, split.get(n, fn), fl) for n, fn, fl in steps_)
     parts = {}
     for pname, fn, flops in steps_:
         pm = timed(fn, max(5, steps), 2)

@@ -29,7 +29,8 @@ EXPORTS = (
     "dig_last_error", "dig_abi_version", "dig_lookback_status", "dig_debug_lookback",
     "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes", "dig_linear",
     "dig_rmsnorm_modulate", "dig_block_cond_workspace_bytes", "dig_block_cond",
-    "dig_block_fwd_workspace_bytes", "dig_block_fwd",
+    "dig_block_fwd_workspace_bytes", "dig_block_fwd", "dig_linear_workspace_bytes",
+    "dig_linear_ws",
 )
 DIG_LINEAR_MAX_OUT = 6
 DIG_ACT_NONE, DIG_ACT_GELU = 0, 1
@@ -123,6 +124,10 @@ def lib() -> ctypes.CDLL:
         L.dig_dwconv3x3_bwd_noalloc_max_bytes.restype = S
         L.dig_linear.argtypes = [I, I, I, P, I, ctypes.POINTER(dig_linear_out), P]
         L.dig_linear.restype = ctypes.c_int
+        L.dig_linear_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(dig_linear_out)]
+        L.dig_linear_workspace_bytes.restype = S
+        L.dig_linear_ws.argtypes = [I, I, I, P, I, ctypes.POINTER(dig_linear_out), P, S, P]
+        L.dig_linear_ws.restype = ctypes.c_int
         I64, F = ctypes.c_int64, ctypes.c_float
         L.dig_rmsnorm_modulate.argtypes = [I64, I, I64, F, P, P, P, I64, P, P]
         L.dig_rmsnorm_modulate.restype = ctypes.c_int
@@ -276,9 +281,7 @@ def linear_out(c, w, bias=None, act=DIG_ACT_NONE, res=None, gate=None, gate_ld=0
                 rows_per_gate=rows_per_gate, n=n)
 
 
-def dig_linear(m, k, a, outs, stream=None):
-    """outs: sequence of (c, w, bias_or_None) tuples or linear_out(...) dicts;
-    c [m, n] bf16, w [n, k] bf16."""
+def _linear_outs(outs):
     arr = (dig_linear_out * max(len(outs), 1))()
     for i, o in enumerate(outs):
         if not isinstance(o, dict):
@@ -287,8 +290,26 @@ def dig_linear(m, k, a, outs, stream=None):
         arr[i] = dig_linear_out(_ptr(o["c"]), _ptr(o["w"]), _ptr(o["bias"]), n, int(o["act"]),
                                 _ptr(o["res"]), _addr(o["gate"]), int(o["gate_ld"]),
                                 int(o["rows_per_gate"]))
-    st = lib().dig_linear(int(m), int(k), DIG_BF16, _ptr(a), len(outs), arr, _stream(stream))
+    return arr
+
+
+def dig_linear(m, k, a, outs, stream=None):
+    """outs: sequence of (c, w, bias_or_None) tuples or linear_out(...) dicts;
+    c [m, n] bf16, w [n, k] bf16."""
+    st = lib().dig_linear(int(m), int(k), DIG_BF16, _ptr(a), len(outs), _linear_outs(outs),
+                          _stream(stream))
     _check(st, "dig_linear")
+
+
+def dig_linear_workspace_bytes(m, k, outs) -> int:
+    return lib().dig_linear_workspace_bytes(int(m), int(k), len(outs), _linear_outs(outs))
+
+
+def dig_linear_ws(m, k, a, outs, workspace, workspace_bytes=None, stream=None):
+    st = lib().dig_linear_ws(int(m), int(k), DIG_BF16, _ptr(a), len(outs), _linear_outs(outs),
+                             _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                             _stream(stream))
+    _check(st, "dig_linear_ws")
 
 
 # ---------------------------------------------------------------- DiG block

@@ -140,7 +140,7 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 102; }
+int32_t dig_abi_version(void) { return 103; }
 
 dig_status dig_lookback_status(hipStream_t stream) {
   unsigned* word = dig::lookback_status_word();
@@ -415,8 +415,14 @@ dig_status dig_dwconv3x3_bwd(int32_t batch, int32_t grid_h, int32_t grid_w, int3
 
 size_t dig_dwconv3x3_bwd_noalloc_max_bytes(void) { return dig::kNoAllocScratchBytes; }
 
-dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
-                      const dig_linear_out* outs, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dig_linear's checks and launch; a workspace (the block's) lets one-output products split K.
+dig_status linear_impl(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                       const dig_linear_out* outs, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   if (dtype != DIG_BF16) return fail(DIG_ERR_UNSUPPORTED, "dig_linear runs on bf16 operands");
   if (m < 0 || k < 1) return fail(DIG_ERR_SHAPE, "m must be >= 0 and k >= 1");
   if (n_out < 1 || n_out > DIG_LINEAR_MAX_OUT)
@@ -476,7 +482,45 @@ dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_
     lo[i] = dig::LinearOut{o.c, o.w, o.bias, o.n, o.act, o.res, o.res ? o.gate : nullptr,
                            (long)o.gate_ld, o.res ? (int)std::min<int64_t>(o.rows_per_gate, m) : 1};
   }
-  return check_dev(dig::launch_linear(m, k, a, n_out, lo, stream), "dig_linear launch");
+  return check_dev(dig::launch_linear(m, k, a, n_out, lo, stream, ws, ws_bytes),
+                   "dig_linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                      const dig_linear_out* outs, hipStream_t stream) {
+  return linear_impl(m, k, dtype, a, n_out, outs, nullptr, 0, stream);
+}
+
+size_t dig_linear_workspace_bytes(int32_t m, int32_t k, int32_t n_out, const dig_linear_out* outs) {
+  if (m < 1 || k < 1 || n_out != 1 || !outs || outs[0].n < 1) return 0;
+  return dig::linear_splitk_bytes(m, k, outs[0].n);
+}
+
+dig_status dig_linear_ws(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                         const dig_linear_out* outs, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const size_t need = dig_linear_workspace_bytes(m, k, n_out, outs);
+  if (need == 0) return linear_impl(m, k, dtype, a, n_out, outs, nullptr, 0, stream);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DIG_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (outs && a) {  // the workspace may not overlap any argument
+    const dig_linear_out& o = outs[0];
+    const size_t cb = (size_t)m * o.n * 2;
+    const Range in[] = {rng("a", a, (size_t)m * k * 2), rng("w", o.w, (size_t)o.n * k * 2),
+                        rng("bias", o.bias, o.bias ? (size_t)o.n * 4 : 0),
+                        rng("c", o.c, cb), rng("res", o.res, o.res ? cb : 0),
+                        rng("gate", o.gate, o.gate ? 16 : 0)};
+    const Range out[] = {rng("workspace", workspace, need)};
+    dig_status st = check_alias(in, 6, out, 1);
+    if (st != DIG_OK) return st;
+  }
+  return linear_impl(m, k, dtype, a, n_out, outs, workspace, workspace_bytes, stream);
 }
 
 dig_status dig_rmsnorm_modulate(int64_t rows, int32_t dim, int64_t rows_per_group, float eps,
@@ -541,7 +585,7 @@ namespace {
 
 // Carving of dig_block_fwd's workspace (bf16 intermediates, then the GLA call's workspace).
 struct BlockWs {
-  size_t h, q, k, v, u, r, z, y, x1, hid, gla, total;
+  size_t h, q, k, v, u, r, z, y, x1, hid, split, split_bytes, gla, total;
 };
 
 dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
@@ -586,6 +630,14 @@ dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
   w->y = take(HV);
   w->x1 = take(d->dim);
   w->hid = take(d->ffn_dim);
+  // fp32 partial sums of the one-output products whose grid would not fill the GPU
+  const int m = (int)M;
+  size_t sb = dig::linear_splitk_bytes(m, (int)HV, d->dim);
+  sb = std::max(sb, dig::linear_splitk_bytes(m, d->dim, d->ffn_dim));
+  sb = std::max(sb, dig::linear_splitk_bytes(m, d->ffn_dim, d->dim));
+  w->split = off;
+  w->split_bytes = sb;
+  off += a256(sb);
   w->gla = off;
   off += a256(dig_gla_fwd_workspace_bytes(g));
   w->total = off;
@@ -690,7 +742,7 @@ dig_status dig_block_fwd(const dig_block_desc* d, const dig_block_weights* wt, c
   {
     const dig_linear_out o{x1, wt->w_out, wt->b_out, D, DIG_ACT_NONE, x, mcol(2), mod_ld,
                            (int64_t)L};
-    st = dig_linear(m, HV, DIG_BF16, y, 1, &o, stream);
+    st = linear_impl(m, HV, DIG_BF16, y, 1, &o, ws + w.split, w.split_bytes, stream);
     if (st != DIG_OK) return st;
   }
   // 6. h = RMSNorm(x1) * gamma_2 + beta_2
@@ -700,14 +752,14 @@ dig_status dig_block_fwd(const dig_block_desc* d, const dig_block_weights* wt, c
   // 7. hid = GELU(h W_ffn1^T + b_ffn1)
   {
     const dig_linear_out o{hid, wt->w_ffn1, wt->b_ffn1, F, DIG_ACT_GELU, nullptr, nullptr, 0, 1};
-    st = dig_linear(m, D, DIG_BF16, h, 1, &o, stream);
+    st = linear_impl(m, D, DIG_BF16, h, 1, &o, ws + w.split, w.split_bytes, stream);
     if (st != DIG_OK) return st;
   }
   // 8. x1 += alpha_2 * (hid W_ffn2^T + b_ffn2)   (in place)
   {
     const dig_linear_out o{x1, wt->w_ffn2, wt->b_ffn2, D, DIG_ACT_NONE, x1, mcol(5), mod_ld,
                            (int64_t)L};
-    st = dig_linear(m, F, DIG_BF16, hid, 1, &o, stream);
+    st = linear_impl(m, F, DIG_BF16, hid, 1, &o, ws + w.split, w.split_bytes, stream);
     if (st != DIG_OK) return st;
   }
   // 9. SREM: 3x3 depthwise conv on the current-order grid, written in the next scan order

@@ -411,11 +411,12 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
 
 // N consecutive elements c0..c0+N-1 of an LDS row with `cols` elements (row pitch
 // pitch_elems, default cols); columns past the row end, and every column of an invalid row,
-// read as zero.  Whole 16- or 8-byte vectors when the row pitch and the range allow it.
+// read as zero.  Whole 16-, 8- or 4-byte vectors when the row pitch and the range allow it
+// (c0 is a multiple of N: the vectors are aligned whenever the pitch is).
 template <typename T, int N>
 __device__ __forceinline__ void lds_row_read(T (&out)[N], const T* row, int c0, int cols,
                                              bool valid, int pitch_elems = -1) {
-  constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T);
+  constexpr int V16 = 16 / (int)sizeof(T), V8 = 8 / (int)sizeof(T), V4 = 4 / (int)sizeof(T);
   const int pitch = (pitch_elems < 0 ? cols : pitch_elems) * (int)sizeof(T);
   if (N % V16 == 0 && (pitch & 15) == 0 && c0 + N <= cols) {
 #pragma unroll
@@ -432,6 +433,17 @@ __device__ __forceinline__ void lds_row_read(T (&out)[N], const T* row, int c0, 
       const T* e = reinterpret_cast<const T*>(&u);
 #pragma unroll
       for (int i = 0; i < V8; ++i) out[j + i] = e[i];
+    }
+  } else if (c0 >= cols) {  // wholly past the row end
+#pragma unroll
+    for (int j = 0; j < N; ++j) out[j] = from_f<T>(0.f);
+  } else if (N % V4 == 0 && (pitch & 3) == 0 && c0 + N <= cols) {
+#pragma unroll
+    for (int j = 0; j < N; j += V4) {
+      const unsigned u = *reinterpret_cast<const unsigned*>(row + c0 + j);
+      const T* e = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int i = 0; i < V4; ++i) out[j + i] = e[i];
     }
   } else {
 #pragma unroll

@@ -143,9 +143,13 @@ struct LinearOut {
   long gate_ld;
   int rows_per_gate;
 };
-// C_o = epilogue_o(A W_o^T + bias_o) for every output o, A [M][K] bf16, one launch.
+// C_o = epilogue_o(A W_o^T + bias_o) for every output o, A [M][K] bf16, one launch.  With a
+// workspace of at least linear_splitk_bytes() (one output only), products whose grid of
+// 128 x 128 tiles would not fill the GPU split K into fp32 partial sums there and finish in a
+// second, reducing launch.
 hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
-                         hipStream_t st);
+                         hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0);
+size_t linear_splitk_bytes(int M, int K, int n);
 
 // ------------------------------------------------------------------ DiG block
 // h[r] = x[r] * rsqrt(mean(x[r]^2) + eps) * scale[r / rows_per_group] + shift[...], bf16 rows

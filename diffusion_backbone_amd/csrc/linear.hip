@@ -85,9 +85,12 @@ __device__ __forceinline__ void store_block(const BlockRegs<BM, BK>& r, bf16* ld
 }
 
 // EPI: which epilogues this instantiation can apply (bit 0: GELU, bit 1: gated residual); the
-// choice per output is uniform over a workgroup.
+// choice per output is uniform over a workgroup.  EPI == kPartial: split K -- workgroup z of
+// the grid's third dimension multiplies K blocks [z kbs, (z + 1) kbs) and stores its fp32 sums
+// to part[z][M][n] (one output), for linear_splitk_reduce to finish.
+constexpr int kPartial = 4;
 template <int BM, int BK, int EPI>
-__global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
+__global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, float* part, int kbs) {
   constexpr int BN = Tile<BM>::BN, NTHR = Tile<BM>::NTHR, CPITCH = Tile<BM>::CPITCH;
   constexpr int WPR = BM / 64;    // waves per tile row
   constexpr int LPITCH = BK + 8;  // elements (16-byte aligned rows, conflict-free reads)
@@ -109,7 +112,9 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
   const LinOut out = p.out[o];
   const int m0 = blockIdx.y * BM, n0 = (nt - out.tile0) * BN;
   const int K = p.K;
-  const int nkb = (K + BK - 1) / BK;
+  const int nkb_all = (K + BK - 1) / BK;
+  const int kb0 = EPI == kPartial ? (int)blockIdx.z * kbs : 0;
+  const int nkb = EPI == kPartial ? min(kbs, nkb_all - kb0) : nkb_all;  // >= 1 by the launch
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -121,8 +126,8 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
 
   BlockRegs<BM, BK> ra, rb;  // the next K block of the A tile and of the W tile
   auto load = [&](int kb) {
-    load_block(ra, p.a, p.M, K, m0, kb * BK, tid);
-    load_block(rb, out.w, out.n, K, n0, kb * BK, tid);
+    load_block(ra, p.a, p.M, K, m0, (kb0 + kb) * BK, tid);
+    load_block(rb, out.w, out.n, K, n0, (kb0 + kb) * BK, tid);
   };
   auto put = [&](int buf) {
     store_block(ra, sA(buf), tid);
@@ -155,6 +160,22 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
       put(buf ^ 1);  // the other buffer was last read before the previous barrier
       __syncthreads();
     }
+  }
+  if constexpr (EPI == kPartial) {  // fp32 sums straight from the accumulators (32 lanes store
+                                    // 128 consecutive bytes of one row)
+    float* dst = part + (long)blockIdx.z * p.M * out.n;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + 32 * j + r32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h32 + (v & 3);
+          if (row < p.M && col < out.n) dst[(long)row * out.n + col] = acc[i][j][v];
+        }
+      }
+    return;
   }
   __syncthreads();  // every wave is done with the operand tiles: reuse them for the output
 
@@ -204,6 +225,39 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p) {
   }
 }
 
+// Finishes a split-K product: sums the S fp32 partial tiles in a fixed order, adds the bias,
+// applies the output's epilogue and stores bf16, eight elements per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void linear_splitk_reduce(LinOut out, const float* part, int M,
+                                                            int S) {
+  const long npc = (long)M * out.n / 8;
+  for (long q = (long)blockIdx.x * 256 + threadIdx.x; q < npc; q += (long)gridDim.x * 256) {
+    const long e0 = q * 8;
+    const int gr = (int)(e0 / out.n), gc = (int)(e0 - (long)gr * out.n);
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = out.bias ? out.bias[gc + e] : 0.f;
+    for (int z = 0; z < S; ++z) {
+      const float4* src = reinterpret_cast<const float4*>(part + (long)z * M * out.n + e0);
+      const float4 a = src[0], b = src[1];
+      t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
+      t[4] += b.x; t[5] += b.y; t[6] += b.z; t[7] += b.w;
+    }
+    bf16x8 val;
+    const bool gelu = (EPI & 1) && out.act == kActGelu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] = from_f<bf16>(gelu ? gelu_exact(t[e]) : t[e]);
+    if ((EPI & 2) && out.res) {
+      const bf16x8 rv = *reinterpret_cast<const bf16x8*>(out.res + e0);
+      const bf16x8 gv = *reinterpret_cast<const bf16x8*>(
+          out.gate + (long)(gr / out.rows_per_gate) * out.gate_ld + gc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] = from_f<bf16>(fmaf(to_f(gv[e]), to_f(val[e]), to_f(rv[e])));
+    }
+    *reinterpret_cast<bf16x8*>(out.c + e0) = val;
+  }
+}
+
 // Launch with BM x BM tiles (tile0 of each output counted in BM-wide column tiles).
 template <int BM>
 static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const LinearOut* outs,
@@ -233,10 +287,61 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
   for (int i = 0; i < nout; ++i) epi |= (outs[i].act == kActGelu ? 1 : 0) | (outs[i].res ? 2 : 0);
   const dim3 grid((unsigned)tiles, (unsigned)mt), block(Tile<BM>::NTHR);
   switch (epi) {
-    case 0: hipLaunchKernelGGL((linear_kernel<BM, 32, 0>), grid, block, 0, st, p); break;
-    case 1: hipLaunchKernelGGL((linear_kernel<BM, 32, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((linear_kernel<BM, 32, 2>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((linear_kernel<BM, 32, 3>), grid, block, 0, st, p); break;
+    case 0: hipLaunchKernelGGL((linear_kernel<BM, 32, 0>), grid, block, 0, st, p, nullptr, 0); break;
+    case 1: hipLaunchKernelGGL((linear_kernel<BM, 32, 1>), grid, block, 0, st, p, nullptr, 0); break;
+    case 2: hipLaunchKernelGGL((linear_kernel<BM, 32, 2>), grid, block, 0, st, p, nullptr, 0); break;
+    default: hipLaunchKernelGGL((linear_kernel<BM, 32, 3>), grid, block, 0, st, p, nullptr, 0); break;
+  }
+  return hipGetLastError();
+}
+
+// Split-K plan of a one-output product on 128 x 128 tiles: the number of K splits that brings
+// the grid to about 384 workgroups (1.5 rounds of the 256 compute units at three per unit),
+// with at least four K blocks of 32 per split; 1 = no split.
+static int splitk_count(int M, int K, int n) {
+  const long tiles = ((long)M + 127) / 128 * ((n + 127) / 128);
+  if (tiles >= 192) return 1;
+  int s = (int)((384 + tiles - 1) / tiles);
+  const int kbmax = ((K + 31) / 32) / 4;
+  if (s > kbmax) s = kbmax;
+  if (s > 8) s = 8;
+  return s < 2 ? 1 : s;
+}
+
+static hipError_t launch_linear_splitk(int M, int K, const void* a, const LinearOut& o, int S,
+                                       float* part, hipStream_t st) {
+  LinParams p{};
+  p.a = static_cast<const bf16*>(a);
+  p.M = M;
+  p.K = K;
+  p.nout = 1;
+  LinOut& lo = p.out[0];
+  lo.c = static_cast<bf16*>(o.c);
+  lo.w = static_cast<const bf16*>(o.w);
+  lo.bias = o.bias;
+  lo.res = static_cast<const bf16*>(o.res);
+  lo.gate = static_cast<const bf16*>(o.gate);
+  lo.gate_ld = o.gate_ld;
+  lo.rows_per_gate = o.rows_per_gate;
+  lo.act = o.act;
+  lo.n = o.n;
+  lo.tile0 = 0;
+  const int nkb = (K + 31) / 32, kbs = (nkb + S - 1) / S;
+  S = (nkb + kbs - 1) / kbs;  // every split holds at least one K block
+  const dim3 grid((unsigned)((o.n + 127) / 128), (unsigned)((M + 127) / 128), (unsigned)S);
+  hipLaunchKernelGGL((linear_kernel<128, 32, kPartial>), grid, dim3(Tile<128>::NTHR), 0, st, p,
+                     part, kbs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long npc = (long)M * o.n / 8;
+  long g = (npc + 255) / 256;
+  if (g > 2048) g = 2048;
+  const int epi = (o.act == kActGelu ? 1 : 0) | (o.res ? 2 : 0);
+  switch (epi) {
+    case 0: hipLaunchKernelGGL(linear_splitk_reduce<0>, dim3((unsigned)g), dim3(256), 0, st, lo, part, M, S); break;
+    case 1: hipLaunchKernelGGL(linear_splitk_reduce<1>, dim3((unsigned)g), dim3(256), 0, st, lo, part, M, S); break;
+    case 2: hipLaunchKernelGGL(linear_splitk_reduce<2>, dim3((unsigned)g), dim3(256), 0, st, lo, part, M, S); break;
+    default: hipLaunchKernelGGL(linear_splitk_reduce<3>, dim3((unsigned)g), dim3(256), 0, st, lo, part, M, S); break;
   }
   return hipGetLastError();
 }
@@ -246,9 +351,19 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
 // 256 x 256 tiles (sixteen waves, one workgroup per compute unit, twice the flops per byte
 // loaded) when they give at least four rounds of workgroups over the 256 compute units; else
 // 128 x 128 tiles (four waves, three workgroups per unit), which fill smaller problems.
+size_t linear_splitk_bytes(int M, int K, int n) {
+  const int s = splitk_count(M, K, n);
+  return s > 1 ? (size_t)s * M * n * sizeof(float) : 0;
+}
+
 hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut* outs,
-                         hipStream_t st) {
+                         hipStream_t st, void* ws, size_t ws_bytes) {
   if (nout < 1 || nout > kLinearMaxOut) return hipErrorInvalidValue;
+  if (nout == 1 && ws) {  // small grids: split K into partial sums in the workspace
+    const int s = splitk_count(M, K, outs[0].n);
+    if (s > 1 && ws_bytes >= (size_t)s * M * outs[0].n * sizeof(float))
+      return launch_linear_splitk(M, K, a, outs[0], s, static_cast<float*>(ws), st);
+  }
   long t256 = 0;
   for (int i = 0; i < nout; ++i) t256 += (outs[i].n + 255) / 256;
   t256 *= ((long)M + 255) / 256;

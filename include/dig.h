@@ -183,6 +183,19 @@ typedef struct {
 dig_status dig_linear(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
                       const dig_linear_out* outs, hipStream_t stream);
 
+/*
+ * dig_linear_ws -- dig_linear with a workspace: a one-output product whose grid of 128 x 128
+ * tiles would not fill the GPU splits K into fp32 partial sums in the workspace (up to eight
+ * splits) and finishes them, with the same epilogue, in a second launch.  Same results up to
+ * the order of the fp32 sums.  dig_linear_workspace_bytes() gives the bytes it uses (0: no
+ * split for this shape; the call then runs exactly as dig_linear).  The workspace may not
+ * overlap any argument.
+ */
+size_t dig_linear_workspace_bytes(int32_t m, int32_t k, int32_t n_out, const dig_linear_out* outs);
+dig_status dig_linear_ws(int32_t m, int32_t k, int32_t dtype, const void* a, int32_t n_out,
+                         const dig_linear_out* outs, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* ---------------------------------------------------------------------- DiG block */
 
 /*

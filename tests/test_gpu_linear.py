@@ -62,3 +62,52 @@ def test_linear_rejects_bad_shapes():
     with pytest.raises(dig.DigError) as ei:     # output overlapping the input
         dig.dig_linear(1, 8, t, [(t, torch.zeros(8, 8, dtype=torch.bfloat16, device="cuda"), None)])
     assert ei.value.status == dig.DIG_ERR_ALIAS
+
+
+@pytest.mark.parametrize("m,k,n,act,gated", [
+    (2048, 1536, 384, 0, True),       # DiG-S/2 256 px second feedforward matrix: 48 tiles
+    (512, 384, 384, 0, True),         # out-projection, small batch
+    (1024, 384, 1536, 1, False),      # first feedforward matrix with GELU, 96 tiles
+    (300, 1000, 136, 0, False),       # ragged rows and K
+])
+def test_linear_split_k_parity(m, k, n, act, gated):
+    """dig_linear_ws: K split into fp32 partial sums in the workspace, finished with the same
+    epilogue; against the oracle, and the workspace query is non-zero for these grids."""
+    import torch
+    import diffusion_backbone_amd as dig
+    announce("linear split-K m=%d k=%d n=%d act=%d gated=%d" % (m, k, n, act, gated))
+    rng = np.random.default_rng(m + k + n)
+    a = W.quantize(rng.standard_normal((m, k)), "bf16")
+    w = W.quantize(rng.standard_normal((n, k)) / np.sqrt(k), "bf16")
+    b = W.f32_round(rng.standard_normal(n) * 0.5)
+    res = W.quantize(rng.standard_normal((m, n)), "bf16")
+    gate = W.quantize(rng.standard_normal((2, n)), "bf16")
+    rpg = (m + 1) // 2
+    c = to_dev(res, "bf16") if gated else empty((m, n), "bf16")
+    o = dig.linear_out(c, to_dev(w, "bf16"),
+                       torch.from_numpy(b.astype(np.float32)).cuda(), act=act,
+                       res=c if gated else None, gate=to_dev(gate, "bf16") if gated else None,
+                       gate_ld=n, rows_per_gate=rpg)
+    need = dig.dig_linear_workspace_bytes(m, k, [o])
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dig.dig_linear_ws(m, k, to_dev(a, "bf16"), [o], ws)
+    torch.cuda.synchronize()
+    t = oracle.linear(a, w, b)
+    if act:
+        t = oracle.gelu(t)
+    ref = res + gate[np.arange(m) // rpg] * t if gated else t
+    e = maxrel(to_f64(c), ref)
+    print("  err %.2e (workspace %d bytes)" % (e, need), flush=True)
+    assert e <= TOL["bf16"]
+    with pytest.raises(dig.DigError) as ei:
+        dig.dig_linear_ws(m, k, to_dev(a, "bf16"), [o], ws, workspace_bytes=need - 16)
+    assert ei.value.status == dig.DIG_ERR_WORKSPACE
+
+
+def test_linear_split_k_not_needed_on_full_grids():
+    import torch
+    import diffusion_backbone_amd as dig
+    c = torch.empty(16384, 1152, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(1152, 1152, dtype=torch.bfloat16, device="cuda")
+    assert dig.dig_linear_workspace_bytes(16384, 1152, [(c, w, None)]) == 0
