@@ -186,6 +186,25 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ps) / max(len(ps), 1)
 
 
+def timed_graph(fn, steps, reps=10):
+    """ms per call of fn with the host out of the way: `reps` calls captured once in a HIP
+    graph, the graph replayed `steps` times (one warm-up replay)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    ms = timed(graph.replay, steps, 1) / reps
+    del graph
+    return ms
+
+
 def timed(fn, steps, warmup):
     """ms per call of fn over exactly `steps` calls after `warmup` untimed ones, with a device
     synchronisation on both sides of the timed region."""
@@ -443,7 +462,8 @@ def block_stack(name, steps, warmup=2):
     directions, on random-init weights of the model's shapes (projections ~ N(0, 1/fan_in),
     DWConv identity + noise, adaLN gamma ~ 1, alpha ~ 0.5) and x ~ N(0, 1).  Reported: images/s
     and tokens/s of the whole forward, the dense-matmul share against the bf16 peak, and one
-    block's steps timed one by one through the public calls the block composes."""
+    block's steps timed one by one through the public calls the block composes (each replayed
+    from a captured graph, so the host's launch cost does not hide the small kernels)."""
     import torch
     import diffusion_backbone_amd as dig
     if name in W.STACKS:
@@ -561,7 +581,7 @@ def block_stack(name, steps, warmup=2):
     steps_ = tuple((n, split.get(n, fn), fl) for n, fn, fl in steps_)
     parts = {}
     for pname, fn, flops in steps_:
-        pm = timed(fn, max(5, steps), 2)
+        pm = timed_graph(fn, max(5, steps))
         e = {"us": round(pm * 1e3, 1)}
         if flops:
             tf = flops / (pm / 1e3) / 1e12

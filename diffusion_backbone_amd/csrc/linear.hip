@@ -297,12 +297,13 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
 
 // Split-K plan of a one-output product on 128 x 128 tiles: the number of K splits that brings
 // the grid to about 384 workgroups (1.5 rounds of the 256 compute units at three per unit),
-// with at least four K blocks of 32 per split; 1 = no split.
+// with at least eight K blocks of 32 per split (shorter splits lose more to the second launch
+// and the partial sums' traffic than they gain); 1 = no split.
 static int splitk_count(int M, int K, int n) {
   const long tiles = ((long)M + 127) / 128 * ((n + 127) / 128);
   if (tiles >= 192) return 1;
   int s = (int)((384 + tiles - 1) / tiles);
-  const int kbmax = ((K + 31) / 32) / 4;
+  const int kbmax = ((K + 31) / 32) / 8;
   if (s > kbmax) s = kbmax;
   if (s > 8) s = 8;
   return s < 2 ? 1 : s;

@@ -66,8 +66,8 @@ def test_linear_rejects_bad_shapes():
 
 @pytest.mark.parametrize("m,k,n,act,gated", [
     (2048, 1536, 384, 0, True),       # DiG-S/2 256 px second feedforward matrix: 48 tiles
-    (512, 384, 384, 0, True),         # out-projection, small batch
-    (1024, 384, 1536, 1, False),      # first feedforward matrix with GELU, 96 tiles
+    (512, 1152, 384, 0, True),        # an XL/2-width out-projection on a small batch
+    (1024, 1152, 1536, 1, False),     # a feedforward matrix with GELU, 96 tiles
     (300, 1000, 136, 0, False),       # ragged rows and K
 ])
 def test_linear_split_k_parity(m, k, n, act, gated):
