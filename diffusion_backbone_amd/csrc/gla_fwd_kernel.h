@@ -676,6 +676,12 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       // y, and for the backward (when saved) o rstd in fragment order and rstd per row
       Quad<float>* ob = p.obar ? static_cast<Quad<float>*>(p.obar) + ((sbase + n) * NT + I) * NDV * 64 + lane
                            : nullptr;
+      // exact widths whose rows are whole 16-byte pieces: y goes through this wave's own 16
+      // rows of the staged r (already read), then out as 16-byte row pieces
+      constexpr bool VST = EXACT && (DV * (int)sizeof(T)) % 16 == 0 &&
+                           (VPE * (int)sizeof(T)) % 16 == 0;
+      const bool vst = VST && !gop;
+      T* sY = const_cast<T*>(sR) + 16 * I * VPE;
 #pragma unroll
       for (int E = 0; E < NDV; ++E) {
         const int e = E * 16 + r16;
@@ -686,14 +692,35 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
           const float o = oacc[E][i];
           const float nv = o * rstd[i];
           q4.v[i] = nv;
-          if ((FULLV || e < dv) && row < valid) {
+          if (FULLV || e < dv) {
             const float rv = to_f(rr[E][i]);
-            const long off = (row0 + (long)row * H) * dv + e;
-            if (gop) gop[off] = from_f<T>(o);
-            gy[off] = from_f<T>(nv * gm[E] * rv * Fm<T>::sig(rv));
+            const T yv = from_f<T>(nv * gm[E] * rv * Fm<T>::sig(rv));
+            if (vst) {
+              sY[(4 * g4 + i) * VPE + e] = yv;
+            } else if (row < valid) {
+              const long off = (row0 + (long)row * H) * dv + e;
+              if (gop) gop[off] = from_f<T>(o);
+              gy[off] = yv;
+            }
           }
         }
         if (ob) ob[E * 64] = q4;
+      }
+      if (vst) {
+        // the wave's LDS writes above land before its reads below (in-order LDS per wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int PPR = DV * (int)sizeof(T) / 16, NPC = 16 * PPR;  // pieces per row, tile
+#pragma unroll
+        for (int u = 0; u < (NPC + 63) / 64; ++u) {
+          const int q = lane + 64 * u, rw = q / PPR, pc = q - rw * PPR;
+          if (q < NPC && 16 * I + rw < valid) {
+            const uint4 v4 = *reinterpret_cast<const uint4*>(sY + rw * VPE + pc * (16 / (int)sizeof(T)));
+            *reinterpret_cast<uint4*>(gy + (row0 + (long)(16 * I + rw) * H) * dv +
+                                      pc * (16 / (int)sizeof(T))) = v4;
+          }
+        }
       }
       if (ob && r16 == 0)
         *reinterpret_cast<float4*>(p.rstd + (sbase + n) * C + 16 * I + 4 * g4) =
