@@ -10,12 +10,14 @@
 // One launch covers every output: the grid runs over (row tile, column tile of the
 // concatenated outputs), and a tile never straddles two outputs.  Each wave owns 64 x 64
 // outputs as 2 x 2 MFMA tiles of 32 x 32 (K step 16: on gfx950 the 32x32x16 bf16 instruction
-// sustains about 1.7 times the rate of 16x16x32); K blocks of 32 staged in LDS (A rows and W
-// rows, both K-contiguous, 80-byte pitch: conflict-free 16-byte reads) with the next block
-// loaded into registers while the current one is multiplied (two LDS buffers).  Tiles of
-// 128 x 128 (four waves, three workgroups per compute unit) or 256 x 256 (sixteen waves, one
-// per unit).  fp32 accumulation; bias and GELU in fp32; bf16 output stored from LDS in 16-byte
-// row pieces, where the gated residual is applied.
+// sustains about 1.7 times the rate of 16x16x32); K blocks of 32 or 64 staged in LDS (A rows
+// and W rows, both K-contiguous, pitch 16 bytes past a multiple of 64: conflict-free 16-byte
+// reads) with the next block loaded into registers while the current one is multiplied (two
+// LDS buffers).  Tiles of 128 x 128 (four waves, two or three workgroups per compute unit) or
+// 256 x 256 (sixteen waves, one per unit).  fp32 accumulation; bias and GELU in fp32; bf16
+// output stored from LDS in 16-byte row pieces, where the gated residual is applied.  Products
+// whose grid would not fill the GPU can split K over a workspace (fp32 partial sums, then a
+// reducing launch with the epilogue).
 #include "dig_device.h"
 #include "dig_internal.h"
 
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(256) void linear_splitk_reduce(LinOut out, const fl
 }
 
 // Launch with BM x BM tiles (tile0 of each output counted in BM-wide column tiles).
-template <int BM>
+template <int BM, int BK = 32>
 static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const LinearOut* outs,
                                    hipStream_t st) {
   LinParams p{};
@@ -287,10 +289,10 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
   for (int i = 0; i < nout; ++i) epi |= (outs[i].act == kActGelu ? 1 : 0) | (outs[i].res ? 2 : 0);
   const dim3 grid((unsigned)tiles, (unsigned)mt), block(Tile<BM>::NTHR);
   switch (epi) {
-    case 0: hipLaunchKernelGGL((linear_kernel<BM, 32, 0>), grid, block, 0, st, p, nullptr, 0); break;
-    case 1: hipLaunchKernelGGL((linear_kernel<BM, 32, 1>), grid, block, 0, st, p, nullptr, 0); break;
-    case 2: hipLaunchKernelGGL((linear_kernel<BM, 32, 2>), grid, block, 0, st, p, nullptr, 0); break;
-    default: hipLaunchKernelGGL((linear_kernel<BM, 32, 3>), grid, block, 0, st, p, nullptr, 0); break;
+    case 0: hipLaunchKernelGGL((linear_kernel<BM, BK, 0>), grid, block, 0, st, p, nullptr, 0); break;
+    case 1: hipLaunchKernelGGL((linear_kernel<BM, BK, 1>), grid, block, 0, st, p, nullptr, 0); break;
+    case 2: hipLaunchKernelGGL((linear_kernel<BM, BK, 2>), grid, block, 0, st, p, nullptr, 0); break;
+    default: hipLaunchKernelGGL((linear_kernel<BM, BK, 3>), grid, block, 0, st, p, nullptr, 0); break;
   }
   return hipGetLastError();
 }
@@ -368,8 +370,17 @@ hipError_t launch_linear(int M, int K, const void* a, int nout, const LinearOut*
   long t256 = 0;
   for (int i = 0; i < nout; ++i) t256 += (outs[i].n + 255) / 256;
   t256 *= ((long)M + 255) / 256;
-  if (t256 >= 4 * 256) return launch_linear_bm<256>(M, K, a, nout, outs, st);
-  return launch_linear_bm<128>(M, K, a, nout, outs, st);
+  // K stages of 64 (half the barriers and load round trips per flop) pay off once K is long
+  // and the grid holds at least three rounds of 128 x 128 tiles; smaller problems keep 32
+  long t128 = 0;
+  for (int i = 0; i < nout; ++i) t128 += (outs[i].n + 127) / 128;
+  t128 *= ((long)M + 127) / 128;
+  const bool k64 = K >= 1024 && t128 >= 3 * 256;
+  if (t256 >= 4 * 256)
+    return k64 ? launch_linear_bm<256, 64>(M, K, a, nout, outs, st)
+               : launch_linear_bm<256>(M, K, a, nout, outs, st);
+  return k64 ? launch_linear_bm<128, 64>(M, K, a, nout, outs, st)
+             : launch_linear_bm<128>(M, K, a, nout, outs, st);
 }
 
 }  // namespace dig
