@@ -45,6 +45,7 @@ __device__ __forceinline__ float gelu_exact(float x) {
 struct LinParams {
   const bf16* a;
   int M, K, nout;
+  int ntot;  // packed launches: the outputs' columns side by side (tile0 = first column)
   LinOut out[kLinearMaxOut];
 };
 
@@ -76,6 +77,23 @@ __device__ __forceinline__ void load_block(BlockRegs<BM, BK>& r, const bf16* src
     r.v[u] = in ? x : make_uint4(0, 0, 0, 0);
   }
 }
+// The same for W rows gathered from several outputs: piece u of this thread reads the row at
+// wrow[u] (nullptr: a row past the last output, read as zero; the load then goes to `safe`,
+// any readable 16 bytes, so that no load sits under a branch).
+template <int BM, int BK>
+__device__ __forceinline__ void load_rows(BlockRegs<BM, BK>& r,
+                                          const bf16* const (&wrow)[BlockRegs<BM, BK>::NP],
+                                          const bf16* safe, int K, int k0, int tid) {
+  constexpr int PPR = BlockRegs<BM, BK>::PPR, NTHR = Tile<BM>::NTHR;
+#pragma unroll
+  for (int u = 0; u < BlockRegs<BM, BK>::NP; ++u) {
+    const int q = tid + NTHR * u, piece = q % PPR;
+    const int gk = k0 + piece * 8;
+    const bool in = wrow[u] != nullptr && gk < K;
+    const uint4 x = *reinterpret_cast<const uint4*>(in ? wrow[u] + gk : safe);
+    r.v[u] = in ? x : make_uint4(0, 0, 0, 0);
+  }
+}
 template <int BM, int BK>
 __device__ __forceinline__ void store_block(const BlockRegs<BM, BK>& r, bf16* lds, int tid) {
   constexpr int PPR = BlockRegs<BM, BK>::PPR, LPITCH = BK + 8, NTHR = Tile<BM>::NTHR;
@@ -89,8 +107,11 @@ __device__ __forceinline__ void store_block(const BlockRegs<BM, BK>& r, bf16* ld
 // EPI: which epilogues this instantiation can apply (bit 0: GELU, bit 1: gated residual); the
 // choice per output is uniform over a workgroup.  EPI == kPartial: split K -- workgroup z of
 // the grid's third dimension multiplies K blocks [z kbs, (z + 1) kbs) and stores its fp32 sums
-// to part[z][M][n] (one output), for linear_splitk_reduce to finish.
-constexpr int kPartial = 4;
+// to part[z][M][n] (one output), for linear_splitk_reduce to finish.  EPI & kPacked: the
+// outputs' columns side by side (p.ntot of them, output o from column p.out[o].tile0), column
+// tiles straddling outputs: W rows are gathered per row, bias and stores per column (outputs
+// sharing one activation, no residual).
+constexpr int kPartial = 4, kPacked = 8;
 template <int BM, int BK, int EPI>
 __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, float* part, int kbs) {
   constexpr int BN = Tile<BM>::BN, NTHR = Tile<BM>::NTHR, CPITCH = Tile<BM>::CPITCH;
@@ -105,14 +126,25 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, flo
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave / WPR, wn = wave % WPR;  // waves of 64 x 64
-  // which output this column tile belongs to (uniform)
+  constexpr bool PK = (EPI & kPacked) != 0;
+  // which output this column tile belongs to (uniform; packed: output 0 for K and the shared
+  // activation, the columns mapped one by one below)
   const int nt = blockIdx.x;
   int o = 0;
+  if constexpr (!PK) {
 #pragma unroll
-  for (int i = 1; i < kLinearMaxOut; ++i)
-    if (i < p.nout && nt >= p.out[i].tile0) o = i;
+    for (int i = 1; i < kLinearMaxOut; ++i)
+      if (i < p.nout && nt >= p.out[i].tile0) o = i;
+  }
   const LinOut out = p.out[o];
-  const int m0 = blockIdx.y * BM, n0 = (nt - out.tile0) * BN;
+  const int m0 = blockIdx.y * BM, n0 = PK ? nt * BN : (nt - out.tile0) * BN;
+  auto owner = [&](int col) {  // packed: the output holding global column col
+    int oo = 0;
+#pragma unroll
+    for (int i = 1; i < kLinearMaxOut; ++i)
+      if (i < p.nout && col >= p.out[i].tile0) oo = i;
+    return oo;
+  };
   const int K = p.K;
   const int nkb_all = (K + BK - 1) / BK;
   const int kb0 = EPI == kPartial ? (int)blockIdx.z * kbs : 0;
@@ -127,9 +159,20 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, flo
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   BlockRegs<BM, BK> ra, rb;  // the next K block of the A tile and of the W tile
+  // packed: this thread's W rows (fixed over K)
+  const bf16* wrow[BlockRegs<BM, BK>::NP];
+  if constexpr (PK) {
+#pragma unroll
+    for (int u = 0; u < BlockRegs<BM, BK>::NP; ++u) {
+      const int gcol = n0 + (tid + NTHR * u) / BlockRegs<BM, BK>::PPR;
+      const int oo = owner(gcol);
+      wrow[u] = gcol < p.ntot ? p.out[oo].w + (long)(gcol - p.out[oo].tile0) * K : nullptr;
+    }
+  }
   auto load = [&](int kb) {
     load_block(ra, p.a, p.M, K, m0, (kb0 + kb) * BK, tid);
-    load_block(rb, out.w, out.n, K, n0, (kb0 + kb) * BK, tid);
+    if constexpr (PK) load_rows(rb, wrow, p.out[0].w, K, (kb0 + kb) * BK, tid);
+    else load_block(rb, out.w, out.n, K, n0, (kb0 + kb) * BK, tid);
   };
   auto put = [&](int buf) {
     store_block(ra, sA(buf), tid);
@@ -191,7 +234,14 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, flo
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = wn * 64 + 32 * j + r32;
-        const float bias = (out.bias && n0 + col < out.n) ? out.bias[n0 + col] : 0.f;
+        float bias;
+        if constexpr (PK) {
+          const int gcol = n0 + col, oo = owner(gcol);
+          const float* bp = p.out[oo].bias;
+          bias = (bp && gcol < p.ntot) ? bp[gcol - p.out[oo].tile0] : 0.f;
+        } else {
+          bias = (out.bias && n0 + col < out.n) ? out.bias[n0 + col] : 0.f;
+        }
         const bool gelu = (EPI & 1) && out.act == kActGelu;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -212,6 +262,13 @@ __global__ __launch_bounds__(Tile<BM>::NTHR) void linear_kernel(LinParams p, flo
       const int piece = tid + NTHR * u;
       const int row = piece / PPRC, cp = (piece % PPRC) * 8;
       const int gr = m0 + 128 * half + row, gc = n0 + cp;
+      if constexpr (PK) {  // every output's width is a multiple of 8: pieces never straddle
+        if (gr >= p.M || gc >= p.ntot) continue;
+        const int oo = owner(gc);
+        *reinterpret_cast<bf16x8*>(p.out[oo].c + (long)gr * p.out[oo].n + (gc - p.out[oo].tile0)) =
+            *reinterpret_cast<const bf16x8*>(sC + row * CPITCH + cp);
+        continue;
+      }
       if (gr >= p.M || gc >= out.n) continue;  // n is a multiple of 8: whole pieces only
       bf16x8 val = *reinterpret_cast<const bf16x8*>(sC + row * CPITCH + cp);
       if ((EPI & 2) && out.res) {  // C = R + g * val, each element read and written here only
@@ -287,6 +344,29 @@ static hipError_t launch_linear_bm(int M, int K, const void* a, int nout, const 
   if (mt > 65535) return hipErrorInvalidValue;
   int epi = 0;
   for (int i = 0; i < nout; ++i) epi |= (outs[i].act == kActGelu ? 1 : 0) | (outs[i].res ? 2 : 0);
+  // several outputs sharing one activation and no residual: pack their columns (no tile
+  // padded out per output) when K is long enough for the per-column gathers to pay (at
+  // K = 384 the per-output tiles measured faster)
+  bool pack = nout > 1 && !(epi & 2) && K >= 1024;
+  for (int i = 1; i < nout; ++i) pack = pack && outs[i].act == outs[0].act;
+  if (pack) {
+    int col = 0;
+    for (int i = 0; i < nout; ++i) {
+      p.out[i].tile0 = col;
+      col += outs[i].n;
+    }
+    p.ntot = col;
+    if ((col + BM - 1) / BM < tiles) {
+      const dim3 grid((unsigned)((col + BM - 1) / BM), (unsigned)mt), block(Tile<BM>::NTHR);
+      if (epi & 1) hipLaunchKernelGGL((linear_kernel<BM, BK, kPacked | 1>), grid, block, 0, st, p, nullptr, 0);
+      else hipLaunchKernelGGL((linear_kernel<BM, BK, kPacked>), grid, block, 0, st, p, nullptr, 0);
+      return hipGetLastError();
+    }
+    for (int i = 0, t = 0; i < nout; ++i) {  // no column saved: per-output tiles after all
+      p.out[i].tile0 = t;
+      t += (outs[i].n + BM - 1) / BM;
+    }
+  }
   const dim3 grid((unsigned)tiles, (unsigned)mt), block(Tile<BM>::NTHR);
   switch (epi) {
     case 0: hipLaunchKernelGGL((linear_kernel<BM, BK, 0>), grid, block, 0, st, p, nullptr, 0); break;

@@ -111,3 +111,30 @@ def test_linear_split_k_not_needed_on_full_grids():
     c = torch.empty(16384, 1152, dtype=torch.bfloat16, device="cuda")
     w = torch.empty(1152, 1152, dtype=torch.bfloat16, device="cuda")
     assert dig.dig_linear_workspace_bytes(16384, 1152, [(c, w, None)]) == 0
+
+
+@pytest.mark.parametrize("m,k,ns,act", [(1000, 1024, [136, 8, 264], 0),
+                                        (600, 1152, [264, 136], 1),
+                                        (16384, 1152, [576, 576, 1152, 16, 1152], 0)])
+def test_linear_packed_outputs(m, k, ns, act):
+    """Several outputs with K >= 1024 run with their columns packed side by side (tiles that
+    straddle outputs): per-column bias and activation, ragged widths."""
+    import torch
+    import diffusion_backbone_amd as dig
+    announce("linear packed m=%d k=%d n=%s act=%d" % (m, k, ns, act))
+    rng = np.random.default_rng(m + k + len(ns))
+    a = W.quantize(rng.standard_normal((m, k)), "bf16")
+    ws = [W.quantize(rng.standard_normal((n, k)) / np.sqrt(k), "bf16") for n in ns]
+    bs = [W.f32_round(rng.standard_normal(n) * 0.5) for n in ns]
+    cs = [empty((m, n), "bf16") for n in ns]
+    dig.dig_linear(m, k, to_dev(a, "bf16"),
+                   [dig.linear_out(c, to_dev(w, "bf16"),
+                                   torch.from_numpy(b.astype(np.float32)).cuda(), act=act)
+                    for c, w, b in zip(cs, ws, bs)])
+    torch.cuda.synchronize()
+    errs = []
+    for c, w, b in zip(cs, ws, bs):
+        ref = oracle.linear(a, w, b)
+        errs.append(maxrel(to_f64(c), oracle.gelu(ref) if act else ref))
+    print("  errs " + " ".join("%.2e" % e for e in errs), flush=True)
+    assert max(errs) <= TOL["bf16"], errs
