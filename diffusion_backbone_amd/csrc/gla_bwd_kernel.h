@@ -245,8 +245,9 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
     dma_rows_c(base + Lo::R_Q, reinterpret_cast<const unsigned char*>(gq + row0 * dk), gsk, rbk,
                valid, wave, NW, lane);
-    dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
-               valid, wave, NW, lane);
+    if constexpr (FIN)  // pass A forms no P: no k
+      dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk,
+                 rbk, valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
                valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     const long row0 = ((long)b * p.L + t0) * H + h;
     const long gsk = (long)H * DK * sizeof(T), gsv = (long)H * DV * sizeof(T);
     pq.load(reinterpret_cast<const unsigned char*>(gq + row0 * DK), gsk, valid, tid);
-    pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
+    if constexpr (FIN) pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
     pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
     pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
     if constexpr (!RD) {
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     unsigned char* base = smem + Lo::O_RAW;
     const int valid = min(C, p.L - n * C);
     pq.put(base + Lo::R_Q, valid, tid);
-    pk.put(base + Lo::R_K, valid, tid);
+    if constexpr (FIN) pk.put(base + Lo::R_K, valid, tid);
     pz.put(base + Lo::R_Z, valid, tid);
     pv.put(base + Lo::R_V, valid, tid);
     if constexpr (!RD) {
@@ -399,8 +400,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       write_part(se);
     }
   }
-  f32x4 s0c[STW];  // S0 of the current chunk
-  load_state(n_top - 1, s0c);
+  f32x4 s0c[STW];  // S0 of the current chunk (the final pass: pass A forms no o, dq or dk)
+  if constexpr (FIN) load_state(n_top - 1, s0c);
 
   float gm[NDV], dgam[NDV];
 #pragma unroll
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 
     // ---- S0 (transposed, and row unless LEAN) as bf16 operands; G^T follows the gate
 #pragma unroll
-    for (int m = 0; m < STW; ++m) {
+    for (int m = 0; m < (FIN ? STW : 0); ++m) {
       const int u = wave + NW * m;
       if (u < NST) {
         const int ct = u / NDV, et = u - ct * NDV;
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       load_state(nn, s0p);
     } else if (!LB && n > c_first) {  // (the look-back's workgroups hold one chunk)
       if constexpr (PF) pf_load(n - 1);
-      load_state(n - 1, s0p);
+      if constexpr (FIN) load_state(n - 1, s0p);
     }
 
     // ---------------------------------------------------------------- gate phase
@@ -494,11 +495,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
       if constexpr (FULLK) {
         lds_row_read_k<T, NCL, KPE>(zr, rawz + tg * KPE, c0, tv);
-        lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
+        if constexpr (FIN) lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
         lds_row_read_k<T, NCL, KPE>(qr, rawq + tg * KPE, c0, tv);
       } else {
         lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
-        lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
+        if constexpr (FIN) lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
         lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
       if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
@@ -519,16 +520,19 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
         qf[j] = to_f(qr[j]) * p.q_scale * Fm<T>::exp2(bb[j]);
-        kf[j] = to_f(kr[j]) * Fm<T>::exp2(-bb[j]);
         qs[j] = from_f<T>(qf[j]);
-        ks[j] = from_f<T>(kf[j]);
+        if constexpr (FIN) {
+          kf[j] = to_f(kr[j]) * Fm<T>::exp2(-bb[j]);
+          ks[j] = from_f<T>(kf[j]);
+        }
       }
       float md = 0.f;
 #pragma unroll
       for (int j = 0; j < NCL; ++j) md = fmaxf(md, -bl[j]);
       md = wave_max_dpp(md);
 
-      if (c0 < QKC) {  // a lane's column run lies wholly inside or past the stored columns
+      if (FIN && c0 < QKC) {  // a lane's column run lies wholly inside or past the stored
+                              // columns (fp32 q e^b, k e^-b: the split products of P)
         lds_row_write<float, NCL>(sQ + tg * QKP, c0, qf);
         lds_row_write<float, NCL>(sK + tg * QKP, c0, kf);
       }
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       for (int j = 0; j < NCL; ++j) {
         if (FULLK || c0 + j < 16 * NDK) {
           sQt[(c0 + j) * TP + tg] = qs[j];
-          if (own) sKt[(c0 + j) * TP + tg] = ks[j];
+          if constexpr (FIN) sKt[(c0 + j) * TP + tg] = ks[j];
         }
         if (FULLK || c0 + j < dk) sB[tg * DKB + c0 + j] = bb[j];
       }
@@ -1107,8 +1111,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // one chunk down: its boundary term (this chunk's S0 is its S_end, G is updated), and
     // its S0 (read by nobody before the next top barrier; sPart's last reader, this chunk's
     // dlog phase, is behind the barrier above)
-    if (!LB && n > c_first) {
-      if (FIN) write_part(s0c);
+    if (FIN && !LB && n > c_first) {
+      write_part(s0c);
 #pragma unroll
       for (int m = 0; m < STW; ++m) s0c[m] = s0p[m];
     }
