@@ -543,7 +543,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           sQt[(c0 + j) * TP + tg] = qs[j];
           if constexpr (FIN) sKt[(c0 + j) * TP + tg] = ks[j];
         }
-        if (FULLK || c0 + j < dk) sB[tg * DKB + c0 + j] = bb[j];
+        if (FIN && (FULLK || c0 + j < dk)) sB[tg * DKB + c0 + j] = bb[j];
       }
       if (lane == 0) sMax[wave] = md;
       if (tg == C - 1) {
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
                 (FULLV || e < dv) ? rstd[i] * (dn[Eh][i] - oacc[Eh][i] * md[i]) : 0.f;
             dov4[i] = from_f<T>(dov);
             dof[Eh].v[i] = dov4[i];
-            if constexpr (!LEAN) sdO[row * VP + e] = dov4[i];
+            if constexpr (!LEAN && FIN) sdO[row * VP + e] = dov4[i];  // for D = dO V^T
             dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
           }
           lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
