@@ -227,14 +227,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 145343.5 KiB / 0.50008 + 92098.4 KiB / 1.0, segment scan 1666.7 + 2594.2,
-        # final pass 95169.4 + 94197.1 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
+        # pass A 115314.3 KiB / 0.50008 + 91570.0 KiB / 1.0, segment scan 1666.7 + 2594.2,
+        # final pass 95167.0 + 94370.3 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 689331909,
-        # pass A 79443.0 + 5099.5, state scan 2819.1 + 5184.0, output pass 67650.1 + 156476.2
-        "dig_gla_fwd": 477735727,
+        "dig_gla_bwd": 627473448,
+        # pass A 79447.7 + 5099.5, state scan 2819.1 + 5184.0, output pass 67964.5 + 156784.1
+        "dig_gla_fwd": 478704917,
     },
-    "sources_sha256": "78a45912ba0c9fe80df906d12bf7909ff4fc3da4deed651a746f9fc488ec3e39",
+    "sources_sha256": "bd8bb2155df3f7df9573e0138e318329e0fe9f45ff3379878e213f110eb57728",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
