@@ -337,9 +337,17 @@ def run_config(cfg, steps, warmup, seg_chunks=0, fwd_only=False, events=False):
            "directions": [W.SCAN_NAMES[d] for d in path.sched[:nb]]}
     ms_fwd = timed(path.step_fwd, steps, warmup)
     out["fwd"] = {"tokens_per_s": round(tokens / (ms_fwd / 1e3), 1), "ms_per_step": round(ms_fwd, 4)}
+    # the same step captured once in a HIP graph and replayed: the GPU's own time where the
+    # host's launches (tens of calls of a few us each) would otherwise set the pace
+    ms_g = timed_graph(path.step_fwd, steps, reps=1)
+    out["fwd"]["graph_replay"] = {"tokens_per_s": round(tokens / (ms_g / 1e3), 1),
+                                  "ms_per_step": round(ms_g, 4)}
     if not fwd_only:
         ms = timed(path.step, steps, warmup)
         out["fwd_bwd"] = {"tokens_per_s": round(tokens / (ms / 1e3), 1), "ms_per_step": round(ms, 4)}
+        ms_g = timed_graph(path.step, steps, reps=1)
+        out["fwd_bwd"]["graph_replay"] = {"tokens_per_s": round(tokens / (ms_g / 1e3), 1),
+                                          "ms_per_step": round(ms_g, 4)}
     if not events:
         del path, blocks
         torch.cuda.empty_cache()
@@ -851,6 +859,7 @@ def main():
     torch.cuda.synchronize()
     ms_ev = s1.elapsed_time(e1) / args.steps
     ms_fwd = timed(path.step_fwd, args.steps, 3)
+    ms_graph = timed_graph(path.step, args.steps, reps=1)  # the same step replayed from a graph
 
     th = cfg.batch * cfg.seq_len * cfg.heads
     rl = {}
@@ -893,6 +902,9 @@ def main():
                            % (nblocks, nblocks)},
         "fwd_only": {"value": round(tokens / (ms_fwd / 1e3), 1), "unit": "tokens/s",
                      "ms_per_step": round(ms_fwd, 4)},
+        "graph_replay": {"value": round(tokens / (ms_graph / 1e3), 1), "unit": "tokens/s",
+                         "ms_per_step": round(ms_graph, 4),
+                         "what": "the same K steps, each replayed from one captured HIP graph"},
         "roofline": roof,
         "roofline_other_call": {"call": "dig_" + other, "avg_call_us": round(rl[other]["ms"] * 1e3, 2),
                                 "achieved_gbs": round(rl[other]["gbs"], 1),
