@@ -403,13 +403,27 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   f32x4 s0c[STW];  // S0 of the current chunk (the final pass: pass A forms no o, dq or dk)
   if constexpr (FIN) load_state(n_top - 1, s0c);
 
-  float gm[NDV], dgam[NDV];
+  // dgamma partial sums of this wave's value tiles E0 + Eh of its row tiles (E0 fixed per
+  // wave: the accumulators take compile-time indices only)
+  float gm[NDV], dgl[RNDVH];
 #pragma unroll
   for (int E = 0; E < NDV; ++E) {
     const int e = E * 16 + r16;
     gm[E] = (e < dv && p.norm_w) ? p.norm_w[e] : 1.f;
-    dgam[E] = 0.f;
   }
+#pragma unroll
+  for (int Eh = 0; Eh < RNDVH; ++Eh) dgl[Eh] = 0.f;
+  // this wave's column-tile partial of dgamma for tile E (zero outside its tiles)
+  auto dgam_of = [&](int E) {
+    float v = 0.f;
+    if (wave < NT * bwd_spl<C, NW>()) {
+      const int E0w = (wave / NT) * RNDVH;
+#pragma unroll
+      for (int Eh = 0; Eh < RNDVH; ++Eh)
+        if (E0w + Eh == E) v = dgl[Eh];
+    }
+    return v;
+  };
   const int tg = tid % C, cg = tid / C;
   const int c0 = cg * NCL, e0 = cg * NEL;
   // Every load above has landed before the loop: otherwise the compiler's wait for them,
@@ -706,13 +720,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           const float nv = oacc[Eh][i], rv = to_f(rr[Eh][i]), dyv = to_f(dyr[Eh][i]);
           const float sg = Fm<T>::sig(rv), sw = rv * sg;
           if (col_on) {
-            // register arrays take compile-time indices only (a runtime one sends them to
-            // scratch memory): dgam[E] via a select over every tile
-            if (dg_here) {
-#pragma unroll
-              for (int k = 0; k < NDV; ++k)
-                if (k == E) dgam[k] += dyv * nv * sw;
-            }
+            if (dg_here) dgl[Eh] += dyv * nv * sw;
             if (own || RU) sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
           }
           dn[Eh][i] = dyv * gmE * sw;
@@ -798,7 +806,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     if constexpr (LB) {  // the dgamma partial is complete: per-wave sums
 #pragma unroll
       for (int E = 0; E < NDV; ++E) {
-        float v = dgam[E];
+        float v = dgam_of(E);
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
         if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
@@ -1122,7 +1130,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     // per-workgroup partial of dgamma, reduced in a fixed order by a later kernel
 #pragma unroll
     for (int E = 0; E < NDV; ++E) {
-      float v = dgam[E];
+      float v = dgam_of(E);
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
       if (g4 == 0) sDg[wave * DVP + E * 16 + r16] = v;
