@@ -262,6 +262,42 @@ __device__ __forceinline__ f32x4 mm_split(f32x4 acc, const float* A, int m0, con
   return acc;
 }
 
+// The B side of mm_split for one 16-row tile, split once and reused against several A tiles
+// (the same operations and order as mm_split: identical results).
+template <int COLS, int LD>
+struct SplitB {
+  static constexpr int NS = COLS == 36 ? 1 : (COLS + 31) / 32;
+  SplitFrag s[NS];
+  bf16x8 tail;  // COLS == 36: the packed four-column tail
+};
+template <int COLS, int LD>
+__device__ __forceinline__ SplitB<COLS, LD> split_b(const float* B, int n0, int lane) {
+  static_assert(COLS <= 64, "two K steps");
+  const int r = lane & 15, g = lane >> 4;
+  SplitB<COLS, LD> b;
+  if constexpr (COLS == 36) {
+    b.tail = tail4_frag<LD, true>(B, n0 + r, g);
+    b.s[0] = split_frag<COLS, LD, true>(B, n0 + r, 8 * g);
+  } else {
+    b.s[0] = split_frag<COLS, LD, (32 <= COLS)>(B, n0 + r, 8 * g);
+    if constexpr (COLS > 32) b.s[1] = split_frag<COLS, LD, (64 <= COLS)>(B, n0 + r, 32 + 8 * g);
+  }
+  return b;
+}
+template <int COLS, int LDA, int LDB>
+__device__ __forceinline__ f32x4 mm_split_pre(f32x4 acc, const float* A, int m0,
+                                              const SplitB<COLS, LDB>& b, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  if constexpr (COLS == 36) {
+    acc = mfma_bf16(tail4_frag<LDA, false>(A, m0 + r, g), b.tail, acc);
+    return mfma_split(split_frag<COLS, LDA, true>(A, m0 + r, 8 * g), b.s[0], acc);
+  }
+  acc = mfma_split(split_frag<COLS, LDA, (32 <= COLS)>(A, m0 + r, 8 * g), b.s[0], acc);
+  if constexpr (COLS > 32)
+    acc = mfma_split(split_frag<COLS, LDA, (64 <= COLS)>(A, m0 + r, 32 + 8 * g), b.s[1], acc);
+  return acc;
+}
+
 // The same with a bf16 K-contiguous B tile (pitch LDB elements): A enters as hi + lo parts, B as
 // stored.  A lane group whose first column lies past COLS takes B as zero (its A part is zero);
 // one whose first column lies inside reads eight B columns, so rows of B must hold

@@ -628,10 +628,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
       __syncthreads();
     }
+    // the reading final pass needs P only for P^T (dv): where two waves share a row tile they
+    // form alternate column tiles of it; the recomputing passes need whole rows (o = P V)
+    auto mine = [&](int J) { return !RD || SPL == 1 || (J & 1) == hh; };
     if (part) {
       if constexpr (FIN) {  // P (for dv) in the final pass only
-      float diag;  // exact q_i.k_i from the unscaled inputs (gate factor 1)
-      {
+      float diag = 0.f;  // exact q_i.k_i from the unscaled inputs (gate factor 1)
+      if (mine(I)) {
         constexpr int DQ = DKP / 4;
         const int ir = 16 * I + r16;
         T qd[DQ], kd[DQ];
@@ -652,13 +655,19 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
       if (!slow) {
         // bf16 I/O: split operands (dv takes P_ij times do_i, which is large where rstd_i is,
-        // so P_ij is needed to the accuracy of its own magnitude there)
+        // so P_ij is needed to the accuracy of its own magnitude there); the row tile's side
+        // is split once for every column tile
+        if constexpr (kBf) {
+          const auto bq = split_b<QKC, QKP>(sQ, 16 * I, lane);
 #pragma unroll
-        for (int J = 0; J < NT; ++J) {
-          if constexpr (kBf)
-            pt[J] = J <= I ? mm_split<QKC, QKP, QKP>(zero4(), sK, 16 * J, sQ, 16 * I, lane) : zero4();
-          else
-            pt[J] = J <= I ? Mma<T>::kc(zero4(), sK, QKP, 16 * J, sQ, QKP, 16 * I, DKP, lane) : zero4();
+          for (int J = 0; J < NT; ++J)
+            pt[J] = J <= I && mine(J) ? mm_split_pre<QKC, QKP, QKP>(zero4(), sK, 16 * J, bq, lane)
+                                      : zero4();
+        } else {
+#pragma unroll
+          for (int J = 0; J < NT; ++J)
+            pt[J] = J <= I && mine(J) ? Mma<T>::kc(zero4(), sK, QKP, 16 * J, sQ, QKP, 16 * I, DKP, lane)
+                                      : zero4();
         }
       } else {
         const T* sPw = sSlow + I * 16 * C;
@@ -676,7 +685,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             if (4 * g4 + i == r16) pt[J][i] = diag;
           }
         }
-        if (own && hh == 0 && J <= I) {  // P^T for dv (tiles above the diagonal stay zero)
+        if (own && (RD ? mine(J) : hh == 0) && J <= I) {  // P^T for dv (tiles above the
+                                                           // diagonal stay zero)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sPt[(16 * J + 4 * g4 + i) * TP + 16 * I + r16] = from_f<T>(pt[J][i]);

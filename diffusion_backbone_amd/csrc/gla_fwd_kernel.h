@@ -486,9 +486,10 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         if constexpr (kBf) {
           // split operands: where o_i cancels to a small vector its relative error is that of
           // these sums, and the RMSNorm gradient magnifies it by rstd_i
+          const auto bq = split_b<QKC, QKP>(sQ, 16 * I, lane);  // once for every column tile
 #pragma unroll
           for (int J = 0; J < NT; ++J)
-            pt[J] = J <= I ? mm_split<QKC, QKP, QKP>(zero4(), sK, 16 * J, sQ, 16 * I, lane) : zero4();
+            pt[J] = J <= I ? mm_split_pre<QKC, QKP, QKP>(zero4(), sK, 16 * J, bq, lane) : zero4();
         } else {
 #pragma unroll
           for (int J = 0; J < NT; ++J)

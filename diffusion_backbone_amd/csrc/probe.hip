@@ -93,9 +93,10 @@ __global__ __launch_bounds__(64 * NW) void contraction_kernel(int iters, float* 
     if (wave < NT) {
       const int I = wave;
       f32x4 pt[NT];
+      const auto bq = split_b<QKC, QKP>(sQ, 16 * I, lane);
 #pragma unroll
       for (int J = 0; J < NT; ++J)
-        pt[J] = J <= I ? mm_split<QKC, QKP, QKP>(zero4(), sK, 16 * J, sQ, 16 * I, lane) : zero4();
+        pt[J] = J <= I ? mm_split_pre<QKC, QKP, QKP>(zero4(), sK, 16 * J, bq, lane) : zero4();
 #pragma unroll
       for (int E = 0; E < NDV; ++E)
         oacc[E] = mm_split_b<QKC, QKP, QP>(oacc[E], sQ, 16 * I, sS, 16 * E, lane);
