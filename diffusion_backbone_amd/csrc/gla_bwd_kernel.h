@@ -494,14 +494,18 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       dgw = p.diagws[(sbase + n) * 2 * C + min(tid, 2 * C - 1)];
     }
     f32x4 s0p[STW];  // prefetch S0 of the next chunk down (consumed at the next top)
-    if constexpr (RD) {  // fixed load counts keep the compiler's wait for the loads above exact
-      const int nn = max(n - 1, c_first);
-      if constexpr (PF) pf_load(nn);
-      load_state(nn, s0p);
-    } else if (!LB && n > c_first) {  // (the look-back's workgroups hold one chunk)
-      if constexpr (PF) pf_load(n - 1);
-      if constexpr (FIN) load_state(n - 1, s0p);
-    }
+    // the next chunk's rows and S0 are loaded after the gate phase: issued here, in one burst
+    // with the loads above from every wave, they held the gate phase up
+    auto prefetch_next = [&]() {
+      if constexpr (RD) {  // fixed load counts keep the compiler's wait for the loads exact
+        const int nn = max(n - 1, c_first);
+        if constexpr (PF) pf_load(nn);
+        load_state(nn, s0p);
+      } else if (!LB && n > c_first) {  // (the look-back's workgroups hold one chunk)
+        if constexpr (PF) pf_load(n - 1);
+        if constexpr (FIN) load_state(n - 1, s0p);
+      }
+    };
 
     // ---------------------------------------------------------------- gate phase
     {
@@ -572,6 +576,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
     }
     __syncthreads();
+    prefetch_next();
     float mxa = sMax[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) mxa = fmaxf(mxa, sMax[w]);
