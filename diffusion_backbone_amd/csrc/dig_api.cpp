@@ -66,7 +66,7 @@ constexpr int kLdsLimit = 160 * 1024;
 // Validates the descriptor; fills the plan.  Returns DIG_OK or an error (message set).
 enum Pass { kFwd, kBwd };
 
-dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
+dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass, bool lowrank = false) {
   if (!d) return fail(DIG_ERR_NULL, "desc is NULL");
   if (d->batch < 0 || d->seq_len < 0)
     return fail(DIG_ERR_SHAPE, "batch (%d) and seq_len (%d) must be >= 0", d->batch, d->seq_len);
@@ -91,8 +91,11 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
     return fail(DIG_ERR_UNSUPPORTED, "tensor too large");
   if ((long long)d->batch * d->heads > (1LL << 30))
     return fail(DIG_ERR_UNSUPPORTED, "batch * heads too large");
+  if (lowrank && d->dtype != DIG_BF16)
+    return fail(DIG_ERR_UNSUPPORTED, "the low-rank gate needs DIG_BF16");
   *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, d->chunk,
                      d->dtype == DIG_BF16, d->seg_chunks, pass == kBwd);
+  s->lr = lowrank ? 1 : 0;
   const int lds = pass == kFwd ? dig::gla_fwd_lds_bytes(*s) : dig::gla_bwd_lds_bytes(*s);
   if (lds > kLdsLimit)
     return fail(DIG_ERR_UNSUPPORTED, "%s needs %d bytes of LDS for this shape (limit %d)",
@@ -140,7 +143,7 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 103; }
+int32_t dig_abi_version(void) { return 104; }
 
 dig_status dig_lookback_status(hipStream_t stream) {
   unsigned* word = dig::lookback_status_word();
@@ -184,16 +187,43 @@ size_t dig_gla_bwd_workspace_bytes(const dig_gla_desc* d) {
   return dig::gla_bwd_workspace(s);
 }
 
-dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
-                       const void* gate_logit, const void* r, const float* norm_w, void* y,
-                       void* o_pre_opt, void* saved_opt, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The low-rank key gate's inputs (all null: the caller passes the logits themselves).
+struct LowRank {
+  const void* factor;   // [B*L][16] bf16
+  const void* w;        // [H*d_k][16] bf16
+  const float* bias;    // [H*d_k] fp32 or null
+};
+
+// Checks the low-rank gate's arguments and adds their byte ranges to `in` (at *nin).
+dig_status check_lowrank(const dig_gla_desc* d, const LowRank* lr, int32_t rank, Range* in,
+                         int* nin) {
+  if (rank != dig::kGateRank)
+    return fail(DIG_ERR_UNSUPPORTED, "gate_rank %d: only %d is built", rank, dig::kGateRank);
+  if (!lr->factor || !lr->w) return fail(DIG_ERR_NULL, "gate_factor and gate_w are required");
+  if (!aligned16(lr->factor)) return fail(DIG_ERR_ALIGN, "gate_factor must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lr->w) | reinterpret_cast<uintptr_t>(lr->bias)) & 3u)
+    return fail(DIG_ERR_ALIGN, "gate_w and gate_bias must be 4-byte aligned");
+  const size_t cols = (size_t)d->heads * d->d_k;
+  in[(*nin)++] = rng("gate_factor", lr->factor, (size_t)d->batch * d->seq_len * rank * 2);
+  in[(*nin)++] = rng("gate_w", lr->w, cols * rank * 2);
+  in[(*nin)++] = rng("gate_bias", lr->bias, lr->bias ? cols * 4 : 0);
+  return DIG_OK;
+}
+
+dig_status gla_fwd_impl(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                        const void* gate_logit, const LowRank* lr, int32_t rank, const void* r,
+                        const float* norm_w, void* y, void* o_pre_opt, void* saved_opt,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dig::GlaShape s;
-  dig_status st = check_desc(d, &s, kFwd);
+  dig_status st = check_desc(d, &s, kFwd, lr != nullptr);
   if (st != DIG_OK) return st;
   if ((long long)d->batch * d->seq_len == 0) return ok();
-  if (!q || !k || !v || !gate_logit || !r || !y)
-    return fail(DIG_ERR_NULL, "q, k, v, gate_logit, r and y are required");
+  if (!q || !k || !v || (!lr && !gate_logit) || !r || !y)
+    return fail(DIG_ERR_NULL, "q, k, v, the gate, r and y are required");
   const void* ptrs[] = {q, k, v, gate_logit, r, norm_w, y, o_pre_opt, saved_opt, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -204,18 +234,21 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
   const size_t elt = d->dtype == DIG_BF16 ? 2 : 4;
   const size_t rows = (size_t)d->batch * d->seq_len * d->heads;
   const size_t bk = rows * d->d_k * elt, bv = rows * d->d_v * elt;
-  const size_t sb = dig::gla_states_bytes(s);
-  const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
-                      rng("gate_logit", gate_logit, bk), rng("r", r, bv),
-                      rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0)};
+  Range in[9] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
+                 rng("gate_logit", lr ? nullptr : gate_logit, lr ? 0 : bk), rng("r", r, bv),
+                 rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0)};
+  int nin = 6;
+  if (lr && (st = check_lowrank(d, lr, rank, in, &nin)) != DIG_OK) return st;
   const Range out[] = {rng("y", y, bv), rng("o_pre", o_pre_opt, o_pre_opt ? bv : 0),
                        rng("saved", saved_opt, saved_opt ? dig::gla_saved_bytes(s) : 0),
                        rng("workspace", workspace, workspace ? need : 0)};
-  st = check_alias(in, 6, out, 4);
+  st = check_alias(in, nin, out, 4);
   if (st != DIG_OK) return st;
 
   dig::GlaFwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.z = gate_logit; p.r = r; p.norm_w = norm_w;
+  p.q = q; p.k = k; p.v = v; p.r = r; p.norm_w = norm_w;
+  p.z = lr ? lr->factor : gate_logit;
+  if (lr) { p.zw = lr->w; p.zb = lr->bias; }
   p.y = y; p.o_pre = o_pre_opt;
   char* ws = static_cast<char*>(workspace);
   p.states = saved_opt ? static_cast<float*>(saved_opt) : reinterpret_cast<float*>(ws);
@@ -223,10 +256,11 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
     p.obar = static_cast<char*>(saved_opt) + dig::gla_saved_obar_offset(s);
     p.rstd = reinterpret_cast<float*>(static_cast<char*>(saved_opt) + dig::gla_saved_rstd_offset(s));
   }
-  p.seg_lg = reinterpret_cast<float*>(ws + a256(sb));
+  p.seg_lg = reinterpret_cast<float*>(ws + a256(dig::gla_states_bytes(s)));
   if (s.lookback) {  // chunk contributions, decays and flags
     p.lb_u = reinterpret_cast<float*>(ws);
-    p.lb_flag = reinterpret_cast<unsigned*>(ws + a256(sb) + a256(dig::gla_seglg_bytes(s)));
+    p.lb_flag = reinterpret_cast<unsigned*>(ws + a256(dig::gla_states_bytes(s)) +
+                                            a256(dig::gla_seglg_bytes(s)));
   }
   p.write_states = saved_opt != nullptr;
   p.g2scale = 1.4426950408889634f / d->tau;
@@ -235,13 +269,13 @@ dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, cons
   return check_dev(dig::launch_gla_fwd(s, p, stream), "dig_gla_fwd launch");
 }
 
-dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
-                       const void* gate_logit, const void* r, const float* norm_w,
-                       const void* dy, const void* saved, void* dq, void* dk, void* dv,
-                       void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+dig_status gla_bwd_impl(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                        const void* gate_logit, const LowRank* lr, int32_t rank, const void* r,
+                        const float* norm_w, const void* dy, const void* saved, void* dq,
+                        void* dk, void* dv, void* d_gate_logit, void* dr, float* d_norm_w,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dig::GlaShape s;
-  dig_status st = check_desc(d, &s, kBwd);
+  dig_status st = check_desc(d, &s, kBwd, lr != nullptr);
   if (st != DIG_OK) return st;
   if ((long long)d->batch * d->seq_len == 0) {
     // empty problem: the weight gradient is an empty sum
@@ -251,9 +285,9 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
     }
     return ok();
   }
-  if (!q || !k || !v || !gate_logit || !r || !dy || !saved || !dq || !dk || !dv ||
+  if (!q || !k || !v || (!lr && !gate_logit) || !r || !dy || !saved || !dq || !dk || !dv ||
       !d_gate_logit || !dr)
-    return fail(DIG_ERR_NULL, "q, k, v, gate_logit, r, dy, saved and all gradients are required");
+    return fail(DIG_ERR_NULL, "q, k, v, the gate, r, dy, saved and all gradients are required");
   const void* ptrs[] = {q, k, v, gate_logit, r, norm_w, dy, saved, dq, dk, dv, d_gate_logit, dr,
                         d_norm_w, workspace};
   for (const void* p : ptrs)
@@ -265,21 +299,25 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   const size_t elt = d->dtype == DIG_BF16 ? 2 : 4;
   const size_t rows = (size_t)d->batch * d->seq_len * d->heads;
   const size_t bk = rows * d->d_k * elt, bv = rows * d->d_v * elt;
-  const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
-                      rng("gate_logit", gate_logit, bk), rng("r", r, bv),
-                      rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0), rng("dy", dy, bv),
-                      rng("saved", saved, dig::gla_saved_bytes(s))};
+  Range in[11] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
+                  rng("gate_logit", lr ? nullptr : gate_logit, lr ? 0 : bk), rng("r", r, bv),
+                  rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0), rng("dy", dy, bv),
+                  rng("saved", saved, dig::gla_saved_bytes(s))};
+  int nin = 8;
+  if (lr && (st = check_lowrank(d, lr, rank, in, &nin)) != DIG_OK) return st;
   const Range out[] = {rng("dq", dq, bk), rng("dk", dk, bk), rng("dv", dv, bv),
                        rng("d_gate_logit", d_gate_logit, bk), rng("dr", dr, bv),
                        rng("d_norm_w", d_norm_w, d_norm_w ? d->d_v * 4 : 0),
                        rng("workspace", workspace, workspace ? need : 0)};
-  st = check_alias(in, 8, out, 7);
+  st = check_alias(in, nin, out, 7);
   if (st != DIG_OK) return st;
 
   const size_t BH = (size_t)s.B * s.H;
   char* ws = static_cast<char*>(workspace);
   dig::GlaBwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.z = gate_logit; p.r = r; p.norm_w = norm_w; p.dy = dy;
+  p.q = q; p.k = k; p.v = v; p.r = r; p.norm_w = norm_w; p.dy = dy;
+  p.z = lr ? lr->factor : gate_logit;
+  if (lr) { p.zw = lr->w; p.zb = lr->bias; }
   p.states = static_cast<const float*>(saved);
   p.obar = static_cast<const char*>(saved) + dig::gla_saved_obar_offset(s);
   p.rstd = reinterpret_cast<const float*>(static_cast<const char*>(saved) +
@@ -301,6 +339,49 @@ dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, cons
   p.q_scale = d->q_scale;
   p.eps = d->norm_eps;
   return check_dev(dig::launch_gla_bwd(s, p, stream), "dig_gla_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                       const void* gate_logit, const void* r, const float* norm_w, void* y,
+                       void* o_pre_opt, void* saved_opt, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return gla_fwd_impl(d, q, k, v, gate_logit, nullptr, 0, r, norm_w, y, o_pre_opt, saved_opt,
+                      workspace, workspace_bytes, stream);
+}
+
+dig_status dig_gla_fwd_lowrank(const dig_gla_desc* d, const void* q, const void* k,
+                               const void* v, const void* gate_factor, const void* gate_w,
+                               const float* gate_bias, int32_t gate_rank, const void* r,
+                               const float* norm_w, void* y, void* o_pre_opt, void* saved_opt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const LowRank lr{gate_factor, gate_w, gate_bias};
+  return gla_fwd_impl(d, q, k, v, nullptr, &lr, gate_rank, r, norm_w, y, o_pre_opt, saved_opt,
+                      workspace, workspace_bytes, stream);
+}
+
+dig_status dig_gla_bwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                       const void* gate_logit, const void* r, const float* norm_w,
+                       const void* dy, const void* saved, void* dq, void* dk, void* dv,
+                       void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return gla_bwd_impl(d, q, k, v, gate_logit, nullptr, 0, r, norm_w, dy, saved, dq, dk, dv,
+                      d_gate_logit, dr, d_norm_w, workspace, workspace_bytes, stream);
+}
+
+dig_status dig_gla_bwd_lowrank(const dig_gla_desc* d, const void* q, const void* k,
+                               const void* v, const void* gate_factor, const void* gate_w,
+                               const float* gate_bias, int32_t gate_rank, const void* r,
+                               const float* norm_w, const void* dy, const void* saved, void* dq,
+                               void* dk, void* dv, void* d_gate_logit, void* dr,
+                               float* d_norm_w, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const LowRank lr{gate_factor, gate_w, gate_bias};
+  return gla_bwd_impl(d, q, k, v, nullptr, &lr, gate_rank, r, norm_w, dy, saved, dq, dk, dv,
+                      d_gate_logit, dr, d_norm_w, workspace, workspace_bytes, stream);
 }
 
 dig_status dig_srem_reorient(int32_t batch, int32_t grid_h, int32_t grid_w, int32_t channels,
@@ -586,6 +667,7 @@ namespace {
 // Carving of dig_block_fwd's workspace (bf16 intermediates, then the GLA call's workspace).
 struct BlockWs {
   size_t h, q, k, v, u, r, z, y, x1, hid, split, split_bytes, gla, total;
+  bool fused;  // the gate logits are formed inside the mixer's kernels (rank 16)
 };
 
 dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
@@ -615,6 +697,7 @@ dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
   dig::GlaShape s;
   dig_status st = check_desc(g, &s, kFwd);
   if (st != DIG_OK) return st;
+  w->fused = d->gate_rank == dig::kGateRank && check_desc(g, &s, kFwd, true) == DIG_OK;
   const size_t M = (size_t)d->batch * g->seq_len;
   if (M > (size_t)65535 * 256) return fail(DIG_ERR_UNSUPPORTED, "too many tokens");
   const size_t HK = (size_t)d->heads * d->d_k, HV = (size_t)d->heads * d->d_v;
@@ -626,7 +709,7 @@ dig_status block_plan(const dig_block_desc* d, dig_gla_desc* g, BlockWs* w) {
   w->v = take(HV);
   w->u = take(d->gate_rank);
   w->r = take(HV);
-  w->z = take(HK);
+  w->z = w->fused ? 0 : take(HK);
   w->y = take(HV);
   w->x1 = take(d->dim);
   w->hid = take(d->ffn_dim);
@@ -728,15 +811,19 @@ dig_status dig_block_fwd(const dig_block_desc* d, const dig_block_weights* wt, c
     st = dig_linear(m, D, DIG_BF16, h, 5, o, stream);
     if (st != DIG_OK) return st;
   }
-  // 3. z = u W_gate^T + b_gate
-  {
+  // 3. z = u W_gate^T + b_gate (rank 16: formed inside the mixer's kernels instead)
+  if (!w.fused) {
     const dig_linear_out o{z, wt->w_gate, wt->b_gate, HK, DIG_ACT_NONE, nullptr, nullptr, 0, 1};
     st = dig_linear(m, R, DIG_BF16, u, 1, &o, stream);
     if (st != DIG_OK) return st;
   }
   // 4. the GLA token mixer, eqs. (5)-(10) up to the output projection
-  st = dig_gla_fwd(&g, q, k, v, z, r, wt->gla_norm_w, y, nullptr, nullptr, ws + w.gla,
-                   w.total - w.gla, stream);
+  if (w.fused)
+    st = dig_gla_fwd_lowrank(&g, q, k, v, u, wt->w_gate, wt->b_gate, R, r, wt->gla_norm_w, y,
+                             nullptr, nullptr, ws + w.gla, w.total - w.gla, stream);
+  else
+    st = dig_gla_fwd(&g, q, k, v, z, r, wt->gla_norm_w, y, nullptr, nullptr, ws + w.gla,
+                     w.total - w.gla, stream);
   if (st != DIG_OK) return st;
   // 5. x1 = x + alpha_1 * (y W_out^T + b_out)
   {

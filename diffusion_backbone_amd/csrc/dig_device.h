@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dig_internal.h"
+
 namespace dig {
 
 typedef __bf16 bf16;
@@ -176,6 +178,51 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ------------------------------------------------------------ low-rank key gate
+// The key gate's logits as a rank-16 product formed inside the chunk kernels: for token t and
+// key column c of head h, z = bias[h d_k + c] + sum_r f[t][r] W[h d_k + c][r], with the factor
+// f (16 bf16 per token) staged with the chunk's rows and the head's slice of W (bf16, out x in)
+// and bias (fp32) copied once per workgroup into an LDS table: NCOLS rows of 16 bf16 (32 bytes,
+// zero past d_k), then NCOLS fp32 biases.  Sums run as eight bf16 pair dot products into an
+// fp32 accumulator started at the bias, in the same order in every kernel, so the forward and
+// the backward see identical logits.
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int lowrank_table_bytes(int ncols) { return ncols * (kGateRank * 2 + 4); }
+template <int NCOLS, int NTH>
+__device__ __forceinline__ void lowrank_table_fill(unsigned char* tab, const bf16* w,
+                                                   const float* bias, int h, int dk, int tid) {
+  // rows of W are 32 bytes: eight 4-byte pieces each (W needs only 4-byte alignment)
+  const unsigned* wsrc = reinterpret_cast<const unsigned*>(w + (long)h * dk * kGateRank);
+  unsigned* wdst = reinterpret_cast<unsigned*>(tab);
+  for (int i = tid; i < NCOLS * 8; i += NTH) wdst[i] = i < dk * 8 ? wsrc[i] : 0u;
+  float* bdst = reinterpret_cast<float*>(tab + NCOLS * kGateRank * 2);
+  for (int c = tid; c < NCOLS; c += NTH) bdst[c] = (c < dk && bias) ? bias[(long)h * dk + c] : 0.f;
+}
+// Logits of one token for the N key columns c0..c0+N-1 (frow: the token's 16 factor values in
+// LDS, 16-byte aligned).
+template <int NCOLS, int N>
+__device__ __forceinline__ void lowrank_logits(float (&z)[N], const bf16* frow,
+                                               const unsigned char* tab, int c0) {
+  const uint4 f0 = *reinterpret_cast<const uint4*>(frow);
+  const uint4 f1 = *reinterpret_cast<const uint4*>(frow + 8);
+  const unsigned fp[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+  const float* btab = reinterpret_cast<const float*>(tab + NCOLS * kGateRank * 2);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint4* wr = reinterpret_cast<const uint4*>(tab + (c0 + j) * kGateRank * 2);
+    const uint4 w0 = wr[0], w1 = wr[1];
+    const unsigned wp[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float acc = btab[c0 + j];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, fp[i]),
+                                            __builtin_bit_cast(bf16x2, wp[i]), acc, false);
+    z[j] = acc;
+    if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // two columns' table reads in flight
+  }
+}
+
 // ------------------------------------------------- split-precision operands on bf16 MFMA
 // An fp32 operand x is carried as x_hi + x_lo, x_hi = bf16(x), x_lo = bf16(x - x_hi) (the
 // difference is exact in fp32).  The pair holds about 16 significant bits, so a product
@@ -344,6 +391,19 @@ __device__ __forceinline__ f32x4 mm_split_b(f32x4 acc, const float* A, int m0, c
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// The value computed here: it feeds an empty asm statement with side effects, which nothing
+// moves across, so its computation cannot sink past later loads and branches (where its
+// inputs would stay live across them).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// x where `on`, else +0, through a mask the optimiser cannot see (a select of an expensive
+// operand, such as a logarithm, is otherwise turned into a branch around its computation,
+// one per column, which also holds that computation's inputs live across the branches).
+__device__ __forceinline__ float keep_if(bool on, float x) {
+  const unsigned m = (unsigned)opaque(on ? -1 : 0);
+  return __builtin_bit_cast(float, __builtin_bit_cast(unsigned, x) & m);
 }
 
 // ------------------------------------------------------------ wave primitives

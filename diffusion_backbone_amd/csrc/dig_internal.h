@@ -8,6 +8,9 @@
 
 namespace dig {
 
+// Rank of the low-rank key gate formed inside the chunk kernels (x W_a1 has 16 columns).
+constexpr int kGateRank = 16;
+
 // ------------------------------------------------------------------ GLA forward
 struct GlaShape {
   int B, L, H, dk, dv, C;   // C = chunk
@@ -20,6 +23,7 @@ struct GlaShape {
   int lookback;             // one chunk per workgroup, the carried state through a look-back
                             // over flags (forward: S0; backward: G), one launch
   int ndk, ndv;             // compiled head-dim class: d_k <= 16*ndk, d_v <= 16*ndv
+  int lr;                   // 1: the key gate is the rank-16 product formed in the kernels
 };
 
 // Head-dim classes the kernels are compiled for (16-wide tiles of d_k and d_v).
@@ -30,7 +34,9 @@ struct GlaFwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* z;
+  const void* z;        // gate logits [B*L*H][dk], or (low-rank gate) the factor [B*L][16]
+  const void* zw;       // low-rank gate: up-projection [H*dk][16] bf16, else null
+  const float* zb;      // low-rank gate: bias [H*dk] fp32, or null
   const void* r;
   const float* norm_w;
   void* y;
@@ -78,7 +84,9 @@ struct GlaBwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* z;
+  const void* z;        // gate logits, or the low-rank gate's factor (as in GlaFwdParams)
+  const void* zw;
+  const float* zb;
   const void* r;
   const float* norm_w;
   const void* dy;

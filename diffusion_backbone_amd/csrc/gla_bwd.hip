@@ -115,25 +115,35 @@ hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipS
 }
 
 // Chunk kernels, instantiated per element type in their own translation units.
-template <typename T>
+template <typename T, bool LR>
 hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
                             size_t* ru_out);
-extern template hipError_t launch_gla_bwd_t<bf16>(const GlaShape&, GlaBwdParams, hipStream_t,
-                                                  int*, size_t*);
-extern template hipError_t launch_gla_bwd_t<float>(const GlaShape&, GlaBwdParams, hipStream_t,
-                                                   int*, size_t*);
+extern template hipError_t launch_gla_bwd_t<bf16, false>(const GlaShape&, GlaBwdParams,
+                                                         hipStream_t, int*, size_t*);
+extern template hipError_t launch_gla_bwd_t<float, false>(const GlaShape&, GlaBwdParams,
+                                                          hipStream_t, int*, size_t*);
+extern template hipError_t launch_gla_bwd_t<bf16, true>(const GlaShape&, GlaBwdParams,
+                                                        hipStream_t, int*, size_t*);
+
+// the kernels for the element type and key-gate form (the low-rank gate exists for bf16)
+static hipError_t bwd_kernels(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
+                              size_t* ru_out) {
+  if (s.lr)
+    return s.bf16 ? launch_gla_bwd_t<bf16, true>(s, p, st, lds_out, ru_out)
+                  : hipErrorInvalidValue;
+  return s.bf16 ? launch_gla_bwd_t<bf16, false>(s, p, st, lds_out, ru_out)
+                : launch_gla_bwd_t<float, false>(s, p, st, lds_out, ru_out);
+}
 
 int gla_bwd_lds_bytes(const GlaShape& s) {
   int bytes = 0;
-  const hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, GlaBwdParams{}, nullptr, &bytes, nullptr)
-                              : launch_gla_bwd_t<float>(s, GlaBwdParams{}, nullptr, &bytes, nullptr);
+  const hipError_t e = bwd_kernels(s, GlaBwdParams{}, nullptr, &bytes, nullptr);
   return e == hipSuccess ? bytes : 0;
 }
 
 static void reuse_sizes(const GlaShape& s, size_t (&b)[2]) {
   b[0] = b[1] = 0;
-  const hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, GlaBwdParams{}, nullptr, nullptr, b)
-                              : launch_gla_bwd_t<float>(s, GlaBwdParams{}, nullptr, nullptr, b);
+  const hipError_t e = bwd_kernels(s, GlaBwdParams{}, nullptr, nullptr, b);
   if (e != hipSuccess) b[0] = b[1] = 0;
 }
 static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
@@ -168,8 +178,7 @@ hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st) {
   }
   p.NC = s.NC; p.sc = s.sc; p.nseg = s.nseg;
   p.C = s.C; p.prefix = s.bprefix;
-  hipError_t e = s.bf16 ? launch_gla_bwd_t<bf16>(s, p, st, nullptr, nullptr)
-                        : launch_gla_bwd_t<float>(s, p, st, nullptr, nullptr);
+  hipError_t e = bwd_kernels(s, p, st, nullptr, nullptr);
   if (e != hipSuccess) return e;
   if (p.d_norm_w && s.nseg == 1) {  // with more segments the scan launch reduces dgamma
     const long parts = (long)s.B * s.H * s.nseg;

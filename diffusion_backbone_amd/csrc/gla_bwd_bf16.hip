@@ -3,6 +3,6 @@
 #include "gla_bwd_kernel.h"
 
 namespace dig {
-template hipError_t launch_gla_bwd_t<bf16>(const GlaShape&, GlaBwdParams, hipStream_t, int*,
+template hipError_t launch_gla_bwd_t<bf16, false>(const GlaShape&, GlaBwdParams, hipStream_t, int*,
                                            size_t*);
 }  // namespace dig

@@ -51,7 +51,10 @@ constexpr int bal16(int x) { return (x + 15) / 16 * 16; }
 // would not fit.  PAD gives the raw staging rows pitches at which the gate pass (one lane
 // per token) reads without bank conflicts (register-staged rows only; LDS DMA writes rows
 // packed).  The fp32 per-token rows (b, q.dq - k.dk) have an odd pitch for the same reason.
-template <typename T, int DK, int DV, int C, bool FIN, bool LEAN, int NW = 4, bool PAD = false>
+// LR: the key gate is the rank-16 product formed in the kernel (factor rows staged beside the
+// others, the head's slice of the up-projection in an LDS table; the z rows stage dz only).
+template <typename T, int DK, int DV, int C, bool FIN, bool LEAN, int NW = 4, bool PAD = false,
+          bool LR = false>
 struct BwdLayout {
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
@@ -94,7 +97,8 @@ struct BwdLayout {
   static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [NW][DVP]
   static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [2][C] (halves)
   static constexpr int O_XCH = O_DIAG + bal16(2 * C * 4);            // [4][C] row sums
-  static constexpr int O_RAW = O_XCH + bal16(4 * C * 4);
+  static constexpr int O_ZT = O_XCH + bal16(4 * C * 4);              // low-rank gate table
+  static constexpr int O_RAW = O_ZT + bal16(LR ? lowrank_table_bytes(DKP) : 0);
   // raw staging: q, k, z (pitch KPE, or the runtime d_k when packed), v, r, dy (pitch VPE)
   static constexpr int R_Q = 0;
   static constexpr int R_K = R_Q + bal16(C * KPE * SZ);
@@ -102,13 +106,17 @@ struct BwdLayout {
   static constexpr int R_V = R_Z + bal16(C * KPE * SZ);
   static constexpr int R_R = R_V + bal16(C * (VPE > 2 * KPE ? VPE : 2 * KPE) * SZ);  // v; dq|dk
   static constexpr int R_DY = R_R + bal16(C * VPE * SZ);
-  static constexpr int SLOT = R_DY + bal16(C * VPE * SZ);
+  // factor rows (LR): 16 elements, packed (the final pass has no LDS left for a padded pitch)
+  static constexpr int ZPE = kGateRank;
+  static constexpr int R_F = R_DY + bal16(C * VPE * SZ);
+  static constexpr int SLOT = R_F + bal16(LR ? C * ZPE * SZ : 0);
   static constexpr int bytes = O_RAW + SLOT;
 };
 constexpr int kBwdLdsBudget = 160 * 1024;
-template <typename T, int DK, int DV, int C, bool FIN, int NW = 4, bool PAD = false>
+template <typename T, int DK, int DV, int C, bool FIN, int NW = 4, bool PAD = false,
+          bool LR = false>
 constexpr bool bwd_lean() {
-  return BwdLayout<T, DK, DV, C, FIN, false, NW, PAD>::bytes > kBwdLdsBudget;
+  return BwdLayout<T, DK, DV, C, FIN, false, NW, PAD, LR>::bytes > kBwdLdsBudget;
 }
 
 // Register prefetch of the next chunk's raw rows (exact head shapes).  The recomputing final
@@ -150,14 +158,16 @@ constexpr size_t bwd_reuse_chunk_bytes() {
 // reduces the dgamma partials in a fixed order once every flag is up.  Flags hold this
 // call's tag, so values left by earlier calls never match; each wait is bounded.
 template <typename T, int DK, int DV, bool EXACT, int C, bool FIN, int NW, bool RU = false,
-          bool LB = false>
+          bool LB = false, bool LR = false>
 __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
+  static_assert(!LR || sizeof(T) == 2, "the low-rank gate is bf16");
   static_assert(!RU || bwd_reuse_ok<DK, DV, EXACT, C, NW>(), "reuse needs every wave in the recompute phase");
   static_assert(!LB || (FIN && !RU), "the look-back runs the recomputing final pass");
   constexpr bool RD = FIN && RU;  // the final pass reads dO (skips the output-stage backward)
   constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW, RD>();
-  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF>();
-  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF>;
+  constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF, LR>();
+  using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF, LR>;
+  constexpr int ZPE = Lo::ZPE;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE, DKB = Lo::DKB;
   constexpr int NTH = 64 * NW;  // NW waves
   constexpr bool kBf = sizeof(T) == 2;
@@ -215,6 +225,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   T* rawq = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Q);
   T* rawk = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_K);
   T* rawz = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_Z);  // then dz
+  const bf16* rawf = reinterpret_cast<const bf16*>(smem + Lo::O_RAW + Lo::R_F);  // factor (LR)
   T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);  // then dq | dk
   // raw row pitches: padded for register-staged rows, the runtime widths for DMA-staged ones
   const int kp = PF ? KPE : dk, vp = PF ? VPE : dv;
@@ -248,8 +259,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     if constexpr (FIN)  // pass A forms no P: no k
       dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk,
                  rbk, valid, wave, NW, lane);
-    dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
-               valid, wave, NW, lane);
+    if constexpr (LR)
+      dma_rows_c(base + Lo::R_F,
+                 reinterpret_cast<const unsigned char*>(gz + ((long)b * p.L + t0) * kGateRank),
+                 kGateRank * sizeof(T), kGateRank * (int)sizeof(T), valid, wave, NW, lane);
+    else
+      dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk,
+                 rbk, valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
                valid, wave, NW, lane);
     if constexpr (!RD) {
@@ -306,7 +322,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
   };
 
-  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pq, pk, pz;
+  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pq, pk;
+  RowRegs<(LR ? kGateRank : DK) * (int)sizeof(T), C, NTH, (LR ? ZPE : KPE) * (int)sizeof(T)> pz;
   RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv, pr, pdy;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
@@ -314,7 +331,11 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     const long gsk = (long)H * DK * sizeof(T), gsv = (long)H * DV * sizeof(T);
     pq.load(reinterpret_cast<const unsigned char*>(gq + row0 * DK), gsk, valid, tid);
     if constexpr (FIN) pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
-    pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
+    if constexpr (LR)
+      pz.load(reinterpret_cast<const unsigned char*>(gz + ((long)b * p.L + t0) * kGateRank),
+              kGateRank * sizeof(T), valid, tid);
+    else
+      pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
     pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
     if constexpr (!RD) {
       pr.load(reinterpret_cast<const unsigned char*>(gr + row0 * DV), gsv, valid, tid);
@@ -326,7 +347,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     const int valid = min(C, p.L - n * C);
     pq.put(base + Lo::R_Q, valid, tid);
     if constexpr (FIN) pk.put(base + Lo::R_K, valid, tid);
-    pz.put(base + Lo::R_Z, valid, tid);
+    pz.put(base + (LR ? Lo::R_F : Lo::R_Z), valid, tid);
     pv.put(base + Lo::R_V, valid, tid);
     if constexpr (!RD) {
       pr.put(base + Lo::R_R, valid, tid);
@@ -350,6 +371,9 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
+  if constexpr (LR)  // read from the first chunk's gate pass on (behind the loop's barrier)
+    lowrank_table_fill<DKP, NTH>(smem + Lo::O_ZT, static_cast<const bf16*>(p.zw), p.zb, h, dk,
+                                 tid);
 
   // gradient state G (fp32, tile u = wave + 4m -> (key tile, value tile))
   f32x4 gacc[STW];
@@ -511,24 +535,43 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     {
       const bool tv = tg < valid;
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
-      if constexpr (FULLK) {
+      float zf[NCL], bb[NCL], bl[NCL];  // gate logits, log2 gates
+      if constexpr (LR) {  // formed and turned into log gates before the other rows are read
+        lowrank_logits<DKP, NCL>(zf, rawf + tg * ZPE, smem + Lo::O_ZT, c0);
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+          const bool on = FULLK ? tv : (tv && c0 + j < dk);
+          bb[j] = keep_if(on, Fm<T>::lsig2(zf[j]) * inv_tau);
+          pin(bb[j]);
+        }
+        // sigmoid(-z) for dz, in the z rows (which stage nothing else until dz replaces it)
+        if constexpr (FIN) {
+#pragma unroll
+          for (int j = 0; j < NCL; ++j)
+            if (FULLK || c0 + j < dk) rawz[tg * kp + c0 + j] = from_f<T>(Fm<T>::sig(-zf[j]));
+        }
+      } else if constexpr (FULLK) {
         lds_row_read_k<T, NCL, KPE>(zr, rawz + tg * KPE, c0, tv);
+      } else {
+        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
+      }
+      if constexpr (FULLK) {
         if constexpr (FIN) lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
         lds_row_read_k<T, NCL, KPE>(qr, rawq + tg * KPE, c0, tv);
       } else {
-        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
         if constexpr (FIN) lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
         lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
       if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
       else lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
-
-      float bb[NCL], bl[NCL];
+      if constexpr (!LR) {
 #pragma unroll
-      for (int j = 0; j < NCL; ++j) {
-        const bool on = FULLK ? tv : (tv && c0 + j < dk);
-        bb[j] = on ? Fm<T>::lsig2(to_f(zr[j])) * inv_tau : 0.f;
+        for (int j = 0; j < NCL; ++j) {
+          const bool on = FULLK ? tv : (tv && c0 + j < dk);
+          bb[j] = keep_if(on, Fm<T>::lsig2(to_f(zr[j])) * inv_tau);
+        }
       }
+
 #pragma unroll
       for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
 #pragma unroll
@@ -699,11 +742,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       }
       }  // FIN
       if constexpr (!RD) {  // the reading final pass skips the output-stage backward
-      // o rstd as the forward saved it (its rows are the rows of this tile)
+      // o rstd as the forward saved it (its rows are the rows of this tile); rows past the
+      // sequence end hold whatever the forward formed from stale staging rows: zero here
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[Eh][i] = obr[Eh].v[i];
+        for (int i = 0; i < 4; ++i)
+          oacc[Eh][i] = 16 * I + 4 * g4 + i < valid ? obr[Eh].v[i] : 0.f;
 
       // output-stage backward: r, dy first (one LDS round trip); value tiles past this
       // half's range (an odd tile count) count as zero columns
@@ -721,6 +766,9 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
     if (part && !RD) {
       rstd[0] = rsv.x; rstd[1] = rsv.y; rstd[2] = rsv.z; rstd[3] = rsv.w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // (rows past the sequence end: see oacc)
+        if (16 * I + 4 * g4 + i >= valid) rstd[i] = 0.f;
       // oacc is the normalised output, dn = dy * w * swish(r)
 #pragma unroll
       for (int Eh = 0; Eh < NDVH; ++Eh) {
@@ -1074,14 +1122,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       // prefix scan) + the boundary term; dz = dlog(alpha) sigmoid(-z) / tau, over raw z
       const int tr = C - 1 - tg;
       const bool tv = tr < valid;
-      float w[NCL];
-      T zr[NCL];
+      float w[NCL], zg[NCL];  // q.dq - k.dk; z (low-rank gate: sigmoid(-z), from the gate pass)
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
         const int c = c0 + j;
         const bool on = tv && (FULLK || c < dk);
         w[j] = on ? sW[tr * DKB + c] : 0.f;
-        zr[j] = on ? rawz[tr * kp + c] : from_f<T>(0.f);
+        zg[j] = on ? to_f(rawz[tr * kp + c]) : 0.f;
       }
       float bterm[NCL];
 #pragma unroll
@@ -1099,7 +1146,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         if (tv && (FULLK || c < dk)) {
           float dla = w[j] + bterm[j];
           if (n == 0 && tr == 0) dla = 0.f;  // alpha_0 multiplies the zero initial state
-          rawz[tr * kp + c] = from_f<T>(dla * Fm<T>::sig(-to_f(zr[j])) * inv_tau);
+          const float sgm = LR ? zg[j] : Fm<T>::sig(-zg[j]);
+          rawz[tr * kp + c] = from_f<T>(dla * sgm * inv_tau);
         }
       }
       __syncthreads();
@@ -1225,7 +1273,7 @@ constexpr int bwd_waves() {
   return (EXACT && sizeof(T) == 2 && ((DK == 32 && DV == 64) || (DK == 36 && DV == 72))) ? DIG_BWD_WAVES8 : 4;
 }
 
-template <typename T, int DK, int DV, bool EXACT, int C>
+template <typename T, int DK, int DV, bool EXACT, int C, bool LR>
 static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
                                size_t* ru_out) {
   const long BH = (long)s.B * s.H;
@@ -1242,11 +1290,14 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   constexpr bool PF_RD = bwd_prefetch<DK, DV, EXACT, true, NW, true>();
   constexpr bool PF_A = bwd_prefetch<DK, DV, EXACT, false, NW>();
   constexpr int fin_bytes =
-      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_FIN>(), NW, PF_FIN>::bytes;
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_FIN, LR>(), NW, PF_FIN,
+                LR>::bytes;
   constexpr int rd_bytes =
-      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_RD>(), NW, PF_RD>::bytes;
+      BwdLayout<T, DK, DV, C, true, bwd_lean<T, DK, DV, C, true, NW, PF_RD, LR>(), NW, PF_RD,
+                LR>::bytes;
   constexpr int a_bytes =
-      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, PF_A>(), NW, PF_A>::bytes;
+      BwdLayout<T, DK, DV, C, false, bwd_lean<T, DK, DV, C, false, NW, PF_A, LR>(), NW, PF_A,
+                LR>::bytes;
   if (lds_out) {
     *lds_out = RU && three && rd_bytes > fin_bytes ? rd_bytes : fin_bytes;
     return hipSuccess;
@@ -1254,7 +1305,7 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   if constexpr (RU) {
     if (lb) {
       if (!p.lb_flag) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, false, true>),
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, false, true, LR>),
                          dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
       return hipGetLastError();
     }
@@ -1262,49 +1313,49 @@ static hipError_t launch_bwd_c(const GlaShape& s, GlaBwdParams p, hipStream_t st
   if (three) {
     if constexpr (RU) {
       if (!p.dofrag || !p.diagws) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW, true>),
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW, true, false, LR>),
                          dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
     } else {
-      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW>),
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, false, NW, false, false, LR>),
                          dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), a_bytes, st, p);
     }
     const hipError_t e = launch_gla_gstate_scan(s, p, st);
     if (e != hipSuccess) return e;
     if constexpr (RU) {
-      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, true>),
+      hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, true, false, LR>),
                          dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), rd_bytes, st, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW>),
+  hipLaunchKernelGGL((gla_bwd_kernel<T, DK, DV, EXACT, C, true, NW, false, false, LR>),
                      dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), fin_bytes, st, p);
   return hipGetLastError();
 }
 
-template <typename T, int DK, int DV, bool EXACT>
+template <typename T, int DK, int DV, bool EXACT, bool LR>
 static hipError_t launch_bwd_dims(const GlaShape& s, GlaBwdParams p, hipStream_t st,
                                   int* lds_out, size_t* ru_out) {
   switch (s.C) {
-    case 16: return launch_bwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out, ru_out);
-    case 32: return launch_bwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out, ru_out);
-    case 64: return launch_bwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out, ru_out);
+    case 16: return launch_bwd_c<T, DK, DV, EXACT, 16, LR>(s, p, st, lds_out, ru_out);
+    case 32: return launch_bwd_c<T, DK, DV, EXACT, 32, LR>(s, p, st, lds_out, ru_out);
+    case 64: return launch_bwd_c<T, DK, DV, EXACT, 64, LR>(s, p, st, lds_out, ru_out);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Same shape dispatch as the forward.  Queries: lds_out != nullptr reports the final pass's
 // LDS bytes, ru_out != nullptr the reuse buffers' bytes ({dO fragments, diagonals}).
-template <typename T>
+template <typename T, bool LR>
 hipError_t launch_gla_bwd_t(const GlaShape& s, GlaBwdParams p, hipStream_t st, int* lds_out,
                             size_t* ru_out) {
-  if (s.dk == 32 && s.dv == 64) return launch_bwd_dims<T, 32, 64, true>(s, p, st, lds_out, ru_out);
-  if (s.dk == 36 && s.dv == 72) return launch_bwd_dims<T, 36, 72, true>(s, p, st, lds_out, ru_out);
-  if (s.dk == 16 && s.dv == 32) return launch_bwd_dims<T, 16, 32, true>(s, p, st, lds_out, ru_out);
+  if (s.dk == 32 && s.dv == 64) return launch_bwd_dims<T, 32, 64, true, LR>(s, p, st, lds_out, ru_out);
+  if (s.dk == 36 && s.dv == 72) return launch_bwd_dims<T, 36, 72, true, LR>(s, p, st, lds_out, ru_out);
+  if (s.dk == 16 && s.dv == 32) return launch_bwd_dims<T, 16, 32, true, LR>(s, p, st, lds_out, ru_out);
   switch (s.ndk * 16 + s.ndv) {
-    case 1 * 16 + 2: return launch_bwd_dims<T, 16, 32, false>(s, p, st, lds_out, ru_out);
-    case 2 * 16 + 4: return launch_bwd_dims<T, 32, 64, false>(s, p, st, lds_out, ru_out);
-    case 3 * 16 + 5: return launch_bwd_dims<T, 48, 80, false>(s, p, st, lds_out, ru_out);
-    case 4 * 16 + 8: return launch_bwd_dims<T, 64, 128, false>(s, p, st, lds_out, ru_out);
+    case 1 * 16 + 2: return launch_bwd_dims<T, 16, 32, false, LR>(s, p, st, lds_out, ru_out);
+    case 2 * 16 + 4: return launch_bwd_dims<T, 32, 64, false, LR>(s, p, st, lds_out, ru_out);
+    case 3 * 16 + 5: return launch_bwd_dims<T, 48, 80, false, LR>(s, p, st, lds_out, ru_out);
+    case 4 * 16 + 8: return launch_bwd_dims<T, 64, 128, false, LR>(s, p, st, lds_out, ru_out);
     default: return hipErrorInvalidValue;
   }
 }

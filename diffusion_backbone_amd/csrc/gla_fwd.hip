@@ -45,6 +45,7 @@ GlaShape gla_plan(int B, int L, int H, int dk, int dv, int C, int bf16, int seg_
   GlaShape s;
   s.B = B; s.L = L; s.H = H; s.dk = dk; s.dv = dv; s.C = C; s.bf16 = bf16;
   s.ndk = s.ndv = 0;
+  s.lr = 0;
   gla_dim_class(dk, dv, &s.ndk, &s.ndv);
   s.NC = (L + C - 1) / C;
   int sc = seg_chunks;
@@ -142,17 +143,26 @@ hipError_t launch_gla_state_scan(const GlaShape& s, float* states, const float* 
 }
 
 // Chunk kernels, instantiated per element type in their own translation units.
-template <typename T>
+template <typename T, bool LR>
 hipError_t launch_gla_fwd_t(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out);
-extern template hipError_t launch_gla_fwd_t<bf16>(const GlaShape&, GlaFwdParams, hipStream_t,
-                                                  int*);
-extern template hipError_t launch_gla_fwd_t<float>(const GlaShape&, GlaFwdParams, hipStream_t,
-                                                   int*);
+extern template hipError_t launch_gla_fwd_t<bf16, false>(const GlaShape&, GlaFwdParams,
+                                                         hipStream_t, int*);
+extern template hipError_t launch_gla_fwd_t<float, false>(const GlaShape&, GlaFwdParams,
+                                                          hipStream_t, int*);
+extern template hipError_t launch_gla_fwd_t<bf16, true>(const GlaShape&, GlaFwdParams,
+                                                        hipStream_t, int*);
+
+// the kernels for the element type and key-gate form (the low-rank gate exists for bf16)
+static hipError_t fwd_kernels(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
+  if (s.lr)
+    return s.bf16 ? launch_gla_fwd_t<bf16, true>(s, p, st, lds_out) : hipErrorInvalidValue;
+  return s.bf16 ? launch_gla_fwd_t<bf16, false>(s, p, st, lds_out)
+                : launch_gla_fwd_t<float, false>(s, p, st, lds_out);
+}
 
 int gla_fwd_lds_bytes(const GlaShape& s) {
   int bytes = 0;
-  const hipError_t e = s.bf16 ? launch_gla_fwd_t<bf16>(s, GlaFwdParams{}, nullptr, &bytes)
-                              : launch_gla_fwd_t<float>(s, GlaFwdParams{}, nullptr, &bytes);
+  const hipError_t e = fwd_kernels(s, GlaFwdParams{}, nullptr, &bytes);
   return e == hipSuccess ? bytes : 0;
 }
 
@@ -199,8 +209,7 @@ hipError_t launch_gla_fwd(const GlaShape& s, GlaFwdParams p, hipStream_t st) {
     p.lb_status = lookback_status_word();
     if (!p.lb_status) return hipErrorInvalidSymbol;
   }
-  return s.bf16 ? launch_gla_fwd_t<bf16>(s, p, st, nullptr)
-                : launch_gla_fwd_t<float>(s, p, st, nullptr);
+  return fwd_kernels(s, p, st, nullptr);
 }
 
 }  // namespace dig

@@ -3,5 +3,5 @@
 #include "gla_fwd_kernel.h"
 
 namespace dig {
-template hipError_t launch_gla_fwd_t<bf16>(const GlaShape&, GlaFwdParams, hipStream_t, int*);
+template hipError_t launch_gla_fwd_t<bf16, false>(const GlaShape&, GlaFwdParams, hipStream_t, int*);
 }  // namespace dig

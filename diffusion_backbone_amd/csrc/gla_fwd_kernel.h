@@ -48,7 +48,10 @@ constexpr int al16(int x) { return (x + 15) / 16 * 16; }
 
 // PAD: raw staging rows at pitches the gate pass (one lane per token) reads without bank
 // conflicts (register-staged rows; LDS DMA writes them packed).
-template <typename T, int DK, int DV, int C, bool OUT, int NW = 4, bool PAD = false>
+// LR: the key gate is the rank-16 product formed in the gate pass (the staged z rows are the
+// 16-element factor rows; the head's slice of the up-projection sits in an LDS table).
+template <typename T, int DK, int DV, int C, bool OUT, int NW = 4, bool PAD = false,
+          bool LR = false>
 struct FwdLayout {
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
@@ -78,12 +81,16 @@ struct FwdLayout {
                                al16(OUT && !B_IN_K ? C * DK * 4 : 0);  // e^{b_last} [DKP]
   static constexpr int O_LG = O_GAM + al16(DKP * 4);                     // segment decay
   static constexpr int O_MAX = O_LG + al16(DKP * 4);                     // per-wave decay
-  static constexpr int O_RAW = O_MAX + 64;
+  static constexpr int O_ZT = O_MAX + 64;                 // low-rank gate table (LR)
+  static constexpr int O_RAW = O_ZT + al16(LR ? lowrank_table_bytes(16 * NDK) : 0);
+  // factor rows (LR): 16 elements at a 48-byte pitch when register-staged (conflict-free
+  // 16-byte reads, one lane per token), packed when DMA-staged
+  static constexpr int ZPE = PAD ? 24 : kGateRank;
   // one staging slot: raw k, z, v (+ q, r) rows at pitches KPE, VPE (elements; the runtime
   // widths when DMA-staged).  A padded pitch is kept only if it does not cost the second
   // workgroup per CU.
   static constexpr int slot_bytes(int kpe, int vpe) {
-    return al16(C * kpe * SZ) * 2 + al16(C * vpe * SZ) +
+    return al16(C * kpe * SZ) + al16(C * (LR ? ZPE : kpe) * SZ) + al16(C * vpe * SZ) +
            (OUT ? al16(C * kpe * SZ) + al16(C * vpe * SZ) : 0);
   }
   static constexpr int HALF_CU = 80 * 1024;
@@ -96,7 +103,7 @@ struct FwdLayout {
   static constexpr int VPE = PAD && fits(KPE, VPAD) ? VPAD : DV;
   static constexpr int R_K = 0;
   static constexpr int R_Z = R_K + al16(C * KPE * SZ);
-  static constexpr int R_V = R_Z + al16(C * KPE * SZ);
+  static constexpr int R_V = R_Z + al16(C * (LR ? ZPE : KPE) * SZ);
   static constexpr int R_Q = R_V + al16(C * VPE * SZ);
   static constexpr int R_R = R_Q + al16(OUT ? C * KPE * SZ : 0);
   static constexpr int SLOT = R_R + al16(OUT ? C * VPE * SZ : 0);
@@ -110,11 +117,14 @@ struct FwdLayout {
 //   S0(n) = U(n-1) + diag(e^{b_last(n-1)}) U(n-2) + diag(e^{b_last(n-1) + b_last(n-2)}) U(n-3) ...
 // which the query-row waves then use for (q e^b) S0.  Earlier chunks have lower workgroup
 // indices (dispatched first), every wait is bounded, and flags carry a per-call tag.
-template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW, bool LB = false>
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, int NW, bool LB = false,
+          bool LR = false>
 __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nbuf) {
   static_assert(!LB || OUT, "the look-back runs the output kernel");
+  static_assert(!LR || sizeof(T) == 2, "the low-rank gate is bf16");
   constexpr int NTH = 64 * NW;  // NW waves
-  using Lo = FwdLayout<T, DK, DV, C, OUT, NW, EXACT>;
+  using Lo = FwdLayout<T, DK, DV, C, OUT, NW, EXACT, LR>;
+  constexpr int ZPE = Lo::ZPE;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
@@ -179,8 +189,13 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     const int rbk = dk * (int)sizeof(T), rbv = dv * (int)sizeof(T);
     dma_rows_c(base + Lo::R_K, reinterpret_cast<const unsigned char*>(gk + row0 * dk), gsk, rbk,
                valid, wave, NW, lane);
-    dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk, rbk,
-               valid, wave, NW, lane);
+    if constexpr (LR)
+      dma_rows_c(base + Lo::R_Z,
+                 reinterpret_cast<const unsigned char*>(gz + ((long)b * p.L + t0) * kGateRank),
+                 kGateRank * sizeof(T), kGateRank * (int)sizeof(T), valid, wave, NW, lane);
+    else
+      dma_rows_c(base + Lo::R_Z, reinterpret_cast<const unsigned char*>(gz + row0 * dk), gsk,
+                 rbk, valid, wave, NW, lane);
     dma_rows_c(base + Lo::R_V, reinterpret_cast<const unsigned char*>(gv + row0 * dv), gsv, rbv,
                valid, wave, NW, lane);
     if (OUT && n >= c_first) {
@@ -191,14 +206,19 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     }
   };
   // exact shapes: the raw rows of a chunk in registers (loaded one iteration ahead)
-  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pk, pz, pq;
+  RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pk, pq;
+  RowRegs<(LR ? kGateRank : DK) * (int)sizeof(T), C, NTH, (LR ? ZPE : KPE) * (int)sizeof(T)> pz;
   RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv, pr;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
     const long gsk = (long)H * DK * sizeof(T), gsv = (long)H * DV * sizeof(T);
     pk.load(reinterpret_cast<const unsigned char*>(gk + row0 * DK), gsk, valid, tid);
-    pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
+    if constexpr (LR)
+      pz.load(reinterpret_cast<const unsigned char*>(gz + ((long)b * p.L + t0) * kGateRank),
+              kGateRank * sizeof(T), valid, tid);
+    else
+      pz.load(reinterpret_cast<const unsigned char*>(gz + row0 * DK), gsk, valid, tid);
     pv.load(reinterpret_cast<const unsigned char*>(gv + row0 * DV), gsv, valid, tid);
     if (OUT && n >= c_first) {
       pq.load(reinterpret_cast<const unsigned char*>(gq + row0 * DK), gsk, valid, tid);
@@ -223,6 +243,9 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
+  if constexpr (LR)  // read from the first chunk's gate pass on (behind the loop's barrier)
+    lowrank_table_fill<16 * NDK, NTH>(smem + Lo::O_ZT, static_cast<const bf16*>(p.zw), p.zb, h,
+                                      dk, tid);
 
   f32x4 sacc[STW];
 #pragma unroll
@@ -344,24 +367,39 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
     {
       const bool tv = tg < valid;
       T zr[NCL], kr[NCL], qr[NCL], vr[NEL];
-      if constexpr (FULLK) {
+      float zf[NCL];  // gate logits
+      if constexpr (LR) {  // formed and turned into log gates before the other rows are read
+        lowrank_logits<16 * NDK, NCL>(zf, reinterpret_cast<const bf16*>(rawz) + tg * ZPE,
+                                      smem + Lo::O_ZT, c0);
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+          const bool on = FULLK ? tv : (tv && c0 + j < dk);
+          bb[j] = keep_if(on, Fm<T>::lsig2(zf[j]) * inv_tau);
+          pin(bb[j]);
+        }
+      } else if constexpr (FULLK) {
         lds_row_read_k<T, NCL, KPE>(zr, rawz + tg * KPE, c0, tv);
+      } else {
+        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
+      }
+      if constexpr (FULLK) {
         lds_row_read_k<T, NCL, KPE>(kr, rawk + tg * KPE, c0, tv);
         if (emit) lds_row_read_k<T, NCL, KPE>(qr, rawq + tg * KPE, c0, tv);
       } else {
-        lds_row_read<T, NCL>(zr, rawz + tg * kp, c0, dk, tv, kp);
         lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
         if (emit) lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
       if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
       else lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
+      if constexpr (!LR) {
+#pragma unroll
+        for (int j = 0; j < NCL; ++j) {
+          const bool on = FULLK ? tv : (tv && c0 + j < dk);
+          bb[j] = keep_if(on, Fm<T>::lsig2(to_f(zr[j])) * inv_tau);
+        }
+      }
 
       float bl[NCL];
-#pragma unroll
-      for (int j = 0; j < NCL; ++j) {
-        const bool on = FULLK ? tv : (tv && c0 + j < dk);
-        bb[j] = on ? Fm<T>::lsig2(to_f(zr[j])) * inv_tau : 0.f;
-      }
 #pragma unroll
       for (int j = 0; j < NCL; ++j) bb[j] = scan_dpp<C>(bb[j]);
 #pragma unroll
@@ -770,20 +808,20 @@ constexpr int fwd_waves() {
 
 // LDS bytes and staging slots of one launch.  Exact shapes prefetch into registers (one
 // slot); tile classes use two DMA slots when a workgroup walks more than one chunk and they fit.
-template <typename T, int DK, int DV, bool EXACT, int C, bool OUT>
+template <typename T, int DK, int DV, bool EXACT, int C, bool OUT, bool LR>
 static void fwd_lds(const GlaShape& s, int* bytes, int* nbuf) {
-  using Lo = FwdLayout<T, DK, DV, C, OUT, fwd_waves<T, DK, DV, EXACT>(), EXACT>;
+  using Lo = FwdLayout<T, DK, DV, C, OUT, fwd_waves<T, DK, DV, EXACT>(), EXACT, LR>;
   const int walk = (OUT && s.prefix) ? s.NC : s.sc;
   *nbuf = (!EXACT && walk > 1 && Lo::bytes(2) <= kFwdLdsBudget) ? 2 : 1;
   *bytes = Lo::bytes(*nbuf);
 }
 
-template <typename T, int DK, int DV, bool EXACT, int C>
+template <typename T, int DK, int DV, bool EXACT, int C, bool LR>
 static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
   const long BH = (long)s.B * s.H;
   constexpr int NW = fwd_waves<T, DK, DV, EXACT>();
   int bytes_c, nbuf_c;
-  fwd_lds<T, DK, DV, EXACT, C, true>(s, &bytes_c, &nbuf_c);
+  fwd_lds<T, DK, DV, EXACT, C, true, LR>(s, &bytes_c, &nbuf_c);
   if (lds_out) {  // size query only
     *lds_out = bytes_c;
     return hipSuccess;
@@ -791,48 +829,48 @@ static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st
   if constexpr (EXACT) {
     if (s.lookback) {
       if (!p.lb_u || !p.lb_flag) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW, true>),
+      hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW, true, LR>),
                          dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), bytes_c, st, p, nbuf_c);
       return hipGetLastError();
     }
   }
   if (!s.prefix && s.nseg > 1) {
     int bytes_a, nbuf_a;
-    fwd_lds<T, DK, DV, EXACT, C, false>(s, &bytes_a, &nbuf_a);
-    hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false, NW>),
+    fwd_lds<T, DK, DV, EXACT, C, false, LR>(s, &bytes_a, &nbuf_a);
+    hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false, NW, false, LR>),
                        dim3((unsigned)(BH * (s.nseg - 1))), dim3(64 * NW), bytes_a, st, p,
                        nbuf_a);
     const hipError_t e = launch_gla_state_scan(s, p.states, p.seg_lg, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW>),
+  hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW, false, LR>),
                      dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), bytes_c, st, p, nbuf_c);
   return hipGetLastError();
 }
 
-template <typename T, int DK, int DV, bool EXACT>
+template <typename T, int DK, int DV, bool EXACT, bool LR>
 static hipError_t launch_fwd_dims(const GlaShape& s, GlaFwdParams p, hipStream_t st,
                                   int* lds_out) {
   switch (s.C) {
-    case 16: return launch_fwd_c<T, DK, DV, EXACT, 16>(s, p, st, lds_out);
-    case 32: return launch_fwd_c<T, DK, DV, EXACT, 32>(s, p, st, lds_out);
-    case 64: return launch_fwd_c<T, DK, DV, EXACT, 64>(s, p, st, lds_out);
+    case 16: return launch_fwd_c<T, DK, DV, EXACT, 16, LR>(s, p, st, lds_out);
+    case 32: return launch_fwd_c<T, DK, DV, EXACT, 32, LR>(s, p, st, lds_out);
+    case 64: return launch_fwd_c<T, DK, DV, EXACT, 64, LR>(s, p, st, lds_out);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Exact DiG head shapes (S: 32/64, XL: 36/72, and 16/32), else the enclosing tile class.
 // lds_out != nullptr: only report the LDS bytes of the output pass.
-template <typename T>
+template <typename T, bool LR>
 hipError_t launch_gla_fwd_t(const GlaShape& s, GlaFwdParams p, hipStream_t st, int* lds_out) {
-  if (s.dk == 32 && s.dv == 64) return launch_fwd_dims<T, 32, 64, true>(s, p, st, lds_out);
-  if (s.dk == 36 && s.dv == 72) return launch_fwd_dims<T, 36, 72, true>(s, p, st, lds_out);
-  if (s.dk == 16 && s.dv == 32) return launch_fwd_dims<T, 16, 32, true>(s, p, st, lds_out);
+  if (s.dk == 32 && s.dv == 64) return launch_fwd_dims<T, 32, 64, true, LR>(s, p, st, lds_out);
+  if (s.dk == 36 && s.dv == 72) return launch_fwd_dims<T, 36, 72, true, LR>(s, p, st, lds_out);
+  if (s.dk == 16 && s.dv == 32) return launch_fwd_dims<T, 16, 32, true, LR>(s, p, st, lds_out);
   switch (s.ndk * 16 + s.ndv) {
-    case 1 * 16 + 2: return launch_fwd_dims<T, 16, 32, false>(s, p, st, lds_out);
-    case 2 * 16 + 4: return launch_fwd_dims<T, 32, 64, false>(s, p, st, lds_out);
-    case 3 * 16 + 5: return launch_fwd_dims<T, 48, 80, false>(s, p, st, lds_out);
-    case 4 * 16 + 8: return launch_fwd_dims<T, 64, 128, false>(s, p, st, lds_out);
+    case 1 * 16 + 2: return launch_fwd_dims<T, 16, 32, false, LR>(s, p, st, lds_out);
+    case 2 * 16 + 4: return launch_fwd_dims<T, 32, 64, false, LR>(s, p, st, lds_out);
+    case 3 * 16 + 5: return launch_fwd_dims<T, 48, 80, false, LR>(s, p, st, lds_out);
+    case 4 * 16 + 8: return launch_fwd_dims<T, 64, 128, false, LR>(s, p, st, lds_out);
     default: return hipErrorInvalidValue;
   }
 }

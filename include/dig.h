@@ -142,6 +142,41 @@ dig_status dig_gla_bwd(const dig_gla_desc* desc, const void* q, const void* k, c
                        void* d_gate_logit, void* dr, float* d_norm_w, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * dig_gla_fwd_lowrank -- dig_gla_fwd with the key gate in its low-rank form (slides eq. (5):
+ * the gate logits are (x W_a1) W_a2 + b_alpha) formed inside the chunk kernels instead of read:
+ * for token t, head h and key column c
+ *   z = gate_bias[h d_k + c] + sum_{r < 16} gate_factor[t][r] * gate_w[h d_k + c][r]
+ * summed in fp32 from the bf16 products; the logits are never written to memory.
+ *   gate_factor : [B, L, 16] bf16, x W_a1 per token (shared by every head), 16-byte aligned
+ *   gate_w      : [H d_k][16] bf16, W_a2 as a linear layer's weight (out x in), 4-byte aligned
+ *   gate_bias   : [H d_k] fp32 b_alpha, 4-byte aligned, or NULL for zeros
+ *   gate_rank   : 16 (the only rank built: DIG_ERR_UNSUPPORTED otherwise)
+ * desc->dtype must be DIG_BF16 (DIG_ERR_UNSUPPORTED otherwise).  Everything else, errors
+ * included, as dig_gla_fwd; the gate inputs may not overlap the outputs.  `saved` feeds
+ * dig_gla_bwd_lowrank with the same inputs.  Workspace and saved sizes: dig_gla_fwd's.
+ */
+dig_status dig_gla_fwd_lowrank(const dig_gla_desc* desc, const void* q, const void* k,
+                               const void* v, const void* gate_factor, const void* gate_w,
+                               const float* gate_bias, int32_t gate_rank, const void* r,
+                               const float* norm_w, void* y, void* o_pre_opt, void* saved_opt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dig_gla_bwd_lowrank -- dig_gla_bwd for dig_gla_fwd_lowrank (same gate inputs, the logits
+ * formed again the same way).  d_gate_logit [B, L, H, d_k] is the gradient with respect to
+ * those logits z; the gradients of gate_factor, gate_w and gate_bias are its products with
+ * the up-projection's operands (a projection backward, not part of this call).  Workspace:
+ * dig_gla_bwd_workspace_bytes().
+ */
+dig_status dig_gla_bwd_lowrank(const dig_gla_desc* desc, const void* q, const void* k,
+                               const void* v, const void* gate_factor, const void* gate_w,
+                               const float* gate_bias, int32_t gate_rank, const void* r,
+                               const float* norm_w, const void* dy, const void* saved, void* dq,
+                               void* dk, void* dv, void* d_gate_logit, void* dr,
+                               float* d_norm_w, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* ------------------------------------------------------------------ projections */
 
 /*
@@ -216,7 +251,9 @@ dig_status dig_rmsnorm_modulate(int64_t rows, int32_t dim, int64_t rows_per_grou
  * "Architecture Details").  The GLA layer's projections read the block's normalised input:
  *   [q | k | v | u | r] = h W_in^T + b_in     (q, k: H*d_k; v, r: H*d_v; u: gate_rank)
  *   z = u W_gate^T + b_gate                    (gate logits, H*d_k; b_gate is b_alpha)
- * and the feedforward is dim -> ffn_dim -> dim with GELU between.
+ * and the feedforward is dim -> ffn_dim -> dim with GELU between.  With gate_rank 16 the
+ * logits z are formed inside the mixer's kernels (dig_gla_fwd_lowrank: fp32, never stored);
+ * with another rank a projection writes them (bf16) and dig_gla_fwd reads them.
  */
 typedef struct {
   int32_t batch, grid_h, grid_w; /* tokens per image L = grid_h * grid_w */

@@ -232,6 +232,14 @@ def linear(a, w, bias=None):
     return c
 
 
+def lowrank_gate_logits(factor, w, bias, heads: int, d_k: int):
+    """Gate logits of the low-rank key gate (slides eq. (5): (x W_a1) W_a2 + b_alpha):
+    z[b, t, h, c] = bias[h d_k + c] + sum_r factor[b, t, r] w[h d_k + c, r];
+    factor [B, L, R], w [H d_k, R] (out x in features), bias [H d_k] or None -> [B, L, H, d_k]."""
+    z = linear(factor, w, bias)
+    return z.reshape(z.shape[:-1] + (heads, d_k))
+
+
 # --------------------------------------------------------------------- DiG block
 def rmsnorm_modulate(x, scale, shift, eps: float = 1e-5):
     """h = RMSNorm(x) * scale + shift over the last axis; x [B, L, D], scale/shift [B, D]."""

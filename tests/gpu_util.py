@@ -52,8 +52,10 @@ def empty(shape, dtype: str, fill_nan: bool = True):
 
 
 def nbytes_buf(n: int):
+    """Workspace / saved buffer, every byte 0xFF (NaN in fp32 and bf16), so that a read of
+    an element nothing wrote shows up."""
     import torch
-    return torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+    return torch.full((max(int(n), 16),), 255, dtype=torch.uint8, device="cuda")
 
 
 def maxrel(got: np.ndarray, ref: np.ndarray) -> float:
@@ -72,8 +74,9 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved: bool = False,
                 want_opre: bool = True, gamma=True, tau: float = 16.0, q_scale: float = 1.0,
-                eps: float = 1e-5, ws=None):
-    """Runs dig_gla_fwd on the case; returns dict of device tensors."""
+                eps: float = 1e-5, ws=None, lowrank: W.LowRankGate | None = None):
+    """Runs dig_gla_fwd (dig_gla_fwd_lowrank with `lowrank`: the gate from its factor, W_a2
+    and bias instead of case.z) on the case; returns dict of device tensors."""
     import torch
     import diffusion_backbone_amd as dig
     cfg = case.cfg
@@ -81,7 +84,14 @@ def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved:
     dv = case.v.shape[-1]
     dt = cfg.dtype
     desc = dig.make_desc(B, L, H, dk, dv, chunk, tau, q_scale, eps, dt, seg_chunks)
-    d = {n: to_dev(getattr(case, n), dt) for n in ("q", "k", "v", "z", "r")}
+    d = {n: to_dev(getattr(case, n), dt) for n in ("q", "k", "v", "r")}
+    if lowrank is None:
+        d["z"] = to_dev(case.z, dt)
+    else:
+        d["z"] = to_dev(lowrank.factor, "bf16")
+        d["zw"] = to_dev(lowrank.w, "bf16")
+        d["zb"] = torch.from_numpy(lowrank.bias.astype(np.float32)).cuda()
+    d["lowrank"] = lowrank is not None
     d["gamma"] = torch.from_numpy(case.gamma.astype(np.float32)).cuda() if gamma else None
     d["y"] = empty((B, L, H, dv), dt)
     d["o_pre"] = empty((B, L, H, dv), dt) if want_opre else None
@@ -89,8 +99,12 @@ def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved:
     wsb = dig.dig_gla_fwd_workspace_bytes(desc)
     d["ws"] = (nbytes_buf(wsb) if wsb else None) if ws is None else ws  # may be reused
     assert d["ws"] is None or d["ws"].numel() >= wsb
-    dig.dig_gla_fwd(desc, d["q"], d["k"], d["v"], d["z"], d["r"], d["gamma"], d["y"],
-                    d["o_pre"], d["saved"], d["ws"], wsb)
+    if lowrank is None:
+        dig.dig_gla_fwd(desc, d["q"], d["k"], d["v"], d["z"], d["r"], d["gamma"], d["y"],
+                        d["o_pre"], d["saved"], d["ws"], wsb)
+    else:
+        dig.dig_gla_fwd_lowrank(desc, d["q"], d["k"], d["v"], d["z"], d["zw"], d["zb"], d["r"],
+                                d["gamma"], d["y"], d["o_pre"], d["saved"], d["ws"], wsb)
     d["desc"] = desc
     return d
 
@@ -109,7 +123,12 @@ def gla_backward(case: W.GLACase, fwd: dict, *, dgamma: bool = True, ws=None):
     wsb = dig.dig_gla_bwd_workspace_bytes(desc)
     g["ws"] = nbytes_buf(wsb) if ws is None else ws   # a caller's workspace may be reused
     assert g["ws"].numel() >= wsb
-    dig.dig_gla_bwd(desc, fwd["q"], fwd["k"], fwd["v"], fwd["z"], fwd["r"], fwd["gamma"], g["dy"],
-                    fwd["saved"], g["dq"], g["dk"], g["dv"], g["dz"], g["dr"], g["dgamma"],
-                    g["ws"], wsb)
+    if not fwd.get("lowrank"):
+        dig.dig_gla_bwd(desc, fwd["q"], fwd["k"], fwd["v"], fwd["z"], fwd["r"], fwd["gamma"],
+                        g["dy"], fwd["saved"], g["dq"], g["dk"], g["dv"], g["dz"], g["dr"],
+                        g["dgamma"], g["ws"], wsb)
+    else:
+        dig.dig_gla_bwd_lowrank(desc, fwd["q"], fwd["k"], fwd["v"], fwd["z"], fwd["zw"],
+                                fwd["zb"], fwd["r"], fwd["gamma"], g["dy"], fwd["saved"], g["dq"],
+                                g["dk"], g["dv"], g["dz"], g["dr"], g["dgamma"], g["ws"], wsb)
     return g

@@ -165,7 +165,9 @@ XL16 = W.cfg_replace(W.CONFIGS["dig_xl2_1024"], batch=1, grid_h=16, grid_w=16)
     (XL16, W.ROW, W.ROW_REV), (XL16, W.COL, W.COL_REV),
     (W.cfg_replace(S16, grid_h=9, grid_w=7), W.COL, W.COL_REV),       # ragged chunk, odd grid
     (W.cfg_replace(S16, chunk=16, grid_h=12, grid_w=20), W.ROW_REV, W.COL),
-], ids=["s_row", "s_rowrev", "s_col", "s_colrev", "xl_row", "xl_col", "s_ragged", "s_chunk16"])
+    (W.cfg_replace(S16, rank=8), W.ROW, W.COL),   # rank 8: the logits through a projection
+], ids=["s_row", "s_rowrev", "s_col", "s_colrev", "xl_row", "xl_col", "s_ragged", "s_chunk16",
+        "s_rank8"])
 def test_block_fwd_parity(cfg, d, dn):
     import torch
     import diffusion_backbone_amd as dig

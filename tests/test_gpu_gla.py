@@ -335,6 +335,20 @@ def test_bwd_bf16_shapes(name, batch, seq_len, chunk, seg):
     _check_bwd(case, g, TOL["bf16"])
 
 
+# head dims outside the exact DiG shapes run in the enclosing 16-wide tile class
+@pytest.mark.parametrize("dk,dv,chunk,seq_len,seg", [(20, 40, 16, 77, 0), (40, 72, 32, 150, 0),
+                                                     (64, 100, 32, 130, 0), (64, 100, 32, 130, 2),
+                                                     (64, 128, 16, 90, 0), (50, 80, 32, 70, 100)])
+def test_bwd_bf16_tile_classes(dk, dv, chunk, seq_len, seg):
+    announce("bwd tile class dk=%d dv=%d chunk=%d L=%d seg=%d" % (dk, dv, chunk, seq_len, seg))
+    cfg = W.cfg_replace(W.CONFIGS["dig_s2_256"], d_k=dk, d_v=dv)
+    case = W.make_gla_case(cfg, 7 + dk, batch=2, seq_len=seq_len, random_gamma=True)
+    f = gla_forward(case, chunk, seg_chunks=seg, want_saved=True)
+    _check_fwd(case, f, TOL["bf16"])
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["bf16"])
+
+
 @pytest.mark.parametrize("stress", ["long_memory", "fast_decay", "wide_logits", "extreme_decay"])
 @pytest.mark.parametrize("name", ["dig_s2_256", "dig_xl2_2048"])
 @pytest.mark.parametrize("seg", [2, 0])   # 0: five chunks, one per workgroup (look-back)

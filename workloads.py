@@ -176,6 +176,31 @@ def make_gla_case(cfg: Config, seed: int | None = None, *, batch: int | None = N
 
 
 @dataclass
+class LowRankGate:
+    factor: np.ndarray  # [B, L, rank]  x W_a1 per token
+    w: np.ndarray       # [H d_k, rank]  W_a2 as a linear layer's weight (out x in)
+    bias: np.ndarray    # [H d_k]        b_alpha (fp32 values)
+
+
+def make_lowrank_gate(cfg: Config, seed: int, *, batch: int | None = None,
+                      seq_len: int | None = None, w_std: float | None = None,
+                      bias_std: float = 0.0, bias_mean: float = 0.0) -> LowRankGate:
+    """Inputs of the low-rank key gate: the factor x W_a1 of unit-variance tokens (N(0, 1)
+    entries, as x ~ N(0,1) times weights ~ N(0, 1/D) gives), W_a2 ~ N(0, w_std^2) (default
+    1/D^(1/2), the projections' initialisation), b_alpha ~ N(bias_mean, bias_std^2).  A larger
+    w_std and a spread bias stress the gate (strong decays, saturated sigmoids)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B = cfg.batch if batch is None else batch
+    L = cfg.seq_len if seq_len is None else seq_len
+    hk = cfg.heads * cfg.d_k
+    std = 1.0 / np.sqrt(cfg.d_model) if w_std is None else w_std
+    factor = quantize(rng.standard_normal((B, L, cfg.rank)), "bf16")
+    w = quantize(rng.standard_normal((hk, cfg.rank)) * std, "bf16")
+    bias = f32_round(bias_mean + bias_std * rng.standard_normal(hk))
+    return LowRankGate(factor, w, bias)
+
+
+@dataclass
 class SREMCase:
     cfg: Config
     x: np.ndarray
