@@ -80,7 +80,9 @@ def gen_blocks(cfg, nblocks, seed):
         q = (x @ w(D, H * dk)).view(B, L, H, dk)
         k = (x @ w(D, H * dk)).view(B, L, H, dk)
         v = (x @ w(D, H * dv)).view(B, L, H, dv)
-        z = ((x @ w(D, cfg.rank)) @ w(cfg.rank, H * dk)).view(B, L, H, dk)
+        u = x @ w(D, cfg.rank)          # the low-rank gate's factor x W_a1
+        wa2 = w(cfg.rank, H * dk)
+        z = (u @ wa2).view(B, L, H, dk)
         r = (x @ w(D, H * dv)).view(B, L, H, dv)
         cw = torch.randn(D, 3, 3, device="cuda", generator=g) / 3.0
         dy = torch.randn(B, L, H, dv, device="cuda", generator=g)
@@ -88,18 +90,20 @@ def gen_blocks(cfg, nblocks, seed):
         bf = lambda t: t.to(torch.bfloat16).contiguous()
         blocks.append(dict(q=bf(q), k=bf(k), v=bf(v), z=bf(z), r=bf(r), x=bf(x.view(B, L, D)),
                            cw=cw.contiguous(), dy=bf(dy), dys=bf(dys),
-                           gamma=torch.ones(dv, device="cuda")))
-        del x, q, k, v, z, r, dy, dys
+                           gamma=torch.ones(dv, device="cuda"), u=bf(u.view(B, L, cfg.rank)),
+                           wa2=bf(wa2.t()), ba=torch.zeros(H * dk, device="cuda")))
+        del x, q, k, v, z, r, dy, dys, u
     return blocks
 
 
 class Path:
     """Buffers and the library calls of one step."""
 
-    def __init__(self, cfg, blocks, seg_chunks):
+    def __init__(self, cfg, blocks, seg_chunks, lowrank=False):
         import torch
         import diffusion_backbone_amd as dig
         self.dig, self.cfg, self.blocks = dig, cfg, blocks
+        self.lowrank = lowrank  # the gate formed in the chunk kernels from x W_a1 and W_a2
         B, L, H, dk, dv, D = cfg.batch, cfg.seq_len, cfg.heads, cfg.d_k, cfg.d_v, cfg.d_model
         self.desc = dig.make_desc(B, L, H, dk, dv, cfg.chunk, cfg.tau, 1.0, 1e-5, dig.DIG_BF16,
                                   seg_chunks)
@@ -123,6 +127,11 @@ class Path:
 
     def gla_fwd(self, l):
         b = self.blocks[l]
+        if self.lowrank:
+            self.dig.dig_gla_fwd_lowrank(self.desc, b["q"], b["k"], b["v"], b["u"], b["wa2"],
+                                         b["ba"], b["r"], b["gamma"], self.y[l], None,
+                                         self.saved[l], self.fws, self.fws_b)
+            return
         self.dig.dig_gla_fwd(self.desc, b["q"], b["k"], b["v"], b["z"], b["r"], b["gamma"],
                              self.y[l], None, self.saved[l], self.fws, self.fws_b)
 
@@ -139,6 +148,12 @@ class Path:
 
     def gla_bwd(self, l):
         b, g = self.blocks[l], self.g
+        if self.lowrank:
+            self.dig.dig_gla_bwd_lowrank(self.desc, b["q"], b["k"], b["v"], b["u"], b["wa2"],
+                                         b["ba"], b["r"], b["gamma"], b["dy"], self.saved[l],
+                                         g["dq"], g["dk"], g["dv"], g["dz"], g["dr"], self.dgamma,
+                                         self.bws, self.bws_b)
+            return
         self.dig.dig_gla_bwd(self.desc, b["q"], b["k"], b["v"], b["z"], b["r"], b["gamma"],
                              b["dy"], self.saved[l], g["dq"], g["dk"], g["dv"], g["dz"], g["dr"],
                              self.dgamma, self.bws, self.bws_b)
@@ -323,12 +338,13 @@ def srem_bytes_per_token(cfg, which):
     return (2 if which == "fwd" else 3) * cfg.d_model * 2
 
 
-def run_config(cfg, steps, warmup, seg_chunks=0, fwd_only=False, events=False):
-    """Times the step of one configuration; returns a dict (and the Path when events=True)."""
+def run_config(cfg, steps, warmup, seg_chunks=0, fwd_only=False, events=False, lowrank=False):
+    """Times the step of one configuration; returns a dict (and the Path when events=True).
+    lowrank: the mixer calls take the gate as x W_a1 and W_a2 (dig_gla_*_lowrank)."""
     import torch
     nb = n_blocks(cfg)
     blocks = gen_blocks(cfg, nb, cfg.seed)
-    path = Path(cfg, blocks, seg_chunks)
+    path = Path(cfg, blocks, seg_chunks, lowrank)
     torch.cuda.synchronize()
     tokens = cfg.batch * cfg.seq_len * nb
     out = {"workload": cfg.name, "batch": cfg.batch, "grid": [cfg.grid_h, cfg.grid_w],
@@ -353,6 +369,25 @@ def run_config(cfg, steps, warmup, seg_chunks=0, fwd_only=False, events=False):
         torch.cuda.empty_cache()
         return out, None
     return out, path
+
+
+def lowrank_gate(cfg, steps):
+    """The headline step with the key gate given as x W_a1 (16 per token) and W_a2, the logits
+    formed inside the chunk kernels (dig_gla_fwd_lowrank / dig_gla_bwd_lowrank), and one
+    block's calls of both gate forms timed back to back."""
+    import torch
+    res, path = run_config(cfg, steps, 3, events=True, lowrank=True)
+    calls = {}
+    for lr in (False, True):
+        path.lowrank = lr
+        key = "lowrank" if lr else "logits"
+        calls[key] = {"gla_fwd_us": round(_time_us(lambda: path.gla_fwd(0), reps=20), 2),
+                      "gla_bwd_us": round(_time_us(lambda: path.gla_bwd(0), reps=20), 2)}
+    res["calls"] = calls
+    res["gate_bytes_per_token"] = {"logits": 2 * cfg.heads * cfg.d_k, "lowrank": 2 * cfg.rank}
+    del path
+    torch.cuda.empty_cache()
+    return res
 
 
 def contraction_microbench():
@@ -455,10 +490,21 @@ def projections(cfg, steps):
         proj_out()
         dig.dig_dwconv3x3(B, cfg.grid_h, cfg.grid_w, D, dig.DIG_BF16, W.ROW, W.ROW_REV, yo, cw,
                           None, xs)
+    def layer_lowrank():
+        proj_in()
+        dig.dig_gla_fwd_lowrank(desc, q, k, v, zl, wa2, b_alpha, r, gamma, y, None, None, fws, fwb)
+        proj_out()
+        dig.dig_dwconv3x3(B, cfg.grid_h, cfg.grid_w, D, dig.DIG_BF16, W.ROW, W.ROW_REV, yo, cw,
+                          None, xs)
     ms = timed(layer, steps, 3)
     res["layer_fwd_with_projections"] = {
         "what": "in-projection, gate up-projection, dig_gla_fwd, out-projection, dig_dwconv3x3 "
                 "(fused reorient), one block", "ms": round(ms, 4),
+        "tokens_per_s": round(M / (ms / 1e3), 1)}
+    ms = timed(layer_lowrank, steps, 3)
+    res["layer_fwd_with_projections_lowrank_gate"] = {
+        "what": "in-projection, dig_gla_fwd_lowrank (gate logits formed in the chunk kernels), "
+                "out-projection, dig_dwconv3x3 (fused reorient), one block", "ms": round(ms, 4),
         "tokens_per_s": round(M / (ms / 1e3), 1)}
     res["workload"] = cfg.name
     return res
@@ -528,7 +574,8 @@ def block_stack(name, steps, warmup=2):
         forward()
     ms_graph = timed(graph.replay, steps, warmup)
     del graph
-    gemm = 2.0 * M * (D * nin + R * HK + HV * D + 2 * D * F)
+    fused = R == dig.DIG_GATE_RANK  # dig_block_fwd forms the gate logits in the mixer
+    gemm = 2.0 * M * (D * nin + (0 if fused else R * HK) + HV * D + 2 * D * F)
     out = {"what": "dig_block_cond + %d x dig_block_fwd (four scan directions cycling)" % nb,
            "batch": B, "grid": [cfg.grid_h, cfg.grid_w], "d_model": D, "heads": H, "d_k": dk,
            "d_v": dv, "ffn_dim": F, "blocks": nb, "ms_per_forward": round(ms, 4),
@@ -560,6 +607,9 @@ def block_stack(name, steps, warmup=2):
          2.0 * M * R * HK),
         ("gla_fwd", lambda: dig.dig_gla_fwd(gdesc, q, k, v, z, r, t["gla_norm_w"], y, None, None,
                                             gws, gwb), 0.0),
+        ("gla_fwd_lowrank", lambda: dig.dig_gla_fwd_lowrank(
+            gdesc, q, k, v, u, t["w_gate"], t["b_gate"], r, t["gla_norm_w"], y, None, None, gws,
+            gwb), 0.0),
         ("out_projection_gated_residual", lambda: dig.dig_linear(M, HV, y, [dig.linear_out(
             x1, t["w_out"], t["b_out"], res=x0, gate=mod[:, 2 * D:], gate_ld=mld,
             rows_per_gate=L)]), 2.0 * M * HV * D),
@@ -586,7 +636,9 @@ def block_stack(name, steps, warmup=2):
             x1, t["w_ffn2"], t["b_ffn2"], res=x1, gate=mod[:, 5 * D:], gate_ld=mld,
             rows_per_gate=L)], lws),
     }
-    steps_ = tuple((n, split.get(n, fn), fl) for n, fn, fl in steps_)
+    # the steps dig_block_fwd runs: rank 16 forms the gate logits inside the mixer
+    skip = ("gate_up_projection", "gla_fwd") if fused else ("gla_fwd_lowrank",)
+    steps_ = tuple((n, split.get(n, fn), fl) for n, fn, fl in steps_ if n not in skip)
     parts = {}
     for pname, fn, flops in steps_:
         pm = timed_graph(fn, max(5, steps))
@@ -595,7 +647,8 @@ def block_stack(name, steps, warmup=2):
             tf = flops / (pm / 1e3) / 1e12
             e.update(tflops=round(tf, 1), frac_of_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4))
         else:
-            e["gbs_in_out"] = round(2 * M * D * 2 / (pm / 1e3) / 1e9, 1) if pname != "gla_fwd" \
+            e["gbs_in_out"] = round(2 * M * D * 2 / (pm / 1e3) / 1e9, 1) \
+                if not pname.startswith("gla_fwd") \
                 else round(gla_bytes_per_token_head(cfg, "fwd") * M * H / (pm / 1e3) / 1e9, 1)
         parts[pname] = e
     out["one_block_parts"] = parts
@@ -921,6 +974,8 @@ def main():
                                           fwd_only=(name == "dig_xl2_1024"))
             print("[bench] %s done" % name, file=sys.stderr, flush=True)
         out["configs"] = configs
+        out["lowrank_gate"] = lowrank_gate(cfg, max(10, args.steps // 2))
+        print("[bench] lowrank_gate done", file=sys.stderr, flush=True)
         out["projections"] = projections(cfg, max(10, args.steps // 2))
         stacks = {}
         for sname in ("dig_s2_256_stack", "dig_xl2_256_stack", "dig_xl2_2048_stack"):
