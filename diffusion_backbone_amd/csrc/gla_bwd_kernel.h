@@ -520,14 +520,14 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     f32x4 s0p[STW];  // prefetch S0 of the next chunk down (consumed at the next top)
     // the next chunk's rows and S0 are loaded after the gate phase: issued here, in one burst
     // with the loads above from every wave, they held the gate phase up
+    // Issued on every chunk (the last one loads its own chunk again, unused): fixed load counts
+    // keep the compiler's waits for the loads issued before exact, where a conditional
+    // prefetch made them wait for everything outstanding, the prefetch included.
     auto prefetch_next = [&]() {
-      if constexpr (RD) {  // fixed load counts keep the compiler's wait for the loads exact
+      if constexpr (!LB) {  // (the look-back's workgroups hold one chunk)
         const int nn = max(n - 1, c_first);
         if constexpr (PF) pf_load(nn);
-        load_state(nn, s0p);
-      } else if (!LB && n > c_first) {  // (the look-back's workgroups hold one chunk)
-        if constexpr (PF) pf_load(n - 1);
-        if constexpr (FIN) load_state(n - 1, s0p);
+        if constexpr (FIN) load_state(nn, s0p);
       }
     };
 
@@ -859,10 +859,14 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         Acc dd = dvd[i];
-        dd += __shfl_xor(dd, 1);
-        dd += __shfl_xor(dd, 2);
-        dd += __shfl_xor(dd, 4);
-        dd += __shfl_xor(dd, 8);
+        if constexpr (kBf) {
+          dd = row_sum16(dd);  // DPP within the row of 16 lanes (no LDS permute)
+        } else {
+          dd += __shfl_xor(dd, 1);
+          dd += __shfl_xor(dd, 2);
+          dd += __shfl_xor(dd, 4);
+          dd += __shfl_xor(dd, 8);
+        }
         if ((own || RU) && r16 == 0) sDiag[hh * C + 16 * I + 4 * g4 + i] = (float)dd;
       }
     }
