@@ -104,11 +104,15 @@ struct BwdLayout {
   static constexpr int R_K = R_Q + bal16(C * KPE * SZ);
   static constexpr int R_Z = R_K + bal16(C * KPE * SZ);
   static constexpr int R_V = R_Z + bal16(C * KPE * SZ);
+  // r then dr, dy then dv: rows at a pitch that is a multiple of four elements when
+  // register-staged (the recompute phase reads them through the transpose load; the gate pass
+  // does not read them)
+  static constexpr int RPE = PAD ? (DV + 3) / 4 * 4 : DV;
   static constexpr int R_R = R_V + bal16(C * (VPE > 2 * KPE ? VPE : 2 * KPE) * SZ);  // v; dq|dk
-  static constexpr int R_DY = R_R + bal16(C * VPE * SZ);
+  static constexpr int R_DY = R_R + bal16(C * RPE * SZ);
   // factor rows (LR): 16 elements, packed (the final pass has no LDS left for a padded pitch)
   static constexpr int ZPE = kGateRank;
-  static constexpr int R_F = R_DY + bal16(C * VPE * SZ);
+  static constexpr int R_F = R_DY + bal16(C * RPE * SZ);
   static constexpr int SLOT = R_F + bal16(LR ? C * ZPE * SZ : 0);
   static constexpr int bytes = O_RAW + SLOT;
 };
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr bool PF = bwd_prefetch<DK, DV, EXACT, FIN, NW, RD>();
   constexpr bool LEAN = bwd_lean<T, DK, DV, C, FIN, NW, PF, LR>();
   using Lo = BwdLayout<T, DK, DV, C, FIN, LEAN, NW, PF, LR>;
-  constexpr int ZPE = Lo::ZPE;
+  constexpr int ZPE = Lo::ZPE, RPE = Lo::RPE;
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE, DKB = Lo::DKB;
   constexpr int NTH = 64 * NW;  // NW waves
   constexpr bool kBf = sizeof(T) == 2;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   const bf16* rawf = reinterpret_cast<const bf16*>(smem + Lo::O_RAW + Lo::R_F);  // factor (LR)
   T* rawv = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_V);  // then dq | dk
   // raw row pitches: padded for register-staged rows, the runtime widths for DMA-staged ones
-  const int kp = PF ? KPE : dk, vp = PF ? VPE : dv;
+  const int kp = PF ? KPE : dk, vp = PF ? VPE : dv, rp = PF ? RPE : dv;
   T* sdqs = rawv;
   T* sdks = rawv + C * kp;
   T* sRr = reinterpret_cast<T*>(smem + Lo::O_RAW + Lo::R_R);   // r, then dr
@@ -324,7 +328,8 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 
   RowRegs<DK * (int)sizeof(T), C, NTH, KPE * (int)sizeof(T)> pq, pk;
   RowRegs<(LR ? kGateRank : DK) * (int)sizeof(T), C, NTH, (LR ? ZPE : KPE) * (int)sizeof(T)> pz;
-  RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv, pr, pdy;
+  RowRegs<DV * (int)sizeof(T), C, NTH, VPE * (int)sizeof(T)> pv;
+  RowRegs<DV * (int)sizeof(T), C, NTH, RPE * (int)sizeof(T)> pr, pdy;
   auto pf_load = [&](int n) {
     const int t0 = n * C, valid = min(C, p.L - t0);
     const long row0 = ((long)b * p.L + t0) * H + h;
@@ -751,17 +756,33 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           oacc[Eh][i] = 16 * I + 4 * g4 + i < valid ? obr[Eh].v[i] : 0.f;
 
       // output-stage backward: r, dy first (one LDS round trip); value tiles past this
-      // half's range (an odd tile count) count as zero columns
+      // half's range (an odd tile count) count as zero columns.  Register-staged bf16 rows
+      // (pitch a multiple of 4): a tile whose 16 columns all lie inside the row comes through
+      // the transpose load (the lane's four rows of its column in one 8-byte read)
 #pragma unroll
-      for (int Eh = 0; Eh < NDVH; ++Eh)
+      for (int Eh = 0; Eh < NDVH; ++Eh) {
+        if constexpr (kBf && PF) {
+          if (16 * (E0 + Eh) + 16 <= DV) {
+            const bf16x4 r4 = lds_tr4(sRr, RPE, 16 * (E0 + Eh), 16 * I + 4 * g4, r16);
+            const bf16x4 y4 = lds_tr4(sDy, RPE, 16 * (E0 + Eh), 16 * I + 4 * g4, r16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool on = 16 * I + 4 * g4 + i < valid;  // stale rows: 0
+              rr[Eh][i] = on ? r4[i] : from_f<T>(0.f);
+              dyr[Eh][i] = on ? y4[i] : from_f<T>(0.f);
+            }
+            continue;
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = (E0 + Eh) * 16 + r16, row = 16 * I + 4 * g4 + i;
           const bool on = E0 + Eh < NDV && (FULLV || e < dv) && row < valid;  // stale rows: 0
-          rr[Eh][i] = on ? sRr[row * vp + e] : from_f<T>(0.f);
-          dyr[Eh][i] = on ? sDy[row * vp + e] : from_f<T>(0.f);
+          rr[Eh][i] = on ? sRr[row * rp + e] : from_f<T>(0.f);
+          dyr[Eh][i] = on ? sDy[row * rp + e] : from_f<T>(0.f);
           if (E0 + Eh >= NDV) oacc[Eh][i] = 0.f;
         }
+      }
       }  // !RD
     }
     if (part && !RD) {
@@ -784,7 +805,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           const float sg = Fm<T>::sig(rv), sw = rv * sg;
           if (col_on) {
             if (dg_here) dgl[Eh] += dyv * nv * sw;
-            if (own || RU) sRr[row * vp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
+            if (own || RU) sRr[row * rp + e] = from_f<T>(dyv * nv * gmE * sg * (1.f + rv * (1.f - sg)));
           }
           dn[Eh][i] = dyv * gmE * sw;
           md[i] += dn[Eh][i] * nv;
@@ -834,7 +855,16 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         for (int i = 0; i < 4; ++i) dof[Eh].v[i] = from_f<T>(0.f);
         if (E0 + Eh < NDV) {
           const int e = (E0 + Eh) * 16 + r16;
-          T dov4[4];
+          T dov4[4], v4[4];
+          if constexpr (kBf) {  // the lane's four rows of v in one transpose load
+            const bf16x4 t4 = lds_tr4(reinterpret_cast<const bf16*>(sV), VP, 16 * (E0 + Eh),
+                                      16 * I + 4 * g4, r16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = t4[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = sV[(16 * I + 4 * g4 + i) * VP + e];
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = 16 * I + 4 * g4 + i;
@@ -843,7 +873,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
             dov4[i] = from_f<T>(dov);
             dof[Eh].v[i] = dov4[i];
             if constexpr (!LEAN && FIN) sdO[row * VP + e] = dov4[i];  // for D = dO V^T
-            dvd[i] += (Acc)dov * (Acc)to_f(sV[row * VP + e]);
+            dvd[i] += (Acc)dov * (Acc)to_f(v4[i]);
           }
           lds_row_write<T, 4>(sdOt + e * TP, 16 * I + 4 * g4, dov4);
         }
@@ -1089,7 +1119,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
           }
           if (FULLV || e < dv) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * vp + e] = from_f<T>(dva[i]);
+            for (int i = 0; i < 4; ++i) sDy[(16 * J + 4 * g4 + i) * rp + e] = from_f<T>(dva[i]);
           }
         }
       }
@@ -1112,7 +1142,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     if constexpr (RU && !FIN) {  // pass A emits dr (the reading final pass has no r)
       T* gdr = static_cast<T*>(p.dr);
       if constexpr (PF) {
-        constexpr int RV = DV * (int)sizeof(T), LV = VPE * (int)sizeof(T);
+        constexpr int RV = DV * (int)sizeof(T), LV = RPE * (int)sizeof(T);
         store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<unsigned char*>(gdr + row0 * DV),
                                          (long)H * RV, reinterpret_cast<const unsigned char*>(sRr),
                                          valid, tid);
@@ -1163,7 +1193,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       if constexpr (PF) {
         constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
         using UC = unsigned char;
-        constexpr int LK = KPE * (int)sizeof(T), LV = VPE * (int)sizeof(T);
+        constexpr int LK = KPE * (int)sizeof(T), LV = RPE * (int)sizeof(T);
         store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
                                          reinterpret_cast<const UC*>(sdqs), valid, tid);
         store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
