@@ -71,8 +71,12 @@ struct FwdLayout {
   static constexpr int O_Q = 0;                                         // q e^{b}  [C][QKP]
   static constexpr int O_K = O_Q + al16(OUT ? C * QKP * 4 : 0);          // k e^{-b} [C][QKP]
   static constexpr int O_KBT = O_K + al16(OUT ? C * QKP * 4 : 0);        // kbar^T [16NDK][TP]
+  // VTR: the products read V from the staged rows through the transpose load (register-staged
+  // bf16 rows, padded to DVP zero columns), so the gate pass writes no V^T copy; the token
+  // dimension is a contraction over whole 32-token steps, so the chunk must hold them (32, 64)
+  static constexpr bool VTR = PAD && SZ == 2 && C % 32 == 0;
   static constexpr int O_VT = O_KBT + al16(16 * NDK * TP * SZ);          // v^T    [DVP][TP]
-  static constexpr int O_S = O_VT + al16(DVP * TP * SZ);                 // S^T    [DVP][QP]
+  static constexpr int O_S = O_VT + al16(VTR ? 0 : DVP * TP * SZ);       // S^T    [DVP][QP]
   // b fp32 [C][DK], written only for strong-decay chunks, which do not read k e^{-b}: it
   // takes that tile's place when it fits there
   static constexpr bool B_IN_K = C * DK * 4 <= C * QKP * 4;
@@ -100,7 +104,7 @@ struct FwdLayout {
   static constexpr int KPAD = row_pitch(DK * SZ, NCL * SZ) / SZ;
   static constexpr int VPAD = row_pitch(DV * SZ, NEL * SZ) / SZ;
   static constexpr int KPE = PAD && fits(KPAD, DV) ? KPAD : DK;
-  static constexpr int VPE = PAD && fits(KPE, VPAD) ? VPAD : DV;
+  static constexpr int VPE = VTR ? DVP : (PAD && fits(KPE, VPAD) ? VPAD : DV);
   static constexpr int R_K = 0;
   static constexpr int R_Z = R_K + al16(C * KPE * SZ);
   static constexpr int R_V = R_Z + al16(C * (LR ? ZPE : KPE) * SZ);
@@ -125,6 +129,7 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   constexpr int NTH = 64 * NW;  // NW waves
   using Lo = FwdLayout<T, DK, DV, C, OUT, NW, EXACT, LR>;
   constexpr int ZPE = Lo::ZPE;
+  constexpr bool VTR = Lo::VTR;  // V through the transpose load from the staged rows
   constexpr int KPE = Lo::KPE, VPE = Lo::VPE;
   constexpr bool kBf = sizeof(T) == 2;
   constexpr int NDK = Lo::NDK, NDV = Lo::NDV, DKP = Lo::DKP, DVP = Lo::DVP, CK = Lo::CK;
@@ -238,9 +243,10 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   if constexpr (PF) pf_load(n_begin);
   else issue(n_begin, 0);  // the first chunk's copy overlaps the set-up below
 
-  // zero everything but the staging slots: padding rows/columns of the MFMA operands must
-  // read as zero and are never written afterwards
-  for (int i = tid; i < Lo::O_RAW / 16; i += NTH)
+  // zero everything but the staging slots (with VTR the slot too: the V rows' padding columns
+  // are operands): padding rows/columns of the MFMA operands must read as zero and are never
+  // written afterwards
+  for (int i = tid; i < (VTR ? Lo::bytes(1) : Lo::O_RAW) / 16; i += NTH)
     reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();  // the zero fill is complete before anything below writes LDS
   if constexpr (LR)  // read from the first chunk's gate pass on (behind the loop's barrier)
@@ -389,8 +395,12 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         lds_row_read<T, NCL>(kr, rawk + tg * kp, c0, dk, tv, kp);
         if (emit) lds_row_read<T, NCL>(qr, rawq + tg * kp, c0, dk, tv, kp);
       }
-      if constexpr (FULLV) lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
-      else lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
+      if constexpr (VTR) {
+      } else if constexpr (FULLV) {
+        lds_row_read_k<T, NEL, VPE>(vr, rawv + tg * VPE, e0, tv);
+      } else {
+        lds_row_read<T, NEL>(vr, rawv + tg * vp, e0, dv, tv, vp);
+      }
       if constexpr (!LR) {
 #pragma unroll
         for (int j = 0; j < NCL; ++j) {
@@ -423,8 +433,10 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
 #pragma unroll
       for (int j = 0; j < NCL; ++j)
         if (FULLK || c0 + j < 16 * NDK) sKbT[(c0 + j) * TP + tg] = kb[j];
+      if constexpr (!VTR) {
 #pragma unroll
-      for (int j = 0; j < NEL; ++j) sVt[(e0 + j) * TP + tg] = vr[j];  // V^T, zero past the end
+        for (int j = 0; j < NEL; ++j) sVt[(e0 + j) * TP + tg] = vr[j];  // V^T, zero past the end
+      }
       if (emit) {
         if (c0 < QKC) {  // a lane's column run lies wholly inside or past the stored columns
           lds_row_write<float, NCL>(sQ + tg * QKP, c0, qs);
@@ -468,7 +480,11 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + ct * 16 + g4 * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sacc[m][i] *= gam[i];
-        sacc[m] = Mma<T>::kc(sacc[m], sKbT, TP, 16 * ct, sVt, TP, 16 * et, CK, lane);
+        if constexpr (VTR)
+          sacc[m] = Mma<T>::template mm<true, false>(sacc[m], sKbT, TP, 16 * ct, rawv, VPE,
+                                                     16 * et, CK, lane);
+        else
+          sacc[m] = Mma<T>::kc(sacc[m], sKbT, TP, 16 * ct, sVt, TP, 16 * et, CK, lane);
       }
     }
     if constexpr (LB) {  // publish U (sacc started from zero) and the chunk's decay factors
@@ -582,9 +598,15 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
             }
 #pragma unroll
             for (int E = 0; E < NDV; ++E) {
-              const T* vb = sVt + (E * 16 + r16) * TP + 32 * pp + 4 * g4;
-              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vb);
-              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vb + 16);
+              bf16x4 lo, hi;
+              if constexpr (VTR) {  // tokens 32pp + 4g4.. and +16 of value column 16E + r16
+                lo = lds_tr4(rawv, VPE, 16 * E, 32 * pp + 4 * g4, r16);
+                hi = lds_tr4(rawv, VPE, 16 * E, 32 * pp + 16 + 4 * g4, r16);
+              } else {
+                const T* vb = sVt + (E * 16 + r16) * TP + 32 * pp + 4 * g4;
+                lo = *reinterpret_cast<const bf16x4*>(vb);
+                hi = *reinterpret_cast<const bf16x4*>(vb + 16);
+              }
               bf16x8 bv;
 #pragma unroll
               for (int i = 0; i < 4; ++i) { bv[i] = lo[i]; bv[4 + i] = hi[i]; }
