@@ -93,8 +93,8 @@ struct BwdLayout {
   static constexpr int O_GAM = O_W + bal16(FIN ? C * DKB * 4 : 0);   // e^{b_last}  [DKP]
   static constexpr int O_LG = O_GAM + bal16(DKP * 4);                // b_last / segment decay
   static constexpr int O_MAX = O_LG + bal16(DKP * 4);                // per-wave decay [NW]
-  static constexpr int O_PART = O_MAX + 64;                          // [NDV][DKP]
-  static constexpr int O_DG = O_PART + bal16(NDV * DKP * 4);         // [NW][DVP]
+  static constexpr int O_PART = O_MAX + 64;                          // [DKP][8]
+  static constexpr int O_DG = O_PART + bal16(DKP * 8 * 4);           // [NW][DVP]
   static constexpr int O_DIAG = O_DG + bal16(NW * DVP * 4);          // [2][C] (halves)
   static constexpr int O_XCH = O_DIAG + bal16(2 * C * 4);            // [4][C] row sums
   static constexpr int O_ZT = O_XCH + bal16(4 * C * 4);              // low-rank gate table
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float part = row_sum16(se[m][i] * gacc[m][i]);
-          if (r16 == 0) sPart[et * DKP + ct * 16 + g4 * 4 + i] = part;
+          if (r16 == 0) sPart[(ct * 16 + g4 * 4 + i) * 8 + et] = part;  // (key, value tile)
         }
       }
     }
@@ -1152,6 +1152,26 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
     }
 
     if (own) {
+      if constexpr (PF) {
+        // dq, dk, dv (and dr) are complete in LDS (the barrier above): their stores go out
+        // first and overlap the dlog(alpha) phase, which writes only the z rows
+        T* gdq = static_cast<T*>(p.dq);
+        T* gdk = static_cast<T*>(p.dk_);
+        T* gdv = static_cast<T*>(p.dv_);
+        T* gdr = static_cast<T*>(p.dr);
+        constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
+        using UC = unsigned char;
+        constexpr int LK = KPE * (int)sizeof(T), LV = RPE * (int)sizeof(T);
+        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
+                                         reinterpret_cast<const UC*>(sdqs), valid, tid);
+        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
+                                         reinterpret_cast<const UC*>(sdks), valid, tid);
+        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
+                                         reinterpret_cast<const UC*>(sDy), valid, tid);
+        if constexpr (!RD)
+          store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
+                                           reinterpret_cast<const UC*>(sRr), valid, tid);
+      }
       // ---- dlog(alpha) = suffix sums of q.dq - k.dk (lanes = tokens in reverse order, DPP
       // prefix scan) + the boundary term; dz = dlog(alpha) sigmoid(-z) / tau, over raw z
       const int tr = C - 1 - tg;
@@ -1169,7 +1189,7 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       for (int j = 0; j < NCL; ++j) {
         float s = 0.f;
 #pragma unroll
-        for (int et = 0; et < NDV; ++et) s += sPart[et * DKP + c0 + j];
+        for (int et = 0; et < NDV; ++et) s += sPart[(c0 + j) * 8 + et];  // one row of 8
         bterm[j] = s;
       }
 #pragma unroll
@@ -1185,26 +1205,17 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         }
       }
       __syncthreads();
+      T* gdz = static_cast<T*>(p.dz);
       T* gdq = static_cast<T*>(p.dq);
       T* gdk = static_cast<T*>(p.dk_);
-      T* gdz = static_cast<T*>(p.dz);
       T* gdv = static_cast<T*>(p.dv_);
       T* gdr = static_cast<T*>(p.dr);
       if constexpr (PF) {
-        constexpr int RK = DK * (int)sizeof(T), RV = DV * (int)sizeof(T);
+        constexpr int RK = DK * (int)sizeof(T);
         using UC = unsigned char;
-        constexpr int LK = KPE * (int)sizeof(T), LV = RPE * (int)sizeof(T);
-        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdq + row0 * DK), (long)H * RK,
-                                         reinterpret_cast<const UC*>(sdqs), valid, tid);
-        store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdk + row0 * DK), (long)H * RK,
-                                         reinterpret_cast<const UC*>(sdks), valid, tid);
+        constexpr int LK = KPE * (int)sizeof(T);
         store_rows_fixed<RK, C, NTH, LK>(reinterpret_cast<UC*>(gdz + row0 * DK), (long)H * RK,
                                          reinterpret_cast<const UC*>(rawz), valid, tid);
-        store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdv + row0 * DV), (long)H * RV,
-                                         reinterpret_cast<const UC*>(sDy), valid, tid);
-        if constexpr (!RD)
-          store_rows_fixed<RV, C, NTH, LV>(reinterpret_cast<UC*>(gdr + row0 * DV), (long)H * RV,
-                                           reinterpret_cast<const UC*>(sRr), valid, tid);
       } else {
         store_rows<T>(gdq + row0 * dk, (long)H * dk, sdqs, dk, valid, dk, tid, NTH);
         store_rows<T>(gdk + row0 * dk, (long)H * dk, sdks, dk, valid, dk, tid, NTH);
