@@ -719,13 +719,22 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
       if constexpr (LB) q_s0(oacc, I);
       // output stage: head-wise RMSNorm x weight x Swish(r), stored from the accumulators
       T rr[NDV][4];  // all of this lane's r first (one LDS round trip)
+      if constexpr (VTR) {  // the lane's four rows of each column tile in one transpose load
 #pragma unroll
-      for (int E = 0; E < NDV; ++E)
+        for (int E = 0; E < NDV; ++E) {  // (the rows' padding columns read as zero)
+          const bf16x4 r4 = lds_tr4(sR, VPE, 16 * E, 16 * I + 4 * g4, r16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = E * 16 + r16;
-          rr[E][i] = (FULLV || e < dv) ? sR[(16 * I + 4 * g4 + i) * vp + e] : from_f<T>(0.f);
+          for (int i = 0; i < 4; ++i) rr[E][i] = r4[i];
         }
+      } else {
+#pragma unroll
+        for (int E = 0; E < NDV; ++E)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = E * 16 + r16;
+            rr[E][i] = (FULLV || e < dv) ? sR[(16 * I + 4 * g4 + i) * vp + e] : from_f<T>(0.f);
+          }
+      }
       float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int E = 0; E < NDV; ++E)
