@@ -61,7 +61,10 @@ struct FwdLayout {
   static constexpr int QP = DKP + 8, TP = CK + 8;              // padded LDS row pitches
   // gate columns per lane: the key columns up to the last 16-wide tile (the K-step padding
   // past it stays zero and is never touched), the value columns
-  static constexpr int NCL = 16 * NDK * C / (64 * NW), NEL = DVP * C / (64 * NW);
+  // (exact head shapes whose d_k splits evenly over the lanes cover the true columns only: the
+  // padding columns of the key tiles stay at their zero fill)
+  static constexpr int GCOLS = PAD && (DK * C) % (64 * NW) == 0 ? DK : 16 * NDK;
+  static constexpr int NCL = GCOLS * C / (64 * NW), NEL = DVP * C / (64 * NW);
   // q e^{b} and k e^{-b} are kept in fp32 for either element type (bf16 I/O splits them into
   // hi + lo bf16 fragments for the gated Q K^T): QKC stored columns (the true d_k for exact
   // head shapes, the 16-wide tile class otherwise) at pitch QKP floats
