@@ -60,7 +60,11 @@ struct BwdLayout {
   static constexpr int NDK = (DK + 15) / 16, NDV = (DV + 15) / 16;
   static constexpr int DKP = 16 * NDK, DVP = 16 * NDV;           // contraction pads (K 16)
   static constexpr int QP = DKP + 8, VP = DVP + 8, TP = C + 8;    // padded row pitches
-  static constexpr int NCL = DKP * C / (64 * NW), NEL = DVP * C / (64 * NW);  // gate columns
+  // gate columns per lane: the key tiles' columns over the lanes' column groups, rounded up
+  // (short chunks have more groups than columns: the groups past the tiles do nothing)
+  static constexpr int NGRP = 64 * NW / C;
+  static constexpr int NCL = (DKP + NGRP - 1) / NGRP;
+  static constexpr int NEL = (DVP + NGRP - 1) / NGRP;  // value columns per lane (V rows)
   // the row layouts of q e^{b}, k e^{-b} are fp32 for either element type (bf16 I/O splits
   // them into hi + lo bf16 fragments for the gated Q K^T): QKC stored columns (d_k rounded up
   // to 4) at pitch QKP floats; the transposed copies are of the element type
@@ -182,10 +186,12 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   constexpr int NST = NDK * NDV, STW = (NST + NW - 1) / NW;
   constexpr int NPAIR = NT * NDK, PRW = (NPAIR + NW - 1) / NW;  // dq/dk (row tile, key tile)
   constexpr int NDVT = NT * NDV, DVW = (NDVT + NW - 1) / NW;    // dv (row tile, value tile)
-  constexpr int NCL = DKP * C / NTH;                         // gate: key columns per lane
-  constexpr int NEL = DVP * C / NTH;                         // gate: value columns per lane
+  constexpr int NCL = Lo::NCL;                               // gate: key columns per lane
+  constexpr int NEL = Lo::NEL;                               // gate: value columns per lane
   constexpr bool FULLK = EXACT && DK == DKP, FULLV = EXACT && DV == DVP;
   static_assert(NCL >= 1 && NEL >= 1, "tile split");
+  static_assert(NCL * (NTH / C) >= DKP && NEL * (NTH / C) >= DVP, "the gate pass covers every column");
+  constexpr bool KOVER = NCL * (NTH / C) > DKP;  // column groups past the key tiles (short chunks)
   static_assert(QKC % NCL == 0 || QKC >= DKP, "gate column runs end at the stored columns");
   using Acc = typename std::conditional<kBf, float, double>::type;
   constexpr int RNDVH = (NDV + bwd_spl<C, NW>() - 1) / bwd_spl<C, NW>();  // reuse fragments
@@ -602,10 +608,16 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
         lds_row_write<float, NCL>(sQ + tg * QKP, c0, qf);
         lds_row_write<float, NCL>(sK + tg * QKP, c0, kf);
       }
-      lds_row_write<T, NEL>(sV + tg * VP, e0, vr);
+      if constexpr (NEL * (NTH / C) == DVP) {
+        lds_row_write<T, NEL>(sV + tg * VP, e0, vr);
+      } else {  // more column groups than value columns (short chunks): up to the tiles' end
+#pragma unroll
+        for (int j = 0; j < NEL; ++j)
+          if (e0 + j < DVP) sV[tg * VP + e0 + j] = vr[j];
+      }
 #pragma unroll
       for (int j = 0; j < NCL; ++j) {
-        if (FULLK || c0 + j < 16 * NDK) {
+        if ((FULLK && !KOVER) || c0 + j < DKP) {  // (groups past the key tiles: nothing)
           sQt[(c0 + j) * TP + tg] = qs[j];
           if constexpr (FIN) sKt[(c0 + j) * TP + tg] = ks[j];
         }
@@ -615,11 +627,13 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
       if (tg == C - 1) {
 #pragma unroll
         for (int j = 0; j < NCL; ++j) {
-          sGam[c0 + j] = Fm<T>::exp2(bl[j]);
-          if (FIN)
-            sLg[c0 + j] = bl[j];  // this chunk's log2 decay, for the e^{b_last - b} factors
-          else
-            sLg[c0 + j] += bl[j];  // segment's log2 decay
+          if (!KOVER || c0 + j < DKP) {
+            sGam[c0 + j] = Fm<T>::exp2(bl[j]);
+            if (FIN)
+              sLg[c0 + j] = bl[j];  // this chunk's log2 decay, for the e^{b_last - b} factors
+            else
+              sLg[c0 + j] += bl[j];  // segment's log2 decay
+          }
         }
       }
     }

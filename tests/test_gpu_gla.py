@@ -325,6 +325,8 @@ def test_bwd_tiny_f32(chunk, seg):
     ("dig_xl2_2048", 1, 256, 64, 0),   # the 16x16 crop of the 2048-px config
     ("dig_xl2_2048", 1, 256, 64, 1),
     ("dig_xl2_2048", 1, 999, 32, 3),
+    ("dig_xl2_2048", 1, 150, 16, 0),   # XL at chunk 16: more column groups than key columns
+    ("dig_xl2_2048", 1, 300, 16, 4),
 ])
 def test_bwd_bf16_shapes(name, batch, seq_len, chunk, seg):
     announce("bwd %s B=%d L=%d chunk=%d seg=%d" % (name, batch, seq_len, chunk, seg))
