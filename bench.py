@@ -242,14 +242,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 115314.3 KiB / 0.50008 + 91570.0 KiB / 1.0, segment scan 1666.7 + 2594.2,
-        # final pass 95167.0 + 94370.3 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
+        # pass A 115310.9 KiB / 0.50007 + 91441.4 KiB / 1.0, segment scan 1666.7 + 2594.2,
+        # final pass 95167.9 + 92217.7 (FETCH_SIZE, WRITE_SIZE; copy: 131091.5 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 627473448,
-        # pass A 79447.7 + 5099.5, state scan 2819.1 + 5184.0, output pass 67964.5 + 156784.1
-        "dig_gla_fwd": 478704917,
+        "dig_gla_bwd": 625132891,
+        # pass A 79429.4 + 5099.5, state scan 2819.1 + 5184.0, output pass 68181.8 + 157010.7
+        "dig_gla_fwd": 479344505,
     },
-    "sources_sha256": "bd8bb2155df3f7df9573e0138e318329e0fe9f45ff3379878e213f110eb57728",
+    "sources_sha256": "db2c008d8aea51eb9d1550aae91c695718d911b4df040b8a47a4261a2166df26",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
