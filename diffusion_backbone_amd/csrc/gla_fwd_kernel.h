@@ -357,8 +357,10 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
         if (wave >= SW0 && u < NST) {
           const int ct = u / NDV, et = u - ct * NDV;
           const int e = et * 16 + r16;
+          T s4[4];  // the lane's four key rows of column e: one 8-byte write
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sS[e * QP + ct * 16 + g4 * 4 + i] = from_f<T>(sacc[m][i]);
+          for (int i = 0; i < 4; ++i) s4[i] = from_f<T>(sacc[m][i]);
+          lds_row_write<T, 4>(sS + e * QP, ct * 16 + g4 * 4, s4);
         }
       }
     }
