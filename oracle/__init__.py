@@ -59,6 +59,9 @@ def _load():
                                               D, D, D, D, D, D]
         lib.oref_gla_bwd.argtypes = [i, i, i, i, i, D, D, D, D, D, D, d, d, d, D,
                                      D, D, D, D, D, D]
+        lib.oref_gla_fwd_beta.argtypes = [i, i, i, i, i, D, D, D, D, D, D, D, d, d, d, D, D, D]
+        lib.oref_gla_bwd_beta.argtypes = [i, i, i, i, i, D, D, D, D, D, D, D, d, d, d, D,
+                                          D, D, D, D, D, D, D]
         lib.oref_scan_canonical.argtypes = [i, i64, i64, i64]
         lib.oref_scan_canonical.restype = i64
         lib.oref_scan_perm.argtypes = [i, i64, i64, I64, I64]
@@ -169,6 +172,40 @@ def gla_bwd(q, k, v, z, r, dy, gamma=None, tau: float = 16.0, q_scale: float = 1
     _load().oref_gla_bwd(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(z), _p(r), _p(g), float(tau),
                          float(q_scale), float(eps), _p(dy), _p(out["dq"]), _p(out["dk"]),
                          _p(out["dv"]), _p(out["dz"]), _p(out["dr"]), _p(out["dgamma"]))
+    return out
+
+
+# ---------------------------------------------------- value-side gate beta (eq. 5)
+def gla_fwd_beta(q, k, v, z, w, r, gamma=None, tau: float = 16.0, q_scale: float = 1.0,
+                 eps: float = 1e-5):
+    """(y, o_pre, rstd) of the mixer forward with the outer-product gate G_t = alpha_t^T beta_t:
+    key-gate logits z [B,L,H,d_k], value-gate logits w [B,L,H,d_v]."""
+    q, k, v, z, w, r = map(_f64, (q, k, v, z, w, r))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    g = None if gamma is None else _f64(gamma)
+    y = np.empty((B, L, H, dv))
+    o = np.empty((B, L, H, dv))
+    rstd = np.empty((B, L, H))
+    _load().oref_gla_fwd_beta(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(z), _p(w), _p(r), _p(g),
+                              float(tau), float(q_scale), float(eps), _p(y), _p(o), _p(rstd))
+    return y, o, rstd
+
+
+def gla_bwd_beta(q, k, v, z, w, r, dy, gamma=None, tau: float = 16.0, q_scale: float = 1.0,
+                 eps: float = 1e-5):
+    """dict of dq, dk, dv, dz, dw, dr, dgamma for L = <dy, y> of gla_fwd_beta."""
+    q, k, v, z, w, r, dy = map(_f64, (q, k, v, z, w, r, dy))
+    B, L, H, dk = q.shape
+    dv = v.shape[-1]
+    g = None if gamma is None else _f64(gamma)
+    out = {n: np.empty_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dz", z),
+                                            ("dw", w), ("dr", r))}
+    out["dgamma"] = np.empty(dv)
+    _load().oref_gla_bwd_beta(B, L, H, dk, dv, _p(q), _p(k), _p(v), _p(z), _p(w), _p(r), _p(g),
+                              float(tau), float(q_scale), float(eps), _p(dy), _p(out["dq"]),
+                              _p(out["dk"]), _p(out["dv"]), _p(out["dz"]), _p(out["dw"]),
+                              _p(out["dr"]), _p(out["dgamma"]))
     return out
 
 

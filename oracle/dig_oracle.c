@@ -309,6 +309,200 @@ void oref_gla_bwd(int B, int L, int H, int dk, int dv,
     free(dloga);
 }
 
+/* ------------------------------------------- value-side gate beta [GLA eq.5][TAU] */
+
+/*
+ * The general gate of eq. (5): G_t = alpha_t^T beta_t, an outer product of a key-side gate
+ * alpha_t (d_k) and a value-side gate beta_t (d_v), both sigmoid(.)^(1/tau) of their logits:
+ *   S_t = G_t (.) S_{t-1} + k_t^T v_t,  o_t = (q_scale q_t) S_t,  S_{-1} = 0,
+ * with G_t[c,e] = alpha_t[c] beta_t[e].  loga is [B,L,H,d_k], logb is [B,L,H,d_v].
+ * beta = 1 (logb = 0) is the recurrence above.
+ */
+static void recur_unit_beta(int L, int H, int dk, int dv, int b, int h,
+                            const double *q, const double *k, const double *v,
+                            const double *loga, const double *logb, double q_scale,
+                            double *o_unit, double *states_opt)
+{
+    /* o_unit: this unit's [L][dv] outputs; states_opt: its [L][dk][dv] states S_t */
+    size_t sz = (size_t)dk * dv;
+    double *S = (double *)calloc(sz, sizeof(double));
+    for (int t = 0; t < L; ++t) {
+        const double *qt = q + IDX4(b, t, h, 0, L, H, dk);
+        const double *kt = k + IDX4(b, t, h, 0, L, H, dk);
+        const double *vt = v + IDX4(b, t, h, 0, L, H, dv);
+        const double *ga = loga + IDX4(b, t, h, 0, L, H, dk);
+        const double *gb = logb + IDX4(b, t, h, 0, L, H, dv);
+        for (int c = 0; c < dk; ++c)
+            for (int e = 0; e < dv; ++e) {
+                double g = exp(ga[c]) * exp(gb[e]);
+                S[(size_t)c * dv + e] = g * S[(size_t)c * dv + e] + kt[c] * vt[e];
+            }
+        if (states_opt) memcpy(states_opt + (size_t)t * sz, S, sizeof(double) * sz);
+        double *ot = o_unit + (size_t)t * dv;
+        for (int e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += (q_scale * qt[c]) * S[(size_t)c * dv + e];
+            ot[e] = acc;
+        }
+    }
+    free(S);
+}
+
+/* Whole forward with both gates: gate logits z (keys) and w (values), recurrence, output
+ * stage.  o_pre and rstd are optional. */
+void oref_gla_fwd_beta(int B, int L, int H, int dk, int dv,
+                       const double *q, const double *k, const double *v, const double *z,
+                       const double *w, const double *r, const double *gamma, double tau,
+                       double q_scale, double eps, double *y, double *o_pre_opt,
+                       double *rstd_opt)
+{
+    size_t nk = (size_t)B * L * H * dk, nv = (size_t)B * L * H * dv;
+    double *loga = (double *)malloc(sizeof(double) * nk);
+    double *logb = (double *)malloc(sizeof(double) * nv);
+    double *o = o_pre_opt ? o_pre_opt : (double *)malloc(sizeof(double) * nv);
+    oref_gate_logalpha(nk, z, tau, loga);
+    oref_gate_logalpha(nv, w, tau, logb);
+    int units = B * H;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int u = 0; u < units; ++u) {
+        int b = u / H, h = u % H;
+        double *ou = (double *)malloc(sizeof(double) * (size_t)L * dv);
+        recur_unit_beta(L, H, dk, dv, b, h, q, k, v, loga, logb, q_scale, ou, NULL);
+        for (int t = 0; t < L; ++t)
+            memcpy(o + IDX4(b, t, h, 0, L, H, dv), ou + (size_t)t * dv, sizeof(double) * dv);
+        free(ou);
+    }
+    oref_output_stage(B, L, H, dv, o, r, gamma, eps, y, rstd_opt);
+    if (!o_pre_opt) free(o);
+    free(loga);
+    free(logb);
+}
+
+/*
+ * Backward with both gates, L = <dy, y>.  The output stage is the one of bwd_unit; the
+ * recurrence runs in reverse time with dS = 0:
+ *   dS += q_scale q_t^T do_t;  dq_t = q_scale S_t do_t;  dk_t = dS v_t;  dv_t = k_t dS;
+ *   dloga_t[c] = sum_e G_t[c,e] dS[c,e] S_{t-1}[c,e];
+ *   dlogb_t[e] = sum_c G_t[c,e] dS[c,e] S_{t-1}[c,e];
+ *   dS = G_t (.) dS.
+ * dz = dloga sigmoid(-z) / tau and dw = dlogb sigmoid(-w) / tau.
+ */
+static void bwd_unit_beta(int L, int H, int dk, int dv, int b, int h,
+                          const double *q, const double *k, const double *v,
+                          const double *loga, const double *logb, const double *r,
+                          const double *gamma, double q_scale, double eps, const double *dy,
+                          double *dq, double *dk_, double *dv_, double *dloga, double *dlogb,
+                          double *dr, double *dgamma_unit)
+{
+    size_t sz = (size_t)dk * dv;
+    double *states = (double *)malloc(sizeof(double) * sz * (size_t)L);
+    double *o = (double *)malloc(sizeof(double) * (size_t)L * dv);
+    double *dO = (double *)malloc(sizeof(double) * (size_t)L * dv);
+    double *dS = (double *)calloc(sz, sizeof(double));
+
+    /* forward, keeping every state S_t (o is this unit's [L][dv] slice) */
+    recur_unit_beta(L, H, dk, dv, b, h, q, k, v, loga, logb, q_scale, o, states);
+
+    /* output-stage backward (as in bwd_unit) */
+    for (int t = 0; t < L; ++t) {
+        const double *ot = o + (size_t)t * dv;
+        const double *rt = r + IDX4(b, t, h, 0, L, H, dv);
+        const double *dyt = dy + IDX4(b, t, h, 0, L, H, dv);
+        double *drt = dr + IDX4(b, t, h, 0, L, H, dv);
+        double ss = 0.0;
+        for (int e = 0; e < dv; ++e) ss += ot[e] * ot[e];
+        double rstd = 1.0 / sqrt(ss / dv + eps);
+        double m = 0.0;
+        for (int e = 0; e < dv; ++e) {
+            double g = gamma ? gamma[e] : 1.0;
+            double sg = oref_sigmoid(rt[e]);
+            double s = rt[e] * sg;
+            double n = ot[e] * rstd;
+            dgamma_unit[e] += dyt[e] * n * s;
+            drt[e] = dyt[e] * n * g * sg * (1.0 + rt[e] * (1.0 - sg));
+            m += dyt[e] * g * s * n;
+        }
+        m /= dv;
+        for (int e = 0; e < dv; ++e) {
+            double g = gamma ? gamma[e] : 1.0;
+            double s = rt[e] * oref_sigmoid(rt[e]);
+            dO[(size_t)t * dv + e] = rstd * (dyt[e] * g * s - ot[e] * rstd * m);
+        }
+    }
+
+    /* reverse-time recurrence */
+    for (int t = L - 1; t >= 0; --t) {
+        const double *qt = q + IDX4(b, t, h, 0, L, H, dk);
+        const double *kt = k + IDX4(b, t, h, 0, L, H, dk);
+        const double *vt = v + IDX4(b, t, h, 0, L, H, dv);
+        const double *ga = loga + IDX4(b, t, h, 0, L, H, dk);
+        const double *gb = logb + IDX4(b, t, h, 0, L, H, dv);
+        const double *dot = dO + (size_t)t * dv;
+        const double *St = states + (size_t)t * sz;
+        const double *Sp = t > 0 ? states + (size_t)(t - 1) * sz : NULL;
+        for (int c = 0; c < dk; ++c)
+            for (int e = 0; e < dv; ++e) dS[c * dv + e] += q_scale * qt[c] * dot[e];
+        for (int c = 0; c < dk; ++c) {
+            double aq = 0.0, ak = 0.0;
+            for (int e = 0; e < dv; ++e) {
+                aq += St[c * dv + e] * dot[e];
+                ak += dS[c * dv + e] * vt[e];
+            }
+            dq[IDX4(b, t, h, c, L, H, dk)] = q_scale * aq;
+            dk_[IDX4(b, t, h, c, L, H, dk)] = ak;
+        }
+        for (int e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += kt[c] * dS[c * dv + e];
+            dv_[IDX4(b, t, h, e, L, H, dv)] = acc;
+        }
+        for (int c = 0; c < dk; ++c) dloga[IDX4(b, t, h, c, L, H, dk)] = 0.0;
+        for (int e = 0; e < dv; ++e) dlogb[IDX4(b, t, h, e, L, H, dv)] = 0.0;
+        for (int c = 0; c < dk; ++c)
+            for (int e = 0; e < dv; ++e) {
+                double g = exp(ga[c]) * exp(gb[e]);
+                double x = Sp ? g * dS[c * dv + e] * Sp[c * dv + e] : 0.0;
+                dloga[IDX4(b, t, h, c, L, H, dk)] += x;
+                dlogb[IDX4(b, t, h, e, L, H, dv)] += x;
+                dS[c * dv + e] *= g;
+            }
+    }
+    free(states); free(o); free(dO); free(dS);
+}
+
+void oref_gla_bwd_beta(int B, int L, int H, int dk, int dv,
+                       const double *q, const double *k, const double *v, const double *z,
+                       const double *w, const double *r, const double *gamma, double tau,
+                       double q_scale, double eps, const double *dy, double *dq, double *dk_,
+                       double *dv_, double *dz, double *dw, double *dr, double *dgamma)
+{
+    size_t nk = (size_t)B * L * H * dk, nv = (size_t)B * L * H * dv;
+    int units = B * H;
+    double *loga = (double *)malloc(sizeof(double) * nk);
+    double *logb = (double *)malloc(sizeof(double) * nv);
+    double *dloga = (double *)malloc(sizeof(double) * nk);
+    double *dlogb = (double *)malloc(sizeof(double) * nv);
+    double *dg_units = (double *)calloc((size_t)units * dv, sizeof(double));
+    oref_gate_logalpha(nk, z, tau, loga);
+    oref_gate_logalpha(nv, w, tau, logb);
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int u = 0; u < units; ++u)
+        bwd_unit_beta(L, H, dk, dv, u / H, u % H, q, k, v, loga, logb, r, gamma, q_scale, eps,
+                      dy, dq, dk_, dv_, dloga, dlogb, dr, dg_units + (size_t)u * dv);
+    if (dgamma) {
+        for (int e = 0; e < dv; ++e) dgamma[e] = 0.0;
+        for (int u = 0; u < units; ++u)
+            for (int e = 0; e < dv; ++e) dgamma[e] += dg_units[(size_t)u * dv + e];
+    }
+    for (size_t i = 0; i < nk; ++i) dz[i] = dloga[i] * oref_sigmoid(-z[i]) / tau;
+    for (size_t i = 0; i < nv; ++i) dw[i] = dlogb[i] * oref_sigmoid(-w[i]) / tau;
+    free(loga); free(logb); free(dloga); free(dlogb); free(dg_units);
+}
+
 /* ------------------------------------------------------ scan directions [SREM] */
 
 enum { OREF_ROW = 0, OREF_ROW_REV = 1, OREF_COL = 2, OREF_COL_REV = 3 };
