@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--pmc-target", choices=["gla_fwd", "gla_bwd", "srem_fwd", "srem_bwd"],
                     default=None)
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--value-gate", action="store_true",
+                    help="time only the value-gate calls (dig_gla_*_beta) at --workload")
     ap.add_argument("--stack", default=None,
                     choices=["dig_s2_256_stack", "dig_xl2_256_stack", "dig_xl2_2048_stack"],
                     help="time only this DiG block stack forward (for kernel traces)")
@@ -386,6 +388,44 @@ def lowrank_gate(cfg, steps):
     res["calls"] = calls
     res["gate_bytes_per_token"] = {"logits": 2 * cfg.heads * cfg.d_k, "lowrank": 2 * cfg.rank}
     del path
+    torch.cuda.empty_cache()
+    return res
+
+
+def value_gate(cfg):
+    """The mixer with the general gate of eq. (5), G_t = alpha_t^T beta_t (dig_gla_fwd_beta /
+    dig_gla_bwd_beta), at the headline shape: one block's calls, timed per call (HIP events on
+    the stream), against the bytes their bf16 inputs and outputs must move."""
+    import torch
+    import diffusion_backbone_amd as dig
+    B, L, H, dk, dv = cfg.batch, cfg.seq_len, cfg.heads, cfg.d_k, cfg.d_v
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    bf = lambda d, s=1.0: (torch.randn(B, L, H, d, device="cuda", generator=g) * s).to(torch.bfloat16)
+    q, k, z, v, w, r, dy = bf(dk, 0.5), bf(dk, 0.5), bf(dk), bf(dv), bf(dv), bf(dv), bf(dv)
+    nw = torch.ones(dv, device="cuda")
+    desc = dig.make_desc(B, L, H, dk, dv, 64, 16.0, 1.0, 1e-5, "bf16", 0)
+    saved = torch.empty(dig.dig_gla_beta_saved_bytes(desc), dtype=torch.uint8, device="cuda")
+    fwb, bwb = dig.dig_gla_beta_fwd_workspace_bytes(desc), dig.dig_gla_beta_bwd_workspace_bytes(desc)
+    fws = torch.empty(fwb, dtype=torch.uint8, device="cuda")
+    bws = torch.empty(bwb, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(r)
+    grads = [torch.empty_like(t) for t in (q, k, v, z, w, r)]
+    dnw = torch.empty(dv, device="cuda")
+    fwd = lambda: dig.dig_gla_fwd_beta(desc, q, k, v, z, w, r, nw, y, None, saved, fws, fwb)
+    bwd = lambda: dig.dig_gla_bwd_beta(desc, q, k, v, z, w, r, nw, dy, saved, grads[0], grads[1],
+                                       grads[2], grads[3], grads[4], grads[5], dnw, bws, bwb)
+    fwd()
+    fu, bu = _time_us(fwd, reps=20), _time_us(bwd, reps=20)
+    tok = B * L * H
+    fb, bb = 2 * (3 * dk + 4 * dv) * tok, 2 * (6 * dk + 7 * dv) * tok
+    res = {"shape": {"batch": B, "seq_len": L, "heads": H, "d_k": dk, "d_v": dv, "chunk": 64},
+           "gla_fwd_beta_us": round(fu, 2), "gla_bwd_beta_us": round(bu, 2),
+           "fwd_algorithmic_bytes": fb, "bwd_algorithmic_bytes": bb,
+           "fwd_frac_of_hbm_peak": round(fb / (fu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "bwd_frac_of_hbm_peak": round(bb / (bu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "layer_tokens_per_s_fwd_bwd": round(B * L / ((fu + bu) * 1e-6), 1)}
+    del saved, fws, bws
     torch.cuda.empty_cache()
     return res
 
@@ -865,6 +905,9 @@ def main():
     if args.stack:
         print(json.dumps({args.stack: block_stack(args.stack, max(1, args.steps))}), flush=True)
         return
+    if args.value_gate:
+        print(json.dumps({"value_gate": value_gate(W.CONFIGS[args.workload])}), flush=True)
+        return
     cfg = W.CONFIGS[args.workload]
     nblocks = n_blocks(cfg)
     if args.pmc_target:  # one library call per block, `steps` times (for counter runs)
@@ -976,6 +1019,8 @@ def main():
         out["configs"] = configs
         out["lowrank_gate"] = lowrank_gate(cfg, max(10, args.steps // 2))
         print("[bench] lowrank_gate done", file=sys.stderr, flush=True)
+        out["value_gate"] = value_gate(cfg)
+        print("[bench] value_gate done", file=sys.stderr, flush=True)
         out["projections"] = projections(cfg, max(10, args.steps // 2))
         stacks = {}
         for sname in ("dig_s2_256_stack", "dig_xl2_256_stack", "dig_xl2_2048_stack"):

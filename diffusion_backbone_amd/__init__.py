@@ -30,7 +30,9 @@ EXPORTS = (
     "dig_dwconv3x3_bwd_noalloc", "dig_dwconv3x3_bwd_noalloc_max_bytes", "dig_linear",
     "dig_rmsnorm_modulate", "dig_block_cond_workspace_bytes", "dig_block_cond",
     "dig_block_fwd_workspace_bytes", "dig_block_fwd", "dig_linear_workspace_bytes",
-    "dig_linear_ws", "dig_gla_fwd_lowrank", "dig_gla_bwd_lowrank",
+    "dig_linear_ws", "dig_gla_fwd_lowrank", "dig_gla_bwd_lowrank", "dig_gla_beta_saved_bytes",
+    "dig_gla_beta_fwd_workspace_bytes", "dig_gla_beta_bwd_workspace_bytes", "dig_gla_fwd_beta",
+    "dig_gla_bwd_beta",
 )
 DIG_GATE_RANK = 16  # the rank of the low-rank key gate the chunk kernels form
 DIG_LINEAR_MAX_OUT = 6
@@ -107,6 +109,14 @@ def lib() -> ctypes.CDLL:
         L.dig_gla_bwd_lowrank.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, P, P,
                                           P, S, P]
         L.dig_gla_bwd_lowrank.restype = ctypes.c_int
+        for n in ("dig_gla_beta_saved_bytes", "dig_gla_beta_fwd_workspace_bytes",
+                  "dig_gla_beta_bwd_workspace_bytes"):
+            getattr(L, n).argtypes = [D]
+            getattr(L, n).restype = S
+        L.dig_gla_fwd_beta.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.dig_gla_fwd_beta.restype = ctypes.c_int
+        L.dig_gla_bwd_beta.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.dig_gla_bwd_beta.restype = ctypes.c_int
         L.dig_srem_reorient.argtypes = [I, I, I, I, I, I, I, P, P, P]
         L.dig_srem_reorient.restype = ctypes.c_int
         L.dig_dwconv3x3.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
@@ -253,6 +263,39 @@ def dig_gla_bwd_lowrank(desc, q, k, v, gate_factor, gate_w, gate_bias, r, norm_w
                                    _ptr(d_norm_w), _ptr(workspace),
                                    _nbytes(workspace, workspace_bytes), _stream(stream))
     _check(st, "dig_gla_bwd_lowrank")
+
+
+def dig_gla_beta_saved_bytes(desc: dig_gla_desc) -> int:
+    return lib().dig_gla_beta_saved_bytes(ctypes.byref(desc))
+
+
+def dig_gla_beta_fwd_workspace_bytes(desc: dig_gla_desc) -> int:
+    return lib().dig_gla_beta_fwd_workspace_bytes(ctypes.byref(desc))
+
+
+def dig_gla_beta_bwd_workspace_bytes(desc: dig_gla_desc) -> int:
+    return lib().dig_gla_beta_bwd_workspace_bytes(ctypes.byref(desc))
+
+
+def dig_gla_fwd_beta(desc, q, k, v, gate_logit, value_gate_logit, r, norm_w, y, o_pre=None,
+                     saved=None, workspace=None, workspace_bytes=None, stream=None):
+    st = lib().dig_gla_fwd_beta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate_logit),
+                                _ptr(value_gate_logit), _ptr(r), _ptr(norm_w), _ptr(y),
+                                _ptr(o_pre), _ptr(saved), _ptr(workspace),
+                                _nbytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "dig_gla_fwd_beta")
+
+
+def dig_gla_bwd_beta(desc, q, k, v, gate_logit, value_gate_logit, r, norm_w, dy, saved, dq, dk,
+                     dv, d_gate_logit, d_value_gate_logit, dr, d_norm_w=None, workspace=None,
+                     workspace_bytes=None, stream=None):
+    st = lib().dig_gla_bwd_beta(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate_logit),
+                                _ptr(value_gate_logit), _ptr(r), _ptr(norm_w), _ptr(dy),
+                                _ptr(saved), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_gate_logit),
+                                _ptr(d_value_gate_logit), _ptr(dr), _ptr(d_norm_w),
+                                _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                _stream(stream))
+    _check(st, "dig_gla_bwd_beta")
 
 
 def dig_srem_reorient(batch, grid_h, grid_w, channels, dtype, frm, to, x, y, stream=None):

@@ -16,7 +16,7 @@ PROBE_LIB = os.path.join(HERE, "libdig_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["dig_api.cpp", "gla_fwd.hip", "gla_fwd_bf16.hip", "gla_fwd_f32.hip",
            "gla_fwd_bf16_lr.hip", "gla_bwd.hip", "gla_bwd_bf16.hip", "gla_bwd_f32.hip",
-           "gla_bwd_bf16_lr.hip", "srem.hip", "linear.hip", "block.hip"]
+           "gla_bwd_bf16_lr.hip", "gla_beta.hip", "srem.hip", "linear.hip", "block.hip"]
 HEADERS = ["dig_device.h", "dig_internal.h", "gla_fwd_kernel.h", "gla_bwd_kernel.h"]
 
 ARCH = "gfx950"

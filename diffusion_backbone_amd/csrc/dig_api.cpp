@@ -66,7 +66,8 @@ constexpr int kLdsLimit = 160 * 1024;
 // Validates the descriptor; fills the plan.  Returns DIG_OK or an error (message set).
 enum Pass { kFwd, kBwd };
 
-dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass, bool lowrank = false) {
+dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass, bool lowrank = false,
+                      bool key_gate_kernels = true) {
   if (!d) return fail(DIG_ERR_NULL, "desc is NULL");
   if (d->batch < 0 || d->seq_len < 0)
     return fail(DIG_ERR_SHAPE, "batch (%d) and seq_len (%d) must be >= 0", d->batch, d->seq_len);
@@ -96,6 +97,7 @@ dig_status check_desc(const dig_gla_desc* d, dig::GlaShape* s, Pass pass, bool l
   *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, d->chunk,
                      d->dtype == DIG_BF16, d->seg_chunks, pass == kBwd);
   s->lr = lowrank ? 1 : 0;
+  if (!key_gate_kernels) return DIG_OK;  // the caller checks its own kernels' limits
   const int lds = pass == kFwd ? dig::gla_fwd_lds_bytes(*s) : dig::gla_bwd_lds_bytes(*s);
   if (lds > kLdsLimit)
     return fail(DIG_ERR_UNSUPPORTED, "%s needs %d bytes of LDS for this shape (limit %d)",
@@ -143,7 +145,7 @@ const char* dig_status_str(dig_status s) {
 
 const char* dig_last_error(void) { return g_err; }
 
-int32_t dig_abi_version(void) { return 104; }
+int32_t dig_abi_version(void) { return 105; }
 
 dig_status dig_lookback_status(hipStream_t stream) {
   unsigned* word = dig::lookback_status_word();
@@ -341,9 +343,141 @@ dig_status gla_bwd_impl(const dig_gla_desc* d, const void* q, const void* k, con
   return check_dev(dig::launch_gla_bwd(s, p, stream), "dig_gla_bwd launch");
 }
 
+// The value-gate calls: the common descriptor checks, then bf16, chunk 64 and the head-dim
+// classes their kernels are built for.
+dig_status check_beta(const dig_gla_desc* d, dig::GlaShape* s, Pass pass) {
+  dig_status st = check_desc(d, s, pass, false, false);
+  if (st != DIG_OK) return st;
+  if (d->dtype != DIG_BF16) return fail(DIG_ERR_UNSUPPORTED, "the value gate needs DIG_BF16");
+  if (d->chunk != 64) return fail(DIG_ERR_UNSUPPORTED, "the value gate runs chunk 64 only");
+  *s = dig::gla_plan(d->batch, d->seq_len, d->heads, d->d_k, d->d_v, 64, 1, 0, pass == kBwd);
+  const int lds = dig::gla_beta_lds_bytes(*s, pass == kBwd);
+  if (lds > kLdsLimit)
+    return fail(DIG_ERR_UNSUPPORTED, "the value gate is built for d_k <= 48 and d_v <= 80 "
+                "(head-dim classes 16/32, 32/64, 48/80); got %d/%d", d->d_k, d->d_v);
+  return DIG_OK;
+}
+
+dig_status gla_fwd_beta_impl(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                             const void* z, const void* w, const void* r, const float* norm_w,
+                             void* y, void* o_pre_opt, void* saved_opt, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  dig::GlaShape s;
+  dig_status st = check_beta(d, &s, kFwd);
+  if (st != DIG_OK) return st;
+  if ((long long)d->batch * d->seq_len == 0) return ok();
+  if (!q || !k || !v || !z || !w || !r || !y)
+    return fail(DIG_ERR_NULL, "q, k, v, both gates, r and y are required");
+  const void* ptrs[] = {q, k, v, z, w, r, norm_w, y, o_pre_opt, saved_opt, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t need = dig::gla_beta_fwd_workspace(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const size_t rows = (size_t)d->batch * d->seq_len * d->heads;
+  const size_t bk = rows * d->d_k * 2, bv = rows * d->d_v * 2;
+  const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
+                      rng("gate_logit", z, bk), rng("value_gate_logit", w, bv), rng("r", r, bv),
+                      rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0)};
+  const Range out[] = {rng("y", y, bv), rng("o_pre", o_pre_opt, o_pre_opt ? bv : 0),
+                       rng("saved", saved_opt, saved_opt ? dig::gla_beta_saved_bytes(s) : 0),
+                       rng("workspace", workspace, need)};
+  st = check_alias(in, 7, out, 4);
+  if (st != DIG_OK) return st;
+  dig::GlaBetaFwd f{};
+  f.q = q; f.k = k; f.v = v; f.z = z; f.w = w; f.r = r; f.norm_w = norm_w;
+  f.y = y; f.o_pre = o_pre_opt; f.saved = saved_opt; f.workspace = workspace;
+  f.inv_tau = 1.f / d->tau; f.q_scale = d->q_scale; f.eps = d->norm_eps;
+  return check_dev(dig::launch_gla_beta_fwd(s, f, stream), "dig_gla_fwd_beta launch");
+}
+
+dig_status gla_bwd_beta_impl(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                             const void* z, const void* w, const void* r, const float* norm_w,
+                             const void* dy, const void* saved, void* dq, void* dk, void* dv,
+                             void* dz, void* dw, void* dr, float* d_norm_w, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  dig::GlaShape s;
+  dig_status st = check_beta(d, &s, kBwd);
+  if (st != DIG_OK) return st;
+  if ((long long)d->batch * d->seq_len == 0) {
+    if (d_norm_w) {
+      if (!aligned16(d_norm_w)) return fail(DIG_ERR_ALIGN, "d_norm_w must be 16-byte aligned");
+      return check_dev(dig::launch_fill_zero(d_norm_w, (size_t)d->d_v, stream),
+                       "dig_gla_bwd_beta fill");
+    }
+    return ok();
+  }
+  if (!q || !k || !v || !z || !w || !r || !dy || !saved || !dq || !dk || !dv || !dz || !dw || !dr)
+    return fail(DIG_ERR_NULL, "q, k, v, both gates, r, dy, saved and all gradients are required");
+  const void* ptrs[] = {q, k, v, z, w, r, norm_w, dy, saved, dq, dk, dv, dz, dw, dr, d_norm_w,
+                        workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(DIG_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const size_t need = dig::gla_beta_bwd_workspace(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const size_t rows = (size_t)d->batch * d->seq_len * d->heads;
+  const size_t bk = rows * d->d_k * 2, bv = rows * d->d_v * 2;
+  const Range in[] = {rng("q", q, bk), rng("k", k, bk), rng("v", v, bv),
+                      rng("gate_logit", z, bk), rng("value_gate_logit", w, bv), rng("r", r, bv),
+                      rng("norm_w", norm_w, norm_w ? d->d_v * 4 : 0), rng("dy", dy, bv),
+                      rng("saved", saved, dig::gla_beta_saved_bytes(s))};
+  const Range out[] = {rng("dq", dq, bk), rng("dk", dk, bk), rng("dv", dv, bv),
+                       rng("d_gate_logit", dz, bk), rng("d_value_gate_logit", dw, bv),
+                       rng("dr", dr, bv), rng("d_norm_w", d_norm_w, d_norm_w ? d->d_v * 4 : 0),
+                       rng("workspace", workspace, need)};
+  st = check_alias(in, 9, out, 8);
+  if (st != DIG_OK) return st;
+  dig::GlaBetaBwd f{};
+  f.q = q; f.k = k; f.v = v; f.z = z; f.w = w; f.r = r; f.norm_w = norm_w; f.dy = dy;
+  f.saved = saved; f.dq = dq; f.dk = dk; f.dv = dv; f.dz = dz; f.dw = dw; f.dr = dr;
+  f.d_norm_w = d_norm_w; f.workspace = workspace;
+  f.inv_tau = 1.f / d->tau; f.q_scale = d->q_scale; f.eps = d->norm_eps;
+  return check_dev(dig::launch_gla_beta_bwd(s, f, stream), "dig_gla_bwd_beta launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t dig_gla_beta_saved_bytes(const dig_gla_desc* d) {
+  dig::GlaShape s;
+  if (check_beta(d, &s, kFwd) != DIG_OK) return 0;
+  return dig::gla_beta_saved_bytes(s);
+}
+
+size_t dig_gla_beta_fwd_workspace_bytes(const dig_gla_desc* d) {
+  dig::GlaShape s;
+  if (check_beta(d, &s, kFwd) != DIG_OK) return 0;
+  return dig::gla_beta_fwd_workspace(s);
+}
+
+size_t dig_gla_beta_bwd_workspace_bytes(const dig_gla_desc* d) {
+  dig::GlaShape s;
+  if (check_beta(d, &s, kBwd) != DIG_OK) return 0;
+  return dig::gla_beta_bwd_workspace(s);
+}
+
+dig_status dig_gla_fwd_beta(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                            const void* gate_logit, const void* value_gate_logit, const void* r,
+                            const float* norm_w, void* y, void* o_pre_opt, void* saved_opt,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gla_fwd_beta_impl(d, q, k, v, gate_logit, value_gate_logit, r, norm_w, y, o_pre_opt,
+                           saved_opt, workspace, workspace_bytes, stream);
+}
+
+dig_status dig_gla_bwd_beta(const dig_gla_desc* d, const void* q, const void* k, const void* v,
+                            const void* gate_logit, const void* value_gate_logit, const void* r,
+                            const float* norm_w, const void* dy, const void* saved, void* dq,
+                            void* dk, void* dv, void* d_gate_logit, void* d_value_gate_logit,
+                            void* dr, float* d_norm_w, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return gla_bwd_beta_impl(d, q, k, v, gate_logit, value_gate_logit, r, norm_w, dy, saved, dq,
+                           dk, dv, d_gate_logit, d_value_gate_logit, dr, d_norm_w, workspace,
+                           workspace_bytes, stream);
+}
 
 dig_status dig_gla_fwd(const dig_gla_desc* d, const void* q, const void* k, const void* v,
                        const void* gate_logit, const void* r, const float* norm_w, void* y,

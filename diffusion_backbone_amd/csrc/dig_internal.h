@@ -137,6 +137,54 @@ void set_lookback_wait(unsigned spins, bool never_match);
 unsigned* lookback_status_word();
 hipError_t launch_gla_bwd(const GlaShape& s, GlaBwdParams p, hipStream_t st);
 
+// ------------------------------------------------------- GLA with the value-side gate
+// The general gate of eq. (5), G_t = alpha_t^T beta_t (gla_beta.hip): bf16 I/O, chunk 64,
+// head-dim classes (1,2), (2,4), (3,5).
+struct GlaBetaFwd {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* z;  // key-gate logits [B, L, H, dk]
+  const void* w;  // value-gate logits [B, L, H, dv]
+  const void* r;
+  const float* norm_w;
+  void* y;
+  void* o_pre;
+  void* saved;      // gla_beta_saved_bytes, or null
+  void* workspace;  // gla_beta_fwd_workspace
+  float inv_tau, q_scale, eps;
+};
+struct GlaBetaBwd {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* z;
+  const void* w;
+  const void* r;
+  const float* norm_w;
+  const void* dy;
+  const void* saved;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dz;
+  void* dw;
+  void* dr;
+  float* d_norm_w;  // or null
+  void* workspace;  // gla_beta_bwd_workspace
+  float inv_tau, q_scale, eps;
+};
+// LDS bytes of the forward (bwd false) or backward output pass; above any limit when no kernel
+// exists for the shape's head-dim class.
+int gla_beta_lds_bytes(const GlaShape& s, bool bwd);
+// saved: the fp32 state entering every 64-token chunk, then the fp32 pre-norm output of every
+// token ([B*H][NC*64][dv]), each 256-byte aligned.
+size_t gla_beta_saved_bytes(const GlaShape& s);
+size_t gla_beta_fwd_workspace(const GlaShape& s);
+size_t gla_beta_bwd_workspace(const GlaShape& s);
+hipError_t launch_gla_beta_fwd(const GlaShape& s, const GlaBetaFwd& f, hipStream_t st);
+hipError_t launch_gla_beta_bwd(const GlaShape& s, const GlaBetaBwd& f, hipStream_t st);
+
 // ------------------------------------------------------------------- projections
 constexpr int kLinearMaxOut = 6;
 enum { kActNone = 0, kActGelu = 1 };

@@ -1,0 +1,1016 @@
+// gla_beta.hip -- the GLA mixer with the general gate of eq. (5), G_t = alpha_t^T beta_t
+// (DiG study-group slides, slide "GLA の導入": a key-side gate alpha and a value-side gate
+// beta), forward and backward, bf16 I/O and fp32 arithmetic.
+//
+// Per image and head: S_t = (alpha_t^T beta_t) (.) S_{t-1} + k_t^T v_t, o_t = (q_scale q_t) S_t,
+// then the key-gate mixer's output stage y = RMSNorm(o) norm_w Swish(r).  log2 alpha =
+// log2 sigmoid(z) / tau per key column, log2 beta = log2 sigmoid(w) / tau per value column;
+// B and C are their inclusive running sums over a chunk's rows.
+//
+// Work layout.  Chunks of 64 tokens, one workgroup of four waves per chunk; wave w owns the
+// 16-token tile w.  Every factor 2^x formed below has x <= 0, so no gate strength overflows
+// a factor or loses the small ones:
+//   across chunks  each chunk's contribution U = sum_s (k_s 2^{B_end-B_s})^T (v_s 2^{C_end-C_s})
+//                  and decays (pass 1); a scan over chunks (pass 2) gives the state entering
+//                  every chunk, saved for the backward;
+//   across tiles   the state entering tile w, S_w = 2^{B_w+C_w} (.) S_{w-1} + U_{w-1} (U of a
+//                  tile formed like a chunk's), reaches tile w's rows as
+//                  (q_t 2^{B_t-B_ref}) S_w 2^{C_t-C_ref}, ref = the row before the tile;
+//   inside a tile  each of the 16 x 16 causal pairs takes its own factors 2^{B_t[c]-B_s[c]} and
+//                  2^{C_t[e]-C_s[e]} on the vector ALU.
+// The matrix products (chunk and tile contributions, the products with tile states) run on
+// the fp32 matrix cores (16 x 16 x 4).  The backward mirrors this with gradient states G
+// carried from later tiles and chunks (a reverse scan) and the boundary identity
+//   dlog alpha_t = sum_{u >= t in chunk} (q_u dq_u - k_u dk_u) + sum_e (S_end (.) G_end)[:, e]
+//   dlog beta_t  = sum_{u >= t in chunk} (do_u o_u - v_u dv_u) + sum_c (S_end (.) G_end)[c, :]
+// (shifting every later running sum by eps scales S_end by 2^eps).
+#include "dig_device.h"
+#include "dig_internal.h"
+
+namespace dig {
+namespace {
+
+constexpr int kBC = 64;   // tokens per chunk
+constexpr int kBT = 256;  // threads per workgroup (four waves, one 16-token tile each)
+
+__device__ __forceinline__ float bf(bf16 x) { return static_cast<float>(x); }
+
+template <int NDK, int NDV>
+struct BetaLay {
+  static constexpr int DKP = 16 * NDK, DVP = 16 * NDV;
+  static constexpr int PQ = DKP + 8;    // bf16 row pitch of q and k
+  static constexpr int PV = DVP + 8;    // bf16 row pitch of v
+  static constexpr int PB = DKP + 4;    // fp32 row pitch of the key-gate sums
+  static constexpr int PC = DVP + 4;    // fp32 row pitch of the value-gate sums, dO and states
+  static constexpr int SZS = DKP * PC;  // floats of one state [DKP][PC]
+  static constexpr int PA = 17;         // pitch of one wave's 16 x 16 pair table
+  static constexpr int NQ = kBC * PQ * 2, NV = kBC * PV * 2;
+  static constexpr int NB = kBC * PB * 4, NCB = kBC * PC * 4;
+  // forward output pass: q, k, v, B, C, four states, four pair tables
+  static constexpr int F_Q = 0, F_K = F_Q + NQ, F_V = F_K + NQ, F_B = F_V + NV, F_C = F_B + NB,
+                       F_S = F_C + NCB, F_A = F_S + 4 * SZS * 4, F_END = F_A + 4 * 16 * PA * 4;
+  // chunk-contribution passes: two operand tiles and the two gate sums
+  static constexpr int U_X = 0, U_Y = U_X + kBC * PC * 4, U_B = U_Y + kBC * PC * 4,
+                       U_C = U_B + NB, U_END = U_C + NCB;
+  // backward output pass: q, k, v, dO, B, C, four states, two sets of pair tables, boundary
+  // sums and the norm-weight partials
+  static constexpr int G_Q = 0, G_K = G_Q + NQ, G_V = G_K + NQ, G_D = G_V + NV, G_B = G_D + NCB,
+                       G_C = G_B + NB, G_S = G_C + NCB, G_A = G_S + 4 * SZS * 4,
+                       G_M = G_A + 4 * 16 * PA * 4, G_BA = G_M + 4 * 16 * PA * 4,
+                       G_BB = G_BA + DKP * 4, G_GP = G_BB + DVP * 4, G_END = G_GP + 4 * DVP * 4;
+};
+
+struct BetaArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* z;   // key-gate logits [B, L, H, dk]
+  const bf16* w;   // value-gate logits [B, L, H, dv]
+  const bf16* r;
+  const bf16* dy;
+  const float* norm_w;
+  bf16* y;
+  bf16* o_pre;
+  float* obuf;     // fp32 o [B*H][NC*64][dv] (saved), or null
+  float* states;   // [B*H][NC][dk][dv] state entering each chunk (after the scan)
+  float* dec;      // [B*H][NC][dk + dv] log2 decay of each chunk (key part, value part)
+  float* gst;      // backward: [B*H][NC][dk][dv] gradient reaching each chunk's end
+  float* dgp;      // backward: [B*H*NC][dv] norm-weight partials
+  bf16* dq;
+  bf16* dk_;
+  bf16* dv_;
+  bf16* dz;
+  bf16* dw;
+  bf16* dr;
+  int B, L, H, dk, dv, NC;
+  float inv_tau, q_scale, eps;
+};
+
+struct ChunkIx {
+  int b, h, j, valid;
+  long row0;  // element offset of (b, token 64 j, h, 0) divided by the row width
+  long bh;
+};
+__device__ __forceinline__ ChunkIx chunk_ix(const BetaArgs& p) {
+  ChunkIx c;
+  const long blk = blockIdx.x;
+  c.bh = blk / p.NC;
+  c.j = (int)(blk - c.bh * p.NC);
+  c.b = (int)(c.bh / p.H);
+  c.h = (int)(c.bh - (long)c.b * p.H);
+  c.valid = min(kBC, p.L - kBC * c.j);
+  c.row0 = ((long)c.b * p.L + (long)kBC * c.j) * p.H + c.h;
+  return c;
+}
+
+// Rows [0, valid) of a [B, L, H, n] bf16 tensor into an LDS tile of 64 rows x NP columns
+// (pitch P elements), zero elsewhere.  Row t starts at src + (row0 + t H) n.
+template <int NP, int P>
+__device__ __forceinline__ void stage_bf16(bf16* dst, const bf16* src, long row0, int H, int n,
+                                           int valid, int tid) {
+  for (int i = tid; i < kBC * NP; i += kBT) {
+    const int t = i / NP, c = i - t * NP;
+    bf16 x = from_f<bf16>(0.f);
+    if (t < valid && c < n) x = src[(row0 + (long)t * H) * n + c];
+    dst[t * P + c] = x;
+  }
+}
+// The same into fp32.
+template <int NP, int P>
+__device__ __forceinline__ void stage_f32(float* dst, const bf16* src, long row0, int H, int n,
+                                          int valid, int tid) {
+  for (int i = tid; i < kBC * NP; i += kBT) {
+    const int t = i / NP, c = i - t * NP;
+    float x = 0.f;
+    if (t < valid && c < n) x = bf(src[(row0 + (long)t * H) * n + c]);
+    dst[t * P + c] = x;
+  }
+}
+// A [dk][dv] fp32 state into [DKP][P] LDS, zero padded.
+template <int DKP, int DVP, int P>
+__device__ __forceinline__ void stage_state(float* dst, const float* src, int dk, int dv, int tid) {
+  for (int i = tid; i < DKP * DVP; i += kBT) {
+    const int c = i / DVP, e = i - c * DVP;
+    dst[c * P + e] = (c < dk && e < dv) ? src[(long)c * dv + e] : 0.f;
+  }
+}
+
+// In place: the raw logits of columns < n become the inclusive running sums over the chunk's
+// rows of log2 sigmoid(.) / tau (rows >= valid add 0).  Lanes = rows; waves take columns.
+template <int P>
+__device__ __forceinline__ void gate_cumsum(float* s, int n, int valid, float inv_tau, int wave,
+                                            int lane) {
+  for (int c = wave; c < n; c += 4) {
+    float x = lane < valid ? log2_sigmoid(s[lane * P + c]) * inv_tau : 0.f;
+    x = scan_dpp<64>(x);
+    s[lane * P + c] = x;
+  }
+}
+
+// Running-sum value at row `ref` (0 for ref < 0: the chunk start).
+__device__ __forceinline__ float at_ref(const float* s, int P, int ref, int c) {
+  return ref >= 0 ? s[ref * P + c] : 0.f;
+}
+
+// acc[ct][et] (lane: rows c = 16 ct + 4 g + i, column e = 16 et + r) =
+//   sum_{s in [s0, s0 + 16 NS)} (X[s][c] 2^{GX[end][c] - GX[s][c]}) (Y[s][e] 2^{GY[end][e] - GY[s][e]})
+// X, Y given as bf16 (pitch PX/PY) or fp32 rows; GX, GY running sums (pitch PGX/PGY).
+template <int NDK, int NDV, int NS, typename TX, int PX, int PGX, typename TY, int PY, int PGY>
+__device__ __forceinline__ void outer_sum(f32x4 (&acc)[NDK][NDV], const TX* X, const float* GX,
+                                          const TY* Y, const float* GY, int s0, int end,
+                                          float xscale, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < NDK; ++ct)
+#pragma unroll
+    for (int et = 0; et < NDV; ++et) acc[ct][et] = zero4();
+#pragma unroll 2
+  for (int ks = 0; ks < 4 * NS; ++ks) {
+    const int s = s0 + 4 * ks + g;
+    float a[NDK], b[NDV];
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct) {
+      const int c = 16 * ct + r;
+      a[ct] = xscale * to_f(X[s * PX + c]) * fexp2(GX[end * PGX + c] - GX[s * PGX + c]);
+    }
+#pragma unroll
+    for (int et = 0; et < NDV; ++et) {
+      const int e = 16 * et + r;
+      b[et] = to_f(Y[s * PY + e]) * fexp2(GY[end * PGY + e] - GY[s * PGY + e]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct)
+#pragma unroll
+      for (int et = 0; et < NDV; ++et) acc[ct][et] = mfma_f32(a[ct], b[et], acc[ct][et]);
+  }
+}
+
+// The same with the sums taken from the chunk start (2^{G[s]} factors, no end row).
+template <int NDK, int NDV, typename TX, int PX, int PGX, typename TY, int PY, int PGY>
+__device__ __forceinline__ f32x4 outer_from_start(const TX* X, const float* GX, const TY* Y,
+                                                  const float* GY, int ct, int et, float xscale,
+                                                  int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  f32x4 acc = zero4();
+  const int c = 16 * ct + r, e = 16 * et + r;
+#pragma unroll 4
+  for (int ks = 0; ks < kBC / 4; ++ks) {
+    const int s = 4 * ks + g;
+    const float a = xscale * to_f(X[s * PX + c]) * fexp2(GX[s * PGX + c]);
+    const float b = to_f(Y[s * PY + e]) * fexp2(GY[s * PGY + e]);
+    acc = mfma_f32(a, b, acc);
+  }
+  return acc;
+}
+
+template <int P, int NDK, int NDV>
+__device__ __forceinline__ void store_tiles(float* dst, const f32x4 (&acc)[NDK][NDV], int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ct = 0; ct < NDK; ++ct)
+#pragma unroll
+    for (int et = 0; et < NDV; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g + i) * P + 16 * et + r] = acc[ct][et][i];
+}
+
+// Output-stage backward for the rows t = 16 w + 4 g + i of this lane, columns e = 16 E + r:
+// dO = rstd (dn - n mean(dn n)), dn = dy norm_w Swish(r), n = o rstd, from the saved fp32 o.
+// With EXTRA also dr (stored) and the per-column sums of dy n Swish(r) (gp) and do.o (od).
+template <int NDV, bool EXTRA>
+__device__ __forceinline__ void out_stage_bwd(const BetaArgs& p, const ChunkIx& ci, int w,
+                                              int lane, float (&dO)[NDV][4], float (&od)[NDV][4],
+                                              float (&gp)[NDV]) {
+  const int r = lane & 15, g = lane >> 4;
+  const float inv_dv = 1.f / (float)p.dv;
+  float o[NDV][4], dn[NDV][4], sg[NDV][4], rr[NDV][4], dyv[NDV][4];
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* obase = p.obuf + ((ci.bh * p.NC + ci.j) * (long)kBC) * p.dv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * g + i;
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
+      const bool in = t < ci.valid && e < p.dv;
+      const long gi = (ci.row0 + (long)t * p.H) * p.dv + e;
+      o[E][i] = in ? obase[(long)t * p.dv + e] : 0.f;
+      rr[E][i] = in ? bf(p.r[gi]) : 0.f;
+      dyv[E][i] = in ? bf(p.dy[gi]) : 0.f;
+      ss[i] += o[E][i] * o[E][i];
+    }
+  }
+  float rstd[4], m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) * inv_dv + p.eps);
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+    const float nw = (p.norm_w && e < p.dv) ? p.norm_w[e] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sg[E][i] = fast_sigmoid(rr[E][i]);
+      const float s = rr[E][i] * sg[E][i];
+      dn[E][i] = dyv[E][i] * nw * s;
+      m[i] += dn[E][i] * o[E][i] * rstd[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = row_sum16(m[i]) * inv_dv;
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+    const float nw = (p.norm_w && e < p.dv) ? p.norm_w[e] : 1.f;
+    float gsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * g + i;
+      const float n = o[E][i] * rstd[i];
+      dO[E][i] = rstd[i] * (dn[E][i] - n * m[i]);
+      if constexpr (EXTRA) {
+        od[E][i] = dO[E][i] * o[E][i];
+        const float s = rr[E][i] * sg[E][i];
+        gsum += dyv[E][i] * n * s;
+        if (t < ci.valid && e < p.dv) {
+          const float d = dyv[E][i] * n * nw * sg[E][i] * (1.f + rr[E][i] * (1.f - sg[E][i]));
+          p.dr[(ci.row0 + (long)t * p.H) * p.dv + e] = from_f<bf16>(d);
+        }
+      }
+    }
+    if constexpr (EXTRA) gp[E] = gsum;
+  }
+}
+
+// ------------------------------------------------------------------------- pass 1 (forward)
+// Each chunk's state contribution U (relative to its last row) and its log2 decays.
+template <int NDK, int NDV>
+__global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
+  using Lo = BetaLay<NDK, NDV>;
+  constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sX = reinterpret_cast<float*>(smem + Lo::U_X);  // k (fp32, pitch PC)
+  float* sY = reinterpret_cast<float*>(smem + Lo::U_Y);  // v
+  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);
+  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ChunkIx ci = chunk_ix(p);
+  stage_f32<DKP, PC>(sX, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DVP, PC>(sY, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  __syncthreads();
+  gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
+  gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
+  __syncthreads();
+  const long slot = ci.bh * p.NC + ci.j;
+  const int r = lane & 15, g = lane >> 4;
+  for (int u = wave; u < NDK * NDV; u += 4) {
+    const int ct = u / NDV, et = u - ct * NDV;
+    const int c = 16 * ct + r, e = 16 * et + r;
+    f32x4 acc = zero4();
+#pragma unroll 4
+    for (int ks = 0; ks < kBC / 4; ++ks) {
+      const int s = 4 * ks + g;
+      const float a = sX[s * PC + c] * fexp2(sB[(kBC - 1) * PB + c] - sB[s * PB + c]);
+      const float b = sY[s * PC + e] * fexp2(sC[(kBC - 1) * PC + e] - sC[s * PC + e]);
+      acc = mfma_f32(a, b, acc);
+    }
+    float* dst = p.states + slot * p.dk * p.dv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cc = 16 * ct + 4 * g + i;
+      if (cc < p.dk && e < p.dv) dst[(long)cc * p.dv + e] = acc[i];
+    }
+  }
+  for (int i = tid; i < p.dk + p.dv; i += kBT)
+    p.dec[slot * (p.dk + p.dv) + i] =
+        i < p.dk ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - p.dk)];
+}
+
+// ----------------------------------------------------------------------- pass 2 (both ways)
+// In place over chunks, per (image, head) and state element (c, e):
+//   forward:  slot j <- S entering chunk j;  S <- 2^{dec_j[c] + dec_j[e]} S + U_j
+//   reverse:  slot j <- G reaching chunk j's end;  G <- 2^{dec_j[c] + dec_j[e]} G + dU_j
+constexpr int kScanBatch = 16;
+__global__ __launch_bounds__(256) void beta_scan(float* st, const float* dec, int NC, int dk,
+                                                 int dv, int reverse) {
+  const long bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= dk * dv) return;
+  const int c = idx / dv, e = idx - c * dv;
+  const long sz = (long)dk * dv;
+  float* base = st + bh * NC * sz + idx;
+  const float* d = dec + bh * NC * (dk + dv);
+  float S = 0.f;
+  for (int j0 = 0; j0 < NC; j0 += kScanBatch) {
+    float u[kScanBatch], f[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+      const int jj = min(j0 + i, NC - 1);
+      const int j = reverse ? NC - 1 - jj : jj;
+      u[i] = base[j * sz];
+      f[i] = d[(long)j * (dk + dv) + c] + d[(long)j * (dk + dv) + dk + e];
+    }
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+      if (j0 + i < NC) {
+        const int j = reverse ? NC - 1 - (j0 + i) : j0 + i;
+        base[j * sz] = S;
+        S = fexp2(f[i]) * S + u[i];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------- pass 3 (forward)
+template <int NDK, int NDV>
+__global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
+  using Lo = BetaLay<NDK, NDV>;
+  constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PQ = Lo::PQ, PV = Lo::PV, PB = Lo::PB,
+                PC = Lo::PC, PA = Lo::PA, SZS = Lo::SZS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* sQ = reinterpret_cast<bf16*>(smem + Lo::F_Q);
+  bf16* sK = reinterpret_cast<bf16*>(smem + Lo::F_K);
+  bf16* sV = reinterpret_cast<bf16*>(smem + Lo::F_V);
+  float* sB = reinterpret_cast<float*>(smem + Lo::F_B);
+  float* sC = reinterpret_cast<float*>(smem + Lo::F_C);
+  float* sS = reinterpret_cast<float*>(smem + Lo::F_S);  // S_0..S_3
+  float* sA = reinterpret_cast<float*>(smem + Lo::F_A);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const ChunkIx ci = chunk_ix(p);
+  const long slot = ci.bh * p.NC + ci.j;
+  stage_bf16<DKP, PQ>(sQ, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_bf16<DKP, PQ>(sK, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_bf16<DVP, PV>(sV, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  stage_state<DKP, DVP, PC>(sS, p.states + slot * p.dk * p.dv, p.dk, p.dv, tid);
+  __syncthreads();
+  gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
+  gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
+  __syncthreads();
+  // tile contributions U_0..U_2 (relative to each tile's last row) into S_1..S_3
+  if (wave < 3) {
+    f32x4 acc[NDK][NDV];
+    outer_sum<NDK, NDV, 1, bf16, PQ, PB, bf16, PV, PC>(acc, sK, sB, sV, sC, 16 * wave,
+                                                         16 * wave + 15, 1.f, lane);
+    store_tiles<PC>(sS + (wave + 1) * SZS, acc, lane);
+  }
+  __syncthreads();
+  // S_{w+1} = 2^{B_w + C_w} S_w + U_w, elementwise, each thread the same elements throughout
+  for (int i = tid; i < DKP * DVP; i += kBT) {
+    const int c = i / DVP, e = i - c * DVP;
+    float S = sS[c * PC + e];
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const float d = (sB[(16 * w + 15) * PB + c] - at_ref(sB, PB, 16 * w - 1, c)) +
+                      (sC[(16 * w + 15) * PC + e] - at_ref(sC, PC, 16 * w - 1, e));
+      S = fexp2(d) * S + sS[(w + 1) * SZS + c * PC + e];
+      sS[(w + 1) * SZS + c * PC + e] = S;
+    }
+  }
+  __syncthreads();
+  const int w = wave, t0 = 16 * w, ref = t0 - 1;
+  // across tiles: (q_t 2^{B_t - B_ref}) S_w, then 2^{C_t - C_ref}
+  f32x4 acc[NDV];
+  {
+    float a[DKP / 4];
+#pragma unroll
+    for (int ks = 0; ks < DKP / 4; ++ks) {
+      const int c = 4 * ks + g, t = t0 + r;
+      a[ks] = p.q_scale * bf(sQ[t * PQ + c]) * fexp2(sB[t * PB + c] - at_ref(sB, PB, ref, c));
+    }
+    const float* S = sS + w * SZS;
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      acc[E] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKP / 4; ++ks)
+        acc[E] = mfma_f32(a[ks], S[(4 * ks + g) * PC + 16 * E + r], acc[E]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * g + i, e = 16 * E + r;
+        acc[E][i] *= fexp2(sC[t * PC + e] - at_ref(sC, PC, ref, e));
+      }
+    }
+  }
+  // inside the tile: pair weights A[t][s] = q_scale sum_c q_t k_s 2^{B_t - B_s}, s <= t
+  float* myA = sA + w * 16 * PA;
+  {
+    const int tl = r, sg = 4 * g;
+    float pa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = 0; c < DKP; ++c) {
+      const float qv = bf(sQ[(t0 + tl) * PQ + c]), bt = sB[(t0 + tl) * PB + c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = t0 + sg + i;
+        pa[i] += qv * bf(sK[s * PQ + c]) * fexp2(fminf(bt - sB[s * PB + c], 0.f));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) myA[tl * PA + sg + i] = (sg + i <= tl) ? p.q_scale * pa[i] : 0.f;
+  }
+  __syncthreads();
+  // o_t += sum_{s <= t in tile} A[t][s] v_s 2^{C_t - C_s}
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tl = 4 * g + i, t = t0 + tl;
+      const float ct = sC[t * PC + e];
+      float sum = 0.f;
+      for (int sl = 0; sl <= 12 + i; ++sl) {
+        const int s = t0 + sl;
+        const float term = myA[tl * PA + sl] * bf(sV[s * PV + e]) *
+                           fexp2(fminf(ct - sC[s * PC + e], 0.f));
+        sum += sl <= tl ? term : 0.f;
+      }
+      acc[E][i] += sum;
+    }
+  }
+  // output stage
+  const float inv_dv = 1.f / (float)p.dv;
+  float rstd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float ss = 0.f;
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) ss += acc[E][i] * acc[E][i];
+    rstd[i] = rsqrtf(row_sum16(ss) * inv_dv + p.eps);
+  }
+  float* obase = p.obuf ? p.obuf + (slot * (long)kBC) * p.dv : nullptr;
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+    if (e >= p.dv) continue;
+    const float nw = p.norm_w ? p.norm_w[e] : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      if (t >= ci.valid) continue;
+      const long gi = (ci.row0 + (long)t * p.H) * p.dv + e;
+      const float o = acc[E][i];
+      if (obase) obase[(long)t * p.dv + e] = o;
+      if (p.o_pre) p.o_pre[gi] = from_f<bf16>(o);
+      const float rv = bf(p.r[gi]);
+      p.y[gi] = from_f<bf16>(o * rstd[i] * nw * rv * fast_sigmoid(rv));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ pass 1 (backward)
+// Each chunk's gradient-state contribution dU = sum_t (q_scale q_t 2^{B_t})^T (dO_t 2^{C_t})
+// (relative to the chunk start) and its log2 decays.
+template <int NDK, int NDV>
+__global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
+  using Lo = BetaLay<NDK, NDV>;
+  constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sX = reinterpret_cast<float*>(smem + Lo::U_X);  // q (fp32, pitch PC)
+  float* sY = reinterpret_cast<float*>(smem + Lo::U_Y);  // dO
+  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);
+  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const ChunkIx ci = chunk_ix(p);
+  stage_f32<DKP, PC>(sX, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  {
+    float dO[NDV][4], od[NDV][4], gp[NDV];
+    out_stage_bwd<NDV, false>(p, ci, wave, lane, dO, od, gp);
+#pragma unroll
+    for (int E = 0; E < NDV; ++E)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sY[(16 * wave + 4 * g + i) * PC + 16 * E + r] = dO[E][i];
+  }
+  __syncthreads();
+  gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
+  gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
+  __syncthreads();
+  const long slot = ci.bh * p.NC + ci.j;
+  for (int u = wave; u < NDK * NDV; u += 4) {
+    const int ct = u / NDV, et = u - ct * NDV;
+    const f32x4 acc = outer_from_start<NDK, NDV, float, PC, PB, float, PC, PC>(
+        sX, sB, sY, sC, ct, et, p.q_scale, lane);
+    float* dst = p.gst + slot * p.dk * p.dv;
+    const int e = 16 * et + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * ct + 4 * g + i;
+      if (c < p.dk && e < p.dv) dst[(long)c * p.dv + e] = acc[i];
+    }
+  }
+  for (int i = tid; i < p.dk + p.dv; i += kBT)
+    p.dec[slot * (p.dk + p.dv) + i] =
+        i < p.dk ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - p.dk)];
+}
+
+// ------------------------------------------------------------------------ pass 3 (backward)
+template <int NDK, int NDV>
+__global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
+  using Lo = BetaLay<NDK, NDV>;
+  constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PQ = Lo::PQ, PV = Lo::PV, PB = Lo::PB,
+                PC = Lo::PC, PA = Lo::PA, SZS = Lo::SZS;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* sQ = reinterpret_cast<bf16*>(smem + Lo::G_Q);
+  bf16* sK = reinterpret_cast<bf16*>(smem + Lo::G_K);
+  bf16* sV = reinterpret_cast<bf16*>(smem + Lo::G_V);
+  float* sD = reinterpret_cast<float*>(smem + Lo::G_D);  // dO
+  float* sB = reinterpret_cast<float*>(smem + Lo::G_B);
+  float* sC = reinterpret_cast<float*>(smem + Lo::G_C);
+  float* sS = reinterpret_cast<float*>(smem + Lo::G_S);  // S_0..S_3, then G_0..G_3
+  float* sA = reinterpret_cast<float*>(smem + Lo::G_A);
+  float* sM = reinterpret_cast<float*>(smem + Lo::G_M);
+  float* sBa = reinterpret_cast<float*>(smem + Lo::G_BA);
+  float* sBb = reinterpret_cast<float*>(smem + Lo::G_BB);
+  float* sGp = reinterpret_cast<float*>(smem + Lo::G_GP);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const ChunkIx ci = chunk_ix(p);
+  const long slot = ci.bh * p.NC + ci.j;
+  const long sz = (long)p.dk * p.dv;
+  const int w = wave, t0 = 16 * w, ref = t0 - 1, end = t0 + 15;
+  stage_bf16<DKP, PQ>(sQ, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_bf16<DKP, PQ>(sK, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_bf16<DVP, PV>(sV, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  stage_state<DKP, DVP, PC>(sS, p.states + slot * sz, p.dk, p.dv, tid);
+  float od[NDV][4];
+  {
+    float dO[NDV][4], gp[NDV];
+    out_stage_bwd<NDV, true>(p, ci, w, lane, dO, od, gp);
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sD[(t0 + 4 * g + i) * PC + 16 * E + r] = dO[E][i];
+      // norm-weight partial: this wave's 16 rows, summed over the lane groups below
+      float x = gp[E];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (g == 0) sGp[w * DVP + 16 * E + r] = x;
+    }
+  }
+  // boundary sums with the state leaving the chunk (the next chunk's entering state)
+  const bool has_end = ci.j + 1 < p.NC;
+  if (tid < DKP) {
+    float x = 0.f;
+    if (has_end && tid < p.dk) {
+      const float* se = p.states + (slot + 1) * sz + (long)tid * p.dv;
+      const float* ge = p.gst + slot * sz + (long)tid * p.dv;
+      for (int e = 0; e < p.dv; ++e) x += se[e] * ge[e];
+    }
+    sBa[tid] = x;
+  } else if (tid < DKP + DVP) {
+    const int e = tid - DKP;
+    float x = 0.f;
+    if (has_end && e < p.dv) {
+      const float* se = p.states + (slot + 1) * sz + e;
+      const float* ge = p.gst + slot * sz + e;
+      for (int c = 0; c < p.dk; ++c) x += se[(long)c * p.dv] * ge[(long)c * p.dv];
+    }
+    sBb[e] = x;
+  }
+  __syncthreads();
+  if (tid < DVP && p.dgp && tid < p.dv)
+    p.dgp[slot * p.dv + tid] = (sGp[tid] + sGp[DVP + tid]) + (sGp[2 * DVP + tid] + sGp[3 * DVP + tid]);
+  gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
+  gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
+  __syncthreads();
+
+  // ---- forward tile states S_1..S_3 (as in the forward output pass)
+  if (w < 3) {
+    f32x4 acc[NDK][NDV];
+    outer_sum<NDK, NDV, 1, bf16, PQ, PB, bf16, PV, PC>(acc, sK, sB, sV, sC, t0, end, 1.f, lane);
+    store_tiles<PC>(sS + (w + 1) * SZS, acc, lane);
+  }
+  __syncthreads();
+  for (int i = tid; i < DKP * DVP; i += kBT) {
+    const int c = i / DVP, e = i - c * DVP;
+    float S = sS[c * PC + e];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const float d = (sB[(16 * u + 15) * PB + c] - at_ref(sB, PB, 16 * u - 1, c)) +
+                      (sC[(16 * u + 15) * PC + e] - at_ref(sC, PC, 16 * u - 1, e));
+      S = fexp2(d) * S + sS[(u + 1) * SZS + c * PC + e];
+      sS[(u + 1) * SZS + c * PC + e] = S;
+    }
+  }
+  __syncthreads();
+  // dq across tiles: q_scale 2^{B_t - B_ref} sum_e (dO_t 2^{C_t - C_ref})[e] S_w[c][e]
+  f32x4 dqa[NDK];
+  {
+    float a[DVP / 4];
+#pragma unroll
+    for (int ks = 0; ks < DVP / 4; ++ks) {
+      const int e = 4 * ks + g, t = t0 + r;
+      a[ks] = sD[t * PC + e] * fexp2(sC[t * PC + e] - at_ref(sC, PC, ref, e));
+    }
+    const float* S = sS + w * SZS;
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct) {
+      dqa[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DVP / 4; ++ks)
+        dqa[ct] = mfma_f32(a[ks], S[(16 * ct + r) * PC + 4 * ks + g], dqa[ct]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * g + i, c = 16 * ct + r;
+        dqa[ct][i] *= p.q_scale * fexp2(sB[t * PB + c] - at_ref(sB, PB, ref, c));
+      }
+    }
+  }
+  __syncthreads();  // every read of S_w done
+  // ---- gradient tile states: G_3 = gradient reaching the chunk's end; tile contributions
+  // dU_1..dU_3 (relative to each tile's start) into slots 0..2; then
+  // G_{u-1} = 2^{B_u + C_u} G_u + dU_u
+  stage_state<DKP, DVP, PC>(sS + 3 * SZS, p.gst + slot * sz, p.dk, p.dv, tid);
+  if (w >= 1) {
+    const int s0 = t0, rf = t0 - 1;
+    const int r_ = lane & 15, g_ = lane >> 4;
+    f32x4 acc[NDK][NDV];
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct)
+#pragma unroll
+      for (int et = 0; et < NDV; ++et) acc[ct][et] = zero4();
+#pragma unroll 2
+    for (int ks = 0; ks < 4; ++ks) {
+      const int t = s0 + 4 * ks + g_;
+      float a[NDK], b[NDV];
+#pragma unroll
+      for (int ct = 0; ct < NDK; ++ct) {
+        const int c = 16 * ct + r_;
+        a[ct] = p.q_scale * bf(sQ[t * PQ + c]) * fexp2(sB[t * PB + c] - sB[rf * PB + c]);
+      }
+#pragma unroll
+      for (int et = 0; et < NDV; ++et) {
+        const int e = 16 * et + r_;
+        b[et] = sD[t * PC + e] * fexp2(sC[t * PC + e] - sC[rf * PC + e]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NDK; ++ct)
+#pragma unroll
+        for (int et = 0; et < NDV; ++et) acc[ct][et] = mfma_f32(a[ct], b[et], acc[ct][et]);
+    }
+    store_tiles<PC>(sS + (w - 1) * SZS, acc, lane);
+  }
+  __syncthreads();
+  for (int i = tid; i < DKP * DVP; i += kBT) {
+    const int c = i / DVP, e = i - c * DVP;
+    float G = sS[3 * SZS + c * PC + e];
+#pragma unroll
+    for (int u = 3; u >= 1; --u) {
+      const float d = (sB[(16 * u + 15) * PB + c] - sB[(16 * u - 1) * PB + c]) +
+                      (sC[(16 * u + 15) * PC + e] - sC[(16 * u - 1) * PC + e]);
+      G = fexp2(d) * G + sS[(u - 1) * SZS + c * PC + e];
+      sS[(u - 1) * SZS + c * PC + e] = G;
+    }
+  }
+  __syncthreads();
+  // dk, dv across tiles from G_w (gradient reaching the tile's last row):
+  //   dk_s[c] = 2^{B_end - B_s} sum_e (v_s 2^{C_end - C_s})[e] G_w[c][e]
+  //   dv_s[e] = 2^{C_end - C_s} sum_c (k_s 2^{B_end - B_s})[c] G_w[c][e]
+  f32x4 dka[NDK], dva[NDV];
+  {
+    const float* G = sS + w * SZS;
+    float a[DVP / 4];
+#pragma unroll
+    for (int ks = 0; ks < DVP / 4; ++ks) {
+      const int e = 4 * ks + g, s = t0 + r;
+      a[ks] = bf(sV[s * PV + e]) * fexp2(sC[end * PC + e] - sC[s * PC + e]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct) {
+      dka[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DVP / 4; ++ks)
+        dka[ct] = mfma_f32(a[ks], G[(16 * ct + r) * PC + 4 * ks + g], dka[ct]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = t0 + 4 * g + i, c = 16 * ct + r;
+        dka[ct][i] *= fexp2(sB[end * PB + c] - sB[s * PB + c]);
+      }
+    }
+    float b[DKP / 4];
+#pragma unroll
+    for (int ks = 0; ks < DKP / 4; ++ks) {
+      const int c = 4 * ks + g, s = t0 + r;
+      b[ks] = bf(sK[s * PQ + c]) * fexp2(sB[end * PB + c] - sB[s * PB + c]);
+    }
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      dva[E] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DKP / 4; ++ks)
+        dva[E] = mfma_f32(b[ks], G[(4 * ks + g) * PC + 16 * E + r], dva[E]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = t0 + 4 * g + i, e = 16 * E + r;
+        dva[E][i] *= fexp2(sC[end * PC + e] - sC[s * PC + e]);
+      }
+    }
+  }
+  // ---- inside the tile: pair tables A[t][s] (q_scale included) and M[t][s] = sum_e dO_t v_s
+  // 2^{C_t - C_s}, s <= t
+  float* myA = sA + w * 16 * PA;
+  float* myM = sM + w * 16 * PA;
+  {
+    const int tl = r, sg = 4 * g, t = t0 + tl;
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = 0; c < DKP; ++c) {
+      const float qv = bf(sQ[t * PQ + c]), bt = sB[t * PB + c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = t0 + sg + i;
+        pa[i] += qv * bf(sK[s * PQ + c]) * fexp2(fminf(bt - sB[s * PB + c], 0.f));
+      }
+    }
+#pragma unroll 4
+    for (int e = 0; e < DVP; ++e) {
+      const float dov = sD[t * PC + e], ctv = sC[t * PC + e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = t0 + sg + i;
+        pm[i] += dov * bf(sV[s * PV + e]) * fexp2(fminf(ctv - sC[s * PC + e], 0.f));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool on = sg + i <= tl;
+      myA[tl * PA + sg + i] = on ? p.q_scale * pa[i] : 0.f;
+      myM[tl * PA + sg + i] = on ? pm[i] : 0.f;
+    }
+  }
+  __syncthreads();
+  // dq_t[c] += q_scale sum_{s <= t} M[t][s] k_s[c] 2^{B_t - B_s}
+  // dk_s[c] += q_scale sum_{t >= s} M[t][s] q_t[c] 2^{B_t - B_s}
+#pragma unroll
+  for (int ct = 0; ct < NDK; ++ct) {
+    const int c = 16 * ct + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int xl = 4 * g + i, x = t0 + xl;
+      const float bx = sB[x * PB + c];
+      float sq = 0.f, sk = 0.f;
+      for (int ul = 0; ul < 16; ++ul) {
+        const int u = t0 + ul;
+        // u as the key (u <= x) for dq, as the query (u >= x) for dk: one factor
+        // 2^{-|B_x - B_u|} serves both
+        const float f = fexp2(-fabsf(bx - sB[u * PB + c]));
+        const float tq = myM[xl * PA + ul] * bf(sK[u * PQ + c]) * f;
+        const float tk = myM[ul * PA + xl] * bf(sQ[u * PQ + c]) * f;
+        sq += ul <= xl ? tq : 0.f;
+        sk += ul >= xl ? tk : 0.f;
+      }
+      dqa[ct][i] += p.q_scale * sq;
+      dka[ct][i] += p.q_scale * sk;
+    }
+  }
+  // dv_s[e] += sum_{t >= s} A[t][s] dO_t[e] 2^{C_t - C_s}
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = 4 * g + i, s = t0 + sl;
+      const float cs = sC[s * PC + e];
+      float sum = 0.f;
+      for (int ul = i; ul < 16; ++ul) {
+        const int u = t0 + ul;
+        const float term = myA[ul * PA + sl] * sD[u * PC + e] * fexp2(fminf(sC[u * PC + e] - cs, 0.f));
+        sum += ul >= sl ? term : 0.f;
+      }
+      dva[E][i] += sum;
+    }
+  }
+  // ---- gate gradients: per-row terms, suffix sums over the chunk, boundary sums
+  __syncthreads();  // every read of B, C done: their regions take the per-row terms
+#pragma unroll
+  for (int ct = 0; ct < NDK; ++ct) {
+    const int c = 16 * ct + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      sB[t * PB + c] = bf(sQ[t * PQ + c]) * dqa[ct][i] - bf(sK[t * PQ + c]) * dka[ct][i];
+    }
+  }
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) {
+    const int e = 16 * E + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      sC[t * PC + e] = od[E][i] - bf(sV[t * PV + e]) * dva[E][i];
+    }
+  }
+  __syncthreads();
+  {
+    const int t = kBC - 1 - lane;  // lanes walk the rows backwards: a prefix is a suffix
+    for (int c = wave; c < p.dk; c += 4) {
+      const float x = scan_dpp<64>(sB[t * PB + c]) + sBa[c];
+      if (t < ci.valid) {
+        const long gi = (ci.row0 + (long)t * p.H) * p.dk + c;
+        p.dz[gi] = from_f<bf16>(x * fast_sigmoid(-bf(p.z[gi])) * p.inv_tau);
+      }
+    }
+    for (int e = wave; e < p.dv; e += 4) {
+      const float x = scan_dpp<64>(sC[t * PC + e]) + sBb[e];
+      if (t < ci.valid) {
+        const long gi = (ci.row0 + (long)t * p.H) * p.dv + e;
+        p.dw[gi] = from_f<bf16>(x * fast_sigmoid(-bf(p.w[gi])) * p.inv_tau);
+      }
+    }
+  }
+  // ---- dq, dk, dv
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * g + i;
+    if (t >= ci.valid) continue;
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct) {
+      const int c = 16 * ct + r;
+      if (c < p.dk) {
+        const long gi = (ci.row0 + (long)t * p.H) * p.dk + c;
+        p.dq[gi] = from_f<bf16>(dqa[ct][i]);
+        p.dk_[gi] = from_f<bf16>(dka[ct][i]);
+      }
+    }
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
+      if (e < p.dv) p.dv_[(ci.row0 + (long)t * p.H) * p.dv + e] = from_f<bf16>(dva[E][i]);
+    }
+  }
+}
+
+// d_norm_w[e] = sum over chunks of the partials, in a fixed order.
+__global__ __launch_bounds__(256) void beta_dgamma_reduce(const float* part, long nparts, int dv,
+                                                          float* out) {
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  float x = 0.f;
+  for (long i = threadIdx.x; i < nparts; i += 256) x += part[i * dv + e];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[e] = red[0];
+}
+
+template <int NDK, int NDV>
+hipError_t launch_beta(const GlaShape& s, const BetaArgs& a, bool bwd, hipStream_t st) {
+  using Lo = BetaLay<NDK, NDV>;
+  const unsigned grid = (unsigned)((long)s.B * s.H * s.NC);
+  const dim3 sgrid((unsigned)((s.dk * s.dv + 255) / 256), (unsigned)(s.B * s.H));
+  if (!bwd) {
+    hipLaunchKernelGGL((beta_fwd_state<NDK, NDV>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
+    hipLaunchKernelGGL(beta_scan, sgrid, dim3(256), 0, st, a.states, a.dec, s.NC, s.dk, s.dv, 0);
+    hipLaunchKernelGGL((beta_fwd_out<NDK, NDV>), dim3(grid), dim3(kBT), Lo::F_END, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((beta_bwd_state<NDK, NDV>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
+  hipLaunchKernelGGL(beta_scan, sgrid, dim3(256), 0, st, a.gst, a.dec, s.NC, s.dk, s.dv, 1);
+  hipLaunchKernelGGL((beta_bwd_out<NDK, NDV>), dim3(grid), dim3(kBT), Lo::G_END, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gla_beta_lds_bytes(const GlaShape& s, bool bwd) {
+  switch (s.ndk * 16 + s.ndv) {
+    case 1 * 16 + 2: return bwd ? BetaLay<1, 2>::G_END : BetaLay<1, 2>::F_END;
+    case 2 * 16 + 4: return bwd ? BetaLay<2, 4>::G_END : BetaLay<2, 4>::F_END;
+    case 3 * 16 + 5: return bwd ? BetaLay<3, 5>::G_END : BetaLay<3, 5>::F_END;
+    default: return 1 << 30;  // no kernel for this class
+  }
+}
+
+static size_t al256b(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t gla_beta_states_bytes(const GlaShape& s) {
+  return (size_t)s.B * s.H * s.NC * s.dk * s.dv * sizeof(float);
+}
+size_t gla_beta_obuf_bytes(const GlaShape& s) {
+  return (size_t)s.B * s.H * s.NC * kBC * s.dv * sizeof(float);
+}
+size_t gla_beta_saved_bytes(const GlaShape& s) {
+  return al256b(gla_beta_states_bytes(s)) + al256b(gla_beta_obuf_bytes(s));
+}
+size_t gla_beta_dec_bytes(const GlaShape& s) {
+  return (size_t)s.B * s.H * s.NC * (s.dk + s.dv) * sizeof(float);
+}
+size_t gla_beta_fwd_workspace(const GlaShape& s) {
+  return al256b(gla_beta_states_bytes(s)) + al256b(gla_beta_dec_bytes(s));
+}
+size_t gla_beta_bwd_workspace(const GlaShape& s) {
+  return al256b(gla_beta_states_bytes(s)) + al256b(gla_beta_dec_bytes(s)) +
+         al256b((size_t)s.B * s.H * s.NC * s.dv * sizeof(float));
+}
+
+hipError_t launch_gla_beta_fwd(const GlaShape& s, const GlaBetaFwd& f, hipStream_t st) {
+  BetaArgs a{};
+  a.q = static_cast<const bf16*>(f.q); a.k = static_cast<const bf16*>(f.k);
+  a.v = static_cast<const bf16*>(f.v); a.z = static_cast<const bf16*>(f.z);
+  a.w = static_cast<const bf16*>(f.w); a.r = static_cast<const bf16*>(f.r);
+  a.norm_w = f.norm_w;
+  a.y = static_cast<bf16*>(f.y); a.o_pre = static_cast<bf16*>(f.o_pre);
+  char* ws = static_cast<char*>(f.workspace);
+  if (f.saved) {
+    a.states = static_cast<float*>(f.saved);
+    a.obuf = reinterpret_cast<float*>(static_cast<char*>(f.saved) +
+                                      al256b(gla_beta_states_bytes(s)));
+  } else {
+    a.states = reinterpret_cast<float*>(ws);
+  }
+  a.dec = reinterpret_cast<float*>(ws + al256b(gla_beta_states_bytes(s)));
+  a.B = s.B; a.L = s.L; a.H = s.H; a.dk = s.dk; a.dv = s.dv; a.NC = s.NC;
+  a.inv_tau = f.inv_tau; a.q_scale = f.q_scale; a.eps = f.eps;
+  switch (s.ndk * 16 + s.ndv) {
+    case 1 * 16 + 2: return launch_beta<1, 2>(s, a, false, st);
+    case 2 * 16 + 4: return launch_beta<2, 4>(s, a, false, st);
+    case 3 * 16 + 5: return launch_beta<3, 5>(s, a, false, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gla_beta_bwd(const GlaShape& s, const GlaBetaBwd& f, hipStream_t st) {
+  BetaArgs a{};
+  a.q = static_cast<const bf16*>(f.q); a.k = static_cast<const bf16*>(f.k);
+  a.v = static_cast<const bf16*>(f.v); a.z = static_cast<const bf16*>(f.z);
+  a.w = static_cast<const bf16*>(f.w); a.r = static_cast<const bf16*>(f.r);
+  a.dy = static_cast<const bf16*>(f.dy);
+  a.norm_w = f.norm_w;
+  a.states = const_cast<float*>(static_cast<const float*>(f.saved));
+  a.obuf = reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(f.saved)) +
+                                    al256b(gla_beta_states_bytes(s)));
+  char* ws = static_cast<char*>(f.workspace);
+  a.gst = reinterpret_cast<float*>(ws);
+  a.dec = reinterpret_cast<float*>(ws + al256b(gla_beta_states_bytes(s)));
+  a.dgp = reinterpret_cast<float*>(ws + al256b(gla_beta_states_bytes(s)) +
+                                   al256b(gla_beta_dec_bytes(s)));
+  a.dq = static_cast<bf16*>(f.dq); a.dk_ = static_cast<bf16*>(f.dk);
+  a.dv_ = static_cast<bf16*>(f.dv); a.dz = static_cast<bf16*>(f.dz);
+  a.dw = static_cast<bf16*>(f.dw); a.dr = static_cast<bf16*>(f.dr);
+  a.B = s.B; a.L = s.L; a.H = s.H; a.dk = s.dk; a.dv = s.dv; a.NC = s.NC;
+  a.inv_tau = f.inv_tau; a.q_scale = f.q_scale; a.eps = f.eps;
+  hipError_t e;
+  switch (s.ndk * 16 + s.ndv) {
+    case 1 * 16 + 2: e = launch_beta<1, 2>(s, a, true, st); break;
+    case 2 * 16 + 4: e = launch_beta<2, 4>(s, a, true, st); break;
+    case 3 * 16 + 5: e = launch_beta<3, 5>(s, a, true, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || !f.d_norm_w) return e;
+  hipLaunchKernelGGL(beta_dgamma_reduce, dim3((unsigned)s.dv), dim3(256), 0, st, a.dgp,
+                     (long)s.B * s.H * s.NC, s.dv, f.d_norm_w);
+  return hipGetLastError();
+}
+
+}  // namespace dig

@@ -177,6 +177,54 @@ dig_status dig_gla_bwd_lowrank(const dig_gla_desc* desc, const void* q, const vo
                                float* d_norm_w, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/*
+ * The general gate of eq. (5) (slides, slide "GLA の導入"): G_t = alpha_t^T beta_t, a key-side
+ * gate alpha_t (d_k) times a value-side gate beta_t (d_v), both sigmoid(logit)^(1/tau):
+ *   S_t = (alpha_t^T beta_t) (.) S_{t-1} + k_t^T v_t,  o_t = (q_scale q_t) S_t,
+ * output stage as dig_gla_fwd.  DiG itself runs beta = 1 (dig_gla_fwd); these calls are the
+ * variant with a value gate.  desc->dtype must be DIG_BF16, desc->chunk 64, d_k <= 48 and
+ * d_v <= 80 with d_k <= 16, d_v <= 32 or d_k <= 32, d_v <= 64 or d_k <= 48, d_v <= 80
+ * (DIG_ERR_UNSUPPORTED otherwise); desc->seg_chunks is ignored.  Every gate strength is
+ * exact: no factor 2^x with x > 0 is ever formed.
+ *
+ * Bytes of the forward->backward buffer (opaque; regions 256-byte aligned): the fp32 state
+ * entering every 64-token chunk, [B][H][ceil(L/64)][d_k][d_v], then the fp32 pre-norm
+ * output of every token.  0 for a descriptor these calls reject.
+ */
+size_t dig_gla_beta_saved_bytes(const dig_gla_desc* desc);
+/* Workspace bytes of dig_gla_fwd_beta (chunk states and decays) and dig_gla_bwd_beta
+ * (gradient states, decays, norm-weight partials).  0 for a rejected descriptor. */
+size_t dig_gla_beta_fwd_workspace_bytes(const dig_gla_desc* desc);
+size_t dig_gla_beta_bwd_workspace_bytes(const dig_gla_desc* desc);
+
+/*
+ * dig_gla_fwd_beta -- forward with both gates.
+ *   q, k, gate_logit : [B, L, H, d_k] bf16;  v, value_gate_logit, r : [B, L, H, d_v] bf16
+ *   norm_w, y, o_pre_opt : as dig_gla_fwd
+ *   saved_opt        : dig_gla_beta_saved_bytes() bytes for dig_gla_bwd_beta, or NULL
+ *   workspace        : dig_gla_beta_fwd_workspace_bytes() bytes
+ * Errors as dig_gla_fwd.
+ */
+dig_status dig_gla_fwd_beta(const dig_gla_desc* desc, const void* q, const void* k,
+                            const void* v, const void* gate_logit, const void* value_gate_logit,
+                            const void* r, const float* norm_w, void* y, void* o_pre_opt,
+                            void* saved_opt, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * dig_gla_bwd_beta -- gradients of <dy, y> for dig_gla_fwd_beta, given its `saved`:
+ *   dq, dk, d_gate_logit : [B, L, H, d_k];  dv, d_value_gate_logit, dr : [B, L, H, d_v]
+ *   d_norm_w             : [d_v] fp32 (overwritten; fixed-order sum), or NULL
+ * d_gate_logit = dlog(alpha) sigmoid(-z) / tau, d_value_gate_logit = dlog(beta) sigmoid(-w) /
+ * tau.  Workspace: dig_gla_beta_bwd_workspace_bytes().  Errors as dig_gla_bwd.
+ */
+dig_status dig_gla_bwd_beta(const dig_gla_desc* desc, const void* q, const void* k,
+                            const void* v, const void* gate_logit, const void* value_gate_logit,
+                            const void* r, const float* norm_w, const void* dy,
+                            const void* saved, void* dq, void* dk, void* dv, void* d_gate_logit,
+                            void* d_value_gate_logit, void* dr, float* d_norm_w,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ projections */
 
 /*

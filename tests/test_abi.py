@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(dig.EXPORTS) == declared
-    assert dig.dig_abi_version() == 104
+    assert dig.dig_abi_version() == 105
 
 
 def test_status_strings():

@@ -1,0 +1,192 @@
+"""GPU parity of the mixer with the general gate of eq. (5), G_t = alpha_t^T beta_t
+(dig_gla_fwd_beta / dig_gla_bwd_beta), against the fp64 oracle (oracle.gla_fwd_beta /
+oracle.gla_bwd_beta, the token-by-token recurrence with both gates).
+
+Both sides get the same bf16-quantised q, k, v, key-gate logits z, value-gate logits w, r, dy
+and fp32 norm weight.  Bar: normwise max-relative error <= 2e-2 per output (bf16 I/O), outputs
+NaN-poisoned before each call.  Shapes: the exact DiG head shapes (S: 32/64, XL: 36/72), the
+16/32 class and tile classes, ragged tails, one chunk and many, gate stress (strong decay on
+either side, saturated gates, wide logits), beta = 1 against the key-gate-only call, the full
+DiG-XL/2 2048-px layer, determinism and argument errors.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import TOL, announce, empty, has_gpu, maxrel, nbytes_buf, to_dev, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+GRADS = ("dq", "dk", "dv", "dz", "dw", "dr")
+
+
+def _case(name, seed, *, batch=None, seq_len=None, dk=None, dv=None, z_std=None, gate_bias=0.0,
+          w_std=1.0, w_mean=0.0):
+    cfg = W.CONFIGS[name]
+    if dk is not None:
+        cfg = W.cfg_replace(cfg, d_k=dk, d_v=dv)
+    case = W.make_gla_case(cfg, seed, batch=batch, seq_len=seq_len, random_gamma=True,
+                           z_std=z_std, gate_bias=gate_bias)
+    B, L, H, _ = case.q.shape
+    w = W.make_value_gate_logits(cfg, seed, batch=B, seq_len=L, std=w_std, mean=w_mean)
+    return case, w
+
+
+def beta_forward(case, w, *, want_saved=True, tau=16.0, q_scale=1.0, eps=1e-5):
+    import torch
+    import diffusion_backbone_amd as dig
+    B, L, H, dk = case.q.shape
+    dv = case.v.shape[-1]
+    desc = dig.make_desc(B, L, H, dk, dv, 64, tau, q_scale, eps, "bf16", 0)
+    d = {n: to_dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "z", "r")}
+    d["w"] = to_dev(w, "bf16")
+    d["gamma"] = torch.from_numpy(case.gamma.astype(np.float32)).cuda()
+    d["y"] = empty((B, L, H, dv), "bf16")
+    d["o_pre"] = empty((B, L, H, dv), "bf16")
+    d["saved"] = nbytes_buf(dig.dig_gla_beta_saved_bytes(desc)) if want_saved else None
+    wsb = dig.dig_gla_beta_fwd_workspace_bytes(desc)
+    d["ws"] = nbytes_buf(wsb)
+    dig.dig_gla_fwd_beta(desc, d["q"], d["k"], d["v"], d["z"], d["w"], d["r"], d["gamma"],
+                         d["y"], d["o_pre"], d["saved"], d["ws"], wsb)
+    d["desc"] = desc
+    return d
+
+
+def beta_backward(case, f):
+    import torch
+    import diffusion_backbone_amd as dig
+    B, L, H, dk = case.q.shape
+    dv = case.v.shape[-1]
+    g = {"dy": to_dev(case.dy, "bf16")}
+    for n, d in (("dq", dk), ("dk", dk), ("dz", dk), ("dv", dv), ("dw", dv), ("dr", dv)):
+        g[n] = empty((B, L, H, d), "bf16")
+    g["dgamma"] = torch.full((dv,), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = dig.dig_gla_beta_bwd_workspace_bytes(f["desc"])
+    g["ws"] = nbytes_buf(wsb)
+    dig.dig_gla_bwd_beta(f["desc"], f["q"], f["k"], f["v"], f["z"], f["w"], f["r"], f["gamma"],
+                         g["dy"], f["saved"], g["dq"], g["dk"], g["dv"], g["dz"], g["dw"],
+                         g["dr"], g["dgamma"], g["ws"], wsb)
+    return g
+
+
+def _check(case, w, what, bwd=True):
+    f = beta_forward(case, w, want_saved=bwd)
+    y_ref, o_ref, _ = oracle.gla_fwd_beta(case.q, case.k, case.v, case.z, w, case.r, case.gamma)
+    errs = {"y": maxrel(to_f64(f["y"]), y_ref), "o_pre": maxrel(to_f64(f["o_pre"]), o_ref)}
+    if bwd:
+        g = beta_backward(case, f)
+        ref = oracle.gla_bwd_beta(case.q, case.k, case.v, case.z, w, case.r, case.dy, case.gamma)
+        for n in GRADS:
+            errs[n] = maxrel(to_f64(g[n]), ref[n])
+        errs["dgamma"] = maxrel(g["dgamma"].cpu().numpy().astype(np.float64), ref["dgamma"])
+    print("  %s " % what + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
+    return f
+
+
+@pytest.mark.parametrize("name,batch,seq_len", [
+    ("dig_s2_256", 2, 256),      # S head shape (32/64), four chunks
+    ("dig_s2_256", 1, 200),      # S, ragged last chunk
+    ("dig_xl2_2048", 1, 256),    # XL head shape (36/72)
+    ("dig_xl2_2048", 2, 87),     # XL, ragged
+    ("dig_xl2_2048", 1, 50),     # one partial chunk
+    ("dig_xl2_2048", 1, 1000),   # many chunks
+])
+def test_beta_exact_shapes(name, batch, seq_len):
+    announce("beta %s B=%d L=%d" % (name, batch, seq_len))
+    case, w = _case(name, 100 + seq_len, batch=batch, seq_len=seq_len)
+    _check(case, w, name)
+
+
+@pytest.mark.parametrize("dk,dv,seq_len", [(16, 32, 130), (20, 40, 77), (40, 72, 150),
+                                           (48, 80, 64), (7, 13, 70)])
+def test_beta_tile_classes(dk, dv, seq_len):
+    announce("beta tile class dk=%d dv=%d L=%d" % (dk, dv, seq_len))
+    case, w = _case("dig_s2_256", 9 + dk, batch=2, seq_len=seq_len, dk=dk, dv=dv)
+    _check(case, w, "dk=%d dv=%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("stress", ["key_strong", "value_strong", "both_strong", "saturated",
+                                    "wide"])
+def test_beta_gate_stress(stress):
+    # strong decay: logits ~ -40 (alpha or beta ~ 0.08 per token); saturated: +12 (gate -> 1,
+    # sigmoid(-z) tiny in the gate gradient); wide: logits ~ N(0, 4^2)
+    kw = {"key_strong": dict(z_std=2.0, gate_bias=-40.0),
+          "value_strong": dict(w_std=2.0, w_mean=-40.0),
+          "both_strong": dict(z_std=4.0, gate_bias=-30.0, w_std=4.0, w_mean=-30.0),
+          "saturated": dict(z_std=2.0, gate_bias=12.0, w_std=2.0, w_mean=12.0),
+          "wide": dict(z_std=4.0, w_std=4.0)}[stress]
+    announce("beta stress %s" % stress)
+    case, w = _case("dig_xl2_2048", 41, batch=1, seq_len=320, **kw)
+    _check(case, w, stress)
+
+
+def test_beta_one_matches_key_gate_call():
+    # value logits +60: log2 sigmoid rounds to 0 in fp32, beta = 1 exactly; the outputs then
+    # match dig_gla_fwd's within the bar, and the value-gate gradient carries the factor
+    # sigmoid(-60) ~ 1e-26
+    import diffusion_backbone_amd as dig
+    from gpu_util import gla_forward
+    announce("beta = 1 against dig_gla_fwd")
+    case, _ = _case("dig_s2_256", 5, batch=2, seq_len=256)
+    w = np.full(case.v.shape, 60.0)
+    f = _check(case, w, "beta=1")
+    f0 = gla_forward(case, 64)
+    assert maxrel(to_f64(f["y"]), to_f64(f0["y"])) <= TOL["bf16"]
+    g = beta_backward(case, f)
+    assert float(np.max(np.abs(to_f64(g["dw"])))) < 1e-20
+
+
+def test_beta_full_xl2_2048():
+    announce("beta fwd+bwd dig_xl2_2048 full B=1 L=16384")
+    case, w = _case("dig_xl2_2048", 6)
+    _check(case, w, "xl2_2048")
+
+
+def test_beta_deterministic():
+    case, w = _case("dig_s2_256", 3, batch=2, seq_len=192)
+    f1 = _check(case, w, "first")
+    f2 = beta_forward(case, w)
+    assert np.array_equal(to_f64(f1["y"]), to_f64(f2["y"]))
+    g1, g2 = beta_backward(case, f1), beta_backward(case, f2)
+    for n in GRADS + ("dgamma",):
+        assert np.array_equal(to_f64(g1[n]), to_f64(g2[n])), n
+
+
+def test_beta_rejects_bad_arguments():
+    import torch
+    import diffusion_backbone_amd as dig
+    B, L, H, dk, dv = 1, 128, 2, 32, 64
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device="cuda")
+    q, k, z = bf(B, L, H, dk), bf(B, L, H, dk), bf(B, L, H, dk)
+    v, w, r, y = bf(B, L, H, dv), bf(B, L, H, dv), bf(B, L, H, dv), bf(B, L, H, dv)
+
+    def code(desc, **over):
+        a = dict(q=q, k=k, v=v, z=z, w=w, r=r, y=y)
+        a.update(over)
+        wsb = max(dig.dig_gla_beta_fwd_workspace_bytes(desc), 16)
+        ws = nbytes_buf(wsb)
+        try:
+            dig.dig_gla_fwd_beta(desc, a["q"], a["k"], a["v"], a["z"], a["w"], a["r"], None,
+                                 a["y"], None, None, ws, wsb)
+        except dig.DigError as e:
+            return e.status
+        return dig.DIG_OK
+
+    ok = dig.make_desc(B, L, H, dk, dv, 64, 16.0, 1.0, 1e-5, "bf16", 0)
+    assert code(ok) == dig.DIG_OK
+    torch.cuda.synchronize()
+    assert code(ok, w=None) == dig.DIG_ERR_NULL
+    assert code(ok, y=w) == dig.DIG_ERR_ALIAS
+    assert code(dig.make_desc(B, L, H, dk, dv, 32, 16.0, 1.0, 1e-5, "bf16", 0)) == \
+        dig.DIG_ERR_UNSUPPORTED                                           # chunk 64 only
+    assert code(dig.make_desc(B, L, H, dk, dv, 64, 16.0, 1.0, 1e-5, "f32", 0)) == \
+        dig.DIG_ERR_UNSUPPORTED                                           # bf16 only
+    big = dig.make_desc(B, L, H, 64, 128, 64, 16.0, 1.0, 1e-5, "bf16", 0)
+    assert dig.dig_gla_beta_saved_bytes(big) == 0
+    assert code(big, q=bf(B, L, H, 64), k=bf(B, L, H, 64), z=bf(B, L, H, 64),
+                v=bf(B, L, H, 128), w=bf(B, L, H, 128), r=bf(B, L, H, 128),
+                y=bf(B, L, H, 128)) == dig.DIG_ERR_UNSUPPORTED           # class 64/128

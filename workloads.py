@@ -200,6 +200,18 @@ def make_lowrank_gate(cfg: Config, seed: int, *, batch: int | None = None,
     return LowRankGate(factor, w, bias)
 
 
+def make_value_gate_logits(cfg: Config, seed: int, *, batch: int | None = None,
+                           seq_len: int | None = None, std: float = 1.0,
+                           mean: float = 0.0) -> np.ndarray:
+    """Value-side gate logits w [B, L, H, d_v] ~ N(mean, std^2), quantised to bf16 (a
+    projection x W_beta + b_beta of unit-variance tokens has unit-scale entries; a large std
+    or a very negative mean stresses the gate)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    B = cfg.batch if batch is None else batch
+    L = cfg.seq_len if seq_len is None else seq_len
+    return quantize(mean + std * rng.standard_normal((B, L, cfg.heads, cfg.d_v)), "bf16")
+
+
 @dataclass
 class SREMCase:
     cfg: Config
