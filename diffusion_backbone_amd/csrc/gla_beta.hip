@@ -103,37 +103,55 @@ __device__ __forceinline__ ChunkIx chunk_ix(const BetaArgs& p) {
   return c;
 }
 
-// Rows [0, valid) of a [B, L, H, n] bf16 tensor into an LDS tile of 64 rows x NP columns
-// (pitch P elements), zero elsewhere.  Row t starts at src + (row0 + t H) n.
-template <int NP, int P>
-__device__ __forceinline__ void stage_bf16(bf16* dst, const bf16* src, long row0, int H, int n,
-                                           int valid, int tid) {
-  for (int i = tid; i < kBC * NP; i += kBT) {
-    const int t = i / NP, c = i - t * NP;
-    bf16 x = from_f<bf16>(0.f);
-    if (t < valid && c < n) x = src[(row0 + (long)t * H) * n + c];
-    dst[t * P + c] = x;
+// Rows [0, valid) of a [B, L, H, n] bf16 tensor, for an LDS tile of 64 rows x NP columns
+// (pitch P elements), zero elsewhere; row t starts at src + (row0 + t H) n.  load() issues
+// every one of the thread's loads unconditionally (indices clamped into the tile's valid
+// part; valid >= 1, n >= 1) so that a kernel can issue all its tiles' loads before it waits
+// for any; store() selects the zeros and writes the tile.
+template <int NP>
+struct Rows {
+  static_assert((kBC * NP) % kBT == 0, "tile must split evenly over the threads");
+  static constexpr int N = kBC * NP / kBT;
+  bf16 x[N];
+  __device__ __forceinline__ void load(const bf16* src, long row0, int H, int n, int valid,
+                                       int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kBT, t = i / NP, c = i - t * NP;
+      x[j] = src[(row0 + (long)min(t, valid - 1) * H) * n + min(c, n - 1)];
+    }
   }
-}
-// The same into fp32.
-template <int NP, int P>
-__device__ __forceinline__ void stage_f32(float* dst, const bf16* src, long row0, int H, int n,
-                                          int valid, int tid) {
-  for (int i = tid; i < kBC * NP; i += kBT) {
-    const int t = i / NP, c = i - t * NP;
-    float x = 0.f;
-    if (t < valid && c < n) x = bf(src[(row0 + (long)t * H) * n + c]);
-    dst[t * P + c] = x;
+  template <int P, typename T>
+  __device__ __forceinline__ void store(T* dst, int n, int valid, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kBT, t = i / NP, c = i - t * NP;
+      dst[t * P + c] = from_f<T>((t < valid && c < n) ? bf(x[j]) : 0.f);
+    }
   }
-}
-// A [dk][dv] fp32 state into [DKP][P] LDS, zero padded.
-template <int DKP, int DVP, int P>
-__device__ __forceinline__ void stage_state(float* dst, const float* src, int dk, int dv, int tid) {
-  for (int i = tid; i < DKP * DVP; i += kBT) {
-    const int c = i / DVP, e = i - c * DVP;
-    dst[c * P + e] = (c < dk && e < dv) ? src[(long)c * dv + e] : 0.f;
+};
+// A [dk][dv] fp32 state for [DKP][P] LDS, zero padded, loaded and stored the same way.
+template <int DKP, int DVP>
+struct StateRegs {
+  static_assert((DKP * DVP) % kBT == 0, "state must split evenly over the threads");
+  static constexpr int N = DKP * DVP / kBT;
+  float x[N];
+  __device__ __forceinline__ void load(const float* src, int dk, int dv, int tid) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kBT, c = i / DVP, e = i - c * DVP;
+      x[j] = src[(long)min(c, dk - 1) * dv + min(e, dv - 1)];
+    }
   }
-}
+  template <int P>
+  __device__ __forceinline__ void store(float* dst, int dk, int dv, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kBT, c = i / DVP, e = i - c * DVP;
+      dst[c * P + e] = (c < dk && e < dv) ? x[j] : 0.f;
+    }
+  }
+};
 
 // In place: the raw logits of columns < n become the inclusive running sums over the chunk's
 // rows of log2 sigmoid(.) / tau (rows >= valid add 0).  Lanes = rows; waves take columns.
@@ -233,20 +251,31 @@ __device__ __forceinline__ void out_stage_bwd(const BetaArgs& p, const ChunkIx& 
     for (int E = 0; E < NDV; ++E) {
       const int e = 16 * E + r;
       const bool in = t < ci.valid && e < p.dv;
-      const long gi = (ci.row0 + (long)t * p.H) * p.dv + e;
-      o[E][i] = in ? obase[(long)t * p.dv + e] : 0.f;
-      rr[E][i] = in ? bf(p.r[gi]) : 0.f;
-      dyv[E][i] = in ? bf(p.dy[gi]) : 0.f;
+      const int tc = min(t, ci.valid - 1), ec = min(e, p.dv - 1);
+      const long gi = (ci.row0 + (long)tc * p.H) * p.dv + ec;
+      const float ov = obase[(long)tc * p.dv + ec], rv = bf(p.r[gi]), dv = bf(p.dy[gi]);
+      o[E][i] = in ? ov : 0.f;
+      rr[E][i] = in ? rv : 0.f;
+      dyv[E][i] = in ? dv : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
       ss[i] += o[E][i] * o[E][i];
     }
   }
+  float nwv[NDV];
+#pragma unroll
+  for (int E = 0; E < NDV; ++E) nwv[E] = p.norm_w ? p.norm_w[min(16 * E + r, p.dv - 1)] : 1.f;
   float rstd[4], m[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) rstd[i] = rsqrtf(row_sum16(ss[i]) * inv_dv + p.eps);
 #pragma unroll
   for (int E = 0; E < NDV; ++E) {
     const int e = 16 * E + r;
-    const float nw = (p.norm_w && e < p.dv) ? p.norm_w[e] : 1.f;
+    const float nw = (p.norm_w && e < p.dv) ? nwv[E] : 1.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sg[E][i] = fast_sigmoid(rr[E][i]);
@@ -260,7 +289,7 @@ __device__ __forceinline__ void out_stage_bwd(const BetaArgs& p, const ChunkIx& 
 #pragma unroll
   for (int E = 0; E < NDV; ++E) {
     const int e = 16 * E + r;
-    const float nw = (p.norm_w && e < p.dv) ? p.norm_w[e] : 1.f;
+    const float nw = (p.norm_w && e < p.dv) ? nwv[E] : 1.f;
     float gsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -294,10 +323,18 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   float* sC = reinterpret_cast<float*>(smem + Lo::U_C);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ChunkIx ci = chunk_ix(p);
-  stage_f32<DKP, PC>(sX, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DVP, PC>(sY, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
-  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  {
+    Rows<DKP> xk, xz;
+    Rows<DVP> xv, xw;
+    xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+    xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+    xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+    xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+    xk.template store<PC>(sX, p.dk, ci.valid, tid);
+    xv.template store<PC>(sY, p.dv, ci.valid, tid);
+    xz.template store<PB>(sB, p.dk, ci.valid, tid);
+    xw.template store<PC>(sC, p.dv, ci.valid, tid);
+  }
   __syncthreads();
   gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
   gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
@@ -380,12 +417,36 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   const int r = lane & 15, g = lane >> 4;
   const ChunkIx ci = chunk_ix(p);
   const long slot = ci.bh * p.NC + ci.j;
-  stage_bf16<DKP, PQ>(sQ, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_bf16<DKP, PQ>(sK, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_bf16<DVP, PV>(sV, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
-  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
-  stage_state<DKP, DVP, PC>(sS, p.states + slot * p.dk * p.dv, p.dk, p.dv, tid);
+  bf16 rpre[NDV][4];
+  float nwv[NDV];
+  {
+    Rows<DKP> xq, xk, xz;
+    Rows<DVP> xv, xw;
+    StateRegs<DKP, DVP> xs;
+    xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+    xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+    xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+    xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+    xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+    xs.load(p.states + slot * p.dk * p.dv, p.dk, p.dv, tid);
+    // r and the norm weight for the output stage (this lane's rows and columns)
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      const int ec = min(16 * E + r, p.dv - 1);
+      nwv[E] = p.norm_w ? p.norm_w[ec] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tc = min(16 * wave + 4 * g + i, ci.valid - 1);
+        rpre[E][i] = p.r[(ci.row0 + (long)tc * p.H) * p.dv + ec];
+      }
+    }
+    xq.template store<PQ>(sQ, p.dk, ci.valid, tid);
+    xk.template store<PQ>(sK, p.dk, ci.valid, tid);
+    xv.template store<PV>(sV, p.dv, ci.valid, tid);
+    xz.template store<PB>(sB, p.dk, ci.valid, tid);
+    xw.template store<PC>(sC, p.dv, ci.valid, tid);
+    xs.template store<PC>(sS, p.dk, p.dv, tid);
+  }
   __syncthreads();
   gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
   gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
@@ -486,7 +547,7 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   for (int E = 0; E < NDV; ++E) {
     const int e = 16 * E + r;
     if (e >= p.dv) continue;
-    const float nw = p.norm_w ? p.norm_w[e] : 1.f;
+    const float nw = nwv[E];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 4 * g + i;
@@ -495,7 +556,7 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
       const float o = acc[E][i];
       if (obase) obase[(long)t * p.dv + e] = o;
       if (p.o_pre) p.o_pre[gi] = from_f<bf16>(o);
-      const float rv = bf(p.r[gi]);
+      const float rv = bf(rpre[E][i]);
       p.y[gi] = from_f<bf16>(o * rstd[i] * nw * rv * fast_sigmoid(rv));
     }
   }
@@ -516,9 +577,16 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const ChunkIx ci = chunk_ix(p);
-  stage_f32<DKP, PC>(sX, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+  {
+    Rows<DKP> xq, xz;
+    Rows<DVP> xw;
+    xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+    xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+    xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+    xq.template store<PC>(sX, p.dk, ci.valid, tid);
+    xz.template store<PB>(sB, p.dk, ci.valid, tid);
+    xw.template store<PC>(sC, p.dv, ci.valid, tid);
+  }
   {
     float dO[NDV][4], od[NDV][4], gp[NDV];
     out_stage_bwd<NDV, false>(p, ci, wave, lane, dO, od, gp);
@@ -574,12 +642,32 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   const long slot = ci.bh * p.NC + ci.j;
   const long sz = (long)p.dk * p.dv;
   const int w = wave, t0 = 16 * w, ref = t0 - 1, end = t0 + 15;
-  stage_bf16<DKP, PQ>(sQ, p.q, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_bf16<DKP, PQ>(sK, p.k, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_bf16<DVP, PV>(sV, p.v, ci.row0, p.H, p.dv, ci.valid, tid);
-  stage_f32<DKP, PB>(sB, p.z, ci.row0, p.H, p.dk, ci.valid, tid);
-  stage_f32<DVP, PC>(sC, p.w, ci.row0, p.H, p.dv, ci.valid, tid);
-  stage_state<DKP, DVP, PC>(sS, p.states + slot * sz, p.dk, p.dv, tid);
+  const bool has_end = ci.j + 1 < p.NC;
+  {
+    Rows<DKP> xq, xk, xz;
+    Rows<DVP> xv, xw;
+    StateRegs<DKP, DVP> xs;
+    xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
+    xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
+    xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
+    xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
+    xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
+    xs.load(p.states + slot * sz, p.dk, p.dv, tid);
+    // the state leaving the chunk (the next chunk's entering state) and the gradient reaching
+    // the chunk's end, for the boundary sums; the last chunk has none (zero products)
+    StateRegs<DKP, DVP> xe, xg;
+    xe.load(p.states + (has_end ? slot + 1 : slot) * sz, p.dk, p.dv, tid);
+    xg.load(p.gst + slot * sz, p.dk, p.dv, tid);
+#pragma unroll
+    for (int j = 0; j < StateRegs<DKP, DVP>::N; ++j) xe.x[j] = has_end ? xe.x[j] * xg.x[j] : 0.f;
+    xe.template store<PC>(sS + 3 * SZS, p.dk, p.dv, tid);
+    xq.template store<PQ>(sQ, p.dk, ci.valid, tid);
+    xk.template store<PQ>(sK, p.dk, ci.valid, tid);
+    xv.template store<PV>(sV, p.dv, ci.valid, tid);
+    xz.template store<PB>(sB, p.dk, ci.valid, tid);
+    xw.template store<PC>(sC, p.dv, ci.valid, tid);
+    xs.template store<PC>(sS, p.dk, p.dv, tid);
+  }
   float od[NDV][4];
   {
     float dO[NDV][4], gp[NDV];
@@ -595,24 +683,21 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
       if (g == 0) sGp[w * DVP + 16 * E + r] = x;
     }
   }
-  // boundary sums with the state leaving the chunk (the next chunk's entering state)
-  const bool has_end = ci.j + 1 < p.NC;
+  // boundary sums of S_end (.) G_end (staged in slot 3, zero padded) over value columns (per
+  // key column) and over key columns (per value column)
+  __syncthreads();
   if (tid < DKP) {
+    const float* row = sS + 3 * SZS + tid * PC;
     float x = 0.f;
-    if (has_end && tid < p.dk) {
-      const float* se = p.states + (slot + 1) * sz + (long)tid * p.dv;
-      const float* ge = p.gst + slot * sz + (long)tid * p.dv;
-      for (int e = 0; e < p.dv; ++e) x += se[e] * ge[e];
-    }
+#pragma unroll 8
+    for (int e = 0; e < DVP; ++e) x += row[e];
     sBa[tid] = x;
   } else if (tid < DKP + DVP) {
     const int e = tid - DKP;
+    const float* col = sS + 3 * SZS + e;
     float x = 0.f;
-    if (has_end && e < p.dv) {
-      const float* se = p.states + (slot + 1) * sz + e;
-      const float* ge = p.gst + slot * sz + e;
-      for (int c = 0; c < p.dk; ++c) x += se[(long)c * p.dv] * ge[(long)c * p.dv];
-    }
+#pragma unroll 8
+    for (int c = 0; c < DKP; ++c) x += col[c * PC];
     sBb[e] = x;
   }
   __syncthreads();
@@ -668,7 +753,11 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   // ---- gradient tile states: G_3 = gradient reaching the chunk's end; tile contributions
   // dU_1..dU_3 (relative to each tile's start) into slots 0..2; then
   // G_{u-1} = 2^{B_u + C_u} G_u + dU_u
-  stage_state<DKP, DVP, PC>(sS + 3 * SZS, p.gst + slot * sz, p.dk, p.dv, tid);
+  {
+    StateRegs<DKP, DVP> xg;
+    xg.load(p.gst + slot * sz, p.dk, p.dv, tid);
+    xg.template store<PC>(sS + 3 * SZS, p.dk, p.dv, tid);
+  }
   if (w >= 1) {
     const int s0 = t0, rf = t0 - 1;
     const int r_ = lane & 15, g_ = lane >> 4;
@@ -851,19 +940,26 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   __syncthreads();
   {
     const int t = kBC - 1 - lane;  // lanes walk the rows backwards: a prefix is a suffix
-    for (int c = wave; c < p.dk; c += 4) {
+    const long rowt = ci.row0 + (long)min(t, ci.valid - 1) * p.H;
+    constexpr int NZ = DKP / 4, NW = DVP / 4;
+    bf16 zr[NZ], wr[NW];  // the raw logits, loaded together (clamped columns)
+#pragma unroll
+    for (int k = 0; k < NZ; ++k) zr[k] = p.z[rowt * p.dk + min(wave + 4 * k, p.dk - 1)];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) wr[k] = p.w[rowt * p.dv + min(wave + 4 * k, p.dv - 1)];
+#pragma unroll
+    for (int k = 0; k < NZ; ++k) {
+      const int c = wave + 4 * k;
       const float x = scan_dpp<64>(sB[t * PB + c]) + sBa[c];
-      if (t < ci.valid) {
-        const long gi = (ci.row0 + (long)t * p.H) * p.dk + c;
-        p.dz[gi] = from_f<bf16>(x * fast_sigmoid(-bf(p.z[gi])) * p.inv_tau);
-      }
+      if (t < ci.valid && c < p.dk)
+        p.dz[rowt * p.dk + c] = from_f<bf16>(x * fast_sigmoid(-bf(zr[k])) * p.inv_tau);
     }
-    for (int e = wave; e < p.dv; e += 4) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int e = wave + 4 * k;
       const float x = scan_dpp<64>(sC[t * PC + e]) + sBb[e];
-      if (t < ci.valid) {
-        const long gi = (ci.row0 + (long)t * p.H) * p.dv + e;
-        p.dw[gi] = from_f<bf16>(x * fast_sigmoid(-bf(p.w[gi])) * p.inv_tau);
-      }
+      if (t < ci.valid && e < p.dv)
+        p.dw[rowt * p.dv + e] = from_f<bf16>(x * fast_sigmoid(-bf(wr[k])) * p.inv_tau);
     }
   }
   // ---- dq, dk, dv
