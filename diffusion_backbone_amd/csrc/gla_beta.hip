@@ -24,6 +24,8 @@
 //   dlog alpha_t = sum_{u >= t in chunk} (q_u dq_u - k_u dk_u) + sum_e (S_end (.) G_end)[:, e]
 //   dlog beta_t  = sum_{u >= t in chunk} (do_u o_u - v_u dv_u) + sum_c (S_end (.) G_end)[c, :]
 // (shifting every later running sum by eps scales S_end by 2^eps).
+#include <type_traits>
+
 #include "dig_device.h"
 #include "dig_internal.h"
 
@@ -107,48 +109,96 @@ __device__ __forceinline__ ChunkIx chunk_ix(const BetaArgs& p) {
 // (pitch P elements), zero elsewhere; row t starts at src + (row0 + t H) n.  load() issues
 // every one of the thread's loads unconditionally (indices clamped into the tile's valid
 // part; valid >= 1, n >= 1) so that a kernel can issue all its tiles' loads before it waits
-// for any; store() selects the zeros and writes the tile.
-template <int NP>
+// for any; store() selects the zeros and writes the tile.  VEC: pieces of four elements
+// (8-byte loads; needs n % 4 == 0 and 8-byte aligned rows), else single elements.
+template <int NP, bool VEC>
 struct Rows {
-  static_assert((kBC * NP) % kBT == 0, "tile must split evenly over the threads");
-  static constexpr int N = kBC * NP / kBT;
-  bf16 x[N];
+  static constexpr int W = VEC ? 4 : 1;  // elements per piece
+  static constexpr int NPP = NP / W;     // pieces per row
+  static_assert((kBC * NPP) % kBT == 0, "tile must split evenly over the threads");
+  static constexpr int N = kBC * NPP / kBT;
+  using Piece = typename std::conditional<VEC, uint2, bf16>::type;
+  Piece x[N];
   __device__ __forceinline__ void load(const bf16* src, long row0, int H, int n, int valid,
                                        int tid) {
+    const int last = n / W - 1;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kBT, t = i / NP, c = i - t * NP;
-      x[j] = src[(row0 + (long)min(t, valid - 1) * H) * n + min(c, n - 1)];
+      const int i = tid + j * kBT, t = i / NPP, c = i - t * NPP;
+      const bf16* q = src + (row0 + (long)min(t, valid - 1) * H) * n + W * min(c, last);
+      x[j] = *reinterpret_cast<const Piece*>(q);
     }
   }
   template <int P, typename T>
   __device__ __forceinline__ void store(T* dst, int n, int valid, int tid) const {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kBT, t = i / NP, c = i - t * NP;
-      dst[t * P + c] = from_f<T>((t < valid && c < n) ? bf(x[j]) : 0.f);
+      const int i = tid + j * kBT, t = i / NPP, c = i - t * NPP;
+      const bool in = t < valid && W * c < n;
+      if constexpr (VEC) {
+        const bf16* e = reinterpret_cast<const bf16*>(&x[j]);
+        if constexpr (sizeof(T) == 2) {
+          uint2 z = in ? x[j] : make_uint2(0u, 0u);
+          *reinterpret_cast<uint2*>(dst + t * P + W * c) = z;
+        } else {
+          float4 f;
+          f.x = in ? bf(e[0]) : 0.f;
+          f.y = in ? bf(e[1]) : 0.f;
+          f.z = in ? bf(e[2]) : 0.f;
+          f.w = in ? bf(e[3]) : 0.f;
+          *reinterpret_cast<float4*>(dst + t * P + W * c) = f;
+        }
+      } else {
+        dst[t * P + c] = from_f<T>(in ? bf(x[j]) : 0.f);
+      }
     }
   }
 };
-// A [dk][dv] fp32 state for [DKP][P] LDS, zero padded, loaded and stored the same way.
-template <int DKP, int DVP>
+// A [dk][dv] fp32 state for [DKP][P] LDS, zero padded, loaded and stored the same way (VEC:
+// 16-byte pieces along a row, dv % 4 == 0; the last thread's surplus pieces repeat the last
+// one, which writes the same values twice).
+template <int DKP, int DVP, bool VEC>
 struct StateRegs {
-  static_assert((DKP * DVP) % kBT == 0, "state must split evenly over the threads");
-  static constexpr int N = DKP * DVP / kBT;
-  float x[N];
+  static constexpr int W = VEC ? 4 : 1;
+  static constexpr int NPP = DVP / W, TOT = DKP * NPP;
+  static constexpr int N = (TOT + kBT - 1) / kBT;
+  using Piece = typename std::conditional<VEC, float4, float>::type;
+  Piece x[N];
   __device__ __forceinline__ void load(const float* src, int dk, int dv, int tid) {
+    const int last = dv / W - 1;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kBT, c = i / DVP, e = i - c * DVP;
-      x[j] = src[(long)min(c, dk - 1) * dv + min(e, dv - 1)];
+      const int i = min(tid + j * kBT, TOT - 1), c = i / NPP, e = i - c * NPP;
+      x[j] = *reinterpret_cast<const Piece*>(src + (long)min(c, dk - 1) * dv + W * min(e, last));
     }
   }
   template <int P>
   __device__ __forceinline__ void store(float* dst, int dk, int dv, int tid) const {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int i = tid + j * kBT, c = i / DVP, e = i - c * DVP;
-      dst[c * P + e] = (c < dk && e < dv) ? x[j] : 0.f;
+      const int i = min(tid + j * kBT, TOT - 1), c = i / NPP, e = i - c * NPP;
+      const bool in = c < dk && W * e < dv;
+      if constexpr (VEC) {
+        float4 f = x[j];
+        if (!in) f = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(dst + c * P + W * e) = f;
+      } else {
+        dst[c * P + e] = in ? x[j] : 0.f;
+      }
+    }
+  }
+  // elementwise product with another state of the same layout (the boundary sums)
+  __device__ __forceinline__ void mul(const StateRegs& o, bool on) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if constexpr (VEC) {
+        x[j].x = on ? x[j].x * o.x[j].x : 0.f;
+        x[j].y = on ? x[j].y * o.x[j].y : 0.f;
+        x[j].z = on ? x[j].z * o.x[j].z : 0.f;
+        x[j].w = on ? x[j].w * o.x[j].w : 0.f;
+      } else {
+        x[j] = on ? x[j] * o.x[j] : 0.f;
+      }
     }
   }
 };
@@ -168,6 +218,20 @@ __device__ __forceinline__ void gate_cumsum(float* s, int n, int valid, float in
 // Running-sum value at row `ref` (0 for ref < 0: the chunk start).
 __device__ __forceinline__ float at_ref(const float* s, int P, int ref, int c) {
   return ref >= 0 ? s[ref * P + c] : 0.f;
+}
+
+// In place over a chunk's 64 rows x NP columns: X[s][c] <- xscale X[s][c] 2^{G[end][c] - G[s][c]}
+// (end >= 0: factors relative to row end), or xscale X[s][c] 2^{G[s][c]} (end < 0: relative to
+// the chunk start).  Every exponent is <= 0.
+template <int NP, int PX, int PG>
+__device__ __forceinline__ void prescale(float* X, const float* G, int end, float xscale, int tid) {
+  static_assert((kBC * NP) % kBT == 0, "tile must split evenly over the threads");
+#pragma unroll
+  for (int j = 0; j < kBC * NP / kBT; ++j) {
+    const int i = tid + j * kBT, s = i / NP, c = i - s * NP;
+    const float d = end >= 0 ? G[end * PG + c] - G[s * PG + c] : G[s * PG + c];
+    X[s * PX + c] *= xscale * fexp2(d);
+  }
 }
 
 // acc[ct][et] (lane: rows c = 16 ct + 4 g + i, column e = 16 et + r) =
@@ -203,22 +267,29 @@ __device__ __forceinline__ void outer_sum(f32x4 (&acc)[NDK][NDV], const TX* X, c
   }
 }
 
-// The same with the sums taken from the chunk start (2^{G[s]} factors, no end row).
-template <int NDK, int NDV, typename TX, int PX, int PGX, typename TY, int PY, int PGY>
-__device__ __forceinline__ f32x4 outer_from_start(const TX* X, const float* GX, const TY* Y,
-                                                  const float* GY, int ct, int et, float xscale,
-                                                  int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  f32x4 acc = zero4();
-  const int c = 16 * ct + r, e = 16 * et + r;
-#pragma unroll 4
-  for (int ks = 0; ks < kBC / 4; ++ks) {
-    const int s = 4 * ks + g;
-    const float a = xscale * to_f(X[s * PX + c]) * fexp2(GX[s * PGX + c]);
-    const float b = to_f(Y[s * PY + e]) * fexp2(GY[s * PGY + e]);
-    acc = mfma_f32(a, b, acc);
+// Whether the products inside this wave's 16-token tile may be factored about the row before
+// it: the largest log2 decay of either gate from that row to the tile's last row, over every
+// column, is at most kFactorMax (so every factor 2^{B_ref - B_s}, 2^{C_ref - C_s} stays below
+// 2^64 and its partner above 2^-64).  Wave-uniform.
+constexpr float kFactorMax = 64.f;
+template <int DKP, int DVP, int PB, int PC>
+__device__ __forceinline__ bool tile_factorable(const float* sB, const float* sC, int t0,
+                                                int lane) {
+  const int ref = t0 - 1, end = t0 + 15;
+  float d = 0.f;
+#pragma unroll
+  for (int j = 0; j < (DKP + 63) / 64; ++j) {
+    const int c = min(lane + 64 * j, DKP - 1);
+    d = fmaxf(d, at_ref(sB, PB, ref, c) - sB[end * PB + c]);
   }
-  return acc;
+#pragma unroll
+  for (int j = 0; j < (DVP + 63) / 64; ++j) {
+    const int e = min(lane + 64 * j, DVP - 1);
+    d = fmaxf(d, at_ref(sC, PC, ref, e) - sC[end * PC + e]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) d = fmaxf(d, __shfl_xor(d, off));
+  return __builtin_amdgcn_readfirstlane((int)(d <= kFactorMax)) != 0;
 }
 
 template <int P, int NDK, int NDV>
@@ -312,7 +383,7 @@ __device__ __forceinline__ void out_stage_bwd(const BetaArgs& p, const ChunkIx& 
 
 // ------------------------------------------------------------------------- pass 1 (forward)
 // Each chunk's state contribution U (relative to its last row) and its log2 decays.
-template <int NDK, int NDV>
+template <int NDK, int NDV, bool VEC>
 __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
@@ -324,8 +395,8 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ChunkIx ci = chunk_ix(p);
   {
-    Rows<DKP> xk, xz;
-    Rows<DVP> xv, xw;
+    Rows<DKP, VEC> xk, xz;
+    Rows<DVP, VEC> xv, xw;
     xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
     xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
     xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
@@ -341,16 +412,18 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   __syncthreads();
   const long slot = ci.bh * p.NC + ci.j;
   const int r = lane & 15, g = lane >> 4;
+  // k_s 2^{B_end - B_s} and v_s 2^{C_end - C_s} in place, once per element
+  prescale<DKP, PC, PB>(sX, sB, kBC - 1, 1.f, tid);
+  prescale<DVP, PC, PC>(sY, sC, kBC - 1, 1.f, tid);
+  __syncthreads();
   for (int u = wave; u < NDK * NDV; u += 4) {
     const int ct = u / NDV, et = u - ct * NDV;
     const int c = 16 * ct + r, e = 16 * et + r;
     f32x4 acc = zero4();
-#pragma unroll 4
+#pragma unroll 8
     for (int ks = 0; ks < kBC / 4; ++ks) {
       const int s = 4 * ks + g;
-      const float a = sX[s * PC + c] * fexp2(sB[(kBC - 1) * PB + c] - sB[s * PB + c]);
-      const float b = sY[s * PC + e] * fexp2(sC[(kBC - 1) * PC + e] - sC[s * PC + e]);
-      acc = mfma_f32(a, b, acc);
+      acc = mfma_f32(sX[s * PC + c], sY[s * PC + e], acc);
     }
     float* dst = p.states + slot * p.dk * p.dv;
 #pragma unroll
@@ -400,7 +473,7 @@ __global__ __launch_bounds__(256) void beta_scan(float* st, const float* dec, in
 }
 
 // --------------------------------------------------------------------- pass 3 (forward)
-template <int NDK, int NDV>
+template <int NDK, int NDV, bool VEC>
 __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PQ = Lo::PQ, PV = Lo::PV, PB = Lo::PB,
@@ -420,9 +493,9 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   bf16 rpre[NDV][4];
   float nwv[NDV];
   {
-    Rows<DKP> xq, xk, xz;
-    Rows<DVP> xv, xw;
-    StateRegs<DKP, DVP> xs;
+    Rows<DKP, VEC> xq, xk, xz;
+    Rows<DVP, VEC> xv, xw;
+    StateRegs<DKP, DVP, VEC> xs;
     xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
     xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
     xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
@@ -473,15 +546,16 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   }
   __syncthreads();
   const int w = wave, t0 = 16 * w, ref = t0 - 1;
-  // across tiles: (q_t 2^{B_t - B_ref}) S_w, then 2^{C_t - C_ref}
+  const bool fast = tile_factorable<DKP, DVP, PB, PC>(sB, sC, t0, lane);
+  // across tiles: (q_t 2^{B_t - B_ref}) S_w
   f32x4 acc[NDV];
-  {
-    float a[DKP / 4];
+  float a[DKP / 4];  // A operand: q_scale q_t 2^{B_t - B_ref}, t = t0 + r, c = 4 ks + g
 #pragma unroll
-    for (int ks = 0; ks < DKP / 4; ++ks) {
-      const int c = 4 * ks + g, t = t0 + r;
-      a[ks] = p.q_scale * bf(sQ[t * PQ + c]) * fexp2(sB[t * PB + c] - at_ref(sB, PB, ref, c));
-    }
+  for (int ks = 0; ks < DKP / 4; ++ks) {
+    const int c = 4 * ks + g, t = t0 + r;
+    a[ks] = p.q_scale * bf(sQ[t * PQ + c]) * fexp2(sB[t * PB + c] - at_ref(sB, PB, ref, c));
+  }
+  {
     const float* S = sS + w * SZS;
 #pragma unroll
     for (int E = 0; E < NDV; ++E) {
@@ -489,16 +563,44 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
 #pragma unroll
       for (int ks = 0; ks < DKP / 4; ++ks)
         acc[E] = mfma_f32(a[ks], S[(4 * ks + g) * PC + 16 * E + r], acc[E]);
+    }
+  }
+  if (fast) {
+    // inside the tile, factored about the row before it (every factor within 2^64):
+    // A^T = Khat Qhat^T with Khat_s = k_s 2^{B_ref - B_s}; this lane holds A[t0 + r][t0 + 4 g + i]
+    f32x4 at = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DKP / 4; ++ks) {
+      const int c = 4 * ks + g, s = t0 + r;
+      const float kh = bf(sK[s * PQ + c]) * fexp2(at_ref(sB, PB, ref, c) - sB[s * PB + c]);
+      at = mfma_f32(kh, a[ks], at);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) at[i] = (4 * g + i <= r) ? at[i] : 0.f;
+    // o_t += sum_s A[t][s] Vhat_s, Vhat_s = v_s 2^{C_ref - C_s} (k step i: s = t0 + 4 g + i)
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
+      const float cr = at_ref(sC, PC, ref, e);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * g + i, e = 16 * E + r;
-        acc[E][i] *= fexp2(sC[t * PC + e] - at_ref(sC, PC, ref, e));
+        const int s = t0 + 4 * g + i;
+        acc[E] = mfma_f32(at[i], bf(sV[s * PV + e]) * fexp2(cr - sC[s * PC + e]), acc[E]);
       }
     }
   }
-  // inside the tile: pair weights A[t][s] = q_scale sum_c q_t k_s 2^{B_t - B_s}, s <= t
+  // then 2^{C_t - C_ref}
+#pragma unroll
+  for (int E = 0; E < NDV; ++E)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i, e = 16 * E + r;
+      acc[E][i] *= fexp2(sC[t * PC + e] - at_ref(sC, PC, ref, e));
+    }
+  // inside a tile with stronger decay: pair weights A[t][s] = q_scale sum_c q_t k_s 2^{B_t - B_s},
+  // s <= t, each with its own factor
   float* myA = sA + w * 16 * PA;
-  {
+  if (!fast) {
     const int tl = r, sg = 4 * g;
     float pa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -515,21 +617,23 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
   }
   __syncthreads();
   // o_t += sum_{s <= t in tile} A[t][s] v_s 2^{C_t - C_s}
+  if (!fast) {
 #pragma unroll
-  for (int E = 0; E < NDV; ++E) {
-    const int e = 16 * E + r;
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tl = 4 * g + i, t = t0 + tl;
-      const float ct = sC[t * PC + e];
-      float sum = 0.f;
-      for (int sl = 0; sl <= 12 + i; ++sl) {
-        const int s = t0 + sl;
-        const float term = myA[tl * PA + sl] * bf(sV[s * PV + e]) *
-                           fexp2(fminf(ct - sC[s * PC + e], 0.f));
-        sum += sl <= tl ? term : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int tl = 4 * g + i, t = t0 + tl;
+        const float ct = sC[t * PC + e];
+        float sum = 0.f;
+        for (int sl = 0; sl <= 12 + i; ++sl) {
+          const int s = t0 + sl;
+          const float term = myA[tl * PA + sl] * bf(sV[s * PV + e]) *
+                             fexp2(fminf(ct - sC[s * PC + e], 0.f));
+          sum += sl <= tl ? term : 0.f;
+        }
+        acc[E][i] += sum;
       }
-      acc[E][i] += sum;
     }
   }
   // output stage
@@ -565,7 +669,7 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
 // ------------------------------------------------------------------------ pass 1 (backward)
 // Each chunk's gradient-state contribution dU = sum_t (q_scale q_t 2^{B_t})^T (dO_t 2^{C_t})
 // (relative to the chunk start) and its log2 decays.
-template <int NDK, int NDV>
+template <int NDK, int NDV, bool VEC>
 __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
@@ -578,8 +682,8 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
   const int r = lane & 15, g = lane >> 4;
   const ChunkIx ci = chunk_ix(p);
   {
-    Rows<DKP> xq, xz;
-    Rows<DVP> xw;
+    Rows<DKP, VEC> xq, xz;
+    Rows<DVP, VEC> xw;
     xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
     xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
     xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
@@ -600,10 +704,21 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
   gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
   __syncthreads();
   const long slot = ci.bh * p.NC + ci.j;
+  // q_scale q_t 2^{B_t} and dO_t 2^{C_t} in place, once per element
+  prescale<DKP, PC, PB>(sX, sB, -1, p.q_scale, tid);
+  prescale<DVP, PC, PC>(sY, sC, -1, 1.f, tid);
+  __syncthreads();
   for (int u = wave; u < NDK * NDV; u += 4) {
     const int ct = u / NDV, et = u - ct * NDV;
-    const f32x4 acc = outer_from_start<NDK, NDV, float, PC, PB, float, PC, PC>(
-        sX, sB, sY, sC, ct, et, p.q_scale, lane);
+    f32x4 acc = zero4();
+    {
+      const int c = 16 * ct + r, e = 16 * et + r;
+#pragma unroll 8
+      for (int ks = 0; ks < kBC / 4; ++ks) {
+        const int s = 4 * ks + g;
+        acc = mfma_f32(sX[s * PC + c], sY[s * PC + e], acc);
+      }
+    }
     float* dst = p.gst + slot * p.dk * p.dv;
     const int e = 16 * et + r;
 #pragma unroll
@@ -618,7 +733,7 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
 }
 
 // ------------------------------------------------------------------------ pass 3 (backward)
-template <int NDK, int NDV>
+template <int NDK, int NDV, bool VEC>
 __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PQ = Lo::PQ, PV = Lo::PV, PB = Lo::PB,
@@ -644,9 +759,9 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   const int w = wave, t0 = 16 * w, ref = t0 - 1, end = t0 + 15;
   const bool has_end = ci.j + 1 < p.NC;
   {
-    Rows<DKP> xq, xk, xz;
-    Rows<DVP> xv, xw;
-    StateRegs<DKP, DVP> xs;
+    Rows<DKP, VEC> xq, xk, xz;
+    Rows<DVP, VEC> xv, xw;
+    StateRegs<DKP, DVP, VEC> xs;
     xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
     xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
     xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
@@ -655,11 +770,10 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
     xs.load(p.states + slot * sz, p.dk, p.dv, tid);
     // the state leaving the chunk (the next chunk's entering state) and the gradient reaching
     // the chunk's end, for the boundary sums; the last chunk has none (zero products)
-    StateRegs<DKP, DVP> xe, xg;
+    StateRegs<DKP, DVP, VEC> xe, xg;
     xe.load(p.states + (has_end ? slot + 1 : slot) * sz, p.dk, p.dv, tid);
     xg.load(p.gst + slot * sz, p.dk, p.dv, tid);
-#pragma unroll
-    for (int j = 0; j < StateRegs<DKP, DVP>::N; ++j) xe.x[j] = has_end ? xe.x[j] * xg.x[j] : 0.f;
+    xe.mul(xg, has_end);
     xe.template store<PC>(sS + 3 * SZS, p.dk, p.dv, tid);
     xq.template store<PQ>(sQ, p.dk, ci.valid, tid);
     xk.template store<PQ>(sK, p.dk, ci.valid, tid);
@@ -754,7 +868,7 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
   // dU_1..dU_3 (relative to each tile's start) into slots 0..2; then
   // G_{u-1} = 2^{B_u + C_u} G_u + dU_u
   {
-    StateRegs<DKP, DVP> xg;
+    StateRegs<DKP, DVP, VEC> xg;
     xg.load(p.gst + slot * sz, p.dk, p.dv, tid);
     xg.template store<PC>(sS + 3 * SZS, p.dk, p.dv, tid);
   }
@@ -843,11 +957,85 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
       }
     }
   }
-  // ---- inside the tile: pair tables A[t][s] (q_scale included) and M[t][s] = sum_e dO_t v_s
-  // 2^{C_t - C_s}, s <= t
-  float* myA = sA + w * 16 * PA;
-  float* myM = sM + w * 16 * PA;
-  {
+  // ---- inside the tile.  Where both gates' decay across the tile stays within 2^64 the
+  // products are factored about the row before the tile (ref) and run on the matrix cores:
+  //   Qhat_t = q_scale q_t 2^{B_t - B_ref}, Khat_s = k_s 2^{B_ref - B_s},
+  //   dOhat_t = dO_t 2^{C_t - C_ref},       Vhat_s = v_s 2^{C_ref - C_s},
+  //   A = Qhat Khat^T, M = dOhat Vhat^T (causal), dq += q_scale 2^{B_t - B_ref} (M Khat),
+  //   dk += 2^{B_ref - B_s} (M^T Qhat), dv += 2^{C_ref - C_s} (A^T dOhat);
+  // otherwise every pair takes its own factors (pair tables below).
+  const bool fast = tile_factorable<DKP, DVP, PB, PC>(sB, sC, t0, lane);
+  if (fast) {
+    // A and M in this lane's accumulator order ([t0 + 4 g + i][t0 + r]) and M transposed
+    // ([t0 + r][t0 + 4 g + i]); operands of row t0 + r, column 4 ks + g
+    f32x4 an = zero4(), mn = zero4(), mt = zero4();
+    {
+      const int t = t0 + r;
+#pragma unroll 2
+      for (int ks = 0; ks < DKP / 4; ++ks) {
+        const int c = 4 * ks + g;
+        const float br = at_ref(sB, PB, ref, c), bt = sB[t * PB + c];
+        const float qh = p.q_scale * bf(sQ[t * PQ + c]) * fexp2(bt - br);
+        const float kh = bf(sK[t * PQ + c]) * fexp2(br - bt);
+        an = mfma_f32(qh, kh, an);
+      }
+#pragma unroll 2
+      for (int ks = 0; ks < DVP / 4; ++ks) {
+        const int e = 4 * ks + g;
+        const float cr = at_ref(sC, PC, ref, e), cv = sC[t * PC + e];
+        const float dh = sD[t * PC + e] * fexp2(cv - cr);
+        const float vh = bf(sV[t * PV + e]) * fexp2(cr - cv);
+        mn = mfma_f32(dh, vh, mn);
+        mt = mfma_f32(vh, dh, mt);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool nat = r <= 4 * g + i;  // s = t0 + r <= t = t0 + 4 g + i
+      an[i] = nat ? an[i] : 0.f;
+      mn[i] = nat ? mn[i] : 0.f;
+      mt[i] = (4 * g + i <= r) ? mt[i] : 0.f;
+    }
+    // k step i: the contracted row is t0 + 4 g + i
+#pragma unroll
+    for (int ct = 0; ct < NDK; ++ct) {
+      const int c = 16 * ct + r;
+      const float br = at_ref(sB, PB, ref, c);
+      f32x4 xq = zero4(), xk = zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = t0 + 4 * g + i;
+        const float bu = sB[u * PB + c];
+        xq = mfma_f32(mt[i], bf(sK[u * PQ + c]) * fexp2(br - bu), xq);              // M Khat
+        xk = mfma_f32(mn[i], p.q_scale * bf(sQ[u * PQ + c]) * fexp2(bu - br), xk);  // M^T Qhat
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bx = sB[(t0 + 4 * g + i) * PB + c];
+        dqa[ct][i] += p.q_scale * fexp2(bx - br) * xq[i];
+        dka[ct][i] += fexp2(br - bx) * xk[i];
+      }
+    }
+#pragma unroll
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
+      const float cr = at_ref(sC, PC, ref, e);
+      f32x4 xv = zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = t0 + 4 * g + i;
+        xv = mfma_f32(an[i], sD[u * PC + e] * fexp2(sC[u * PC + e] - cr), xv);      // A^T dOhat
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float cx = sC[(t0 + 4 * g + i) * PC + e];
+        dva[E][i] += fexp2(cr - cx) * xv[i];
+      }
+    }
+  } else {
+    // pair tables A[t][s] (q_scale included) and M[t][s] = sum_e dO_t v_s 2^{C_t - C_s}, s <= t
+    float* myA = sA + w * 16 * PA;
+    float* myM = sM + w * 16 * PA;
     const int tl = r, sg = 4 * g, t = t0 + tl;
     float pa[4] = {0.f, 0.f, 0.f, 0.f}, pm[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -874,47 +1062,49 @@ __global__ __launch_bounds__(kBT) void beta_bwd_out(BetaArgs p) {
       myA[tl * PA + sg + i] = on ? p.q_scale * pa[i] : 0.f;
       myM[tl * PA + sg + i] = on ? pm[i] : 0.f;
     }
-  }
-  __syncthreads();
-  // dq_t[c] += q_scale sum_{s <= t} M[t][s] k_s[c] 2^{B_t - B_s}
-  // dk_s[c] += q_scale sum_{t >= s} M[t][s] q_t[c] 2^{B_t - B_s}
+    // the tables are this wave's own: its LDS accesses complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // dq_t[c] += q_scale sum_{s <= t} M[t][s] k_s[c] 2^{B_t - B_s}
+    // dk_s[c] += q_scale sum_{t >= s} M[t][s] q_t[c] 2^{B_t - B_s}
 #pragma unroll
-  for (int ct = 0; ct < NDK; ++ct) {
-    const int c = 16 * ct + r;
+    for (int ct = 0; ct < NDK; ++ct) {
+      const int c = 16 * ct + r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int xl = 4 * g + i, x = t0 + xl;
-      const float bx = sB[x * PB + c];
-      float sq = 0.f, sk = 0.f;
-      for (int ul = 0; ul < 16; ++ul) {
-        const int u = t0 + ul;
-        // u as the key (u <= x) for dq, as the query (u >= x) for dk: one factor
-        // 2^{-|B_x - B_u|} serves both
-        const float f = fexp2(-fabsf(bx - sB[u * PB + c]));
-        const float tq = myM[xl * PA + ul] * bf(sK[u * PQ + c]) * f;
-        const float tk = myM[ul * PA + xl] * bf(sQ[u * PQ + c]) * f;
-        sq += ul <= xl ? tq : 0.f;
-        sk += ul >= xl ? tk : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int xl = 4 * g + i, x = t0 + xl;
+        const float bx = sB[x * PB + c];
+        float sq = 0.f, sk = 0.f;
+        for (int ul = 0; ul < 16; ++ul) {
+          const int u = t0 + ul;
+          // u as the key (u <= x) for dq, as the query (u >= x) for dk: one factor
+          // 2^{-|B_x - B_u|} serves both
+          const float f = fexp2(-fabsf(bx - sB[u * PB + c]));
+          const float tq = myM[xl * PA + ul] * bf(sK[u * PQ + c]) * f;
+          const float tk = myM[ul * PA + xl] * bf(sQ[u * PQ + c]) * f;
+          sq += ul <= xl ? tq : 0.f;
+          sk += ul >= xl ? tk : 0.f;
+        }
+        dqa[ct][i] += p.q_scale * sq;
+        dka[ct][i] += p.q_scale * sk;
       }
-      dqa[ct][i] += p.q_scale * sq;
-      dka[ct][i] += p.q_scale * sk;
     }
-  }
-  // dv_s[e] += sum_{t >= s} A[t][s] dO_t[e] 2^{C_t - C_s}
+    // dv_s[e] += sum_{t >= s} A[t][s] dO_t[e] 2^{C_t - C_s}
 #pragma unroll
-  for (int E = 0; E < NDV; ++E) {
-    const int e = 16 * E + r;
+    for (int E = 0; E < NDV; ++E) {
+      const int e = 16 * E + r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = 4 * g + i, s = t0 + sl;
-      const float cs = sC[s * PC + e];
-      float sum = 0.f;
-      for (int ul = i; ul < 16; ++ul) {
-        const int u = t0 + ul;
-        const float term = myA[ul * PA + sl] * sD[u * PC + e] * fexp2(fminf(sC[u * PC + e] - cs, 0.f));
-        sum += ul >= sl ? term : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * g + i, s = t0 + sl;
+        const float cs = sC[s * PC + e];
+        float sum = 0.f;
+        for (int ul = i; ul < 16; ++ul) {
+          const int u = t0 + ul;
+          const float term = myA[ul * PA + sl] * sD[u * PC + e] * fexp2(fminf(sC[u * PC + e] - cs, 0.f));
+          sum += ul >= sl ? term : 0.f;
+        }
+        dva[E][i] += sum;
       }
-      dva[E][i] += sum;
     }
   }
   // ---- gate gradients: per-row terms, suffix sums over the chunk, boundary sums
@@ -1000,21 +1190,31 @@ __global__ __launch_bounds__(256) void beta_dgamma_reduce(const float* part, lon
   if (threadIdx.x == 0) out[e] = red[0];
 }
 
-template <int NDK, int NDV>
-hipError_t launch_beta(const GlaShape& s, const BetaArgs& a, bool bwd, hipStream_t st) {
+template <int NDK, int NDV, bool VEC>
+hipError_t launch_beta_v(const GlaShape& s, const BetaArgs& a, bool bwd, hipStream_t st) {
   using Lo = BetaLay<NDK, NDV>;
   const unsigned grid = (unsigned)((long)s.B * s.H * s.NC);
   const dim3 sgrid((unsigned)((s.dk * s.dv + 255) / 256), (unsigned)(s.B * s.H));
   if (!bwd) {
-    hipLaunchKernelGGL((beta_fwd_state<NDK, NDV>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
+    hipLaunchKernelGGL((beta_fwd_state<NDK, NDV, VEC>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
     hipLaunchKernelGGL(beta_scan, sgrid, dim3(256), 0, st, a.states, a.dec, s.NC, s.dk, s.dv, 0);
-    hipLaunchKernelGGL((beta_fwd_out<NDK, NDV>), dim3(grid), dim3(kBT), Lo::F_END, st, a);
+    hipLaunchKernelGGL((beta_fwd_out<NDK, NDV, VEC>), dim3(grid), dim3(kBT), Lo::F_END, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((beta_bwd_state<NDK, NDV>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
+  hipLaunchKernelGGL((beta_bwd_state<NDK, NDV, VEC>), dim3(grid), dim3(kBT), Lo::U_END, st, a);
   hipLaunchKernelGGL(beta_scan, sgrid, dim3(256), 0, st, a.gst, a.dec, s.NC, s.dk, s.dv, 1);
-  hipLaunchKernelGGL((beta_bwd_out<NDK, NDV>), dim3(grid), dim3(kBT), Lo::G_END, st, a);
+  hipLaunchKernelGGL((beta_bwd_out<NDK, NDV, VEC>), dim3(grid), dim3(kBT), Lo::G_END, st, a);
   return hipGetLastError();
+}
+
+// Four-element staging where every staged row is whole 8-byte pieces.
+template <int NDK, int NDV>
+hipError_t launch_beta(const GlaShape& s, const BetaArgs& a, bool bwd, hipStream_t st) {
+  auto al8 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 7) == 0; };
+  const bool vec = s.dk % 4 == 0 && s.dv % 4 == 0 && al8(a.q) && al8(a.k) && al8(a.v) &&
+                   al8(a.z) && al8(a.w);
+  return vec ? launch_beta_v<NDK, NDV, true>(s, a, bwd, st)
+             : launch_beta_v<NDK, NDV, false>(s, a, bwd, st);
 }
 
 }  // namespace

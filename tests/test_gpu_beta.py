@@ -110,11 +110,16 @@ def test_beta_tile_classes(dk, dv, seq_len):
 
 
 @pytest.mark.parametrize("stress", ["key_strong", "value_strong", "both_strong", "saturated",
-                                    "wide"])
+                                    "wide", "key_extreme", "value_extreme"])
 def test_beta_gate_stress(stress):
-    # strong decay: logits ~ -40 (alpha or beta ~ 0.08 per token); saturated: +12 (gate -> 1,
-    # sigmoid(-z) tiny in the gate gradient); wide: logits ~ N(0, 4^2)
+    # strong decay: logits ~ -40 (alpha or beta ~ 0.08 per token: about 2^-58 across a
+    # 16-token tile, so some tiles take the factored products and some the per-pair factors);
+    # extreme: logits ~ -90 (about 2^-130 across a tile: every tile takes the per-pair
+    # factors); saturated: +12 (gate -> 1, sigmoid(-z) tiny in the gate gradient); wide:
+    # logits ~ N(0, 4^2)
     kw = {"key_strong": dict(z_std=2.0, gate_bias=-40.0),
+          "key_extreme": dict(z_std=2.0, gate_bias=-90.0),
+          "value_extreme": dict(w_std=2.0, w_mean=-90.0),
           "value_strong": dict(w_std=2.0, w_mean=-40.0),
           "both_strong": dict(z_std=4.0, gate_bias=-30.0, w_std=4.0, w_mean=-30.0),
           "saturated": dict(z_std=2.0, gate_bias=12.0, w_std=2.0, w_mean=12.0),
