@@ -8,16 +8,20 @@
 // B and C are their inclusive running sums over a chunk's rows.
 //
 // Work layout.  Chunks of 64 tokens, one workgroup of four waves per chunk; wave w owns the
-// 16-token tile w.  Every factor 2^x formed below has x <= 0, so no gate strength overflows
-// a factor or loses the small ones:
+// 16-token tile w:
 //   across chunks  each chunk's contribution U = sum_s (k_s 2^{B_end-B_s})^T (v_s 2^{C_end-C_s})
 //                  and decays (pass 1); a scan over chunks (pass 2) gives the state entering
 //                  every chunk, saved for the backward;
 //   across tiles   the state entering tile w, S_w = 2^{B_w+C_w} (.) S_{w-1} + U_{w-1} (U of a
 //                  tile formed like a chunk's), reaches tile w's rows as
 //                  (q_t 2^{B_t-B_ref}) S_w 2^{C_t-C_ref}, ref = the row before the tile;
-//   inside a tile  each of the 16 x 16 causal pairs takes its own factors 2^{B_t[c]-B_s[c]} and
-//                  2^{C_t[e]-C_s[e]} on the vector ALU.
+//   inside a tile  where both gates decay by at most 2^64 from ref to the tile's last row,
+//                  the pair products are factored about ref, (q_t 2^{B_t-B_ref}) .
+//                  (k_s 2^{B_ref-B_s}) and v_s 2^{C_ref-C_s}, 2^{C_t-C_ref}, on the matrix
+//                  cores; elsewhere each of the 16 x 16 causal pairs takes its own factors
+//                  2^{B_t[c]-B_s[c]} and 2^{C_t[e]-C_s[e]} on the vector ALU.
+// Across chunks and tiles every factor 2^x has x <= 0; inside a tile |x| <= 64, so no gate
+// strength overflows a factor or loses the small ones.
 // The matrix products (chunk and tile contributions, the products with tile states) run on
 // the fp32 matrix cores (16 x 16 x 4).  The backward mirrors this with gradient states G
 // carried from later tiles and chunks (a reverse scan) and the boundary identity

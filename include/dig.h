@@ -184,8 +184,10 @@ dig_status dig_gla_bwd_lowrank(const dig_gla_desc* desc, const void* q, const vo
  * output stage as dig_gla_fwd.  DiG itself runs beta = 1 (dig_gla_fwd); these calls are the
  * variant with a value gate.  desc->dtype must be DIG_BF16, desc->chunk 64, d_k <= 48 and
  * d_v <= 80 with d_k <= 16, d_v <= 32 or d_k <= 32, d_v <= 64 or d_k <= 48, d_v <= 80
- * (DIG_ERR_UNSUPPORTED otherwise); desc->seg_chunks is ignored.  Every gate strength is
- * exact: no factor 2^x with x > 0 is ever formed.
+ * (DIG_ERR_UNSUPPORTED otherwise); desc->seg_chunks is ignored.  Any gate strength is
+ * handled: inside a 16-token tile the products are factored about the row before the tile
+ * only where both gates decay by at most 2^64 across it (factors within 2^-64..2^64), and
+ * every pair takes its own factor <= 1 elsewhere.
  *
  * Bytes of the forward->backward buffer (opaque; regions 256-byte aligned): the fp32 state
  * entering every 64-token chunk, [B][H][ceil(L/64)][d_k][d_v], then the fp32 pre-norm
