@@ -244,14 +244,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 115310.9 KiB / 0.50007 + 91441.4 KiB / 1.0, segment scan 1666.7 + 2594.2,
-        # final pass 95167.9 + 92217.7 (FETCH_SIZE, WRITE_SIZE; copy: 131091.5 KiB read per
+        # pass A 115313.1 KiB / 0.500075 + 91422.0 KiB / 1.0, segment scan 1666.6 + 2594.2,
+        # final pass 95167.8 + 92273.5 (FETCH_SIZE, WRITE_SIZE; copy: 131091.7 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 625132891,
-        # pass A 79429.4 + 5099.5, state scan 2819.1 + 5184.0, output pass 68181.8 + 157010.7
-        "dig_gla_fwd": 479344505,
+        "dig_gla_bwd": 625173379,
+        # pass A 79429.4 + 5099.5, state scan 2819.1 + 5184.0, output pass 68157.4 + 157023.4
+        "dig_gla_fwd": 479307215,
     },
-    "sources_sha256": "db2c008d8aea51eb9d1550aae91c695718d911b4df040b8a47a4261a2166df26",
+    "sources_sha256": "bbef3c1f3dc9e17b71f2214907a9655e83f3ff5e8558cd007ef96222e452a558",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
