@@ -55,9 +55,9 @@ struct BetaLay {
   // forward output pass: q, k, v, B, C, four states, four pair tables
   static constexpr int F_Q = 0, F_K = F_Q + NQ, F_V = F_K + NQ, F_B = F_V + NV, F_C = F_B + NB,
                        F_S = F_C + NCB, F_A = F_S + 4 * SZS * 4, F_END = F_A + 4 * 16 * PA * 4;
-  // chunk-contribution passes: two operand tiles and the two gate sums
-  static constexpr int U_X = 0, U_Y = U_X + kBC * PC * 4, U_B = U_Y + kBC * PC * 4,
-                       U_C = U_B + NB, U_END = U_C + NCB;
+  // chunk-contribution passes: the two gate sums (then, in place, the scaled operands) and
+  // the chunk's last row of each
+  static constexpr int U_B = 0, U_C = U_B + NB, U_D = U_C + NCB, U_END = U_D + (DKP + DVP) * 4;
   // backward output pass: q, k, v, dO, B, C, four states, two sets of pair tables, boundary
   // sums and the norm-weight partials
   static constexpr int G_Q = 0, G_K = G_Q + NQ, G_V = G_K + NQ, G_D = G_V + NV, G_B = G_D + NCB,
@@ -157,6 +157,26 @@ struct Rows {
       }
     }
   }
+  // In place over the same elements as store<P>(): G holds running sums G[t][c]; each becomes
+  // xscale x 2^{dec[c] - G[t][c]} (dec given: the chunk's last row) or xscale x 2^{G[t][c]}
+  // (dec null), zero outside the valid part.  A thread touches only its own elements.
+  template <int P>
+  __device__ __forceinline__ void scale_into(float* G, const float* dec, float xscale, int n,
+                                             int valid, int tid) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + j * kBT, t = i / NPP, c = i - t * NPP;
+      const bool in = t < valid && W * c < n;
+      const bf16* e = reinterpret_cast<const bf16*>(&x[j]);
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        const int col = W * c + k;
+        const float gv = G[t * P + col];
+        const float f = fexp2(dec ? dec[col] - gv : gv);
+        G[t * P + col] = in ? xscale * bf(e[k]) * f : 0.f;
+      }
+    }
+  }
 };
 // A [dk][dv] fp32 state for [DKP][P] LDS, zero padded, loaded and stored the same way (VEC:
 // 16-byte pieces along a row, dv % 4 == 0; the last thread's surplus pieces repeat the last
@@ -222,20 +242,6 @@ __device__ __forceinline__ void gate_cumsum(float* s, int n, int valid, float in
 // Running-sum value at row `ref` (0 for ref < 0: the chunk start).
 __device__ __forceinline__ float at_ref(const float* s, int P, int ref, int c) {
   return ref >= 0 ? s[ref * P + c] : 0.f;
-}
-
-// In place over a chunk's 64 rows x NP columns: X[s][c] <- xscale X[s][c] 2^{G[end][c] - G[s][c]}
-// (end >= 0: factors relative to row end), or xscale X[s][c] 2^{G[s][c]} (end < 0: relative to
-// the chunk start).  Every exponent is <= 0.
-template <int NP, int PX, int PG>
-__device__ __forceinline__ void prescale(float* X, const float* G, int end, float xscale, int tid) {
-  static_assert((kBC * NP) % kBT == 0, "tile must split evenly over the threads");
-#pragma unroll
-  for (int j = 0; j < kBC * NP / kBT; ++j) {
-    const int i = tid + j * kBT, s = i / NP, c = i - s * NP;
-    const float d = end >= 0 ? G[end * PG + c] - G[s * PG + c] : G[s * PG + c];
-    X[s * PX + c] *= xscale * fexp2(d);
-  }
 }
 
 // acc[ct][et] (lane: rows c = 16 ct + 4 g + i, column e = 16 et + r) =
@@ -392,21 +398,20 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sX = reinterpret_cast<float*>(smem + Lo::U_X);  // k (fp32, pitch PC)
-  float* sY = reinterpret_cast<float*>(smem + Lo::U_Y);  // v
-  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);
-  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);
+  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);  // key-gate sums, then k scaled
+  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);  // value-gate sums, then v scaled
+  float* sD = reinterpret_cast<float*>(smem + Lo::U_D);  // the sums' last row (the decays)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ChunkIx ci = chunk_ix(p);
+  Rows<DKP, VEC> xk;
+  Rows<DVP, VEC> xv;
   {
-    Rows<DKP, VEC> xk, xz;
-    Rows<DVP, VEC> xv, xw;
+    Rows<DKP, VEC> xz;
+    Rows<DVP, VEC> xw;
     xk.load(p.k, ci.row0, p.H, p.dk, ci.valid, tid);
     xv.load(p.v, ci.row0, p.H, p.dv, ci.valid, tid);
     xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
     xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
-    xk.template store<PC>(sX, p.dk, ci.valid, tid);
-    xv.template store<PC>(sY, p.dv, ci.valid, tid);
     xz.template store<PB>(sB, p.dk, ci.valid, tid);
     xw.template store<PC>(sC, p.dv, ci.valid, tid);
   }
@@ -414,12 +419,18 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
   gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
   gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
   __syncthreads();
+  for (int i = tid; i < DKP + DVP; i += kBT)
+    sD[i] = i < DKP ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - DKP)];
+  __syncthreads();
   const long slot = ci.bh * p.NC + ci.j;
   const int r = lane & 15, g = lane >> 4;
-  // k_s 2^{B_end - B_s} and v_s 2^{C_end - C_s} in place, once per element
-  prescale<DKP, PC, PB>(sX, sB, kBC - 1, 1.f, tid);
-  prescale<DVP, PC, PC>(sY, sC, kBC - 1, 1.f, tid);
+  // k_s 2^{B_end - B_s} over B and v_s 2^{C_end - C_s} over C, in place (the thread that staged
+  // an element of z or w holds the same element of k or v)
+  xk.template scale_into<PB>(sB, sD, 1.f, p.dk, ci.valid, tid);
+  xv.template scale_into<PC>(sC, sD + DKP, 1.f, p.dv, ci.valid, tid);
   __syncthreads();
+  const float* sX = sB;
+  const float* sY = sC;
   for (int u = wave; u < NDK * NDV; u += 4) {
     const int ct = u / NDV, et = u - ct * NDV;
     const int c = 16 * ct + r, e = 16 * et + r;
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
 #pragma unroll 8
     for (int ks = 0; ks < kBC / 4; ++ks) {
       const int s = 4 * ks + g;
-      acc = mfma_f32(sX[s * PC + c], sY[s * PC + e], acc);
+      acc = mfma_f32(sX[s * PB + c], sY[s * PC + e], acc);
     }
     float* dst = p.states + slot * p.dk * p.dv;
 #pragma unroll
@@ -437,15 +448,14 @@ __global__ __launch_bounds__(kBT) void beta_fwd_state(BetaArgs p) {
     }
   }
   for (int i = tid; i < p.dk + p.dv; i += kBT)
-    p.dec[slot * (p.dk + p.dv) + i] =
-        i < p.dk ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - p.dk)];
+    p.dec[slot * (p.dk + p.dv) + i] = i < p.dk ? sD[i] : sD[DKP + (i - p.dk)];
 }
 
 // ----------------------------------------------------------------------- pass 2 (both ways)
 // In place over chunks, per (image, head) and state element (c, e):
 //   forward:  slot j <- S entering chunk j;  S <- 2^{dec_j[c] + dec_j[e]} S + U_j
 //   reverse:  slot j <- G reaching chunk j's end;  G <- 2^{dec_j[c] + dec_j[e]} G + dU_j
-constexpr int kScanBatch = 16;
+constexpr int kScanBatch = 64;
 __global__ __launch_bounds__(256) void beta_scan(float* st, const float* dec, int NC, int dk,
                                                  int dv, int reverse) {
   const long bh = blockIdx.y;
@@ -674,44 +684,53 @@ __global__ __launch_bounds__(kBT) void beta_fwd_out(BetaArgs p) {
 // Each chunk's gradient-state contribution dU = sum_t (q_scale q_t 2^{B_t})^T (dO_t 2^{C_t})
 // (relative to the chunk start) and its log2 decays.
 template <int NDK, int NDV, bool VEC>
-__global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 1))) void beta_bwd_state(
+    BetaArgs p) {
   using Lo = BetaLay<NDK, NDV>;
   constexpr int DKP = Lo::DKP, DVP = Lo::DVP, PB = Lo::PB, PC = Lo::PC;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sX = reinterpret_cast<float*>(smem + Lo::U_X);  // q (fp32, pitch PC)
-  float* sY = reinterpret_cast<float*>(smem + Lo::U_Y);  // dO
-  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);
-  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);
+  float* sB = reinterpret_cast<float*>(smem + Lo::U_B);  // key-gate sums, then q scaled
+  float* sC = reinterpret_cast<float*>(smem + Lo::U_C);  // value-gate sums, then dO scaled
+  float* sD = reinterpret_cast<float*>(smem + Lo::U_D);  // the sums' last row (the decays)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const ChunkIx ci = chunk_ix(p);
+  Rows<DKP, VEC> xq;
   {
-    Rows<DKP, VEC> xq, xz;
+    Rows<DKP, VEC> xz;
     Rows<DVP, VEC> xw;
     xq.load(p.q, ci.row0, p.H, p.dk, ci.valid, tid);
     xz.load(p.z, ci.row0, p.H, p.dk, ci.valid, tid);
     xw.load(p.w, ci.row0, p.H, p.dv, ci.valid, tid);
-    xq.template store<PC>(sX, p.dk, ci.valid, tid);
     xz.template store<PB>(sB, p.dk, ci.valid, tid);
     xw.template store<PC>(sC, p.dv, ci.valid, tid);
   }
+  float dO[NDV][4];
   {
-    float dO[NDV][4], od[NDV][4], gp[NDV];
+    float od[NDV][4], gp[NDV];
     out_stage_bwd<NDV, false>(p, ci, wave, lane, dO, od, gp);
-#pragma unroll
-    for (int E = 0; E < NDV; ++E)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sY[(16 * wave + 4 * g + i) * PC + 16 * E + r] = dO[E][i];
   }
   __syncthreads();
   gate_cumsum<PB>(sB, p.dk, ci.valid, p.inv_tau, wave, lane);
   gate_cumsum<PC>(sC, p.dv, ci.valid, p.inv_tau, wave, lane);
   __syncthreads();
-  const long slot = ci.bh * p.NC + ci.j;
-  // q_scale q_t 2^{B_t} and dO_t 2^{C_t} in place, once per element
-  prescale<DKP, PC, PB>(sX, sB, -1, p.q_scale, tid);
-  prescale<DVP, PC, PC>(sY, sC, -1, 1.f, tid);
+  for (int i = tid; i < DKP + DVP; i += kBT)
+    sD[i] = i < DKP ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - DKP)];
   __syncthreads();
+  const long slot = ci.bh * p.NC + ci.j;
+  // q_scale q_t 2^{B_t} over B and dO_t 2^{C_t} over C, in place (each thread its own elements:
+  // q as staged, dO as the output-stage backward left it in this lane)
+  xq.template scale_into<PB>(sB, nullptr, p.q_scale, p.dk, ci.valid, tid);
+#pragma unroll
+  for (int E = 0; E < NDV; ++E)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* cp = sC + (16 * wave + 4 * g + i) * PC + 16 * E + r;
+      *cp = dO[E][i] * fexp2(*cp);
+    }
+  __syncthreads();
+  const float* sX = sB;
+  const float* sY = sC;
   for (int u = wave; u < NDK * NDV; u += 4) {
     const int ct = u / NDV, et = u - ct * NDV;
     f32x4 acc = zero4();
@@ -720,7 +739,7 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
 #pragma unroll 8
       for (int ks = 0; ks < kBC / 4; ++ks) {
         const int s = 4 * ks + g;
-        acc = mfma_f32(sX[s * PC + c], sY[s * PC + e], acc);
+        acc = mfma_f32(sX[s * PB + c], sY[s * PC + e], acc);
       }
     }
     float* dst = p.gst + slot * p.dk * p.dv;
@@ -732,8 +751,7 @@ __global__ __launch_bounds__(kBT) void beta_bwd_state(BetaArgs p) {
     }
   }
   for (int i = tid; i < p.dk + p.dv; i += kBT)
-    p.dec[slot * (p.dk + p.dv) + i] =
-        i < p.dk ? sB[(kBC - 1) * PB + i] : sC[(kBC - 1) * PC + (i - p.dk)];
+    p.dec[slot * (p.dk + p.dv) + i] = i < p.dk ? sD[i] : sD[DKP + (i - p.dk)];
 }
 
 // ------------------------------------------------------------------------ pass 3 (backward)
