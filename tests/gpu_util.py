@@ -72,6 +72,17 @@ def maxrel(got: np.ndarray, ref: np.ndarray) -> float:
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
+def elementwise_diag(got: np.ndarray, ref: np.ndarray) -> str:
+    """Elementwise diagnostics of a [B, L, H, d] tensor (logged, not asserted): where the
+    normwise error peaks (token, head) and the largest elementwise relative error over the
+    elements whose reference exceeds 1e-3 of the tensor's max."""
+    d = np.abs(got - ref)
+    at = np.unravel_index(int(np.argmax(d)), d.shape)
+    big = np.abs(ref) > 1e-3 * np.max(np.abs(ref))
+    ew = float(np.max(d[big] / np.abs(ref[big]))) if np.any(big) else 0.0
+    return "t%d/h%d ew%.1e" % (at[1], at[2], ew)
+
+
 def gla_forward(case: W.GLACase, chunk: int, *, seg_chunks: int = 0, want_saved: bool = False,
                 want_opre: bool = True, gamma=True, tau: float = 16.0, q_scale: float = 1.0,
                 eps: float = 1e-5, ws=None, lowrank: W.LowRankGate | None = None):
