@@ -244,14 +244,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 115313.1 KiB / 0.500075 + 91422.0 KiB / 1.0, segment scan 1666.6 + 2594.2,
-        # final pass 95167.8 + 92273.5 (FETCH_SIZE, WRITE_SIZE; copy: 131091.7 KiB read per
+        # pass A 115312.8 KiB / 0.500076 + 91437.4 KiB / 1.0, segment scan 1701.6 + 2594.2,
+        # final pass 95168.0 + 92276.5 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 625173379,
-        # pass A 79429.4 + 5099.5, state scan 2819.1 + 5184.0, output pass 68157.4 + 157023.4
-        "dig_gla_fwd": 479307215,
+        "dig_gla_bwd": 625263374,
+        # pass A 79430.4 + 5099.5, state scan 2866.6 + 5184.0, output pass 68226.5 + 157036.7
+        "dig_gla_fwd": 479561422,
     },
-    "sources_sha256": "bbef3c1f3dc9e17b71f2214907a9655e83f3ff5e8558cd007ef96222e452a558",
+    "sources_sha256": "0d26e9258c8ea4f44e462aa26fcc91689b518bb847be70b743ded39aaf6e3448",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",

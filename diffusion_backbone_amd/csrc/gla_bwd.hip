@@ -58,10 +58,24 @@ __device__ __forceinline__ void gstate_scan_one(float* gst, const float* seg_lg,
   float* base = gst + bh * nseg * per + ce;
   const float* lg = seg_lg + bh * nseg * dk + c;
   float G = 0.f;
-  for (int ps = nseg - 1; ps >= 1; --ps) {
-    const float d = base[(long)ps * per];
-    base[(long)ps * per] = G;
-    G = exp2f(lg[ps * dk]) * G + d;
+  // each batch's loads are issued together (indices clamped; they read segments no store of
+  // the batch before touches), then the recurrence runs through them in order
+  constexpr int NB = 32;
+  for (int p0 = nseg - 1; p0 >= 1; p0 -= NB) {
+    float d[NB], l[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int ps = max(p0 - i, 1);
+      d[i] = base[(long)ps * per];
+      l[i] = lg[ps * dk];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (p0 - i >= 1) {
+        base[(long)(p0 - i) * per] = G;
+        G = exp2f(l[i]) * G + d[i];
+      }
+    }
   }
   base[0] = G;
 }

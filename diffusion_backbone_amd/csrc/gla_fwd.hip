@@ -111,23 +111,24 @@ __global__ __launch_bounds__(kScanThreads) void gla_state_scan(float* states,
   float S = 0.f;
   float* base = states + bh * NC * per + ce;
   const float* lg = seg_lg + bh * nseg * dk + c;
-  int pseg = 0;
-  for (; pseg + 4 <= nseg - 1; pseg += 4) {
-    float d0 = base[(long)(pseg + 0) * sc * per];
-    float d1 = base[(long)(pseg + 1) * sc * per];
-    float d2 = base[(long)(pseg + 2) * sc * per];
-    float d3 = base[(long)(pseg + 3) * sc * per];
-    float l0 = lg[(pseg + 0) * dk], l1 = lg[(pseg + 1) * dk];
-    float l2 = lg[(pseg + 2) * dk], l3 = lg[(pseg + 3) * dk];
-    base[(long)(pseg + 0) * sc * per] = S; S = exp2f(l0) * S + d0;
-    base[(long)(pseg + 1) * sc * per] = S; S = exp2f(l1) * S + d1;
-    base[(long)(pseg + 2) * sc * per] = S; S = exp2f(l2) * S + d2;
-    base[(long)(pseg + 3) * sc * per] = S; S = exp2f(l3) * S + d3;
-  }
-  for (; pseg < nseg - 1; ++pseg) {
-    float d = base[(long)pseg * sc * per];
-    base[(long)pseg * sc * per] = S;
-    S = exp2f(lg[pseg * dk]) * S + d;
+  // each batch's loads are issued together (indices clamped; they read segments no store of
+  // the batch before touches), then the recurrence runs through them in order
+  constexpr int NB = 32;
+  for (int p0 = 0; p0 < nseg - 1; p0 += NB) {
+    float d[NB], l[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int ps = min(p0 + i, nseg - 2);
+      d[i] = base[(long)ps * sc * per];
+      l[i] = lg[ps * dk];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (p0 + i < nseg - 1) {
+        base[(long)(p0 + i) * sc * per] = S;
+        S = exp2f(l[i]) * S + d[i];
+      }
+    }
   }
   base[(long)(nseg - 1) * sc * per] = S;
 }
