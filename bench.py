@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--pmc-target", choices=["gla_fwd", "gla_bwd", "srem_fwd", "srem_bwd"],
                     default=None)
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--copy-probe-width", type=int, default=16, choices=[4, 8, 16])
     ap.add_argument("--value-gate", action="store_true",
                     help="time only the value-gate calls (dig_gla_*_beta) at --workload")
     ap.add_argument("--stack", default=None,
@@ -244,14 +245,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 115312.8 KiB / 0.500076 + 91437.4 KiB / 1.0, segment scan 1701.6 + 2594.2,
-        # final pass 95168.0 + 92276.5 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
+        # pass A 115314.3 KiB / 0.500076 + 91434.7 KiB / 1.0, segment scan 1701.6 + 2594.2,
+        # final pass 95167.9 + 92278.1 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 625263374,
-        # pass A 79430.4 + 5099.5, state scan 2866.6 + 5184.0, output pass 68226.5 + 157036.7
-        "dig_gla_fwd": 479561422,
+        "dig_gla_bwd": 625265115,
+        # pass A 35783.0 + 5099.5, state scan 2866.6 + 5184.0, output pass 68167.8 + 156961.7
+        "dig_gla_fwd": 389988058,
     },
-    "sources_sha256": "0d26e9258c8ea4f44e462aa26fcc91689b518bb847be70b743ded39aaf6e3448",
+    "sources_sha256": "21889e1d38fa6354f05e8a1f0ed474698eb11d885cc9c4dfbea5758323a05e01",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",
@@ -293,6 +294,8 @@ def probe_lib():
                                          ctypes.POINTER(ctypes.c_double)]
     L.digp_copy.argtypes = [P, P, ctypes.c_size_t, P]
     L.digp_copy.restype = I
+    L.digp_copy_w.argtypes = [P, P, ctypes.c_size_t, I, P]
+    L.digp_copy_w.restype = I
     L.digp_mfma_rate.argtypes = [I, I, I, P, P]
     L.digp_mfma_rate.restype = I
     L.digp_mfma_rate_flops.argtypes = [I, I, I]
@@ -311,18 +314,21 @@ def device_copy(L, src, dst):
         raise RuntimeError("digp_copy failed: %d" % err)
 
 
-def copy_probe(mib, reps):
-    """A plain streaming copy of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE
-    counter readings to bytes."""
+def copy_probe(mib, reps, width=16):
+    """A plain streaming copy of known size with `width`-byte lanes: the reference for scaling
+    FETCH_SIZE / WRITE_SIZE counter readings to bytes."""
     import torch
     L = probe_lib()
     x = torch.ones(mib * 1024 * 1024 // 2, dtype=torch.bfloat16, device="cuda")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     for _ in range(reps):
-        device_copy(L, x, y)
+        err = L.digp_copy_w(x.data_ptr(), y.data_ptr(), x.numel() * 2, width, _stream())
+        if err:
+            raise RuntimeError("digp_copy_w failed: %d" % err)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 2, "reps": reps}), flush=True)
+    print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 2, "reps": reps,
+                      "lane_bytes": width}), flush=True)
 
 
 def gla_bytes_per_token_head(cfg, which):
@@ -900,7 +906,7 @@ def main():
         sys.exit(2)
     import torch
     if args.copy_probe_mib:
-        copy_probe(args.copy_probe_mib, max(1, args.steps))
+        copy_probe(args.copy_probe_mib, max(1, args.steps), args.copy_probe_width)
         return
     if args.stack:
         print(json.dumps({args.stack: block_stack(args.stack, max(1, args.steps))}), flush=True)

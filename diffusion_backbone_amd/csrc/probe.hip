@@ -11,6 +11,11 @@
 //                     chip) from the memory traffic around them.
 //   digp_copy         a streaming device copy (16-byte vectors, eight in flight per thread):
 //                     the HBM ceiling a read-once/write-once kernel can reach.
+//   digp_copy_w       the same copy with 4-, 8- or 16-byte lanes: how the byte counters read
+//                     for each access width.
+//   digp_head_slices  one workgroup per (head, segment) reading that head's slice of every
+//                     token row of the segment, in three workgroup orders: whether the heads
+//                     that share 128-byte lines meet in one XCD's L2.
 //   digp_mfma_rate    bf16 MFMA instructions with operands and accumulators in registers only
 //                     (independent accumulators, no memory): the rate each instruction shape
 //                     can sustain, the ceiling under the contraction microbenchmark.
@@ -191,6 +196,51 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   }
 }
 
+// The same with narrower lanes (V = uint2: 8 bytes, uint32_t: 4 bytes per lane and access).
+template <typename V>
+__global__ __launch_bounds__(256) void copy_kernel_w(const V* __restrict__ src,
+                                                     V* __restrict__ dst, long n) {
+  constexpr int U = 8;
+  const long stride = (long)gridDim.x * 256 * U;
+  for (long base = (long)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[min(base + 256L * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + 256L * u < n) dst[base + 256L * u] = v[u];
+  }
+}
+
+// Reads one head's d-element slice of every token row of a segment ([rows][H][d] bf16, the
+// mixer's layout), one workgroup per (head, segment), and writes one sum per workgroup.  order
+// 0: workgroup = head * nseg + segment (the chunk kernels' order); 1: segment * H + head;
+// 2: order 0 with the segment's rows walked from a per-head offset (heads out of step).
+__global__ __launch_bounds__(256) void head_slice_kernel(const unsigned* __restrict__ src,
+                                                         float* __restrict__ out, int rows, int H,
+                                                         int d, int nseg, int order) {
+  const int blk = blockIdx.x;
+  const int h = order == 1 ? blk % H : blk / nseg;
+  const int seg = order == 1 ? blk / H : blk % nseg;
+  const int rps = rows / nseg, pairs = d / 2;
+  const int n = rps * pairs;
+  float acc = 0.f;
+  for (int i0 = 0; i0 < n; i0 += 256 * 4) {
+    unsigned v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + 256 * u + (int)threadIdx.x, n - 1);
+      int t = i / pairs;
+      const int c = i - t * pairs;
+      if (order == 2) t = (t + h * (rps / H)) % rps;
+      v[u] = src[((long)(seg * rps + t) * H + h) * pairs + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += __uint_as_float(v[u] << 16);
+  }
+  out[(long)blk * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace dig
 
@@ -228,6 +278,37 @@ int digp_mfma_rate(int wide, int nwg, int iters, float* sink, hipStream_t st) {
 }
 double digp_mfma_rate_flops(int wide, int nwg, int iters) {
   return wide ? 4.0 * 32768 * 4 * iters * nwg : 8.0 * 16384 * 4 * iters * nwg;
+}
+
+// A streaming copy with `width`-byte lanes (4, 8 or 16): how the HBM byte counters read for
+// accesses of each width.
+int digp_copy_w(const void* src, void* dst, size_t bytes, int width, hipStream_t st) {
+  if (!src || !dst || (width != 4 && width != 8 && width != 16) || bytes % 16)
+    return (int)hipErrorInvalidValue;
+  const long n = (long)(bytes / width);
+  long g = (n + 256 * 8 - 1) / (256 * 8);
+  if (g > 256 * 8) g = 256 * 8;
+  if (g < 1) g = 1;
+  if (width == 16)
+    hipLaunchKernelGGL(dig::copy_kernel, dim3((unsigned)g), dim3(256), 0, st,
+                       static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  else if (width == 8)
+    hipLaunchKernelGGL(dig::copy_kernel_w<uint2>, dim3((unsigned)g), dim3(256), 0, st,
+                       static_cast<const uint2*>(src), static_cast<uint2*>(dst), n);
+  else
+    hipLaunchKernelGGL(dig::copy_kernel_w<uint32_t>, dim3((unsigned)g), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), n);
+  return (int)hipGetLastError();
+}
+
+// src: rows * H * d bf16 (d even); out: H * nseg * 256 floats.
+int digp_head_slices(const void* src, float* out, int rows, int H, int d, int nseg, int order,
+                     hipStream_t st) {
+  if (!src || !out || d % 2 || rows % nseg || order < 0 || order > 2)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(dig::head_slice_kernel, dim3((unsigned)(H * nseg)), dim3(256), 0, st,
+                     static_cast<const unsigned*>(src), out, rows, H, d, nseg, order);
+  return (int)hipGetLastError();
 }
 
 int digp_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {
