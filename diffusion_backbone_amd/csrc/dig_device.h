@@ -18,6 +18,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Workgroup i of n runs on XCD i mod 8; returns the work item it takes when XCD x takes the
+// x-th contiguous run of items (n / 8 items, one more for the first n mod 8 XCDs).
+__device__ __forceinline__ int xcd_item(int i, int n) {
+  const int q = n >> 3, r = n & 7, x = i & 7, k = i >> 3;
+  return x * q + min(x, r) + k;
+}
+
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x);

@@ -45,8 +45,6 @@ constexpr float kSlowDecayLog2 = 96.0f;  // e^{-b} factors up to 2^96 stay finit
 constexpr int kFwdLdsBudget = 160 * 1024;
 
 constexpr int al16(int x) { return (x + 15) / 16 * 16; }
-// segments launched per (image, head) without the look-back: a multiple of the 8 XCDs
-__host__ __device__ constexpr int fwd_seg_launch(int nseg) { return (nseg + 7) / 8 * 8; }
 
 // PAD: raw staging rows at pitches the gate pass (one lane per token) reads without bank
 // conflicts (register-staged rows; LDS DMA writes them packed).
@@ -159,15 +157,20 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   // Workgroups are handed to the 8 XCDs (each with its own L2) in turn, workgroup i to XCD
-  // i mod 8.  A head's rows are d_k- or d_v-wide slices of each token row, sharing 128-byte
+  // i mod 8.  A head's rows are d_k- or d_v-wide slices of each token row that share 128-byte
   // lines with the neighbouring heads, so the heads of one segment should meet in one L2:
-  // without the look-back the launch pads the segments per (image, head) to a multiple of 8
-  // (workgroup bh * nseg8 + seg lands on XCD seg mod 8) and the padding workgroups, and pass
-  // A's for the last segment (whose state nobody needs), exit at once.
-  const int nseg_launch = LB ? p.nseg : fwd_seg_launch(p.nseg);
-  const int seg = blockIdx.x % nseg_launch;
-  const int bh = blockIdx.x / nseg_launch;
-  if (seg >= (OUT ? p.nseg : p.nseg - 1)) return;
+  // without the look-back, the work items are numbered segment-major (heads fastest) and XCD
+  // x takes the x-th contiguous eighth of them (a bijection of the grid, nothing padded).
+  int seg, bh;
+  if constexpr (LB) {
+    seg = blockIdx.x % p.nseg;
+    bh = blockIdx.x / p.nseg;
+  } else {
+    const int nbh = p.B * p.H;
+    const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+    seg = item / nbh;
+    bh = item - seg * nbh;
+  }
   const int b = bh / p.H, h = bh - b * p.H;
   const int H = p.H;
   const int dk = EXACT ? DK : p.dk, dv = EXACT ? DV : p.dv;
@@ -883,14 +886,13 @@ static hipError_t launch_fwd_c(const GlaShape& s, GlaFwdParams p, hipStream_t st
     int bytes_a, nbuf_a;
     fwd_lds<T, DK, DV, EXACT, C, false, LR>(s, &bytes_a, &nbuf_a);
     hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, false, NW, false, LR>),
-                       dim3((unsigned)(BH * fwd_seg_launch(s.nseg))), dim3(64 * NW), bytes_a,
-                       st, p, nbuf_a);
+                       dim3((unsigned)(BH * (s.nseg - 1))), dim3(64 * NW), bytes_a, st, p,
+                       nbuf_a);
     const hipError_t e = launch_gla_state_scan(s, p.states, p.seg_lg, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((gla_fwd_kernel<T, DK, DV, EXACT, C, true, NW, false, LR>),
-                     dim3((unsigned)(BH * fwd_seg_launch(s.nseg))), dim3(64 * NW), bytes_c, st,
-                     p, nbuf_c);
+                     dim3((unsigned)(BH * s.nseg)), dim3(64 * NW), bytes_c, st, p, nbuf_c);
   return hipGetLastError();
 }
 
