@@ -97,11 +97,15 @@ struct ChunkIx {
   long row0;  // element offset of (b, token 64 j, h, 0) divided by the row width
   long bh;
 };
+// Work items numbered chunk-major (heads fastest), XCD x (workgroup i runs on XCD i mod 8)
+// taking the x-th contiguous eighth of them: the heads of a chunk, whose rows share 128-byte
+// lines, meet in one L2.
 __device__ __forceinline__ ChunkIx chunk_ix(const BetaArgs& p) {
   ChunkIx c;
-  const long blk = blockIdx.x;
-  c.bh = blk / p.NC;
-  c.j = (int)(blk - c.bh * p.NC);
+  const int nbh = p.B * p.H;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  c.j = item / nbh;
+  c.bh = item - (long)c.j * nbh;
   c.b = (int)(c.bh / p.H);
   c.h = (int)(c.bh - (long)c.b * p.H);
   c.valid = min(kBC, p.L - kBC * c.j);
