@@ -378,6 +378,18 @@ def test_bwd_cancelling_first_token(dtype):
     _check_bwd(case, gla_backward(case, f), TOL[dtype])
 
 
+def test_fwd_bwd_multi_round_grid():
+    # three passes with grids that are no multiple of the 8 XCDs and take several rounds of
+    # workgroups (37 images x 6 heads x 4 segments: pass A 666 workgroups forward, 888 for the
+    # output pass and both backward passes): the work-item order is a bijection of any grid
+    announce("fwd+bwd multi-round grid B=37 L=640 seg=3")
+    case = _case("dig_s2_256", batch=37, seq_len=640, random_gamma=True)
+    f = gla_forward(case, 64, seg_chunks=3, want_saved=True)
+    _check_fwd(case, f, TOL["bf16"])
+    g = gla_backward(case, f)
+    _check_bwd(case, g, TOL["bf16"])
+
+
 def test_bwd_determinism():
     announce("bwd determinism")
     case = _case("dig_xl2_2048", batch=1, seq_len=512)
