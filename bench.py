@@ -15,7 +15,7 @@ roofline of the dominant call, an LDS-resident contraction microbenchmark (MFMA 
 the contraction phases), steady-state and cold-cache probes against a measured streaming-copy
 ceiling, and the fp64 oracle timed on the host (single thread and all cores).
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: the library measures one GPU.
 """
 from __future__ import annotations
 
