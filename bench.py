@@ -245,14 +245,14 @@ def timed(fn, steps, warmup):
 TRAFFIC = {
     "workload": "dig_xl2_2048",
     "bytes": {
-        # pass A 115312.6 KiB / 0.500076 + 91396.1 KiB / 1.0, segment scan 1701.6 + 2594.2,
-        # final pass 95163.4 + 92261.7 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
+        # pass A 115319.7 KiB / 0.500076 + 91413.1 KiB / 1.0, segment scan 1695.6 + 2594.2,
+        # final pass 95167.8 + 92273.1 (FETCH_SIZE, WRITE_SIZE; copy: 131091.8 KiB read per
         # 262144 KiB moved, 262144 KiB written per 262144 KiB moved)
-        "dig_gla_bwd": 625196099,
-        # pass A 36422.4 + 5093.8, state scan 2866.6 + 5184.0, output pass 67292.1 + 157266.0
-        "dig_gla_fwd": 389809955,
+        "dig_gla_bwd": 625236564,
+        # pass A 36420.3 + 5093.8, state scan 2864.6 + 5184.0, output pass 68264.5 + 157063.7
+        "dig_gla_fwd": 391585479,
     },
-    "sources_sha256": "f9458cc253e5ec3db38cd363ea544b11be75a24ac9fea8ffc861e19d7de142be",
+    "sources_sha256": "cd034969375aacdffccbc2e98c79b112e10608749f42542ca169771c4c8f2843",
 }
 TRAFFIC_SOURCES = ("diffusion_backbone_amd/csrc/gla_bwd_kernel.h",
                    "diffusion_backbone_amd/csrc/gla_bwd.hip",

@@ -50,6 +50,7 @@ size_t gla_bwd_flag_offset(const GlaShape& s) {
 
 // Reverse exclusive scan over segments, in place: slot(p) <- gradient reaching the end of
 // segment p from later segments.  G(nseg-1) = 0, G(p-1) = 2^{lg(p)} G(p) + dG(p).
+template <int NB>
 __device__ __forceinline__ void gstate_scan_one(float* gst, const float* seg_lg, long idx,
                                                 int nseg, int dk, int dv) {
   const long per = (long)dk * dv;
@@ -59,8 +60,8 @@ __device__ __forceinline__ void gstate_scan_one(float* gst, const float* seg_lg,
   const float* lg = seg_lg + bh * nseg * dk + c;
   float G = 0.f;
   // each batch's loads are issued together (indices clamped; they read segments no store of
-  // the batch before touches), then the recurrence runs through them in order
-  constexpr int NB = 32;
+  // the batch before touches), then the recurrence runs through them in order; NB is sized to
+  // the segment count (clamped loads past the first segment still cost instructions)
   for (int p0 = nseg - 1; p0 >= 1; p0 -= NB) {
     float d[NB], l[NB];
 #pragma unroll
@@ -99,6 +100,7 @@ __device__ __forceinline__ void dgamma_reduce_one(const float* part, int nparts,
 
 // Pass B of the backward: blocks [0, nscan) scan the segment gradient states; the next dv
 // blocks (when out is given) reduce the dgamma partials that pass A wrote.
+template <int NB>
 __global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const float* seg_lg,
                                                             int BH, int nseg, int dk, int dv,
                                                             int nscan, const float* part,
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(kBThreads) void gla_gstate_scan(float* gst, const f
     return;
   }
   const long idx = (long)blockIdx.x * kBThreads + threadIdx.x;
-  if (idx < (long)BH * dk * dv) gstate_scan_one(gst, seg_lg, idx, nseg, dk, dv);
+  if (idx < (long)BH * dk * dv) gstate_scan_one<NB>(gst, seg_lg, idx, nseg, dk, dv);
 }
 
 // dgamma alone (single-segment backward: the final pass wrote the partials).
@@ -122,9 +124,14 @@ hipError_t launch_gla_gstate_scan(const GlaShape& s, const GlaBwdParams& p, hipS
   const long nthreads = BH * s.dk * s.dv;
   const int nscan = (int)((nthreads + kBThreads - 1) / kBThreads);
   const int nred = p.d_norm_w ? s.dv : 0;
-  hipLaunchKernelGGL(gla_gstate_scan, dim3((unsigned)(nscan + nred)), dim3(kBThreads), 0, st,
-                     p.gstates, p.seg_lg, (int)BH, s.nseg, s.dk, s.dv, nscan, p.dgamma_part,
-                     (int)(BH * s.nseg), p.d_norm_w);
+  if (s.nseg - 1 <= 8)
+    hipLaunchKernelGGL(gla_gstate_scan<8>, dim3((unsigned)(nscan + nred)), dim3(kBThreads), 0,
+                       st, p.gstates, p.seg_lg, (int)BH, s.nseg, s.dk, s.dv, nscan,
+                       p.dgamma_part, (int)(BH * s.nseg), p.d_norm_w);
+  else
+    hipLaunchKernelGGL(gla_gstate_scan<32>, dim3((unsigned)(nscan + nred)), dim3(kBThreads), 0,
+                       st, p.gstates, p.seg_lg, (int)BH, s.nseg, s.dk, s.dv, nscan,
+                       p.dgamma_part, (int)(BH * s.nseg), p.d_norm_w);
   return hipGetLastError();
 }
 

@@ -201,20 +201,9 @@ __global__ __launch_bounds__(64 * NW) void gla_bwd_kernel(GlaBwdParams p) {
   const int r16 = lane & 15, g4 = lane >> 4;
   // pass A covers every segment: segment 0's G is not needed, but its dgamma partial is (with
   // more than one segment the dgamma partials come from pass A and the scan reduces them)
-  // (look-back: later segments first, so that a workgroup waits only on earlier ones).
-  // Without the look-back the work items are numbered segment-major (heads fastest) and XCD x
-  // (workgroup i runs on XCD i mod 8) takes the x-th contiguous eighth of them: the heads of
-  // a segment, whose rows share 128-byte lines, meet in one L2.
-  int seg, bh;
-  if constexpr (LB) {
-    seg = p.nseg - 1 - (int)(blockIdx.x % p.nseg);
-    bh = blockIdx.x / p.nseg;
-  } else {
-    const int nbh = p.B * p.H;
-    const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
-    seg = item / nbh;
-    bh = item - seg * nbh;
-  }
+  // (look-back: later segments first, so that a workgroup waits only on earlier ones)
+  const int seg = LB ? p.nseg - 1 - (int)(blockIdx.x % p.nseg) : (int)(blockIdx.x % p.nseg);
+  const int bh = blockIdx.x / p.nseg;
   const bool dg_here = FIN ? (p.nseg == 1 || LB) : true;
   const int b = bh / p.H, h = bh - b * p.H;
   const int H = p.H;

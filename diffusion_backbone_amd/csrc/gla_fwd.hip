@@ -99,6 +99,7 @@ size_t gla_seglg_bytes(const GlaShape& s) {
 // Exclusive scan over segments, in place: slot(p) <- state entering segment p.
 // Forward direction: S(0) = 0, S(p+1) = 2^{lg(p)} S(p) + dS(p).
 constexpr int kScanThreads = 256;
+template <int NB>
 __global__ __launch_bounds__(kScanThreads) void gla_state_scan(float* states,
                                                               const float* seg_lg, int BH,
                                                               int NC, int sc, int nseg, int dk,
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(kScanThreads) void gla_state_scan(float* states,
   float* base = states + bh * NC * per + ce;
   const float* lg = seg_lg + bh * nseg * dk + c;
   // each batch's loads are issued together (indices clamped; they read segments no store of
-  // the batch before touches), then the recurrence runs through them in order
-  constexpr int NB = 32;
+  // the batch before touches), then the recurrence runs through them in order; NB is sized to
+  // the segment count (clamped loads past the last segment still cost instructions)
   for (int p0 = 0; p0 < nseg - 1; p0 += NB) {
     float d[NB], l[NB];
 #pragma unroll
@@ -137,9 +138,13 @@ hipError_t launch_gla_state_scan(const GlaShape& s, float* states, const float* 
                                  hipStream_t st) {
   const long BH = (long)s.B * s.H;
   const long nthreads = BH * s.dk * s.dv;
-  hipLaunchKernelGGL(gla_state_scan, dim3((unsigned)((nthreads + kScanThreads - 1) / kScanThreads)),
-                     dim3(kScanThreads), 0, st, states, seg_lg, (int)BH, s.NC, s.sc, s.nseg, s.dk,
-                     s.dv);
+  const dim3 grid((unsigned)((nthreads + kScanThreads - 1) / kScanThreads));
+  if (s.nseg - 1 <= 8)
+    hipLaunchKernelGGL(gla_state_scan<8>, grid, dim3(kScanThreads), 0, st, states, seg_lg,
+                       (int)BH, s.NC, s.sc, s.nseg, s.dk, s.dv);
+  else
+    hipLaunchKernelGGL(gla_state_scan<32>, grid, dim3(kScanThreads), 0, st, states, seg_lg,
+                       (int)BH, s.NC, s.sc, s.nseg, s.dk, s.dv);
   return hipGetLastError();
 }
 

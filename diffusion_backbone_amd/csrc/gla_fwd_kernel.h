@@ -158,11 +158,13 @@ __global__ __launch_bounds__(64 * NW) void gla_fwd_kernel(GlaFwdParams p, int nb
   const int r16 = lane & 15, g4 = lane >> 4;
   // Workgroups are handed to the 8 XCDs (each with its own L2) in turn, workgroup i to XCD
   // i mod 8.  A head's rows are d_k- or d_v-wide slices of each token row that share 128-byte
-  // lines with the neighbouring heads, so the heads of one segment should meet in one L2:
-  // without the look-back, the work items are numbered segment-major (heads fastest) and XCD
-  // x takes the x-th contiguous eighth of them (a bijection of the grid, nothing padded).
+  // lines with the neighbouring heads.  The output pass numbers workgroups head x segments +
+  // segment.  Pass A launches one segment fewer per head (the last segment's state is never
+  // needed), which in that numbering would spread a segment's heads over the XCDs: its work
+  // items are numbered segment-major (heads fastest) and XCD x takes the x-th contiguous
+  // eighth of them, so the heads of a segment meet in one L2.
   int seg, bh;
-  if constexpr (LB) {
+  if constexpr (OUT) {
     seg = blockIdx.x % p.nseg;
     bh = blockIdx.x / p.nseg;
   } else {
